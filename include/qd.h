@@ -1,0 +1,225 @@
+/*
+ * qd.h -- C ABI of the int8 weight-only Qwen3-family decoder step for AMD MI355X (gfx950).
+ *
+ * The library runs the forward step of a Qwen3-family decoder whose projection
+ * weights are stored as int8 with one fp32 scale per output row: prompt token ids
+ * in, greedily generated token ids out.  It has three workloads: prefill over the
+ * whole prompt, single-stream decode (one token per step) and batched decode
+ * (B sequences per step, weights swept once per step).  Sources:
+ *   - "Model-agnostic LLM inference", section "Supported models": the decoder
+ *     family (grouped-query attention, RMSNorm on Q and K, RoPE, SiLU-gated
+ *     feed-forward, tied embeddings, no attention bias) and its gates.
+ *   - same page, section "The quantized load cache": int8 weights with per-row
+ *     scales; section "Notes": greedy arg-max by default, one call runs prefill
+ *     then decode up to max_new_tokens or end-of-text; section "Long context":
+ *     context sizing and the 65,536-token ceiling; section "Errors": named
+ *     error codes, every problem named before any GPU work.
+ *   - "LLM inference overview", sections "Results" and "Workload
+ *     characteristics": prefill fills the KV cache, decode sweeps all weights per
+ *     token, batched decode sweeps them once per step for all B sequences.
+ *
+ * Precision contract (the pages leave it open; this library fixes it):
+ * symmetric per-output-channel int8 codes in [-127, 127] with fp32 scales
+ * (scale = absmax / 127, code = round-half-even(w / scale), IEEE fp32 division),
+ * bf16 activations rounded at every tensor the model produces, fp32 accumulation,
+ * fp32 RMSNorm and softmax, a bf16 KV cache and fp32 logits.
+ *
+ * Memory ownership: the library never allocates device memory.  The caller
+ * allocates three device buffers whose sizes qd_query_sizes() returns (weights,
+ * KV cache, workspace) and keeps them alive until qd_free().  A qd_model handle
+ * owns host memory and HIP graph objects only.  Every call that takes a stream
+ * enqueues its work on that stream and returns without waiting, except where a
+ * comment says otherwise.  A handle must be used from one host thread at a time.
+ *
+ * Errors: every entry point returns a qd_status.  On failure nothing has been
+ * enqueued unless the code is QD_ERR_DEVICE, and qd_last_error() returns a
+ * message (thread-local, valid until the next call on the same thread) that names
+ * every problem found.
+ */
+#ifndef QD_H
+#define QD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* qd_stream;  /* a hipStream_t; NULL is the default stream */
+
+typedef enum {
+  QD_OK = 0,
+  /* The shape is outside the supported family or its gates ("Model-agnostic LLM
+   * inference", sections "Supported models" and "Errors"). */
+  QD_ERR_UNSUPPORTED_ARCH = 1,
+  /* Empty or out-of-range token ids, max_new_tokens < 1, a batch or context
+   * larger than the model was loaded for ("Errors", invalid_arguments). */
+  QD_ERR_INVALID_ARGUMENTS = 2,
+  /* A context length above 65,536 tokens ("Long context"). */
+  QD_ERR_CONTEXT_CEILING = 3,
+  /* A required weight pointer is NULL ("Errors", checkpoint_not_found). */
+  QD_ERR_CHECKPOINT_NOT_FOUND = 4,
+  /* A caller buffer is smaller than qd_query_sizes() asked for. */
+  QD_ERR_BUFFER_TOO_SMALL = 5,
+  /* A HIP runtime call failed, or no gfx950 device is present. */
+  QD_ERR_DEVICE = 6,
+} qd_status;
+
+#define QD_MAX_CONTEXT 65536
+
+/* Model dimensions; field names follow the checkpoint's config.json.
+ * Gates from "Model-agnostic LLM inference", section "Supported models":
+ *   n_heads % n_kv_heads == 0; hidden, intermediate and n_heads*head_dim each a
+ *   multiple of 32; tie_word_embeddings != 0; attention_bias == 0.
+ * Gates this library adds for its kernels: every size > 0; head_dim a power of
+ * two in [16, 256]; vocab >= 2; n_heads / n_kv_heads <= 8. */
+typedef struct {
+  int32_t hidden;        /* hidden_size */
+  int32_t n_layers;      /* num_hidden_layers */
+  int32_t n_heads;       /* num_attention_heads */
+  int32_t n_kv_heads;    /* num_key_value_heads */
+  int32_t head_dim;      /* head_dim */
+  int32_t intermediate;  /* intermediate_size */
+  int32_t vocab;         /* vocab_size */
+  float rms_eps;         /* rms_norm_eps */
+  float rope_theta;      /* rope_theta */
+  int32_t tie_word_embeddings;
+  int32_t attention_bias;
+} qd_model_shape;
+
+/* Limits the buffers are sized for. */
+typedef struct {
+  int32_t max_batch;           /* sequences decoded together, 1..64 */
+  int32_t max_ctx;             /* positions per sequence, 1..QD_MAX_CONTEXT */
+  int32_t max_prefill_tokens;  /* prompt tokens summed over one qd_prefill call */
+} qd_limits;
+
+typedef struct {
+  uint64_t weight_bytes;     /* int8 codes, fp32 scales and gains, RoPE table */
+  uint64_t kv_bytes;         /* bf16 K and V: layers x max_batch x kv_heads x max_ctx x head_dim x 2 */
+  uint64_t workspace_bytes;  /* activations, attention partials, counters */
+  uint64_t packed_model_bytes; /* int8 + one fp32 scale per row + fp32 gains, embedding once */
+} qd_sizes;
+
+/* fp32 weights of one layer in checkpoint layout: row-major [out, in], device
+ * pointers.  q [H*D, d], k and v [KV*D, d], o [d, H*D], gate and up [I, d],
+ * down [d, I]; gains in_norm and post_norm [d], q_norm and k_norm [D]. */
+typedef struct {
+  const float *q, *k, *v, *o, *gate, *up, *down;
+  const float *in_norm, *post_norm, *q_norm, *k_norm;
+} qd_layer_f32;
+
+/* All fp32 weights.  embed [V, d] device pointer (also the LM head: tied),
+ * final_norm [d] device pointer, layers: host array of n_layers entries. */
+typedef struct {
+  const float* embed;
+  const float* final_norm;
+  const qd_layer_f32* layers;
+} qd_weights_f32;
+
+/* Caller-owned device buffers, each at least the size qd_query_sizes() gives,
+ * 256-byte aligned. */
+typedef struct {
+  void* weights;   uint64_t weight_bytes;
+  void* kv;        uint64_t kv_bytes;
+  void* workspace; uint64_t workspace_bytes;
+} qd_buffers;
+
+typedef struct qd_model qd_model;
+
+/* Timing of the last qd_generate_greedy call, from HIP events on its stream. */
+typedef struct {
+  double prefill_us;   /* prompt processing up to the first generated id */
+  double decode_us;    /* the max_new_tokens - 1 decode steps */
+  int32_t steps;       /* decode steps run */
+  int32_t n_prompt_tokens;
+} qd_stats;
+
+/* Message for the last failing call on this thread ("" if none). */
+const char* qd_last_error(void);
+
+/* Checks the architecture gates on the host only (no GPU work).  Returns
+ * QD_ERR_UNSUPPORTED_ARCH naming every failed gate, or QD_OK. */
+qd_status qd_check_shape(const qd_model_shape* shape);
+
+/* Byte sizes of the three caller buffers for a shape and limits (host only).
+ * QD_ERR_CONTEXT_CEILING if limits->max_ctx > QD_MAX_CONTEXT. */
+qd_status qd_query_sizes(const qd_model_shape* shape, const qd_limits* limits, qd_sizes* out);
+
+/* Validates everything on the host, then quantizes every projection and the
+ * embedding on the GPU (per-row absmax / 127, round-half-even, bit-exact with
+ * an IEEE fp32 reference) into buffers->weights, builds the RoPE table and
+ * clears the KV positions.  The fp32 inputs may be freed once the stream has
+ * passed this call.  On success *out is a new handle.
+ * Quantization: "Model-agnostic LLM inference", section "The quantized load cache". */
+qd_status qd_load_weights(const qd_model_shape* shape, const qd_limits* limits,
+                          const qd_weights_f32* weights, const qd_buffers* buffers,
+                          qd_stream stream, qd_model** out);
+
+/* Identifiers of quantized tensors for qd_export_quantized. */
+typedef enum {
+  QD_T_EMBED = 0, QD_T_Q = 1, QD_T_K = 2, QD_T_V = 3, QD_T_O = 4,
+  QD_T_GATE = 5, QD_T_UP = 6, QD_T_DOWN = 7,
+} qd_tensor;
+
+/* Copies one quantized matrix back in checkpoint layout: codes [rows, cols] int8
+ * and scales [rows] fp32, to HOST memory.  Synchronizes the stream.  For
+ * bit-exact checks of the quantizer. */
+qd_status qd_export_quantized(qd_model* m, int32_t tensor, int32_t layer,
+                              int8_t* codes_host, float* scales_host, qd_stream stream);
+
+/* Prefill ("LLM inference overview", section "Workload characteristics"): runs
+ * n_seqs prompts, concatenated in ids_dev (device, int32, sum(lens) ids), with
+ * lengths lens_host[n_seqs] (host), into KV slots 0..n_seqs-1 starting at
+ * position 0.  Resets those slots' lengths to their prompt lengths.  Writes the
+ * greedy id of each prompt's last row to next_ids_dev[n_seqs] (device) and, if
+ * logits_dev is not NULL, that row's fp32 logits to logits_dev[n_seqs, V].
+ * Ids are validated on the host (ids_host may be given for that; if NULL the ids
+ * are not range-checked). */
+qd_status qd_prefill(qd_model* m, int32_t n_seqs, const int32_t* ids_dev,
+                     const int32_t* ids_host, const int32_t* lens_host,
+                     float* logits_dev, int32_t* next_ids_dev, qd_stream stream);
+
+/* One decode step for slots 0..B-1: feeds in_ids_dev[B] (device) at each slot's
+ * current length p, appends K/V at p, increments p, writes the greedy ids to
+ * next_ids_dev[B] and, if logits_dev is not NULL, fp32 logits [B, V].  Teacher
+ * forcing is the caller choosing in_ids.  No host synchronization; the slot
+ * lengths live on the device.  Returns QD_ERR_INVALID_ARGUMENTS if B is out of
+ * range; the caller must not step a slot past max_ctx. */
+qd_status qd_decode_step(qd_model* m, int32_t B, const int32_t* in_ids_dev,
+                         float* logits_dev, int32_t* next_ids_dev, qd_stream stream);
+
+/* One call, start to finish ("Model-agnostic LLM inference", section "Notes"):
+ * prefill of B prompts (host ids, concatenated; lens_host[B]) then
+ * max_new_tokens - 1 decode steps replayed from a captured HIP graph, greedy ids
+ * kept on the device between steps.  out_ids_host[B * max_new_tokens] receives
+ * the generated ids (row b = sequence b); n_out_host[b] the count up to and
+ * including the first eos_id (eos_id < 0 disables the stop).  Synchronizes the
+ * stream once at the end.  stats may be NULL. */
+qd_status qd_generate_greedy(qd_model* m, int32_t B, const int32_t* prompt_ids_host,
+                             const int32_t* lens_host, int32_t max_new_tokens, int32_t eos_id,
+                             int32_t* out_ids_host, int32_t* n_out_host, qd_stats* stats,
+                             qd_stream stream);
+
+/* Kernel classes of one decode step, for qd_profile_kernels. */
+typedef enum {
+  QD_PROF_EMBED = 0, QD_PROF_QKV = 1, QD_PROF_ATTN = 2, QD_PROF_O = 3,
+  QD_PROF_GATEUP = 4, QD_PROF_DOWN = 5, QD_PROF_LMHEAD = 6, QD_PROF_COUNT = 7,
+} qd_prof_kernel;
+
+/* Measurement aid (not part of the forward pass): launches each decode-step kernel
+ * class of layer 0 (and the LM head) `iters` times back to back for slots 0..B-1
+ * at their current positions, bracketed by HIP events on `stream`, and writes the
+ * mean microseconds per launch to us_out[QD_PROF_COUNT].  The residual and
+ * activation buffers are overwritten (run it after the outputs of interest are
+ * read); positions and generated ids are left unchanged.  Synchronizes the stream. */
+qd_status qd_profile_kernels(qd_model* m, int32_t B, int32_t iters, float* us_out,
+                             qd_stream stream);
+
+/* Frees host state and graphs.  Caller buffers remain the caller's. */
+void qd_free(qd_model* m);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QD_H */

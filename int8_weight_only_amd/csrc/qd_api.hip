@@ -1,0 +1,835 @@
+// Host side of the C ABI declared in include/qd.h: shape gates, buffer planning,
+// weight loading, and the prefill / decode / generate drivers.
+//
+// The call shape follows "Model-agnostic LLM inference": gates checked from the
+// shape alone before any GPU work (section "Supported models"), named errors that
+// list every problem (section "Errors"), one call from prompt ids to generated ids
+// with greedy arg-max (section "Notes"), context ceiling 65,536 (section "Long
+// context").  Prefill fills the KV cache and decode sweeps the weights once per
+// step for all sequences ("LLM inference overview", section "Workload
+// characteristics").
+#include "qd.h"
+#include "qd_common.h"
+
+#include <map>
+#include <string>
+#include <tuple>
+#include <vector>
+#include <cstring>
+#include <cstdio>
+
+using namespace qd;
+
+namespace {
+
+thread_local std::string g_err;
+
+qd_status fail(qd_status st, const std::string& msg) {
+  g_err = msg;
+  return st;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct LayerOff {
+  size_t qkv_q, qkv_s, o_q, o_s, gu_q, gu_s, dn_q, dn_s;
+  size_t in_g, post_g, qn_g, kn_g;
+};
+
+struct Plan {
+  // weights arena
+  size_t emb_q = 0, emb_s = 0, final_g = 0, rope = 0;
+  std::vector<LayerOff> L;
+  size_t weight_bytes = 0;
+  // workspace
+  size_t x = 0, h = 0, qkv = 0, attn = 0, act = 0, part_o = 0, part_ml = 0;
+  size_t ids = 0, row_slot = 0, row_pos = 0, last_rows = 0, lens = 0, slot_ident = 0;
+  size_t pos = 0, next_ids = 0, lm_keys = 0, att_cnt = 0, done = 0, step = 0, out_ids = 0;
+  size_t ws_bytes = 0;
+  size_t kv_bytes = 0;
+  size_t kv_layer_elems = 0;  // bf16 elements of K (or V) per layer
+  int mmax = 0;
+  int nsplit_cap = 0;
+  uint64_t packed = 0;
+};
+
+struct Dims {
+  int d, L, H, KV, D, I, V, G, HD, KVD, NQKV;
+};
+
+Dims dims_of(const qd_model_shape& s) {
+  Dims d;
+  d.d = s.hidden; d.L = s.n_layers; d.H = s.n_heads; d.KV = s.n_kv_heads; d.D = s.head_dim;
+  d.I = s.intermediate; d.V = s.vocab; d.G = s.n_kv_heads > 0 ? s.n_heads / s.n_kv_heads : 0;
+  d.HD = s.n_heads * s.head_dim; d.KVD = s.n_kv_heads * s.head_dim;
+  d.NQKV = d.HD + 2 * d.KVD;
+  return d;
+}
+
+std::string gate_problems(const qd_model_shape* s) {
+  std::string p;
+  auto add = [&](const std::string& m) { p += (p.empty() ? "" : "; ") + m; };
+  if (!s) return "shape is NULL";
+  const char* names[] = {"hidden_size", "num_hidden_layers", "num_attention_heads",
+                         "num_key_value_heads", "head_dim", "intermediate_size", "vocab_size"};
+  const int vals[] = {s->hidden, s->n_layers, s->n_heads, s->n_kv_heads, s->head_dim,
+                      s->intermediate, s->vocab};
+  bool sizes_ok = true;
+  for (int i = 0; i < 7; ++i)
+    if (vals[i] <= 0) {
+      add(std::string(names[i]) + "=" + std::to_string(vals[i]) + " must be > 0");
+      sizes_ok = false;
+    }
+  // gates of the pages ("Supported models")
+  if (s->n_kv_heads > 0 && s->n_heads % s->n_kv_heads != 0)
+    add("num_attention_heads (" + std::to_string(s->n_heads) + ") % num_key_value_heads (" +
+        std::to_string(s->n_kv_heads) + ") != 0");
+  if (s->hidden % 32 != 0) add("hidden_size " + std::to_string(s->hidden) + " not divisible by 32");
+  if (s->intermediate % 32 != 0)
+    add("intermediate_size " + std::to_string(s->intermediate) + " not divisible by 32");
+  if (((long long)s->n_heads * s->head_dim) % 32 != 0)
+    add("num_attention_heads * head_dim = " + std::to_string((long long)s->n_heads * s->head_dim) +
+        " not divisible by 32");
+  if (!s->tie_word_embeddings) add("tie_word_embeddings must be true");
+  if (s->attention_bias) add("attention_bias must be false");
+  // gates of this library's kernels
+  if (sizes_ok) {
+    const int D = s->head_dim;
+    if (D < 16 || D > 256 || (D & (D - 1)) != 0)
+      add("head_dim " + std::to_string(D) + " must be a power of two in [16, 256] (kernel limit)");
+    if (s->vocab < 2) add("vocab_size must be >= 2");
+    if (s->n_kv_heads > 0 && s->n_heads % s->n_kv_heads == 0 && s->n_heads / s->n_kv_heads > 8)
+      add("num_attention_heads / num_key_value_heads > 8 (kernel limit)");
+  }
+  if (!(s->rms_eps > 0.0f)) add("rms_norm_eps must be > 0");
+  if (!(s->rope_theta > 0.0f)) add("rope_theta must be > 0");
+  return p;
+}
+
+qd_status check_limits(const qd_limits* lim) {
+  if (!lim) return fail(QD_ERR_INVALID_ARGUMENTS, "limits is NULL");
+  if (lim->max_ctx > QD_MAX_CONTEXT)
+    return fail(QD_ERR_CONTEXT_CEILING, "max_ctx " + std::to_string(lim->max_ctx) +
+                                            " exceeds the context ceiling " +
+                                            std::to_string(QD_MAX_CONTEXT));
+  std::string p;
+  if (lim->max_batch < 1 || lim->max_batch > 64) p += "max_batch must be in [1, 64]; ";
+  if (lim->max_ctx < 1) p += "max_ctx must be >= 1; ";
+  if (lim->max_prefill_tokens < 1) p += "max_prefill_tokens must be >= 1; ";
+  if (!p.empty()) return fail(QD_ERR_INVALID_ARGUMENTS, p);
+  return QD_OK;
+}
+
+Plan make_plan(const qd_model_shape& s, const qd_limits& lim) {
+  const Dims d = dims_of(s);
+  Plan P;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  P.emb_q = take((size_t)d.V * d.d);
+  P.emb_s = take((size_t)d.V * 4);
+  P.final_g = take((size_t)d.d * 4);
+  P.L.resize(d.L);
+  for (int l = 0; l < d.L; ++l) {
+    LayerOff& o = P.L[l];
+    o.qkv_q = take((size_t)d.NQKV * d.d);
+    o.qkv_s = take((size_t)d.NQKV * 4);
+    o.o_q = take((size_t)d.d * d.HD);
+    o.o_s = take((size_t)d.d * 4);
+    o.gu_q = take((size_t)2 * d.I * d.d);
+    o.gu_s = take((size_t)2 * d.I * 4);
+    o.dn_q = take((size_t)d.d * d.I);
+    o.dn_s = take((size_t)d.d * 4);
+    o.in_g = take((size_t)d.d * 4);
+    o.post_g = take((size_t)d.d * 4);
+    o.qn_g = take((size_t)d.D * 4);
+    o.kn_g = take((size_t)d.D * 4);
+  }
+  P.rope = take((size_t)lim.max_ctx * (d.D / 2) * 8);
+  P.weight_bytes = off;
+
+  const int B = lim.max_batch;
+  const int M = std::max(lim.max_batch, lim.max_prefill_tokens);
+  P.mmax = M;
+  const int chunks = (lim.max_ctx + ATT_CHUNK - 1) / ATT_CHUNK;
+  P.nsplit_cap = std::min(chunks, ATT_MAX_SPLITS);
+  off = 0;
+  P.x = take((size_t)M * d.d * 2);
+  P.h = take((size_t)M * d.d * 2);
+  P.qkv = take((size_t)M * d.NQKV * 2);
+  P.attn = take((size_t)M * d.HD * 2);
+  P.act = take((size_t)M * d.I * 2);
+  P.part_o = take((size_t)B * d.H * P.nsplit_cap * d.D * 4);
+  P.part_ml = take((size_t)B * d.H * P.nsplit_cap * 2 * 4);
+  P.ids = take((size_t)M * 4);
+  P.row_slot = take((size_t)M * 4);
+  P.row_pos = take((size_t)M * 4);
+  P.last_rows = take((size_t)B * 4);
+  P.lens = take((size_t)B * 4);
+  P.slot_ident = take((size_t)B * 4);
+  P.pos = take((size_t)B * 4);
+  P.next_ids = take((size_t)B * 4);
+  P.lm_keys = take((size_t)B * LM_MAX_GRID * 8);
+  P.att_cnt = take((size_t)B * d.KV * 4);
+  P.done = take(64);
+  P.step = take(64);
+  P.out_ids = take((size_t)B * lim.max_ctx * 4);
+  P.ws_bytes = off;
+
+  P.kv_layer_elems = (size_t)B * d.KV * lim.max_ctx * d.D;
+  P.kv_bytes = (size_t)d.L * 2 * P.kv_layer_elems * 2;
+
+  // int8 codes + one fp32 scale per output row + fp32 gains, tied embedding once
+  uint64_t per_layer = 0;
+  const int64_t rc[7][2] = {{d.HD, d.d}, {d.KVD, d.d}, {d.KVD, d.d}, {d.d, d.HD},
+                            {d.I, d.d},  {d.I, d.d},   {d.d, d.I}};
+  for (auto& r : rc) per_layer += (uint64_t)(r[0] * r[1] + 4 * r[0]);
+  per_layer += 4ull * (2 * d.d + 2 * d.D);
+  P.packed = (uint64_t)d.L * per_layer + (uint64_t)d.V * d.d + 4ull * d.V + 4ull * d.d;
+  return P;
+}
+
+}  // namespace
+
+struct qd_model {
+  qd_model_shape shape;
+  qd_limits lim;
+  Dims d;
+  Plan P;
+  char* W = nullptr;   // weights arena
+  char* KVb = nullptr; // KV cache
+  char* WS = nullptr;  // workspace
+  int device = 0;
+  hipStream_t cap_stream = nullptr;
+  std::map<std::tuple<int, int, int>, hipGraphExec_t> graphs;  // (B, nsplit, split_len)
+  std::vector<int> host_pos;                                   // mirror of device positions
+  hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+
+  template <class T> T* w(size_t off) { return reinterpret_cast<T*>(W + off); }
+  template <class T> T* ws(size_t off) { return reinterpret_cast<T*>(WS + off); }
+  bf16_t* kcache(int l) { return reinterpret_cast<bf16_t*>(KVb) + (size_t)(2 * l) * P.kv_layer_elems; }
+  bf16_t* vcache(int l) { return reinterpret_cast<bf16_t*>(KVb) + (size_t)(2 * l + 1) * P.kv_layer_elems; }
+};
+
+#define HIPCHK(expr)                                                                  \
+  do {                                                                                \
+    hipError_t e_ = (expr);                                                           \
+    if (e_ != hipSuccess)                                                             \
+      return fail(QD_ERR_DEVICE, std::string(#expr) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+namespace {
+
+// attention split over positions 0..ctx-1: depends on the context only, so a sequence's
+// result does not depend on the batch it runs in
+void attn_split(int ctx, int cap, int* nsplit, int* split_len) {
+  const int chunks = std::max(1, (ctx + ATT_CHUNK - 1) / ATT_CHUNK);
+  const int want = std::max(1, std::min(chunks, std::min(cap, 64)));
+  const int per = (chunks + want - 1) / want;
+  *split_len = per * ATT_CHUNK;
+  *nsplit = (chunks + per - 1) / per;
+}
+
+// LM head + fused arg-max over batch rows [b0, b0+nb)
+qd_status enqueue_lm_head(qd_model* m, const bf16_t* x, const int* x_rows, int B, float* logits,
+                          int* next_ids, bool bump_pos, bool write_out, hipStream_t st) {
+  const Dims& d = m->d;
+  for (int b0 = 0; b0 < B; b0 += 8) {
+    GemvArgs a{};
+    a.x = x_rows ? x : x + (size_t)b0 * d.d;
+    a.ldx = d.d;
+    a.x_rows = x_rows ? x_rows + b0 : nullptr;
+    a.gain = m->w<float>(m->P.final_g);
+    a.eps = m->shape.rms_eps;
+    a.W = m->w<int8_t>(m->P.emb_q);
+    a.scale = m->w<float>(m->P.emb_s);
+    a.N = d.V;
+    a.K = d.d;
+    a.nb = std::min(8, B - b0);
+    a.logits = logits ? logits + (size_t)b0 * d.V : nullptr;
+    a.ldl = d.V;
+    a.part_keys = m->ws<unsigned long long>(m->P.lm_keys) + (size_t)b0 * LM_MAX_GRID;
+    a.done = m->ws<unsigned int>(m->P.done);
+    a.next_ids = next_ids + b0;
+    a.pos = bump_pos ? m->ws<int>(m->P.pos) + b0 : nullptr;
+    a.out_ids = write_out ? m->ws<int>(m->P.out_ids) : nullptr;
+    a.out_ld = m->lim.max_ctx;
+    a.step = m->ws<int>(m->P.step);
+    a.bump_step = (write_out && b0 + 8 >= B) ? 1 : 0;
+    a.batch0 = b0;
+    HIPCHK(launch_gemv(a, EPI_LOGITS, st));
+  }
+  return QD_OK;
+}
+
+// ---- the kernels of one decode step, for slots 0..B-1 (rows == slots) -------------------
+qd_status dec_qkv(qd_model* m, int l, int B, hipStream_t st) {
+  const Dims& d = m->d;
+  const LayerOff& o = m->P.L[l];
+  bf16_t* x = m->ws<bf16_t>(m->P.x);
+  bf16_t* qkv = m->ws<bf16_t>(m->P.qkv);
+  for (int b0 = 0; b0 < B; b0 += 8) {
+    GemvArgs a{};
+    a.x = x + (size_t)b0 * d.d; a.ldx = d.d;
+    a.gain = m->w<float>(o.in_g); a.eps = m->shape.rms_eps;
+    a.W = m->w<int8_t>(o.qkv_q); a.scale = m->w<float>(o.qkv_s);
+    a.N = d.NQKV; a.K = d.d; a.nb = std::min(8, B - b0);
+    a.out = qkv + (size_t)b0 * d.NQKV; a.ldo = d.NQKV;
+    HIPCHK(launch_gemv(a, EPI_STORE, st));
+  }
+  return QD_OK;
+}
+
+qd_status dec_attn(qd_model* m, int l, int B, int nsplit, int split_len, hipStream_t st) {
+  const Dims& d = m->d;
+  const LayerOff& o = m->P.L[l];
+  AttnDecArgs aa{};
+  aa.qkv = m->ws<bf16_t>(m->P.qkv); aa.ldqkv = d.NQKV;
+  aa.q_gain = m->w<float>(o.qn_g); aa.k_gain = m->w<float>(o.kn_g); aa.eps = m->shape.rms_eps;
+  aa.rope = m->w<float2>(m->P.rope);
+  aa.pos = m->ws<int>(m->P.pos);
+  aa.kcache = m->kcache(l); aa.vcache = m->vcache(l);
+  aa.H = d.H; aa.KV = d.KV; aa.D = d.D; aa.max_ctx = m->lim.max_ctx; aa.B = B;
+  aa.split_len = split_len; aa.nsplit = nsplit;
+  aa.part_o = m->ws<float>(m->P.part_o); aa.part_ml = m->ws<float>(m->P.part_ml);
+  aa.counters = m->ws<unsigned int>(m->P.att_cnt);
+  aa.out = m->ws<bf16_t>(m->P.attn); aa.ldo = d.HD;
+  HIPCHK(launch_attention_decode(aa, st));
+  return QD_OK;
+}
+
+qd_status dec_o(qd_model* m, int l, int B, hipStream_t st) {
+  const Dims& d = m->d;
+  const LayerOff& o = m->P.L[l];
+  bf16_t* attn = m->ws<bf16_t>(m->P.attn);
+  bf16_t* x = m->ws<bf16_t>(m->P.x);
+  for (int b0 = 0; b0 < B; b0 += 8) {
+    GemvArgs a{};
+    a.x = attn + (size_t)b0 * d.HD; a.ldx = d.HD;
+    a.W = m->w<int8_t>(o.o_q); a.scale = m->w<float>(o.o_s);
+    a.N = d.d; a.K = d.HD; a.nb = std::min(8, B - b0);
+    a.out = x + (size_t)b0 * d.d; a.ldo = d.d;
+    HIPCHK(launch_gemv(a, EPI_RESID, st));
+  }
+  return QD_OK;
+}
+
+qd_status dec_gateup(qd_model* m, int l, int B, hipStream_t st) {
+  const Dims& d = m->d;
+  const LayerOff& o = m->P.L[l];
+  bf16_t* x = m->ws<bf16_t>(m->P.x);
+  bf16_t* act = m->ws<bf16_t>(m->P.act);
+  for (int b0 = 0; b0 < B; b0 += 8) {
+    GemvArgs a{};
+    a.x = x + (size_t)b0 * d.d; a.ldx = d.d;
+    a.gain = m->w<float>(o.post_g); a.eps = m->shape.rms_eps;
+    a.W = m->w<int8_t>(o.gu_q); a.scale = m->w<float>(o.gu_s);
+    a.N = 2 * d.I; a.K = d.d; a.nb = std::min(8, B - b0);
+    a.out = act + (size_t)b0 * d.I; a.ldo = d.I;
+    HIPCHK(launch_gemv(a, EPI_SILU, st));
+  }
+  return QD_OK;
+}
+
+qd_status dec_down(qd_model* m, int l, int B, hipStream_t st) {
+  const Dims& d = m->d;
+  const LayerOff& o = m->P.L[l];
+  bf16_t* act = m->ws<bf16_t>(m->P.act);
+  bf16_t* x = m->ws<bf16_t>(m->P.x);
+  for (int b0 = 0; b0 < B; b0 += 8) {
+    GemvArgs a{};
+    a.x = act + (size_t)b0 * d.I; a.ldx = d.I;
+    a.W = m->w<int8_t>(o.dn_q); a.scale = m->w<float>(o.dn_s);
+    a.N = d.d; a.K = d.I; a.nb = std::min(8, B - b0);
+    a.out = x + (size_t)b0 * d.d; a.ldo = d.d;
+    HIPCHK(launch_gemv(a, EPI_RESID, st));
+  }
+  return QD_OK;
+}
+
+#define QDCHK(expr)                   \
+  do {                                \
+    qd_status s_ = (expr);            \
+    if (s_ != QD_OK) return s_;       \
+  } while (0)
+
+// one decode step; positions read from the device
+qd_status enqueue_decode(qd_model* m, int B, const int* in_ids, float* logits, int* next_ids,
+                         bool write_out, int nsplit, int split_len, hipStream_t st) {
+  const Dims& d = m->d;
+  HIPCHK(launch_embed(in_ids, B, m->w<int8_t>(m->P.emb_q), m->w<float>(m->P.emb_s), d.d, d.V,
+                      m->ws<bf16_t>(m->P.x), st));
+  for (int l = 0; l < d.L; ++l) {
+    QDCHK(dec_qkv(m, l, B, st));
+    QDCHK(dec_attn(m, l, B, nsplit, split_len, st));
+    QDCHK(dec_o(m, l, B, st));
+    QDCHK(dec_gateup(m, l, B, st));
+    QDCHK(dec_down(m, l, B, st));
+  }
+  return enqueue_lm_head(m, m->ws<bf16_t>(m->P.x), nullptr, B, logits, next_ids, true,
+                         write_out, st);
+}
+
+// prefill of n prompts whose ids are already in the workspace (P.ids), metadata on host
+qd_status enqueue_prefill(qd_model* m, int n, const int* ids_dev, const std::vector<int>& lens,
+                          float* logits, int* next_ids, bool write_out, hipStream_t st) {
+  const Dims& d = m->d;
+  const Plan& P = m->P;
+  int M = 0, maxlen = 0;
+  std::vector<int> rs, rp, last(n);
+  for (int b = 0; b < n; ++b) {
+    for (int t = 0; t < lens[b]; ++t) {
+      rs.push_back(b);
+      rp.push_back(t);
+    }
+    M += lens[b];
+    last[b] = M - 1;
+    maxlen = std::max(maxlen, lens[b]);
+  }
+  int* row_slot = m->ws<int>(P.row_slot);
+  int* row_pos = m->ws<int>(P.row_pos);
+  int* last_rows = m->ws<int>(P.last_rows);
+  int* dlens = m->ws<int>(P.lens);
+  HIPCHK(hipMemcpyAsync(row_slot, rs.data(), M * 4, hipMemcpyHostToDevice, st));
+  HIPCHK(hipMemcpyAsync(row_pos, rp.data(), M * 4, hipMemcpyHostToDevice, st));
+  HIPCHK(hipMemcpyAsync(last_rows, last.data(), n * 4, hipMemcpyHostToDevice, st));
+  HIPCHK(hipMemcpyAsync(dlens, lens.data(), n * 4, hipMemcpyHostToDevice, st));
+
+  bf16_t* x = m->ws<bf16_t>(P.x);
+  bf16_t* h = m->ws<bf16_t>(P.h);
+  bf16_t* qkv = m->ws<bf16_t>(P.qkv);
+  bf16_t* attn = m->ws<bf16_t>(P.attn);
+  bf16_t* act = m->ws<bf16_t>(P.act);
+  HIPCHK(launch_embed(ids_dev, M, m->w<int8_t>(P.emb_q), m->w<float>(P.emb_s), d.d, d.V, x, st));
+  const int split_len = ((maxlen + ATT_CHUNK - 1) / ATT_CHUNK) * ATT_CHUNK;
+  for (int l = 0; l < d.L; ++l) {
+    const LayerOff& o = P.L[l];
+    HIPCHK(launch_rmsnorm(x, M, d.d, m->w<float>(o.in_g), m->shape.rms_eps, h, st));
+    GemmArgs g{};
+    g.A = h; g.lda = d.d; g.W = m->w<int8_t>(o.qkv_q); g.scale = m->w<float>(o.qkv_s);
+    g.M = M; g.N = d.NQKV; g.K = d.d; g.epi = EPI_STORE; g.out = qkv; g.ldo = d.NQKV;
+    HIPCHK(launch_gemm(g, st));
+    RopeArgs ra{};
+    ra.qkv = qkv; ra.ldqkv = d.NQKV;
+    ra.q_gain = m->w<float>(o.qn_g); ra.k_gain = m->w<float>(o.kn_g); ra.eps = m->shape.rms_eps;
+    ra.rope = m->w<float2>(P.rope);
+    ra.row_slot = row_slot; ra.row_pos = row_pos;
+    ra.kcache = m->kcache(l); ra.vcache = m->vcache(l);
+    ra.H = d.H; ra.KV = d.KV; ra.D = d.D; ra.max_ctx = m->lim.max_ctx; ra.M = M;
+    HIPCHK(launch_qk_rope(ra, st));
+    AttnArgs aa{};
+    aa.q = qkv; aa.ldq = d.NQKV;
+    aa.kcache = m->kcache(l); aa.vcache = m->vcache(l);
+    aa.row_slot = row_slot; aa.row_pos = row_pos;
+    aa.H = d.H; aa.KV = d.KV; aa.D = d.D; aa.max_ctx = m->lim.max_ctx; aa.M = M;
+    aa.split_len = split_len; aa.nsplit = 1;
+    aa.out = attn; aa.ldo = d.HD;
+    HIPCHK(launch_attention(aa, st));
+    g = GemmArgs{};
+    g.A = attn; g.lda = d.HD; g.W = m->w<int8_t>(o.o_q); g.scale = m->w<float>(o.o_s);
+    g.M = M; g.N = d.d; g.K = d.HD; g.epi = EPI_RESID; g.out = x; g.ldo = d.d;
+    HIPCHK(launch_gemm(g, st));
+    HIPCHK(launch_rmsnorm(x, M, d.d, m->w<float>(o.post_g), m->shape.rms_eps, h, st));
+    g = GemmArgs{};
+    g.A = h; g.lda = d.d; g.W = m->w<int8_t>(o.gu_q); g.scale = m->w<float>(o.gu_s);
+    g.M = M; g.N = 2 * d.I; g.K = d.d; g.epi = EPI_SILU; g.out = act; g.ldo = d.I;
+    HIPCHK(launch_gemm(g, st));
+    g = GemmArgs{};
+    g.A = act; g.lda = d.I; g.W = m->w<int8_t>(o.dn_q); g.scale = m->w<float>(o.dn_s);
+    g.M = M; g.N = d.d; g.K = d.I; g.epi = EPI_RESID; g.out = x; g.ldo = d.d;
+    HIPCHK(launch_gemm(g, st));
+  }
+  qd_status s = enqueue_lm_head(m, x, last_rows, n, logits, next_ids, false, write_out, st);
+  if (s != QD_OK) return s;
+  HIPCHK(launch_set_positions(m->ws<int>(P.pos), dlens, n, st));
+  return QD_OK;
+}
+
+std::string check_ids(const int32_t* ids, long n, int V) {
+  for (long i = 0; i < n; ++i)
+    if (ids[i] < 0 || ids[i] >= V)
+      return "token id " + std::to_string(ids[i]) + " at index " + std::to_string(i) +
+             " is outside [0, " + std::to_string(V) + ")";
+  return "";
+}
+
+}  // namespace
+
+// ============================================================================================
+extern "C" {
+
+const char* qd_last_error(void) { return g_err.c_str(); }
+
+qd_status qd_check_shape(const qd_model_shape* shape) {
+  g_err.clear();
+  const std::string p = gate_problems(shape);
+  if (!p.empty()) return fail(QD_ERR_UNSUPPORTED_ARCH, "unsupported architecture: " + p);
+  return QD_OK;
+}
+
+qd_status qd_query_sizes(const qd_model_shape* shape, const qd_limits* limits, qd_sizes* out) {
+  qd_status st = qd_check_shape(shape);
+  if (st != QD_OK) return st;
+  if ((st = check_limits(limits)) != QD_OK) return st;
+  if (!out) return fail(QD_ERR_INVALID_ARGUMENTS, "out is NULL");
+  const Plan P = make_plan(*shape, *limits);
+  out->weight_bytes = P.weight_bytes;
+  out->kv_bytes = P.kv_bytes;
+  out->workspace_bytes = P.ws_bytes;
+  out->packed_model_bytes = P.packed;
+  return QD_OK;
+}
+
+qd_status qd_load_weights(const qd_model_shape* shape, const qd_limits* limits,
+                          const qd_weights_f32* wts, const qd_buffers* bufs, qd_stream stream,
+                          qd_model** out) {
+  qd_status st = qd_check_shape(shape);
+  if (st != QD_OK) return st;
+  if ((st = check_limits(limits)) != QD_OK) return st;
+  if (!out) return fail(QD_ERR_INVALID_ARGUMENTS, "out is NULL");
+  *out = nullptr;
+  // every tensor must be present ("checkpoint_not_found" names each missing one)
+  std::string missing;
+  auto need = [&](const void* p, const std::string& n) {
+    if (!p) missing += (missing.empty() ? "" : ", ") + n;
+  };
+  if (!wts) return fail(QD_ERR_CHECKPOINT_NOT_FOUND, "weights is NULL");
+  need(wts->embed, "embed_tokens");
+  need(wts->final_norm, "norm");
+  if (!wts->layers) {
+    missing += (missing.empty() ? "" : ", ") + std::string("layers");
+  } else {
+    for (int l = 0; l < shape->n_layers; ++l) {
+      const qd_layer_f32& L = wts->layers[l];
+      const std::string pre = "layers." + std::to_string(l) + ".";
+      need(L.q, pre + "q_proj"); need(L.k, pre + "k_proj"); need(L.v, pre + "v_proj");
+      need(L.o, pre + "o_proj"); need(L.gate, pre + "gate_proj"); need(L.up, pre + "up_proj");
+      need(L.down, pre + "down_proj"); need(L.in_norm, pre + "input_layernorm");
+      need(L.post_norm, pre + "post_attention_layernorm"); need(L.q_norm, pre + "q_norm");
+      need(L.k_norm, pre + "k_norm");
+    }
+  }
+  if (!missing.empty()) return fail(QD_ERR_CHECKPOINT_NOT_FOUND, "missing tensors: " + missing);
+  const Plan P = make_plan(*shape, *limits);
+  if (!bufs || !bufs->weights || !bufs->kv || !bufs->workspace)
+    return fail(QD_ERR_INVALID_ARGUMENTS, "a device buffer pointer is NULL");
+  std::string small;
+  if (bufs->weight_bytes < P.weight_bytes)
+    small += "weights " + std::to_string(bufs->weight_bytes) + " < " + std::to_string(P.weight_bytes) + "; ";
+  if (bufs->kv_bytes < P.kv_bytes)
+    small += "kv " + std::to_string(bufs->kv_bytes) + " < " + std::to_string(P.kv_bytes) + "; ";
+  if (bufs->workspace_bytes < P.ws_bytes)
+    small += "workspace " + std::to_string(bufs->workspace_bytes) + " < " + std::to_string(P.ws_bytes) + "; ";
+  if (!small.empty()) return fail(QD_ERR_BUFFER_TOO_SMALL, "buffers too small: " + small);
+  if ((((uintptr_t)bufs->weights) | ((uintptr_t)bufs->kv) | ((uintptr_t)bufs->workspace)) & 255)
+    return fail(QD_ERR_INVALID_ARGUMENTS, "device buffers must be 256-byte aligned");
+
+  int dev = 0;
+  HIPCHK(hipGetDevice(&dev));
+  hipDeviceProp_t prop;
+  HIPCHK(hipGetDeviceProperties(&prop, dev));
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(QD_ERR_DEVICE, std::string("device is ") + prop.gcnArchName + ", need gfx950");
+
+  qd_model* m = new qd_model();
+  m->shape = *shape;
+  m->lim = *limits;
+  m->d = dims_of(*shape);
+  m->P = P;
+  m->W = (char*)bufs->weights;
+  m->KVb = (char*)bufs->kv;
+  m->WS = (char*)bufs->workspace;
+  m->device = dev;
+  m->host_pos.assign(limits->max_batch, 0);
+  hipStream_t s = (hipStream_t)stream;
+  auto cleanup_fail = [&](qd_status code) {
+    delete m;
+    return code;
+  };
+#define LCHK(expr)                                                                        \
+  do {                                                                                    \
+    hipError_t e_ = (expr);                                                               \
+    if (e_ != hipSuccess)                                                                 \
+      return cleanup_fail(fail(QD_ERR_DEVICE, std::string(#expr) + ": " + hipGetErrorString(e_))); \
+  } while (0)
+  const Dims& d = m->d;
+  LCHK(launch_quantize_rows(wts->embed, d.V, d.d, m->w<int8_t>(P.emb_q), m->w<float>(P.emb_s), 0, -1, s));
+  LCHK(hipMemcpyAsync(m->w<float>(P.final_g), wts->final_norm, d.d * 4, hipMemcpyDeviceToDevice, s));
+  for (int l = 0; l < d.L; ++l) {
+    const qd_layer_f32& L = wts->layers[l];
+    const LayerOff& o = P.L[l];
+    int8_t* qkv = m->w<int8_t>(o.qkv_q);
+    float* qkvs = m->w<float>(o.qkv_s);
+    LCHK(launch_quantize_rows(L.q, d.HD, d.d, qkv, qkvs, 0, -1, s));
+    LCHK(launch_quantize_rows(L.k, d.KVD, d.d, qkv, qkvs, d.HD, -1, s));
+    LCHK(launch_quantize_rows(L.v, d.KVD, d.d, qkv, qkvs, d.HD + d.KVD, -1, s));
+    LCHK(launch_quantize_rows(L.o, d.d, d.HD, m->w<int8_t>(o.o_q), m->w<float>(o.o_s), 0, -1, s));
+    LCHK(launch_quantize_rows(L.gate, d.I, d.d, m->w<int8_t>(o.gu_q), m->w<float>(o.gu_s), 0, 0, s));
+    LCHK(launch_quantize_rows(L.up, d.I, d.d, m->w<int8_t>(o.gu_q), m->w<float>(o.gu_s), 0, 1, s));
+    LCHK(launch_quantize_rows(L.down, d.d, d.I, m->w<int8_t>(o.dn_q), m->w<float>(o.dn_s), 0, -1, s));
+    LCHK(hipMemcpyAsync(m->w<float>(o.in_g), L.in_norm, d.d * 4, hipMemcpyDeviceToDevice, s));
+    LCHK(hipMemcpyAsync(m->w<float>(o.post_g), L.post_norm, d.d * 4, hipMemcpyDeviceToDevice, s));
+    LCHK(hipMemcpyAsync(m->w<float>(o.qn_g), L.q_norm, d.D * 4, hipMemcpyDeviceToDevice, s));
+    LCHK(hipMemcpyAsync(m->w<float>(o.kn_g), L.k_norm, d.D * 4, hipMemcpyDeviceToDevice, s));
+  }
+  LCHK(launch_rope_table(m->w<float2>(P.rope), limits->max_ctx, d.D, shape->rope_theta, s));
+  LCHK(launch_fill_i32(m->ws<int>(P.pos), limits->max_batch, 0, s));
+  LCHK(launch_iota(m->ws<int>(P.slot_ident), limits->max_batch, s));
+  LCHK(launch_fill_i32(m->ws<int>(P.att_cnt), limits->max_batch * d.KV, 0, s));
+  LCHK(launch_fill_i32(m->ws<int>(P.done), 16, 0, s));
+  LCHK(launch_fill_i32(m->ws<int>(P.step), 16, 0, s));
+  LCHK(hipStreamCreateWithFlags(&m->cap_stream, hipStreamNonBlocking));
+  for (int i = 0; i < 3; ++i) LCHK(hipEventCreate(&m->ev[i]));
+#undef LCHK
+  *out = m;
+  return QD_OK;
+}
+
+qd_status qd_export_quantized(qd_model* m, int32_t tensor, int32_t layer, int8_t* codes_host,
+                              float* scales_host, qd_stream stream) {
+  g_err.clear();
+  if (!m || !codes_host || !scales_host) return fail(QD_ERR_INVALID_ARGUMENTS, "NULL argument");
+  const Dims& d = m->d;
+  if (tensor != QD_T_EMBED && (layer < 0 || layer >= d.L))
+    return fail(QD_ERR_INVALID_ARGUMENTS, "layer out of range");
+  hipStream_t s = (hipStream_t)stream;
+  const int8_t* q = nullptr;
+  const float* sc = nullptr;
+  int rows = 0, cols = 0, row0 = 0, half = -1;
+  const LayerOff* o = tensor == QD_T_EMBED ? nullptr : &m->P.L[layer];
+  switch (tensor) {
+    case QD_T_EMBED: q = m->w<int8_t>(m->P.emb_q); sc = m->w<float>(m->P.emb_s); rows = d.V; cols = d.d; break;
+    case QD_T_Q: q = m->w<int8_t>(o->qkv_q); sc = m->w<float>(o->qkv_s); rows = d.HD; cols = d.d; break;
+    case QD_T_K: q = m->w<int8_t>(o->qkv_q); sc = m->w<float>(o->qkv_s); rows = d.KVD; cols = d.d; row0 = d.HD; break;
+    case QD_T_V: q = m->w<int8_t>(o->qkv_q); sc = m->w<float>(o->qkv_s); rows = d.KVD; cols = d.d; row0 = d.HD + d.KVD; break;
+    case QD_T_O: q = m->w<int8_t>(o->o_q); sc = m->w<float>(o->o_s); rows = d.d; cols = d.HD; break;
+    case QD_T_GATE: q = m->w<int8_t>(o->gu_q); sc = m->w<float>(o->gu_s); rows = d.I; cols = d.d; half = 0; break;
+    case QD_T_UP: q = m->w<int8_t>(o->gu_q); sc = m->w<float>(o->gu_s); rows = d.I; cols = d.d; half = 1; break;
+    case QD_T_DOWN: q = m->w<int8_t>(o->dn_q); sc = m->w<float>(o->dn_s); rows = d.d; cols = d.I; break;
+    default: return fail(QD_ERR_INVALID_ARGUMENTS, "unknown tensor id");
+  }
+  if (half < 0) {
+    HIPCHK(hipMemcpyAsync(codes_host, q + (size_t)row0 * cols, (size_t)rows * cols, hipMemcpyDeviceToHost, s));
+    HIPCHK(hipMemcpyAsync(scales_host, sc + row0, (size_t)rows * 4, hipMemcpyDeviceToHost, s));
+    HIPCHK(hipStreamSynchronize(s));
+  } else {
+    std::vector<int8_t> tq((size_t)2 * rows * cols);
+    std::vector<float> ts((size_t)2 * rows);
+    HIPCHK(hipMemcpyAsync(tq.data(), q, tq.size(), hipMemcpyDeviceToHost, s));
+    HIPCHK(hipMemcpyAsync(ts.data(), sc, ts.size() * 4, hipMemcpyDeviceToHost, s));
+    HIPCHK(hipStreamSynchronize(s));
+    for (int j = 0; j < rows; ++j) {
+      const int r = gu_row(j, half);
+      std::memcpy(codes_host + (size_t)j * cols, tq.data() + (size_t)r * cols, cols);
+      scales_host[j] = ts[r];
+    }
+  }
+  return QD_OK;
+}
+
+qd_status qd_prefill(qd_model* m, int32_t n_seqs, const int32_t* ids_dev, const int32_t* ids_host,
+                     const int32_t* lens_host, float* logits_dev, int32_t* next_ids_dev,
+                     qd_stream stream) {
+  g_err.clear();
+  if (!m) return fail(QD_ERR_INVALID_ARGUMENTS, "model is NULL");
+  if (n_seqs < 1 || n_seqs > m->lim.max_batch)
+    return fail(QD_ERR_INVALID_ARGUMENTS, "n_seqs must be in [1, max_batch]");
+  if (!ids_dev || !lens_host || !next_ids_dev)
+    return fail(QD_ERR_INVALID_ARGUMENTS, "ids_dev, lens_host and next_ids_dev must be set");
+  std::vector<int> lens(lens_host, lens_host + n_seqs);
+  long total = 0;
+  for (int b = 0; b < n_seqs; ++b) {
+    if (lens[b] < 1) return fail(QD_ERR_INVALID_ARGUMENTS, "empty prompt for sequence " + std::to_string(b));
+    if (lens[b] > m->lim.max_ctx)
+      return fail(QD_ERR_INVALID_ARGUMENTS, "prompt of sequence " + std::to_string(b) + " exceeds max_ctx");
+    total += lens[b];
+  }
+  if (total > m->lim.max_prefill_tokens)
+    return fail(QD_ERR_INVALID_ARGUMENTS, "prompt tokens exceed max_prefill_tokens");
+  if (ids_host) {
+    const std::string e = check_ids(ids_host, total, m->d.V);
+    if (!e.empty()) return fail(QD_ERR_INVALID_ARGUMENTS, e);
+  }
+  qd_status s = enqueue_prefill(m, n_seqs, ids_dev, lens, logits_dev, next_ids_dev, false,
+                                (hipStream_t)stream);
+  if (s == QD_OK)
+    for (int b = 0; b < n_seqs; ++b) m->host_pos[b] = lens[b];
+  return s;
+}
+
+qd_status qd_decode_step(qd_model* m, int32_t B, const int32_t* in_ids_dev, float* logits_dev,
+                         int32_t* next_ids_dev, qd_stream stream) {
+  g_err.clear();
+  if (!m) return fail(QD_ERR_INVALID_ARGUMENTS, "model is NULL");
+  if (B < 1 || B > m->lim.max_batch) return fail(QD_ERR_INVALID_ARGUMENTS, "B must be in [1, max_batch]");
+  if (!in_ids_dev || !next_ids_dev) return fail(QD_ERR_INVALID_ARGUMENTS, "ids pointers must be set");
+  int ctx = 0;
+  for (int b = 0; b < B; ++b) {
+    if (m->host_pos[b] >= m->lim.max_ctx)
+      return fail(QD_ERR_INVALID_ARGUMENTS, "slot " + std::to_string(b) + " is full (max_ctx)");
+    ctx = std::max(ctx, m->host_pos[b] + 1);
+  }
+  int nsplit, split_len;
+  attn_split(ctx, m->P.nsplit_cap, &nsplit, &split_len);
+  qd_status s = enqueue_decode(m, B, in_ids_dev, logits_dev, next_ids_dev, false, nsplit,
+                               split_len, (hipStream_t)stream);
+  if (s == QD_OK)
+    for (int b = 0; b < B; ++b) m->host_pos[b] += 1;
+  return s;
+}
+
+qd_status qd_generate_greedy(qd_model* m, int32_t B, const int32_t* prompt_ids_host,
+                             const int32_t* lens_host, int32_t max_new_tokens, int32_t eos_id,
+                             int32_t* out_ids_host, int32_t* n_out_host, qd_stats* stats,
+                             qd_stream stream) {
+  g_err.clear();
+  if (!m) return fail(QD_ERR_INVALID_ARGUMENTS, "model is NULL");
+  std::string p;
+  if (B < 1 || B > m->lim.max_batch) p += "B must be in [1, max_batch]; ";
+  if (max_new_tokens < 1) p += "max_new_tokens must be >= 1; ";
+  if (!prompt_ids_host || !lens_host || !out_ids_host || !n_out_host) p += "NULL pointer argument; ";
+  if (!p.empty()) return fail(QD_ERR_INVALID_ARGUMENTS, p);
+  std::vector<int> lens(lens_host, lens_host + B);
+  long total = 0;
+  int need = 0;
+  for (int b = 0; b < B; ++b) {
+    if (lens[b] < 1) return fail(QD_ERR_INVALID_ARGUMENTS, "empty prompt for sequence " + std::to_string(b));
+    total += lens[b];
+    need = std::max(need, lens[b] + max_new_tokens - 1);
+  }
+  if (need > QD_MAX_CONTEXT)
+    return fail(QD_ERR_CONTEXT_CEILING, "prompt + max_new_tokens needs " + std::to_string(need) +
+                                            " positions, above the ceiling " + std::to_string(QD_MAX_CONTEXT));
+  if (need > m->lim.max_ctx || max_new_tokens > m->lim.max_ctx)
+    return fail(QD_ERR_INVALID_ARGUMENTS, "prompt + max_new_tokens needs " + std::to_string(need) +
+                                              " positions, model loaded with max_ctx " + std::to_string(m->lim.max_ctx));
+  if (total > m->lim.max_prefill_tokens)
+    return fail(QD_ERR_INVALID_ARGUMENTS, "prompt tokens exceed max_prefill_tokens");
+  const std::string e = check_ids(prompt_ids_host, total, m->d.V);
+  if (!e.empty()) return fail(QD_ERR_INVALID_ARGUMENTS, e);
+
+  hipStream_t st = (hipStream_t)stream;
+  const Plan& P = m->P;
+  int* ids_dev = m->ws<int>(P.ids);
+  int* next_ids = m->ws<int>(P.next_ids);
+  HIPCHK(hipMemcpyAsync(ids_dev, prompt_ids_host, total * 4, hipMemcpyHostToDevice, st));
+  HIPCHK(launch_fill_i32(m->ws<int>(P.step), 1, 0, st));
+  HIPCHK(hipEventRecord(m->ev[0], st));
+  qd_status s = enqueue_prefill(m, B, ids_dev, lens, nullptr, next_ids, true, st);
+  if (s != QD_OK) return s;
+  HIPCHK(hipEventRecord(m->ev[1], st));
+  const int steps = max_new_tokens - 1;
+  if (steps > 0) {
+    int nsplit, split_len;
+    // round the context up so one captured graph serves many calls
+    const int ctx_cap = std::min(m->lim.max_ctx, ((need + 255) / 256) * 256);
+    attn_split(ctx_cap, P.nsplit_cap, &nsplit, &split_len);
+    auto key = std::make_tuple(B, nsplit, split_len);
+    auto it = m->graphs.find(key);
+    hipGraphExec_t exec = nullptr;
+    if (it == m->graphs.end()) {
+      hipGraph_t graph;
+      HIPCHK(hipStreamBeginCapture(m->cap_stream, hipStreamCaptureModeThreadLocal));
+      qd_status cs = enqueue_decode(m, B, next_ids, nullptr, next_ids, true, nsplit, split_len,
+                                    m->cap_stream);
+      hipError_t ee = hipStreamEndCapture(m->cap_stream, &graph);
+      if (cs != QD_OK) return cs;
+      if (ee != hipSuccess) return fail(QD_ERR_DEVICE, std::string("hipStreamEndCapture: ") + hipGetErrorString(ee));
+      HIPCHK(hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0));
+      HIPCHK(hipGraphDestroy(graph));
+      m->graphs[key] = exec;
+    } else {
+      exec = it->second;
+    }
+    for (int i = 0; i < steps; ++i) HIPCHK(hipGraphLaunch(exec, st));
+  }
+  HIPCHK(hipEventRecord(m->ev[2], st));
+  HIPCHK(hipMemcpy2DAsync(out_ids_host, (size_t)max_new_tokens * 4, m->ws<int>(P.out_ids),
+                          (size_t)m->lim.max_ctx * 4, (size_t)max_new_tokens * 4, B,
+                          hipMemcpyDeviceToHost, st));
+  HIPCHK(hipStreamSynchronize(st));
+  for (int b = 0; b < B; ++b) {
+    m->host_pos[b] = lens[b] + max_new_tokens - 1;
+    int n = max_new_tokens;
+    if (eos_id >= 0)
+      for (int k = 0; k < max_new_tokens; ++k)
+        if (out_ids_host[(size_t)b * max_new_tokens + k] == eos_id) {
+          n = k + 1;
+          break;
+        }
+    n_out_host[b] = n;
+  }
+  if (stats) {
+    float t0 = 0, t1 = 0;
+    HIPCHK(hipEventElapsedTime(&t0, m->ev[0], m->ev[1]));
+    HIPCHK(hipEventElapsedTime(&t1, m->ev[1], m->ev[2]));
+    stats->prefill_us = t0 * 1e3;
+    stats->decode_us = t1 * 1e3;
+    stats->steps = steps;
+    stats->n_prompt_tokens = (int)total;
+  }
+  return QD_OK;
+}
+
+qd_status qd_profile_kernels(qd_model* m, int32_t B, int32_t iters, float* us_out,
+                             qd_stream stream) {
+  g_err.clear();
+  if (!m || !us_out) return fail(QD_ERR_INVALID_ARGUMENTS, "NULL argument");
+  if (B < 1 || B > m->lim.max_batch) return fail(QD_ERR_INVALID_ARGUMENTS, "B must be in [1, max_batch]");
+  if (iters < 1) return fail(QD_ERR_INVALID_ARGUMENTS, "iters must be >= 1");
+  int ctx = 0;
+  for (int b = 0; b < B; ++b) {
+    if (m->host_pos[b] >= m->lim.max_ctx)
+      return fail(QD_ERR_INVALID_ARGUMENTS, "slot " + std::to_string(b) + " is full (max_ctx)");
+    ctx = std::max(ctx, m->host_pos[b] + 1);
+  }
+  int nsplit, split_len;
+  attn_split(ctx, m->P.nsplit_cap, &nsplit, &split_len);
+  hipStream_t st = (hipStream_t)stream;
+  int* scratch_ids = m->ws<int>(m->P.ids);   // prompt-id area doubles as the profiling id list
+  HIPCHK(launch_fill_i32(scratch_ids, B, 0, st));
+  int* scratch_next = m->ws<int>(m->P.last_rows);  // [max_batch], used by prefill only
+  for (int k = 0; k < QD_PROF_COUNT; ++k) {
+    // one warm launch, then the timed ones
+    for (int rep = 0; rep < 2; ++rep) {
+      const int n = rep == 0 ? 1 : iters;
+      if (rep == 1) HIPCHK(hipEventRecord(m->ev[0], st));
+      for (int i = 0; i < n; ++i) {
+        switch (k) {
+          case QD_PROF_EMBED:
+            HIPCHK(launch_embed(scratch_ids, B, m->w<int8_t>(m->P.emb_q), m->w<float>(m->P.emb_s),
+                                m->d.d, m->d.V, m->ws<bf16_t>(m->P.x), st));
+            break;
+          case QD_PROF_QKV: QDCHK(dec_qkv(m, 0, B, st)); break;
+          case QD_PROF_ATTN: QDCHK(dec_attn(m, 0, B, nsplit, split_len, st)); break;
+          case QD_PROF_O: QDCHK(dec_o(m, 0, B, st)); break;
+          case QD_PROF_GATEUP: QDCHK(dec_gateup(m, 0, B, st)); break;
+          case QD_PROF_DOWN: QDCHK(dec_down(m, 0, B, st)); break;
+          default:
+            QDCHK(enqueue_lm_head(m, m->ws<bf16_t>(m->P.x), nullptr, B, nullptr, scratch_next,
+                                  false, false, st));
+        }
+      }
+      if (rep == 1) HIPCHK(hipEventRecord(m->ev[1], st));
+    }
+    HIPCHK(hipEventSynchronize(m->ev[1]));
+    float ms = 0;
+    HIPCHK(hipEventElapsedTime(&ms, m->ev[0], m->ev[1]));
+    us_out[k] = ms * 1e3f / iters;
+  }
+  return QD_OK;
+}
+
+void qd_free(qd_model* m) {
+  if (!m) return;
+  for (auto& kv : m->graphs) (void)hipGraphExecDestroy(kv.second);
+  for (int i = 0; i < 3; ++i)
+    if (m->ev[i]) (void)hipEventDestroy(m->ev[i]);
+  if (m->cap_stream) (void)hipStreamDestroy(m->cap_stream);
+  delete m;
+}
+
+}  // extern "C"

@@ -1,0 +1,1274 @@
+// HIP kernels for the int8 weight-only Qwen3-family decoder step, written for
+// gfx950 (CDNA4, wave64).  The decoder follows "Model-agnostic LLM inference",
+// section "Supported models"; the int8 weights with one scale per row follow the
+// section "The quantized load cache" of the same page.
+//
+// Rounding: every tensor the model produces is rounded to bf16 (round to nearest
+// even) at the same points as the CPU oracle: embedding rows, RMSNorm outputs,
+// projection outputs, QK-norm and RoPE outputs, attention outputs, residual sums,
+// SiLU(gate)*up.  Logits stay fp32.  Accumulation is fp32.
+#include "qd_common.h"
+#include <math.h>
+
+namespace qd {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+__device__ __forceinline__ float rbf(float f) { return bf2f(f2bf(f)); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// 256-thread block reductions through LDS
+__device__ __forceinline__ float block_sum256(float v, float* red4) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red4[wid] = v;
+  __syncthreads();
+  return red4[0] + red4[1] + red4[2] + red4[3];
+}
+__device__ __forceinline__ float block_max256(float v, float* red4) {
+  v = wave_max(v);
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red4[wid] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(red4[0], red4[1]), fmaxf(red4[2], red4[3]));
+}
+
+// arg-max key: larger value wins, equal values go to the lower index; -0.0 == +0.0
+__device__ __forceinline__ unsigned long long argmax_key(float v, int idx) {
+  if (v == 0.0f) v = 0.0f;
+  uint32_t u = __float_as_uint(v);
+  uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((unsigned long long)ord << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)idx);
+}
+__device__ __forceinline__ int key_index(unsigned long long k) {
+  return (int)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
+}
+
+// ------------------------------------------------------------------------------------------
+// load time: per-row symmetric int8 quantization (bit-exact contract)
+//   s = absmax / 127 (IEEE fp32 division), q = clamp(rint(w / s), -127, 127); zero row -> 0
+__global__ __launch_bounds__(256) void k_quantize_rows(const float* __restrict__ w, int cols,
+                                                       int8_t* __restrict__ q,
+                                                       float* __restrict__ s, int dst_row0,
+                                                       int gu_half) {
+  __shared__ float red[4];
+  const int r = blockIdx.x;
+  const float* wr = w + (size_t)r * cols;
+  float amax = 0.0f;
+  for (int c = threadIdx.x; c < cols; c += 256) amax = fmaxf(amax, fabsf(wr[c]));
+  amax = block_max256(amax, red);
+  const float sc = amax / 127.0f;
+  const int dr = gu_half >= 0 ? dst_row0 + gu_row(r, gu_half) : dst_row0 + r;
+  int8_t* qr = q + (size_t)dr * cols;
+  if (threadIdx.x == 0) s[dr] = sc;
+  for (int c = threadIdx.x; c < cols; c += 256) {
+    int v = 0;
+    if (sc != 0.0f) {
+      float t = rintf(wr[c] / sc);
+      t = fminf(fmaxf(t, -127.0f), 127.0f);
+      v = (int)t;
+    }
+    qr[c] = (int8_t)v;
+  }
+}
+
+// RoPE table: (cos, sin) of p * theta^(-2i/D) computed in float64, stored fp32
+__global__ void k_rope_table(float2* tab, int max_ctx, int D, double theta) {
+  const int half = D / 2;
+  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (long)max_ctx * half) return;
+  const int p = (int)(idx / half), i = (int)(idx % half);
+  const double inv = pow(theta, -2.0 * (double)i / (double)D);
+  const double ang = (double)p * inv;
+  tab[idx] = make_float2((float)cos(ang), (float)sin(ang));
+}
+
+__global__ void k_fill_i32(int* p, int n, int v) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+__global__ void k_fill_u64(unsigned long long* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0ull;
+}
+__global__ void k_iota(int* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = i;
+}
+__global__ void k_set_positions(int* pos, const int* lens, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) pos[i] = lens[i];
+}
+
+// ------------------------------------------------------------------------------------------
+// embedding gather: x = bf16(code * row scale), product in fp32
+// (ids outside [0, V) are clamped into range so a bad id can never read out of bounds;
+// the host validates ids wherever it sees them)
+__global__ __launch_bounds__(256) void k_embed(const int* __restrict__ ids,
+                                               const int8_t* __restrict__ E,
+                                               const float* __restrict__ Es, int d, int V,
+                                               bf16_t* __restrict__ x) {
+  const int r = blockIdx.x;
+  const int t = min(max(ids[r], 0), V - 1);
+  const float s = Es[t];
+  const int8_t* er = E + (size_t)t * d;
+  for (int c = threadIdx.x; c < d; c += 256) x[(size_t)r * d + c] = f2bf((float)er[c] * s);
+}
+
+// RMSNorm of M rows: y = bf16(x / sqrt(mean(x^2) + eps) * g)
+__global__ __launch_bounds__(256) void k_rmsnorm(const bf16_t* __restrict__ x, int d,
+                                                 const float* __restrict__ g, float eps,
+                                                 bf16_t* __restrict__ y) {
+  __shared__ float red[4];
+  const int r = blockIdx.x;
+  const bf16_t* xr = x + (size_t)r * d;
+  float ss = 0.0f;
+  for (int c = threadIdx.x; c < d; c += 256) {
+    const float v = bf2f(xr[c]);
+    ss += v * v;
+  }
+  ss = block_sum256(ss, red);
+  const float denom = sqrtf(ss / (float)d + eps);
+  for (int c = threadIdx.x; c < d; c += 256)
+    y[(size_t)r * d + c] = f2bf(bf2f(xr[c]) / denom * g[c]);
+}
+
+// ------------------------------------------------------------------------------------------
+// decode GEMV helpers
+
+__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int m) {
+  const uint32_t lo = __shfl_xor((uint32_t)v, m, 64), hi = __shfl_xor((uint32_t)(v >> 32), m, 64);
+  return ((unsigned long long)hi << 32) | lo;
+}
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const unsigned long long t = shfl_xor_u64(v, o);
+    v = t > v ? t : v;
+  }
+  return v;
+}
+
+// unpack 16 signed int8 codes to float
+__device__ __forceinline__ void i8x16_to_f32(const int4 v, float* f) {
+  const int w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f[j * 4 + e] = (float)((int)((uint32_t)w4[j] << (24 - 8 * e)) >> 24);
+}
+
+// LM head tail: each work-group's best (value, index) keys are stored per batch row;
+// the last work-group to finish reduces them and writes the greedy ids.  best[b] is
+// valid in thread b (b < nb).
+__device__ void lm_head_finish(const GemvArgs& a, unsigned long long best, int nb_max) {
+  __shared__ int last_flag;
+  __shared__ unsigned long long red[4];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  if (tid < a.nb && tid < nb_max) a.part_keys[(size_t)tid * LM_MAX_GRID + blockIdx.x] = best;
+  __syncthreads();
+  if (tid == 0) {
+    __threadfence();
+    const unsigned int t = atomicAdd(a.done, 1u);
+    last_flag = (t == gridDim.x - 1) ? 1 : 0;
+  }
+  __syncthreads();
+  if (!last_flag) return;
+  __threadfence();
+  for (int b = 0; b < a.nb; ++b) {
+    unsigned long long k = 0ull;
+    for (int i = tid; i < (int)gridDim.x; i += 256) {
+      const unsigned long long v = __hip_atomic_load(a.part_keys + (size_t)b * LM_MAX_GRID + i,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      k = v > k ? v : k;
+    }
+    k = wave_max_u64(k);
+    if (lane == 0) red[wid] = k;
+    __syncthreads();
+    if (tid == 0) {
+      unsigned long long m = red[0];
+      for (int w = 1; w < 4; ++w) m = red[w] > m ? red[w] : m;
+      const int id = key_index(m);
+      a.next_ids[b] = id;
+      if (a.out_ids) a.out_ids[(size_t)(a.batch0 + b) * a.out_ld + *a.step] = id;
+      if (a.pos) a.pos[b] += 1;
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    if (a.bump_step) *a.step += 1;
+    atomicExch(a.done, 0u);
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// single-row decode GEMV: y[n] = scale[n] * sum_k x[k] * W[n][k].
+// Every wave keeps the whole activation row in registers (lane l owns the 16-element
+// chunks l, l+64, ...), so the RMSNorm prologue is a wave reduction with no LDS and no
+// block barrier.  The first weight chunks are requested before the activations, so
+// the two memory latencies overlap.  A work-group owns 4*R rows (EPI_SILU: R gate rows
+// and their R up rows per wave) and loops over row blocks when the grid is capped.
+template <int R, int KC, int EPI>
+__global__ __launch_bounds__(256) void k_gemv1(GemvArgs a) {
+  constexpr int NR = (EPI == EPI_SILU) ? 2 * R : R;  // weight rows per wave
+  const int K = a.K;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int nchunk = K >> 4;
+  const int rows_per_blk = (EPI == EPI_SILU) ? 4 * R : 4 * R;  // logical outputs per block
+  const int nout = (EPI == EPI_SILU) ? a.N / 2 : a.N;
+  const int nblk = (nout + rows_per_blk - 1) / rows_per_blk;
+
+  auto row_of = [&](int blk, int i) -> int {
+    if (EPI == EPI_SILU) {
+      const int j = blk * rows_per_blk + wid * R + (i % R);
+      return j < nout ? gu_row(j, i / R) : a.N;
+    }
+    return blk * rows_per_blk + wid * R + i;
+  };
+
+  int blk = blockIdx.x;
+  // weights of the first block, requested before the activations
+  int4 wv[NR][KC];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    const int r = row_of(blk, i);
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      const int ch = lane + 64 * c;
+      wv[i][c] = (r < a.N && ch < nchunk && blk < nblk)
+                     ? *reinterpret_cast<const int4*>(a.W + (size_t)r * K + ch * 16)
+                     : make_int4(0, 0, 0, 0);
+    }
+  }
+  // activations (and the RMSNorm prologue) in registers
+  const bf16_t* xrow = a.x + (size_t)(a.x_rows ? a.x_rows[0] : 0) * a.ldx;
+  float xf[KC][16];
+  float ss = 0.0f;
+#pragma unroll
+  for (int c = 0; c < KC; ++c) {
+    const int ch = lane + 64 * c;
+    uint4 u0 = make_uint4(0, 0, 0, 0), u1 = u0;
+    if (ch < nchunk) {
+      const uint4* xv = reinterpret_cast<const uint4*>(xrow + ch * 16);
+      u0 = xv[0];
+      u1 = xv[1];
+    }
+    const uint32_t w8[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      xf[c][2 * j] = __uint_as_float(w8[j] << 16);
+      xf[c][2 * j + 1] = __uint_as_float(w8[j] & 0xFFFF0000u);
+      ss += xf[c][2 * j] * xf[c][2 * j] + xf[c][2 * j + 1] * xf[c][2 * j + 1];
+    }
+  }
+  if (a.gain) {
+    const float denom = sqrtf(wave_sum(ss) / (float)K + a.eps);
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      const int ch = lane + 64 * c;
+      if (ch < nchunk) {
+        const float4* g4 = reinterpret_cast<const float4*>(a.gain + ch * 16);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 g = g4[q];
+          xf[c][4 * q + 0] = rbf(xf[c][4 * q + 0] / denom * g.x);
+          xf[c][4 * q + 1] = rbf(xf[c][4 * q + 1] / denom * g.y);
+          xf[c][4 * q + 2] = rbf(xf[c][4 * q + 2] / denom * g.z);
+          xf[c][4 * q + 3] = rbf(xf[c][4 * q + 3] / denom * g.w);
+        }
+      }
+    }
+  }
+
+  unsigned long long best = 0ull;
+  for (; blk < nblk; blk += gridDim.x) {
+    float acc[NR];
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      acc[i] = 0.0f;
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        float wf[16];
+        i8x16_to_f32(wv[i][c], wf);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[i] = fmaf(wf[j], xf[c][j], acc[i]);
+      }
+    }
+    // next block's weights go out before the reductions
+    const int nxt = blk + gridDim.x;
+    if (nxt < nblk) {
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        const int r = row_of(nxt, i);
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+          const int ch = lane + 64 * c;
+          wv[i][c] = (r < a.N && ch < nchunk)
+                         ? *reinterpret_cast<const int4*>(a.W + (size_t)r * K + ch * 16)
+                         : make_int4(0, 0, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NR; ++i) acc[i] = wave_sum(acc[i]);
+    if (lane == 0) {
+      if (EPI == EPI_SILU) {
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+          const int j = blk * rows_per_blk + wid * R + i;
+          if (j >= nout) continue;
+          const float g = rbf(acc[i] * a.scale[gu_row(j, 0)]);
+          const float u = rbf(acc[i + R] * a.scale[gu_row(j, 1)]);
+          a.out[j] = f2bf(g / (1.0f + expf(-g)) * u);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+          const int r = row_of(blk, i);
+          if (r >= a.N) continue;
+          const float v = acc[i] * a.scale[r];
+          if (EPI == EPI_STORE) {
+            a.out[r] = f2bf(v);
+          } else if (EPI == EPI_RESID) {
+            a.out[r] = f2bf(bf2f(a.out[r]) + rbf(v));
+          } else {
+            if (a.logits) a.logits[r] = v;
+            const unsigned long long k = argmax_key(v, r);
+            best = k > best ? k : best;
+          }
+        }
+      }
+    }
+  }
+  if (EPI == EPI_LOGITS) {
+    __shared__ unsigned long long wbest[4];
+    if (lane == 0) wbest[wid] = best;
+    __syncthreads();
+    unsigned long long b0 = 0ull;
+    if (tid == 0) {
+      b0 = wbest[0];
+      for (int w = 1; w < 4; ++w) b0 = wbest[w] > b0 ? wbest[w] : b0;
+    }
+    lm_head_finish(a, b0, 1);
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// batched decode GEMV for 2..8 rows: y[b][n] = scale[n] * sum_k x[b][k] * W[n][k].
+// Activations (RMS-normalized in the prologue when a gain is given) are staged in LDS
+// as bf16; each wave streams R weight rows, 16 bytes per lane per row per step.
+template <int NB, int EPI>
+__global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
+  constexpr int R = (EPI == EPI_SILU) ? 8 : 4;
+  extern __shared__ __align__(16) unsigned char smem[];
+  bf16_t* xs = reinterpret_cast<bf16_t*>(smem);  // [NB][K]
+  __shared__ float red[4][NB];
+  __shared__ unsigned long long wkey[4][NB];
+
+  const int K = a.K;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int nvec = K >> 3;  // 8 bf16 per 16-byte vector
+
+  // ---- stage x rows (with optional RMSNorm) ----
+  float ss[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    ss[b] = 0.0f;
+    const bool live = b < a.nb;
+    const int xr = live ? (a.x_rows ? a.x_rows[b] : b) : 0;
+    const uint4* src = reinterpret_cast<const uint4*>(a.x + (size_t)xr * a.ldx);
+    uint4* dst = reinterpret_cast<uint4*>(xs + (size_t)b * K);
+    for (int v = tid; v < nvec; v += 256) {
+      uint4 u = live ? src[v] : make_uint4(0, 0, 0, 0);
+      dst[v] = u;
+      const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float lo = __uint_as_float(w4[j] << 16), hi = __uint_as_float(w4[j] & 0xFFFF0000u);
+        ss[b] += lo * lo + hi * hi;
+      }
+    }
+  }
+  if (a.gain) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const float t = wave_sum(ss[b]);
+      if (lane == 0) red[wid][b] = t;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const float tot = red[0][b] + red[1][b] + red[2][b] + red[3][b];
+      const float denom = sqrtf(tot / (float)K + a.eps);
+      bf16_t* row = xs + (size_t)b * K;
+      for (int c = tid; c < K; c += 256) row[c] = f2bf(bf2f(row[c]) / denom * a.gain[c]);
+    }
+  }
+  __syncthreads();
+
+  const int nblk = (EPI == EPI_SILU) ? (a.N + 2 * GU_BLOCK - 1) / (2 * GU_BLOCK) : (a.N + 15) / 16;
+  unsigned long long best[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) best[b] = 0ull;
+
+  for (int blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
+    int rows[R];
+    if (EPI == EPI_SILU) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        rows[i] = blk * 2 * GU_BLOCK + wid * 4 + i;
+        rows[i + 4] = blk * 2 * GU_BLOCK + GU_BLOCK + wid * 4 + i;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < R; ++i) rows[i] = blk * 16 + wid * 4 + i;
+    }
+
+    float acc[R][NB];
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) acc[i][b] = 0.0f;
+
+    const int nchunk = K >> 4;
+    for (int c = lane; c < nchunk; c += 64) {
+      float wf[R][16];
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        int4 v = make_int4(0, 0, 0, 0);
+        if (rows[i] < a.N) v = *reinterpret_cast<const int4*>(a.W + (size_t)rows[i] * K + c * 16);
+        i8x16_to_f32(v, wf[i]);
+      }
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const uint4* xv = reinterpret_cast<const uint4*>(xs + (size_t)b * K + c * 16);
+        const uint4 u0 = xv[0], u1 = xv[1];
+        const uint32_t w8[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+        float xf[16];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          xf[2 * j] = __uint_as_float(w8[j] << 16);
+          xf[2 * j + 1] = __uint_as_float(w8[j] & 0xFFFF0000u);
+        }
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) acc[i][b] = fmaf(wf[i][j], xf[j], acc[i][b]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) acc[i][b] = wave_sum(acc[i][b]);
+
+    if (lane != 0) continue;
+    if (EPI == EPI_STORE) {
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        if (rows[i] >= a.N) continue;
+        const float s = a.scale[rows[i]];
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          if (b < a.nb) a.out[(size_t)b * a.ldo + rows[i]] = f2bf(acc[i][b] * s);
+      }
+    } else if (EPI == EPI_RESID) {
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        if (rows[i] >= a.N) continue;
+        const float s = a.scale[rows[i]];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          if (b >= a.nb) continue;
+          bf16_t* o = a.out + (size_t)b * a.ldo + rows[i];
+          *o = f2bf(bf2f(*o) + rbf(acc[i][b] * s));
+        }
+      }
+    } else if (EPI == EPI_SILU) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (rows[i + 4] >= a.N) continue;
+        const float sg = a.scale[rows[i]], su = a.scale[rows[i + 4]];
+        const int j = blk * GU_BLOCK + wid * 4 + i;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          if (b >= a.nb) continue;
+          const float g = rbf(acc[i][b] * sg), u = rbf(acc[i + 4][b] * su);
+          a.out[(size_t)b * a.ldo + j] = f2bf(g / (1.0f + expf(-g)) * u);
+        }
+      }
+    } else {  // EPI_LOGITS
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+          if (rows[i] >= a.N || b >= a.nb) continue;
+          const float v = acc[i][b] * a.scale[rows[i]];
+          if (a.logits) a.logits[(size_t)b * a.ldl + rows[i]] = v;
+          const unsigned long long k = argmax_key(v, rows[i]);
+          best[b] = k > best[b] ? k : best[b];
+        }
+      }
+    }
+  }
+  if (EPI == EPI_LOGITS) {
+    if (lane == 0) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) wkey[wid][b] = best[b];
+    }
+    __syncthreads();
+    unsigned long long mine = 0ull;
+    if (tid < NB) {
+      mine = wkey[0][tid];
+      for (int w = 1; w < 4; ++w) mine = wkey[w][tid] > mine ? wkey[w][tid] : mine;
+    }
+    lm_head_finish(a, mine, NB);
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// prefill GEMM on MFMA: C[m][n] = scale[n] * sum_k A[m][k] * W[n][k]
+// A bf16 [M][K], W int8 [N][K] converted to bf16 in registers (exact for |q| <= 127).
+// 64x64 output tile per work-group, 4 waves in 2x2, each 32x32 = 2x2 MFMA 16x16x32 tiles.
+__device__ __forceinline__ bf16x8_t i8x8_to_bf16x8(uint2 w) {
+  const uint32_t in[2] = {w.x, w.y};
+  uint32_t out[4];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int v0 = ((int)(in[h] << (24 - 16 * e))) >> 24;
+      const int v1 = ((int)(in[h] << (16 - 16 * e))) >> 24;
+      const uint32_t b0 = __float_as_uint((float)v0) >> 16;
+      const uint32_t b1 = __float_as_uint((float)v1) & 0xFFFF0000u;
+      out[h * 2 + e] = b0 | b1;
+    }
+  }
+  return __builtin_bit_cast(bf16x8_t, make_uint4(out[0], out[1], out[2], out[3]));
+}
+
+template <int EPI>
+__global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
+  constexpr int BM = 64, BN = 64, BK = 32;
+  __shared__ __align__(16) bf16_t As[BM][BK + 8];
+  __shared__ __align__(16) int8_t Ws[BN][BK + 16];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid & 1, wn = wid >> 1;
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  f32x4_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int k0 = 0; k0 < a.K; k0 += BK) {
+    {
+      const int row = tid >> 2, part = tid & 3;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (m0 + row < a.M)
+        v = *reinterpret_cast<const uint4*>(a.A + (size_t)(m0 + row) * a.lda + k0 + part * 8);
+      *reinterpret_cast<uint4*>(&As[row][part * 8]) = v;
+    }
+    if (tid < 128) {
+      const int row = tid >> 1, part = tid & 1;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (n0 + row < a.N)
+        v = *reinterpret_cast<const uint4*>(a.W + (size_t)(n0 + row) * a.K + k0 + part * 16);
+      *reinterpret_cast<uint4*>(&Ws[row][part * 16]) = v;
+    }
+    __syncthreads();
+    bf16x8_t af[2], bw[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+      af[mt] = __builtin_bit_cast(
+          bf16x8_t, *reinterpret_cast<const uint4*>(&As[wm * 32 + mt * 16 + (lane & 15)][8 * (lane >> 4)]));
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+      bw[nt] = i8x8_to_bf16x8(
+          *reinterpret_cast<const uint2*>(&Ws[wn * 32 + nt * 16 + (lane & 15)][8 * (lane >> 4)]));
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt], bw[nt], acc[mt][nt], 0, 0, 0);
+    __syncthreads();
+  }
+
+  // lane holds D[4*(lane/16)+i][lane%16]: token rows, channel columns
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + wm * 32 + mt * 16 + 4 * (lane >> 4) + i;
+      if (m >= a.M) continue;
+      if (EPI == EPI_SILU) {
+        const int ng = n0 + wn * 32 + (lane & 15), nu = ng + GU_BLOCK;
+        if (nu >= a.N) continue;
+        const float g = rbf(acc[mt][0][i] * a.scale[ng]);
+        const float u = rbf(acc[mt][1][i] * a.scale[nu]);
+        const int j = (ng / (2 * GU_BLOCK)) * GU_BLOCK + (lane & 15);
+        a.out[(size_t)m * a.ldo + j] = f2bf(g / (1.0f + expf(-g)) * u);
+      } else {
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          const int n = n0 + wn * 32 + nt * 16 + (lane & 15);
+          if (n >= a.N) continue;
+          const float v = acc[mt][nt][i] * a.scale[n];
+          bf16_t* o = a.out + (size_t)m * a.ldo + n;
+          if (EPI == EPI_STORE) *o = f2bf(v);
+          else *o = f2bf(bf2f(*o) + rbf(v));
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// QK-norm + RoPE + KV-cache write, one work-group per token row.
+// q and k heads: RMSNorm over head_dim with a shared gain, then rotate-half RoPE at
+// the row's position; q is written back in place, k and v go to the cache.
+__global__ __launch_bounds__(256) void k_qk_rope(RopeArgs a) {
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int D = a.D, half = D / 2;
+  const int slot = a.row_slot[r], p = a.row_pos[r];
+  bf16_t* row = a.qkv + (size_t)r * a.ldqkv;
+  const float2* tab = a.rope + (size_t)p * half;
+  for (int hh = wid; hh < a.H + 2 * a.KV; hh += 4) {
+    bf16_t* src = row + (size_t)hh * D;
+    if (hh < a.H + a.KV) {
+      const bool isq = hh < a.H;
+      const float* gn = isq ? a.q_gain : a.k_gain;
+      float x1[2], x2[2], ss = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int i = lane + 64 * j;
+        x1[j] = x2[j] = 0.0f;
+        if (i < half) {
+          x1[j] = bf2f(src[i]);
+          x2[j] = bf2f(src[i + half]);
+          ss += x1[j] * x1[j] + x2[j] * x2[j];
+        }
+      }
+      ss = wave_sum(ss);
+      const float denom = sqrtf(ss / (float)D + a.eps);
+      bf16_t* dst = src;
+      if (!isq) {
+        const int g = hh - a.H;
+        dst = a.kcache + (((size_t)slot * a.KV + g) * a.max_ctx + p) * D;
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int i = lane + 64 * j;
+        if (i < half) {
+          const float y1 = rbf(x1[j] / denom * gn[i]);
+          const float y2 = rbf(x2[j] / denom * gn[i + half]);
+          const float2 cs = tab[i];
+          dst[i] = f2bf(y1 * cs.x - y2 * cs.y);
+          dst[i + half] = f2bf(y2 * cs.x + y1 * cs.y);
+        }
+      }
+    } else {
+      const int g = hh - a.H - a.KV;
+      bf16_t* dst = a.vcache + (((size_t)slot * a.KV + g) * a.max_ctx + p) * D;
+      for (int i = lane; i < D; i += 64) dst[i] = src[i];
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// GQA attention over the KV cache for one token row, one KV head and one split of the
+// positions 0..p.  The G query heads of the group share every K/V row read.  Softmax is
+// computed online across 64-position chunks in fp32; with several splits the partial
+// (max, sum, unnormalized output) go to a merge kernel.
+template <int D, int G>
+__global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
+  constexpr int CH = ATT_CHUNK;
+  constexpr int HALF = D / 2;
+  constexpr int NG = 256 / HALF;  // position groups in the P*V phase
+  __shared__ float qs[G][D];
+  __shared__ float sc[G][CH];
+  __shared__ float ored[NG][G][D];
+  const int s = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int slot = a.row_slot[r], p = a.row_pos[r];
+  const int n = p + 1;
+  const int t_begin = s * a.split_len;
+  const int t_end = min(n, t_begin + a.split_len);
+  const bf16_t* q = a.q + (size_t)r * a.ldq + (size_t)g * G * D;
+  for (int idx = tid; idx < G * D; idx += 256) qs[idx / D][idx % D] = bf2f(q[idx]);
+  const bf16_t* Kb = a.kcache + ((size_t)slot * a.KV + g) * a.max_ctx * D;
+  const bf16_t* Vb = a.vcache + ((size_t)slot * a.KV + g) * a.max_ctx * D;
+  const float scale = 1.0f / sqrtf((float)D);
+  __syncthreads();
+
+  float m[G], l[G], o[G][2];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.0f;
+    o[h][0] = o[h][1] = 0.0f;
+  }
+  const int dp = tid % HALF, grp = tid / HALF;
+  for (int t0 = t_begin; t0 < t_end; t0 += CH) {
+    {  // scores: 4 lanes per position
+      const int tl = tid >> 2, part = tid & 3;
+      const int t = t0 + tl;
+      float sp[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) sp[h] = 0.0f;
+      if (t < t_end) {
+        const bf16_t* kr = Kb + (size_t)t * D + part * (D / 4);
+#pragma unroll
+        for (int j = 0; j < D / 4; j += 2) {
+          const uint32_t kk = *reinterpret_cast<const uint32_t*>(kr + j);
+          const float k0 = __uint_as_float(kk << 16), k1 = __uint_as_float(kk & 0xFFFF0000u);
+#pragma unroll
+          for (int h = 0; h < G; ++h)
+            sp[h] += qs[h][part * (D / 4) + j] * k0 + qs[h][part * (D / 4) + j + 1] * k1;
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        sp[h] += __shfl_xor(sp[h], 1, 64);
+        sp[h] += __shfl_xor(sp[h], 2, 64);
+      }
+      if (part == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) sc[h][tl] = (t < t_end) ? sp[h] * scale : -INFINITY;
+      }
+    }
+    __syncthreads();
+    float mnew[G], alpha[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float cm = -INFINITY;
+      for (int t = 0; t < CH; ++t) cm = fmaxf(cm, sc[h][t]);
+      mnew[h] = fmaxf(m[h], cm);
+      alpha[h] = (m[h] == -INFINITY) ? 0.0f : expf(m[h] - mnew[h]);
+    }
+    __syncthreads();
+    if (tid < CH) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float v = sc[h][tid];
+        sc[h][tid] = (v == -INFINITY) ? 0.0f : expf(v - mnew[h]);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float cs = 0.0f;
+      for (int t = 0; t < CH; ++t) cs += sc[h][t];
+      l[h] = l[h] * alpha[h] + cs;
+      m[h] = mnew[h];
+      o[h][0] *= alpha[h];
+      o[h][1] *= alpha[h];
+    }
+    for (int tl = grp; tl < CH; tl += NG) {
+      const int t = t0 + tl;
+      if (t >= t_end) break;
+      const uint32_t vv = *reinterpret_cast<const uint32_t*>(Vb + (size_t)t * D + 2 * dp);
+      const float v0 = __uint_as_float(vv << 16), v1 = __uint_as_float(vv & 0xFFFF0000u);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float pw = sc[h][tl];
+        o[h][0] += pw * v0;
+        o[h][1] += pw * v1;
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    ored[grp][h][2 * dp] = o[h][0];
+    ored[grp][h][2 * dp + 1] = o[h][1];
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * D; idx += 256) {
+    const int h = idx / D, dd = idx % D;
+    float acc = 0.0f;
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) acc += ored[gg][h][dd];
+    const int head = g * G + h;
+    if (a.nsplit == 1) {
+      a.out[(size_t)r * a.ldo + (size_t)head * D + dd] = f2bf(acc / l[h]);
+    } else {
+      const size_t pi = ((size_t)r * a.H + head) * a.nsplit + s;
+      a.part_o[pi * D + dd] = acc;
+      if (dd == 0) {
+        a.part_ml[pi * 2] = m[h];
+        a.part_ml[pi * 2 + 1] = l[h];
+      }
+    }
+  }
+}
+
+// Decode attention for one token row b, one KV head g and one split of positions.
+// Fused in front: RMSNorm (shared [D] gain) and rotate-half RoPE at position p of the
+// group's G query heads and of its key head, done in LDS from the raw projections; the
+// split that holds position p writes the new K and V rows to the cache and every split
+// uses the fresh rows for p from LDS.  Fused behind: with several splits, each writes
+// its partial (max, sum, unnormalized output); the split that finishes last merges them.
+template <int D, int G>
+__global__ __launch_bounds__(256) void k_attn_dec(AttnDecArgs a) {
+  constexpr int CH = ATT_CHUNK;
+  constexpr int HALF = D / 2;
+  constexpr int NG = 256 / HALF;
+  __shared__ float qs[G][D];
+  __shared__ float kn[D], vn[D];
+  __shared__ float sc[G][CH];
+  __shared__ float ored[NG][G][D];
+  __shared__ int last_flag;
+  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int p = a.pos[b];
+  const int n = p + 1;
+  const int t_begin = s * a.split_len;
+  const int t_end = min(n, t_begin + a.split_len);
+  const bf16_t* row = a.qkv + (size_t)b * a.ldqkv;
+  const float2* tab = a.rope + (size_t)p * HALF;
+  bf16_t* Kb = a.kcache + ((size_t)b * a.KV + g) * a.max_ctx * D;
+  bf16_t* Vb = a.vcache + ((size_t)b * a.KV + g) * a.max_ctx * D;
+  const bool owner = (t_begin <= p) && (p < t_begin + a.split_len);
+
+  // ---- QK-norm + RoPE of the G query heads and the key head; copy of v ----
+  for (int hh = wid; hh <= G; hh += 4) {
+    const bool isq = hh < G;
+    const bf16_t* src = isq ? row + (size_t)(g * G + hh) * D : row + (size_t)(a.H + g) * D;
+    const float* gn = isq ? a.q_gain : a.k_gain;
+    float x1[2], x2[2], ss = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int i = lane + 64 * j;
+      x1[j] = x2[j] = 0.0f;
+      if (i < HALF) {
+        x1[j] = bf2f(src[i]);
+        x2[j] = bf2f(src[i + HALF]);
+        ss += x1[j] * x1[j] + x2[j] * x2[j];
+      }
+    }
+    ss = wave_sum(ss);
+    const float denom = sqrtf(ss / (float)D + a.eps);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int i = lane + 64 * j;
+      if (i < HALF) {
+        const float y1 = rbf(x1[j] / denom * gn[i]);
+        const float y2 = rbf(x2[j] / denom * gn[i + HALF]);
+        const float2 cs = tab[i];
+        const bf16_t o1 = f2bf(y1 * cs.x - y2 * cs.y), o2 = f2bf(y2 * cs.x + y1 * cs.y);
+        if (isq) {
+          qs[hh][i] = bf2f(o1);
+          qs[hh][i + HALF] = bf2f(o2);
+        } else {
+          kn[i] = bf2f(o1);
+          kn[i + HALF] = bf2f(o2);
+          if (owner) {
+            Kb[(size_t)p * D + i] = o1;
+            Kb[(size_t)p * D + i + HALF] = o2;
+          }
+        }
+      }
+    }
+  }
+  {
+    const bf16_t* vsrc = row + (size_t)(a.H + a.KV + g) * D;
+    for (int i = tid; i < D; i += 256) {
+      const bf16_t v = vsrc[i];
+      vn[i] = bf2f(v);
+      if (owner) Vb[(size_t)p * D + i] = v;
+    }
+  }
+  __syncthreads();
+
+  const float scale = 1.0f / sqrtf((float)D);
+  float m[G], l[G], o[G][2];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.0f;
+    o[h][0] = o[h][1] = 0.0f;
+  }
+  const int dp = tid % HALF, grp = tid / HALF;
+  for (int t0 = t_begin; t0 < t_end; t0 += CH) {
+    {  // scores: 4 lanes per position
+      const int tl = tid >> 2, part = tid & 3;
+      const int t = t0 + tl;
+      float sp[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) sp[h] = 0.0f;
+      if (t < t_end) {
+        if (t == p) {
+#pragma unroll
+          for (int j = 0; j < D / 4; ++j) {
+            const float kv = kn[part * (D / 4) + j];
+#pragma unroll
+            for (int h = 0; h < G; ++h) sp[h] += qs[h][part * (D / 4) + j] * kv;
+          }
+        } else {
+          const bf16_t* kr = Kb + (size_t)t * D + part * (D / 4);
+#pragma unroll
+          for (int j = 0; j < D / 4; j += 2) {
+            const uint32_t kk = *reinterpret_cast<const uint32_t*>(kr + j);
+            const float k0 = __uint_as_float(kk << 16), k1 = __uint_as_float(kk & 0xFFFF0000u);
+#pragma unroll
+            for (int h = 0; h < G; ++h)
+              sp[h] += qs[h][part * (D / 4) + j] * k0 + qs[h][part * (D / 4) + j + 1] * k1;
+          }
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        sp[h] += __shfl_xor(sp[h], 1, 64);
+        sp[h] += __shfl_xor(sp[h], 2, 64);
+      }
+      if (part == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) sc[h][tl] = (t < t_end) ? sp[h] * scale : -INFINITY;
+      }
+    }
+    __syncthreads();
+    float mnew[G], alpha[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float cm = -INFINITY;
+      for (int t = 0; t < CH; ++t) cm = fmaxf(cm, sc[h][t]);
+      mnew[h] = fmaxf(m[h], cm);
+      alpha[h] = (m[h] == -INFINITY) ? 0.0f : expf(m[h] - mnew[h]);
+    }
+    __syncthreads();
+    if (tid < CH) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float v = sc[h][tid];
+        sc[h][tid] = (v == -INFINITY) ? 0.0f : expf(v - mnew[h]);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float cs = 0.0f;
+      for (int t = 0; t < CH; ++t) cs += sc[h][t];
+      l[h] = l[h] * alpha[h] + cs;
+      m[h] = mnew[h];
+      o[h][0] *= alpha[h];
+      o[h][1] *= alpha[h];
+    }
+    for (int tl = grp; tl < CH; tl += NG) {
+      const int t = t0 + tl;
+      if (t >= t_end) break;
+      float v0, v1;
+      if (t == p) {
+        v0 = vn[2 * dp];
+        v1 = vn[2 * dp + 1];
+      } else {
+        const uint32_t vv = *reinterpret_cast<const uint32_t*>(Vb + (size_t)t * D + 2 * dp);
+        v0 = __uint_as_float(vv << 16);
+        v1 = __uint_as_float(vv & 0xFFFF0000u);
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float pw = sc[h][tl];
+        o[h][0] += pw * v0;
+        o[h][1] += pw * v1;
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    ored[grp][h][2 * dp] = o[h][0];
+    ored[grp][h][2 * dp + 1] = o[h][1];
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * D; idx += 256) {
+    const int h = idx / D, dd = idx % D;
+    float acc = 0.0f;
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) acc += ored[gg][h][dd];
+    const int head = g * G + h;
+    if (a.nsplit == 1) {
+      a.out[(size_t)b * a.ldo + (size_t)head * D + dd] = f2bf(acc / l[h]);
+    } else {
+      const size_t pi = ((size_t)b * a.H + head) * a.nsplit + s;
+      a.part_o[pi * D + dd] = acc;
+      if (dd == 0) {
+        a.part_ml[pi * 2] = m[h];
+        a.part_ml[pi * 2 + 1] = l[h];
+      }
+    }
+  }
+  if (a.nsplit == 1) return;
+  // ---- the last split to finish merges all partials of this (row, KV head) ----
+  __syncthreads();
+  if (tid == 0) {
+    __threadfence();
+    const unsigned int t = atomicAdd(a.counters + (size_t)b * a.KV + g, 1u);
+    last_flag = (t == (unsigned)a.nsplit - 1) ? 1 : 0;
+  }
+  __syncthreads();
+  if (!last_flag) return;
+  __threadfence();
+  for (int idx = tid; idx < G * D; idx += 256) {
+    const int h = idx / D, dd = idx % D;
+    const int head = g * G + h;
+    const size_t base = ((size_t)b * a.H + head) * a.nsplit;
+    float mx = -INFINITY;
+    for (int q = 0; q < a.nsplit; ++q) mx = fmaxf(mx, a.part_ml[(base + q) * 2]);
+    float lsum = 0.0f, acc = 0.0f;
+    for (int q = 0; q < a.nsplit; ++q) {
+      const float ms = a.part_ml[(base + q) * 2];
+      if (ms == -INFINITY) continue;
+      const float w = expf(ms - mx);
+      lsum += a.part_ml[(base + q) * 2 + 1] * w;
+      acc += a.part_o[(base + q) * D + dd] * w;
+    }
+    a.out[(size_t)b * a.ldo + (size_t)head * D + dd] = f2bf(acc / lsum);
+  }
+  if (tid == 0) atomicExch(a.counters + (size_t)b * a.KV + g, 0u);
+}
+
+// merge split partials: o = sum_s o_s e^(m_s - m) / sum_s l_s e^(m_s - m)
+__global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
+  const int head = blockIdx.x, r = blockIdx.y;
+  const int D = a.D;
+  const size_t base = ((size_t)r * a.H + head) * a.nsplit;
+  float mx = -INFINITY;
+  for (int s = 0; s < a.nsplit; ++s) mx = fmaxf(mx, a.part_ml[(base + s) * 2]);
+  float lsum = 0.0f;
+  for (int s = 0; s < a.nsplit; ++s) {
+    const float ms = a.part_ml[(base + s) * 2];
+    if (ms != -INFINITY) lsum += a.part_ml[(base + s) * 2 + 1] * expf(ms - mx);
+  }
+  for (int dd = threadIdx.x; dd < D; dd += blockDim.x) {
+    float acc = 0.0f;
+    for (int s = 0; s < a.nsplit; ++s) {
+      const float ms = a.part_ml[(base + s) * 2];
+      if (ms != -INFINITY) acc += a.part_o[(base + s) * D + dd] * expf(ms - mx);
+    }
+    a.out[(size_t)r * a.ldo + (size_t)head * D + dd] = f2bf(acc / lsum);
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// launchers
+
+hipError_t launch_quantize_rows(const float* w, int rows, int cols, int8_t* q, float* s,
+                                int dst_row0, int gu_half, hipStream_t st) {
+  hipLaunchKernelGGL(k_quantize_rows, dim3(rows), dim3(256), 0, st, w, cols, q, s, dst_row0,
+                     gu_half);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_table(float2* tab, int max_ctx, int D, float theta, hipStream_t st) {
+  const long n = (long)max_ctx * (D / 2);
+  hipLaunchKernelGGL(k_rope_table, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, tab,
+                     max_ctx, D, (double)theta);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_i32(int* p, int n, int v, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_fill_i32, dim3((n + 255) / 256), dim3(256), 0, st, p, n, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_u64(unsigned long long* p, int n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_fill_u64, dim3((n + 255) / 256), dim3(256), 0, st, p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_set_positions(int* pos, const int* lens, int n, hipStream_t st) {
+  hipLaunchKernelGGL(k_set_positions, dim3((n + 255) / 256), dim3(256), 0, st, pos, lens, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_iota(int* p, int n, hipStream_t st) {
+  hipLaunchKernelGGL(k_iota, dim3((n + 255) / 256), dim3(256), 0, st, p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_embed(const int* ids, int M, const int8_t* E, const float* Es, int d, int V,
+                        bf16_t* x, hipStream_t st) {
+  hipLaunchKernelGGL(k_embed, dim3(M), dim3(256), 0, st, ids, E, Es, d, V, x);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(const bf16_t* x, int M, int d, const float* g, float eps, bf16_t* y,
+                          hipStream_t st) {
+  hipLaunchKernelGGL(k_rmsnorm, dim3(M), dim3(256), 0, st, x, d, g, eps, y);
+  return hipGetLastError();
+}
+
+template <int NB>
+static hipError_t gemv_nb(const GemvArgs& a, int epi, hipStream_t st) {
+  const size_t lds = (size_t)NB * a.K * sizeof(bf16_t);
+  const int nblk = epi == EPI_SILU ? (a.N + 2 * GU_BLOCK - 1) / (2 * GU_BLOCK) : (a.N + 15) / 16;
+  dim3 grid(epi == EPI_LOGITS ? (nblk < LM_MAX_GRID ? nblk : LM_MAX_GRID) : nblk);
+  if (epi == EPI_SILU) hipLaunchKernelGGL((k_gemv<NB, EPI_SILU>), grid, dim3(256), lds, st, a);
+  else if (epi == EPI_STORE) hipLaunchKernelGGL((k_gemv<NB, EPI_STORE>), grid, dim3(256), lds, st, a);
+  else if (epi == EPI_RESID) hipLaunchKernelGGL((k_gemv<NB, EPI_RESID>), grid, dim3(256), lds, st, a);
+  else hipLaunchKernelGGL((k_gemv<NB, EPI_LOGITS>), grid, dim3(256), lds, st, a);
+  return hipGetLastError();
+}
+
+template <int R, int KC>
+static hipError_t gemv1_rk(const GemvArgs& a, int epi, hipStream_t st) {
+  const int nout = epi == EPI_SILU ? a.N / 2 : a.N;
+  const int nblk = (nout + 4 * R - 1) / (4 * R);
+  dim3 grid(epi == EPI_LOGITS ? (nblk < LM_MAX_GRID ? nblk : LM_MAX_GRID) : nblk);
+  switch (epi) {
+    case EPI_STORE: hipLaunchKernelGGL((k_gemv1<R, KC, EPI_STORE>), grid, dim3(256), 0, st, a); break;
+    case EPI_RESID: hipLaunchKernelGGL((k_gemv1<R, KC, EPI_RESID>), grid, dim3(256), 0, st, a); break;
+    case EPI_SILU: hipLaunchKernelGGL((k_gemv1<R, KC, EPI_SILU>), grid, dim3(256), 0, st, a); break;
+    default: hipLaunchKernelGGL((k_gemv1<R, KC, EPI_LOGITS>), grid, dim3(256), 0, st, a); break;
+  }
+  return hipGetLastError();
+}
+
+template <int R>
+static hipError_t gemv1_r(const GemvArgs& a, int epi, hipStream_t st) {
+  const int kc = (a.K + 1023) / 1024;
+  switch (kc) {
+    case 1: return gemv1_rk<R, 1>(a, epi, st);
+    case 2: return gemv1_rk<R, 2>(a, epi, st);
+    case 3: return gemv1_rk<R, 3>(a, epi, st);
+    case 4: return gemv1_rk<R, 4>(a, epi, st);
+    case 5: case 6: return gemv1_rk<R, 6>(a, epi, st);
+    default: return gemv1_rk<R, 8>(a, epi, st);
+  }
+}
+
+// one row: register kernel; enough work-groups per matrix to cover the GPU
+static hipError_t gemv1(const GemvArgs& a, int epi, hipStream_t st) {
+  if (a.K > 8192) return hipErrorInvalidValue;
+  const int nout = epi == EPI_SILU ? a.N / 2 : a.N;
+  if ((epi == EPI_LOGITS || nout >= 4096) && a.K <= 2048) return gemv1_r<4>(a, epi, st);
+  return gemv1_r<1>(a, epi, st);
+}
+
+static hipError_t gemv_dispatch(const GemvArgs& a, int epi, hipStream_t st) {
+  if (a.nb <= 1) return gemv1(a, epi, st);
+  if (a.nb <= 2) return gemv_nb<2>(a, epi, st);
+  if (a.nb <= 4) return gemv_nb<4>(a, epi, st);
+  return gemv_nb<8>(a, epi, st);
+}
+
+// rows staged in LDS must fit in 64 KiB: larger batches run as several launches
+hipError_t launch_gemv(const GemvArgs& a, int epi, hipStream_t st) {
+  if (a.nb < 1 || a.nb > 8) return hipErrorInvalidValue;
+  if (a.nb == 1) return gemv_dispatch(a, epi, st);
+  int cap = 8;
+  while (cap > 1 && (size_t)cap * a.K * sizeof(bf16_t) > 65536) cap >>= 1;
+  if (cap == 1 && (size_t)2 * a.K * sizeof(bf16_t) > 65536 && a.nb > 1 && epi == EPI_LOGITS)
+    return hipErrorInvalidValue;
+  if (a.nb <= cap) return gemv_dispatch(a, epi, st);
+  if (epi == EPI_LOGITS) return hipErrorInvalidValue;  // the LM head keeps its batch in one launch
+  for (int b0 = 0; b0 < a.nb; b0 += cap) {
+    GemvArgs s = a;
+    s.nb = a.nb - b0 < cap ? a.nb - b0 : cap;
+    if (a.x_rows) s.x_rows = a.x_rows + b0;
+    else s.x = a.x + (size_t)b0 * a.ldx;
+    s.out = a.out + (size_t)b0 * a.ldo;
+    hipError_t e = gemv_dispatch(s, epi, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
+  dim3 grid((a.N + 63) / 64, (a.M + 63) / 64);
+  switch (a.epi) {
+    case EPI_STORE: hipLaunchKernelGGL(k_gemm<EPI_STORE>, grid, dim3(256), 0, st, a); break;
+    case EPI_RESID: hipLaunchKernelGGL(k_gemm<EPI_RESID>, grid, dim3(256), 0, st, a); break;
+    default: hipLaunchKernelGGL(k_gemm<EPI_SILU>, grid, dim3(256), 0, st, a); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_qk_rope(const RopeArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(k_qk_rope, dim3(a.M), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t attn_d(const AttnArgs& a, int G, hipStream_t st) {
+  dim3 grid(a.nsplit, a.KV, a.M);
+  switch (G) {
+    case 1: hipLaunchKernelGGL((k_attn<D, 1>), grid, dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((k_attn<D, 2>), grid, dim3(256), 0, st, a); break;
+    case 3: hipLaunchKernelGGL((k_attn<D, 3>), grid, dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((k_attn<D, 4>), grid, dim3(256), 0, st, a); break;
+    case 5: hipLaunchKernelGGL((k_attn<D, 5>), grid, dim3(256), 0, st, a); break;
+    case 6: hipLaunchKernelGGL((k_attn<D, 6>), grid, dim3(256), 0, st, a); break;
+    case 7: hipLaunchKernelGGL((k_attn<D, 7>), grid, dim3(256), 0, st, a); break;
+    default: hipLaunchKernelGGL((k_attn<D, 8>), grid, dim3(256), 0, st, a); break;
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t attn_dec_d(const AttnDecArgs& a, int G, hipStream_t st) {
+  dim3 grid(a.nsplit, a.KV, a.B);
+  switch (G) {
+    case 1: hipLaunchKernelGGL((k_attn_dec<D, 1>), grid, dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((k_attn_dec<D, 2>), grid, dim3(256), 0, st, a); break;
+    case 3: hipLaunchKernelGGL((k_attn_dec<D, 3>), grid, dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((k_attn_dec<D, 4>), grid, dim3(256), 0, st, a); break;
+    case 5: hipLaunchKernelGGL((k_attn_dec<D, 5>), grid, dim3(256), 0, st, a); break;
+    case 6: hipLaunchKernelGGL((k_attn_dec<D, 6>), grid, dim3(256), 0, st, a); break;
+    case 7: hipLaunchKernelGGL((k_attn_dec<D, 7>), grid, dim3(256), 0, st, a); break;
+    default: hipLaunchKernelGGL((k_attn_dec<D, 8>), grid, dim3(256), 0, st, a); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_decode(const AttnDecArgs& a, hipStream_t st) {
+  const int G = a.H / a.KV;
+  if (G < 1 || G > 8 || a.nsplit < 1) return hipErrorInvalidValue;
+  switch (a.D) {
+    case 16: return attn_dec_d<16>(a, G, st);
+    case 32: return attn_dec_d<32>(a, G, st);
+    case 64: return attn_dec_d<64>(a, G, st);
+    case 128: return attn_dec_d<128>(a, G, st);
+    case 256: return attn_dec_d<256>(a, G, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
+  const int G = a.H / a.KV;
+  hipError_t e;
+  switch (a.D) {
+    case 16: e = attn_d<16>(a, G, st); break;
+    case 32: e = attn_d<32>(a, G, st); break;
+    case 64: e = attn_d<64>(a, G, st); break;
+    case 128: e = attn_d<128>(a, G, st); break;
+    default: e = attn_d<256>(a, G, st); break;
+  }
+  if (e != hipSuccess || a.nsplit == 1) return e;
+  hipLaunchKernelGGL(k_attn_merge, dim3(a.H, a.M), dim3(128), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace qd

@@ -1,0 +1,193 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Every input is seeded and synthetic (workloads): N(0, 0.02^2) weights, uniform prompt
+ids, at the Qwen3 family's shapes ("Model-agnostic LLM inference", section "Supported
+models").  Quantization ("The quantized load cache") must be bit-exact; logits and ids
+must meet the bar in parity.py.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from oracle import Oracle, quantize_model, quantize_rows
+from workloads import SHAPES, ModelShape, make_weights, make_prompt, make_prompts
+from parity import say, check_step, logit_err, margin_of, bar_for, STRICT_TOL
+
+pytestmark = pytest.mark.gpu
+
+TINY = SHAPES["tiny"]
+WIDE = ModelShape(hidden=128, n_layers=2, n_heads=4, n_kv_heads=2, head_dim=64,
+                  intermediate=256, vocab=512)
+# ragged tails everywhere: vocab not a multiple of any tile, 3 query heads per KV head
+ODD = ModelShape(hidden=96, n_layers=3, n_heads=6, n_kv_heads=2, head_dim=32,
+                 intermediate=160, vocab=1000)
+
+
+def _model(shape, weights, **kw):
+    import int8_weight_only_amd as qd
+    return qd.Model(shape, weights, **kw)
+
+
+@pytest.fixture(scope="module")
+def tiny_setup():
+    w = make_weights(TINY, seed=0, gains="uniform")
+    qm = quantize_model(w)
+    say("[gpu] loading tiny model")
+    m = _model(TINY, w, max_batch=4, max_ctx=128, max_prefill_tokens=256)
+    yield TINY, w, qm, m
+    m.close()
+
+
+@pytest.mark.parametrize("shape", [TINY, WIDE, ODD], ids=["tiny", "wide", "odd"])
+def test_quantization_bit_exact(shape):
+    w = make_weights(shape, seed=3)
+    say(f"[gpu] quantization bit-exact {shape}")
+    m = _model(shape, w, max_batch=1, max_ctx=64, max_prefill_tokens=64)
+    try:
+        q, s = m.export_quantized("embed")
+        qr, sr = quantize_rows(w["embed"])
+        np.testing.assert_array_equal(s, sr)
+        np.testing.assert_array_equal(q, qr)
+        for li in range(shape.n_layers):
+            for t in ("q", "k", "v", "o", "gate", "up", "down"):
+                q, s = m.export_quantized(t, li)
+                qr, sr = quantize_rows(w["layers"][li][t])
+                np.testing.assert_array_equal(s, sr, err_msg=f"{t}{li}")
+                np.testing.assert_array_equal(q, qr, err_msg=f"{t}{li}")
+    finally:
+        m.close()
+
+
+def _teacher_forced(m, shape, qm, prompt, n_steps, label, config):
+    """Prefill + n_steps decode steps fed the oracle's ids; check every step."""
+    orc = Oracle(shape, qm, mode="bf16").generate(prompt, n_steps + 1)
+    nxt, lg = m.prefill([prompt], logits=True)
+    torch.cuda.synchronize()
+    errs = [check_step(lg[0].cpu().numpy(), nxt[0].item(), orc["logits"][0], orc["margin"][0],
+                       config, f"{label} prefill")]
+    for k in range(1, n_steps + 1):
+        feed = torch.tensor([orc["ids"][k - 1]], dtype=torch.int32, device="cuda")
+        nxt, lg = m.decode_step(feed, logits=True)
+        torch.cuda.synchronize()
+        errs.append(check_step(lg[0].cpu().numpy(), nxt[0].item(), orc["logits"][k],
+                               orc["margin"][k], config, f"{label} step {k}"))
+    strict = sum(e <= STRICT_TOL for e in errs)
+    say(f"[gpu] {label}: max logit err {max(errs):.3g} (bar {bar_for(config)[0]}), "
+        f"{strict}/{len(errs)} steps within {STRICT_TOL}")
+    return errs
+
+
+def test_teacher_forced_tiny(tiny_setup):
+    shape, w, qm, m = tiny_setup
+    say("[gpu] teacher-forced tiny, 16-token prompt, 16 steps")
+    _teacher_forced(m, shape, qm, make_prompt(shape.vocab, 16, 1000), 16, "tiny", "tiny")
+
+
+@pytest.mark.parametrize("shape,config", [(WIDE, "wide"), (ODD, "odd")], ids=["wide", "odd"])
+def test_teacher_forced_other_shapes(shape, config):
+    w = make_weights(shape, seed=1, gains="uniform")
+    qm = quantize_model(w)
+    say(f"[gpu] teacher-forced {shape}")
+    m = _model(shape, w, max_batch=2, max_ctx=200, max_prefill_tokens=200)
+    try:
+        # a prompt longer than one 64-position attention chunk, with a ragged tail
+        _teacher_forced(m, shape, qm, make_prompt(shape.vocab, 77, 1001), 12, config, config)
+    finally:
+        m.close()
+
+
+def test_generate_greedy_matches_oracle(tiny_setup):
+    shape, w, qm, m = tiny_setup
+    prompt = make_prompt(shape.vocab, 16, 1000)
+    say("[gpu] generate_greedy tiny 16+16")
+    res = m.generate_greedy([prompt], 16)
+    orc = Oracle(shape, qm, mode="bf16").generate(prompt, 16)
+    got = res.generated[0]
+    # identical up to the first step whose oracle margin is not decisive
+    gate = bar_for("tiny")[1]
+    for k in range(16):
+        if orc["margin"][k] <= gate:
+            break
+        assert got[k] == orc["ids"][k], f"step {k}"
+    assert res.token_ids[0][:16] == list(prompt)
+    assert res.steps == 15 and res.decode_us > 0 and res.prefill_us > 0
+
+
+def test_generate_repeat_is_deterministic(tiny_setup):
+    shape, w, qm, m = tiny_setup
+    prompt = make_prompt(shape.vocab, 20, 1002)
+    say("[gpu] generate twice, compare")
+    a = m.generate_greedy([prompt], 24).generated
+    b = m.generate_greedy([prompt], 24).generated
+    np.testing.assert_array_equal(a, b)
+
+
+def test_batched_ragged_generate_matches_single(tiny_setup):
+    """Each sequence's output is independent of the batch it runs in."""
+    shape, w, qm, m = tiny_setup
+    prompts = [make_prompt(shape.vocab, n, 1010 + i) for i, n in enumerate((16, 5, 33))]
+    say("[gpu] batched ragged B=3")
+    batched = m.generate_greedy(prompts, 12).generated
+    for i, p in enumerate(prompts):
+        single = m.generate_greedy([p], 12).generated[0]
+        orc = Oracle(shape, qm, mode="bf16").generate(p, 12)
+        for k in range(12):
+            if orc["margin"][k] <= bar_for("tiny")[1]:
+                break
+            assert batched[i, k] == orc["ids"][k] == single[k], (i, k)
+
+
+def test_batched_teacher_forced_logits():
+    """B=9 (two GEMV batch groups) teacher-forced against the oracle per sequence."""
+    shape = TINY
+    w = make_weights(shape, seed=2, gains="uniform")
+    qm = quantize_model(w)
+    B = 9
+    prompts = make_prompts(shape.vocab, 12, B, seed0=2000)
+    say("[gpu] batched teacher-forced B=9")
+    m = _model(shape, w, max_batch=B, max_ctx=64, max_prefill_tokens=B * 12)
+    try:
+        orcs = [Oracle(shape, qm, mode="bf16").generate(p, 6) for p in prompts]
+        nxt, lg = m.prefill(list(prompts), logits=True)
+        torch.cuda.synchronize()
+        for b in range(B):
+            check_step(lg[b].cpu().numpy(), nxt[b].item(), orcs[b]["logits"][0],
+                       orcs[b]["margin"][0], "tiny-b", f"b{b} prefill")
+        for k in range(1, 6):
+            feed = torch.tensor([o["ids"][k - 1] for o in orcs], dtype=torch.int32, device="cuda")
+            nxt, lg = m.decode_step(feed, logits=True)
+            torch.cuda.synchronize()
+            for b in range(B):
+                check_step(lg[b].cpu().numpy(), nxt[b].item(), orcs[b]["logits"][k],
+                           orcs[b]["margin"][k], "tiny-b", f"b{b} step {k}")
+    finally:
+        m.close()
+
+
+def test_error_paths_do_no_gpu_work(tiny_setup):
+    import int8_weight_only_amd as qd
+    shape, w, qm, m = tiny_setup
+    with pytest.raises(qd.QdError) as e:
+        m.generate_greedy([np.array([], np.int32)], 4)
+    assert e.value.code == "invalid_arguments"
+    with pytest.raises(qd.QdError) as e:
+        m.generate_greedy([np.array([shape.vocab], np.int32)], 4)
+    assert e.value.code == "invalid_arguments"
+    with pytest.raises(qd.QdError) as e:
+        m.generate_greedy([np.array([1, 2], np.int32)], 0)
+    assert e.value.code == "invalid_arguments"
+    with pytest.raises(qd.QdError) as e:
+        m.generate_greedy([np.array([1, 2], np.int32)], 200)  # past max_ctx 128
+    assert e.value.code == "invalid_arguments"
+    with pytest.raises(qd.QdError) as e:
+        m.generate_greedy([np.array([1, 2], np.int32)] * 5, 4)  # past max_batch
+    assert e.value.code == "invalid_arguments"
+    bad = {"embed": w["embed"], "final_norm": w["final_norm"],
+           "layers": [dict(L) for L in w["layers"]]}
+    bad["layers"][1]["down"] = None
+    with pytest.raises(qd.QdError) as e:
+        qd.Model(shape, bad, max_batch=1, max_ctx=32, max_prefill_tokens=32)
+    assert e.value.code == "checkpoint_not_found" and "layers.1.down_proj" in str(e.value)
