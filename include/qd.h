@@ -72,7 +72,7 @@ typedef enum {
  *   n_heads % n_kv_heads == 0; hidden, intermediate and n_heads*head_dim each a
  *   multiple of 32; tie_word_embeddings != 0; attention_bias == 0.
  * Gates this library adds for its kernels: every size > 0; head_dim a power of
- * two in [16, 256]; vocab >= 2; n_heads / n_kv_heads <= 8. */
+ * two in [32, 256]; vocab >= 2; n_heads / n_kv_heads <= 8. */
 typedef struct {
   int32_t hidden;        /* hidden_size */
   int32_t n_layers;      /* num_hidden_layers */
@@ -215,6 +215,16 @@ typedef enum {
  * read); positions and generated ids are left unchanged.  Synchronizes the stream. */
 qd_status qd_profile_kernels(qd_model* m, int32_t B, int32_t iters, float* us_out,
                              qd_stream stream);
+
+/* Launch-policy knobs (performance only; results stay within the parity bar). */
+typedef enum {
+  QD_TUNE_ATTN_MAX_SPLITS = 0,    /* most position splits per (sequence, KV head); default 64 */
+  QD_TUNE_ATTN_MIN_CHUNKS = 1,    /* fewest 64-position chunks per split; default 1 */
+} qd_tune_knob;
+
+/* Sets a knob; captured decode graphs are dropped so the next call re-captures.
+ * QD_ERR_INVALID_ARGUMENTS for an unknown knob or a value < 1. */
+qd_status qd_set_tuning(qd_model* m, int32_t knob, int32_t value);
 
 /* Frees host state and graphs.  Caller buffers remain the caller's. */
 void qd_free(qd_model* m);

@@ -87,7 +87,8 @@ class StatsC(ctypes.Structure):
 
 EXPORTS = ("qd_last_error", "qd_check_shape", "qd_query_sizes", "qd_load_weights",
            "qd_export_quantized", "qd_prefill", "qd_decode_step", "qd_generate_greedy",
-           "qd_free", "qd_profile_kernels")
+           "qd_free", "qd_profile_kernels", "qd_set_tuning")
+TUNING = {"attn_max_splits": 0, "attn_min_chunks": 1}
 PROF_KERNELS = ("embed", "qkv", "attn", "o", "gateup", "down", "lmhead")
 
 _lib = None
@@ -124,6 +125,8 @@ def load_library(path: str = LIB_PATH):
                                        ctypes.POINTER(StatsC), vp]
     lib.qd_profile_kernels.restype = i32
     lib.qd_profile_kernels.argtypes = [vp, i32, i32, vp, vp]
+    lib.qd_set_tuning.restype = i32
+    lib.qd_set_tuning.argtypes = [vp, i32, i32]
     lib.qd_free.restype = None
     lib.qd_free.argtypes = [vp]
     _lib = lib
@@ -279,6 +282,11 @@ class Model:
                                    lg.data_ptr() if lg is not None else None, nxt.data_ptr(),
                                    _stream_handle()))
         return nxt, lg
+
+    def set_tuning(self, **knobs):
+        """Launch-policy knobs, e.g. attn_max_splits=8 (performance only)."""
+        for k, v in knobs.items():
+            _check(_lib.qd_set_tuning(self._h, TUNING[k], int(v)))
 
     def profile_kernels(self, B: int, iters: int = 50) -> dict:
         """Mean microseconds per launch of each decode-step kernel class (HIP events)."""

@@ -95,8 +95,8 @@ std::string gate_problems(const qd_model_shape* s) {
   // gates of this library's kernels
   if (sizes_ok) {
     const int D = s->head_dim;
-    if (D < 16 || D > 256 || (D & (D - 1)) != 0)
-      add("head_dim " + std::to_string(D) + " must be a power of two in [16, 256] (kernel limit)");
+    if (D < 32 || D > 256 || (D & (D - 1)) != 0)
+      add("head_dim " + std::to_string(D) + " must be a power of two in [32, 256] (kernel limit)");
     if (s->vocab < 2) add("vocab_size must be >= 2");
     if (s->n_kv_heads > 0 && s->n_heads % s->n_kv_heads == 0 && s->n_heads / s->n_kv_heads > 8)
       add("num_attention_heads / num_key_value_heads > 8 (kernel limit)");
@@ -207,6 +207,8 @@ struct qd_model {
   std::map<std::tuple<int, int, int>, hipGraphExec_t> graphs;  // (B, nsplit, split_len)
   std::vector<int> host_pos;                                   // mirror of device positions
   hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+  int attn_max_splits = 64;
+  int attn_min_chunks = 1;
 
   template <class T> T* w(size_t off) { return reinterpret_cast<T*>(W + off); }
   template <class T> T* ws(size_t off) { return reinterpret_cast<T*>(WS + off); }
@@ -225,62 +227,89 @@ namespace {
 
 // attention split over positions 0..ctx-1: depends on the context only, so a sequence's
 // result does not depend on the batch it runs in
-void attn_split(int ctx, int cap, int* nsplit, int* split_len) {
+// work-groups in flight are capped near one per CU: more splits only add merge traffic
+void attn_split(int ctx, int cap, int max_splits, int min_chunks, int rows_x_kv, int* nsplit,
+                int* split_len) {
   const int chunks = std::max(1, (ctx + ATT_CHUNK - 1) / ATT_CHUNK);
-  const int want = std::max(1, std::min(chunks, std::min(cap, 64)));
+  max_splits = std::min(max_splits, std::max(1, 256 / std::max(1, rows_x_kv)));
+  int want = std::max(1, std::min(std::min(chunks, cap), max_splits));
+  want = std::max(1, std::min(want, chunks / std::max(1, min_chunks)));
   const int per = (chunks + want - 1) / want;
   *split_len = per * ATT_CHUNK;
   *nsplit = (chunks + per - 1) / per;
 }
 
-// LM head + fused arg-max over batch rows [b0, b0+nb)
-qd_status enqueue_lm_head(qd_model* m, const bf16_t* x, const int* x_rows, int B, float* logits,
-                          int* next_ids, bool bump_pos, bool write_out, hipStream_t st) {
+// LM head + fused arg-max.  One row: the register GEMV normalizes in its prologue.
+// Several rows: the rows are RMS-normalized into the h buffer (rows_total rows of x,
+// gathered through x_rows when given) and one MFMA sweep of the embedding serves all.
+qd_status enqueue_lm_head(qd_model* m, const bf16_t* x, const int* x_rows, int rows_total, int B,
+                          float* logits, int* next_ids, bool bump_pos, bool write_out,
+                          hipStream_t st) {
   const Dims& d = m->d;
-  for (int b0 = 0; b0 < B; b0 += 8) {
-    GemvArgs a{};
-    a.x = x_rows ? x : x + (size_t)b0 * d.d;
+  GemvArgs a{};
+  a.W = m->w<int8_t>(m->P.emb_q);
+  a.scale = m->w<float>(m->P.emb_s);
+  a.N = d.V;
+  a.K = d.d;
+  a.nb = B;
+  a.logits = logits;
+  a.ldl = d.V;
+  a.part_keys = m->ws<unsigned long long>(m->P.lm_keys);
+  a.done = m->ws<unsigned int>(m->P.done);
+  a.next_ids = next_ids;
+  a.pos = bump_pos ? m->ws<int>(m->P.pos) : nullptr;
+  a.out_ids = write_out ? m->ws<int>(m->P.out_ids) : nullptr;
+  a.out_ld = m->lim.max_ctx;
+  a.step = m->ws<int>(m->P.step);
+  a.bump_step = write_out ? 1 : 0;
+  a.batch0 = 0;
+  if (B == 1) {
+    a.x = x;
     a.ldx = d.d;
-    a.x_rows = x_rows ? x_rows + b0 : nullptr;
+    a.x_rows = x_rows;
     a.gain = m->w<float>(m->P.final_g);
     a.eps = m->shape.rms_eps;
-    a.W = m->w<int8_t>(m->P.emb_q);
-    a.scale = m->w<float>(m->P.emb_s);
-    a.N = d.V;
-    a.K = d.d;
-    a.nb = std::min(8, B - b0);
-    a.logits = logits ? logits + (size_t)b0 * d.V : nullptr;
-    a.ldl = d.V;
-    a.part_keys = m->ws<unsigned long long>(m->P.lm_keys) + (size_t)b0 * LM_MAX_GRID;
-    a.done = m->ws<unsigned int>(m->P.done);
-    a.next_ids = next_ids + b0;
-    a.pos = bump_pos ? m->ws<int>(m->P.pos) + b0 : nullptr;
-    a.out_ids = write_out ? m->ws<int>(m->P.out_ids) : nullptr;
-    a.out_ld = m->lim.max_ctx;
-    a.step = m->ws<int>(m->P.step);
-    a.bump_step = (write_out && b0 + 8 >= B) ? 1 : 0;
-    a.batch0 = b0;
     HIPCHK(launch_gemv(a, EPI_LOGITS, st));
+  } else {
+    bf16_t* h = m->ws<bf16_t>(m->P.h);
+    HIPCHK(launch_rmsnorm(x, rows_total, d.d, m->w<float>(m->P.final_g), m->shape.rms_eps, h, st));
+    a.x = h;
+    a.ldx = d.d;
+    a.x_rows = x_rows;
+    HIPCHK(launch_skinny(a, EPI_LOGITS, st));
   }
   return QD_OK;
 }
 
 // ---- the kernels of one decode step, for slots 0..B-1 (rows == slots) -------------------
+// one projection for B rows: B == 1 runs the register GEMV (RMSNorm in its prologue when
+// gain is set); B >= 2 normalizes into h first and runs the MFMA skinny GEMM
+qd_status dec_proj(qd_model* m, int B, const bf16_t* x, int ldx, const float* gain,
+                   const int8_t* W, const float* scale, int N, int K, int epi, bf16_t* out,
+                   int ldo, hipStream_t st) {
+  GemvArgs a{};
+  a.W = W; a.scale = scale; a.N = N; a.K = K; a.nb = B; a.out = out; a.ldo = ldo;
+  if (B == 1) {
+    a.x = x; a.ldx = ldx; a.gain = gain; a.eps = m->shape.rms_eps;
+    HIPCHK(launch_gemv(a, epi, st));
+    return QD_OK;
+  }
+  if (gain) {
+    bf16_t* h = m->ws<bf16_t>(m->P.h);
+    HIPCHK(launch_rmsnorm(x, B, K, gain, m->shape.rms_eps, h, st));
+    x = h;
+    ldx = K;
+  }
+  a.x = x; a.ldx = ldx;
+  HIPCHK(launch_skinny(a, epi, st));
+  return QD_OK;
+}
+
 qd_status dec_qkv(qd_model* m, int l, int B, hipStream_t st) {
   const Dims& d = m->d;
   const LayerOff& o = m->P.L[l];
-  bf16_t* x = m->ws<bf16_t>(m->P.x);
-  bf16_t* qkv = m->ws<bf16_t>(m->P.qkv);
-  for (int b0 = 0; b0 < B; b0 += 8) {
-    GemvArgs a{};
-    a.x = x + (size_t)b0 * d.d; a.ldx = d.d;
-    a.gain = m->w<float>(o.in_g); a.eps = m->shape.rms_eps;
-    a.W = m->w<int8_t>(o.qkv_q); a.scale = m->w<float>(o.qkv_s);
-    a.N = d.NQKV; a.K = d.d; a.nb = std::min(8, B - b0);
-    a.out = qkv + (size_t)b0 * d.NQKV; a.ldo = d.NQKV;
-    HIPCHK(launch_gemv(a, EPI_STORE, st));
-  }
-  return QD_OK;
+  return dec_proj(m, B, m->ws<bf16_t>(m->P.x), d.d, m->w<float>(o.in_g), m->w<int8_t>(o.qkv_q),
+                  m->w<float>(o.qkv_s), d.NQKV, d.d, EPI_STORE, m->ws<bf16_t>(m->P.qkv), d.NQKV, st);
 }
 
 qd_status dec_attn(qd_model* m, int l, int B, int nsplit, int split_len, hipStream_t st) {
@@ -304,50 +333,22 @@ qd_status dec_attn(qd_model* m, int l, int B, int nsplit, int split_len, hipStre
 qd_status dec_o(qd_model* m, int l, int B, hipStream_t st) {
   const Dims& d = m->d;
   const LayerOff& o = m->P.L[l];
-  bf16_t* attn = m->ws<bf16_t>(m->P.attn);
-  bf16_t* x = m->ws<bf16_t>(m->P.x);
-  for (int b0 = 0; b0 < B; b0 += 8) {
-    GemvArgs a{};
-    a.x = attn + (size_t)b0 * d.HD; a.ldx = d.HD;
-    a.W = m->w<int8_t>(o.o_q); a.scale = m->w<float>(o.o_s);
-    a.N = d.d; a.K = d.HD; a.nb = std::min(8, B - b0);
-    a.out = x + (size_t)b0 * d.d; a.ldo = d.d;
-    HIPCHK(launch_gemv(a, EPI_RESID, st));
-  }
-  return QD_OK;
+  return dec_proj(m, B, m->ws<bf16_t>(m->P.attn), d.HD, nullptr, m->w<int8_t>(o.o_q),
+                  m->w<float>(o.o_s), d.d, d.HD, EPI_RESID, m->ws<bf16_t>(m->P.x), d.d, st);
 }
 
 qd_status dec_gateup(qd_model* m, int l, int B, hipStream_t st) {
   const Dims& d = m->d;
   const LayerOff& o = m->P.L[l];
-  bf16_t* x = m->ws<bf16_t>(m->P.x);
-  bf16_t* act = m->ws<bf16_t>(m->P.act);
-  for (int b0 = 0; b0 < B; b0 += 8) {
-    GemvArgs a{};
-    a.x = x + (size_t)b0 * d.d; a.ldx = d.d;
-    a.gain = m->w<float>(o.post_g); a.eps = m->shape.rms_eps;
-    a.W = m->w<int8_t>(o.gu_q); a.scale = m->w<float>(o.gu_s);
-    a.N = 2 * d.I; a.K = d.d; a.nb = std::min(8, B - b0);
-    a.out = act + (size_t)b0 * d.I; a.ldo = d.I;
-    HIPCHK(launch_gemv(a, EPI_SILU, st));
-  }
-  return QD_OK;
+  return dec_proj(m, B, m->ws<bf16_t>(m->P.x), d.d, m->w<float>(o.post_g), m->w<int8_t>(o.gu_q),
+                  m->w<float>(o.gu_s), 2 * d.I, d.d, EPI_SILU, m->ws<bf16_t>(m->P.act), d.I, st);
 }
 
 qd_status dec_down(qd_model* m, int l, int B, hipStream_t st) {
   const Dims& d = m->d;
   const LayerOff& o = m->P.L[l];
-  bf16_t* act = m->ws<bf16_t>(m->P.act);
-  bf16_t* x = m->ws<bf16_t>(m->P.x);
-  for (int b0 = 0; b0 < B; b0 += 8) {
-    GemvArgs a{};
-    a.x = act + (size_t)b0 * d.I; a.ldx = d.I;
-    a.W = m->w<int8_t>(o.dn_q); a.scale = m->w<float>(o.dn_s);
-    a.N = d.d; a.K = d.I; a.nb = std::min(8, B - b0);
-    a.out = x + (size_t)b0 * d.d; a.ldo = d.d;
-    HIPCHK(launch_gemv(a, EPI_RESID, st));
-  }
-  return QD_OK;
+  return dec_proj(m, B, m->ws<bf16_t>(m->P.act), d.I, nullptr, m->w<int8_t>(o.dn_q),
+                  m->w<float>(o.dn_s), d.d, d.I, EPI_RESID, m->ws<bf16_t>(m->P.x), d.d, st);
 }
 
 #define QDCHK(expr)                   \
@@ -369,7 +370,7 @@ qd_status enqueue_decode(qd_model* m, int B, const int* in_ids, float* logits, i
     QDCHK(dec_gateup(m, l, B, st));
     QDCHK(dec_down(m, l, B, st));
   }
-  return enqueue_lm_head(m, m->ws<bf16_t>(m->P.x), nullptr, B, logits, next_ids, true,
+  return enqueue_lm_head(m, m->ws<bf16_t>(m->P.x), nullptr, B, B, logits, next_ids, true,
                          write_out, st);
 }
 
@@ -442,7 +443,7 @@ qd_status enqueue_prefill(qd_model* m, int n, const int* ids_dev, const std::vec
     g.M = M; g.N = d.d; g.K = d.I; g.epi = EPI_RESID; g.out = x; g.ldo = d.d;
     HIPCHK(launch_gemm(g, st));
   }
-  qd_status s = enqueue_lm_head(m, x, last_rows, n, logits, next_ids, false, write_out, st);
+  qd_status s = enqueue_lm_head(m, x, last_rows, M, n, logits, next_ids, false, write_out, st);
   if (s != QD_OK) return s;
   HIPCHK(launch_set_positions(m->ws<int>(P.pos), dlens, n, st));
   return QD_OK;
@@ -673,7 +674,7 @@ qd_status qd_decode_step(qd_model* m, int32_t B, const int32_t* in_ids_dev, floa
     ctx = std::max(ctx, m->host_pos[b] + 1);
   }
   int nsplit, split_len;
-  attn_split(ctx, m->P.nsplit_cap, &nsplit, &split_len);
+  attn_split(ctx, m->P.nsplit_cap, m->attn_max_splits, m->attn_min_chunks, B * m->d.KV, &nsplit, &split_len);
   qd_status s = enqueue_decode(m, B, in_ids_dev, logits_dev, next_ids_dev, false, nsplit,
                                split_len, (hipStream_t)stream);
   if (s == QD_OK)
@@ -726,7 +727,7 @@ qd_status qd_generate_greedy(qd_model* m, int32_t B, const int32_t* prompt_ids_h
     int nsplit, split_len;
     // round the context up so one captured graph serves many calls
     const int ctx_cap = std::min(m->lim.max_ctx, ((need + 255) / 256) * 256);
-    attn_split(ctx_cap, P.nsplit_cap, &nsplit, &split_len);
+    attn_split(ctx_cap, P.nsplit_cap, m->attn_max_splits, m->attn_min_chunks, B * m->d.KV, &nsplit, &split_len);
     auto key = std::make_tuple(B, nsplit, split_len);
     auto it = m->graphs.find(key);
     hipGraphExec_t exec = nullptr;
@@ -787,7 +788,7 @@ qd_status qd_profile_kernels(qd_model* m, int32_t B, int32_t iters, float* us_ou
     ctx = std::max(ctx, m->host_pos[b] + 1);
   }
   int nsplit, split_len;
-  attn_split(ctx, m->P.nsplit_cap, &nsplit, &split_len);
+  attn_split(ctx, m->P.nsplit_cap, m->attn_max_splits, m->attn_min_chunks, B * m->d.KV, &nsplit, &split_len);
   hipStream_t st = (hipStream_t)stream;
   int* scratch_ids = m->ws<int>(m->P.ids);   // prompt-id area doubles as the profiling id list
   HIPCHK(launch_fill_i32(scratch_ids, B, 0, st));
@@ -809,7 +810,7 @@ qd_status qd_profile_kernels(qd_model* m, int32_t B, int32_t iters, float* us_ou
           case QD_PROF_GATEUP: QDCHK(dec_gateup(m, 0, B, st)); break;
           case QD_PROF_DOWN: QDCHK(dec_down(m, 0, B, st)); break;
           default:
-            QDCHK(enqueue_lm_head(m, m->ws<bf16_t>(m->P.x), nullptr, B, nullptr, scratch_next,
+            QDCHK(enqueue_lm_head(m, m->ws<bf16_t>(m->P.x), nullptr, B, B, nullptr, scratch_next,
                                   false, false, st));
         }
       }
@@ -820,6 +821,20 @@ qd_status qd_profile_kernels(qd_model* m, int32_t B, int32_t iters, float* us_ou
     HIPCHK(hipEventElapsedTime(&ms, m->ev[0], m->ev[1]));
     us_out[k] = ms * 1e3f / iters;
   }
+  return QD_OK;
+}
+
+qd_status qd_set_tuning(qd_model* m, int32_t knob, int32_t value) {
+  g_err.clear();
+  if (!m) return fail(QD_ERR_INVALID_ARGUMENTS, "model is NULL");
+  if (value < 1) return fail(QD_ERR_INVALID_ARGUMENTS, "value must be >= 1");
+  switch (knob) {
+    case QD_TUNE_ATTN_MAX_SPLITS: m->attn_max_splits = value; break;
+    case QD_TUNE_ATTN_MIN_CHUNKS: m->attn_min_chunks = value; break;
+    default: return fail(QD_ERR_INVALID_ARGUMENTS, "unknown knob");
+  }
+  for (auto& kv : m->graphs) (void)hipGraphExecDestroy(kv.second);
+  m->graphs.clear();
   return QD_OK;
 }
 

@@ -32,7 +32,7 @@ struct GemvArgs {
   const int8_t* W;      // [N][K] int8 codes (rows possibly gate/up interleaved)
   const float* scale;   // [N]
   int N, K;
-  int nb;               // batch rows in this launch (1..8)
+  int nb;               // batch rows in this launch (GEMV 1..8, skinny MFMA 1..64)
   bf16_t* out; int ldo; // EPI_STORE/EPI_SILU: output; EPI_RESID: residual updated in place
   // EPI_LOGITS
   float* logits; int ldl;            // optional fp32 logits [nb][ldl]
@@ -105,6 +105,7 @@ hipError_t launch_embed(const int* ids, int M, const int8_t* E, const float* Es,
 hipError_t launch_rmsnorm(const bf16_t* x, int M, int d, const float* g, float eps, bf16_t* y,
                           hipStream_t st);
 hipError_t launch_gemv(const GemvArgs& a, int epi, hipStream_t st);
+hipError_t launch_skinny(const GemvArgs& a, int epi, hipStream_t st);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
 hipError_t launch_qk_rope(const RopeArgs& a, hipStream_t st);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st);

@@ -23,15 +23,32 @@ __device__ __forceinline__ bf16_t f2bf(float f) {
 }
 __device__ __forceinline__ float rbf(float f) { return bf2f(f2bf(f)); }
 
+// wave64 reductions on DPP: quad swaps, half-row and row mirrors give every lane its
+// 16-lane row total; two row broadcasts fold the four rows into lane 63, which is read
+// back as a wave-uniform value
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_f(float old, float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old),
+                                                               __builtin_bit_cast(int, v), CTRL,
+                                                               ROW_MASK, 0xf, false));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v += dpp_f<0xB1>(0.0f, v);        // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(0.0f, v);        // quad_perm [2,3,0,1]
+  v += dpp_f<0x141>(0.0f, v);       // row_half_mirror
+  v += dpp_f<0x140>(0.0f, v);       // row_mirror
+  v += dpp_f<0x142, 0xa>(0.0f, v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_f<0x143, 0xc>(0.0f, v);  // row_bcast:31 into rows 2 and 3
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = fmaxf(v, dpp_f<0xB1>(v, v));
+  v = fmaxf(v, dpp_f<0x4E>(v, v));
+  v = fmaxf(v, dpp_f<0x141>(v, v));
+  v = fmaxf(v, dpp_f<0x140>(v, v));
+  v = fmaxf(v, dpp_f<0x142, 0xa>(v, v));
+  v = fmaxf(v, dpp_f<0x143, 0xc>(v, v));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
 // 256-thread block reductions through LDS
@@ -642,6 +659,131 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
+// batched decode GEMM on MFMA ("skinny": 2..64 token rows, weights swept once):
+// Y[t][n] = scale[n] * sum_k X[t][k] * W[n][k], X bf16 (already RMS-normalized where the
+// model normalizes), W int8 converted exactly to bf16 in registers.  The MFMA A operand is
+// a 16-channel x 32-k slice of W, the B operand a 32-k x 16-token slice of X^T.  A
+// work-group owns CTW 16-channel tiles; its four waves take interleaved 128-k blocks
+// (each lane group streams 128 contiguous bytes of a weight row) and the partial sums
+// meet in LDS.  The k order inside a block is permuted identically for both operands.
+template <int TT, int EPI>
+__global__ __launch_bounds__(256) void k_skinny(GemvArgs a) {
+  constexpr int CTW = (EPI == EPI_SILU) ? 2 : 1;
+  constexpr int NACC = CTW * TT;
+  __shared__ float red[4][NACC][4][64];
+  __shared__ unsigned long long kl[TT * 16][16];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int K = a.K;
+  const int grp = lane >> 4, r16 = lane & 15;
+  const int ntiles = (a.N + 16 * CTW - 1) / (16 * CTW);
+  unsigned long long best = 0ull;  // LOGITS: running best key of token tid (tid < 16*TT)
+
+  // token rows of this lane's B operand, one per token tile
+  const bf16_t* xrow[TT];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) {
+    int tok = tt * 16 + r16;
+    tok = tok < a.nb ? tok : a.nb - 1;
+    const int xr = a.x_rows ? a.x_rows[tok] : tok;
+    xrow[tt] = a.x + (size_t)xr * a.ldx;
+  }
+
+  for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    f32x4_t acc[CTW][TT];
+#pragma unroll
+    for (int c = 0; c < CTW; ++c)
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) acc[c][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int* wrow[CTW];
+    bool wok[CTW];
+#pragma unroll
+    for (int c = 0; c < CTW; ++c) {
+      const int ch = tile * 16 * CTW + c * 16 + r16;
+      wok[c] = ch < a.N;
+      wrow[c] = reinterpret_cast<const int*>(a.W + (size_t)(wok[c] ? ch : 0) * K);
+    }
+    for (int kb = 128 * wid; kb < K; kb += 512) {
+      const int k0 = kb + 32 * grp;
+      const bool kok = k0 < K;
+      uint4 wv[CTW][2];
+#pragma unroll
+      for (int c = 0; c < CTW; ++c) {
+        const uint4* src = reinterpret_cast<const uint4*>(wrow[c] + k0 / 4);
+        wv[c][0] = (kok && wok[c]) ? src[0] : make_uint4(0, 0, 0, 0);
+        wv[c][1] = (kok && wok[c]) ? src[1] : make_uint4(0, 0, 0, 0);
+      }
+      uint4 xv[TT][4];
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) {
+        const uint4* src = reinterpret_cast<const uint4*>(xrow[tt] + k0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) xv[tt][q] = kok ? src[q] : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int c = 0; c < CTW; ++c) {
+          const uint4 w16 = wv[c][j >> 1];
+          const uint2 w8 = (j & 1) ? make_uint2(w16.z, w16.w) : make_uint2(w16.x, w16.y);
+          const bf16x8_t af = i8x8_to_bf16x8(w8);
+#pragma unroll
+          for (int tt = 0; tt < TT; ++tt)
+            acc[c][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                af, __builtin_bit_cast(bf16x8_t, xv[tt][j]), acc[c][tt], 0, 0, 0);
+        }
+      }
+    }
+    // partial sums of the four waves meet in LDS
+#pragma unroll
+    for (int c = 0; c < CTW; ++c)
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[wid][c * TT + tt][i][lane] = acc[c][tt][i];
+    __syncthreads();
+    // element (tt, i, l): channel tile*16*CTW + c*16 + 4*(l/16) + i, token tt*16 + l%16
+    for (int e = tid; e < TT * 4 * 64; e += 256) {
+      const int tt = e / 256, i = (e / 64) % 4, l = e % 64;
+      const int tok = tt * 16 + (l & 15);
+      float v[CTW];
+#pragma unroll
+      for (int c = 0; c < CTW; ++c)
+        v[c] = red[0][c * TT + tt][i][l] + red[1][c * TT + tt][i][l] + red[2][c * TT + tt][i][l] +
+               red[3][c * TT + tt][i][l];
+      const int ch = tile * 16 * CTW + 4 * (l >> 4) + i;
+      if (EPI == EPI_SILU) {
+        if (tok < a.nb && ch + 16 < a.N) {
+          const float g = rbf(v[0] * a.scale[ch]), u = rbf(v[1] * a.scale[ch + 16]);
+          const int j = tile * GU_BLOCK + 4 * (l >> 4) + i;
+          a.out[(size_t)tok * a.ldo + j] = f2bf(g / (1.0f + expf(-g)) * u);
+        }
+      } else if (EPI == EPI_LOGITS) {
+        unsigned long long k = 0ull;
+        if (tok < a.nb && ch < a.N) {
+          const float lv = v[0] * a.scale[ch];
+          if (a.logits) a.logits[(size_t)tok * a.ldl + ch] = lv;
+          k = argmax_key(lv, ch);
+        }
+        kl[tok][4 * (l >> 4) + i] = k;
+      } else if (tok < a.nb && ch < a.N) {
+        const float y = v[0] * a.scale[ch];
+        bf16_t* o = a.out + (size_t)tok * a.ldo + ch;
+        *o = (EPI == EPI_STORE) ? f2bf(y) : f2bf(bf2f(*o) + rbf(y));
+      }
+    }
+    if (EPI == EPI_LOGITS) {
+      __syncthreads();
+      if (tid < TT * 16) {
+#pragma unroll
+        for (int c = 0; c < 16; ++c) best = kl[tid][c] > best ? kl[tid][c] : best;
+      }
+    }
+    __syncthreads();
+  }
+  if (EPI == EPI_LOGITS) lm_head_finish(a, best, 64);
+}
+
+// ------------------------------------------------------------------------------------------
 // QK-norm + RoPE + KV-cache write, one work-group per token row.
 // q and k heads: RMSNorm over head_dim with a shared gain, then rotate-half RoPE at
 // the row's position; q is written back in place, k and v go to the cache.
@@ -826,20 +968,26 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
 // Fused in front: RMSNorm (shared [D] gain) and rotate-half RoPE at position p of the
 // group's G query heads and of its key head, done in LDS from the raw projections; the
 // split that holds position p writes the new K and V rows to the cache and every split
-// uses the fresh rows for p from LDS.  Fused behind: with several splits, each writes
-// its partial (max, sum, unnormalized output); the split that finishes last merges them.
+// uses the fresh rows for p from LDS.  Each wave owns 16 positions of every 64-position
+// chunk and keeps its own online-softmax state (no block barrier inside the loop); K and
+// V tiles are requested one chunk ahead, the first ones before the prologue.  The four
+// waves merge in LDS at the end.  Fused behind: with several splits, each writes its
+// partial (max, sum, unnormalized output); the split that finishes last merges them.
 template <int D, int G>
 __global__ __launch_bounds__(256) void k_attn_dec(AttnDecArgs a) {
-  constexpr int CH = ATT_CHUNK;
   constexpr int HALF = D / 2;
-  constexpr int NG = 256 / HALF;
-  __shared__ float qs[G][D];
+  constexpr int KQ = D / 4;                    // key elements per lane (4 lanes per position)
+  constexpr int KV4 = KQ / 8;                  // uint4 loads per lane per key row
+  constexpr int DPL = D >= 64 ? D / 64 : 1;    // output dims per lane
+  constexpr int VW = DPL >= 2 ? DPL / 2 : 1;   // 32-bit words of V per lane per row
+  __shared__ __align__(16) float qs[G][D];
   __shared__ float kn[D], vn[D];
-  __shared__ float sc[G][CH];
-  __shared__ float ored[NG][G][D];
+  __shared__ float wm[4][G], wl[4][G];
+  __shared__ float wo[4][G][D];
   __shared__ int last_flag;
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tl = lane >> 2, part = lane & 3;
   const int p = a.pos[b];
   const int n = p + 1;
   const int t_begin = s * a.split_len;
@@ -849,6 +997,33 @@ __global__ __launch_bounds__(256) void k_attn_dec(AttnDecArgs a) {
   bf16_t* Kb = a.kcache + ((size_t)b * a.KV + g) * a.max_ctx * D;
   bf16_t* Vb = a.vcache + ((size_t)b * a.KV + g) * a.max_ctx * D;
   const bool owner = (t_begin <= p) && (p < t_begin + a.split_len);
+  const bool vlane = (D >= 64) || (lane < D);
+
+  // ---- K/V tiles of the first chunk, requested before anything else ----
+  uint4 kc[KV4], kx[KV4];
+  uint32_t vc[16][VW], vx[16][VW];
+  auto load_tiles = [&](uint4 (&kk)[KV4], uint32_t (&vv)[16][VW], int t0) {
+    const int t = t0 + 16 * wid + tl;
+#pragma unroll
+    for (int j = 0; j < KV4; ++j)
+      kk[j] = (t < t_end && t != p)
+                         ? *reinterpret_cast<const uint4*>(Kb + (size_t)t * D + part * KQ + 8 * j)
+                         : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int tv = t0 + 16 * wid + i;
+      const bool ok = tv < t_end && tv != p && vlane;
+#pragma unroll
+      for (int w = 0; w < VW; ++w) {
+        if (DPL >= 2) {
+          vv[i][w] = ok ? *reinterpret_cast<const uint32_t*>(Vb + (size_t)tv * D + DPL * lane + 2 * w) : 0u;
+        } else {
+          vv[i][w] = ok ? (uint32_t)Vb[(size_t)tv * D + lane] : 0u;
+        }
+      }
+    }
+  };
+  if (t_begin < t_end) load_tiles(kc, vc, t_begin);
 
   // ---- QK-norm + RoPE of the G query heads and the key head; copy of v ----
   for (int hh = wid; hh <= G; hh += 4) {
@@ -867,13 +1042,13 @@ __global__ __launch_bounds__(256) void k_attn_dec(AttnDecArgs a) {
       }
     }
     ss = wave_sum(ss);
-    const float denom = sqrtf(ss / (float)D + a.eps);
+    const float inv = 1.0f / sqrtf(ss / (float)D + a.eps);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int i = lane + 64 * j;
       if (i < HALF) {
-        const float y1 = rbf(x1[j] / denom * gn[i]);
-        const float y2 = rbf(x2[j] / denom * gn[i + HALF]);
+        const float y1 = rbf(x1[j] * inv * gn[i]);
+        const float y2 = rbf(x2[j] * inv * gn[i + HALF]);
         const float2 cs = tab[i];
         const bf16_t o1 = f2bf(y1 * cs.x - y2 * cs.y), o2 = f2bf(y2 * cs.x + y1 * cs.y);
         if (isq) {
@@ -901,119 +1076,129 @@ __global__ __launch_bounds__(256) void k_attn_dec(AttnDecArgs a) {
   __syncthreads();
 
   const float scale = 1.0f / sqrtf((float)D);
-  float m[G], l[G], o[G][2];
+  float m[G], l[G], o[G][DPL];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     m[h] = -INFINITY;
     l[h] = 0.0f;
-    o[h][0] = o[h][1] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) o[h][e] = 0.0f;
   }
-  const int dp = tid % HALF, grp = tid / HALF;
-  for (int t0 = t_begin; t0 < t_end; t0 += CH) {
-    {  // scores: 4 lanes per position
-      const int tl = tid >> 2, part = tid & 3;
-      const int t = t0 + tl;
-      float sp[G];
+  for (int t0 = t_begin; t0 < t_end; t0 += ATT_CHUNK) {
+    const int t = t0 + 16 * wid + tl;
+    // scores of this lane's position (4 lanes per position, KQ key elements each)
+    float sp[G];
 #pragma unroll
-      for (int h = 0; h < G; ++h) sp[h] = 0.0f;
-      if (t < t_end) {
-        if (t == p) {
+    for (int h = 0; h < G; ++h) sp[h] = 0.0f;
+    if (t == p) {
 #pragma unroll
-          for (int j = 0; j < D / 4; ++j) {
-            const float kv = kn[part * (D / 4) + j];
+      for (int j = 0; j < KQ; ++j) {
+        const float kv = kn[part * KQ + j];
 #pragma unroll
-            for (int h = 0; h < G; ++h) sp[h] += qs[h][part * (D / 4) + j] * kv;
-          }
-        } else {
-          const bf16_t* kr = Kb + (size_t)t * D + part * (D / 4);
+        for (int h = 0; h < G; ++h) sp[h] += qs[h][part * KQ + j] * kv;
+      }
+    } else {
 #pragma unroll
-          for (int j = 0; j < D / 4; j += 2) {
-            const uint32_t kk = *reinterpret_cast<const uint32_t*>(kr + j);
-            const float k0 = __uint_as_float(kk << 16), k1 = __uint_as_float(kk & 0xFFFF0000u);
+      for (int j = 0; j < KV4; ++j) {
+        const uint32_t w4[4] = {kc[j].x, kc[j].y, kc[j].z, kc[j].w};
 #pragma unroll
-            for (int h = 0; h < G; ++h)
-              sp[h] += qs[h][part * (D / 4) + j] * k0 + qs[h][part * (D / 4) + j + 1] * k1;
-          }
+        for (int e = 0; e < 4; ++e) {
+          const float k0 = __uint_as_float(w4[e] << 16), k1 = __uint_as_float(w4[e] & 0xFFFF0000u);
+          const int c = part * KQ + 8 * j + 2 * e;
+#pragma unroll
+          for (int h = 0; h < G; ++h) sp[h] += qs[h][c] * k0 + qs[h][c + 1] * k1;
         }
       }
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        sp[h] += __shfl_xor(sp[h], 1, 64);
-        sp[h] += __shfl_xor(sp[h], 2, 64);
-      }
-      if (part == 0) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) sc[h][tl] = (t < t_end) ? sp[h] * scale : -INFINITY;
-      }
     }
-    __syncthreads();
-    float mnew[G], alpha[G];
+    // next chunk's tiles go out before the softmax and P*V work of this one
+    const bool more = t0 + ATT_CHUNK < t_end;
+    if (more) load_tiles(kx, vx, t0 + ATT_CHUNK);
+    const bool valid = t < t_end;
+    float pr[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float cm = -INFINITY;
-      for (int t = 0; t < CH; ++t) cm = fmaxf(cm, sc[h][t]);
-      mnew[h] = fmaxf(m[h], cm);
-      alpha[h] = (m[h] == -INFINITY) ? 0.0f : expf(m[h] - mnew[h]);
-    }
-    __syncthreads();
-    if (tid < CH) {
+      sp[h] += __shfl_xor(sp[h], 1, 64);
+      sp[h] += __shfl_xor(sp[h], 2, 64);
+      const float z = valid ? sp[h] * scale : -INFINITY;
+      const float mnew = fmaxf(m[h], wave_max(z));
+      const float alpha = (m[h] == -INFINITY) ? 0.0f : expf(m[h] - mnew);
+      pr[h] = valid ? expf(z - mnew) : 0.0f;
+      l[h] = l[h] * alpha + wave_sum(part == 0 ? pr[h] : 0.0f);
+      m[h] = mnew;
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float v = sc[h][tid];
-        sc[h][tid] = (v == -INFINITY) ? 0.0f : expf(v - mnew[h]);
-      }
+      for (int e = 0; e < DPL; ++e) o[h][e] *= alpha;
     }
-    __syncthreads();
+    // P*V: lanes over head dims, the wave's 16 positions in turn
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float cs = 0.0f;
-      for (int t = 0; t < CH; ++t) cs += sc[h][t];
-      l[h] = l[h] * alpha[h] + cs;
-      m[h] = mnew[h];
-      o[h][0] *= alpha[h];
-      o[h][1] *= alpha[h];
-    }
-    for (int tl = grp; tl < CH; tl += NG) {
-      const int t = t0 + tl;
-      if (t >= t_end) break;
-      float v0, v1;
-      if (t == p) {
-        v0 = vn[2 * dp];
-        v1 = vn[2 * dp + 1];
+    for (int i = 0; i < 16; ++i) {
+      const int tv = t0 + 16 * wid + i;
+      float vf[DPL];
+      if (tv == p) {
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) vf[e] = vlane ? vn[DPL * lane + e] : 0.0f;
+      } else if (DPL >= 2) {
+#pragma unroll
+        for (int w = 0; w < VW; ++w) {
+          vf[2 * w] = __uint_as_float(vc[i][w] << 16);
+          vf[2 * w + 1] = __uint_as_float(vc[i][w] & 0xFFFF0000u);
+        }
       } else {
-        const uint32_t vv = *reinterpret_cast<const uint32_t*>(Vb + (size_t)t * D + 2 * dp);
-        v0 = __uint_as_float(vv << 16);
-        v1 = __uint_as_float(vv & 0xFFFF0000u);
+        vf[0] = __uint_as_float(vc[i][0] << 16);
       }
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float pw = sc[h][tl];
-        o[h][0] += pw * v0;
-        o[h][1] += pw * v1;
+        const float pw = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pr[h]), 4 * i));
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) o[h][e] += pw * vf[e];
       }
     }
-    __syncthreads();
-  }
+    if (more) {
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    ored[grp][h][2 * dp] = o[h][0];
-    ored[grp][h][2 * dp + 1] = o[h][1];
+      for (int j = 0; j < KV4; ++j) kc[j] = kx[j];
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+#pragma unroll
+        for (int w = 0; w < VW; ++w) vc[i][w] = vx[i][w];
+    }
+  }
+  // ---- merge the four waves' softmax states ----
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      wm[wid][h] = m[h];
+      wl[wid][h] = l[h];
+    }
+  }
+  if (vlane) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) wo[wid][h][DPL * lane + e] = o[h][e];
   }
   __syncthreads();
   for (int idx = tid; idx < G * D; idx += 256) {
     const int h = idx / D, dd = idx % D;
-    float acc = 0.0f;
+    float M = -INFINITY;
 #pragma unroll
-    for (int gg = 0; gg < NG; ++gg) acc += ored[gg][h][dd];
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, wm[w][h]);
+    float L = 0.0f, O = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      if (wm[w][h] == -INFINITY) continue;
+      const float f = expf(wm[w][h] - M);
+      L += wl[w][h] * f;
+      O += wo[w][h][dd] * f;
+    }
     const int head = g * G + h;
     if (a.nsplit == 1) {
-      a.out[(size_t)b * a.ldo + (size_t)head * D + dd] = f2bf(acc / l[h]);
+      a.out[(size_t)b * a.ldo + (size_t)head * D + dd] = f2bf(O / L);
     } else {
       const size_t pi = ((size_t)b * a.H + head) * a.nsplit + s;
-      a.part_o[pi * D + dd] = acc;
+      a.part_o[pi * D + dd] = O;
       if (dd == 0) {
-        a.part_ml[pi * 2] = m[h];
-        a.part_ml[pi * 2 + 1] = l[h];
+        a.part_ml[pi * 2] = M;
+        a.part_ml[pi * 2 + 1] = L;
       }
     }
   }
@@ -1163,7 +1348,8 @@ static hipError_t gemv1_r(const GemvArgs& a, int epi, hipStream_t st) {
 static hipError_t gemv1(const GemvArgs& a, int epi, hipStream_t st) {
   if (a.K > 8192) return hipErrorInvalidValue;
   const int nout = epi == EPI_SILU ? a.N / 2 : a.N;
-  if ((epi == EPI_LOGITS || nout >= 4096) && a.K <= 2048) return gemv1_r<4>(a, epi, st);
+  if ((epi == EPI_LOGITS || nout >= 4096) && a.K <= 2048)
+    return a.K <= 1024 ? gemv1_rk<4, 1>(a, epi, st) : gemv1_rk<4, 2>(a, epi, st);
   return gemv1_r<1>(a, epi, st);
 }
 
@@ -1194,6 +1380,28 @@ hipError_t launch_gemv(const GemvArgs& a, int epi, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+template <int TT>
+static hipError_t skinny_tt(const GemvArgs& a, int epi, hipStream_t st) {
+  const int ctw = epi == EPI_SILU ? 2 : 1;
+  const int ntiles = (a.N + 16 * ctw - 1) / (16 * ctw);
+  dim3 grid(epi == EPI_LOGITS ? (ntiles < LM_MAX_GRID ? ntiles : LM_MAX_GRID) : ntiles);
+  switch (epi) {
+    case EPI_STORE: hipLaunchKernelGGL((k_skinny<TT, EPI_STORE>), grid, dim3(256), 0, st, a); break;
+    case EPI_RESID: hipLaunchKernelGGL((k_skinny<TT, EPI_RESID>), grid, dim3(256), 0, st, a); break;
+    case EPI_SILU: hipLaunchKernelGGL((k_skinny<TT, EPI_SILU>), grid, dim3(256), 0, st, a); break;
+    default: hipLaunchKernelGGL((k_skinny<TT, EPI_LOGITS>), grid, dim3(256), 0, st, a); break;
+  }
+  return hipGetLastError();
+}
+
+// 2..64 token rows; activations must already be normalized (gain must be NULL)
+hipError_t launch_skinny(const GemvArgs& a, int epi, hipStream_t st) {
+  if (a.gain || a.nb < 1 || a.nb > 64 || (a.K & 31)) return hipErrorInvalidValue;
+  if (a.nb <= 16) return skinny_tt<1>(a, epi, st);
+  if (a.nb <= 32) return skinny_tt<2>(a, epi, st);
+  return skinny_tt<4>(a, epi, st);
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
@@ -1247,7 +1455,6 @@ hipError_t launch_attention_decode(const AttnDecArgs& a, hipStream_t st) {
   const int G = a.H / a.KV;
   if (G < 1 || G > 8 || a.nsplit < 1) return hipErrorInvalidValue;
   switch (a.D) {
-    case 16: return attn_dec_d<16>(a, G, st);
     case 32: return attn_dec_d<32>(a, G, st);
     case 64: return attn_dec_d<64>(a, G, st);
     case 128: return attn_dec_d<128>(a, G, st);
@@ -1260,7 +1467,6 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
   const int G = a.H / a.KV;
   hipError_t e;
   switch (a.D) {
-    case 16: e = attn_d<16>(a, G, st); break;
     case 32: e = attn_d<32>(a, G, st); break;
     case 64: e = attn_d<64>(a, G, st); break;
     case 128: e = attn_d<128>(a, G, st); break;

@@ -191,3 +191,28 @@ def test_error_paths_do_no_gpu_work(tiny_setup):
     with pytest.raises(qd.QdError) as e:
         qd.Model(shape, bad, max_batch=1, max_ctx=32, max_prefill_tokens=32)
     assert e.value.code == "checkpoint_not_found" and "layers.1.down_proj" in str(e.value)
+
+
+def test_large_batch_teacher_forced_logits():
+    """B=40 runs the skinny MFMA path with four 16-token tiles."""
+    shape = TINY
+    w = make_weights(shape, seed=2, gains="uniform")
+    qm = quantize_model(w)
+    B = 40
+    prompts = [make_prompt(shape.vocab, 5 + (b % 7), 3000 + b) for b in range(B)]
+    say("[gpu] batched teacher-forced B=40, ragged prompts")
+    m = _model(shape, w, max_batch=B, max_ctx=32, max_prefill_tokens=B * 12)
+    try:
+        orcs = [Oracle(shape, qm, mode="bf16").generate(p, 3) for p in prompts]
+        nxt, lg = m.prefill(prompts, logits=True)
+        torch.cuda.synchronize()
+        for k in range(3):
+            if k:
+                feed = torch.tensor([o["ids"][k - 1] for o in orcs], dtype=torch.int32, device="cuda")
+                nxt, lg = m.decode_step(feed, logits=True)
+                torch.cuda.synchronize()
+            for b in range(B):
+                check_step(lg[b].cpu().numpy(), nxt[b].item(), orcs[b]["logits"][k],
+                           orcs[b]["margin"][k], "tiny-b", f"b{b} step {k}")
+    finally:
+        m.close()
