@@ -208,9 +208,10 @@ typedef enum {
 } qd_prof_kernel;
 
 /* Measurement aid (not part of the forward pass): launches each decode-step kernel
- * class of layer 0 (and the LM head) `iters` times back to back for slots 0..B-1
- * at their current positions, bracketed by HIP events on `stream`, and writes the
- * mean microseconds per launch to us_out[QD_PROF_COUNT].  The residual and
+ * class `iters` times back to back for slots 0..B-1 at their current positions,
+ * cycling through the layers (so weights and KV rows come from memory as in a real
+ * step), bracketed by HIP events on `stream`, and writes the mean microseconds per
+ * launch to us_out[QD_PROF_COUNT] (the LM head and embedding have one instance).  The residual and
  * activation buffers are overwritten (run it after the outputs of interest are
  * read); positions and generated ids are left unchanged.  Synchronizes the stream. */
 qd_status qd_profile_kernels(qd_model* m, int32_t B, int32_t iters, float* us_out,

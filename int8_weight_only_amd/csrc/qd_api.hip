@@ -43,8 +43,9 @@ struct Plan {
   size_t weight_bytes = 0;
   // workspace
   size_t x = 0, h = 0, qkv = 0, attn = 0, act = 0, part_o = 0, part_ml = 0;
-  size_t ids = 0, row_slot = 0, row_pos = 0, last_rows = 0, lens = 0, slot_ident = 0;
+  size_t ids = 0, row_slot = 0, row_pos = 0, last_rows = 0, lens = 0, slot_ident = 0, tiles = 0;
   size_t pos = 0, next_ids = 0, lm_keys = 0, att_cnt = 0, done = 0, step = 0, out_ids = 0;
+  size_t gemm_part = 0;
   size_t ws_bytes = 0;
   size_t kv_bytes = 0;
   size_t kv_layer_elems = 0;  // bf16 elements of K (or V) per layer
@@ -168,6 +169,7 @@ Plan make_plan(const qd_model_shape& s, const qd_limits& lim) {
   P.row_slot = take((size_t)M * 4);
   P.row_pos = take((size_t)M * 4);
   P.last_rows = take((size_t)B * 4);
+  P.tiles = take((size_t)(M / FLASH_ROWS + B + 1) * 16);
   P.lens = take((size_t)B * 4);
   P.slot_ident = take((size_t)B * 4);
   P.pos = take((size_t)B * 4);
@@ -177,6 +179,7 @@ Plan make_plan(const qd_model_shape& s, const qd_limits& lim) {
   P.done = take(64);
   P.step = take(64);
   P.out_ids = take((size_t)B * lim.max_ctx * 4);
+  P.gemm_part = take(GEMM_PART_FLOATS * 4);
   P.ws_bytes = off;
 
   P.kv_layer_elems = (size_t)B * d.KV * lim.max_ctx * d.D;
@@ -380,8 +383,14 @@ qd_status enqueue_prefill(qd_model* m, int n, const int* ids_dev, const std::vec
   const Dims& d = m->d;
   const Plan& P = m->P;
   int M = 0, maxlen = 0;
-  std::vector<int> rs, rp, last(n);
+  std::vector<int> rs, rp, last(n), tiles;
   for (int b = 0; b < n; ++b) {
+    for (int p0 = 0; p0 < lens[b]; p0 += FLASH_ROWS) {
+      tiles.push_back(M + p0);
+      tiles.push_back(b);
+      tiles.push_back(p0);
+      tiles.push_back(std::min(FLASH_ROWS, lens[b] - p0));
+    }
     for (int t = 0; t < lens[b]; ++t) {
       rs.push_back(b);
       rp.push_back(t);
@@ -390,28 +399,31 @@ qd_status enqueue_prefill(qd_model* m, int n, const int* ids_dev, const std::vec
     last[b] = M - 1;
     maxlen = std::max(maxlen, lens[b]);
   }
+  const int n_tiles = (int)tiles.size() / 4;
   int* row_slot = m->ws<int>(P.row_slot);
   int* row_pos = m->ws<int>(P.row_pos);
   int* last_rows = m->ws<int>(P.last_rows);
   int* dlens = m->ws<int>(P.lens);
+  int4* dtiles = m->ws<int4>(P.tiles);
   HIPCHK(hipMemcpyAsync(row_slot, rs.data(), M * 4, hipMemcpyHostToDevice, st));
   HIPCHK(hipMemcpyAsync(row_pos, rp.data(), M * 4, hipMemcpyHostToDevice, st));
   HIPCHK(hipMemcpyAsync(last_rows, last.data(), n * 4, hipMemcpyHostToDevice, st));
   HIPCHK(hipMemcpyAsync(dlens, lens.data(), n * 4, hipMemcpyHostToDevice, st));
+  HIPCHK(hipMemcpyAsync(dtiles, tiles.data(), tiles.size() * 4, hipMemcpyHostToDevice, st));
 
   bf16_t* x = m->ws<bf16_t>(P.x);
   bf16_t* h = m->ws<bf16_t>(P.h);
   bf16_t* qkv = m->ws<bf16_t>(P.qkv);
   bf16_t* attn = m->ws<bf16_t>(P.attn);
   bf16_t* act = m->ws<bf16_t>(P.act);
+  float* gpart = m->ws<float>(P.gemm_part);
   HIPCHK(launch_embed(ids_dev, M, m->w<int8_t>(P.emb_q), m->w<float>(P.emb_s), d.d, d.V, x, st));
-  const int split_len = ((maxlen + ATT_CHUNK - 1) / ATT_CHUNK) * ATT_CHUNK;
   for (int l = 0; l < d.L; ++l) {
     const LayerOff& o = P.L[l];
     HIPCHK(launch_rmsnorm(x, M, d.d, m->w<float>(o.in_g), m->shape.rms_eps, h, st));
     GemmArgs g{};
     g.A = h; g.lda = d.d; g.W = m->w<int8_t>(o.qkv_q); g.scale = m->w<float>(o.qkv_s);
-    g.M = M; g.N = d.NQKV; g.K = d.d; g.epi = EPI_STORE; g.out = qkv; g.ldo = d.NQKV;
+    g.M = M; g.N = d.NQKV; g.K = d.d; g.epi = EPI_STORE; g.out = qkv; g.ldo = d.NQKV; g.part = gpart;
     HIPCHK(launch_gemm(g, st));
     RopeArgs ra{};
     ra.qkv = qkv; ra.ldqkv = d.NQKV;
@@ -421,26 +433,25 @@ qd_status enqueue_prefill(qd_model* m, int n, const int* ids_dev, const std::vec
     ra.kcache = m->kcache(l); ra.vcache = m->vcache(l);
     ra.H = d.H; ra.KV = d.KV; ra.D = d.D; ra.max_ctx = m->lim.max_ctx; ra.M = M;
     HIPCHK(launch_qk_rope(ra, st));
-    AttnArgs aa{};
-    aa.q = qkv; aa.ldq = d.NQKV;
-    aa.kcache = m->kcache(l); aa.vcache = m->vcache(l);
-    aa.row_slot = row_slot; aa.row_pos = row_pos;
-    aa.H = d.H; aa.KV = d.KV; aa.D = d.D; aa.max_ctx = m->lim.max_ctx; aa.M = M;
-    aa.split_len = split_len; aa.nsplit = 1;
-    aa.out = attn; aa.ldo = d.HD;
-    HIPCHK(launch_attention(aa, st));
+    FlashArgs fa{};
+    fa.q = qkv; fa.ldq = d.NQKV;
+    fa.kcache = m->kcache(l); fa.vcache = m->vcache(l);
+    fa.tiles = dtiles;
+    fa.H = d.H; fa.KV = d.KV; fa.D = d.D; fa.max_ctx = m->lim.max_ctx;
+    fa.out = attn; fa.ldo = d.HD;
+    HIPCHK(launch_flash_prefill(fa, n_tiles, st));
     g = GemmArgs{};
     g.A = attn; g.lda = d.HD; g.W = m->w<int8_t>(o.o_q); g.scale = m->w<float>(o.o_s);
-    g.M = M; g.N = d.d; g.K = d.HD; g.epi = EPI_RESID; g.out = x; g.ldo = d.d;
+    g.M = M; g.N = d.d; g.K = d.HD; g.epi = EPI_RESID; g.out = x; g.ldo = d.d; g.part = gpart;
     HIPCHK(launch_gemm(g, st));
     HIPCHK(launch_rmsnorm(x, M, d.d, m->w<float>(o.post_g), m->shape.rms_eps, h, st));
     g = GemmArgs{};
     g.A = h; g.lda = d.d; g.W = m->w<int8_t>(o.gu_q); g.scale = m->w<float>(o.gu_s);
-    g.M = M; g.N = 2 * d.I; g.K = d.d; g.epi = EPI_SILU; g.out = act; g.ldo = d.I;
+    g.M = M; g.N = 2 * d.I; g.K = d.d; g.epi = EPI_SILU; g.out = act; g.ldo = d.I; g.part = gpart;
     HIPCHK(launch_gemm(g, st));
     g = GemmArgs{};
     g.A = act; g.lda = d.I; g.W = m->w<int8_t>(o.dn_q); g.scale = m->w<float>(o.dn_s);
-    g.M = M; g.N = d.d; g.K = d.I; g.epi = EPI_RESID; g.out = x; g.ldo = d.d;
+    g.M = M; g.N = d.d; g.K = d.I; g.epi = EPI_RESID; g.out = x; g.ldo = d.d; g.part = gpart;
     HIPCHK(launch_gemm(g, st));
   }
   qd_status s = enqueue_lm_head(m, x, last_rows, M, n, logits, next_ids, false, write_out, st);
@@ -804,11 +815,11 @@ qd_status qd_profile_kernels(qd_model* m, int32_t B, int32_t iters, float* us_ou
             HIPCHK(launch_embed(scratch_ids, B, m->w<int8_t>(m->P.emb_q), m->w<float>(m->P.emb_s),
                                 m->d.d, m->d.V, m->ws<bf16_t>(m->P.x), st));
             break;
-          case QD_PROF_QKV: QDCHK(dec_qkv(m, 0, B, st)); break;
-          case QD_PROF_ATTN: QDCHK(dec_attn(m, 0, B, nsplit, split_len, st)); break;
-          case QD_PROF_O: QDCHK(dec_o(m, 0, B, st)); break;
-          case QD_PROF_GATEUP: QDCHK(dec_gateup(m, 0, B, st)); break;
-          case QD_PROF_DOWN: QDCHK(dec_down(m, 0, B, st)); break;
+          case QD_PROF_QKV: QDCHK(dec_qkv(m, i % m->d.L, B, st)); break;
+          case QD_PROF_ATTN: QDCHK(dec_attn(m, i % m->d.L, B, nsplit, split_len, st)); break;
+          case QD_PROF_O: QDCHK(dec_o(m, i % m->d.L, B, st)); break;
+          case QD_PROF_GATEUP: QDCHK(dec_gateup(m, i % m->d.L, B, st)); break;
+          case QD_PROF_DOWN: QDCHK(dec_down(m, i % m->d.L, B, st)); break;
           default:
             QDCHK(enqueue_lm_head(m, m->ws<bf16_t>(m->P.x), nullptr, B, B, nullptr, scratch_next,
                                   false, false, st));

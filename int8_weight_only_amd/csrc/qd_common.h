@@ -53,7 +53,10 @@ struct GemmArgs {
   int M, N, K;
   int epi;                    // EPI_STORE / EPI_RESID / EPI_SILU
   bf16_t* out; int ldo;
+  float* part;                // split-K partial sums [splits][M][N] (fp32), PART_FLOATS max
+  int splits;                 // set by the launcher
 };
+constexpr size_t GEMM_PART_FLOATS = (size_t)8 << 20;  // 32 MiB of split-K partials
 
 struct RopeArgs {
   bf16_t* qkv; int ldqkv;     // [M][(H+2KV)*D]; q heads rewritten in place
@@ -92,6 +95,17 @@ struct AttnDecArgs {
   bf16_t* out; int ldo;           // [B][H*D]
 };
 
+// prefill attention: a work-group owns a tile of up to 64 query rows of one sequence and
+// one query head; tiles are described by (first row, slot, first position, rows)
+struct FlashArgs {
+  const bf16_t* q; int ldq;                    // roped q rows; head h at q + r*ldq + h*D
+  const bf16_t* kcache; const bf16_t* vcache;  // this layer's [slots][KV][ctx][D]
+  const int4* tiles;                           // [grid.x]
+  int H, KV, D, max_ctx;
+  bf16_t* out; int ldo;                        // [M][H*D]
+};
+constexpr int FLASH_ROWS = 64;
+
 constexpr int LM_MAX_GRID = 1024;  // work-groups of the LM-head GEMV (row blocks looped)
 
 // ---- launchers (qd_kernels.hip) ------------------------------------------------------------
@@ -110,6 +124,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
 hipError_t launch_qk_rope(const RopeArgs& a, hipStream_t st);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
 hipError_t launch_attention_decode(const AttnDecArgs& a, hipStream_t st);
+hipError_t launch_flash_prefill(const FlashArgs& a, int n_tiles, hipStream_t st);
 hipError_t launch_set_positions(int* pos, const int* lens, int n, hipStream_t st);
 hipError_t launch_iota(int* p, int n, hipStream_t st);
 

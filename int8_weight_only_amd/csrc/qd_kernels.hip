@@ -582,51 +582,92 @@ __device__ __forceinline__ bf16x8_t i8x8_to_bf16x8(uint2 w) {
   return __builtin_bit_cast(bf16x8_t, make_uint4(out[0], out[1], out[2], out[3]));
 }
 
+// 64x64 output tile per work-group (4 waves in 2x2, each 32x32 = 2x2 MFMA 16x16x32
+// tiles), k advancing 64 at a time.  The next k-tile is fetched into registers while
+// the current one is multiplied out of LDS (double-buffered, one barrier per step).
+// With split-K (blockIdx.z) each work-group covers a slice of K and stores fp32
+// partials; k_gemm_finish sums them in split order and applies the epilogue.
+template <int EPI>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, int m, int n, float v, float vu) {
+  if (EPI == EPI_SILU) {
+    const float g = rbf(v * a.scale[n]);
+    const float u = rbf(vu * a.scale[n + GU_BLOCK]);
+    const int j = (n / (2 * GU_BLOCK)) * GU_BLOCK + (n % GU_BLOCK);
+    a.out[(size_t)m * a.ldo + j] = f2bf(g / (1.0f + expf(-g)) * u);
+  } else {
+    const float y = v * a.scale[n];
+    bf16_t* o = a.out + (size_t)m * a.ldo + n;
+    *o = (EPI == EPI_STORE) ? f2bf(y) : f2bf(bf2f(*o) + rbf(y));
+  }
+}
+
 template <int EPI>
 __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
-  constexpr int BM = 64, BN = 64, BK = 32;
-  __shared__ __align__(16) bf16_t As[BM][BK + 8];
-  __shared__ __align__(16) int8_t Ws[BN][BK + 16];
+  constexpr int BM = 64, BN = 64, BK = 64;
+  __shared__ __align__(16) bf16_t As[2][BM][BK + 8];
+  __shared__ __align__(16) int8_t Ws[2][BN][BK + 16];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid & 1, wn = wid >> 1;
+  const int grp = lane >> 4, r16 = lane & 15;
   const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const int kper = ((a.K + a.splits - 1) / a.splits + 31) & ~31;
+  const int kbeg = blockIdx.z * kper;
+  const int kend = min(a.K, kbeg + kper);
+
+  // staging: A rows tid/4 (two 16-byte pieces), W row tid/4 (one 16-byte piece)
+  const int ar = tid >> 2, ac = (tid & 3) * 16;
+  const int wr = tid >> 2, wc = (tid & 3) * 16;
+  uint4 ra0, ra1, rw;
+  auto fetch = [&](int k0) {
+    const int ka = k0 + ac;
+    const bool aok = m0 + ar < a.M;
+    const bf16_t* ap = a.A + (size_t)(aok ? m0 + ar : 0) * a.lda;
+    ra0 = (aok && ka < kend) ? *reinterpret_cast<const uint4*>(ap + ka) : make_uint4(0, 0, 0, 0);
+    ra1 = (aok && ka + 8 < kend) ? *reinterpret_cast<const uint4*>(ap + ka + 8) : make_uint4(0, 0, 0, 0);
+    const bool wok = n0 + wr < a.N && k0 + wc < kend;
+    rw = wok ? *reinterpret_cast<const uint4*>(a.W + (size_t)(n0 + wr) * a.K + k0 + wc) : make_uint4(0, 0, 0, 0);
+  };
+  auto stash = [&](int buf) {
+    *reinterpret_cast<uint4*>(&As[buf][ar][ac]) = ra0;
+    *reinterpret_cast<uint4*>(&As[buf][ar][ac + 8]) = ra1;
+    *reinterpret_cast<uint4*>(&Ws[buf][wr][wc]) = rw;
+  };
+
   f32x4_t acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int k0 = 0; k0 < a.K; k0 += BK) {
-    {
-      const int row = tid >> 2, part = tid & 3;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (m0 + row < a.M)
-        v = *reinterpret_cast<const uint4*>(a.A + (size_t)(m0 + row) * a.lda + k0 + part * 8);
-      *reinterpret_cast<uint4*>(&As[row][part * 8]) = v;
-    }
-    if (tid < 128) {
-      const int row = tid >> 1, part = tid & 1;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (n0 + row < a.N)
-        v = *reinterpret_cast<const uint4*>(a.W + (size_t)(n0 + row) * a.K + k0 + part * 16);
-      *reinterpret_cast<uint4*>(&Ws[row][part * 16]) = v;
-    }
-    __syncthreads();
-    bf16x8_t af[2], bw[2];
+  int buf = 0;
+  if (kbeg < kend) {
+    fetch(kbeg);
+    stash(0);
+  }
+  __syncthreads();
+  for (int k0 = kbeg; k0 < kend; k0 += BK) {
+    const bool more = k0 + BK < kend;
+    if (more) fetch(k0 + BK);
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-      af[mt] = __builtin_bit_cast(
-          bf16x8_t, *reinterpret_cast<const uint4*>(&As[wm * 32 + mt * 16 + (lane & 15)][8 * (lane >> 4)]));
+    for (int sub = 0; sub < 2; ++sub) {
+      bf16x8_t af[2], bw[2];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-      bw[nt] = i8x8_to_bf16x8(
-          *reinterpret_cast<const uint2*>(&Ws[wn * 32 + nt * 16 + (lane & 15)][8 * (lane >> 4)]));
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < 2; ++mt)
+        af[mt] = __builtin_bit_cast(
+            bf16x8_t, *reinterpret_cast<const uint4*>(&As[buf][wm * 32 + mt * 16 + r16][32 * sub + 8 * grp]));
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
-        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt], bw[nt], acc[mt][nt], 0, 0, 0);
+        bw[nt] = i8x8_to_bf16x8(
+            *reinterpret_cast<const uint2*>(&Ws[buf][wn * 32 + nt * 16 + r16][32 * sub + 8 * grp]));
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt], bw[nt], acc[mt][nt], 0, 0, 0);
+    }
+    if (more) stash(buf ^ 1);
     __syncthreads();
+    buf ^= 1;
   }
 
   // lane holds D[4*(lane/16)+i][lane%16]: token rows, channel columns
@@ -634,28 +675,42 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
   for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int m = m0 + wm * 32 + mt * 16 + 4 * (lane >> 4) + i;
+      const int m = m0 + wm * 32 + mt * 16 + 4 * grp + i;
       if (m >= a.M) continue;
-      if (EPI == EPI_SILU) {
-        const int ng = n0 + wn * 32 + (lane & 15), nu = ng + GU_BLOCK;
-        if (nu >= a.N) continue;
-        const float g = rbf(acc[mt][0][i] * a.scale[ng]);
-        const float u = rbf(acc[mt][1][i] * a.scale[nu]);
-        const int j = (ng / (2 * GU_BLOCK)) * GU_BLOCK + (lane & 15);
-        a.out[(size_t)m * a.ldo + j] = f2bf(g / (1.0f + expf(-g)) * u);
+      if (a.splits > 1) {
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          const int n = n0 + wn * 32 + nt * 16 + r16;
+          if (n < a.N) a.part[((size_t)blockIdx.z * a.M + m) * a.N + n] = acc[mt][nt][i];
+        }
+      } else if (EPI == EPI_SILU) {
+        const int ng = n0 + wn * 32 + r16;
+        if (ng + GU_BLOCK < a.N) gemm_epilogue<EPI_SILU>(a, m, ng, acc[mt][0][i], acc[mt][1][i]);
       } else {
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
-          const int n = n0 + wn * 32 + nt * 16 + (lane & 15);
-          if (n >= a.N) continue;
-          const float v = acc[mt][nt][i] * a.scale[n];
-          bf16_t* o = a.out + (size_t)m * a.ldo + n;
-          if (EPI == EPI_STORE) *o = f2bf(v);
-          else *o = f2bf(bf2f(*o) + rbf(v));
+          const int n = n0 + wn * 32 + nt * 16 + r16;
+          if (n < a.N) gemm_epilogue<EPI>(a, m, n, acc[mt][nt][i], 0.0f);
         }
       }
     }
   }
+}
+
+// split-K tail: out = epilogue(sum of the partials in split order)
+template <int EPI>
+__global__ __launch_bounds__(256) void k_gemm_finish(GemmArgs a) {
+  const int nn = (EPI == EPI_SILU) ? a.N / 2 : a.N;
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long)a.M * nn) return;
+  const int m = (int)(idx / nn), c = (int)(idx % nn);
+  const int n = (EPI == EPI_SILU) ? gu_row(c, 0) : c;
+  float v = 0.0f, vu = 0.0f;
+  for (int z = 0; z < a.splits; ++z) {
+    v += a.part[((size_t)z * a.M + m) * a.N + n];
+    if (EPI == EPI_SILU) vu += a.part[((size_t)z * a.M + m) * a.N + n + GU_BLOCK];
+  }
+  gemm_epilogue<EPI>(a, m, n, v, vu);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1232,6 +1287,167 @@ __global__ __launch_bounds__(256) void k_attn_dec(AttnDecArgs a) {
   if (tid == 0) atomicExch(a.counters + (size_t)b * a.KV + g, 0u);
 }
 
+// ------------------------------------------------------------------------------------------
+// Prefill attention on MFMA (causal, flash style).  A work-group owns up to 64 query rows
+// of one sequence (4 waves x 16 rows) and one query head h of KV group g = h / (H/KV).
+// Keys and values advance in blocks of 32 positions staged once in LDS for all waves
+// (V transposed so it feeds the MFMA B operand directly).  Per wave and block:
+// S = Q K^T (16 rows x 32 keys, fp32 accumulation of bf16 products), causal mask, online
+// softmax in fp32 with each row's state in the lanes that hold that row of O, then
+// O += P V.  P is split into bf16 high and low parts (two MFMAs), so the probabilities
+// enter the product with ~16 significant bits rather than bf16's 8.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v, v));
+  v = fmaxf(v, dpp_f<0x4E>(v, v));
+  v = fmaxf(v, dpp_f<0x141>(v, v));
+  v = fmaxf(v, dpp_f<0x140>(v, v));
+  return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<0xB1>(0.0f, v);
+  v += dpp_f<0x4E>(0.0f, v);
+  v += dpp_f<0x141>(0.0f, v);
+  v += dpp_f<0x140>(0.0f, v);
+  return v;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void k_flash_prefill(FlashArgs a) {
+  constexpr int KB = 32;             // keys per block
+  constexpr int KS = D / 32;         // MFMA k-steps over the head dim
+  constexpr int NT = D / 16;         // 16-dim output tiles
+  constexpr int VPR = D / 8;         // uint4 per key row
+  constexpr int LD_PER_T = (KB * VPR + 255) / 256;  // uint4 per thread per tensor and block
+  __shared__ __align__(16) bf16_t Ks[KB][D + 8];
+  __shared__ __align__(16) bf16_t Vt[D][KB + 8];
+  __shared__ __align__(16) bf16_t Ps[4][2][16][KB + 8];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int grp = lane >> 4, r16 = lane & 15;
+  const int4 tile = a.tiles[blockIdx.x];
+  const int row0 = tile.x, slot = tile.y, pos0 = tile.z, nrows = tile.w;
+  const int h = blockIdx.y, G = a.H / a.KV, g = h / G;
+  const bf16_t* Kb = a.kcache + ((size_t)slot * a.KV + g) * a.max_ctx * D;
+  const bf16_t* Vb = a.vcache + ((size_t)slot * a.KV + g) * a.max_ctx * D;
+  const int kmax = pos0 + nrows;  // keys 0..kmax-1 are visible to some row of the tile
+
+  // Q fragments of this wave's 16 rows (A operand of S): row r16, dims 32*ks + 8*grp
+  bf16x8_t qf[KS];
+  {
+    const int r = 16 * wid + r16;
+    const bool ok = r < nrows;
+    const bf16_t* qr = a.q + (size_t)(row0 + (ok ? r : 0)) * a.ldq + (size_t)h * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[ks] = __builtin_bit_cast(
+          bf16x8_t, ok ? *reinterpret_cast<const uint4*>(qr + 32 * ks + 8 * grp) : make_uint4(0, 0, 0, 0));
+  }
+  // softmax state of rows 4*grp + i of this wave
+  float m[4], l[4];
+  f32x4_t o[NT];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m[i] = -INFINITY;
+    l[i] = 0.0f;
+  }
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) o[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const float scale = 1.0f / sqrtf((float)D);
+
+  // global -> register staging of one K/V block
+  uint4 kst[LD_PER_T], vst[LD_PER_T];
+  auto fetch = [&](int kb) {
+#pragma unroll
+    for (int u = 0; u < LD_PER_T; ++u) {
+      const int idx = tid + 256 * u;
+      const int key = idx / VPR, c = idx % VPR;
+      const bool ok = idx < KB * VPR && kb + key < kmax;
+      kst[u] = ok ? *reinterpret_cast<const uint4*>(Kb + (size_t)(kb + key) * D + 8 * c) : make_uint4(0, 0, 0, 0);
+      vst[u] = ok ? *reinterpret_cast<const uint4*>(Vb + (size_t)(kb + key) * D + 8 * c) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  fetch(0);
+  for (int kb = 0; kb < kmax; kb += KB) {
+#pragma unroll
+    for (int u = 0; u < LD_PER_T; ++u) {
+      const int idx = tid + 256 * u;
+      if (idx < KB * VPR) {
+        const int key = idx / VPR, c = idx % VPR;
+        *reinterpret_cast<uint4*>(&Ks[key][8 * c]) = kst[u];
+        const uint32_t w4[4] = {vst[u].x, vst[u].y, vst[u].z, vst[u].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          Vt[8 * c + 2 * e][key] = (bf16_t)(w4[e] & 0xFFFFu);
+          Vt[8 * c + 2 * e + 1][key] = (bf16_t)(w4[e] >> 16);
+        }
+      }
+    }
+    __syncthreads();
+    if (kb + KB < kmax) fetch(kb + KB);
+
+    // S = Q K^T for 16 rows x 32 keys (two 16-key tiles)
+    f32x4_t sacc[2];
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      sacc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8_t kf = __builtin_bit_cast(
+            bf16x8_t, *reinterpret_cast<const uint4*>(&Ks[16 * n + r16][32 * ks + 8 * grp]));
+        sacc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ks], kf, sacc[n], 0, 0, 0);
+      }
+    }
+    // causal mask + online softmax; lane holds rows 4*grp+i, keys 16n + r16
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * wid + 4 * grp + i;
+      const int qpos = pos0 + r;
+      float sv[2];
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        const int key = kb + 16 * n + r16;
+        sv[n] = (r < nrows && key <= qpos) ? sacc[n][i] * scale : -INFINITY;
+      }
+      const float mnew = fmaxf(m[i], row16_max(fmaxf(sv[0], sv[1])));
+      const float alpha = (m[i] == -INFINITY) ? 0.0f : expf(m[i] - mnew);
+      float pr[2];
+#pragma unroll
+      for (int n = 0; n < 2; ++n) pr[n] = (sv[n] == -INFINITY) ? 0.0f : expf(sv[n] - mnew);
+      l[i] = l[i] * alpha + row16_sum(pr[0] + pr[1]);
+      m[i] = mnew;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) o[nt][i] *= alpha;
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        const bf16_t hi = f2bf(pr[n]);
+        const bf16_t lo = f2bf(pr[n] - bf2f(hi));
+        Ps[wid][0][4 * grp + i][16 * n + r16] = hi;
+        Ps[wid][1][4 * grp + i][16 * n + r16] = lo;
+      }
+    }
+    __syncthreads();
+    // O += P V: A = P (rows r16, keys 8*grp..), B = V (keys 8*grp.., dims 16*nt + r16)
+    const bf16x8_t phi = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(&Ps[wid][0][r16][8 * grp]));
+    const bf16x8_t plo = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(&Ps[wid][1][r16][8 * grp]));
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const bf16x8_t vf = __builtin_bit_cast(
+          bf16x8_t, *reinterpret_cast<const uint4*>(&Vt[16 * nt + r16][8 * grp]));
+      o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi, vf, o[nt], 0, 0, 0);
+      o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo, vf, o[nt], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+  // out[r][h*D + d] for rows 4*grp + i, dims 16*nt + r16
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 16 * wid + 4 * grp + i;
+    if (r >= nrows) continue;
+    bf16_t* orow = a.out + (size_t)(row0 + r) * a.ldo + (size_t)h * D;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) orow[16 * nt + r16] = f2bf(o[nt][i] / l[i]);
+  }
+}
+
 // merge split partials: o = sum_s o_s e^(m_s - m) / sum_s l_s e^(m_s - m)
 __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   const int head = blockIdx.x, r = blockIdx.y;
@@ -1404,12 +1620,29 @@ hipError_t launch_skinny(const GemvArgs& a, int epi, hipStream_t st) {
   return skinny_tt<4>(a, epi, st);
 }
 
-hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
-  dim3 grid((a.N + 63) / 64, (a.M + 63) / 64);
+hipError_t launch_gemm(const GemmArgs& a0, hipStream_t st) {
+  GemmArgs a = a0;
+  const int tiles = ((a.N + 63) / 64) * ((a.M + 63) / 64);
+  // split K when the tile grid leaves most of the 256 CUs idle
+  int splits = 1;
+  while (splits < 8 && tiles * splits < 256 && a.K / (splits * 2) >= 256 &&
+         (size_t)(splits * 2) * a.M * a.N <= GEMM_PART_FLOATS && a.part)
+    splits *= 2;
+  a.splits = splits;
+  dim3 grid((a.N + 63) / 64, (a.M + 63) / 64, splits);
   switch (a.epi) {
     case EPI_STORE: hipLaunchKernelGGL(k_gemm<EPI_STORE>, grid, dim3(256), 0, st, a); break;
     case EPI_RESID: hipLaunchKernelGGL(k_gemm<EPI_RESID>, grid, dim3(256), 0, st, a); break;
     default: hipLaunchKernelGGL(k_gemm<EPI_SILU>, grid, dim3(256), 0, st, a); break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  const long n = (long)a.M * (a.epi == EPI_SILU ? a.N / 2 : a.N);
+  dim3 g2((unsigned)((n + 255) / 256));
+  switch (a.epi) {
+    case EPI_STORE: hipLaunchKernelGGL(k_gemm_finish<EPI_STORE>, g2, dim3(256), 0, st, a); break;
+    case EPI_RESID: hipLaunchKernelGGL(k_gemm_finish<EPI_RESID>, g2, dim3(256), 0, st, a); break;
+    default: hipLaunchKernelGGL(k_gemm_finish<EPI_SILU>, g2, dim3(256), 0, st, a); break;
   }
   return hipGetLastError();
 }
@@ -1461,6 +1694,19 @@ hipError_t launch_attention_decode(const AttnDecArgs& a, hipStream_t st) {
     case 256: return attn_dec_d<256>(a, G, st);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_flash_prefill(const FlashArgs& a, int n_tiles, hipStream_t st) {
+  if (n_tiles < 1) return hipSuccess;
+  dim3 grid(n_tiles, a.H);
+  switch (a.D) {
+    case 32: hipLaunchKernelGGL(k_flash_prefill<32>, grid, dim3(256), 0, st, a); break;
+    case 64: hipLaunchKernelGGL(k_flash_prefill<64>, grid, dim3(256), 0, st, a); break;
+    case 128: hipLaunchKernelGGL(k_flash_prefill<128>, grid, dim3(256), 0, st, a); break;
+    case 256: hipLaunchKernelGGL(k_flash_prefill<256>, grid, dim3(256), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {

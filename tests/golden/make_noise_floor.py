@@ -38,7 +38,13 @@ CONFIGS = {
                         intermediate=256, vocab=512), 1, "uniform", 77, 1001, 12),
     "odd": (ModelShape(hidden=96, n_layers=3, n_heads=6, n_kv_heads=2, head_dim=32,
                        intermediate=160, vocab=1000), 1, "uniform", 77, 1001, 12),
+    "mid": (ModelShape(hidden=512, n_layers=2, n_heads=8, n_kv_heads=4, head_dim=128,
+                       intermediate=1024, vocab=4096), 4, "uniform", 200, 1004, 8),
+    # long context at a small shape: many attention splits and prefill tiles
+    "wide-long": (ModelShape(hidden=128, n_layers=2, n_heads=4, n_kv_heads=2, head_dim=64,
+                             intermediate=256, vocab=512), 5, "uniform", 1500, 1005, 24),
     "qwen3-0.6b": (SHAPES["qwen3-0.6b"], 0, "ones", 256, 1000, 4),
+    "qwen3-1.7b": (SHAPES["qwen3-1.7b"], 0, "ones", 256, 1000, 3),
 }
 PERT = 6e-8
 FACTOR = 1.5

@@ -216,3 +216,33 @@ def test_large_batch_teacher_forced_logits():
                            orcs[b]["margin"][k], "tiny-b", f"b{b} step {k}")
     finally:
         m.close()
+
+
+MID = ModelShape(hidden=512, n_layers=2, n_heads=8, n_kv_heads=4, head_dim=128,
+                 intermediate=1024, vocab=4096)
+
+
+def test_teacher_forced_mid_split_k():
+    """hidden 512 / head_dim 128: prefill GEMMs take the split-K path, flash prefill D=128."""
+    w = make_weights(MID, seed=4, gains="uniform")
+    qm = quantize_model(w)
+    say("[gpu] teacher-forced mid (split-K prefill), 200-token prompt")
+    m = _model(MID, w, max_batch=2, max_ctx=256, max_prefill_tokens=512)
+    try:
+        _teacher_forced(m, MID, qm, make_prompt(MID.vocab, 200, 1004), 7, "mid", "mid")
+    finally:
+        m.close()
+
+
+def test_teacher_forced_long_context():
+    """1500-token prompt: 24 prefill tiles per head, decode attention over ~24 splits that the
+    last split merges (the long-context path at a shape the oracle runs in seconds)."""
+    w = make_weights(WIDE, seed=5, gains="uniform")
+    qm = quantize_model(w)
+    say("[gpu] teacher-forced long context: 1500-token prompt, 23 decode steps")
+    m = _model(WIDE, w, max_batch=1, max_ctx=2048, max_prefill_tokens=2048)
+    try:
+        _teacher_forced(m, WIDE, qm, make_prompt(WIDE.vocab, 1500, 1005), 23, "wide-long",
+                        "wide-long")
+    finally:
+        m.close()
