@@ -221,10 +221,12 @@ qd_status qd_profile_kernels(qd_model* m, int32_t B, int32_t iters, float* us_ou
 typedef enum {
   QD_TUNE_ATTN_MAX_SPLITS = 0,    /* most position splits per (sequence, KV head); default 64 */
   QD_TUNE_ATTN_MIN_CHUNKS = 1,    /* fewest 64-position chunks per split; default 1 */
+  QD_TUNE_ATTN_WAVES = 2,         /* decode-attention waves per work-group: 4, 8, or 0 = by batch (default) */
+  QD_TUNE_ATTN_MERGE_LAST = 3,    /* 1: the last split merges in-kernel; 0: a merge launch (default) */
 } qd_tune_knob;
 
 /* Sets a knob; captured decode graphs are dropped so the next call re-captures.
- * QD_ERR_INVALID_ARGUMENTS for an unknown knob or a value < 1. */
+ * QD_ERR_INVALID_ARGUMENTS for an unknown knob or a value out of its range. */
 qd_status qd_set_tuning(qd_model* m, int32_t knob, int32_t value);
 
 /* Frees host state and graphs.  Caller buffers remain the caller's. */

@@ -212,6 +212,8 @@ struct qd_model {
   hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
   int attn_max_splits = 64;
   int attn_min_chunks = 1;
+  int attn_waves = 0;  // 0: eight waves only when B x KV heads fill the GPU without splits
+  int attn_merge_last = 0;
 
   template <class T> T* w(size_t off) { return reinterpret_cast<T*>(W + off); }
   template <class T> T* ws(size_t off) { return reinterpret_cast<T*>(WS + off); }
@@ -326,6 +328,8 @@ qd_status dec_attn(qd_model* m, int l, int B, int nsplit, int split_len, hipStre
   aa.kcache = m->kcache(l); aa.vcache = m->vcache(l);
   aa.H = d.H; aa.KV = d.KV; aa.D = d.D; aa.max_ctx = m->lim.max_ctx; aa.B = B;
   aa.split_len = split_len; aa.nsplit = nsplit;
+  aa.nwaves = m->attn_waves ? m->attn_waves : (B * d.KV >= 256 ? 8 : 4);
+  aa.merge_last = m->attn_merge_last;
   aa.part_o = m->ws<float>(m->P.part_o); aa.part_ml = m->ws<float>(m->P.part_ml);
   aa.counters = m->ws<unsigned int>(m->P.att_cnt);
   aa.out = m->ws<bf16_t>(m->P.attn); aa.ldo = d.HD;
@@ -838,10 +842,20 @@ qd_status qd_profile_kernels(qd_model* m, int32_t B, int32_t iters, float* us_ou
 qd_status qd_set_tuning(qd_model* m, int32_t knob, int32_t value) {
   g_err.clear();
   if (!m) return fail(QD_ERR_INVALID_ARGUMENTS, "model is NULL");
-  if (value < 1) return fail(QD_ERR_INVALID_ARGUMENTS, "value must be >= 1");
+  if (value < 0 || (value < 1 && knob != QD_TUNE_ATTN_MERGE_LAST && knob != QD_TUNE_ATTN_WAVES))
+    return fail(QD_ERR_INVALID_ARGUMENTS, "value out of range");
   switch (knob) {
     case QD_TUNE_ATTN_MAX_SPLITS: m->attn_max_splits = value; break;
     case QD_TUNE_ATTN_MIN_CHUNKS: m->attn_min_chunks = value; break;
+    case QD_TUNE_ATTN_MERGE_LAST:
+      if (value > 1) return fail(QD_ERR_INVALID_ARGUMENTS, "merge mode must be 0 or 1");
+      m->attn_merge_last = value;
+      break;
+    case QD_TUNE_ATTN_WAVES:
+      if (value != 0 && value != 4 && value != 8)
+        return fail(QD_ERR_INVALID_ARGUMENTS, "attention waves must be 0 (by batch), 4 or 8");
+      m->attn_waves = value;
+      break;
     default: return fail(QD_ERR_INVALID_ARGUMENTS, "unknown knob");
   }
   for (auto& kv : m->graphs) (void)hipGraphExecDestroy(kv.second);

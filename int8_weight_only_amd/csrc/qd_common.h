@@ -32,7 +32,7 @@ struct GemvArgs {
   const int8_t* W;      // [N][K] int8 codes (rows possibly gate/up interleaved)
   const float* scale;   // [N]
   int N, K;
-  int nb;               // batch rows in this launch (GEMV 1..8, skinny MFMA 1..64)
+  int nb;               // batch rows in this launch (GEMV 1, skinny MFMA 1..64)
   bf16_t* out; int ldo; // EPI_STORE/EPI_SILU: output; EPI_RESID: residual updated in place
   // EPI_LOGITS
   float* logits; int ldl;            // optional fp32 logits [nb][ldl]
@@ -67,17 +67,6 @@ struct RopeArgs {
   int H, KV, D, max_ctx, M;
 };
 
-struct AttnArgs {
-  const bf16_t* q; int ldq;   // roped q heads, row r at q + r*ldq
-  const bf16_t* kcache; const bf16_t* vcache;  // this layer's [slots][KV][ctx][D]
-  const int* row_slot; const int* row_pos;
-  int H, KV, D, max_ctx, M;
-  int split_len;              // positions per work-group (multiple of ATT_CHUNK)
-  int nsplit;                 // grid.x
-  float* part_o;              // [M][H][nsplit][D] unnormalized partial outputs
-  float* part_ml;             // [M][H][nsplit][2] (running max, sum)
-  bf16_t* out; int ldo;       // final [M][H*D] when nsplit == 1
-};
 
 // decode attention with QK-norm, RoPE and the KV write fused in; splits of the context
 // are merged by the last split to finish (per-(row, KV head) counters)
@@ -89,6 +78,8 @@ struct AttnDecArgs {
   bf16_t* kcache; bf16_t* vcache; // this layer's [slots][KV][ctx][D]
   int H, KV, D, max_ctx, B;
   int split_len, nsplit;
+  int nwaves;                     // 4 or 8 waves per work-group (8 only when G*D <= 512)
+  int merge_last;                 // 1: the last split merges (fence + counter); 0: merge kernel
   float* part_o;                  // [B][H][nsplit][D]
   float* part_ml;                 // [B][H][nsplit][2]
   unsigned int* counters;         // [B][KV], zero on entry; the merging split resets it
@@ -113,7 +104,6 @@ hipError_t launch_quantize_rows(const float* w, int rows, int cols, int8_t* q, f
                                 int dst_row0, int gu_half, hipStream_t st);
 hipError_t launch_rope_table(float2* tab, int max_ctx, int D, float theta, hipStream_t st);
 hipError_t launch_fill_i32(int* p, int n, int v, hipStream_t st);
-hipError_t launch_fill_u64(unsigned long long* p, int n, hipStream_t st);
 hipError_t launch_embed(const int* ids, int M, const int8_t* E, const float* Es, int d, int V,
                         bf16_t* x, hipStream_t st);
 hipError_t launch_rmsnorm(const bf16_t* x, int M, int d, const float* g, float eps, bf16_t* y,
@@ -122,7 +112,6 @@ hipError_t launch_gemv(const GemvArgs& a, int epi, hipStream_t st);
 hipError_t launch_skinny(const GemvArgs& a, int epi, hipStream_t st);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
 hipError_t launch_qk_rope(const RopeArgs& a, hipStream_t st);
-hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
 hipError_t launch_attention_decode(const AttnDecArgs& a, hipStream_t st);
 hipError_t launch_flash_prefill(const FlashArgs& a, int n_tiles, hipStream_t st);
 hipError_t launch_set_positions(int* pos, const int* lens, int n, hipStream_t st);

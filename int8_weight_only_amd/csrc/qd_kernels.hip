@@ -123,10 +123,6 @@ __global__ void k_fill_i32(int* p, int n, int v) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
 }
-__global__ void k_fill_u64(unsigned long long* p, int n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0ull;
-}
 __global__ void k_iota(int* p, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = i;
@@ -194,47 +190,34 @@ __device__ __forceinline__ void i8x16_to_f32(const int4 v, float* f) {
     for (int e = 0; e < 4; ++e) f[j * 4 + e] = (float)((int)((uint32_t)w4[j] << (24 - 8 * e)) >> 24);
 }
 
-// LM head tail: each work-group's best (value, index) keys are stored per batch row;
-// the last work-group to finish reduces them and writes the greedy ids.  best[b] is
-// valid in thread b (b < nb).
-__device__ void lm_head_finish(const GemvArgs& a, unsigned long long best, int nb_max) {
-  __shared__ int last_flag;
-  __shared__ unsigned long long red[4];
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+// LM head tail: each work-group stores its best (value, index) key per batch row; the
+// keys are reduced by k_lm_finish in the next launch (the kernel boundary makes them
+// visible without a device-wide fence in every work-group).  best is valid in thread b.
+__device__ __forceinline__ void lm_head_store(const GemvArgs& a, unsigned long long best, int nb_max) {
+  const int tid = threadIdx.x;
   if (tid < a.nb && tid < nb_max) a.part_keys[(size_t)tid * LM_MAX_GRID + blockIdx.x] = best;
-  __syncthreads();
-  if (tid == 0) {
-    __threadfence();
-    const unsigned int t = atomicAdd(a.done, 1u);
-    last_flag = (t == gridDim.x - 1) ? 1 : 0;
-  }
-  __syncthreads();
-  if (!last_flag) return;
-  __threadfence();
-  for (int b = 0; b < a.nb; ++b) {
+}
+
+// one work-group: wave w reduces batch rows w, w+4, ... over the LM-head work-groups'
+// keys and writes the greedy ids (and advances positions and the step counter)
+__global__ __launch_bounds__(256) void k_lm_finish(GemvArgs a, int nblocks) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  for (int b = wid; b < a.nb; b += 4) {
     unsigned long long k = 0ull;
-    for (int i = tid; i < (int)gridDim.x; i += 256) {
-      const unsigned long long v = __hip_atomic_load(a.part_keys + (size_t)b * LM_MAX_GRID + i,
-                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = lane; i < nblocks; i += 64) {
+      const unsigned long long v = a.part_keys[(size_t)b * LM_MAX_GRID + i];
       k = v > k ? v : k;
     }
     k = wave_max_u64(k);
-    if (lane == 0) red[wid] = k;
-    __syncthreads();
-    if (tid == 0) {
-      unsigned long long m = red[0];
-      for (int w = 1; w < 4; ++w) m = red[w] > m ? red[w] : m;
-      const int id = key_index(m);
+    if (lane == 0) {
+      const int id = key_index(k);
       a.next_ids[b] = id;
       if (a.out_ids) a.out_ids[(size_t)(a.batch0 + b) * a.out_ld + *a.step] = id;
       if (a.pos) a.pos[b] += 1;
     }
-    __syncthreads();
   }
-  if (tid == 0) {
-    if (a.bump_step) *a.step += 1;
-    atomicExch(a.done, 0u);
-  }
+  __syncthreads();
+  if (tid == 0 && a.bump_step) *a.step += 1;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -385,179 +368,7 @@ __global__ __launch_bounds__(256) void k_gemv1(GemvArgs a) {
       b0 = wbest[0];
       for (int w = 1; w < 4; ++w) b0 = wbest[w] > b0 ? wbest[w] : b0;
     }
-    lm_head_finish(a, b0, 1);
-  }
-}
-
-// ------------------------------------------------------------------------------------------
-// batched decode GEMV for 2..8 rows: y[b][n] = scale[n] * sum_k x[b][k] * W[n][k].
-// Activations (RMS-normalized in the prologue when a gain is given) are staged in LDS
-// as bf16; each wave streams R weight rows, 16 bytes per lane per row per step.
-template <int NB, int EPI>
-__global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
-  constexpr int R = (EPI == EPI_SILU) ? 8 : 4;
-  extern __shared__ __align__(16) unsigned char smem[];
-  bf16_t* xs = reinterpret_cast<bf16_t*>(smem);  // [NB][K]
-  __shared__ float red[4][NB];
-  __shared__ unsigned long long wkey[4][NB];
-
-  const int K = a.K;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int nvec = K >> 3;  // 8 bf16 per 16-byte vector
-
-  // ---- stage x rows (with optional RMSNorm) ----
-  float ss[NB];
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    ss[b] = 0.0f;
-    const bool live = b < a.nb;
-    const int xr = live ? (a.x_rows ? a.x_rows[b] : b) : 0;
-    const uint4* src = reinterpret_cast<const uint4*>(a.x + (size_t)xr * a.ldx);
-    uint4* dst = reinterpret_cast<uint4*>(xs + (size_t)b * K);
-    for (int v = tid; v < nvec; v += 256) {
-      uint4 u = live ? src[v] : make_uint4(0, 0, 0, 0);
-      dst[v] = u;
-      const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float lo = __uint_as_float(w4[j] << 16), hi = __uint_as_float(w4[j] & 0xFFFF0000u);
-        ss[b] += lo * lo + hi * hi;
-      }
-    }
-  }
-  if (a.gain) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const float t = wave_sum(ss[b]);
-      if (lane == 0) red[wid][b] = t;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const float tot = red[0][b] + red[1][b] + red[2][b] + red[3][b];
-      const float denom = sqrtf(tot / (float)K + a.eps);
-      bf16_t* row = xs + (size_t)b * K;
-      for (int c = tid; c < K; c += 256) row[c] = f2bf(bf2f(row[c]) / denom * a.gain[c]);
-    }
-  }
-  __syncthreads();
-
-  const int nblk = (EPI == EPI_SILU) ? (a.N + 2 * GU_BLOCK - 1) / (2 * GU_BLOCK) : (a.N + 15) / 16;
-  unsigned long long best[NB];
-#pragma unroll
-  for (int b = 0; b < NB; ++b) best[b] = 0ull;
-
-  for (int blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
-    int rows[R];
-    if (EPI == EPI_SILU) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        rows[i] = blk * 2 * GU_BLOCK + wid * 4 + i;
-        rows[i + 4] = blk * 2 * GU_BLOCK + GU_BLOCK + wid * 4 + i;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < R; ++i) rows[i] = blk * 16 + wid * 4 + i;
-    }
-
-    float acc[R][NB];
-#pragma unroll
-    for (int i = 0; i < R; ++i)
-#pragma unroll
-      for (int b = 0; b < NB; ++b) acc[i][b] = 0.0f;
-
-    const int nchunk = K >> 4;
-    for (int c = lane; c < nchunk; c += 64) {
-      float wf[R][16];
-#pragma unroll
-      for (int i = 0; i < R; ++i) {
-        int4 v = make_int4(0, 0, 0, 0);
-        if (rows[i] < a.N) v = *reinterpret_cast<const int4*>(a.W + (size_t)rows[i] * K + c * 16);
-        i8x16_to_f32(v, wf[i]);
-      }
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const uint4* xv = reinterpret_cast<const uint4*>(xs + (size_t)b * K + c * 16);
-        const uint4 u0 = xv[0], u1 = xv[1];
-        const uint32_t w8[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-        float xf[16];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          xf[2 * j] = __uint_as_float(w8[j] << 16);
-          xf[2 * j + 1] = __uint_as_float(w8[j] & 0xFFFF0000u);
-        }
-#pragma unroll
-        for (int i = 0; i < R; ++i)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) acc[i][b] = fmaf(wf[i][j], xf[j], acc[i][b]);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < R; ++i)
-#pragma unroll
-      for (int b = 0; b < NB; ++b) acc[i][b] = wave_sum(acc[i][b]);
-
-    if (lane != 0) continue;
-    if (EPI == EPI_STORE) {
-#pragma unroll
-      for (int i = 0; i < R; ++i) {
-        if (rows[i] >= a.N) continue;
-        const float s = a.scale[rows[i]];
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-          if (b < a.nb) a.out[(size_t)b * a.ldo + rows[i]] = f2bf(acc[i][b] * s);
-      }
-    } else if (EPI == EPI_RESID) {
-#pragma unroll
-      for (int i = 0; i < R; ++i) {
-        if (rows[i] >= a.N) continue;
-        const float s = a.scale[rows[i]];
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          if (b >= a.nb) continue;
-          bf16_t* o = a.out + (size_t)b * a.ldo + rows[i];
-          *o = f2bf(bf2f(*o) + rbf(acc[i][b] * s));
-        }
-      }
-    } else if (EPI == EPI_SILU) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (rows[i + 4] >= a.N) continue;
-        const float sg = a.scale[rows[i]], su = a.scale[rows[i + 4]];
-        const int j = blk * GU_BLOCK + wid * 4 + i;
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          if (b >= a.nb) continue;
-          const float g = rbf(acc[i][b] * sg), u = rbf(acc[i + 4][b] * su);
-          a.out[(size_t)b * a.ldo + j] = f2bf(g / (1.0f + expf(-g)) * u);
-        }
-      }
-    } else {  // EPI_LOGITS
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-#pragma unroll
-        for (int i = 0; i < R; ++i) {
-          if (rows[i] >= a.N || b >= a.nb) continue;
-          const float v = acc[i][b] * a.scale[rows[i]];
-          if (a.logits) a.logits[(size_t)b * a.ldl + rows[i]] = v;
-          const unsigned long long k = argmax_key(v, rows[i]);
-          best[b] = k > best[b] ? k : best[b];
-        }
-      }
-    }
-  }
-  if (EPI == EPI_LOGITS) {
-    if (lane == 0) {
-#pragma unroll
-      for (int b = 0; b < NB; ++b) wkey[wid][b] = best[b];
-    }
-    __syncthreads();
-    unsigned long long mine = 0ull;
-    if (tid < NB) {
-      mine = wkey[0][tid];
-      for (int w = 1; w < 4; ++w) mine = wkey[w][tid] > mine ? wkey[w][tid] : mine;
-    }
-    lm_head_finish(a, mine, NB);
+    lm_head_store(a, b0, 1);
   }
 }
 
@@ -757,7 +568,12 @@ __global__ __launch_bounds__(256) void k_skinny(GemvArgs a) {
       wok[c] = ch < a.N;
       wrow[c] = reinterpret_cast<const int*>(a.W + (size_t)(wok[c] ? ch : 0) * K);
     }
-    for (int kb = 128 * wid; kb < K; kb += 512) {
+    const int nkb = (K + 127) / 128;
+    const int nmine = (nkb - wid + 3) / 4;  // this wave's blocks: wid, wid+4, ...
+    const int rot = nmine > 0 ? tile % nmine : 0;
+    for (int ib = 0; ib < nmine; ++ib) {
+      const int ii = ib + rot;
+      const int kb = (wid + 4 * (ii >= nmine ? ii - nmine : ii)) * 128;
       const int k0 = kb + 32 * grp;
       const bool kok = k0 < K;
       uint4 wv[CTW][2];
@@ -835,7 +651,115 @@ __global__ __launch_bounds__(256) void k_skinny(GemvArgs a) {
     }
     __syncthreads();
   }
-  if (EPI == EPI_LOGITS) lm_head_finish(a, best, 64);
+  if (EPI == EPI_LOGITS) lm_head_store(a, best, 64);
+}
+
+// Batched LM head (vocabulary-sized N): a work-group owns 4 waves x LMT 16-channel tiles
+// and walks K in chunks; each chunk of the activations is staged once in LDS for all
+// 4*LMT tiles (the activations are read from L2 once per work-group instead of once per
+// tile), and every tile's accumulators stay in registers across the chunks.
+constexpr int LMT = 4;
+template <int TT>
+__global__ __launch_bounds__(256) void k_lm_skinny(GemvArgs a) {
+  constexpr int KC = 1024 / TT;                 // k per chunk: LDS = 16*TT rows x KC
+  __shared__ __align__(16) bf16_t xs[TT * 16][KC + 8];
+  __shared__ unsigned long long wkey[4][TT * 16];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int K = a.K;
+  const int grp = lane >> 4, r16 = lane & 15;
+  const int ntiles = (a.N + 15) / 16;
+  f32x4_t acc[LMT][TT];
+#pragma unroll
+  for (int t = 0; t < LMT; ++t)
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) acc[t][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  int tile[LMT];
+  const int8_t* wrow[LMT];
+#pragma unroll
+  for (int t = 0; t < LMT; ++t) {
+    tile[t] = (blockIdx.x * LMT + t) * 4 + wid;
+    const int ch = tile[t] * 16 + r16;
+    wrow[t] = a.W + (size_t)(ch < a.N ? ch : 0) * K;
+  }
+  for (int kc = 0; kc < K; kc += KC) {
+    const int klen = min(KC, K - kc);
+    __syncthreads();
+    // stage rows (tokens) x [kc, kc+klen) of the activations, 16 bytes per thread-step
+    const int vpr = klen / 8;
+    for (int idx = tid; idx < TT * 16 * vpr; idx += 256) {
+      const int r = idx / vpr, c = idx % vpr;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (r < a.nb) {
+        const int xr = a.x_rows ? a.x_rows[r] : r;
+        v = *reinterpret_cast<const uint4*>(a.x + (size_t)xr * a.ldx + kc + 8 * c);
+      }
+      *reinterpret_cast<uint4*>(&xs[r][8 * c]) = v;
+    }
+    __syncthreads();
+    for (int kb = 0; kb < klen; kb += 128) {
+      const int k0 = kb + 32 * grp;     // within the chunk
+      const bool kok = k0 < klen;
+      uint4 xv[TT][4];
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          xv[tt][q] = kok ? *reinterpret_cast<const uint4*>(&xs[tt * 16 + r16][k0 + 8 * q])
+                          : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < LMT; ++t) {
+        if (tile[t] >= ntiles) continue;
+        uint4 wv0 = make_uint4(0, 0, 0, 0), wv1 = wv0;
+        if (kok && tile[t] * 16 + r16 < a.N) {
+          const uint4* src = reinterpret_cast<const uint4*>(wrow[t] + kc + k0);
+          wv0 = src[0];
+          wv1 = src[1];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint4 w16 = (j >> 1) ? wv1 : wv0;
+          const uint2 w8 = (j & 1) ? make_uint2(w16.z, w16.w) : make_uint2(w16.x, w16.y);
+          const bf16x8_t af = i8x8_to_bf16x8(w8);
+#pragma unroll
+          for (int tt = 0; tt < TT; ++tt)
+            acc[t][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                af, __builtin_bit_cast(bf16x8_t, xv[tt][j]), acc[t][tt], 0, 0, 0);
+        }
+      }
+    }
+  }
+  // lane holds channel tile*16 + 4*grp + i, token tt*16 + r16
+  unsigned long long best[TT];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) {
+    best[tt] = 0ull;
+    const int tok = tt * 16 + r16;
+#pragma unroll
+    for (int t = 0; t < LMT; ++t) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ch = tile[t] * 16 + 4 * grp + i;
+        if (tok < a.nb && tile[t] < ntiles && ch < a.N) {
+          const float lv = acc[t][tt][i] * a.scale[ch];
+          if (a.logits) a.logits[(size_t)tok * a.ldl + ch] = lv;
+          const unsigned long long k = argmax_key(lv, ch);
+          best[tt] = k > best[tt] ? k : best[tt];
+        }
+      }
+    }
+    unsigned long long t1 = shfl_xor_u64(best[tt], 16);
+    best[tt] = t1 > best[tt] ? t1 : best[tt];
+    t1 = shfl_xor_u64(best[tt], 32);
+    best[tt] = t1 > best[tt] ? t1 : best[tt];
+    if (lane < 16) wkey[wid][tt * 16 + lane] = best[tt];
+  }
+  __syncthreads();
+  unsigned long long mine = 0ull;
+  if (tid < TT * 16) {
+    mine = wkey[0][tid];
+    for (int w = 1; w < 4; ++w) mine = wkey[w][tid] > mine ? wkey[w][tid] : mine;
+  }
+  lm_head_store(a, mine, TT * 16);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -892,133 +816,6 @@ __global__ __launch_bounds__(256) void k_qk_rope(RopeArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
-// GQA attention over the KV cache for one token row, one KV head and one split of the
-// positions 0..p.  The G query heads of the group share every K/V row read.  Softmax is
-// computed online across 64-position chunks in fp32; with several splits the partial
-// (max, sum, unnormalized output) go to a merge kernel.
-template <int D, int G>
-__global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
-  constexpr int CH = ATT_CHUNK;
-  constexpr int HALF = D / 2;
-  constexpr int NG = 256 / HALF;  // position groups in the P*V phase
-  __shared__ float qs[G][D];
-  __shared__ float sc[G][CH];
-  __shared__ float ored[NG][G][D];
-  const int s = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
-  const int tid = threadIdx.x;
-  const int slot = a.row_slot[r], p = a.row_pos[r];
-  const int n = p + 1;
-  const int t_begin = s * a.split_len;
-  const int t_end = min(n, t_begin + a.split_len);
-  const bf16_t* q = a.q + (size_t)r * a.ldq + (size_t)g * G * D;
-  for (int idx = tid; idx < G * D; idx += 256) qs[idx / D][idx % D] = bf2f(q[idx]);
-  const bf16_t* Kb = a.kcache + ((size_t)slot * a.KV + g) * a.max_ctx * D;
-  const bf16_t* Vb = a.vcache + ((size_t)slot * a.KV + g) * a.max_ctx * D;
-  const float scale = 1.0f / sqrtf((float)D);
-  __syncthreads();
-
-  float m[G], l[G], o[G][2];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = -INFINITY;
-    l[h] = 0.0f;
-    o[h][0] = o[h][1] = 0.0f;
-  }
-  const int dp = tid % HALF, grp = tid / HALF;
-  for (int t0 = t_begin; t0 < t_end; t0 += CH) {
-    {  // scores: 4 lanes per position
-      const int tl = tid >> 2, part = tid & 3;
-      const int t = t0 + tl;
-      float sp[G];
-#pragma unroll
-      for (int h = 0; h < G; ++h) sp[h] = 0.0f;
-      if (t < t_end) {
-        const bf16_t* kr = Kb + (size_t)t * D + part * (D / 4);
-#pragma unroll
-        for (int j = 0; j < D / 4; j += 2) {
-          const uint32_t kk = *reinterpret_cast<const uint32_t*>(kr + j);
-          const float k0 = __uint_as_float(kk << 16), k1 = __uint_as_float(kk & 0xFFFF0000u);
-#pragma unroll
-          for (int h = 0; h < G; ++h)
-            sp[h] += qs[h][part * (D / 4) + j] * k0 + qs[h][part * (D / 4) + j + 1] * k1;
-        }
-      }
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        sp[h] += __shfl_xor(sp[h], 1, 64);
-        sp[h] += __shfl_xor(sp[h], 2, 64);
-      }
-      if (part == 0) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) sc[h][tl] = (t < t_end) ? sp[h] * scale : -INFINITY;
-      }
-    }
-    __syncthreads();
-    float mnew[G], alpha[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float cm = -INFINITY;
-      for (int t = 0; t < CH; ++t) cm = fmaxf(cm, sc[h][t]);
-      mnew[h] = fmaxf(m[h], cm);
-      alpha[h] = (m[h] == -INFINITY) ? 0.0f : expf(m[h] - mnew[h]);
-    }
-    __syncthreads();
-    if (tid < CH) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float v = sc[h][tid];
-        sc[h][tid] = (v == -INFINITY) ? 0.0f : expf(v - mnew[h]);
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float cs = 0.0f;
-      for (int t = 0; t < CH; ++t) cs += sc[h][t];
-      l[h] = l[h] * alpha[h] + cs;
-      m[h] = mnew[h];
-      o[h][0] *= alpha[h];
-      o[h][1] *= alpha[h];
-    }
-    for (int tl = grp; tl < CH; tl += NG) {
-      const int t = t0 + tl;
-      if (t >= t_end) break;
-      const uint32_t vv = *reinterpret_cast<const uint32_t*>(Vb + (size_t)t * D + 2 * dp);
-      const float v0 = __uint_as_float(vv << 16), v1 = __uint_as_float(vv & 0xFFFF0000u);
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float pw = sc[h][tl];
-        o[h][0] += pw * v0;
-        o[h][1] += pw * v1;
-      }
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    ored[grp][h][2 * dp] = o[h][0];
-    ored[grp][h][2 * dp + 1] = o[h][1];
-  }
-  __syncthreads();
-  for (int idx = tid; idx < G * D; idx += 256) {
-    const int h = idx / D, dd = idx % D;
-    float acc = 0.0f;
-#pragma unroll
-    for (int gg = 0; gg < NG; ++gg) acc += ored[gg][h][dd];
-    const int head = g * G + h;
-    if (a.nsplit == 1) {
-      a.out[(size_t)r * a.ldo + (size_t)head * D + dd] = f2bf(acc / l[h]);
-    } else {
-      const size_t pi = ((size_t)r * a.H + head) * a.nsplit + s;
-      a.part_o[pi * D + dd] = acc;
-      if (dd == 0) {
-        a.part_ml[pi * 2] = m[h];
-        a.part_ml[pi * 2 + 1] = l[h];
-      }
-    }
-  }
-}
-
 // Decode attention for one token row b, one KV head g and one split of positions.
 // Fused in front: RMSNorm (shared [D] gain) and rotate-half RoPE at position p of the
 // group's G query heads and of its key head, done in LDS from the raw projections; the
@@ -1028,8 +825,10 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
 // V tiles are requested one chunk ahead, the first ones before the prologue.  The four
 // waves merge in LDS at the end.  Fused behind: with several splits, each writes its
 // partial (max, sum, unnormalized output); the split that finishes last merges them.
-template <int D, int G>
-__global__ __launch_bounds__(256) void k_attn_dec(AttnDecArgs a) {
+template <int D, int G, int NW>
+__global__ __launch_bounds__(64 * NW) void k_attn_dec(AttnDecArgs a) {
+  constexpr int NT = 64 * NW;              // threads
+  constexpr int CHW = 16 * NW;             // positions per iteration
   constexpr int HALF = D / 2;
   constexpr int KQ = D / 4;                    // key elements per lane (4 lanes per position)
   constexpr int KV4 = KQ / 8;                  // uint4 loads per lane per key row
@@ -1037,8 +836,8 @@ __global__ __launch_bounds__(256) void k_attn_dec(AttnDecArgs a) {
   constexpr int VW = DPL >= 2 ? DPL / 2 : 1;   // 32-bit words of V per lane per row
   __shared__ __align__(16) float qs[G][D];
   __shared__ float kn[D], vn[D];
-  __shared__ float wm[4][G], wl[4][G];
-  __shared__ float wo[4][G][D];
+  __shared__ float wm[NW][G], wl[NW][G];
+  __shared__ float wo[NW][G][D];
   __shared__ int last_flag;
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -1081,7 +880,7 @@ __global__ __launch_bounds__(256) void k_attn_dec(AttnDecArgs a) {
   if (t_begin < t_end) load_tiles(kc, vc, t_begin);
 
   // ---- QK-norm + RoPE of the G query heads and the key head; copy of v ----
-  for (int hh = wid; hh <= G; hh += 4) {
+  for (int hh = wid; hh <= G; hh += NW) {
     const bool isq = hh < G;
     const bf16_t* src = isq ? row + (size_t)(g * G + hh) * D : row + (size_t)(a.H + g) * D;
     const float* gn = isq ? a.q_gain : a.k_gain;
@@ -1122,7 +921,7 @@ __global__ __launch_bounds__(256) void k_attn_dec(AttnDecArgs a) {
   }
   {
     const bf16_t* vsrc = row + (size_t)(a.H + a.KV + g) * D;
-    for (int i = tid; i < D; i += 256) {
+    for (int i = tid; i < D; i += NT) {
       const bf16_t v = vsrc[i];
       vn[i] = bf2f(v);
       if (owner) Vb[(size_t)p * D + i] = v;
@@ -1139,7 +938,7 @@ __global__ __launch_bounds__(256) void k_attn_dec(AttnDecArgs a) {
 #pragma unroll
     for (int e = 0; e < DPL; ++e) o[h][e] = 0.0f;
   }
-  for (int t0 = t_begin; t0 < t_end; t0 += ATT_CHUNK) {
+  for (int t0 = t_begin; t0 < t_end; t0 += CHW) {
     const int t = t0 + 16 * wid + tl;
     // scores of this lane's position (4 lanes per position, KQ key elements each)
     float sp[G];
@@ -1166,8 +965,8 @@ __global__ __launch_bounds__(256) void k_attn_dec(AttnDecArgs a) {
       }
     }
     // next chunk's tiles go out before the softmax and P*V work of this one
-    const bool more = t0 + ATT_CHUNK < t_end;
-    if (more) load_tiles(kx, vx, t0 + ATT_CHUNK);
+    const bool more = t0 + CHW < t_end;
+    if (more) load_tiles(kx, vx, t0 + CHW);
     const bool valid = t < t_end;
     float pr[G];
 #pragma unroll
@@ -1232,14 +1031,14 @@ __global__ __launch_bounds__(256) void k_attn_dec(AttnDecArgs a) {
       for (int e = 0; e < DPL; ++e) wo[wid][h][DPL * lane + e] = o[h][e];
   }
   __syncthreads();
-  for (int idx = tid; idx < G * D; idx += 256) {
+  for (int idx = tid; idx < G * D; idx += NT) {
     const int h = idx / D, dd = idx % D;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, wm[w][h]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, wm[w][h]);
     float L = 0.0f, O = 0.0f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NW; ++w) {
       if (wm[w][h] == -INFINITY) continue;
       const float f = expf(wm[w][h] - M);
       L += wl[w][h] * f;
@@ -1257,7 +1056,7 @@ __global__ __launch_bounds__(256) void k_attn_dec(AttnDecArgs a) {
       }
     }
   }
-  if (a.nsplit == 1) return;
+  if (a.nsplit == 1 || !a.merge_last) return;
   // ---- the last split to finish merges all partials of this (row, KV head) ----
   __syncthreads();
   if (tid == 0) {
@@ -1268,7 +1067,7 @@ __global__ __launch_bounds__(256) void k_attn_dec(AttnDecArgs a) {
   __syncthreads();
   if (!last_flag) return;
   __threadfence();
-  for (int idx = tid; idx < G * D; idx += 256) {
+  for (int idx = tid; idx < G * D; idx += NT) {
     const int h = idx / D, dd = idx % D;
     const int head = g * G + h;
     const size_t base = ((size_t)b * a.H + head) * a.nsplit;
@@ -1285,6 +1084,28 @@ __global__ __launch_bounds__(256) void k_attn_dec(AttnDecArgs a) {
     a.out[(size_t)b * a.ldo + (size_t)head * D + dd] = f2bf(acc / lsum);
   }
   if (tid == 0) atomicExch(a.counters + (size_t)b * a.KV + g, 0u);
+}
+
+// split merge as its own launch: o = sum_s o_s e^(m_s - m) / sum_s l_s e^(m_s - m)
+// for one (row b, query head); the kernel boundary orders it after every split
+__global__ __launch_bounds__(128) void k_attn_dec_merge(AttnDecArgs a) {
+  const int head = blockIdx.x, b = blockIdx.y;
+  const size_t base = ((size_t)b * a.H + head) * a.nsplit;
+  float mx = -INFINITY;
+  for (int q = 0; q < a.nsplit; ++q) mx = fmaxf(mx, a.part_ml[(base + q) * 2]);
+  float lsum = 0.0f;
+  for (int q = 0; q < a.nsplit; ++q) {
+    const float ms = a.part_ml[(base + q) * 2];
+    if (ms != -INFINITY) lsum += a.part_ml[(base + q) * 2 + 1] * expf(ms - mx);
+  }
+  for (int dd = threadIdx.x; dd < a.D; dd += 128) {
+    float acc = 0.0f;
+    for (int q = 0; q < a.nsplit; ++q) {
+      const float ms = a.part_ml[(base + q) * 2];
+      if (ms != -INFINITY) acc += a.part_o[(base + q) * a.D + dd] * expf(ms - mx);
+    }
+    a.out[(size_t)b * a.ldo + (size_t)head * a.D + dd] = f2bf(acc / lsum);
+  }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1448,28 +1269,6 @@ __global__ __launch_bounds__(256) void k_flash_prefill(FlashArgs a) {
   }
 }
 
-// merge split partials: o = sum_s o_s e^(m_s - m) / sum_s l_s e^(m_s - m)
-__global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
-  const int head = blockIdx.x, r = blockIdx.y;
-  const int D = a.D;
-  const size_t base = ((size_t)r * a.H + head) * a.nsplit;
-  float mx = -INFINITY;
-  for (int s = 0; s < a.nsplit; ++s) mx = fmaxf(mx, a.part_ml[(base + s) * 2]);
-  float lsum = 0.0f;
-  for (int s = 0; s < a.nsplit; ++s) {
-    const float ms = a.part_ml[(base + s) * 2];
-    if (ms != -INFINITY) lsum += a.part_ml[(base + s) * 2 + 1] * expf(ms - mx);
-  }
-  for (int dd = threadIdx.x; dd < D; dd += blockDim.x) {
-    float acc = 0.0f;
-    for (int s = 0; s < a.nsplit; ++s) {
-      const float ms = a.part_ml[(base + s) * 2];
-      if (ms != -INFINITY) acc += a.part_o[(base + s) * D + dd] * expf(ms - mx);
-    }
-    a.out[(size_t)r * a.ldo + (size_t)head * D + dd] = f2bf(acc / lsum);
-  }
-}
-
 // ------------------------------------------------------------------------------------------
 // launchers
 
@@ -1493,11 +1292,6 @@ hipError_t launch_fill_i32(int* p, int n, int v, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_fill_u64(unsigned long long* p, int n, hipStream_t st) {
-  if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_fill_u64, dim3((n + 255) / 256), dim3(256), 0, st, p, n);
-  return hipGetLastError();
-}
 
 hipError_t launch_set_positions(int* pos, const int* lens, int n, hipStream_t st) {
   hipLaunchKernelGGL(k_set_positions, dim3((n + 255) / 256), dim3(256), 0, st, pos, lens, n);
@@ -1518,18 +1312,6 @@ hipError_t launch_embed(const int* ids, int M, const int8_t* E, const float* Es,
 hipError_t launch_rmsnorm(const bf16_t* x, int M, int d, const float* g, float eps, bf16_t* y,
                           hipStream_t st) {
   hipLaunchKernelGGL(k_rmsnorm, dim3(M), dim3(256), 0, st, x, d, g, eps, y);
-  return hipGetLastError();
-}
-
-template <int NB>
-static hipError_t gemv_nb(const GemvArgs& a, int epi, hipStream_t st) {
-  const size_t lds = (size_t)NB * a.K * sizeof(bf16_t);
-  const int nblk = epi == EPI_SILU ? (a.N + 2 * GU_BLOCK - 1) / (2 * GU_BLOCK) : (a.N + 15) / 16;
-  dim3 grid(epi == EPI_LOGITS ? (nblk < LM_MAX_GRID ? nblk : LM_MAX_GRID) : nblk);
-  if (epi == EPI_SILU) hipLaunchKernelGGL((k_gemv<NB, EPI_SILU>), grid, dim3(256), lds, st, a);
-  else if (epi == EPI_STORE) hipLaunchKernelGGL((k_gemv<NB, EPI_STORE>), grid, dim3(256), lds, st, a);
-  else if (epi == EPI_RESID) hipLaunchKernelGGL((k_gemv<NB, EPI_RESID>), grid, dim3(256), lds, st, a);
-  else hipLaunchKernelGGL((k_gemv<NB, EPI_LOGITS>), grid, dim3(256), lds, st, a);
   return hipGetLastError();
 }
 
@@ -1569,45 +1351,37 @@ static hipError_t gemv1(const GemvArgs& a, int epi, hipStream_t st) {
   return gemv1_r<1>(a, epi, st);
 }
 
-static hipError_t gemv_dispatch(const GemvArgs& a, int epi, hipStream_t st) {
-  if (a.nb <= 1) return gemv1(a, epi, st);
-  if (a.nb <= 2) return gemv_nb<2>(a, epi, st);
-  if (a.nb <= 4) return gemv_nb<4>(a, epi, st);
-  return gemv_nb<8>(a, epi, st);
+static hipError_t lm_finish(const GemvArgs& a, int nblocks, hipStream_t st) {
+  hipLaunchKernelGGL(k_lm_finish, dim3(1), dim3(256), 0, st, a, nblocks);
+  return hipGetLastError();
 }
 
-// rows staged in LDS must fit in 64 KiB: larger batches run as several launches
+// one row only; batches go through launch_skinny
 hipError_t launch_gemv(const GemvArgs& a, int epi, hipStream_t st) {
-  if (a.nb < 1 || a.nb > 8) return hipErrorInvalidValue;
-  if (a.nb == 1) return gemv_dispatch(a, epi, st);
-  int cap = 8;
-  while (cap > 1 && (size_t)cap * a.K * sizeof(bf16_t) > 65536) cap >>= 1;
-  if (cap == 1 && (size_t)2 * a.K * sizeof(bf16_t) > 65536 && a.nb > 1 && epi == EPI_LOGITS)
-    return hipErrorInvalidValue;
-  if (a.nb <= cap) return gemv_dispatch(a, epi, st);
-  if (epi == EPI_LOGITS) return hipErrorInvalidValue;  // the LM head keeps its batch in one launch
-  for (int b0 = 0; b0 < a.nb; b0 += cap) {
-    GemvArgs s = a;
-    s.nb = a.nb - b0 < cap ? a.nb - b0 : cap;
-    if (a.x_rows) s.x_rows = a.x_rows + b0;
-    else s.x = a.x + (size_t)b0 * a.ldx;
-    s.out = a.out + (size_t)b0 * a.ldo;
-    hipError_t e = gemv_dispatch(s, epi, st);
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
+  if (a.nb != 1) return hipErrorInvalidValue;
+  hipError_t e = gemv1(a, epi, st);
+  if (e != hipSuccess || epi != EPI_LOGITS) return e;
+  const int nblk = (a.N + 15) / 16;
+  return lm_finish(a, nblk < LM_MAX_GRID ? nblk : LM_MAX_GRID, st);
 }
 
 template <int TT>
 static hipError_t skinny_tt(const GemvArgs& a, int epi, hipStream_t st) {
+  if (epi == EPI_LOGITS) {
+    // vocabulary-sized: 4 x LMT wave tiles per work-group, activations staged in LDS
+    const int ntiles = (a.N + 15) / 16;
+    const int g = (ntiles + 4 * LMT - 1) / (4 * LMT);
+    if (g > LM_MAX_GRID) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_lm_skinny<TT>), dim3(g), dim3(256), 0, st, a);
+    hipError_t e = hipGetLastError();
+    return e != hipSuccess ? e : lm_finish(a, g, st);
+  }
   const int ctw = epi == EPI_SILU ? 2 : 1;
-  const int ntiles = (a.N + 16 * ctw - 1) / (16 * ctw);
-  dim3 grid(epi == EPI_LOGITS ? (ntiles < LM_MAX_GRID ? ntiles : LM_MAX_GRID) : ntiles);
+  dim3 grid((a.N + 16 * ctw - 1) / (16 * ctw));
   switch (epi) {
     case EPI_STORE: hipLaunchKernelGGL((k_skinny<TT, EPI_STORE>), grid, dim3(256), 0, st, a); break;
     case EPI_RESID: hipLaunchKernelGGL((k_skinny<TT, EPI_RESID>), grid, dim3(256), 0, st, a); break;
-    case EPI_SILU: hipLaunchKernelGGL((k_skinny<TT, EPI_SILU>), grid, dim3(256), 0, st, a); break;
-    default: hipLaunchKernelGGL((k_skinny<TT, EPI_LOGITS>), grid, dim3(256), 0, st, a); break;
+    default: hipLaunchKernelGGL((k_skinny<TT, EPI_SILU>), grid, dim3(256), 0, st, a); break;
   }
   return hipGetLastError();
 }
@@ -1652,48 +1426,44 @@ hipError_t launch_qk_rope(const RopeArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int D>
-static hipError_t attn_d(const AttnArgs& a, int G, hipStream_t st) {
-  dim3 grid(a.nsplit, a.KV, a.M);
+template <int D, int NW>
+static hipError_t attn_dec_dw(const AttnDecArgs& a, int G, hipStream_t st) {
+  dim3 grid(a.nsplit, a.KV, a.B);
+  dim3 blk(64 * NW);
   switch (G) {
-    case 1: hipLaunchKernelGGL((k_attn<D, 1>), grid, dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((k_attn<D, 2>), grid, dim3(256), 0, st, a); break;
-    case 3: hipLaunchKernelGGL((k_attn<D, 3>), grid, dim3(256), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((k_attn<D, 4>), grid, dim3(256), 0, st, a); break;
-    case 5: hipLaunchKernelGGL((k_attn<D, 5>), grid, dim3(256), 0, st, a); break;
-    case 6: hipLaunchKernelGGL((k_attn<D, 6>), grid, dim3(256), 0, st, a); break;
-    case 7: hipLaunchKernelGGL((k_attn<D, 7>), grid, dim3(256), 0, st, a); break;
-    default: hipLaunchKernelGGL((k_attn<D, 8>), grid, dim3(256), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((k_attn_dec<D, 1, NW>), grid, blk, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((k_attn_dec<D, 2, NW>), grid, blk, 0, st, a); break;
+    case 3: hipLaunchKernelGGL((k_attn_dec<D, 3, NW>), grid, blk, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((k_attn_dec<D, 4, NW>), grid, blk, 0, st, a); break;
+    case 5: hipLaunchKernelGGL((k_attn_dec<D, 5, NW>), grid, blk, 0, st, a); break;
+    case 6: hipLaunchKernelGGL((k_attn_dec<D, 6, NW>), grid, blk, 0, st, a); break;
+    case 7: hipLaunchKernelGGL((k_attn_dec<D, 7, NW>), grid, blk, 0, st, a); break;
+    default: hipLaunchKernelGGL((k_attn_dec<D, 8, NW>), grid, blk, 0, st, a); break;
   }
   return hipGetLastError();
 }
 
+// eight waves (128 positions per iteration) when the wave-merge buffers stay small
 template <int D>
 static hipError_t attn_dec_d(const AttnDecArgs& a, int G, hipStream_t st) {
-  dim3 grid(a.nsplit, a.KV, a.B);
-  switch (G) {
-    case 1: hipLaunchKernelGGL((k_attn_dec<D, 1>), grid, dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((k_attn_dec<D, 2>), grid, dim3(256), 0, st, a); break;
-    case 3: hipLaunchKernelGGL((k_attn_dec<D, 3>), grid, dim3(256), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((k_attn_dec<D, 4>), grid, dim3(256), 0, st, a); break;
-    case 5: hipLaunchKernelGGL((k_attn_dec<D, 5>), grid, dim3(256), 0, st, a); break;
-    case 6: hipLaunchKernelGGL((k_attn_dec<D, 6>), grid, dim3(256), 0, st, a); break;
-    case 7: hipLaunchKernelGGL((k_attn_dec<D, 7>), grid, dim3(256), 0, st, a); break;
-    default: hipLaunchKernelGGL((k_attn_dec<D, 8>), grid, dim3(256), 0, st, a); break;
-  }
-  return hipGetLastError();
+  if (a.nwaves == 8 && G * D <= 512) return attn_dec_dw<D, 8>(a, G, st);
+  return attn_dec_dw<D, 4>(a, G, st);
 }
 
 hipError_t launch_attention_decode(const AttnDecArgs& a, hipStream_t st) {
   const int G = a.H / a.KV;
   if (G < 1 || G > 8 || a.nsplit < 1) return hipErrorInvalidValue;
+  hipError_t e;
   switch (a.D) {
-    case 32: return attn_dec_d<32>(a, G, st);
-    case 64: return attn_dec_d<64>(a, G, st);
-    case 128: return attn_dec_d<128>(a, G, st);
-    case 256: return attn_dec_d<256>(a, G, st);
+    case 32: e = attn_dec_d<32>(a, G, st); break;
+    case 64: e = attn_dec_d<64>(a, G, st); break;
+    case 128: e = attn_dec_d<128>(a, G, st); break;
+    case 256: e = attn_dec_d<256>(a, G, st); break;
     default: return hipErrorInvalidValue;
   }
+  if (e != hipSuccess || a.nsplit == 1 || a.merge_last) return e;
+  hipLaunchKernelGGL(k_attn_dec_merge, dim3(a.H, a.B), dim3(128), 0, st, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_flash_prefill(const FlashArgs& a, int n_tiles, hipStream_t st) {
@@ -1709,18 +1479,5 @@ hipError_t launch_flash_prefill(const FlashArgs& a, int n_tiles, hipStream_t st)
   return hipGetLastError();
 }
 
-hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
-  const int G = a.H / a.KV;
-  hipError_t e;
-  switch (a.D) {
-    case 32: e = attn_d<32>(a, G, st); break;
-    case 64: e = attn_d<64>(a, G, st); break;
-    case 128: e = attn_d<128>(a, G, st); break;
-    default: e = attn_d<256>(a, G, st); break;
-  }
-  if (e != hipSuccess || a.nsplit == 1) return e;
-  hipLaunchKernelGGL(k_attn_merge, dim3(a.H, a.M), dim3(128), 0, st, a);
-  return hipGetLastError();
-}
 
 }  // namespace qd
