@@ -65,6 +65,30 @@ def prefill_flops(s, M):
     return L * (gemm + attn) + 2 * d * V
 
 
+KERNEL_SOURCE = os.path.join(ROOT, "int8_weight_only_amd", "csrc", "qd_kernels.hip")
+
+
+def measured_traffic(path, kernel_class):
+    """HBM bytes per launch of a decode kernel class from a committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, calibrated against a plain copy), or None when the
+    summary is missing or was taken on a different kernel source."""
+    import hashlib
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    if f"kernel source sha256: {sha}" not in text:
+        return None
+    for line in text.splitlines():
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) >= 4 and cells[0] == kernel_class:
+            try:
+                return int(cells[3])
+            except ValueError:
+                return None
+    return None
+
+
 def oracle_gate(model, shape, w, prompt, bar, n_chk=3):
     """Sampled full-size parity: quantized codes/scales bit-exact on sampled matrices;
     teacher-forced logits of the prefill row and the next decode steps within ``bar``;
@@ -167,7 +191,23 @@ def main():
                     help="batched decode lines measured after the main one ('' for none)")
     ap.add_argument("--no-extra", action="store_true", help="same as --extra-batches ''")
     ap.add_argument("--no-oracle", action="store_true", help="skip parity gate and CPU baseline")
+    ap.add_argument("--kernels-only", action="store_true",
+                    help="no captured graphs and few dispatches: prefill prompt+new-2 tokens, "
+                         "one decode step, then the per-kernel timing pass (for counter runs)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB five times (to calibrate "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE against known bytes) and exit")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_per_dispatch": n}), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the decode path is not "
               f"sharded across GPUs", file=sys.stderr)
@@ -190,7 +230,7 @@ def main():
     log(f"[bench] weights drawn in {time.time() - t:.1f}s")
     t = time.time()
     model = qd.Model(shape, w, max_batch=max_batch, max_ctx=ctx,
-                     max_prefill_tokens=max_batch * NP)
+                     max_prefill_tokens=max_batch * (NP + NN if args.kernels_only else NP))
     torch.cuda.synchronize()
     log(f"[bench] loaded + quantized on GPU in {time.time() - t:.1f}s")
     prompts = make_prompts(shape.vocab, NP, B, seed0=1000)
@@ -198,6 +238,18 @@ def main():
         bar = bar_for(args.shape)[0]
     except KeyError:
         bar = None
+
+    if args.kernels_only:
+        # same launch configuration as the timing pass below (context NP + NN - 1) with few
+        # dispatches: prefill NP + NN - 2 tokens, one decode step, then the per-kernel pass
+        long_prompts = make_prompts(shape.vocab, NP + NN - 2, B, seed0=1000)
+        nxt, _ = model.prefill(list(long_prompts))
+        model.decode_step(nxt)
+        prof = model.profile_kernels(B, iters=4 * shape.n_layers)
+        torch.cuda.synchronize()
+        print(json.dumps({"kernels_only": True, "per_kernel_us": prof}), flush=True)
+        model.close()
+        return
 
     parity, cpu = {"checked": False}, None
     if not args.no_oracle:
@@ -227,8 +279,10 @@ def main():
     per_token = {k: prof[k] * (shape.n_layers if k not in ("lmhead", "embed") else 1) for k in prof}
     dom = max(per_token, key=per_token.get)
     achieved = kb[dom] / (prof[dom] * 1e-6) / 1e9
+    traffic = measured_traffic(os.path.join(ROOT, "profiles", f"decode_b{B}_{args.shape}_traffic.md"),
+                               dom) if (NP, NN) == (256, 128) else None
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
                 "kernel": dom, "avg_launch_us": round(prof[dom], 3),
                 "bytes_per_launch": kb[dom],
                 "per_kernel_us": {k: round(v, 3) for k, v in prof.items()},

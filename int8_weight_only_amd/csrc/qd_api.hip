@@ -210,6 +210,12 @@ struct qd_model {
   std::map<std::tuple<int, int, int>, hipGraphExec_t> graphs;  // (B, nsplit, split_len)
   std::vector<int> host_pos;                                   // mirror of device positions
   hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+  // pinned host staging for prompt ids and prefill metadata: asynchronous uploads read
+  // from here, so the source outlives the copy; stage_ev guards reuse
+  int* hstage = nullptr;
+  size_t hstage_ints = 0;
+  hipEvent_t stage_ev = nullptr;
+  bool stage_pending = false;
   int attn_max_splits = 64;
   int attn_min_chunks = 1;
   int attn_waves = 0;  // 0: eight waves only when B x KV heads fill the GPU without splits
@@ -381,39 +387,68 @@ qd_status enqueue_decode(qd_model* m, int B, const int* in_ids, float* logits, i
                          write_out, st);
 }
 
+// staging layout (ints): [prompt ids: Mmax][row_slot: Mmax][row_pos: Mmax][last: B][lens: B]
+// [tiles: 4 * (Mmax / FLASH_ROWS + B + 1)]
+size_t stage_ints(const Plan& P, int B) {
+  return (size_t)4 * P.mmax + 2 * (size_t)B + 4 * ((size_t)P.mmax / FLASH_ROWS + B + 1);
+}
+
+qd_status stage_wait(qd_model* m) {
+  if (m->stage_pending) {
+    HIPCHK(hipEventSynchronize(m->stage_ev));
+    m->stage_pending = false;
+  }
+  return QD_OK;
+}
+
+qd_status stage_mark(qd_model* m, hipStream_t st) {
+  HIPCHK(hipEventRecord(m->stage_ev, st));
+  m->stage_pending = true;
+  return QD_OK;
+}
+
 // prefill of n prompts whose ids are already in the workspace (P.ids), metadata on host
 qd_status enqueue_prefill(qd_model* m, int n, const int* ids_dev, const std::vector<int>& lens,
                           float* logits, int* next_ids, bool write_out, hipStream_t st) {
   const Dims& d = m->d;
   const Plan& P = m->P;
-  int M = 0, maxlen = 0;
-  std::vector<int> rs, rp, last(n), tiles;
+  qd_status sw = stage_wait(m);
+  if (sw != QD_OK) return sw;
+  const int Bmax = m->lim.max_batch;
+  int* h_rs = m->hstage + P.mmax;
+  int* h_rp = h_rs + P.mmax;
+  int* h_last = h_rp + P.mmax;
+  int* h_lens = h_last + Bmax;
+  int* h_tiles = h_lens + Bmax;
+  int M = 0, n_tiles = 0;
   for (int b = 0; b < n; ++b) {
     for (int p0 = 0; p0 < lens[b]; p0 += FLASH_ROWS) {
-      tiles.push_back(M + p0);
-      tiles.push_back(b);
-      tiles.push_back(p0);
-      tiles.push_back(std::min(FLASH_ROWS, lens[b] - p0));
+      h_tiles[4 * n_tiles + 0] = M + p0;
+      h_tiles[4 * n_tiles + 1] = b;
+      h_tiles[4 * n_tiles + 2] = p0;
+      h_tiles[4 * n_tiles + 3] = std::min(FLASH_ROWS, lens[b] - p0);
+      ++n_tiles;
     }
     for (int t = 0; t < lens[b]; ++t) {
-      rs.push_back(b);
-      rp.push_back(t);
+      h_rs[M + t] = b;
+      h_rp[M + t] = t;
     }
     M += lens[b];
-    last[b] = M - 1;
-    maxlen = std::max(maxlen, lens[b]);
+    h_last[b] = M - 1;
+    h_lens[b] = lens[b];
   }
-  const int n_tiles = (int)tiles.size() / 4;
   int* row_slot = m->ws<int>(P.row_slot);
   int* row_pos = m->ws<int>(P.row_pos);
   int* last_rows = m->ws<int>(P.last_rows);
   int* dlens = m->ws<int>(P.lens);
   int4* dtiles = m->ws<int4>(P.tiles);
-  HIPCHK(hipMemcpyAsync(row_slot, rs.data(), M * 4, hipMemcpyHostToDevice, st));
-  HIPCHK(hipMemcpyAsync(row_pos, rp.data(), M * 4, hipMemcpyHostToDevice, st));
-  HIPCHK(hipMemcpyAsync(last_rows, last.data(), n * 4, hipMemcpyHostToDevice, st));
-  HIPCHK(hipMemcpyAsync(dlens, lens.data(), n * 4, hipMemcpyHostToDevice, st));
-  HIPCHK(hipMemcpyAsync(dtiles, tiles.data(), tiles.size() * 4, hipMemcpyHostToDevice, st));
+  HIPCHK(hipMemcpyAsync(row_slot, h_rs, M * 4, hipMemcpyHostToDevice, st));
+  HIPCHK(hipMemcpyAsync(row_pos, h_rp, M * 4, hipMemcpyHostToDevice, st));
+  HIPCHK(hipMemcpyAsync(last_rows, h_last, n * 4, hipMemcpyHostToDevice, st));
+  HIPCHK(hipMemcpyAsync(dlens, h_lens, n * 4, hipMemcpyHostToDevice, st));
+  HIPCHK(hipMemcpyAsync(dtiles, h_tiles, (size_t)n_tiles * 16, hipMemcpyHostToDevice, st));
+  sw = stage_mark(m, st);
+  if (sw != QD_OK) return sw;
 
   bf16_t* x = m->ws<bf16_t>(P.x);
   bf16_t* h = m->ws<bf16_t>(P.h);
@@ -562,7 +597,7 @@ qd_status qd_load_weights(const qd_model_shape* shape, const qd_limits* limits,
   m->host_pos.assign(limits->max_batch, 0);
   hipStream_t s = (hipStream_t)stream;
   auto cleanup_fail = [&](qd_status code) {
-    delete m;
+    qd_free(m);
     return code;
   };
 #define LCHK(expr)                                                                        \
@@ -598,6 +633,9 @@ qd_status qd_load_weights(const qd_model_shape* shape, const qd_limits* limits,
   LCHK(launch_fill_i32(m->ws<int>(P.done), 16, 0, s));
   LCHK(launch_fill_i32(m->ws<int>(P.step), 16, 0, s));
   LCHK(hipStreamCreateWithFlags(&m->cap_stream, hipStreamNonBlocking));
+  m->hstage_ints = stage_ints(P, limits->max_batch);
+  LCHK(hipHostMalloc((void**)&m->hstage, m->hstage_ints * 4, hipHostMallocDefault));
+  LCHK(hipEventCreateWithFlags(&m->stage_ev, hipEventDisableTiming));
   for (int i = 0; i < 3; ++i) LCHK(hipEventCreate(&m->ev[i]));
 #undef LCHK
   *out = m;
@@ -731,7 +769,12 @@ qd_status qd_generate_greedy(qd_model* m, int32_t B, const int32_t* prompt_ids_h
   const Plan& P = m->P;
   int* ids_dev = m->ws<int>(P.ids);
   int* next_ids = m->ws<int>(P.next_ids);
-  HIPCHK(hipMemcpyAsync(ids_dev, prompt_ids_host, total * 4, hipMemcpyHostToDevice, st));
+  {
+    qd_status sw = stage_wait(m);
+    if (sw != QD_OK) return sw;
+    std::memcpy(m->hstage, prompt_ids_host, (size_t)total * 4);
+    HIPCHK(hipMemcpyAsync(ids_dev, m->hstage, total * 4, hipMemcpyHostToDevice, st));
+  }
   HIPCHK(launch_fill_i32(m->ws<int>(P.step), 1, 0, st));
   HIPCHK(hipEventRecord(m->ev[0], st));
   qd_status s = enqueue_prefill(m, B, ids_dev, lens, nullptr, next_ids, true, st);
@@ -852,8 +895,8 @@ qd_status qd_set_tuning(qd_model* m, int32_t knob, int32_t value) {
       m->attn_merge_last = value;
       break;
     case QD_TUNE_ATTN_WAVES:
-      if (value != 0 && value != 4 && value != 8)
-        return fail(QD_ERR_INVALID_ARGUMENTS, "attention waves must be 0 (by batch), 4 or 8");
+      if (value != 0 && value != 4 && value != 8 && value != 16)
+        return fail(QD_ERR_INVALID_ARGUMENTS, "attention waves must be 0 (by batch), 4, 8 or 16");
       m->attn_waves = value;
       break;
     default: return fail(QD_ERR_INVALID_ARGUMENTS, "unknown knob");
@@ -869,6 +912,11 @@ void qd_free(qd_model* m) {
   for (int i = 0; i < 3; ++i)
     if (m->ev[i]) (void)hipEventDestroy(m->ev[i]);
   if (m->cap_stream) (void)hipStreamDestroy(m->cap_stream);
+  if (m->stage_ev) {
+    (void)hipEventSynchronize(m->stage_ev);
+    (void)hipEventDestroy(m->stage_ev);
+  }
+  if (m->hstage) (void)hipHostFree(m->hstage);
   delete m;
 }
 

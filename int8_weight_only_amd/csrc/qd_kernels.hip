@@ -198,27 +198,32 @@ __device__ __forceinline__ void lm_head_store(const GemvArgs& a, unsigned long l
   if (tid < a.nb && tid < nb_max) a.part_keys[(size_t)tid * LM_MAX_GRID + blockIdx.x] = best;
 }
 
-// one work-group: wave w reduces batch rows w, w+4, ... over the LM-head work-groups'
-// keys and writes the greedy ids (and advances positions and the step counter)
+// one work-group per batch row: reduces that row's keys over the LM-head work-groups and
+// writes the greedy id (advancing its position); work-group 0 advances the step counter
+// once every row has read it (k_lm_finish_step, launched after)
 __global__ __launch_bounds__(256) void k_lm_finish(GemvArgs a, int nblocks) {
+  __shared__ unsigned long long red[4];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  for (int b = wid; b < a.nb; b += 4) {
-    unsigned long long k = 0ull;
-    for (int i = lane; i < nblocks; i += 64) {
-      const unsigned long long v = a.part_keys[(size_t)b * LM_MAX_GRID + i];
-      k = v > k ? v : k;
-    }
-    k = wave_max_u64(k);
-    if (lane == 0) {
-      const int id = key_index(k);
-      a.next_ids[b] = id;
-      if (a.out_ids) a.out_ids[(size_t)(a.batch0 + b) * a.out_ld + *a.step] = id;
-      if (a.pos) a.pos[b] += 1;
-    }
+  const int b = blockIdx.x;
+  unsigned long long k = 0ull;
+  for (int i = tid; i < nblocks; i += 256) {
+    const unsigned long long v = a.part_keys[(size_t)b * LM_MAX_GRID + i];
+    k = v > k ? v : k;
   }
+  k = wave_max_u64(k);
+  if (lane == 0) red[wid] = k;
   __syncthreads();
-  if (tid == 0 && a.bump_step) *a.step += 1;
+  if (tid == 0) {
+    for (int w = 1; w < 4; ++w) k = red[w] > k ? red[w] : k;
+    k = red[0] > k ? red[0] : k;
+    const int id = key_index(k);
+    a.next_ids[b] = id;
+    if (a.out_ids) a.out_ids[(size_t)(a.batch0 + b) * a.out_ld + *a.step] = id;
+    if (a.pos) a.pos[b] += 1;
+  }
 }
+
+__global__ void k_lm_finish_step(int* step) { *step += 1; }
 
 // ------------------------------------------------------------------------------------------
 // single-row decode GEMV: y[n] = scale[n] * sum_k x[k] * W[n][k].
@@ -532,11 +537,11 @@ __global__ __launch_bounds__(256) void k_gemm_finish(GemmArgs a) {
 // work-group owns CTW 16-channel tiles; its four waves take interleaved 128-k blocks
 // (each lane group streams 128 contiguous bytes of a weight row) and the partial sums
 // meet in LDS.  The k order inside a block is permuted identically for both operands.
-template <int TT, int EPI>
-__global__ __launch_bounds__(256) void k_skinny(GemvArgs a) {
+template <int TT, int EPI, int NWS>
+__global__ __launch_bounds__(64 * NWS) void k_skinny(GemvArgs a) {
   constexpr int CTW = (EPI == EPI_SILU) ? 2 : 1;
   constexpr int NACC = CTW * TT;
-  __shared__ float red[4][NACC][4][64];
+  __shared__ float red[NWS][NACC][4][64];
   __shared__ unsigned long long kl[TT * 16][16];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int K = a.K;
@@ -569,11 +574,11 @@ __global__ __launch_bounds__(256) void k_skinny(GemvArgs a) {
       wrow[c] = reinterpret_cast<const int*>(a.W + (size_t)(wok[c] ? ch : 0) * K);
     }
     const int nkb = (K + 127) / 128;
-    const int nmine = (nkb - wid + 3) / 4;  // this wave's blocks: wid, wid+4, ...
+    const int nmine = (nkb - wid + NWS - 1) / NWS;  // this wave's blocks: wid, wid+NWS, ...
     const int rot = nmine > 0 ? tile % nmine : 0;
     for (int ib = 0; ib < nmine; ++ib) {
       const int ii = ib + rot;
-      const int kb = (wid + 4 * (ii >= nmine ? ii - nmine : ii)) * 128;
+      const int kb = (wid + NWS * (ii >= nmine ? ii - nmine : ii)) * 128;
       const int k0 = kb + 32 * grp;
       const bool kok = k0 < K;
       uint4 wv[CTW][2];
@@ -613,14 +618,16 @@ __global__ __launch_bounds__(256) void k_skinny(GemvArgs a) {
         for (int i = 0; i < 4; ++i) red[wid][c * TT + tt][i][lane] = acc[c][tt][i];
     __syncthreads();
     // element (tt, i, l): channel tile*16*CTW + c*16 + 4*(l/16) + i, token tt*16 + l%16
-    for (int e = tid; e < TT * 4 * 64; e += 256) {
-      const int tt = e / 256, i = (e / 64) % 4, l = e % 64;
+    for (int e = tid; e < TT * 4 * 64; e += 64 * NWS) {
+      const int tt = e / 256, i = (e / 64) % 4, l = e % 64;  // e < TT*256
       const int tok = tt * 16 + (l & 15);
       float v[CTW];
 #pragma unroll
-      for (int c = 0; c < CTW; ++c)
-        v[c] = red[0][c * TT + tt][i][l] + red[1][c * TT + tt][i][l] + red[2][c * TT + tt][i][l] +
-               red[3][c * TT + tt][i][l];
+      for (int c = 0; c < CTW; ++c) {
+        v[c] = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NWS; ++w) v[c] += red[w][c * TT + tt][i][l];
+      }
       const int ch = tile * 16 * CTW + 4 * (l >> 4) + i;
       if (EPI == EPI_SILU) {
         if (tok < a.nb && ch + 16 < a.N) {
@@ -1352,7 +1359,10 @@ static hipError_t gemv1(const GemvArgs& a, int epi, hipStream_t st) {
 }
 
 static hipError_t lm_finish(const GemvArgs& a, int nblocks, hipStream_t st) {
-  hipLaunchKernelGGL(k_lm_finish, dim3(1), dim3(256), 0, st, a, nblocks);
+  hipLaunchKernelGGL(k_lm_finish, dim3(a.nb), dim3(256), 0, st, a, nblocks);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !a.bump_step) return e;
+  hipLaunchKernelGGL(k_lm_finish_step, dim3(1), dim3(1), 0, st, a.step);
   return hipGetLastError();
 }
 
@@ -1377,11 +1387,20 @@ static hipError_t skinny_tt(const GemvArgs& a, int epi, hipStream_t st) {
     return e != hipSuccess ? e : lm_finish(a, g, st);
   }
   const int ctw = epi == EPI_SILU ? 2 : 1;
-  dim3 grid((a.N + 16 * ctw - 1) / (16 * ctw));
-  switch (epi) {
-    case EPI_STORE: hipLaunchKernelGGL((k_skinny<TT, EPI_STORE>), grid, dim3(256), 0, st, a); break;
-    case EPI_RESID: hipLaunchKernelGGL((k_skinny<TT, EPI_RESID>), grid, dim3(256), 0, st, a); break;
-    default: hipLaunchKernelGGL((k_skinny<TT, EPI_SILU>), grid, dim3(256), 0, st, a); break;
+  const int ntiles = (a.N + 16 * ctw - 1) / (16 * ctw);
+  dim3 grid(ntiles);
+  if (ntiles < 128) {  // few tiles: eight waves split K eight ways
+    switch (epi) {
+      case EPI_STORE: hipLaunchKernelGGL((k_skinny<TT, EPI_STORE, 8>), grid, dim3(512), 0, st, a); break;
+      case EPI_RESID: hipLaunchKernelGGL((k_skinny<TT, EPI_RESID, 8>), grid, dim3(512), 0, st, a); break;
+      default: hipLaunchKernelGGL((k_skinny<TT, EPI_SILU, 8>), grid, dim3(512), 0, st, a); break;
+    }
+  } else {
+    switch (epi) {
+      case EPI_STORE: hipLaunchKernelGGL((k_skinny<TT, EPI_STORE, 4>), grid, dim3(256), 0, st, a); break;
+      case EPI_RESID: hipLaunchKernelGGL((k_skinny<TT, EPI_RESID, 4>), grid, dim3(256), 0, st, a); break;
+      default: hipLaunchKernelGGL((k_skinny<TT, EPI_SILU, 4>), grid, dim3(256), 0, st, a); break;
+    }
   }
   return hipGetLastError();
 }
@@ -1443,10 +1462,11 @@ static hipError_t attn_dec_dw(const AttnDecArgs& a, int G, hipStream_t st) {
   return hipGetLastError();
 }
 
-// eight waves (128 positions per iteration) when the wave-merge buffers stay small
+// 8 or 16 waves (128 or 256 positions per iteration) when the wave-merge buffers stay small
 template <int D>
 static hipError_t attn_dec_d(const AttnDecArgs& a, int G, hipStream_t st) {
-  if (a.nwaves == 8 && G * D <= 512) return attn_dec_dw<D, 8>(a, G, st);
+  if (a.nwaves == 16 && G * D <= 512) return attn_dec_dw<D, 16>(a, G, st);
+  if (a.nwaves >= 8 && G * D <= 512) return attn_dec_dw<D, 8>(a, G, st);
   return attn_dec_dw<D, 4>(a, G, st);
 }
 
