@@ -61,9 +61,17 @@ def test_quantization_bit_exact(shape):
         m.close()
 
 
-def _teacher_forced(m, shape, qm, prompt, n_steps, label, config):
-    """Prefill + n_steps decode steps fed the oracle's ids; check every step."""
-    orc = Oracle(shape, qm, mode="bf16").generate(prompt, n_steps + 1)
+PERSIST = [1, 0]
+PERSIST_IDS = ["persistent", "per-step"]
+
+
+def _teacher_forced(m, shape, qm, prompt, n_steps, label, config, persist=1, orc=None):
+    """Prefill + n_steps decode steps fed the oracle's ids; check every step.  persist=1:
+    B=1 steps run as the persistent cooperative launch; 0: the per-step kernels."""
+    if orc is None:
+        orc = Oracle(shape, qm, mode="bf16").generate(prompt, n_steps + 1)
+    m.set_tuning(persistent=persist)
+    label = f"{label} {PERSIST_IDS[1 - persist]}"
     nxt, lg = m.prefill([prompt], logits=True)
     torch.cuda.synchronize()
     errs = [check_step(lg[0].cpu().numpy(), nxt[0].item(), orc["logits"][0], orc["margin"][0],
@@ -80,30 +88,44 @@ def _teacher_forced(m, shape, qm, prompt, n_steps, label, config):
     return errs
 
 
-def test_teacher_forced_tiny(tiny_setup):
+@pytest.mark.parametrize("persist", PERSIST, ids=PERSIST_IDS)
+def test_teacher_forced_tiny(tiny_setup, persist):
     shape, w, qm, m = tiny_setup
-    say("[gpu] teacher-forced tiny, 16-token prompt, 16 steps")
-    _teacher_forced(m, shape, qm, make_prompt(shape.vocab, 16, 1000), 16, "tiny", "tiny")
+    say(f"[gpu] teacher-forced tiny, 16-token prompt, 16 steps, persistent={persist}")
+    try:
+        _teacher_forced(m, shape, qm, make_prompt(shape.vocab, 16, 1000), 16, "tiny", "tiny",
+                        persist)
+    finally:
+        m.set_tuning(persistent=0)
 
 
 @pytest.mark.parametrize("shape,config", [(WIDE, "wide"), (ODD, "odd")], ids=["wide", "odd"])
 def test_teacher_forced_other_shapes(shape, config):
     w = make_weights(shape, seed=1, gains="uniform")
     qm = quantize_model(w)
+    prompt = make_prompt(shape.vocab, 77, 1001)
+    orc = Oracle(shape, qm, mode="bf16").generate(prompt, 13)
     say(f"[gpu] teacher-forced {shape}")
     m = _model(shape, w, max_batch=2, max_ctx=200, max_prefill_tokens=200)
     try:
-        # a prompt longer than one 64-position attention chunk, with a ragged tail
-        _teacher_forced(m, shape, qm, make_prompt(shape.vocab, 77, 1001), 12, config, config)
+        # a prompt longer than one attention chunk, with a ragged tail
+        for persist in PERSIST:
+            _teacher_forced(m, shape, qm, prompt, 12, config, config, persist, orc)
     finally:
         m.close()
 
 
-def test_generate_greedy_matches_oracle(tiny_setup):
+@pytest.mark.parametrize("persist", PERSIST, ids=PERSIST_IDS)
+def test_generate_greedy_matches_oracle(tiny_setup, persist):
     shape, w, qm, m = tiny_setup
     prompt = make_prompt(shape.vocab, 16, 1000)
-    say("[gpu] generate_greedy tiny 16+16")
-    res = m.generate_greedy([prompt], 16)
+    say(f"[gpu] generate_greedy tiny 16+16, persistent={persist}")
+    m.set_tuning(persistent=persist)
+    try:
+        res = m.generate_greedy([prompt], 16)
+    finally:
+        m.set_tuning(persistent=0)
+    assert res.persistent == bool(persist)
     orc = Oracle(shape, qm, mode="bf16").generate(prompt, 16)
     got = res.generated[0]
     # identical up to the first step whose oracle margin is not decisive
@@ -114,6 +136,31 @@ def test_generate_greedy_matches_oracle(tiny_setup):
         assert got[k] == orc["ids"][k], f"step {k}"
     assert res.token_ids[0][:16] == list(prompt)
     assert res.steps == 15 and res.decode_us > 0 and res.prefill_us > 0
+
+
+@pytest.mark.parametrize("shape,config,seed", [(TINY, "tiny", 0), (WIDE, "wide", 1),
+                                               (ODD, "odd", 1)], ids=["tiny", "wide", "odd"])
+def test_persistent_generate_matches_per_step(shape, config, seed):
+    """One persistent launch of all steps gives the ids of the per-step kernels wherever the
+    oracle's margin decides them (and the launch reports that it was persistent)."""
+    w = make_weights(shape, seed=seed, gains="uniform")
+    qm = quantize_model(w)
+    prompt = make_prompt(shape.vocab, 40, 1020)
+    say(f"[gpu] persistent vs per-step generate {config}, 40+24")
+    m = _model(shape, w, max_batch=1, max_ctx=128, max_prefill_tokens=64)
+    try:
+        m.set_tuning(persistent=1)
+        a = m.generate_greedy([prompt], 24)
+        m.set_tuning(persistent=0)
+        b = m.generate_greedy([prompt], 24)
+    finally:
+        m.close()
+    assert a.persistent and not b.persistent and a.steps == b.steps == 23
+    orc = Oracle(shape, qm, mode="bf16").generate(prompt, 24)
+    for k in range(24):
+        if orc["margin"][k] <= bar_for(config)[1]:
+            break
+        assert a.generated[0, k] == b.generated[0, k] == orc["ids"][k], k
 
 
 def test_generate_repeat_is_deterministic(tiny_setup):
@@ -226,23 +273,31 @@ def test_teacher_forced_mid_split_k():
     """hidden 512 / head_dim 128: prefill GEMMs take the split-K path, flash prefill D=128."""
     w = make_weights(MID, seed=4, gains="uniform")
     qm = quantize_model(w)
+    prompt = make_prompt(MID.vocab, 200, 1004)
+    orc = Oracle(MID, qm, mode="bf16").generate(prompt, 8)
     say("[gpu] teacher-forced mid (split-K prefill), 200-token prompt")
     m = _model(MID, w, max_batch=2, max_ctx=256, max_prefill_tokens=512)
     try:
-        _teacher_forced(m, MID, qm, make_prompt(MID.vocab, 200, 1004), 7, "mid", "mid")
+        for persist in PERSIST:
+            _teacher_forced(m, MID, qm, prompt, 7, "mid", "mid", persist, orc)
     finally:
         m.close()
 
 
 def test_teacher_forced_long_context():
-    """1500-token prompt: 24 prefill tiles per head, decode attention over ~24 splits that the
-    last split merges (the long-context path at a shape the oracle runs in seconds)."""
+    """1500-token prompt: 24 prefill tiles per head; decode attention over many position
+    splits (per-step kernels: ~24 merged splits; persistent: 12 splits of one 128-position
+    chunk, then 2 splits of 6 chunks each to run the multi-chunk loop)."""
     w = make_weights(WIDE, seed=5, gains="uniform")
     qm = quantize_model(w)
+    prompt = make_prompt(WIDE.vocab, 1500, 1005)
+    orc = Oracle(WIDE, qm, mode="bf16").generate(prompt, 24)
     say("[gpu] teacher-forced long context: 1500-token prompt, 23 decode steps")
     m = _model(WIDE, w, max_batch=1, max_ctx=2048, max_prefill_tokens=2048)
     try:
-        _teacher_forced(m, WIDE, qm, make_prompt(WIDE.vocab, 1500, 1005), 23, "wide-long",
-                        "wide-long")
+        for persist in PERSIST:
+            _teacher_forced(m, WIDE, qm, prompt, 23, "wide-long", "wide-long", persist, orc)
+        m.set_tuning(persist_splits=2)
+        _teacher_forced(m, WIDE, qm, prompt, 23, "wide-long 2 splits", "wide-long", 1, orc)
     finally:
         m.close()
