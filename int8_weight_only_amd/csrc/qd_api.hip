@@ -1052,8 +1052,8 @@ qd_status qd_set_tuning(qd_model* m, int32_t knob, int32_t value) {
       m->persist_splits = value;
       break;
     case QD_TUNE_ATTN_WAVES:
-      if (value != 0 && value != 4 && value != 8 && value != 16)
-        return fail(QD_ERR_INVALID_ARGUMENTS, "attention waves must be 0 (by batch), 4, 8 or 16");
+      if (value != 0 && value != 4 && value != 8)
+        return fail(QD_ERR_INVALID_ARGUMENTS, "attention waves must be 0 (by batch), 4 or 8");
       m->attn_waves = value;
       break;
     default: return fail(QD_ERR_INVALID_ARGUMENTS, "unknown knob");

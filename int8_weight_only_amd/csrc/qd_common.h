@@ -78,7 +78,7 @@ struct AttnDecArgs {
   bf16_t* kcache; bf16_t* vcache; // this layer's [slots][KV][ctx][D]
   int H, KV, D, max_ctx, B;
   int split_len, nsplit;
-  int nwaves;                     // 4, 8 or 16 waves per work-group (8, 16 only when G*D <= 512)
+  int nwaves;                     // 4 or 8 waves per work-group (8 only when G*D <= 512)
   int merge_last;                 // 1: the last split merges (fence + counter); 0: merge kernel
   float* part_o;                  // [B][H][nsplit][D]
   float* part_ml;                 // [B][H][nsplit][2]

@@ -806,33 +806,52 @@ __global__ __launch_bounds__(64 * NW) void k_attn_dec(AttnDecArgs a) {
       }
     }
   };
-  if (t_begin < t_end) load_tiles(kc, vc, t_begin);
-
   // ---- QK-norm + RoPE of the G query heads and the key head; copy of v ----
-  for (int hh = wid; hh <= G; hh += NW) {
-    const bool isq = hh < G;
-    const bf16_t* src = isq ? row + (size_t)(g * G + hh) * D : row + (size_t)(a.H + g) * D;
-    const float* gn = isq ? a.q_gain : a.k_gain;
-    float x1[2], x2[2], ss = 0.0f;
+  // The projections, gains and RoPE factors of this wave's first head are requested before
+  // the K/V tiles: a wave's loads retire in order, so the prologue then waits only for its
+  // own inputs while the tiles are still in flight.
+  auto head_src = [&](int hh) {
+    return hh < G ? row + (size_t)(g * G + hh) * D : row + (size_t)(a.H + g) * D;
+  };
+  float x1[2], x2[2], gg1[2], gg2[2];
+  float2 cs2[2];
+  auto head_load = [&](int hh) {
+    const bf16_t* src = head_src(hh);
+    const float* gn = hh < G ? a.q_gain : a.k_gain;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int i = lane + 64 * j;
-      x1[j] = x2[j] = 0.0f;
+      x1[j] = x2[j] = gg1[j] = gg2[j] = 0.0f;
+      cs2[j] = make_float2(0.0f, 0.0f);
       if (i < HALF) {
         x1[j] = bf2f(src[i]);
         x2[j] = bf2f(src[i + HALF]);
-        ss += x1[j] * x1[j] + x2[j] * x2[j];
+        gg1[j] = gn[i];
+        gg2[j] = gn[i + HALF];
+        cs2[j] = tab[i];
       }
     }
+  };
+  const bf16_t* vsrc = row + (size_t)(a.H + a.KV + g) * D;
+  const int vi = tid < D ? tid : 0;
+  const bf16_t vfirst = vsrc[vi];
+  if (wid <= G) head_load(wid);
+  if (t_begin < t_end) load_tiles(kc, vc, t_begin);
+  for (int hh = wid; hh <= G; hh += NW) {
+    if (hh != wid) head_load(hh);
+    const bool isq = hh < G;
+    float ss = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) ss += x1[j] * x1[j] + x2[j] * x2[j];
     ss = wave_sum(ss);
     const float inv = 1.0f / sqrtf(ss / (float)D + a.eps);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int i = lane + 64 * j;
       if (i < HALF) {
-        const float y1 = rbf(x1[j] * inv * gn[i]);
-        const float y2 = rbf(x2[j] * inv * gn[i + HALF]);
-        const float2 cs = tab[i];
+        const float y1 = rbf(x1[j] * inv * gg1[j]);
+        const float y2 = rbf(x2[j] * inv * gg2[j]);
+        const float2 cs = cs2[j];
         const bf16_t o1 = f2bf(y1 * cs.x - y2 * cs.y), o2 = f2bf(y2 * cs.x + y1 * cs.y);
         if (isq) {
           qs[hh][i] = bf2f(o1);
@@ -848,13 +867,10 @@ __global__ __launch_bounds__(64 * NW) void k_attn_dec(AttnDecArgs a) {
       }
     }
   }
-  {
-    const bf16_t* vsrc = row + (size_t)(a.H + a.KV + g) * D;
-    for (int i = tid; i < D; i += NT) {
-      const bf16_t v = vsrc[i];
-      vn[i] = bf2f(v);
-      if (owner) Vb[(size_t)p * D + i] = v;
-    }
+  for (int i = tid; i < D; i += NT) {
+    const bf16_t v = i == tid ? vfirst : vsrc[i];
+    vn[i] = bf2f(v);
+    if (owner) Vb[(size_t)p * D + i] = v;
   }
   __syncthreads();
 
@@ -1016,24 +1032,63 @@ __global__ __launch_bounds__(64 * NW) void k_attn_dec(AttnDecArgs a) {
 }
 
 // split merge as its own launch: o = sum_s o_s e^(m_s - m) / sum_s l_s e^(m_s - m)
-// for one (row b, query head); the kernel boundary orders it after every split
+// for one (row b, query head); the kernel boundary orders it after every split.  All
+// (max, sum) pairs and the first eight splits' partials are requested at once, so a short
+// context costs one memory round trip.
 __global__ __launch_bounds__(128) void k_attn_dec_merge(AttnDecArgs a) {
-  const int head = blockIdx.x, b = blockIdx.y;
-  const size_t base = ((size_t)b * a.H + head) * a.nsplit;
-  float mx = -INFINITY;
-  for (int q = 0; q < a.nsplit; ++q) mx = fmaxf(mx, a.part_ml[(base + q) * 2]);
-  float lsum = 0.0f;
-  for (int q = 0; q < a.nsplit; ++q) {
-    const float ms = a.part_ml[(base + q) * 2];
-    if (ms != -INFINITY) lsum += a.part_ml[(base + q) * 2 + 1] * expf(ms - mx);
+  __shared__ float wsp[ATT_MAX_SPLITS];  // e^(m_s - m), zero for an empty split
+  __shared__ float red[2];
+  constexpr int SB = 8;
+  const int head = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wid = tid >> 6;
+  const int ns = a.nsplit, D = a.D;
+  const size_t base = ((size_t)b * a.H + head) * ns;
+  float ov[2][SB];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int dd = tid + 128 * k;
+#pragma unroll
+    for (int s = 0; s < SB; ++s) ov[k][s] = (dd < D && s < ns) ? a.part_o[(base + s) * D + dd] : 0.0f;
   }
-  for (int dd = threadIdx.x; dd < a.D; dd += 128) {
+  float m0 = -INFINITY, l0 = 0.0f, m1 = -INFINITY, l1 = 0.0f;
+  if (tid < ns) {
+    m0 = a.part_ml[(base + tid) * 2];
+    l0 = a.part_ml[(base + tid) * 2 + 1];
+  }
+  if (tid + 128 < ns) {
+    m1 = a.part_ml[(base + tid + 128) * 2];
+    l1 = a.part_ml[(base + tid + 128) * 2 + 1];
+  }
+  float mx = wave_max(fmaxf(m0, m1));
+  if (lane == 0) red[wid] = mx;
+  __syncthreads();
+  mx = fmaxf(red[0], red[1]);
+  const float f0 = m0 == -INFINITY ? 0.0f : expf(m0 - mx);
+  const float f1 = m1 == -INFINITY ? 0.0f : expf(m1 - mx);
+  if (tid < ns) wsp[tid] = f0;
+  if (tid + 128 < ns) wsp[tid + 128] = f1;
+  float ls = wave_sum(l0 * f0 + l1 * f1);
+  __syncthreads();
+  if (lane == 0) red[wid] = ls;
+  __syncthreads();
+  const float lsum = red[0] + red[1];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int dd = tid + 128 * k;
+    if (dd >= D) continue;
     float acc = 0.0f;
-    for (int q = 0; q < a.nsplit; ++q) {
-      const float ms = a.part_ml[(base + q) * 2];
-      if (ms != -INFINITY) acc += a.part_o[(base + q) * a.D + dd] * expf(ms - mx);
+#pragma unroll
+    for (int s = 0; s < SB; ++s)
+      if (s < ns) acc += ov[k][s] * wsp[s];
+    for (int s0 = SB; s0 < ns; s0 += SB) {
+      float v[SB];
+#pragma unroll
+      for (int s = 0; s < SB; ++s) v[s] = s0 + s < ns ? a.part_o[(base + s0 + s) * D + dd] : 0.0f;
+#pragma unroll
+      for (int s = 0; s < SB; ++s)
+        if (s0 + s < ns) acc += v[s] * wsp[s0 + s];
     }
-    a.out[(size_t)b * a.ldo + (size_t)head * a.D + dd] = f2bf(acc / lsum);
+    a.out[(size_t)b * a.ldo + (size_t)head * D + dd] = f2bf(acc / lsum);
   }
 }
 
@@ -1384,10 +1439,9 @@ static hipError_t attn_dec_dw(const AttnDecArgs& a, int G, hipStream_t st) {
   return hipGetLastError();
 }
 
-// 8 or 16 waves (128 or 256 positions per iteration) when the wave-merge buffers stay small
+// 8 waves (128 positions per iteration) when the wave-merge buffers stay small
 template <int D>
 static hipError_t attn_dec_d(const AttnDecArgs& a, int G, hipStream_t st) {
-  if (a.nwaves == 16 && G * D <= 512) return attn_dec_dw<D, 16>(a, G, st);
   if (a.nwaves >= 8 && G * D <= 512) return attn_dec_dw<D, 8>(a, G, st);
   return attn_dec_dw<D, 4>(a, G, st);
 }
