@@ -227,7 +227,7 @@ typedef enum {
   QD_TUNE_ATTN_MAX_SPLITS = 0,    /* most position splits per (sequence, KV head); default 64 */
   QD_TUNE_ATTN_MIN_CHUNKS = 1,    /* fewest 64-position chunks per split; default 1 */
   QD_TUNE_ATTN_WAVES = 2,         /* decode-attention waves per work-group: 4, 8, or 0 = by batch (default) */
-  QD_TUNE_ATTN_MERGE_LAST = 3,    /* 1: the last split merges in-kernel; 0: a merge launch (default) */
+  QD_TUNE_ATTN_MERGE_LAST = 3,    /* 1 (default): the last split merges in-kernel; 0: a merge launch */
   QD_TUNE_PERSISTENT = 4,         /* 1: B = 1 decode runs as one persistent cooperative launch
                                      where the shape allows it (head_dim 32, 64 or 128, at most
                                      8 query heads per KV head); 0 (default): per-step kernels */

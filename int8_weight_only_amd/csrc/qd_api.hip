@@ -229,7 +229,7 @@ struct qd_model {
   int attn_max_splits = 64;
   int attn_min_chunks = 1;
   int attn_waves = 0;  // 0: eight waves only when B x KV heads fill the GPU without splits
-  int attn_merge_last = 0;
+  int attn_merge_last = 1;
   // persistent single-sequence decode (one cooperative launch per call)
   bool persist_ok = false;     // this shape and device can run it
   std::string persist_why;     // why not, when persist_ok is false

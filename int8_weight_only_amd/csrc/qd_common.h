@@ -79,7 +79,7 @@ struct AttnDecArgs {
   int H, KV, D, max_ctx, B;
   int split_len, nsplit;
   int nwaves;                     // 4 or 8 waves per work-group (8 only when G*D <= 512)
-  int merge_last;                 // 1: the last split merges (fence + counter); 0: merge kernel
+  int merge_last;                 // 1: the last split merges (agent-coherent partials + counter); 0: merge kernel
   float* part_o;                  // [B][H][nsplit][D]
   float* part_ml;                 // [B][H][nsplit][2]
   unsigned int* counters;         // [B][KV], zero on entry; the merging split resets it

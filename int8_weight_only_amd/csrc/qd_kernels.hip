@@ -994,41 +994,74 @@ __global__ __launch_bounds__(64 * NW) void k_attn_dec(AttnDecArgs a) {
       a.out[(size_t)b * a.ldo + (size_t)head * D + dd] = f2bf(O / L);
     } else {
       const size_t pi = ((size_t)b * a.H + head) * a.nsplit + s;
-      a.part_o[pi * D + dd] = O;
-      if (dd == 0) {
-        a.part_ml[pi * 2] = M;
-        a.part_ml[pi * 2 + 1] = L;
+      if (a.merge_last) {  // agent-coherent: the merging split reads them without a fence
+        __hip_atomic_store(a.part_o + pi * D + dd, O, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (dd == 0) {
+          __hip_atomic_store(a.part_ml + pi * 2, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(a.part_ml + pi * 2 + 1, L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      } else {
+        a.part_o[pi * D + dd] = O;
+        if (dd == 0) {
+          a.part_ml[pi * 2] = M;
+          a.part_ml[pi * 2 + 1] = L;
+        }
       }
     }
   }
   if (a.nsplit == 1 || !a.merge_last) return;
   // ---- the last split to finish merges all partials of this (row, KV head) ----
+  // Each wave's agent-coherent partial stores have completed (s_waitcnt 0) before thread 0
+  // counts the split in; the split that counts last reads every partial with
+  // agent-coherent loads issued after its count returned, so no cache write-back or
+  // invalidate is needed.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) {
-    __threadfence();
-    const unsigned int t = atomicAdd(a.counters + (size_t)b * a.KV + g, 1u);
+    const unsigned int t = __hip_atomic_fetch_add(a.counters + (size_t)b * a.KV + g, 1u,
+                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     last_flag = (t == (unsigned)a.nsplit - 1) ? 1 : 0;
   }
   __syncthreads();
   if (!last_flag) return;
-  __threadfence();
+  constexpr int SB = 8;
+  const int ns = a.nsplit;
+  auto ld = [](const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
   for (int idx = tid; idx < G * D; idx += NT) {
     const int h = idx / D, dd = idx % D;
     const int head = g * G + h;
-    const size_t base = ((size_t)b * a.H + head) * a.nsplit;
+    const size_t base = ((size_t)b * a.H + head) * ns;
+    // the first SB splits' (max, sum, output) in one round trip; later splits' maxima after
+    float mv[SB], lv[SB], ov[SB];
+#pragma unroll
+    for (int k = 0; k < SB; ++k) {
+      mv[k] = k < ns ? ld(a.part_ml + (base + k) * 2) : -INFINITY;
+      lv[k] = k < ns ? ld(a.part_ml + (base + k) * 2 + 1) : 0.0f;
+      ov[k] = k < ns ? ld(a.part_o + (base + k) * D + dd) : 0.0f;
+    }
     float mx = -INFINITY;
-    for (int q = 0; q < a.nsplit; ++q) mx = fmaxf(mx, a.part_ml[(base + q) * 2]);
+#pragma unroll
+    for (int k = 0; k < SB; ++k) mx = fmaxf(mx, mv[k]);
+    for (int q = SB; q < ns; ++q) mx = fmaxf(mx, ld(a.part_ml + (base + q) * 2));
     float lsum = 0.0f, acc = 0.0f;
-    for (int q = 0; q < a.nsplit; ++q) {
-      const float ms = a.part_ml[(base + q) * 2];
+#pragma unroll
+    for (int k = 0; k < SB; ++k) {
+      if (mv[k] == -INFINITY) continue;
+      const float w = expf(mv[k] - mx);
+      lsum += lv[k] * w;
+      acc += ov[k] * w;
+    }
+    for (int q = SB; q < ns; ++q) {
+      const float ms = ld(a.part_ml + (base + q) * 2);
       if (ms == -INFINITY) continue;
       const float w = expf(ms - mx);
-      lsum += a.part_ml[(base + q) * 2 + 1] * w;
-      acc += a.part_o[(base + q) * D + dd] * w;
+      lsum += ld(a.part_ml + (base + q) * 2 + 1) * w;
+      acc += ld(a.part_o + (base + q) * D + dd) * w;
     }
     a.out[(size_t)b * a.ldo + (size_t)head * D + dd] = f2bf(acc / lsum);
   }
-  if (tid == 0) atomicExch(a.counters + (size_t)b * a.KV + g, 0u);
+  if (tid == 0) __hip_atomic_store(a.counters + (size_t)b * a.KV + g, 0u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // split merge as its own launch: o = sum_s o_s e^(m_s - m) / sum_s l_s e^(m_s - m)
