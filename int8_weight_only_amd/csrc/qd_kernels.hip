@@ -173,6 +173,21 @@ __global__ __launch_bounds__(256) void k_gemv1(GemvArgs a) {
   };
 
   int blk = blockIdx.x;
+  // per-row scales (and residual values) of a block: requested with its weights, so the
+  // epilogue after the reductions does not wait for another round trip
+  float sc[NR], rs[R];
+  auto load_rowdata = [&](int b) {
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int r = row_of(b, i);
+      sc[i] = (r < a.N && b < nblk) ? a.scale[r] : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const int r = row_of(b, i);
+      rs[i] = (EPI == EPI_RESID && r < a.N && b < nblk) ? bf2f(a.out[r]) : 0.0f;
+    }
+  };
   // weights of the first block, requested before the activations
   int4 wv[NR][KC];
 #pragma unroll
@@ -186,18 +201,27 @@ __global__ __launch_bounds__(256) void k_gemv1(GemvArgs a) {
                      : make_int4(0, 0, 0, 0);
     }
   }
+  load_rowdata(blk);
   // activations (and the RMSNorm prologue) in registers
   const bf16_t* xrow = a.x + (size_t)(a.x_rows ? a.x_rows[0] : 0) * a.ldx;
   float xf[KC][16];
+  float4 gq[KC][4];  // RMSNorm gains of this lane's chunks, requested with the activations
   float ss = 0.0f;
 #pragma unroll
   for (int c = 0; c < KC; ++c) {
     const int ch = lane + 64 * c;
     uint4 u0 = make_uint4(0, 0, 0, 0), u1 = u0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) gq[c][q] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (ch < nchunk) {
       const uint4* xv = reinterpret_cast<const uint4*>(xrow + ch * 16);
       u0 = xv[0];
       u1 = xv[1];
+      if (a.gain) {
+        const float4* g4 = reinterpret_cast<const float4*>(a.gain + ch * 16);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) gq[c][q] = g4[q];
+      }
     }
     const uint32_t w8[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
 #pragma unroll
@@ -213,10 +237,9 @@ __global__ __launch_bounds__(256) void k_gemv1(GemvArgs a) {
     for (int c = 0; c < KC; ++c) {
       const int ch = lane + 64 * c;
       if (ch < nchunk) {
-        const float4* g4 = reinterpret_cast<const float4*>(a.gain + ch * 16);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const float4 g = g4[q];
+          const float4 g = gq[c][q];
           xf[c][4 * q + 0] = rbf(xf[c][4 * q + 0] / denom * g.x);
           xf[c][4 * q + 1] = rbf(xf[c][4 * q + 1] / denom * g.y);
           xf[c][4 * q + 2] = rbf(xf[c][4 * q + 2] / denom * g.z);
@@ -240,8 +263,14 @@ __global__ __launch_bounds__(256) void k_gemv1(GemvArgs a) {
         for (int j = 0; j < 16; ++j) acc[i] = fmaf(wf[j], xf[c][j], acc[i]);
       }
     }
-    // next block's weights go out before the reductions
+    // next block's weights (and its scales, below) go out before the reductions
     const int nxt = blk + gridDim.x;
+    float scn[NR];
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int r = row_of(nxt, i);
+      scn[i] = (nxt < nblk && r < a.N) ? a.scale[r] : 0.0f;
+    }
     if (nxt < nblk) {
 #pragma unroll
       for (int i = 0; i < NR; ++i) {
@@ -263,8 +292,8 @@ __global__ __launch_bounds__(256) void k_gemv1(GemvArgs a) {
         for (int i = 0; i < R; ++i) {
           const int j = blk * rows_per_blk + wid * R + i;
           if (j >= nout) continue;
-          const float g = rbf(acc[i] * a.scale[gu_row(j, 0)]);
-          const float u = rbf(acc[i + R] * a.scale[gu_row(j, 1)]);
+          const float g = rbf(acc[i] * sc[i]);
+          const float u = rbf(acc[i + R] * sc[i + R]);
           a.out[j] = f2bf(g / (1.0f + expf(-g)) * u);
         }
       } else {
@@ -272,11 +301,11 @@ __global__ __launch_bounds__(256) void k_gemv1(GemvArgs a) {
         for (int i = 0; i < R; ++i) {
           const int r = row_of(blk, i);
           if (r >= a.N) continue;
-          const float v = acc[i] * a.scale[r];
+          const float v = acc[i] * sc[i];
           if (EPI == EPI_STORE) {
             a.out[r] = f2bf(v);
           } else if (EPI == EPI_RESID) {
-            a.out[r] = f2bf(bf2f(a.out[r]) + rbf(v));
+            a.out[r] = f2bf(rs[i] + rbf(v));
           } else {
             if (a.logits) a.logits[r] = v;
             const unsigned long long k = argmax_key(v, r);
@@ -284,6 +313,13 @@ __global__ __launch_bounds__(256) void k_gemv1(GemvArgs a) {
           }
         }
       }
+    }
+#pragma unroll
+    for (int i = 0; i < NR; ++i) sc[i] = scn[i];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const int r = row_of(nxt, i);
+      rs[i] = (EPI == EPI_RESID && nxt < nblk && r < a.N) ? bf2f(a.out[r]) : 0.0f;
     }
   }
   if (EPI == EPI_LOGITS) {
@@ -481,7 +517,23 @@ __global__ __launch_bounds__(64 * NWS) void k_skinny(GemvArgs a) {
     xrow[tt] = a.x + (size_t)xr * a.ldx;
   }
 
+  // epilogue elements of this thread: e = tid + 64*NWS*q (token tile, row i, lane l)
+  constexpr int NE = (TT * 256 + 64 * NWS - 1) / (64 * NWS);
   for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    // their scales and residual inputs are requested before the k loop, so the epilogue
+    // after the wave reduction does not wait for another round trip
+    float esc[NE][CTW], eres[NE];
+#pragma unroll
+    for (int q = 0; q < NE; ++q) {
+      const int e = tid + 64 * NWS * q;
+      const int tt = e / 256, i = (e / 64) % 4, l = e % 64;
+      const int tok = tt * 16 + (l & 15);
+      const int ch = tile * 16 * CTW + 4 * (l >> 4) + i;
+      const bool ok = e < TT * 256 && tok < a.nb;
+#pragma unroll
+      for (int c = 0; c < CTW; ++c) esc[q][c] = (ok && ch + 16 * c < a.N) ? a.scale[ch + 16 * c] : 0.0f;
+      eres[q] = (EPI == EPI_RESID && ok && ch < a.N) ? bf2f(a.out[(size_t)tok * a.ldo + ch]) : 0.0f;
+    }
     f32x4_t acc[CTW][TT];
 #pragma unroll
     for (int c = 0; c < CTW; ++c)
@@ -540,7 +592,10 @@ __global__ __launch_bounds__(64 * NWS) void k_skinny(GemvArgs a) {
         for (int i = 0; i < 4; ++i) red[wid][c * TT + tt][i][lane] = acc[c][tt][i];
     __syncthreads();
     // element (tt, i, l): channel tile*16*CTW + c*16 + 4*(l/16) + i, token tt*16 + l%16
-    for (int e = tid; e < TT * 4 * 64; e += 64 * NWS) {
+#pragma unroll
+    for (int q = 0; q < NE; ++q) {
+      const int e = tid + 64 * NWS * q;
+      if (e >= TT * 4 * 64) break;
       const int tt = e / 256, i = (e / 64) % 4, l = e % 64;  // e < TT*256
       const int tok = tt * 16 + (l & 15);
       float v[CTW];
@@ -553,22 +608,22 @@ __global__ __launch_bounds__(64 * NWS) void k_skinny(GemvArgs a) {
       const int ch = tile * 16 * CTW + 4 * (l >> 4) + i;
       if (EPI == EPI_SILU) {
         if (tok < a.nb && ch + 16 < a.N) {
-          const float g = rbf(v[0] * a.scale[ch]), u = rbf(v[1] * a.scale[ch + 16]);
+          const float g = rbf(v[0] * esc[q][0]), u = rbf(v[CTW - 1] * esc[q][CTW - 1]);
           const int j = tile * GU_BLOCK + 4 * (l >> 4) + i;
           a.out[(size_t)tok * a.ldo + j] = f2bf(g / (1.0f + expf(-g)) * u);
         }
       } else if (EPI == EPI_LOGITS) {
         unsigned long long k = 0ull;
         if (tok < a.nb && ch < a.N) {
-          const float lv = v[0] * a.scale[ch];
+          const float lv = v[0] * esc[q][0];
           if (a.logits) a.logits[(size_t)tok * a.ldl + ch] = lv;
           k = argmax_key(lv, ch);
         }
         kl[tok][4 * (l >> 4) + i] = k;
       } else if (tok < a.nb && ch < a.N) {
-        const float y = v[0] * a.scale[ch];
+        const float y = v[0] * esc[q][0];
         bf16_t* o = a.out + (size_t)tok * a.ldo + ch;
-        *o = (EPI == EPI_STORE) ? f2bf(y) : f2bf(bf2f(*o) + rbf(y));
+        *o = (EPI == EPI_STORE) ? f2bf(y) : f2bf(eres[q] + rbf(y));
       }
     }
     if (EPI == EPI_LOGITS) {
