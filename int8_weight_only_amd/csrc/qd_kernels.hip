@@ -78,22 +78,65 @@ __global__ __launch_bounds__(256) void k_embed(const int* __restrict__ ids,
   for (int c = threadIdx.x; c < d; c += 256) x[(size_t)r * d + c] = f2bf((float)er[c] * s);
 }
 
-// RMSNorm of M rows: y = bf16(x / sqrt(mean(x^2) + eps) * g)
+// RMSNorm of M rows: y = bf16(x / sqrt(mean(x^2) + eps) * g).  Each thread owns chunks of
+// 8 elements (d % 8 == 0); a row of up to 8192 elements is requested in one round trip
+// together with its gains, larger rows loop.
 __global__ __launch_bounds__(256) void k_rmsnorm(const bf16_t* __restrict__ x, int d,
                                                  const float* __restrict__ g, float eps,
                                                  bf16_t* __restrict__ y) {
   __shared__ float red[4];
-  const int r = blockIdx.x;
+  constexpr int CPT = 4;
+  const int r = blockIdx.x, tid = threadIdx.x;
   const bf16_t* xr = x + (size_t)r * d;
+  bf16_t* yr = y + (size_t)r * d;
+  const int nch = d >> 3;
   float ss = 0.0f;
-  for (int c = threadIdx.x; c < d; c += 256) {
-    const float v = bf2f(xr[c]);
-    ss += v * v;
+  for (int c0 = 0; c0 < nch; c0 += CPT * 256) {
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) {
+      const int c = c0 + tid + 256 * q;
+      if (c < nch) {
+        const uint4 u = *reinterpret_cast<const uint4*>(xr + 8 * c);
+        const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float lo = __uint_as_float(w4[j] << 16), hi = __uint_as_float(w4[j] & 0xFFFF0000u);
+          ss += lo * lo + hi * hi;
+        }
+      }
+    }
   }
   ss = block_sum256(ss, red);
   const float denom = sqrtf(ss / (float)d + eps);
-  for (int c = threadIdx.x; c < d; c += 256)
-    y[(size_t)r * d + c] = f2bf(bf2f(xr[c]) / denom * g[c]);
+  for (int c0 = 0; c0 < nch; c0 += CPT * 256) {
+    uint4 u[CPT];
+    float4 g0[CPT], g1[CPT];
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) {
+      const int c = c0 + tid + 256 * q;
+      if (c < nch) {
+        u[q] = *reinterpret_cast<const uint4*>(xr + 8 * c);
+        g0[q] = *reinterpret_cast<const float4*>(g + 8 * c);
+        g1[q] = *reinterpret_cast<const float4*>(g + 8 * c + 4);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) {
+      const int c = c0 + tid + 256 * q;
+      if (c < nch) {
+        const uint32_t w4[4] = {u[q].x, u[q].y, u[q].z, u[q].w};
+        const float gv[8] = {g0[q].x, g0[q].y, g0[q].z, g0[q].w, g1[q].x, g1[q].y, g1[q].z, g1[q].w};
+        uint32_t o4[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bf16_t y0 = f2bf(__uint_as_float(w4[j] << 16) / denom * gv[2 * j]);
+          const bf16_t y1 = f2bf(__uint_as_float(w4[j] & 0xFFFF0000u) / denom * gv[2 * j + 1]);
+          o4[j] = (uint32_t)y0 | ((uint32_t)y1 << 16);
+        }
+        *reinterpret_cast<uint4*>(yr + 8 * c) = make_uint4(o4[0], o4[1], o4[2], o4[3]);
+      }
+    }
+  }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -362,14 +405,15 @@ __device__ __forceinline__ bf16x8_t i8x8_to_bf16x8(uint2 w) {
 // With split-K (blockIdx.z) each work-group covers a slice of K and stores fp32
 // partials; k_gemm_finish sums them in split order and applies the epilogue.
 template <int EPI>
-__device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, int m, int n, float v, float vu) {
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, int m, int n, float v, float vu,
+                                              float sv, float su) {
   if (EPI == EPI_SILU) {
-    const float g = rbf(v * a.scale[n]);
-    const float u = rbf(vu * a.scale[n + GU_BLOCK]);
+    const float g = rbf(v * sv);
+    const float u = rbf(vu * su);
     const int j = (n / (2 * GU_BLOCK)) * GU_BLOCK + (n % GU_BLOCK);
     a.out[(size_t)m * a.ldo + j] = f2bf(g / (1.0f + expf(-g)) * u);
   } else {
-    const float y = v * a.scale[n];
+    const float y = v * sv;
     bf16_t* o = a.out + (size_t)m * a.ldo + n;
     *o = (EPI == EPI_STORE) ? f2bf(y) : f2bf(bf2f(*o) + rbf(y));
   }
@@ -412,6 +456,14 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // scales of this lane's two output channels (gate/up: the pair), requested before the
+  // k loop so the epilogue does not wait for them
+  float gsc[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int n = n0 + wn * 32 + nt * 16 + r16;
+    gsc[nt] = (a.splits == 1 && n < a.N) ? a.scale[n] : 0.0f;
+  }
 
   int buf = 0;
   if (kbeg < kend) {
@@ -459,12 +511,13 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
         }
       } else if (EPI == EPI_SILU) {
         const int ng = n0 + wn * 32 + r16;
-        if (ng + GU_BLOCK < a.N) gemm_epilogue<EPI_SILU>(a, m, ng, acc[mt][0][i], acc[mt][1][i]);
+        if (ng + GU_BLOCK < a.N)
+          gemm_epilogue<EPI_SILU>(a, m, ng, acc[mt][0][i], acc[mt][1][i], gsc[0], gsc[1]);
       } else {
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
           const int n = n0 + wn * 32 + nt * 16 + r16;
-          if (n < a.N) gemm_epilogue<EPI>(a, m, n, acc[mt][nt][i], 0.0f);
+          if (n < a.N) gemm_epilogue<EPI>(a, m, n, acc[mt][nt][i], 0.0f, gsc[nt], 0.0f);
         }
       }
     }
@@ -484,7 +537,7 @@ __global__ __launch_bounds__(256) void k_gemm_finish(GemmArgs a) {
     v += a.part[((size_t)z * a.M + m) * a.N + n];
     if (EPI == EPI_SILU) vu += a.part[((size_t)z * a.M + m) * a.N + n + GU_BLOCK];
   }
-  gemm_epilogue<EPI>(a, m, n, v, vu);
+  gemm_epilogue<EPI>(a, m, n, v, vu, a.scale[n], EPI == EPI_SILU ? a.scale[n + GU_BLOCK] : 0.0f);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -665,6 +718,15 @@ __global__ __launch_bounds__(256) void k_lm_skinny(GemvArgs a) {
     const int ch = tile[t] * 16 + r16;
     wrow[t] = a.W + (size_t)(ch < a.N ? ch : 0) * K;
   }
+  // the scales of this lane's output channels are requested before the k loop
+  float lsc[LMT][4];
+#pragma unroll
+  for (int t = 0; t < LMT; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ch = tile[t] * 16 + 4 * grp + i;
+      lsc[t][i] = (tile[t] < ntiles && ch < a.N) ? a.scale[ch] : 0.0f;
+    }
   for (int kc = 0; kc < K; kc += KC) {
     const int klen = min(KC, K - kc);
     __syncthreads();
@@ -724,7 +786,7 @@ __global__ __launch_bounds__(256) void k_lm_skinny(GemvArgs a) {
       for (int i = 0; i < 4; ++i) {
         const int ch = tile[t] * 16 + 4 * grp + i;
         if (tok < a.nb && tile[t] < ntiles && ch < a.N) {
-          const float lv = acc[t][tt][i] * a.scale[ch];
+          const float lv = acc[t][tt][i] * lsc[t][i];
           if (a.logits) a.logits[(size_t)tok * a.ldl + ch] = lv;
           const unsigned long long k = argmax_key(lv, ch);
           best[tt] = k > best[tt] ? k : best[tt];
