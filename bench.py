@@ -65,19 +65,28 @@ def prefill_flops(s, M):
     return L * (gemm + attn) + 2 * d * V
 
 
-KERNEL_SOURCE = os.path.join(ROOT, "int8_weight_only_amd", "csrc", "qd_kernels.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "int8_weight_only_amd", "csrc", f)
+                  for f in ("qd_common.h", "qd_device.h", "qd_kernels.hip", "qd_persist.hip")]
+
+
+def kernel_source_sha() -> str:
+    """sha256 over the device sources, in a fixed order (a traffic summary is valid only for
+    the sources it was measured on)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 def measured_traffic(path, kernel_class):
     """HBM bytes per launch of a decode kernel class from a committed rocprofv3 counter
     summary (FETCH_SIZE + WRITE_SIZE, calibrated against a plain copy), or None when the
     summary is missing or was taken on a different kernel source."""
-    import hashlib
     if not os.path.exists(path):
         return None
     text = open(path).read()
-    sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
-    if f"kernel source sha256: {sha}" not in text:
+    if f"kernel source sha256: {kernel_source_sha()}" not in text:
         return None
     for line in text.splitlines():
         cells = [c.strip() for c in line.strip().strip("|").split("|")]

@@ -1245,9 +1245,9 @@ __global__ __launch_bounds__(128) void k_attn_dec_merge(AttnDecArgs a) {
 // ------------------------------------------------------------------------------------------
 // Prefill attention on MFMA (causal, flash style).  A work-group owns up to 64 query rows
 // of one sequence (4 waves x 16 rows) and one query head h of KV group g = h / (H/KV).
-// Keys and values advance in blocks of 32 positions staged once in LDS for all waves
+// Keys and values advance in blocks of 64 positions staged once in LDS for all waves
 // (V transposed so it feeds the MFMA B operand directly).  Per wave and block:
-// S = Q K^T (16 rows x 32 keys, fp32 accumulation of bf16 products), causal mask, online
+// S = Q K^T (16 rows x 64 keys, fp32 accumulation of bf16 products), causal mask, online
 // softmax in fp32 with each row's state in the lanes that hold that row of O, then
 // O += P V.  P is split into bf16 high and low parts (two MFMAs), so the probabilities
 // enter the product with ~16 significant bits rather than bf16's 8.
@@ -1268,7 +1268,8 @@ __device__ __forceinline__ float row16_sum(float v) {
 
 template <int D>
 __global__ __launch_bounds__(256) void k_flash_prefill(FlashArgs a) {
-  constexpr int KB = 32;             // keys per block
+  constexpr int KB = 64;             // keys per block
+  constexpr int NKT = KB / 16;       // 16-key tiles of S per block
   constexpr int KS = D / 32;         // MFMA k-steps over the head dim
   constexpr int NT = D / 16;         // 16-dim output tiles
   constexpr int VPR = D / 8;         // uint4 per key row
@@ -1339,10 +1340,10 @@ __global__ __launch_bounds__(256) void k_flash_prefill(FlashArgs a) {
     __syncthreads();
     if (kb + KB < kmax) fetch(kb + KB);
 
-    // S = Q K^T for 16 rows x 32 keys (two 16-key tiles)
-    f32x4_t sacc[2];
+    // S = Q K^T for 16 rows x KB keys (NKT 16-key tiles)
+    f32x4_t sacc[NKT];
 #pragma unroll
-    for (int n = 0; n < 2; ++n) {
+    for (int n = 0; n < NKT; ++n) {
       sacc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
@@ -1356,23 +1357,28 @@ __global__ __launch_bounds__(256) void k_flash_prefill(FlashArgs a) {
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * wid + 4 * grp + i;
       const int qpos = pos0 + r;
-      float sv[2];
+      float sv[NKT];
+      float smax = -INFINITY;
 #pragma unroll
-      for (int n = 0; n < 2; ++n) {
+      for (int n = 0; n < NKT; ++n) {
         const int key = kb + 16 * n + r16;
         sv[n] = (r < nrows && key <= qpos) ? sacc[n][i] * scale : -INFINITY;
+        smax = fmaxf(smax, sv[n]);
       }
-      const float mnew = fmaxf(m[i], row16_max(fmaxf(sv[0], sv[1])));
+      const float mnew = fmaxf(m[i], row16_max(smax));
       const float alpha = (m[i] == -INFINITY) ? 0.0f : expf(m[i] - mnew);
-      float pr[2];
+      float pr[NKT], psum = 0.0f;
 #pragma unroll
-      for (int n = 0; n < 2; ++n) pr[n] = (sv[n] == -INFINITY) ? 0.0f : expf(sv[n] - mnew);
-      l[i] = l[i] * alpha + row16_sum(pr[0] + pr[1]);
+      for (int n = 0; n < NKT; ++n) {
+        pr[n] = (sv[n] == -INFINITY) ? 0.0f : expf(sv[n] - mnew);
+        psum += pr[n];
+      }
+      l[i] = l[i] * alpha + row16_sum(psum);
       m[i] = mnew;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) o[nt][i] *= alpha;
 #pragma unroll
-      for (int n = 0; n < 2; ++n) {
+      for (int n = 0; n < NKT; ++n) {
         const bf16_t hi = f2bf(pr[n]);
         const bf16_t lo = f2bf(pr[n] - bf2f(hi));
         Ps[wid][0][4 * grp + i][16 * n + r16] = hi;
@@ -1380,15 +1386,20 @@ __global__ __launch_bounds__(256) void k_flash_prefill(FlashArgs a) {
       }
     }
     __syncthreads();
-    // O += P V: A = P (rows r16, keys 8*grp..), B = V (keys 8*grp.., dims 16*nt + r16)
-    const bf16x8_t phi = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(&Ps[wid][0][r16][8 * grp]));
-    const bf16x8_t plo = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(&Ps[wid][1][r16][8 * grp]));
+    // O += P V: A = P (rows r16, keys 32*kk + 8*grp..), B = V (those keys, dims 16*nt + r16)
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const bf16x8_t vf = __builtin_bit_cast(
-          bf16x8_t, *reinterpret_cast<const uint4*>(&Vt[16 * nt + r16][8 * grp]));
-      o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi, vf, o[nt], 0, 0, 0);
-      o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo, vf, o[nt], 0, 0, 0);
+    for (int kk = 0; kk < KB / 32; ++kk) {
+      const bf16x8_t phi = __builtin_bit_cast(
+          bf16x8_t, *reinterpret_cast<const uint4*>(&Ps[wid][0][r16][32 * kk + 8 * grp]));
+      const bf16x8_t plo = __builtin_bit_cast(
+          bf16x8_t, *reinterpret_cast<const uint4*>(&Ps[wid][1][r16][32 * kk + 8 * grp]));
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const bf16x8_t vf = __builtin_bit_cast(
+            bf16x8_t, *reinterpret_cast<const uint4*>(&Vt[16 * nt + r16][32 * kk + 8 * grp]));
+        o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi, vf, o[nt], 0, 0, 0);
+        o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo, vf, o[nt], 0, 0, 0);
+      }
     }
     __syncthreads();
   }
