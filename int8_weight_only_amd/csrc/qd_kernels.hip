@@ -164,8 +164,8 @@ __device__ __forceinline__ void lm_head_store(const GemvArgs& a, unsigned long l
 }
 
 // one work-group per batch row: reduces that row's keys over the LM-head work-groups and
-// writes the greedy id (advancing its position); work-group 0 advances the step counter
-// once every row has read it (k_lm_finish_step, launched after)
+// writes the greedy id (advancing its position).  The step counter advances once every
+// row has read it: in k_lm_finish_step, launched after, or here when there is one row
 __global__ __launch_bounds__(256) void k_lm_finish(GemvArgs a, int nblocks) {
   __shared__ unsigned long long red[4];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -185,6 +185,8 @@ __global__ __launch_bounds__(256) void k_lm_finish(GemvArgs a, int nblocks) {
     a.next_ids[b] = id;
     if (a.out_ids) a.out_ids[(size_t)(a.batch0 + b) * a.out_ld + *a.step] = id;
     if (a.pos) a.pos[b] += 1;
+    // a single row advances the step counter itself (no other work-group reads it)
+    if (a.bump_step && gridDim.x == 1) *a.step += 1;
   }
 }
 
@@ -1499,7 +1501,7 @@ static hipError_t gemv1(const GemvArgs& a, int epi, hipStream_t st) {
 static hipError_t lm_finish(const GemvArgs& a, int nblocks, hipStream_t st) {
   hipLaunchKernelGGL(k_lm_finish, dim3(a.nb), dim3(256), 0, st, a, nblocks);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !a.bump_step) return e;
+  if (e != hipSuccess || !a.bump_step || a.nb == 1) return e;
   hipLaunchKernelGGL(k_lm_finish_step, dim3(1), dim3(1), 0, st, a.step);
   return hipGetLastError();
 }
