@@ -233,6 +233,11 @@ typedef enum {
                                      8 query heads per KV head); 0 (default): per-step kernels */
   QD_TUNE_PERSIST_SPLITS = 5,     /* persistent decode: most position splits per KV head, 1..32
                                      (default 32); each split is one work-group */
+  QD_TUNE_SKINNY_SPLIT = 6,       /* batched decode projections split K over work-groups:
+                                     1 never, 2 (default) projections with fewer than 128
+                                     16-channel tiles at batches over 16, 3 all */
+  QD_TUNE_GEMM_SPLITS = 7,        /* prefill GEMMs: most split-K ways, 1..8, or 0 (default: 8;
+                                     the launcher splits only while the tiles leave CUs idle) */
 } qd_tune_knob;
 
 /* Sets a knob; captured decode graphs are dropped so the next call re-captures.

@@ -44,7 +44,7 @@ struct Plan {
   // workspace
   size_t x = 0, h = 0, qkv = 0, attn = 0, act = 0, part_o = 0, part_ml = 0;
   size_t ids = 0, row_slot = 0, row_pos = 0, last_rows = 0, lens = 0, slot_ident = 0, tiles = 0;
-  size_t pos = 0, next_ids = 0, lm_keys = 0, att_cnt = 0, done = 0, step = 0, out_ids = 0;
+  size_t pos = 0, next_ids = 0, lm_keys = 0, att_cnt = 0, sk_cnt = 0, done = 0, step = 0, out_ids = 0;
   size_t gemm_part = 0;
   // persistent single-sequence decode: exchange buffers, barrier words, error flag
   size_t pxg = 0, pqkv = 0, ppo = 0, pml = 0, pact = 0, pkeys = 0, pbar = 0, perr = 0;
@@ -178,6 +178,7 @@ Plan make_plan(const qd_model_shape& s, const qd_limits& lim) {
   P.next_ids = take((size_t)B * 4);
   P.lm_keys = take((size_t)B * LM_MAX_GRID * 8);
   P.att_cnt = take((size_t)B * d.KV * 4);
+  P.sk_cnt = take((size_t)SKINNY_MAX_TILES * 4);
   P.done = take(64);
   P.step = take(64);
   P.out_ids = take((size_t)B * lim.max_ctx * 4);
@@ -230,6 +231,8 @@ struct qd_model {
   int attn_min_chunks = 1;
   int attn_waves = 0;  // 0: eight waves only when B x KV heads fill the GPU without splits
   int attn_merge_last = 1;
+  int gemm_splits = 0;  // prefill GEMM split-K cap (0: launcher default)
+  int skinny_split = 2;  // 1: never; 2: fewer than 128 channel tiles, over 16 rows; 3: all
   // persistent single-sequence decode (one cooperative launch per call)
   bool persist_ok = false;     // this shape and device can run it
   std::string persist_why;     // why not, when persist_ok is false
@@ -312,6 +315,24 @@ qd_status enqueue_lm_head(qd_model* m, const bf16_t* x, const int* x_rows, int r
 }
 
 // ---- the kernels of one decode step, for slots 0..B-1 (rows == slots) -------------------
+// work-groups per channel tile of a skinny projection: enough to cover the CUs and to
+// give each of the four waves about one 128-k block, bounded by the partial buffer.
+// Default policy: split only projections with fewer than 128 tiles and more than 16 rows
+// (measured: below that the exchange of partials costs more than the added parallelism)
+int skinny_splits(const qd_model* m, int B, int N, int K, int epi) {
+  const int ctw = epi == EPI_SILU ? 2 : 1;
+  const int tt = B <= 16 ? 1 : (B <= 32 ? 2 : 4);
+  const int ntiles = (N + 16 * ctw - 1) / (16 * ctw);
+  const int nkb = (K + 127) / 128;
+  if (m->skinny_split == 1 || (m->skinny_split == 2 && (ntiles >= 128 || tt < 2)) ||
+      ntiles > SKINNY_MAX_TILES)
+    return 1;
+  int S = std::max((256 + ntiles - 1) / ntiles, (nkb + 3) / 4);
+  S = std::min(std::min(S, nkb), SKINNY_MAX_SPLIT);
+  while (S > 1 && (size_t)ntiles * S * ctw * tt * 256 > GEMM_PART_FLOATS) --S;
+  return S;
+}
+
 // one projection for B rows: B == 1 runs the register GEMV (RMSNorm in its prologue when
 // gain is set); B >= 2 normalizes into h first and runs the MFMA skinny GEMM
 qd_status dec_proj(qd_model* m, int B, const bf16_t* x, int ldx, const float* gain,
@@ -331,6 +352,9 @@ qd_status dec_proj(qd_model* m, int B, const bf16_t* x, int ldx, const float* ga
     ldx = K;
   }
   a.x = x; a.ldx = ldx;
+  a.ksplit = skinny_splits(m, B, N, K, epi);
+  a.kpart = m->ws<float>(m->P.gemm_part);
+  a.kcnt = m->ws<unsigned int>(m->P.sk_cnt);
   HIPCHK(launch_skinny(a, epi, st));
   return QD_OK;
 }
@@ -481,7 +505,7 @@ qd_status enqueue_prefill(qd_model* m, int n, const int* ids_dev, const std::vec
     HIPCHK(launch_rmsnorm(x, M, d.d, m->w<float>(o.in_g), m->shape.rms_eps, h, st));
     GemmArgs g{};
     g.A = h; g.lda = d.d; g.W = m->w<int8_t>(o.qkv_q); g.scale = m->w<float>(o.qkv_s);
-    g.M = M; g.N = d.NQKV; g.K = d.d; g.epi = EPI_STORE; g.out = qkv; g.ldo = d.NQKV; g.part = gpart;
+    g.M = M; g.N = d.NQKV; g.K = d.d; g.epi = EPI_STORE; g.out = qkv; g.ldo = d.NQKV; g.part = gpart; g.cnt = m->ws<unsigned int>(P.sk_cnt); g.splits = m->gemm_splits;
     HIPCHK(launch_gemm(g, st));
     RopeArgs ra{};
     ra.qkv = qkv; ra.ldqkv = d.NQKV;
@@ -500,16 +524,16 @@ qd_status enqueue_prefill(qd_model* m, int n, const int* ids_dev, const std::vec
     HIPCHK(launch_flash_prefill(fa, n_tiles, st));
     g = GemmArgs{};
     g.A = attn; g.lda = d.HD; g.W = m->w<int8_t>(o.o_q); g.scale = m->w<float>(o.o_s);
-    g.M = M; g.N = d.d; g.K = d.HD; g.epi = EPI_RESID; g.out = x; g.ldo = d.d; g.part = gpart;
+    g.M = M; g.N = d.d; g.K = d.HD; g.epi = EPI_RESID; g.out = x; g.ldo = d.d; g.part = gpart; g.cnt = m->ws<unsigned int>(P.sk_cnt); g.splits = m->gemm_splits;
     HIPCHK(launch_gemm(g, st));
     HIPCHK(launch_rmsnorm(x, M, d.d, m->w<float>(o.post_g), m->shape.rms_eps, h, st));
     g = GemmArgs{};
     g.A = h; g.lda = d.d; g.W = m->w<int8_t>(o.gu_q); g.scale = m->w<float>(o.gu_s);
-    g.M = M; g.N = 2 * d.I; g.K = d.d; g.epi = EPI_SILU; g.out = act; g.ldo = d.I; g.part = gpart;
+    g.M = M; g.N = 2 * d.I; g.K = d.d; g.epi = EPI_SILU; g.out = act; g.ldo = d.I; g.part = gpart; g.cnt = m->ws<unsigned int>(P.sk_cnt); g.splits = m->gemm_splits;
     HIPCHK(launch_gemm(g, st));
     g = GemmArgs{};
     g.A = act; g.lda = d.I; g.W = m->w<int8_t>(o.dn_q); g.scale = m->w<float>(o.dn_s);
-    g.M = M; g.N = d.d; g.K = d.I; g.epi = EPI_RESID; g.out = x; g.ldo = d.d; g.part = gpart;
+    g.M = M; g.N = d.d; g.K = d.I; g.epi = EPI_RESID; g.out = x; g.ldo = d.d; g.part = gpart; g.cnt = m->ws<unsigned int>(P.sk_cnt); g.splits = m->gemm_splits;
     HIPCHK(launch_gemm(g, st));
   }
   qd_status s = enqueue_lm_head(m, x, last_rows, M, n, logits, next_ids, false, write_out, st);
@@ -754,6 +778,7 @@ qd_status qd_load_weights(const qd_model_shape* shape, const qd_limits* limits,
   LCHK(launch_fill_i32(m->ws<int>(P.pos), limits->max_batch, 0, s));
   LCHK(launch_iota(m->ws<int>(P.slot_ident), limits->max_batch, s));
   LCHK(launch_fill_i32(m->ws<int>(P.att_cnt), limits->max_batch * d.KV, 0, s));
+  LCHK(launch_fill_i32(m->ws<int>(P.sk_cnt), SKINNY_MAX_TILES, 0, s));
   LCHK(launch_fill_i32(m->ws<int>(P.done), 16, 0, s));
   LCHK(launch_fill_i32(m->ws<int>(P.step), 16, 0, s));
   LCHK(hipStreamCreateWithFlags(&m->cap_stream, hipStreamNonBlocking));
@@ -1034,7 +1059,7 @@ qd_status qd_set_tuning(qd_model* m, int32_t knob, int32_t value) {
   g_err.clear();
   if (!m) return fail(QD_ERR_INVALID_ARGUMENTS, "model is NULL");
   if (value < 0 || (value < 1 && knob != QD_TUNE_ATTN_MERGE_LAST && knob != QD_TUNE_ATTN_WAVES &&
-                    knob != QD_TUNE_PERSISTENT))
+                    knob != QD_TUNE_PERSISTENT && knob != QD_TUNE_GEMM_SPLITS))
     return fail(QD_ERR_INVALID_ARGUMENTS, "value out of range");
   switch (knob) {
     case QD_TUNE_ATTN_MAX_SPLITS: m->attn_max_splits = value; break;
@@ -1050,6 +1075,14 @@ qd_status qd_set_tuning(qd_model* m, int32_t knob, int32_t value) {
     case QD_TUNE_PERSIST_SPLITS:
       if (value > PERSIST_SPLITS) return fail(QD_ERR_INVALID_ARGUMENTS, "at most 32 splits");
       m->persist_splits = value;
+      break;
+    case QD_TUNE_GEMM_SPLITS:
+      if (value > 8) return fail(QD_ERR_INVALID_ARGUMENTS, "at most 8 GEMM splits");
+      m->gemm_splits = value;
+      break;
+    case QD_TUNE_SKINNY_SPLIT:
+      if (value > 3) return fail(QD_ERR_INVALID_ARGUMENTS, "skinny split mode must be 1, 2 or 3");
+      m->skinny_split = value;
       break;
     case QD_TUNE_ATTN_WAVES:
       if (value != 0 && value != 4 && value != 8)

@@ -44,7 +44,13 @@ struct GemvArgs {
   int* step;                         // device step counter (read when out_ids is set)
   int bump_step;                     // the last block increments *step
   int batch0;                        // batch index of row 0 of this launch (for pos/out_ids)
+  // skinny split-K (EPI_STORE / EPI_RESID / EPI_SILU): ksplit work-groups per channel tile
+  int ksplit;                        // <= 1: one work-group per tile
+  float* kpart;                      // [tiles][ksplit][CTW][16*TT tokens x 16 channels] partials
+  unsigned int* kcnt;                // [tiles] arrival counters, zero on entry, reset by the last
 };
+constexpr int SKINNY_MAX_SPLIT = 16;
+constexpr int SKINNY_MAX_TILES = 4096;
 
 struct GemmArgs {
   const bf16_t* A; int lda;   // [M][K] bf16 activations
@@ -53,8 +59,9 @@ struct GemmArgs {
   int M, N, K;
   int epi;                    // EPI_STORE / EPI_RESID / EPI_SILU
   bf16_t* out; int ldo;
-  float* part;                // split-K partial sums [splits][M][N] (fp32), PART_FLOATS max
-  int splits;                 // set by the launcher
+  float* part;                // split-K tile partials [tiles][splits][64 x 64] (fp32)
+  unsigned int* cnt;          // split-K arrival counters per tile, zero on entry
+  int splits;                 // in: most split-K ways (0: launcher's default); set by the launcher
 };
 constexpr size_t GEMM_PART_FLOATS = (size_t)8 << 20;  // 32 MiB of split-K partials
 

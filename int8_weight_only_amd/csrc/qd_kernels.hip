@@ -220,7 +220,11 @@ __global__ __launch_bounds__(256) void k_gemv1(GemvArgs a) {
   int blk = blockIdx.x;
   // per-row scales (and residual values) of a block: requested with its weights, so the
   // epilogue after the reductions does not wait for another round trip
-  float sc[NR], rs[R];
+  // The residual values stay raw bf16 bits until the epilogue and are read from a clamped
+  // (always valid) index: a conditional load converted in its branch would make the
+  // wave wait for every load in flight, the weights included, at that point.
+  float sc[NR];
+  bf16_t rsb[R];
   auto load_rowdata = [&](int b) {
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
@@ -230,7 +234,7 @@ __global__ __launch_bounds__(256) void k_gemv1(GemvArgs a) {
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       const int r = row_of(b, i);
-      rs[i] = (EPI == EPI_RESID && r < a.N && b < nblk) ? bf2f(a.out[r]) : 0.0f;
+      rsb[i] = EPI == EPI_RESID ? a.out[(r < a.N && b < nblk) ? r : 0] : (bf16_t)0;
     }
   };
   // weights of the first block, requested before the activations
@@ -350,7 +354,7 @@ __global__ __launch_bounds__(256) void k_gemv1(GemvArgs a) {
           if (EPI == EPI_STORE) {
             a.out[r] = f2bf(v);
           } else if (EPI == EPI_RESID) {
-            a.out[r] = f2bf(rs[i] + rbf(v));
+            a.out[r] = f2bf(bf2f(rsb[i]) + rbf(v));
           } else {
             if (a.logits) a.logits[r] = v;
             const unsigned long long k = argmax_key(v, r);
@@ -364,7 +368,7 @@ __global__ __launch_bounds__(256) void k_gemv1(GemvArgs a) {
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       const int r = row_of(nxt, i);
-      rs[i] = (EPI == EPI_RESID && nxt < nblk && r < a.N) ? bf2f(a.out[r]) : 0.0f;
+      rsb[i] = EPI == EPI_RESID ? a.out[(nxt < nblk && r < a.N) ? r : 0] : (bf16_t)0;
     }
   }
   if (EPI == EPI_LOGITS) {
@@ -402,10 +406,13 @@ __device__ __forceinline__ bf16x8_t i8x8_to_bf16x8(uint2 w) {
 }
 
 // 64x64 output tile per work-group (4 waves in 2x2, each 32x32 = 2x2 MFMA 16x16x32
-// tiles), k advancing 64 at a time.  The next k-tile is fetched into registers while
-// the current one is multiplied out of LDS (double-buffered, one barrier per step).
-// With split-K (blockIdx.z) each work-group covers a slice of K and stores fp32
-// partials; k_gemm_finish sums them in split order and applies the epilogue.
+// tiles), k advancing 64 at a time.  The loads of GEMM_PF k-steps ahead are in flight
+// while one step is multiplied out of LDS (double-buffered, one barrier per step); the
+// weights are converted to bf16 once, when a step is written to LDS.  All loads are
+// buffer loads whose out-of-range offsets read zero, so no load sits in a branch and
+// each step waits only for its own data.  With split-K (blockIdx.z) each work-group
+// stores its fp32 tile partial agent-coherently; the last of a tile's work-groups to
+// arrive adds the partials in split order and runs the epilogue.
 template <int EPI>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, int m, int n, float v, float vu,
                                               float sv, float su) {
@@ -421,36 +428,50 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, int m, int n, f
   }
 }
 
+constexpr int GEMM_PF = 4;  // k-steps of loads in flight
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
 template <int EPI>
 __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
-  constexpr int BM = 64, BN = 64, BK = 64;
+  constexpr int BM = 64, BN = 64, BK = 64, P = GEMM_PF;
+  constexpr int OOB = (int)0x80000000;
   __shared__ __align__(16) bf16_t As[2][BM][BK + 8];
-  __shared__ __align__(16) int8_t Ws[2][BN][BK + 16];
+  __shared__ __align__(16) bf16_t Ws[2][BN][BK + 8];
+  __shared__ int is_last;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid & 1, wn = wid >> 1;
   const int grp = lane >> 4, r16 = lane & 15;
   const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
-  const int kper = ((a.K + a.splits - 1) / a.splits + 31) & ~31;
-  const int kbeg = blockIdx.z * kper;
+  const int S = a.splits, z = blockIdx.z;
+  const int kper = ((a.K + S - 1) / S + 31) & ~31;
+  const int kbeg = z * kper;
   const int kend = min(a.K, kbeg + kper);
+  const int nsteps = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
 
-  // staging: A rows tid/4 (two 16-byte pieces), W row tid/4 (one 16-byte piece)
+  // rows past M (N) lie past the end of A (W) and read zero; k past the split's end is
+  // sent out of range explicitly
+  const __amdgpu_buffer_rsrc_t arsc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.A, 0, a.M * a.lda * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t wrsc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.W, 0, a.N * a.K, 0x00020000);
+  // staging: A row tid/4 (two 16-byte pieces), W row tid/4 (one 16-byte piece)
   const int ar = tid >> 2, ac = (tid & 3) * 16;
   const int wr = tid >> 2, wc = (tid & 3) * 16;
-  uint4 ra0, ra1, rw;
-  auto fetch = [&](int k0) {
+  struct Stage { uint4 a0, a1, w; };
+  auto fetch = [&](int step, Stage& q) {
+    const int k0 = kbeg + step * BK;
     const int ka = k0 + ac;
-    const bool aok = m0 + ar < a.M;
-    const bf16_t* ap = a.A + (size_t)(aok ? m0 + ar : 0) * a.lda;
-    ra0 = (aok && ka < kend) ? *reinterpret_cast<const uint4*>(ap + ka) : make_uint4(0, 0, 0, 0);
-    ra1 = (aok && ka + 8 < kend) ? *reinterpret_cast<const uint4*>(ap + ka + 8) : make_uint4(0, 0, 0, 0);
-    const bool wok = n0 + wr < a.N && k0 + wc < kend;
-    rw = wok ? *reinterpret_cast<const uint4*>(a.W + (size_t)(n0 + wr) * a.K + k0 + wc) : make_uint4(0, 0, 0, 0);
+    const int abase = ((m0 + ar) * a.lda + ka) * 2;
+    q.a0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(arsc, ka < kend ? abase : OOB, 0, 0));
+    q.a1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(arsc, ka + 8 < kend ? abase + 16 : OOB, 0, 0));
+    q.w = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                        wrsc, k0 + wc < kend ? (n0 + wr) * a.K + k0 + wc : OOB, 0, 0));
   };
-  auto stash = [&](int buf) {
-    *reinterpret_cast<uint4*>(&As[buf][ar][ac]) = ra0;
-    *reinterpret_cast<uint4*>(&As[buf][ar][ac + 8]) = ra1;
-    *reinterpret_cast<uint4*>(&Ws[buf][wr][wc]) = rw;
+  auto stash = [&](const Stage& q, int buf) {
+    *reinterpret_cast<uint4*>(&As[buf][ar][ac]) = q.a0;
+    *reinterpret_cast<uint4*>(&As[buf][ar][ac + 8]) = q.a1;
+    *reinterpret_cast<bf16x8_t*>(&Ws[buf][wr][wc]) = i8x8_to_bf16x8(make_uint2(q.w.x, q.w.y));
+    *reinterpret_cast<bf16x8_t*>(&Ws[buf][wr][wc + 8]) = i8x8_to_bf16x8(make_uint2(q.w.z, q.w.w));
   };
 
   f32x4_t acc[2][2];
@@ -458,44 +479,99 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // scales of this lane's two output channels (gate/up: the pair), requested before the
-  // k loop so the epilogue does not wait for them
+  // scales of this lane's two output channels (gate/up: the pair), requested first
   float gsc[2];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const int n = n0 + wn * 32 + nt * 16 + r16;
-    gsc[nt] = (a.splits == 1 && n < a.N) ? a.scale[n] : 0.0f;
+    gsc[nt] = a.scale[n < a.N ? n : 0];
   }
 
-  int buf = 0;
-  if (kbeg < kend) {
-    fetch(kbeg);
-    stash(0);
-  }
+  Stage q[P];
+#pragma unroll
+  for (int u = 0; u < P; ++u) fetch(u, q[u]);
+  stash(q[0], 0);
   __syncthreads();
-  for (int k0 = kbeg; k0 < kend; k0 += BK) {
-    const bool more = k0 + BK < kend;
-    if (more) fetch(k0 + BK);
+  // whole groups of P steps (steps past the end multiply zeros): an early exit from the
+  // unrolled group would leave different loads pending on each path, and the wait at the
+  // loop head would then drain all of them
+  for (int i0 = 0; i0 < nsteps; i0 += P) {
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      bf16x8_t af[2], bw[2];
+    for (int u = 0; u < P; ++u) {
+      const int i = i0 + u;
+      const int buf = i & 1;
+      fetch(i + P, q[u]);  // into the slot step i vacated
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-        af[mt] = __builtin_bit_cast(
-            bf16x8_t, *reinterpret_cast<const uint4*>(&As[buf][wm * 32 + mt * 16 + r16][32 * sub + 8 * grp]));
+      for (int sub = 0; sub < 2; ++sub) {
+        bf16x8_t af[2], bw[2];
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-        bw[nt] = i8x8_to_bf16x8(
-            *reinterpret_cast<const uint2*>(&Ws[buf][wn * 32 + nt * 16 + r16][32 * sub + 8 * grp]));
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+        for (int mt = 0; mt < 2; ++mt)
+          af[mt] = *reinterpret_cast<const bf16x8_t*>(&As[buf][wm * 32 + mt * 16 + r16][32 * sub + 8 * grp]);
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt], bw[nt], acc[mt][nt], 0, 0, 0);
+          bw[nt] = *reinterpret_cast<const bf16x8_t*>(&Ws[buf][wn * 32 + nt * 16 + r16][32 * sub + 8 * grp]);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt)
+            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt], bw[nt], acc[mt][nt], 0, 0, 0);
+      }
+      stash(q[u + 1 < P ? u + 1 : 0], buf ^ 1);  // step i + 1 (zeros past the end)
+      __syncthreads();
     }
-    if (more) stash(buf ^ 1);
+  }
+
+  if (S > 1) {
+    // tile partial, thread-major: 16 floats of thread tid at ((tile * S + z) * 256 + tid) * 16
+    const int tile = blockIdx.y * gridDim.x + blockIdx.x;
+    const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
+        a.part + (size_t)tile * S * 4096, 0, S * 4096 * 4, 0x00020000);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, acc[mt][nt]), prs,
+                                               ((z * 256 + tid) * 16 + (mt * 2 + nt) * 4) * 4, 0, 16);
+    // every store of this work-group has completed before thread 0 counts it in
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    buf ^= 1;
+    if (tid == 0)
+      is_last = __hip_atomic_fetch_add(a.cnt + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                (unsigned)(S - 1);
+    __syncthreads();
+    if (!is_last) return;
+    f32x4_t tot[2][2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) tot[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < S; s0 += 4) {
+      f32x4_t pv[4][2][2];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) {
+            const int sj = s0 + j;
+            const int off = (sj < S && sj != z) ? ((sj * 256 + tid) * 16 + (mt * 2 + nt) * 4) * 4 : OOB;
+            pv[j][mt][nt] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(prs, off, 0, 16));
+          }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) {
+            const int sj = s0 + j;
+            if (sj < S) tot[mt][nt] += sj == z ? acc[mt][nt] : pv[j][mt][nt];
+          }
+    }
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = tot[mt][nt];
+    if (tid == 0) __hip_atomic_store(a.cnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   // lane holds D[4*(lane/16)+i][lane%16]: token rows, channel columns
@@ -505,13 +581,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
     for (int i = 0; i < 4; ++i) {
       const int m = m0 + wm * 32 + mt * 16 + 4 * grp + i;
       if (m >= a.M) continue;
-      if (a.splits > 1) {
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          const int n = n0 + wn * 32 + nt * 16 + r16;
-          if (n < a.N) a.part[((size_t)blockIdx.z * a.M + m) * a.N + n] = acc[mt][nt][i];
-        }
-      } else if (EPI == EPI_SILU) {
+      if (EPI == EPI_SILU) {
         const int ng = n0 + wn * 32 + r16;
         if (ng + GU_BLOCK < a.N)
           gemm_epilogue<EPI_SILU>(a, m, ng, acc[mt][0][i], acc[mt][1][i], gsc[0], gsc[1]);
@@ -526,22 +596,6 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
   }
 }
 
-// split-K tail: out = epilogue(sum of the partials in split order)
-template <int EPI>
-__global__ __launch_bounds__(256) void k_gemm_finish(GemmArgs a) {
-  const int nn = (EPI == EPI_SILU) ? a.N / 2 : a.N;
-  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (long)a.M * nn) return;
-  const int m = (int)(idx / nn), c = (int)(idx % nn);
-  const int n = (EPI == EPI_SILU) ? gu_row(c, 0) : c;
-  float v = 0.0f, vu = 0.0f;
-  for (int z = 0; z < a.splits; ++z) {
-    v += a.part[((size_t)z * a.M + m) * a.N + n];
-    if (EPI == EPI_SILU) vu += a.part[((size_t)z * a.M + m) * a.N + n + GU_BLOCK];
-  }
-  gemm_epilogue<EPI>(a, m, n, v, vu, a.scale[n], EPI == EPI_SILU ? a.scale[n + GU_BLOCK] : 0.0f);
-}
-
 // ------------------------------------------------------------------------------------------
 // batched decode GEMM on MFMA ("skinny": 2..64 token rows, weights swept once):
 // Y[t][n] = scale[n] * sum_k X[t][k] * W[n][k], X bf16 (already RMS-normalized where the
@@ -550,6 +604,92 @@ __global__ __launch_bounds__(256) void k_gemm_finish(GemmArgs a) {
 // work-group owns CTW 16-channel tiles; its four waves take interleaved 128-k blocks
 // (each lane group streams 128 contiguous bytes of a weight row) and the partial sums
 // meet in LDS.  The k order inside a block is permuted identically for both operands.
+// operands of one 128-k block of a skinny tile: lane group grp covers k0 = kb + 32*grp
+// .. +32 of the CTW weight rows and the TT token rows of this lane
+template <int TT, int CTW>
+struct SkinnyOps {
+  uint4 w[CTW][2];
+  uint4 x[TT][4];
+};
+// (lanes of padding token rows, past the batch, load nothing: their B operand is zero)
+template <int TT, int CTW>
+__device__ __forceinline__ void skinny_load(const int* const (&wrow)[CTW], const bool (&wok)[CTW],
+                                            const bf16_t* const (&xrow)[TT], const bool (&xok)[TT],
+                                            int K, int k0, SkinnyOps<TT, CTW>& o) {
+  const bool kok = k0 < K;
+#pragma unroll
+  for (int c = 0; c < CTW; ++c) {
+    const uint4* src = reinterpret_cast<const uint4*>(wrow[c] + k0 / 4);
+    o.w[c][0] = (kok && wok[c]) ? src[0] : make_uint4(0, 0, 0, 0);
+    o.w[c][1] = (kok && wok[c]) ? src[1] : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) {
+    const uint4* src = reinterpret_cast<const uint4*>(xrow[tt] + k0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o.x[tt][q] = (kok && xok[tt]) ? src[q] : make_uint4(0, 0, 0, 0);
+  }
+}
+template <int TT, int CTW>
+__device__ __forceinline__ void skinny_mfma(const SkinnyOps<TT, CTW>& o, f32x4_t (&acc)[CTW][TT]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int c = 0; c < CTW; ++c) {
+      const uint4 w16 = o.w[c][j >> 1];
+      const uint2 w8 = (j & 1) ? make_uint2(w16.z, w16.w) : make_uint2(w16.x, w16.y);
+      const bf16x8_t af = i8x8_to_bf16x8(w8);
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt)
+        acc[c][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            af, __builtin_bit_cast(bf16x8_t, o.x[tt][j]), acc[c][tt], 0, 0, 0);
+    }
+  }
+}
+// blocks per load batch: every batch's loads are in flight before its first MFMA
+template <int TT, int CTW>
+constexpr int skinny_batch() { return TT * CTW >= 4 ? 2 : 3; }
+
+// a wave's n blocks kb(i) = first + stride * ((i + rot) mod n), i < n, in load batches
+template <int TT, int CTW>
+__device__ __forceinline__ void skinny_blocks(const int* const (&wrow)[CTW], const bool (&wok)[CTW],
+                                              const bf16_t* const (&xrow)[TT],
+                                              const bool (&xok)[TT], int K, int grp,
+                                              int first, int stride, int n, int rot,
+                                              f32x4_t (&acc)[CTW][TT]) {
+  constexpr int U = skinny_batch<TT, CTW>();
+  for (int ib = 0; ib < n; ib += U) {
+    SkinnyOps<TT, CTW> ops[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      int ii = ib + u + rot;
+      ii = ii >= n ? ii - n : ii;
+      const int k0 = ib + u < n ? (first + stride * ii) * 128 + 32 * grp : K;
+      skinny_load<TT, CTW>(wrow, wok, xrow, xok, K, k0, ops[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) skinny_mfma<TT, CTW>(ops[u], acc);
+  }
+}
+
+// stores one output element of a skinny tile: channel ch (tile-relative channel cr) of
+// token tok from the raw dot products v (gate, up for SiLU), their scales and the residual
+// (bf16 bits)
+template <int EPI, int CTW>
+__device__ __forceinline__ void skinny_out(const GemvArgs& a, int tile, int tok, int ch, int cr,
+                                           const float (&v)[CTW], const float (&sc)[CTW], bf16_t res) {
+  if (EPI == EPI_SILU) {
+    if (tok < a.nb && ch + 16 < a.N) {
+      const float g = rbf(v[0] * sc[0]), u = rbf(v[CTW - 1] * sc[CTW - 1]);
+      a.out[(size_t)tok * a.ldo + tile * GU_BLOCK + cr] = f2bf(g / (1.0f + expf(-g)) * u);
+    }
+  } else if (tok < a.nb && ch < a.N) {
+    const float y = v[0] * sc[0];
+    bf16_t* o = a.out + (size_t)tok * a.ldo + ch;
+    *o = (EPI == EPI_STORE) ? f2bf(y) : f2bf(bf2f(res) + rbf(y));
+  }
+}
+
 template <int TT, int EPI, int NWS>
 __global__ __launch_bounds__(64 * NWS) void k_skinny(GemvArgs a) {
   constexpr int CTW = (EPI == EPI_SILU) ? 2 : 1;
@@ -564,9 +704,11 @@ __global__ __launch_bounds__(64 * NWS) void k_skinny(GemvArgs a) {
 
   // token rows of this lane's B operand, one per token tile
   const bf16_t* xrow[TT];
+  bool xok[TT];
 #pragma unroll
   for (int tt = 0; tt < TT; ++tt) {
     int tok = tt * 16 + r16;
+    xok[tt] = tok < a.nb;
     tok = tok < a.nb ? tok : a.nb - 1;
     const int xr = a.x_rows ? a.x_rows[tok] : tok;
     xrow[tt] = a.x + (size_t)xr * a.ldx;
@@ -577,7 +719,9 @@ __global__ __launch_bounds__(64 * NWS) void k_skinny(GemvArgs a) {
   for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
     // their scales and residual inputs are requested before the k loop, so the epilogue
     // after the wave reduction does not wait for another round trip
-    float esc[NE][CTW], eres[NE];
+    // (residuals as raw bits from a clamped index: no wait before the k loop's loads)
+    float esc[NE][CTW];
+    bf16_t eres[NE];
 #pragma unroll
     for (int q = 0; q < NE; ++q) {
       const int e = tid + 64 * NWS * q;
@@ -587,7 +731,7 @@ __global__ __launch_bounds__(64 * NWS) void k_skinny(GemvArgs a) {
       const bool ok = e < TT * 256 && tok < a.nb;
 #pragma unroll
       for (int c = 0; c < CTW; ++c) esc[q][c] = (ok && ch + 16 * c < a.N) ? a.scale[ch + 16 * c] : 0.0f;
-      eres[q] = (EPI == EPI_RESID && ok && ch < a.N) ? bf2f(a.out[(size_t)tok * a.ldo + ch]) : 0.0f;
+      eres[q] = EPI == EPI_RESID ? a.out[(ok && ch < a.N) ? (size_t)tok * a.ldo + ch : 0] : (bf16_t)0;
     }
     f32x4_t acc[CTW][TT];
 #pragma unroll
@@ -605,39 +749,7 @@ __global__ __launch_bounds__(64 * NWS) void k_skinny(GemvArgs a) {
     const int nkb = (K + 127) / 128;
     const int nmine = (nkb - wid + NWS - 1) / NWS;  // this wave's blocks: wid, wid+NWS, ...
     const int rot = nmine > 0 ? tile % nmine : 0;
-    for (int ib = 0; ib < nmine; ++ib) {
-      const int ii = ib + rot;
-      const int kb = (wid + NWS * (ii >= nmine ? ii - nmine : ii)) * 128;
-      const int k0 = kb + 32 * grp;
-      const bool kok = k0 < K;
-      uint4 wv[CTW][2];
-#pragma unroll
-      for (int c = 0; c < CTW; ++c) {
-        const uint4* src = reinterpret_cast<const uint4*>(wrow[c] + k0 / 4);
-        wv[c][0] = (kok && wok[c]) ? src[0] : make_uint4(0, 0, 0, 0);
-        wv[c][1] = (kok && wok[c]) ? src[1] : make_uint4(0, 0, 0, 0);
-      }
-      uint4 xv[TT][4];
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt) {
-        const uint4* src = reinterpret_cast<const uint4*>(xrow[tt] + k0);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) xv[tt][q] = kok ? src[q] : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-#pragma unroll
-        for (int c = 0; c < CTW; ++c) {
-          const uint4 w16 = wv[c][j >> 1];
-          const uint2 w8 = (j & 1) ? make_uint2(w16.z, w16.w) : make_uint2(w16.x, w16.y);
-          const bf16x8_t af = i8x8_to_bf16x8(w8);
-#pragma unroll
-          for (int tt = 0; tt < TT; ++tt)
-            acc[c][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                af, __builtin_bit_cast(bf16x8_t, xv[tt][j]), acc[c][tt], 0, 0, 0);
-        }
-      }
-    }
+    skinny_blocks<TT, CTW>(wrow, wok, xrow, xok, K, grp, wid, NWS, nmine, rot, acc);
     // partial sums of the four waves meet in LDS
 #pragma unroll
     for (int c = 0; c < CTW; ++c)
@@ -661,13 +773,7 @@ __global__ __launch_bounds__(64 * NWS) void k_skinny(GemvArgs a) {
         for (int w = 0; w < NWS; ++w) v[c] += red[w][c * TT + tt][i][l];
       }
       const int ch = tile * 16 * CTW + 4 * (l >> 4) + i;
-      if (EPI == EPI_SILU) {
-        if (tok < a.nb && ch + 16 < a.N) {
-          const float g = rbf(v[0] * esc[q][0]), u = rbf(v[CTW - 1] * esc[q][CTW - 1]);
-          const int j = tile * GU_BLOCK + 4 * (l >> 4) + i;
-          a.out[(size_t)tok * a.ldo + j] = f2bf(g / (1.0f + expf(-g)) * u);
-        }
-      } else if (EPI == EPI_LOGITS) {
+      if (EPI == EPI_LOGITS) {
         unsigned long long k = 0ull;
         if (tok < a.nb && ch < a.N) {
           const float lv = v[0] * esc[q][0];
@@ -675,10 +781,8 @@ __global__ __launch_bounds__(64 * NWS) void k_skinny(GemvArgs a) {
           k = argmax_key(lv, ch);
         }
         kl[tok][4 * (l >> 4) + i] = k;
-      } else if (tok < a.nb && ch < a.N) {
-        const float y = v[0] * esc[q][0];
-        bf16_t* o = a.out + (size_t)tok * a.ldo + ch;
-        *o = (EPI == EPI_STORE) ? f2bf(y) : f2bf(eres[q] + rbf(y));
+      } else {
+        skinny_out<EPI, CTW>(a, tile, tok, ch, 4 * (l >> 4) + i, v, esc[q], eres[q]);
       }
     }
     if (EPI == EPI_LOGITS) {
@@ -691,6 +795,138 @@ __global__ __launch_bounds__(64 * NWS) void k_skinny(GemvArgs a) {
     __syncthreads();
   }
   if (EPI == EPI_LOGITS) lm_head_store(a, best, 64);
+}
+
+// Split-K form for projections with few channel tiles: work-group blockIdx = tile * S + s
+// sums the 128-k blocks [s*nkb/S, (s+1)*nkb/S) of one tile, one block per wave per pass.
+// Each work-group's tile partial goes out with agent-coherent stores; the work-group that
+// counts in last adds the S partials in split order (fixed order: the result does not
+// depend on arrival order) and runs the epilogue.  No work-group waits for another.
+template <int TT, int EPI, int NWS>
+__global__ __launch_bounds__(64 * NWS) void k_skinny_split(GemvArgs a) {
+  constexpr int CTW = (EPI == EPI_SILU) ? 2 : 1;
+  constexpr int NACC = CTW * TT;
+  constexpr int NE = (TT * 256 + 64 * NWS - 1) / (64 * NWS);
+  __shared__ float red[NWS][NACC][4][64];
+  __shared__ int is_last;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int K = a.K, S = a.ksplit;
+  const int grp = lane >> 4, r16 = lane & 15;
+  const int tile = blockIdx.x / S, s = blockIdx.x - tile * S;
+
+  const bf16_t* xrow[TT];
+  bool xok[TT];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) {
+    int tok = tt * 16 + r16;
+    xok[tt] = tok < a.nb;
+    tok = tok < a.nb ? tok : a.nb - 1;
+    const int xr = a.x_rows ? a.x_rows[tok] : tok;
+    xrow[tt] = a.x + (size_t)xr * a.ldx;
+  }
+  const int* wrow[CTW];
+  bool wok[CTW];
+#pragma unroll
+  for (int c = 0; c < CTW; ++c) {
+    const int ch = tile * 16 * CTW + c * 16 + r16;
+    wok[c] = ch < a.N;
+    wrow[c] = reinterpret_cast<const int*>(a.W + (size_t)(wok[c] ? ch : 0) * K);
+  }
+  f32x4_t acc[CTW][TT];
+#pragma unroll
+  for (int c = 0; c < CTW; ++c)
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) acc[c][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int nkb = (K + 127) / 128;
+  const int b0 = s * nkb / S, b1 = (s + 1) * nkb / S;
+  const int nmine = (b1 - b0 - wid + NWS - 1) / NWS;
+  skinny_blocks<TT, CTW>(wrow, wok, xrow, xok, K, grp, b0 + wid, NWS, nmine > 0 ? nmine : 0, 0, acc);
+
+  // epilogue inputs, requested while the partials are exchanged
+  float esc[NE][CTW];
+  bf16_t eres[NE];
+#pragma unroll
+  for (int q = 0; q < NE; ++q) {
+    const int e = tid + 64 * NWS * q;
+    const int tt = e / 256, i = (e / 64) % 4, l = e % 64;
+    const int tok = tt * 16 + (l & 15);
+    const int ch = tile * 16 * CTW + 4 * (l >> 4) + i;
+    const bool ok = e < TT * 256 && tok < a.nb;
+#pragma unroll
+    for (int c = 0; c < CTW; ++c) esc[q][c] = (ok && ch + 16 * c < a.N) ? a.scale[ch + 16 * c] : 0.0f;
+    eres[q] = EPI == EPI_RESID ? a.out[(ok && ch < a.N) ? (size_t)tok * a.ldo + ch : 0] : (bf16_t)0;
+  }
+
+#pragma unroll
+  for (int c = 0; c < CTW; ++c)
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[wid][c * TT + tt][i][lane] = acc[c][tt][i];
+  __syncthreads();
+  // this work-group's partial: element e of accumulator c at part[((tile*S + s)*CTW + c)*TT*256 + e]
+  float v[NE][CTW];
+#pragma unroll
+  for (int q = 0; q < NE; ++q) {
+    const int e = tid + 64 * NWS * q;
+    const int tt = e / 256, i = (e / 64) % 4, l = e % 64;
+#pragma unroll
+    for (int c = 0; c < CTW; ++c) {
+      v[q][c] = 0.0f;
+      if (e < TT * 256) {
+#pragma unroll
+        for (int w = 0; w < NWS; ++w) v[q][c] += red[w][c * TT + tt][i][l];
+        __hip_atomic_store(a.kpart + ((size_t)blockIdx.x * CTW + c) * (TT * 256) + e, v[q][c],
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+  // every store of this work-group has completed before thread 0 counts it in
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned t = __hip_atomic_fetch_add(a.kcnt + tile, 1u, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+    is_last = t == (unsigned)(S - 1);
+  }
+  __syncthreads();
+  if (!is_last) return;
+
+  // the S partials of the tile, eight splits per round trip (agent-coherent buffer loads;
+  // an offset past the buffer's end reads zero and is not added)
+  const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.kpart + (size_t)tile * S * CTW * TT * 256), 0, S * CTW * TT * 256 * 4, 0x00020000);
+#pragma unroll
+  for (int q = 0; q < NE; ++q) {
+    const int e = tid + 64 * NWS * q;
+    if (e >= TT * 256) break;
+    const int tt = e / 256, i = (e / 64) % 4, l = e % 64;
+    const int tok = tt * 16 + (l & 15);
+    const int ch = tile * 16 * CTW + 4 * (l >> 4) + i;
+    float tot[CTW];
+#pragma unroll
+    for (int c = 0; c < CTW; ++c) tot[c] = 0.0f;
+    for (int s0 = 0; s0 < S; s0 += 8) {
+      float pv[8][CTW];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int c = 0; c < CTW; ++c) {
+          const int sj = s0 + j;
+          const int off = (sj < S && sj != s) ? ((sj * CTW + c) * (TT * 256) + e) * 4 : (int)0x80000000;
+          pv[j][c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rp, off, 0, 16));
+        }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int c = 0; c < CTW; ++c) {
+          const int sj = s0 + j;
+          if (sj < S) tot[c] += sj == s ? v[q][c] : pv[j][c];
+        }
+    }
+    skinny_out<EPI, CTW>(a, tile, tok, ch, 4 * (l >> 4) + i, tot, esc[q], eres[q]);
+  }
+  if (tid == 0) __hip_atomic_store(a.kcnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Batched LM head (vocabulary-sized N): a work-group owns 4 waves x LMT 16-channel tiles
@@ -811,54 +1047,64 @@ __global__ __launch_bounds__(256) void k_lm_skinny(GemvArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
-// QK-norm + RoPE + KV-cache write, one work-group per token row.
+// QK-norm + RoPE + KV-cache write.  Work-group (row, head group): each wave owns one head
+// slot of the row (q heads, then k heads, then v heads), so a wave makes one round trip.
 // q and k heads: RMSNorm over head_dim with a shared gain, then rotate-half RoPE at
 // the row's position; q is written back in place, k and v go to the cache.
 __global__ __launch_bounds__(256) void k_qk_rope(RopeArgs a) {
   const int r = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int hh = blockIdx.y * 4 + __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (hh >= a.H + 2 * a.KV) return;  // whole waves; the kernel has no block barrier
   const int D = a.D, half = D / 2;
   const int slot = a.row_slot[r], p = a.row_pos[r];
-  bf16_t* row = a.qkv + (size_t)r * a.ldqkv;
+  bf16_t* src = a.qkv + (size_t)r * a.ldqkv + (size_t)hh * D;
+  if (hh >= a.H + a.KV) {
+    const int g = hh - a.H - a.KV;
+    bf16_t* dst = a.vcache + (((size_t)slot * a.KV + g) * a.max_ctx + p) * D;
+    for (int i = lane; i < D; i += 64) dst[i] = src[i];
+    return;
+  }
+  const bool isq = hh < a.H;
+  const float* gn = isq ? a.q_gain : a.k_gain;
   const float2* tab = a.rope + (size_t)p * half;
-  for (int hh = wid; hh < a.H + 2 * a.KV; hh += 4) {
-    bf16_t* src = row + (size_t)hh * D;
-    if (hh < a.H + a.KV) {
-      const bool isq = hh < a.H;
-      const float* gn = isq ? a.q_gain : a.k_gain;
-      float x1[2], x2[2], ss = 0.0f;
+  // every input of the head requested at once, from clamped (valid) indices
+  bf16_t xb1[2], xb2[2];
+  float g1[2], g2[2];
+  float2 cs[2];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int i = lane + 64 * j;
-        x1[j] = x2[j] = 0.0f;
-        if (i < half) {
-          x1[j] = bf2f(src[i]);
-          x2[j] = bf2f(src[i + half]);
-          ss += x1[j] * x1[j] + x2[j] * x2[j];
-        }
-      }
-      ss = wave_sum(ss);
-      const float denom = sqrtf(ss / (float)D + a.eps);
-      bf16_t* dst = src;
-      if (!isq) {
-        const int g = hh - a.H;
-        dst = a.kcache + (((size_t)slot * a.KV + g) * a.max_ctx + p) * D;
-      }
+  for (int j = 0; j < 2; ++j) {
+    const int i = lane + 64 * j;
+    const int ic = i < half ? i : 0;
+    xb1[j] = src[ic];
+    xb2[j] = src[ic + half];
+    g1[j] = gn[ic];
+    g2[j] = gn[ic + half];
+    cs[j] = tab[ic];
+  }
+  float x1[2], x2[2], ss = 0.0f;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int i = lane + 64 * j;
-        if (i < half) {
-          const float y1 = rbf(x1[j] / denom * gn[i]);
-          const float y2 = rbf(x2[j] / denom * gn[i + half]);
-          const float2 cs = tab[i];
-          dst[i] = f2bf(y1 * cs.x - y2 * cs.y);
-          dst[i + half] = f2bf(y2 * cs.x + y1 * cs.y);
-        }
-      }
-    } else {
-      const int g = hh - a.H - a.KV;
-      bf16_t* dst = a.vcache + (((size_t)slot * a.KV + g) * a.max_ctx + p) * D;
-      for (int i = lane; i < D; i += 64) dst[i] = src[i];
+  for (int j = 0; j < 2; ++j) {
+    const bool ok = lane + 64 * j < half;
+    x1[j] = ok ? bf2f(xb1[j]) : 0.0f;
+    x2[j] = ok ? bf2f(xb2[j]) : 0.0f;
+    ss += x1[j] * x1[j] + x2[j] * x2[j];
+  }
+  ss = wave_sum(ss);
+  const float denom = sqrtf(ss / (float)D + a.eps);
+  bf16_t* dst = src;
+  if (!isq) {
+    const int g = hh - a.H;
+    dst = a.kcache + (((size_t)slot * a.KV + g) * a.max_ctx + p) * D;
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int i = lane + 64 * j;
+    if (i < half) {
+      const float y1 = rbf(x1[j] / denom * g1[j]);
+      const float y2 = rbf(x2[j] / denom * g2[j]);
+      dst[i] = f2bf(y1 * cs[j].x - y2 * cs[j].y);
+      dst[i + half] = f2bf(y2 * cs[j].x + y1 * cs[j].y);
     }
   }
 }
@@ -888,7 +1134,8 @@ __global__ __launch_bounds__(64 * NW) void k_attn_dec(AttnDecArgs a) {
   __shared__ float wo[NW][G][D];
   __shared__ int last_flag;
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  // wave index as a scalar: per-wave choices (which head, which gain vector) stay scalar
+  const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tl = lane >> 2, part = lane & 3;
   const int p = a.pos[b];
   const int n = p + 1;
@@ -902,25 +1149,37 @@ __global__ __launch_bounds__(64 * NW) void k_attn_dec(AttnDecArgs a) {
   const bool vlane = (D >= 64) || (lane < D);
 
   // ---- K/V tiles of the first chunk, requested before anything else ----
+  // Buffer loads: a position outside the split (or p itself, taken from LDS) reads zero
+  // through an out-of-range offset, so no load sits in a branch and every wait counts
+  // exactly the loads it needs.
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc(Kb, 0, a.max_ctx * D * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc(Vb, 0, a.max_ctx * D * 2, 0x00020000);
+  constexpr int OOB = (int)0x80000000;
   uint4 kc[KV4], kx[KV4];
   uint32_t vc[16][VW], vx[16][VW];
+  // (the wave index here is the per-lane one: with scalar validity conditions the
+  // compiler branches around groups of loads instead of selecting offsets)
+  const int wv = tid >> 6;
   auto load_tiles = [&](uint4 (&kk)[KV4], uint32_t (&vv)[16][VW], int t0) {
-    const int t = t0 + 16 * wid + tl;
+    const int t = t0 + 16 * wv + tl;
+    const bool kok = t < t_end && t != p;
 #pragma unroll
     for (int j = 0; j < KV4; ++j)
-      kk[j] = (t < t_end && t != p)
-                         ? *reinterpret_cast<const uint4*>(Kb + (size_t)t * D + part * KQ + 8 * j)
-                         : make_uint4(0, 0, 0, 0);
+      kk[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            krs, kok ? (t * D + part * KQ + 8 * j) * 2 : OOB, 0, 0));
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int tv = t0 + 16 * wid + i;
+      const int tv = t0 + 16 * wv + i;
       const bool ok = tv < t_end && tv != p && vlane;
 #pragma unroll
       for (int w = 0; w < VW; ++w) {
         if (DPL >= 2) {
-          vv[i][w] = ok ? *reinterpret_cast<const uint32_t*>(Vb + (size_t)tv * D + DPL * lane + 2 * w) : 0u;
+          vv[i][w] = __builtin_amdgcn_raw_buffer_load_b32(
+              vrs, ok ? (tv * D + DPL * lane + 2 * w) * 2 : OOB, 0, 0);
         } else {
-          vv[i][w] = ok ? (uint32_t)Vb[(size_t)tv * D + lane] : 0u;
+          vv[i][w] = __builtin_amdgcn_raw_buffer_load_b16(vrs, ok ? (tv * D + lane) * 2 : OOB, 0, 0);
         }
       }
     }
@@ -932,40 +1191,46 @@ __global__ __launch_bounds__(64 * NW) void k_attn_dec(AttnDecArgs a) {
   auto head_src = [&](int hh) {
     return hh < G ? row + (size_t)(g * G + hh) * D : row + (size_t)(a.H + g) * D;
   };
-  float x1[2], x2[2], gg1[2], gg2[2];
-  float2 cs2[2];
+  // Loads from clamped (always valid) indices, projections kept as raw bits until used: a
+  // load in a branch, or converted where it lands, makes the wave wait for it there.
+  constexpr int HJ = HALF > 64 ? 2 : 1;  // 64-lane passes over half a head
+  bf16_t xb1[HJ], xb2[HJ];
+  float gg1[HJ], gg2[HJ];
+  float2 cs2[HJ];
   auto head_load = [&](int hh) {
     const bf16_t* src = head_src(hh);
     const float* gn = hh < G ? a.q_gain : a.k_gain;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < HJ; ++j) {
       const int i = lane + 64 * j;
-      x1[j] = x2[j] = gg1[j] = gg2[j] = 0.0f;
-      cs2[j] = make_float2(0.0f, 0.0f);
-      if (i < HALF) {
-        x1[j] = bf2f(src[i]);
-        x2[j] = bf2f(src[i + HALF]);
-        gg1[j] = gn[i];
-        gg2[j] = gn[i + HALF];
-        cs2[j] = tab[i];
-      }
+      const int ic = i < HALF ? i : 0;
+      xb1[j] = src[ic];
+      xb2[j] = src[ic + HALF];
+      gg1[j] = gn[ic];
+      gg2[j] = gn[ic + HALF];
+      cs2[j] = tab[ic];
     }
   };
   const bf16_t* vsrc = row + (size_t)(a.H + a.KV + g) * D;
   const int vi = tid < D ? tid : 0;
   const bf16_t vfirst = vsrc[vi];
-  if (wid <= G) head_load(wid);
-  if (t_begin < t_end) load_tiles(kc, vc, t_begin);
+  head_load(wid <= G ? wid : G);  // unconditional: waves past the G + 1 heads discard it
+  load_tiles(kc, vc, t_begin);    // unconditional: an empty split reads zeros
   for (int hh = wid; hh <= G; hh += NW) {
     if (hh != wid) head_load(hh);
     const bool isq = hh < G;
-    float ss = 0.0f;
+    float ss = 0.0f, x1[HJ], x2[HJ];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) ss += x1[j] * x1[j] + x2[j] * x2[j];
+    for (int j = 0; j < HJ; ++j) {
+      const bool ok = lane + 64 * j < HALF;
+      x1[j] = ok ? bf2f(xb1[j]) : 0.0f;
+      x2[j] = ok ? bf2f(xb2[j]) : 0.0f;
+      ss += x1[j] * x1[j] + x2[j] * x2[j];
+    }
     ss = wave_sum(ss);
     const float inv = 1.0f / sqrtf(ss / (float)D + a.eps);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < HJ; ++j) {
       const int i = lane + 64 * j;
       if (i < HALF) {
         const float y1 = rbf(x1[j] * inv * gg1[j]);
@@ -1311,16 +1576,22 @@ __global__ __launch_bounds__(256) void k_flash_prefill(FlashArgs a) {
   for (int nt = 0; nt < NT; ++nt) o[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const float scale = 1.0f / sqrtf((float)D);
 
-  // global -> register staging of one K/V block
+  // global -> register staging of one K/V block.  K: consecutive lanes take consecutive
+  // 16-byte pieces of a key row.  V: consecutive lanes take consecutive keys (same piece),
+  // so the transposed LDS stores of a quarter-wave hit consecutive addresses instead of
+  // rows 8 apart (which all map to one bank).
   uint4 kst[LD_PER_T], vst[LD_PER_T];
   auto fetch = [&](int kb) {
 #pragma unroll
     for (int u = 0; u < LD_PER_T; ++u) {
       const int idx = tid + 256 * u;
       const int key = idx / VPR, c = idx % VPR;
-      const bool ok = idx < KB * VPR && kb + key < kmax;
-      kst[u] = ok ? *reinterpret_cast<const uint4*>(Kb + (size_t)(kb + key) * D + 8 * c) : make_uint4(0, 0, 0, 0);
-      vst[u] = ok ? *reinterpret_cast<const uint4*>(Vb + (size_t)(kb + key) * D + 8 * c) : make_uint4(0, 0, 0, 0);
+      const int vkey = idx % KB, vc = idx / KB;
+      const bool in = idx < KB * VPR;
+      kst[u] = (in && kb + key < kmax) ? *reinterpret_cast<const uint4*>(Kb + (size_t)(kb + key) * D + 8 * c)
+                                       : make_uint4(0, 0, 0, 0);
+      vst[u] = (in && kb + vkey < kmax) ? *reinterpret_cast<const uint4*>(Vb + (size_t)(kb + vkey) * D + 8 * vc)
+                                        : make_uint4(0, 0, 0, 0);
     }
   };
   fetch(0);
@@ -1331,11 +1602,12 @@ __global__ __launch_bounds__(256) void k_flash_prefill(FlashArgs a) {
       if (idx < KB * VPR) {
         const int key = idx / VPR, c = idx % VPR;
         *reinterpret_cast<uint4*>(&Ks[key][8 * c]) = kst[u];
+        const int vkey = idx % KB, vc = idx / KB;
         const uint32_t w4[4] = {vst[u].x, vst[u].y, vst[u].z, vst[u].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          Vt[8 * c + 2 * e][key] = (bf16_t)(w4[e] & 0xFFFFu);
-          Vt[8 * c + 2 * e + 1][key] = (bf16_t)(w4[e] >> 16);
+          Vt[8 * vc + 2 * e][vkey] = (bf16_t)(w4[e] & 0xFFFFu);
+          Vt[8 * vc + 2 * e + 1][vkey] = (bf16_t)(w4[e] >> 16);
         }
       }
     }
@@ -1528,6 +1800,18 @@ static hipError_t skinny_tt(const GemvArgs& a, int epi, hipStream_t st) {
   }
   const int ctw = epi == EPI_SILU ? 2 : 1;
   const int ntiles = (a.N + 16 * ctw - 1) / (16 * ctw);
+  if (a.ksplit > 1) {
+    if (ntiles > SKINNY_MAX_TILES || a.ksplit > SKINNY_MAX_SPLIT ||
+        (size_t)ntiles * a.ksplit * ctw * TT * 256 > GEMM_PART_FLOATS || !a.kpart || !a.kcnt)
+      return hipErrorInvalidValue;
+    dim3 g(ntiles * a.ksplit);
+    switch (epi) {
+      case EPI_STORE: hipLaunchKernelGGL((k_skinny_split<TT, EPI_STORE, 4>), g, dim3(256), 0, st, a); break;
+      case EPI_RESID: hipLaunchKernelGGL((k_skinny_split<TT, EPI_RESID, 4>), g, dim3(256), 0, st, a); break;
+      default: hipLaunchKernelGGL((k_skinny_split<TT, EPI_SILU, 4>), g, dim3(256), 0, st, a); break;
+    }
+    return hipGetLastError();
+  }
   dim3 grid(ntiles);
   if (ntiles < 128) {  // few tiles: eight waves split K eight ways
     switch (epi) {
@@ -1555,11 +1839,15 @@ hipError_t launch_skinny(const GemvArgs& a, int epi, hipStream_t st) {
 
 hipError_t launch_gemm(const GemmArgs& a0, hipStream_t st) {
   GemmArgs a = a0;
+  if ((a.K & 31) || (size_t)(a.M + 64) * a.lda * 2 > 0x7FFFFFFFu || (size_t)(a.N + 64) * a.K > 0x7FFFFFFFu)
+    return hipErrorInvalidValue;
   const int tiles = ((a.N + 63) / 64) * ((a.M + 63) / 64);
   // split K when the tile grid leaves most of the 256 CUs idle
   int splits = 1;
-  while (splits < 8 && tiles * splits < 256 && a.K / (splits * 2) >= 256 &&
-         (size_t)(splits * 2) * a.M * a.N <= GEMM_PART_FLOATS && a.part)
+  const int max_splits = a.splits > 0 ? a.splits : 8;  // caller's cap (tuning), else 8
+  while (splits < max_splits && tiles * splits < 256 && a.K / (splits * 2) >= 256 &&
+         (size_t)(splits * 2) * tiles * 4096 <= GEMM_PART_FLOATS && a.part && a.cnt &&
+         tiles <= SKINNY_MAX_TILES)
     splits *= 2;
   a.splits = splits;
   dim3 grid((a.N + 63) / 64, (a.M + 63) / 64, splits);
@@ -1568,36 +1856,35 @@ hipError_t launch_gemm(const GemmArgs& a0, hipStream_t st) {
     case EPI_RESID: hipLaunchKernelGGL(k_gemm<EPI_RESID>, grid, dim3(256), 0, st, a); break;
     default: hipLaunchKernelGGL(k_gemm<EPI_SILU>, grid, dim3(256), 0, st, a); break;
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || splits == 1) return e;
-  const long n = (long)a.M * (a.epi == EPI_SILU ? a.N / 2 : a.N);
-  dim3 g2((unsigned)((n + 255) / 256));
-  switch (a.epi) {
-    case EPI_STORE: hipLaunchKernelGGL(k_gemm_finish<EPI_STORE>, g2, dim3(256), 0, st, a); break;
-    case EPI_RESID: hipLaunchKernelGGL(k_gemm_finish<EPI_RESID>, g2, dim3(256), 0, st, a); break;
-    default: hipLaunchKernelGGL(k_gemm_finish<EPI_SILU>, g2, dim3(256), 0, st, a); break;
-  }
   return hipGetLastError();
 }
 
 hipError_t launch_qk_rope(const RopeArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_qk_rope, dim3(a.M), dim3(256), 0, st, a);
+  if (a.M <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_qk_rope, dim3(a.M, (a.H + 2 * a.KV + 3) / 4), dim3(256), 0, st, a);
   return hipGetLastError();
+}
+
+// 8 waves only where the wave-merge buffers stay small (G * D <= 512); other shapes are
+// never instantiated with 8
+template <int D, int G, int NW>
+static void attn_dec_launch(const AttnDecArgs& a, dim3 grid, hipStream_t st) {
+  constexpr int W = (NW == 8 && G * D > 512) ? 4 : NW;
+  hipLaunchKernelGGL((k_attn_dec<D, G, W>), grid, dim3(64 * W), 0, st, a);
 }
 
 template <int D, int NW>
 static hipError_t attn_dec_dw(const AttnDecArgs& a, int G, hipStream_t st) {
   dim3 grid(a.nsplit, a.KV, a.B);
-  dim3 blk(64 * NW);
   switch (G) {
-    case 1: hipLaunchKernelGGL((k_attn_dec<D, 1, NW>), grid, blk, 0, st, a); break;
-    case 2: hipLaunchKernelGGL((k_attn_dec<D, 2, NW>), grid, blk, 0, st, a); break;
-    case 3: hipLaunchKernelGGL((k_attn_dec<D, 3, NW>), grid, blk, 0, st, a); break;
-    case 4: hipLaunchKernelGGL((k_attn_dec<D, 4, NW>), grid, blk, 0, st, a); break;
-    case 5: hipLaunchKernelGGL((k_attn_dec<D, 5, NW>), grid, blk, 0, st, a); break;
-    case 6: hipLaunchKernelGGL((k_attn_dec<D, 6, NW>), grid, blk, 0, st, a); break;
-    case 7: hipLaunchKernelGGL((k_attn_dec<D, 7, NW>), grid, blk, 0, st, a); break;
-    default: hipLaunchKernelGGL((k_attn_dec<D, 8, NW>), grid, blk, 0, st, a); break;
+    case 1: attn_dec_launch<D, 1, NW>(a, grid, st); break;
+    case 2: attn_dec_launch<D, 2, NW>(a, grid, st); break;
+    case 3: attn_dec_launch<D, 3, NW>(a, grid, st); break;
+    case 4: attn_dec_launch<D, 4, NW>(a, grid, st); break;
+    case 5: attn_dec_launch<D, 5, NW>(a, grid, st); break;
+    case 6: attn_dec_launch<D, 6, NW>(a, grid, st); break;
+    case 7: attn_dec_launch<D, 7, NW>(a, grid, st); break;
+    default: attn_dec_launch<D, 8, NW>(a, grid, st); break;
   }
   return hipGetLastError();
 }

@@ -40,6 +40,9 @@ CONFIGS = {
                        intermediate=160, vocab=1000), 1, "uniform", 77, 1001, 12),
     "mid": (ModelShape(hidden=512, n_layers=2, n_heads=8, n_kv_heads=4, head_dim=128,
                        intermediate=1024, vocab=4096), 4, "uniform", 200, 1004, 8),
+    # hidden and intermediate not multiples of 128 (ragged 128-k blocks in split-K)
+    "splitk": (ModelShape(hidden=288, n_layers=2, n_heads=6, n_kv_heads=2, head_dim=32,
+                          intermediate=544, vocab=1000), 5, "uniform", 8, 4000, 4),
     # long context at a small shape: many attention splits and prefill tiles
     "wide-long": (ModelShape(hidden=128, n_layers=2, n_heads=4, n_kv_heads=2, head_dim=64,
                              intermediate=256, vocab=512), 5, "uniform", 1500, 1005, 24),

@@ -214,6 +214,38 @@ def test_batched_teacher_forced_logits():
         m.close()
 
 
+# hidden 288 and intermediate 544 are not multiples of 128: the last 128-k block of a
+# split is partial; down (544 -> 288) splits five ways, q|k|v and gate|up three ways
+SPLITK = ModelShape(hidden=288, n_layers=2, n_heads=6, n_kv_heads=2, head_dim=32,
+                    intermediate=544, vocab=1000)
+
+
+@pytest.mark.parametrize("B,split", [(3, 3), (20, 1), (20, 3), (33, 2)],
+                         ids=["b3-all", "b20-off", "b20-all", "b33-few"])
+def test_batched_split_k_teacher_forced(B, split):
+    """Batched decode projections with K split over work-groups (last arrival adds the
+    partials in split order) against the oracle per sequence, and against no split."""
+    shape = SPLITK
+    w = make_weights(shape, seed=5, gains="uniform")
+    qm = quantize_model(w)
+    prompts = [make_prompt(shape.vocab, 6 + (b % 5), 4000 + b) for b in range(B)]
+    say(f"[gpu] batched split-K teacher-forced B={B} skinny_split={split}")
+    m = _model(shape, w, max_batch=B, max_ctx=32, max_prefill_tokens=B * 12)
+    try:
+        m.set_tuning(skinny_split=split)
+        orcs = [Oracle(shape, qm, mode="bf16").generate(p, 4) for p in prompts]
+        m.prefill(prompts)
+        for k in range(1, 4):
+            feed = torch.tensor([o["ids"][k - 1] for o in orcs], dtype=torch.int32, device="cuda")
+            nxt, lg = m.decode_step(feed, logits=True)
+            torch.cuda.synchronize()
+            for b in range(B):
+                check_step(lg[b].cpu().numpy(), nxt[b].item(), orcs[b]["logits"][k],
+                           orcs[b]["margin"][k], "splitk", f"b{b} step {k}")
+    finally:
+        m.close()
+
+
 def test_error_paths_do_no_gpu_work(tiny_setup):
     import int8_weight_only_amd as qd
     shape, w, qm, m = tiny_setup
