@@ -238,6 +238,12 @@ typedef enum {
                                      16-channel tiles at batches over 16, 3 all */
   QD_TUNE_GEMM_SPLITS = 7,        /* prefill GEMMs: most split-K ways, 1..8, or 0 (default: 8;
                                      the launcher splits only while the tiles leave CUs idle) */
+  QD_TUNE_ATTN_OCCUPANCY = 8,     /* decode attention: splits target this many work-groups per
+                                     CU over all (row, KV head) pairs, 1..8, or 0 (default: as
+                                     many as stay resident, 1 for 8 waves, 3 for 4 waves) */
+  QD_TUNE_SKINNY_NORM = 9,        /* batched decode: 1 (default) folds the RMSNorm before q|k|v
+                                     and gate|up into the projection where the shape allows;
+                                     0: a separate normalization launch */
 } qd_tune_knob;
 
 /* Sets a knob; captured decode graphs are dropped so the next call re-captures.

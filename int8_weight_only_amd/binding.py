@@ -90,7 +90,7 @@ EXPORTS = ("qd_last_error", "qd_check_shape", "qd_query_sizes", "qd_load_weights
            "qd_export_quantized", "qd_prefill", "qd_decode_step", "qd_generate_greedy",
            "qd_free", "qd_profile_kernels", "qd_set_tuning")
 TUNING = {"attn_max_splits": 0, "attn_min_chunks": 1, "attn_waves": 2, "attn_merge_last": 3,
-          "persistent": 4, "persist_splits": 5, "skinny_split": 6, "gemm_splits": 7}
+          "persistent": 4, "persist_splits": 5, "skinny_split": 6, "gemm_splits": 7, "attn_occupancy": 8, "skinny_norm": 9}
 PROF_KERNELS = ("embed", "qkv", "attn", "o", "gateup", "down", "lmhead")
 
 _lib = None

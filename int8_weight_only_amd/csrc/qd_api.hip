@@ -229,9 +229,11 @@ struct qd_model {
   bool stage_pending = false;
   int attn_max_splits = 64;
   int attn_min_chunks = 1;
+  int attn_occupancy = 0;  // attention work-groups per CU the split targets (0: by waves)
   int attn_waves = 0;  // 0: eight waves only when B x KV heads fill the GPU without splits
   int attn_merge_last = 1;
   int gemm_splits = 0;  // prefill GEMM split-K cap (0: launcher default)
+  int skinny_norm = 1;   // batched projections fold the RMSNorm where the shape allows
   int skinny_split = 2;  // 1: never; 2: fewer than 128 channel tiles, over 16 rows; 3: all
   // persistent single-sequence decode (one cooperative launch per call)
   bool persist_ok = false;     // this shape and device can run it
@@ -258,13 +260,23 @@ struct qd_model {
 
 namespace {
 
-// attention split over positions 0..ctx-1: depends on the context only, so a sequence's
-// result does not depend on the batch it runs in
-// work-groups in flight are capped near one per CU: more splits only add merge traffic
-void attn_split(int ctx, int cap, int max_splits, int min_chunks, int rows_x_kv, int* nsplit,
-                int* split_len) {
+// attention split over positions 0..ctx-1, from the context, the tuning knobs and the
+// number of (row, KV head) pairs: work-groups in flight are capped near `occupancy` per CU
+// (256 CUs), since more splits only add merge traffic
+void attn_split(int ctx, int cap, int max_splits, int min_chunks, int occupancy, int rows_x_kv,
+                int* nsplit, int* split_len);
+
+// decode-attention waves per work-group: eight when the (row, KV head) pairs alone cover
+// the CUs, else four
+int attn_waves_for(const qd_model* m, int B);
+// work-groups per CU the split targets: as many as stay resident (the 8-wave kernel holds
+// one per CU, the 4-wave kernel three; measured best at B = 1..32)
+int attn_occupancy_for(const qd_model* m, int B);
+
+void attn_split(int ctx, int cap, int max_splits, int min_chunks, int occupancy, int rows_x_kv,
+                int* nsplit, int* split_len) {
   const int chunks = std::max(1, (ctx + ATT_CHUNK - 1) / ATT_CHUNK);
-  max_splits = std::min(max_splits, std::max(1, 256 / std::max(1, rows_x_kv)));
+  max_splits = std::min(max_splits, std::max(1, 256 * occupancy / std::max(1, rows_x_kv)));
   int want = std::max(1, std::min(std::min(chunks, cap), max_splits));
   want = std::max(1, std::min(want, chunks / std::max(1, min_chunks)));
   const int per = (chunks + want - 1) / want;
@@ -345,14 +357,17 @@ qd_status dec_proj(qd_model* m, int B, const bf16_t* x, int ldx, const float* ga
     HIPCHK(launch_gemv(a, epi, st));
     return QD_OK;
   }
-  if (gain) {
+  a.ksplit = skinny_splits(m, B, N, K, epi);
+  if (gain && m->skinny_norm && skinny_norm_ok(B, K, epi, a.ksplit)) {
+    a.gain = gain;  // the RMSNorm runs inside the projection
+    a.eps = m->shape.rms_eps;
+  } else if (gain) {
     bf16_t* h = m->ws<bf16_t>(m->P.h);
     HIPCHK(launch_rmsnorm(x, B, K, gain, m->shape.rms_eps, h, st));
     x = h;
     ldx = K;
   }
   a.x = x; a.ldx = ldx;
-  a.ksplit = skinny_splits(m, B, N, K, epi);
   a.kpart = m->ws<float>(m->P.gemm_part);
   a.kcnt = m->ws<unsigned int>(m->P.sk_cnt);
   HIPCHK(launch_skinny(a, epi, st));
@@ -366,6 +381,15 @@ qd_status dec_qkv(qd_model* m, int l, int B, hipStream_t st) {
                   m->w<float>(o.qkv_s), d.NQKV, d.d, EPI_STORE, m->ws<bf16_t>(m->P.qkv), d.NQKV, st);
 }
 
+int attn_waves_for(const qd_model* m, int B) {
+  return m->attn_waves ? m->attn_waves : (B * m->d.KV >= 256 ? 8 : 4);
+}
+
+int attn_occupancy_for(const qd_model* m, int B) {
+  if (m->attn_occupancy) return m->attn_occupancy;
+  return attn_waves_for(m, B) == 8 ? 1 : 3;
+}
+
 qd_status dec_attn(qd_model* m, int l, int B, int nsplit, int split_len, hipStream_t st) {
   const Dims& d = m->d;
   const LayerOff& o = m->P.L[l];
@@ -377,7 +401,7 @@ qd_status dec_attn(qd_model* m, int l, int B, int nsplit, int split_len, hipStre
   aa.kcache = m->kcache(l); aa.vcache = m->vcache(l);
   aa.H = d.H; aa.KV = d.KV; aa.D = d.D; aa.max_ctx = m->lim.max_ctx; aa.B = B;
   aa.split_len = split_len; aa.nsplit = nsplit;
-  aa.nwaves = m->attn_waves ? m->attn_waves : (B * d.KV >= 256 ? 8 : 4);
+  aa.nwaves = attn_waves_for(m, B);
   aa.merge_last = m->attn_merge_last;
   aa.part_o = m->ws<float>(m->P.part_o); aa.part_ml = m->ws<float>(m->P.part_ml);
   aa.counters = m->ws<unsigned int>(m->P.att_cnt);
@@ -891,7 +915,7 @@ qd_status qd_decode_step(qd_model* m, int32_t B, const int32_t* in_ids_dev, floa
     s = persist_launch(m, in_ids_dev, 1, nullptr, next_ids_dev, logits_dev, (hipStream_t)stream);
   } else {
     int nsplit, split_len;
-    attn_split(ctx, m->P.nsplit_cap, m->attn_max_splits, m->attn_min_chunks, B * m->d.KV, &nsplit,
+    attn_split(ctx, m->P.nsplit_cap, m->attn_max_splits, m->attn_min_chunks, attn_occupancy_for(m, B), B * m->d.KV, &nsplit,
                &split_len);
     s = enqueue_decode(m, B, in_ids_dev, logits_dev, next_ids_dev, false, nsplit, split_len,
                        (hipStream_t)stream);
@@ -956,7 +980,7 @@ qd_status qd_generate_greedy(qd_model* m, int32_t B, const int32_t* prompt_ids_h
     int nsplit, split_len;
     // round the context up so one captured graph serves many calls
     const int ctx_cap = std::min(m->lim.max_ctx, ((need + 255) / 256) * 256);
-    attn_split(ctx_cap, P.nsplit_cap, m->attn_max_splits, m->attn_min_chunks, B * m->d.KV, &nsplit, &split_len);
+    attn_split(ctx_cap, P.nsplit_cap, m->attn_max_splits, m->attn_min_chunks, attn_occupancy_for(m, B), B * m->d.KV, &nsplit, &split_len);
     auto key = std::make_tuple(B, nsplit, split_len);
     auto it = m->graphs.find(key);
     hipGraphExec_t exec = nullptr;
@@ -1019,7 +1043,7 @@ qd_status qd_profile_kernels(qd_model* m, int32_t B, int32_t iters, float* us_ou
     ctx = std::max(ctx, m->host_pos[b] + 1);
   }
   int nsplit, split_len;
-  attn_split(ctx, m->P.nsplit_cap, m->attn_max_splits, m->attn_min_chunks, B * m->d.KV, &nsplit, &split_len);
+  attn_split(ctx, m->P.nsplit_cap, m->attn_max_splits, m->attn_min_chunks, attn_occupancy_for(m, B), B * m->d.KV, &nsplit, &split_len);
   hipStream_t st = (hipStream_t)stream;
   int* scratch_ids = m->ws<int>(m->P.ids);   // prompt-id area doubles as the profiling id list
   HIPCHK(launch_fill_i32(scratch_ids, B, 0, st));
@@ -1059,7 +1083,8 @@ qd_status qd_set_tuning(qd_model* m, int32_t knob, int32_t value) {
   g_err.clear();
   if (!m) return fail(QD_ERR_INVALID_ARGUMENTS, "model is NULL");
   if (value < 0 || (value < 1 && knob != QD_TUNE_ATTN_MERGE_LAST && knob != QD_TUNE_ATTN_WAVES &&
-                    knob != QD_TUNE_PERSISTENT && knob != QD_TUNE_GEMM_SPLITS))
+                    knob != QD_TUNE_PERSISTENT && knob != QD_TUNE_GEMM_SPLITS &&
+                    knob != QD_TUNE_ATTN_OCCUPANCY && knob != QD_TUNE_SKINNY_NORM))
     return fail(QD_ERR_INVALID_ARGUMENTS, "value out of range");
   switch (knob) {
     case QD_TUNE_ATTN_MAX_SPLITS: m->attn_max_splits = value; break;
@@ -1075,6 +1100,14 @@ qd_status qd_set_tuning(qd_model* m, int32_t knob, int32_t value) {
     case QD_TUNE_PERSIST_SPLITS:
       if (value > PERSIST_SPLITS) return fail(QD_ERR_INVALID_ARGUMENTS, "at most 32 splits");
       m->persist_splits = value;
+      break;
+    case QD_TUNE_SKINNY_NORM:
+      if (value > 1) return fail(QD_ERR_INVALID_ARGUMENTS, "skinny norm mode must be 0 or 1");
+      m->skinny_norm = value;
+      break;
+    case QD_TUNE_ATTN_OCCUPANCY:
+      if (value > 8) return fail(QD_ERR_INVALID_ARGUMENTS, "attention occupancy must be 0..8");
+      m->attn_occupancy = value;
       break;
     case QD_TUNE_GEMM_SPLITS:
       if (value > 8) return fail(QD_ERR_INVALID_ARGUMENTS, "at most 8 GEMM splits");

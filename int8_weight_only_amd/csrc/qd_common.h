@@ -201,6 +201,8 @@ hipError_t launch_rmsnorm(const bf16_t* x, int M, int d, const float* g, float e
                           hipStream_t st);
 hipError_t launch_gemv(const GemvArgs& a, int epi, hipStream_t st);
 hipError_t launch_skinny(const GemvArgs& a, int epi, hipStream_t st);
+// whether launch_skinny can fold the RMSNorm (gain set) for nb rows of a K-long input
+bool skinny_norm_ok(int nb, int K, int epi, int ksplit);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
 hipError_t launch_qk_rope(const RopeArgs& a, hipStream_t st);
 hipError_t launch_attention_decode(const AttnDecArgs& a, hipStream_t st);

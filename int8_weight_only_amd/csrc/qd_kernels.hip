@@ -405,14 +405,16 @@ __device__ __forceinline__ bf16x8_t i8x8_to_bf16x8(uint2 w) {
   return __builtin_bit_cast(bf16x8_t, make_uint4(out[0], out[1], out[2], out[3]));
 }
 
-// 64x64 output tile per work-group (4 waves in 2x2, each 32x32 = 2x2 MFMA 16x16x32
-// tiles), k advancing 64 at a time.  The loads of GEMM_PF k-steps ahead are in flight
-// while one step is multiplied out of LDS (double-buffered, one barrier per step); the
-// weights are converted to bf16 once, when a step is written to LDS.  All loads are
-// buffer loads whose out-of-range offsets read zero, so no load sits in a branch and
-// each step waits only for its own data.  With split-K (blockIdx.z) each work-group
-// stores its fp32 tile partial agent-coherently; the last of a tile's work-groups to
-// arrive adds the partials in split order and runs the epilogue.
+// 64x64 output tile per work-group of 8 waves: k advances 128 per step, waves 0-3 take
+// the first 64 k of each step and waves 4-7 the second (each group 2x2 waves of 32x32 =
+// 2x2 MFMA 16x16x32 tiles), so every SIMD runs two independent chains between the
+// step barriers; the two halves are added in LDS at the end.  The loads of GEMM_PF steps
+// ahead are in flight while one step is multiplied out of LDS (double-buffered, one
+// barrier per step); the weights are converted to bf16 once, when a step is written to
+// LDS.  All loads are buffer loads whose out-of-range offsets read zero, so no load sits
+// in a branch and each step waits only for its own data.  With split-K (blockIdx.z) each
+// work-group stores its fp32 tile partial agent-coherently; the last of a tile's
+// work-groups to arrive adds the partials in split order and runs the epilogue.
 template <int EPI>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, int m, int n, float v, float vu,
                                               float sv, float su) {
@@ -432,14 +434,15 @@ constexpr int GEMM_PF = 4;  // k-steps of loads in flight
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 template <int EPI>
-__global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
-  constexpr int BM = 64, BN = 64, BK = 64, P = GEMM_PF;
+__global__ __launch_bounds__(512) void k_gemm(GemmArgs a) {
+  constexpr int BM = 64, BN = 64, BK = 128, P = GEMM_PF;
   constexpr int OOB = (int)0x80000000;
-  __shared__ __align__(16) bf16_t As[2][BM][BK + 8];
-  __shared__ __align__(16) bf16_t Ws[2][BN][BK + 8];
+  constexpr int LDT = BK + 8;  // LDS row pitch (elements)
+  __shared__ __align__(16) bf16_t As[2][BM][LDT];
+  __shared__ __align__(16) bf16_t Ws[2][BN][LDT];
   __shared__ int is_last;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid & 1, wn = wid >> 1;
+  const int kh = wid >> 2, wm = wid & 1, wn = (wid >> 1) & 1;
   const int grp = lane >> 4, r16 = lane & 15;
   const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
   const int S = a.splits, z = blockIdx.z;
@@ -454,24 +457,24 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
       __builtin_amdgcn_make_buffer_rsrc((void*)a.A, 0, a.M * a.lda * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t wrsc =
       __builtin_amdgcn_make_buffer_rsrc((void*)a.W, 0, a.N * a.K, 0x00020000);
-  // staging: A row tid/4 (two 16-byte pieces), W row tid/4 (one 16-byte piece)
-  const int ar = tid >> 2, ac = (tid & 3) * 16;
-  const int wr = tid >> 2, wc = (tid & 3) * 16;
+  // staging: A row tid/8, pieces at k 8*(tid%8) and 64 + 8*(tid%8) (each load instruction
+  // reads 128 contiguous bytes per row); W row tid/8, one 16-byte piece at k 16*(tid%8)
+  const int sr = tid >> 3, sa = (tid & 7) * 8, sw = (tid & 7) * 16;
   struct Stage { uint4 a0, a1, w; };
   auto fetch = [&](int step, Stage& q) {
-    const int k0 = kbeg + step * BK;
-    const int ka = k0 + ac;
-    const int abase = ((m0 + ar) * a.lda + ka) * 2;
-    q.a0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(arsc, ka < kend ? abase : OOB, 0, 0));
-    q.a1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(arsc, ka + 8 < kend ? abase + 16 : OOB, 0, 0));
+    const int k = kbeg + step * BK;
+    const int abase = ((m0 + sr) * a.lda + k + sa) * 2;
+    q.a0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(arsc, k + sa < kend ? abase : OOB, 0, 0));
+    q.a1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                         arsc, k + 64 + sa < kend ? abase + 128 : OOB, 0, 0));
     q.w = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                        wrsc, k0 + wc < kend ? (n0 + wr) * a.K + k0 + wc : OOB, 0, 0));
+                                        wrsc, k + sw < kend ? (n0 + sr) * a.K + k + sw : OOB, 0, 0));
   };
   auto stash = [&](const Stage& q, int buf) {
-    *reinterpret_cast<uint4*>(&As[buf][ar][ac]) = q.a0;
-    *reinterpret_cast<uint4*>(&As[buf][ar][ac + 8]) = q.a1;
-    *reinterpret_cast<bf16x8_t*>(&Ws[buf][wr][wc]) = i8x8_to_bf16x8(make_uint2(q.w.x, q.w.y));
-    *reinterpret_cast<bf16x8_t*>(&Ws[buf][wr][wc + 8]) = i8x8_to_bf16x8(make_uint2(q.w.z, q.w.w));
+    *reinterpret_cast<uint4*>(&As[buf][sr][sa]) = q.a0;
+    *reinterpret_cast<uint4*>(&As[buf][sr][64 + sa]) = q.a1;
+    *reinterpret_cast<bf16x8_t*>(&Ws[buf][sr][sw]) = i8x8_to_bf16x8(make_uint2(q.w.x, q.w.y));
+    *reinterpret_cast<bf16x8_t*>(&Ws[buf][sr][sw + 8]) = i8x8_to_bf16x8(make_uint2(q.w.z, q.w.w));
   };
 
   f32x4_t acc[2][2];
@@ -503,13 +506,14 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
       fetch(i + P, q[u]);  // into the slot step i vacated
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
+        const int kk = kh * 64 + 32 * sub + 8 * grp;
         bf16x8_t af[2], bw[2];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
-          af[mt] = *reinterpret_cast<const bf16x8_t*>(&As[buf][wm * 32 + mt * 16 + r16][32 * sub + 8 * grp]);
+          af[mt] = *reinterpret_cast<const bf16x8_t*>(&As[buf][wm * 32 + mt * 16 + r16][kk]);
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
-          bw[nt] = *reinterpret_cast<const bf16x8_t*>(&Ws[buf][wn * 32 + nt * 16 + r16][32 * sub + 8 * grp]);
+          bw[nt] = *reinterpret_cast<const bf16x8_t*>(&Ws[buf][wn * 32 + nt * 16 + r16][kk]);
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -520,18 +524,41 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
       __syncthreads();
     }
   }
-
-  if (S > 1) {
-    // tile partial, thread-major: 16 floats of thread tid at ((tile * S + z) * 256 + tid) * 16
-    const int tile = blockIdx.y * gridDim.x + blockIdx.x;
-    const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
-        a.part + (size_t)tile * S * 4096, 0, S * 4096 * 4, 0x00020000);
+  // the second k half joins the first through LDS (the staging buffers are free now);
+  // waves 0-3 continue with the sum
+  float* red = reinterpret_cast<float*>(&As[0][0][0]);  // [4 waves][16][64] floats
+  if (kh == 1) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, acc[mt][nt]), prs,
-                                               ((z * 256 + tid) * 16 + (mt * 2 + nt) * 4) * 4, 0, 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[((wid - 4) * 16 + (mt * 2 + nt) * 4 + i) * 64 + lane] = acc[mt][nt][i];
+  }
+  __syncthreads();
+  const bool lead = kh == 0;  // waves 4-7 stay for the barriers below but do no more work
+  if (lead) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[mt][nt][i] += red[(wid * 16 + (mt * 2 + nt) * 4 + i) * 64 + lane];
+  }
+
+  if (S > 1) {
+    // tile partial, thread-major: 16 floats of lead thread tid at ((tile * S + z) * 256 + tid) * 16
+    const int tile = blockIdx.y * gridDim.x + blockIdx.x;
+    const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
+        a.part + (size_t)tile * S * 4096, 0, S * 4096 * 4, 0x00020000);
+    if (lead) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, acc[mt][nt]), prs,
+                                                 ((z * 256 + tid) * 16 + (mt * 2 + nt) * 4) * 4, 0, 16);
+    }
     // every store of this work-group has completed before thread 0 counts it in
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -539,7 +566,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
       is_last = __hip_atomic_fetch_add(a.cnt + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
                 (unsigned)(S - 1);
     __syncthreads();
-    if (!is_last) return;
+    if (!is_last || !lead) return;
     f32x4_t tot[2][2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
@@ -573,6 +600,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
       for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = tot[mt][nt];
     if (tid == 0) __hip_atomic_store(a.cnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  if (!lead) return;
 
   // lane holds D[4*(lane/16)+i][lane%16]: token rows, channel columns
 #pragma unroll
@@ -795,6 +823,161 @@ __global__ __launch_bounds__(64 * NWS) void k_skinny(GemvArgs a) {
     __syncthreads();
   }
   if (EPI == EPI_LOGITS) lm_head_store(a, best, 64);
+}
+
+// RMSNorm folded in (batched decode, pre-norm activations, gain set): 8 waves, each holding
+// all of its (at most NB) 128-k blocks in registers.  Every wave adds the squares of the raw
+// activations it loaded per token; the partial sums meet in LDS and are added in wave order
+// (fixed order), giving each token's 1/rms.  Each wave then normalizes its own registers,
+// h = bf16(x * (1/rms) * g) with the gains staged in LDS, and runs the MFMAs as k_skinny does.
+constexpr int SKN_WAVES = 8;
+constexpr int SKN_MAX_K = 4096;  // 8 waves x 4 blocks x 128
+template <int TT, int EPI, int NB>
+__global__ __launch_bounds__(64 * SKN_WAVES) void k_skinny_norm(GemvArgs a) {
+  constexpr int NWS = SKN_WAVES;
+  constexpr int CTW = (EPI == EPI_SILU) ? 2 : 1;
+  constexpr int NACC = CTW * TT;
+  constexpr int NE = (TT * 256 + 64 * NWS - 1) / (64 * NWS);
+  __shared__ float red[NWS][NACC][4][64];
+  __shared__ __align__(16) float gs[SKN_MAX_K];
+  __shared__ float sq[NWS][TT * 16];
+  __shared__ float rinv[TT * 16];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int K = a.K;
+  const int grp = lane >> 4, r16 = lane & 15;
+  const int tile = blockIdx.x;
+
+  const bf16_t* xrow[TT];
+  bool xok[TT];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) {
+    int tok = tt * 16 + r16;
+    xok[tt] = tok < a.nb;
+    tok = tok < a.nb ? tok : a.nb - 1;
+    const int xr = a.x_rows ? a.x_rows[tok] : tok;
+    xrow[tt] = a.x + (size_t)xr * a.ldx;
+  }
+  const int* wrow[CTW];
+  bool wok[CTW];
+#pragma unroll
+  for (int c = 0; c < CTW; ++c) {
+    const int ch = tile * 16 * CTW + c * 16 + r16;
+    wok[c] = ch < a.N;
+    wrow[c] = reinterpret_cast<const int*>(a.W + (size_t)(wok[c] ? ch : 0) * K);
+  }
+  // all of this wave's blocks (wid, wid + 8, ...) in one batch
+  SkinnyOps<TT, CTW> ops[NB];
+#pragma unroll
+  for (int u = 0; u < NB; ++u) {
+    const int kb = wid + NWS * u;
+    skinny_load<TT, CTW>(wrow, wok, xrow, xok, K, kb * 128 < K ? kb * 128 + 32 * grp : K, ops[u]);
+  }
+  // epilogue inputs (residuals as raw bits from a clamped index)
+  float esc[NE][CTW];
+  bf16_t eres[NE];
+#pragma unroll
+  for (int q = 0; q < NE; ++q) {
+    const int e = tid + 64 * NWS * q;
+    const int tt = e / 256, i = (e / 64) % 4, l = e % 64;
+    const int tok = tt * 16 + (l & 15);
+    const int ch = tile * 16 * CTW + 4 * (l >> 4) + i;
+    const bool ok = e < TT * 256 && tok < a.nb;
+#pragma unroll
+    for (int c = 0; c < CTW; ++c) esc[q][c] = (ok && ch + 16 * c < a.N) ? a.scale[ch + 16 * c] : 0.0f;
+    eres[q] = EPI == EPI_RESID ? a.out[(ok && ch < a.N) ? (size_t)tok * a.ldo + ch : 0] : (bf16_t)0;
+  }
+  // the gains, staged once per work-group (the LDS store waits for every load above)
+  for (int k = tid * 4; k < K; k += 64 * NWS * 4)
+    *reinterpret_cast<float4*>(&gs[k]) = *reinterpret_cast<const float4*>(a.gain + k);
+  // squares of this lane's raw activations per token row, then over the four lane groups
+  float ss[TT];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) {
+    ss[tt] = 0.0f;
+#pragma unroll
+    for (int u = 0; u < NB; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint4 v = ops[u].x[tt][q];
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float lo = __uint_as_float(w4[e] << 16), hi = __uint_as_float(w4[e] & 0xFFFF0000u);
+          ss[tt] += lo * lo + hi * hi;
+        }
+      }
+    ss[tt] += __shfl_xor(ss[tt], 16, 64);
+    ss[tt] += __shfl_xor(ss[tt], 32, 64);
+    if (grp == 0) sq[wid][tt * 16 + r16] = ss[tt];
+  }
+  __syncthreads();
+  if (tid < TT * 16) {
+    float t = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NWS; ++w) t += sq[w][tid];
+    rinv[tid] = 1.0f / sqrtf(t / (float)K + a.eps);
+  }
+  __syncthreads();
+  float inv[TT];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) inv[tt] = rinv[tt * 16 + r16];
+
+  f32x4_t acc[CTW][TT];
+#pragma unroll
+  for (int c = 0; c < CTW; ++c)
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) acc[c][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < NB; ++u) {
+    const int kb = (wid + NWS * u) * 128;
+    if (kb >= K) break;  // wave-uniform; no load is issued after this point
+    const int k0 = kb + 32 * grp;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      // k0 + 8q .. +8: gains from LDS; positions past K hold zero activations
+      const int kg = k0 + 8 * q < K ? k0 + 8 * q : 0;
+      const float4 g0 = *reinterpret_cast<const float4*>(&gs[kg]);
+      const float4 g1 = *reinterpret_cast<const float4*>(&gs[kg + 4]);
+      const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) {
+        const uint4 v = ops[u].x[tt][q];
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+        uint32_t o4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float lo = __uint_as_float(w4[e] << 16) * inv[tt] * gv[2 * e];
+          const float hi = __uint_as_float(w4[e] & 0xFFFF0000u) * inv[tt] * gv[2 * e + 1];
+          o4[e] = (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+        }
+        ops[u].x[tt][q] = make_uint4(o4[0], o4[1], o4[2], o4[3]);
+      }
+    }
+    skinny_mfma<TT, CTW>(ops[u], acc);
+  }
+#pragma unroll
+  for (int c = 0; c < CTW; ++c)
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[wid][c * TT + tt][i][lane] = acc[c][tt][i];
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < NE; ++q) {
+    const int e = tid + 64 * NWS * q;
+    if (e >= TT * 4 * 64) break;
+    const int tt = e / 256, i = (e / 64) % 4, l = e % 64;
+    const int tok = tt * 16 + (l & 15);
+    float v[CTW];
+#pragma unroll
+    for (int c = 0; c < CTW; ++c) {
+      v[c] = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NWS; ++w) v[c] += red[w][c * TT + tt][i][l];
+    }
+    const int ch = tile * 16 * CTW + 4 * (l >> 4) + i;
+    skinny_out<EPI, CTW>(a, tile, tok, ch, 4 * (l >> 4) + i, v, esc[q], eres[q]);
+  }
 }
 
 // Split-K form for projections with few channel tiles: work-group blockIdx = tile * S + s
@@ -1829,9 +2012,34 @@ static hipError_t skinny_tt(const GemvArgs& a, int epi, hipStream_t st) {
   return hipGetLastError();
 }
 
-// 2..64 token rows; activations must already be normalized (gain must be NULL)
+template <int TT, int NB>
+static hipError_t skinny_norm_launch(const GemvArgs& a, int epi, hipStream_t st) {
+  const int ctw = epi == EPI_SILU ? 2 : 1;
+  dim3 grid((a.N + 16 * ctw - 1) / (16 * ctw)), blk(64 * SKN_WAVES);
+  if (epi == EPI_STORE) hipLaunchKernelGGL((k_skinny_norm<TT, EPI_STORE, NB>), grid, blk, 0, st, a);
+  else hipLaunchKernelGGL((k_skinny_norm<TT, EPI_SILU, NB>), grid, blk, 0, st, a);
+  return hipGetLastError();
+}
+
+// the shapes whose folded-norm kernel keeps every block in registers without spilling:
+// one 16-token tile with up to 4 blocks per wave, two tiles with up to 2
+bool skinny_norm_ok(int nb, int K, int epi, int ksplit) {
+  if (nb < 2 || nb > 32 || (K & 127) || K <= 0 || ksplit > 1) return false;
+  if (epi != EPI_STORE && epi != EPI_SILU) return false;
+  const int blocks = (K + 128 * SKN_WAVES - 1) / (128 * SKN_WAVES);
+  return nb <= 16 ? blocks <= 4 : blocks <= 2;
+}
+
+// 2..64 token rows.  gain NULL: activations already normalized.  gain set: pre-norm
+// activations, RMSNorm folded in (shapes skinny_norm_ok accepts)
 hipError_t launch_skinny(const GemvArgs& a, int epi, hipStream_t st) {
-  if (a.gain || a.nb < 1 || a.nb > 64 || (a.K & 31)) return hipErrorInvalidValue;
+  if (a.nb < 1 || a.nb > 64 || (a.K & 31)) return hipErrorInvalidValue;
+  if (a.gain) {
+    if (!skinny_norm_ok(a.nb, a.K, epi, a.ksplit)) return hipErrorInvalidValue;
+    const int blocks = (a.K + 128 * SKN_WAVES - 1) / (128 * SKN_WAVES);
+    if (a.nb > 16) return skinny_norm_launch<2, 2>(a, epi, st);
+    return blocks <= 2 ? skinny_norm_launch<1, 2>(a, epi, st) : skinny_norm_launch<1, 4>(a, epi, st);
+  }
   if (a.nb <= 16) return skinny_tt<1>(a, epi, st);
   if (a.nb <= 32) return skinny_tt<2>(a, epi, st);
   return skinny_tt<4>(a, epi, st);
@@ -1852,9 +2060,9 @@ hipError_t launch_gemm(const GemmArgs& a0, hipStream_t st) {
   a.splits = splits;
   dim3 grid((a.N + 63) / 64, (a.M + 63) / 64, splits);
   switch (a.epi) {
-    case EPI_STORE: hipLaunchKernelGGL(k_gemm<EPI_STORE>, grid, dim3(256), 0, st, a); break;
-    case EPI_RESID: hipLaunchKernelGGL(k_gemm<EPI_RESID>, grid, dim3(256), 0, st, a); break;
-    default: hipLaunchKernelGGL(k_gemm<EPI_SILU>, grid, dim3(256), 0, st, a); break;
+    case EPI_STORE: hipLaunchKernelGGL(k_gemm<EPI_STORE>, grid, dim3(512), 0, st, a); break;
+    case EPI_RESID: hipLaunchKernelGGL(k_gemm<EPI_RESID>, grid, dim3(512), 0, st, a); break;
+    default: hipLaunchKernelGGL(k_gemm<EPI_SILU>, grid, dim3(512), 0, st, a); break;
   }
   return hipGetLastError();
 }

@@ -246,6 +246,30 @@ def test_batched_split_k_teacher_forced(B, split):
         m.close()
 
 
+@pytest.mark.parametrize("B,norm", [(20, 1), (20, 0), (12, 1)], ids=["b20-folded", "b20-separate", "b12-folded"])
+def test_batched_folded_norm_teacher_forced(B, norm):
+    """hidden 512: the RMSNorm before q|k|v and gate|up runs inside the batched projection
+    (two 16-token tiles at B=20, one at B=12) or as its own launch; both against the oracle."""
+    w = make_weights(MID, seed=6, gains="uniform")
+    qm = quantize_model(w)
+    prompts = [make_prompt(MID.vocab, 6 + (b % 4), 5000 + b) for b in range(B)]
+    say(f"[gpu] batched folded-norm teacher-forced B={B} skinny_norm={norm}")
+    m = _model(MID, w, max_batch=B, max_ctx=32, max_prefill_tokens=B * 12)
+    try:
+        m.set_tuning(skinny_norm=norm)
+        orcs = [Oracle(MID, qm, mode="bf16").generate(p, 4) for p in prompts]
+        m.prefill(prompts)
+        for k in range(1, 4):
+            feed = torch.tensor([o["ids"][k - 1] for o in orcs], dtype=torch.int32, device="cuda")
+            nxt, lg = m.decode_step(feed, logits=True)
+            torch.cuda.synchronize()
+            for b in range(B):
+                check_step(lg[b].cpu().numpy(), nxt[b].item(), orcs[b]["logits"][k],
+                           orcs[b]["margin"][k], "mid", f"b{b} step {k}")
+    finally:
+        m.close()
+
+
 def test_error_paths_do_no_gpu_work(tiny_setup):
     import int8_weight_only_amd as qd
     shape, w, qm, m = tiny_setup
