@@ -10,11 +10,10 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
-__device__ __forceinline__ bf16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
-}
+// round to nearest even: the hardware conversion (v_cvt_pk_bf16_f32 on gfx950), the same
+// bits as adding 0x7FFF plus the lowest kept bit and truncating, for every finite input
+// (f32 denormals are kept, the default for this code)
+__device__ __forceinline__ bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
 __device__ __forceinline__ float rbf(float f) { return bf2f(f2bf(f)); }
 
 // wave64 reductions on DPP: quad swaps, half-row and row mirrors give every lane its

@@ -78,63 +78,56 @@ __global__ __launch_bounds__(256) void k_embed(const int* __restrict__ ids,
   for (int c = threadIdx.x; c < d; c += 256) x[(size_t)r * d + c] = f2bf((float)er[c] * s);
 }
 
-// RMSNorm of M rows: y = bf16(x / sqrt(mean(x^2) + eps) * g).  Each thread owns chunks of
-// 8 elements (d % 8 == 0); a row of up to 8192 elements is requested in one round trip
-// together with its gains, larger rows loop.
-__global__ __launch_bounds__(256) void k_rmsnorm(const bf16_t* __restrict__ x, int d,
+// RMSNorm of M rows, y = bf16(x / sqrt(mean(x^2) + eps) * g) (d % 8 == 0, d <= 8192): one
+// row per wave (four per work-group), the row and its gains loaded once into registers
+// (CPL 16-byte chunks per lane), a wave reduction, no block barrier.
+template <int CPL>
+__global__ __launch_bounds__(256) void k_rmsnorm(const bf16_t* __restrict__ x, int M, int d,
                                                  const float* __restrict__ g, float eps,
                                                  bf16_t* __restrict__ y) {
-  __shared__ float red[4];
-  constexpr int CPT = 4;
-  const int r = blockIdx.x, tid = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= M) return;  // whole waves; no block barrier follows
   const bf16_t* xr = x + (size_t)r * d;
   bf16_t* yr = y + (size_t)r * d;
   const int nch = d >> 3;
+  uint4 u[CPL];
+  float4 g0[CPL], g1[CPL];
+#pragma unroll
+  for (int q = 0; q < CPL; ++q) {  // clamped (valid) indices: no load in a branch
+    const int c = lane + 64 * q;
+    const int cc = c < nch ? c : 0;
+    u[q] = *reinterpret_cast<const uint4*>(xr + 8 * cc);
+    g0[q] = *reinterpret_cast<const float4*>(g + 8 * cc);
+    g1[q] = *reinterpret_cast<const float4*>(g + 8 * cc + 4);
+  }
   float ss = 0.0f;
-  for (int c0 = 0; c0 < nch; c0 += CPT * 256) {
 #pragma unroll
-    for (int q = 0; q < CPT; ++q) {
-      const int c = c0 + tid + 256 * q;
-      if (c < nch) {
-        const uint4 u = *reinterpret_cast<const uint4*>(xr + 8 * c);
-        const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+  for (int q = 0; q < CPL; ++q) {
+    if (lane + 64 * q < nch) {
+      const uint32_t w4[4] = {u[q].x, u[q].y, u[q].z, u[q].w};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float lo = __uint_as_float(w4[j] << 16), hi = __uint_as_float(w4[j] & 0xFFFF0000u);
-          ss += lo * lo + hi * hi;
-        }
+      for (int j = 0; j < 4; ++j) {
+        const float lo = __uint_as_float(w4[j] << 16), hi = __uint_as_float(w4[j] & 0xFFFF0000u);
+        ss += lo * lo + hi * hi;
       }
     }
   }
-  ss = block_sum256(ss, red);
-  const float denom = sqrtf(ss / (float)d + eps);
-  for (int c0 = 0; c0 < nch; c0 += CPT * 256) {
-    uint4 u[CPT];
-    float4 g0[CPT], g1[CPT];
+  const float denom = sqrtf(wave_sum(ss) / (float)d + eps);
 #pragma unroll
-    for (int q = 0; q < CPT; ++q) {
-      const int c = c0 + tid + 256 * q;
-      if (c < nch) {
-        u[q] = *reinterpret_cast<const uint4*>(xr + 8 * c);
-        g0[q] = *reinterpret_cast<const float4*>(g + 8 * c);
-        g1[q] = *reinterpret_cast<const float4*>(g + 8 * c + 4);
+  for (int q = 0; q < CPL; ++q) {
+    const int c = lane + 64 * q;
+    if (c < nch) {
+      const uint32_t w4[4] = {u[q].x, u[q].y, u[q].z, u[q].w};
+      const float gv[8] = {g0[q].x, g0[q].y, g0[q].z, g0[q].w, g1[q].x, g1[q].y, g1[q].z, g1[q].w};
+      uint32_t o4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16_t y0 = f2bf(__uint_as_float(w4[j] << 16) / denom * gv[2 * j]);
+        const bf16_t y1 = f2bf(__uint_as_float(w4[j] & 0xFFFF0000u) / denom * gv[2 * j + 1]);
+        o4[j] = (uint32_t)y0 | ((uint32_t)y1 << 16);
       }
-    }
-#pragma unroll
-    for (int q = 0; q < CPT; ++q) {
-      const int c = c0 + tid + 256 * q;
-      if (c < nch) {
-        const uint32_t w4[4] = {u[q].x, u[q].y, u[q].z, u[q].w};
-        const float gv[8] = {g0[q].x, g0[q].y, g0[q].z, g0[q].w, g1[q].x, g1[q].y, g1[q].z, g1[q].w};
-        uint32_t o4[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const bf16_t y0 = f2bf(__uint_as_float(w4[j] << 16) / denom * gv[2 * j]);
-          const bf16_t y1 = f2bf(__uint_as_float(w4[j] & 0xFFFF0000u) / denom * gv[2 * j + 1]);
-          o4[j] = (uint32_t)y0 | ((uint32_t)y1 << 16);
-        }
-        *reinterpret_cast<uint4*>(yr + 8 * c) = make_uint4(o4[0], o4[1], o4[2], o4[3]);
-      }
+      *reinterpret_cast<uint4*>(yr + 8 * c) = make_uint4(o4[0], o4[1], o4[2], o4[3]);
     }
   }
 }
@@ -1913,7 +1906,15 @@ hipError_t launch_embed(const int* ids, int M, const int8_t* E, const float* Es,
 
 hipError_t launch_rmsnorm(const bf16_t* x, int M, int d, const float* g, float eps, bf16_t* y,
                           hipStream_t st) {
-  hipLaunchKernelGGL(k_rmsnorm, dim3(M), dim3(256), 0, st, x, d, g, eps, y);
+  if (M <= 0) return hipSuccess;
+  if ((d & 7) || d > 8192) return hipErrorInvalidValue;
+  const int cpl = (d / 8 + 63) / 64;  // 16-byte chunks per lane
+  dim3 grid((M + 3) / 4), blk(256);
+  if (cpl <= 1) hipLaunchKernelGGL(k_rmsnorm<1>, grid, blk, 0, st, x, M, d, g, eps, y);
+  else if (cpl <= 2) hipLaunchKernelGGL(k_rmsnorm<2>, grid, blk, 0, st, x, M, d, g, eps, y);
+  else if (cpl <= 4) hipLaunchKernelGGL(k_rmsnorm<4>, grid, blk, 0, st, x, M, d, g, eps, y);
+  else if (cpl <= 8) hipLaunchKernelGGL(k_rmsnorm<8>, grid, blk, 0, st, x, M, d, g, eps, y);
+  else hipLaunchKernelGGL(k_rmsnorm<16>, grid, blk, 0, st, x, M, d, g, eps, y);
   return hipGetLastError();
 }
 
