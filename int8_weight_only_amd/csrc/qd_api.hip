@@ -289,7 +289,7 @@ void attn_split(int ctx, int cap, int max_splits, int min_chunks, int occupancy,
 // gathered through x_rows when given) and one MFMA sweep of the embedding serves all.
 qd_status enqueue_lm_head(qd_model* m, const bf16_t* x, const int* x_rows, int rows_total, int B,
                           float* logits, int* next_ids, bool bump_pos, bool write_out,
-                          hipStream_t st) {
+                          hipStream_t st, bool normed = false) {
   const Dims& d = m->d;
   GemvArgs a{};
   a.W = m->w<int8_t>(m->P.emb_q);
@@ -312,12 +312,13 @@ qd_status enqueue_lm_head(qd_model* m, const bf16_t* x, const int* x_rows, int r
     a.x = x;
     a.ldx = d.d;
     a.x_rows = x_rows;
-    a.gain = m->w<float>(m->P.final_g);
+    a.gain = normed ? nullptr : m->w<float>(m->P.final_g);
     a.eps = m->shape.rms_eps;
     HIPCHK(launch_gemv(a, EPI_LOGITS, st));
   } else {
     bf16_t* h = m->ws<bf16_t>(m->P.h);
-    HIPCHK(launch_rmsnorm(x, rows_total, d.d, m->w<float>(m->P.final_g), m->shape.rms_eps, h, st));
+    if (normed) h = const_cast<bf16_t*>(x);
+    else HIPCHK(launch_rmsnorm(x, rows_total, d.d, m->w<float>(m->P.final_g), m->shape.rms_eps, h, st));
     a.x = h;
     a.ldx = d.d;
     a.x_rows = x_rows;
@@ -524,9 +525,20 @@ qd_status enqueue_prefill(qd_model* m, int n, const int* ids_dev, const std::vec
   bf16_t* act = m->ws<bf16_t>(P.act);
   float* gpart = m->ws<float>(P.gemm_part);
   HIPCHK(launch_embed(ids_dev, M, m->w<int8_t>(P.emb_q), m->w<float>(P.emb_s), d.d, d.V, x, st));
+  // the input RMSNorm of layer 0; every later one (and the final norm) runs fused with
+  // the split-K merge of the down projection before it
+  HIPCHK(launch_rmsnorm(x, M, d.d, m->w<float>(P.L[0].in_g), m->shape.rms_eps, h, st));
+  // residual projection (O or down) with deferred split-K, then x's RMSNorm with gain ng
+  auto resid_proj = [&](GemmArgs g, const float* ng) -> hipError_t {
+    g.defer = 1;
+    int so = 1;
+    hipError_t e = launch_gemm(g, st, &so);
+    if (e != hipSuccess) return e;
+    if (so > 1) return launch_resid_norm(x, M, d.d, gpart, so, g.scale, ng, m->shape.rms_eps, h, st);
+    return launch_rmsnorm(x, M, d.d, ng, m->shape.rms_eps, h, st);
+  };
   for (int l = 0; l < d.L; ++l) {
     const LayerOff& o = P.L[l];
-    HIPCHK(launch_rmsnorm(x, M, d.d, m->w<float>(o.in_g), m->shape.rms_eps, h, st));
     GemmArgs g{};
     g.A = h; g.lda = d.d; g.W = m->w<int8_t>(o.qkv_q); g.scale = m->w<float>(o.qkv_s);
     g.M = M; g.N = d.NQKV; g.K = d.d; g.epi = EPI_STORE; g.out = qkv; g.ldo = d.NQKV; g.part = gpart; g.cnt = m->ws<unsigned int>(P.sk_cnt); g.splits = m->gemm_splits;
@@ -549,8 +561,7 @@ qd_status enqueue_prefill(qd_model* m, int n, const int* ids_dev, const std::vec
     g = GemmArgs{};
     g.A = attn; g.lda = d.HD; g.W = m->w<int8_t>(o.o_q); g.scale = m->w<float>(o.o_s);
     g.M = M; g.N = d.d; g.K = d.HD; g.epi = EPI_RESID; g.out = x; g.ldo = d.d; g.part = gpart; g.cnt = m->ws<unsigned int>(P.sk_cnt); g.splits = m->gemm_splits;
-    HIPCHK(launch_gemm(g, st));
-    HIPCHK(launch_rmsnorm(x, M, d.d, m->w<float>(o.post_g), m->shape.rms_eps, h, st));
+    HIPCHK(resid_proj(g, m->w<float>(o.post_g)));
     g = GemmArgs{};
     g.A = h; g.lda = d.d; g.W = m->w<int8_t>(o.gu_q); g.scale = m->w<float>(o.gu_s);
     g.M = M; g.N = 2 * d.I; g.K = d.d; g.epi = EPI_SILU; g.out = act; g.ldo = d.I; g.part = gpart; g.cnt = m->ws<unsigned int>(P.sk_cnt); g.splits = m->gemm_splits;
@@ -558,9 +569,10 @@ qd_status enqueue_prefill(qd_model* m, int n, const int* ids_dev, const std::vec
     g = GemmArgs{};
     g.A = act; g.lda = d.I; g.W = m->w<int8_t>(o.dn_q); g.scale = m->w<float>(o.dn_s);
     g.M = M; g.N = d.d; g.K = d.I; g.epi = EPI_RESID; g.out = x; g.ldo = d.d; g.part = gpart; g.cnt = m->ws<unsigned int>(P.sk_cnt); g.splits = m->gemm_splits;
-    HIPCHK(launch_gemm(g, st));
+    HIPCHK(resid_proj(g, l + 1 < d.L ? m->w<float>(P.L[l + 1].in_g) : m->w<float>(P.final_g)));
   }
-  qd_status s = enqueue_lm_head(m, x, last_rows, M, n, logits, next_ids, false, write_out, st);
+  // h holds the final-normalized rows
+  qd_status s = enqueue_lm_head(m, h, last_rows, M, n, logits, next_ids, false, write_out, st, true);
   if (s != QD_OK) return s;
   HIPCHK(launch_set_positions(m->ws<int>(P.pos), dlens, n, st));
   return QD_OK;

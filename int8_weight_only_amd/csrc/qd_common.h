@@ -21,7 +21,11 @@ __host__ __device__ inline int gu_row(int j, int half) {  // logical row j of ga
 
 // ---- launch parameter blocks ------------------------------------------------------------
 
-enum Epilogue { EPI_STORE = 0, EPI_RESID = 1, EPI_SILU = 2, EPI_LOGITS = 3 };
+enum Epilogue { EPI_STORE = 0, EPI_RESID = 1, EPI_SILU = 2, EPI_LOGITS = 3,
+                // prefill GEMM only: each split-K work-group stores its fp32 partial in
+                // [split][M][N]; k_resid_norm adds them into the residual (scaled) and
+                // normalizes the result for the next projection
+                EPI_PART = 4 };
 
 struct GemvArgs {
   const bf16_t* x;      // [nb][ldx] input activations (pre-norm when gain != null)
@@ -62,6 +66,8 @@ struct GemmArgs {
   float* part;                // split-K tile partials [tiles][splits][64 x 64] (fp32)
   unsigned int* cnt;          // split-K arrival counters per tile, zero on entry
   int splits;                 // in: most split-K ways (0: launcher's default); set by the launcher
+  int defer;                  // EPI_RESID with split-K: store partials (EPI_PART) instead of
+                              // merging them in-kernel; the caller runs k_resid_norm next
 };
 constexpr size_t GEMM_PART_FLOATS = (size_t)8 << 20;  // 32 MiB of split-K partials
 
@@ -203,7 +209,14 @@ hipError_t launch_gemv(const GemvArgs& a, int epi, hipStream_t st);
 hipError_t launch_skinny(const GemvArgs& a, int epi, hipStream_t st);
 // whether launch_skinny can fold the RMSNorm (gain set) for nb rows of a K-long input
 bool skinny_norm_ok(int nb, int K, int epi, int ksplit);
-hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
+// *splits_used (nullable) receives the split-K ways; with a.defer and more than one
+// split, the residual is not yet updated: launch_resid_norm with that count must follow
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t st, int* splits_used = nullptr);
+// x[m] = bf16(x[m] + bf16(scale * sum_s part[s][m])) in split order, then
+// y[m] = RMSNorm(x[m]) * g; splits in {2, 4, 8}
+hipError_t launch_resid_norm(bf16_t* x, int M, int d, const float* part, int splits,
+                             const float* scale, const float* g, float eps, bf16_t* y,
+                             hipStream_t st);
 hipError_t launch_qk_rope(const RopeArgs& a, hipStream_t st);
 hipError_t launch_attention_decode(const AttnDecArgs& a, hipStream_t st);
 hipError_t launch_flash_prefill(const FlashArgs& a, int n_tiles, hipStream_t st);

@@ -113,7 +113,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const bf16_t* __restrict__ x, i
       }
     }
   }
-  const float denom = sqrtf(wave_sum(ss) / (float)d + eps);
+  const float rinv = 1.0f / sqrtf(wave_sum(ss) / (float)d + eps);
 #pragma unroll
   for (int q = 0; q < CPL; ++q) {
     const int c = lane + 64 * q;
@@ -123,10 +123,91 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const bf16_t* __restrict__ x, i
       uint32_t o4[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const bf16_t y0 = f2bf(__uint_as_float(w4[j] << 16) / denom * gv[2 * j]);
-        const bf16_t y1 = f2bf(__uint_as_float(w4[j] & 0xFFFF0000u) / denom * gv[2 * j + 1]);
+        const bf16_t y0 = f2bf(__uint_as_float(w4[j] << 16) * rinv * gv[2 * j]);
+        const bf16_t y1 = f2bf(__uint_as_float(w4[j] & 0xFFFF0000u) * rinv * gv[2 * j + 1]);
         o4[j] = (uint32_t)y0 | ((uint32_t)y1 << 16);
       }
+      *reinterpret_cast<uint4*>(yr + 8 * c) = make_uint4(o4[0], o4[1], o4[2], o4[3]);
+    }
+  }
+}
+
+// split-K merge of a prefill projection into the residual stream, then the RMSNorm of the
+// updated row (one row per wave): x = bf16(x + bf16(scale * (p_0 + p_1 + ... + p_{S-1})))
+// with the partials added in split order, y = bf16(x / sqrt(mean(x^2) + eps) * g).  Every
+// input of the row (residual, partials, scales, gains) is requested before the first use.
+template <int CPL, int S>
+__global__ __launch_bounds__(256) void k_resid_norm(bf16_t* __restrict__ x, int M, int d,
+                                                    const float* __restrict__ part,
+                                                    const float* __restrict__ scale,
+                                                    const float* __restrict__ g, float eps,
+                                                    bf16_t* __restrict__ y) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= M) return;  // whole waves; no block barrier follows
+  bf16_t* xr = x + (size_t)r * d;
+  bf16_t* yr = y + (size_t)r * d;
+  const int nch = d >> 3;
+  uint4 u[CPL];
+  float4 p[S][CPL][2], sc[CPL][2];
+#pragma unroll
+  for (int q = 0; q < CPL; ++q) {  // clamped (valid) indices: no load in a branch
+    const int c = lane + 64 * q;
+    const int cc = c < nch ? c : 0;
+    u[q] = *reinterpret_cast<const uint4*>(xr + 8 * cc);
+#pragma unroll
+    for (int sp = 0; sp < S; ++sp) {
+      const float* ps = part + ((size_t)sp * M + r) * d + 8 * cc;
+      p[sp][q][0] = *reinterpret_cast<const float4*>(ps);
+      p[sp][q][1] = *reinterpret_cast<const float4*>(ps + 4);
+    }
+    sc[q][0] = *reinterpret_cast<const float4*>(scale + 8 * cc);
+    sc[q][1] = *reinterpret_cast<const float4*>(scale + 8 * cc + 4);
+  }
+  float4 g0[CPL], g1[CPL];
+#pragma unroll
+  for (int q = 0; q < CPL; ++q) {
+    const int c = lane + 64 * q;
+    const int cc = c < nch ? c : 0;
+    g0[q] = *reinterpret_cast<const float4*>(g + 8 * cc);
+    g1[q] = *reinterpret_cast<const float4*>(g + 8 * cc + 4);
+  }
+  float xv[CPL][8];
+  float ss = 0.0f;
+#pragma unroll
+  for (int q = 0; q < CPL; ++q) {
+    const uint32_t w4[4] = {u[q].x, u[q].y, u[q].z, u[q].w};
+    const float s8[8] = {sc[q][0].x, sc[q][0].y, sc[q][0].z, sc[q][0].w,
+                         sc[q][1].x, sc[q][1].y, sc[q][1].z, sc[q][1].w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float v = 0.0f;
+#pragma unroll
+      for (int sp = 0; sp < S; ++sp) {
+        const float4& pp = p[sp][q][e >> 2];
+        const float pe = (e & 3) == 0 ? pp.x : (e & 3) == 1 ? pp.y : (e & 3) == 2 ? pp.z : pp.w;
+        v = sp == 0 ? pe : v + pe;
+      }
+      const float xo = (e & 1) ? __uint_as_float(w4[e >> 1] & 0xFFFF0000u) : __uint_as_float(w4[e >> 1] << 16);
+      xv[q][e] = rbf(xo + rbf(v * s8[e]));
+      ss += lane + 64 * q < nch ? xv[q][e] * xv[q][e] : 0.0f;
+    }
+  }
+  const float rinv = 1.0f / sqrtf(wave_sum(ss) / (float)d + eps);
+#pragma unroll
+  for (int q = 0; q < CPL; ++q) {
+    const int c = lane + 64 * q;
+    if (c < nch) {
+      const float gv[8] = {g0[q].x, g0[q].y, g0[q].z, g0[q].w, g1[q].x, g1[q].y, g1[q].z, g1[q].w};
+      uint32_t o4[4], x4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x4[j] = (uint32_t)f2bf(xv[q][2 * j]) | ((uint32_t)f2bf(xv[q][2 * j + 1]) << 16);
+        const bf16_t y0 = f2bf(xv[q][2 * j] * rinv * gv[2 * j]);
+        const bf16_t y1 = f2bf(xv[q][2 * j + 1] * rinv * gv[2 * j + 1]);
+        o4[j] = (uint32_t)y0 | ((uint32_t)y1 << 16);
+      }
+      *reinterpret_cast<uint4*>(xr + 8 * c) = make_uint4(x4[0], x4[1], x4[2], x4[3]);
       *reinterpret_cast<uint4*>(yr + 8 * c) = make_uint4(o4[0], o4[1], o4[2], o4[3]);
     }
   }
@@ -274,7 +355,7 @@ __global__ __launch_bounds__(256) void k_gemv1(GemvArgs a) {
     }
   }
   if (a.gain) {
-    const float denom = sqrtf(wave_sum(ss) / (float)K + a.eps);
+    const float rinv = 1.0f / sqrtf(wave_sum(ss) / (float)K + a.eps);
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
       const int ch = lane + 64 * c;
@@ -282,10 +363,10 @@ __global__ __launch_bounds__(256) void k_gemv1(GemvArgs a) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const float4 g = gq[c][q];
-          xf[c][4 * q + 0] = rbf(xf[c][4 * q + 0] / denom * g.x);
-          xf[c][4 * q + 1] = rbf(xf[c][4 * q + 1] / denom * g.y);
-          xf[c][4 * q + 2] = rbf(xf[c][4 * q + 2] / denom * g.z);
-          xf[c][4 * q + 3] = rbf(xf[c][4 * q + 3] / denom * g.w);
+          xf[c][4 * q + 0] = rbf(xf[c][4 * q + 0] * rinv * g.x);
+          xf[c][4 * q + 1] = rbf(xf[c][4 * q + 1] * rinv * g.y);
+          xf[c][4 * q + 2] = rbf(xf[c][4 * q + 2] * rinv * g.z);
+          xf[c][4 * q + 3] = rbf(xf[c][4 * q + 3] * rinv * g.w);
         }
       }
     }
@@ -486,6 +567,24 @@ __global__ __launch_bounds__(512) void k_gemm(GemmArgs a) {
   Stage q[P];
 #pragma unroll
   for (int u = 0; u < P; ++u) fetch(u, q[u]);
+  // residual inputs of this lane's 16 outputs, requested behind the first steps' loads as
+  // raw bits from in-range offsets (out-of-range reads zero), so no wait lands in a branch
+  uint32_t res[2][4][2];
+  if constexpr (EPI == EPI_RESID) {
+    const __amdgpu_buffer_rsrc_t orsc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)a.out, 0, a.M * a.ldo * 2, 0x00020000);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          const int m = m0 + wm * 32 + mt * 16 + 4 * grp + i;
+          const int n = n0 + wn * 32 + nt * 16 + r16;
+          res[mt][i][nt] = __builtin_amdgcn_raw_buffer_load_b16(
+              orsc, (m < a.M && n < a.N) ? (m * a.ldo + n) * 2 : OOB, 0, 0);
+        }
+  }
   stash(q[0], 0);
   __syncthreads();
   // whole groups of P steps (steps past the end multiply zeros): an early exit from the
@@ -539,6 +638,24 @@ __global__ __launch_bounds__(512) void k_gemm(GemmArgs a) {
         for (int i = 0; i < 4; ++i) acc[mt][nt][i] += red[(wid * 16 + (mt * 2 + nt) * 4 + i) * 64 + lane];
   }
 
+  if constexpr (EPI == EPI_PART) {
+    // this split's fp32 partial of the lane's 16 outputs, [z][M][N]; merged downstream
+    if (!lead) return;
+    float* pz = a.part + (size_t)z * a.M * a.N;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + wm * 32 + mt * 16 + 4 * grp + i;
+        if (m >= a.M) continue;
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          const int n = n0 + wn * 32 + nt * 16 + r16;
+          if (n < a.N) pz[(size_t)m * a.N + n] = acc[mt][nt][i];
+        }
+      }
+    return;
+  }
   if (S > 1) {
     // tile partial, thread-major: 16 floats of lead thread tid at ((tile * S + z) * 256 + tid) * 16
     const int tile = blockIdx.y * gridDim.x + blockIdx.x;
@@ -610,7 +727,10 @@ __global__ __launch_bounds__(512) void k_gemm(GemmArgs a) {
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
           const int n = n0 + wn * 32 + nt * 16 + r16;
-          if (n < a.N) gemm_epilogue<EPI>(a, m, n, acc[mt][nt][i], 0.0f, gsc[nt], 0.0f);
+          if (n >= a.N) continue;
+          const float y = acc[mt][nt][i] * gsc[nt];
+          a.out[(size_t)m * a.ldo + n] =
+              EPI == EPI_RESID ? f2bf(bf2f((bf16_t)res[mt][i][nt]) + rbf(y)) : f2bf(y);
         }
       }
     }
@@ -1267,7 +1387,7 @@ __global__ __launch_bounds__(256) void k_qk_rope(RopeArgs a) {
     ss += x1[j] * x1[j] + x2[j] * x2[j];
   }
   ss = wave_sum(ss);
-  const float denom = sqrtf(ss / (float)D + a.eps);
+  const float rinv = 1.0f / sqrtf(ss / (float)D + a.eps);
   bf16_t* dst = src;
   if (!isq) {
     const int g = hh - a.H;
@@ -1277,8 +1397,8 @@ __global__ __launch_bounds__(256) void k_qk_rope(RopeArgs a) {
   for (int j = 0; j < 2; ++j) {
     const int i = lane + 64 * j;
     if (i < half) {
-      const float y1 = rbf(x1[j] / denom * g1[j]);
-      const float y2 = rbf(x2[j] / denom * g2[j]);
+      const float y1 = rbf(x1[j] * rinv * g1[j]);
+      const float y2 = rbf(x2[j] * rinv * g2[j]);
       dst[i] = f2bf(y1 * cs[j].x - y2 * cs[j].y);
       dst[i + half] = f2bf(y2 * cs[j].x + y1 * cs[j].y);
     }
@@ -1918,6 +2038,32 @@ hipError_t launch_rmsnorm(const bf16_t* x, int M, int d, const float* g, float e
   return hipGetLastError();
 }
 
+template <int S>
+static hipError_t resid_norm_s(bf16_t* x, int M, int d, const float* part, const float* scale,
+                               const float* g, float eps, bf16_t* y, hipStream_t st) {
+  const int cpl = (d / 8 + 63) / 64;  // 16-byte chunks per lane
+  dim3 grid((M + 3) / 4), blk(256);
+  if (cpl <= 1) hipLaunchKernelGGL((k_resid_norm<1, S>), grid, blk, 0, st, x, M, d, part, scale, g, eps, y);
+  else if (cpl <= 2) hipLaunchKernelGGL((k_resid_norm<2, S>), grid, blk, 0, st, x, M, d, part, scale, g, eps, y);
+  else if (cpl <= 4) hipLaunchKernelGGL((k_resid_norm<4, S>), grid, blk, 0, st, x, M, d, part, scale, g, eps, y);
+  else if (cpl <= 8) hipLaunchKernelGGL((k_resid_norm<8, S>), grid, blk, 0, st, x, M, d, part, scale, g, eps, y);
+  else hipLaunchKernelGGL((k_resid_norm<16, S>), grid, blk, 0, st, x, M, d, part, scale, g, eps, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_resid_norm(bf16_t* x, int M, int d, const float* part, int splits,
+                             const float* scale, const float* g, float eps, bf16_t* y,
+                             hipStream_t st) {
+  if (M <= 0) return hipSuccess;
+  if ((d & 7) || d > 8192) return hipErrorInvalidValue;
+  switch (splits) {
+    case 2: return resid_norm_s<2>(x, M, d, part, scale, g, eps, y, st);
+    case 4: return resid_norm_s<4>(x, M, d, part, scale, g, eps, y, st);
+    case 8: return resid_norm_s<8>(x, M, d, part, scale, g, eps, y, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <int R, int KC>
 static hipError_t gemv1_rk(const GemvArgs& a, int epi, hipStream_t st) {
   const int nout = epi == EPI_SILU ? a.N / 2 : a.N;
@@ -2046,9 +2192,10 @@ hipError_t launch_skinny(const GemvArgs& a, int epi, hipStream_t st) {
   return skinny_tt<4>(a, epi, st);
 }
 
-hipError_t launch_gemm(const GemmArgs& a0, hipStream_t st) {
+hipError_t launch_gemm(const GemmArgs& a0, hipStream_t st, int* splits_used) {
   GemmArgs a = a0;
-  if ((a.K & 31) || (size_t)(a.M + 64) * a.lda * 2 > 0x7FFFFFFFu || (size_t)(a.N + 64) * a.K > 0x7FFFFFFFu)
+  if ((a.K & 31) || (size_t)(a.M + 64) * a.lda * 2 > 0x7FFFFFFFu || (size_t)(a.N + 64) * a.K > 0x7FFFFFFFu ||
+      (size_t)(a.M + 64) * a.ldo * 2 > 0x7FFFFFFFu)
     return hipErrorInvalidValue;
   const int tiles = ((a.N + 63) / 64) * ((a.M + 63) / 64);
   // split K when the tile grid leaves most of the 256 CUs idle
@@ -2059,7 +2206,13 @@ hipError_t launch_gemm(const GemmArgs& a0, hipStream_t st) {
          tiles <= SKINNY_MAX_TILES)
     splits *= 2;
   a.splits = splits;
+  if (splits_used) *splits_used = splits;
   dim3 grid((a.N + 63) / 64, (a.M + 63) / 64, splits);
+  if (a.defer && a.epi == EPI_RESID && splits > 1) {
+    if ((size_t)splits * a.M * a.N > GEMM_PART_FLOATS) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_gemm<EPI_PART>, grid, dim3(512), 0, st, a);
+    return hipGetLastError();
+  }
   switch (a.epi) {
     case EPI_STORE: hipLaunchKernelGGL(k_gemm<EPI_STORE>, grid, dim3(512), 0, st, a); break;
     case EPI_RESID: hipLaunchKernelGGL(k_gemm<EPI_RESID>, grid, dim3(512), 0, st, a); break;

@@ -373,7 +373,7 @@ __device__ __forceinline__ void stage_norm(const bf16_t* g, const int8_t* erow, 
       }
     }
   }
-  const float denom = sqrtf(stage_sum(ss, red, tid) / (float)K + eps);
+  const float rinv = 1.0f / sqrtf(stage_sum(ss, red, tid) / (float)K + eps);
   if (act) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -384,8 +384,8 @@ __device__ __forceinline__ void stage_norm(const bf16_t* g, const int8_t* erow, 
         uint32_t o4[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const bf16_t y0 = f2bf(bf_lo(w4[j]) / denom * gv[2 * j]);
-          const bf16_t y1 = f2bf(bf_hi(w4[j]) / denom * gv[2 * j + 1]);
+          const bf16_t y0 = f2bf(bf_lo(w4[j]) * rinv * gv[2 * j]);
+          const bf16_t y1 = f2bf(bf_hi(w4[j]) * rinv * gv[2 * j + 1]);
           o4[j] = (uint32_t)y0 | ((uint32_t)y1 << 16);
         }
         *reinterpret_cast<uint4*>(xs + 8 * c) = make_uint4(o4[0], o4[1], o4[2], o4[3]);
