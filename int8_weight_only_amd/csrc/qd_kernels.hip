@@ -531,24 +531,26 @@ __global__ __launch_bounds__(512) void k_gemm(GemmArgs a) {
       __builtin_amdgcn_make_buffer_rsrc((void*)a.A, 0, a.M * a.lda * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t wrsc =
       __builtin_amdgcn_make_buffer_rsrc((void*)a.W, 0, a.N * a.K, 0x00020000);
-  // staging: A row tid/8, pieces at k 8*(tid%8) and 64 + 8*(tid%8) (each load instruction
-  // reads 128 contiguous bytes per row); W row tid/8, one 16-byte piece at k 16*(tid%8)
-  const int sr = tid >> 3, sa = (tid & 7) * 8, sw = (tid & 7) * 16;
+  // staging: thread j = tid%8 of row tid/8 brings k 16j .. 16j+15 of the step for both A
+  // and W.  Within a step, k = 16j + e sits in LDS column 8j + e (e < 8) or 64 + 8j + e - 8
+  // (e >= 8), the same permutation for both operands, so the dot products are unchanged
+  // and each 8-lane group writes 128 contiguous bytes of a row (no bank conflicts).
+  const int sr = tid >> 3, sj = tid & 7, sa = sj * 8, sw = sj * 16;
   struct Stage { uint4 a0, a1, w; };
   auto fetch = [&](int step, Stage& q) {
     const int k = kbeg + step * BK;
-    const int abase = ((m0 + sr) * a.lda + k + sa) * 2;
-    q.a0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(arsc, k + sa < kend ? abase : OOB, 0, 0));
+    const int abase = ((m0 + sr) * a.lda + k + sw) * 2;
+    q.a0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(arsc, k + sw < kend ? abase : OOB, 0, 0));
     q.a1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                         arsc, k + 64 + sa < kend ? abase + 128 : OOB, 0, 0));
+                                         arsc, k + sw + 8 < kend ? abase + 16 : OOB, 0, 0));
     q.w = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                         wrsc, k + sw < kend ? (n0 + sr) * a.K + k + sw : OOB, 0, 0));
   };
   auto stash = [&](const Stage& q, int buf) {
     *reinterpret_cast<uint4*>(&As[buf][sr][sa]) = q.a0;
     *reinterpret_cast<uint4*>(&As[buf][sr][64 + sa]) = q.a1;
-    *reinterpret_cast<bf16x8_t*>(&Ws[buf][sr][sw]) = i8x8_to_bf16x8(make_uint2(q.w.x, q.w.y));
-    *reinterpret_cast<bf16x8_t*>(&Ws[buf][sr][sw + 8]) = i8x8_to_bf16x8(make_uint2(q.w.z, q.w.w));
+    *reinterpret_cast<bf16x8_t*>(&Ws[buf][sr][sa]) = i8x8_to_bf16x8(make_uint2(q.w.x, q.w.y));
+    *reinterpret_cast<bf16x8_t*>(&Ws[buf][sr][64 + sa]) = i8x8_to_bf16x8(make_uint2(q.w.z, q.w.w));
   };
 
   f32x4_t acc[2][2];
@@ -1870,36 +1872,45 @@ __global__ __launch_bounds__(256) void k_flash_prefill(FlashArgs a) {
   }
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) o[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const float scale = 1.0f / sqrtf((float)D);
+  // scores in base 2: exp(z - m) = exp2(z*log2(e) - m*log2(e)), one hardware exp each
+  const float scale2 = 1.4426950408889634f / sqrtf((float)D);
 
-  // global -> register staging of one K/V block.  K: consecutive lanes take consecutive
-  // 16-byte pieces of a key row.  V: consecutive lanes take consecutive keys (same piece),
-  // so the transposed LDS stores of a quarter-wave hit consecutive addresses instead of
-  // rows 8 apart (which all map to one bank).
-  uint4 kst[LD_PER_T], vst[LD_PER_T];
-  auto fetch = [&](int kb) {
+  // global -> register staging of one K/V block, two blocks in flight.  K: consecutive
+  // lanes take consecutive 16-byte pieces of a key row.  V: consecutive lanes take
+  // consecutive keys (same piece), so the transposed LDS stores of a quarter-wave hit
+  // consecutive addresses instead of rows 8 apart (which all map to one bank).  Buffer
+  // loads: keys past the tile's last visible one read zero through an out-of-range
+  // offset, so no load sits in a branch and each block waits only for its own data.
+  constexpr int OOB = (int)0x80000000;
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)Kb, 0, a.max_ctx * D * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)Vb, 0, a.max_ctx * D * 2, 0x00020000);
+  uint4 kst[2][LD_PER_T], vst[2][LD_PER_T];
+  auto fetch = [&](int kb, uint4 (&ks)[LD_PER_T], uint4 (&vs)[LD_PER_T]) {
 #pragma unroll
     for (int u = 0; u < LD_PER_T; ++u) {
       const int idx = tid + 256 * u;
       const int key = idx / VPR, c = idx % VPR;
       const int vkey = idx % KB, vc = idx / KB;
       const bool in = idx < KB * VPR;
-      kst[u] = (in && kb + key < kmax) ? *reinterpret_cast<const uint4*>(Kb + (size_t)(kb + key) * D + 8 * c)
-                                       : make_uint4(0, 0, 0, 0);
-      vst[u] = (in && kb + vkey < kmax) ? *reinterpret_cast<const uint4*>(Vb + (size_t)(kb + vkey) * D + 8 * vc)
-                                        : make_uint4(0, 0, 0, 0);
+      ks[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            krs, (in && kb + key < kmax) ? ((kb + key) * D + 8 * c) * 2 : OOB, 0, 0));
+      vs[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            vrs, (in && kb + vkey < kmax) ? ((kb + vkey) * D + 8 * vc) * 2 : OOB, 0, 0));
     }
   };
-  fetch(0);
-  for (int kb = 0; kb < kmax; kb += KB) {
+  // one key block: stage it in LDS, refill its registers with the block two ahead, then
+  // S = Q K^T, online softmax, O += P V
+  auto block = [&](int kb, uint4 (&ks)[LD_PER_T], uint4 (&vs)[LD_PER_T]) {
 #pragma unroll
     for (int u = 0; u < LD_PER_T; ++u) {
       const int idx = tid + 256 * u;
       if (idx < KB * VPR) {
         const int key = idx / VPR, c = idx % VPR;
-        *reinterpret_cast<uint4*>(&Ks[key][8 * c]) = kst[u];
+        *reinterpret_cast<uint4*>(&Ks[key][8 * c]) = ks[u];
         const int vkey = idx % KB, vc = idx / KB;
-        const uint32_t w4[4] = {vst[u].x, vst[u].y, vst[u].z, vst[u].w};
+        const uint32_t w4[4] = {vs[u].x, vs[u].y, vs[u].z, vs[u].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           Vt[8 * vc + 2 * e][vkey] = (bf16_t)(w4[e] & 0xFFFFu);
@@ -1908,7 +1919,7 @@ __global__ __launch_bounds__(256) void k_flash_prefill(FlashArgs a) {
       }
     }
     __syncthreads();
-    if (kb + KB < kmax) fetch(kb + KB);
+    fetch(kb + 2 * KB, ks, vs);  // past kmax: reads zero, never used
 
     // S = Q K^T for 16 rows x KB keys (NKT 16-key tiles)
     f32x4_t sacc[NKT];
@@ -1916,10 +1927,10 @@ __global__ __launch_bounds__(256) void k_flash_prefill(FlashArgs a) {
     for (int n = 0; n < NKT; ++n) {
       sacc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
+      for (int ks2 = 0; ks2 < KS; ++ks2) {
         const bf16x8_t kf = __builtin_bit_cast(
-            bf16x8_t, *reinterpret_cast<const uint4*>(&Ks[16 * n + r16][32 * ks + 8 * grp]));
-        sacc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ks], kf, sacc[n], 0, 0, 0);
+            bf16x8_t, *reinterpret_cast<const uint4*>(&Ks[16 * n + r16][32 * ks2 + 8 * grp]));
+        sacc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ks2], kf, sacc[n], 0, 0, 0);
       }
     }
     // causal mask + online softmax; lane holds rows 4*grp+i, keys 16n + r16
@@ -1932,15 +1943,15 @@ __global__ __launch_bounds__(256) void k_flash_prefill(FlashArgs a) {
 #pragma unroll
       for (int n = 0; n < NKT; ++n) {
         const int key = kb + 16 * n + r16;
-        sv[n] = (r < nrows && key <= qpos) ? sacc[n][i] * scale : -INFINITY;
+        sv[n] = (r < nrows && key <= qpos) ? sacc[n][i] * scale2 : -INFINITY;
         smax = fmaxf(smax, sv[n]);
       }
       const float mnew = fmaxf(m[i], row16_max(smax));
-      const float alpha = (m[i] == -INFINITY) ? 0.0f : expf(m[i] - mnew);
+      const float alpha = (m[i] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m[i] - mnew);
       float pr[NKT], psum = 0.0f;
 #pragma unroll
       for (int n = 0; n < NKT; ++n) {
-        pr[n] = (sv[n] == -INFINITY) ? 0.0f : expf(sv[n] - mnew);
+        pr[n] = (sv[n] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sv[n] - mnew);
         psum += pr[n];
       }
       l[i] = l[i] * alpha + row16_sum(psum);
@@ -1972,6 +1983,14 @@ __global__ __launch_bounds__(256) void k_flash_prefill(FlashArgs a) {
       }
     }
     __syncthreads();
+  };
+  fetch(0, kst[0], vst[0]);
+  fetch(KB, kst[1], vst[1]);
+  // blocks in pairs so each register set has a fixed name; a tile's last odd block is the
+  // only branch, and the loop ends after it
+  for (int kb = 0; kb < kmax; kb += 2 * KB) {
+    block(kb, kst[0], vst[0]);
+    if (kb + KB < kmax) block(kb + KB, kst[1], vst[1]);
   }
   // out[r][h*D + d] for rows 4*grp + i, dims 16*nt + r16
 #pragma unroll
