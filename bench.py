@@ -187,6 +187,46 @@ def time_generate(model, prompts, new, steps, warmup):
     return float(np.mean(dev)), float(np.mean(pre)), float(np.mean(dec)), wall / steps, res
 
 
+def time_continuous(model, shape, S, NP, NN):
+    """Continuous batching ("LLM inference overview", section "Results"): S KV slots hold
+    sequences of ragged lengths; every step lists all slots in a fresh random order
+    (qd_decode_step_slots), and every 16 steps one sequence leaves and a new prompt is
+    prefilled into its slot (qd_prefill_slots).  Device time of the whole schedule."""
+    import torch
+    from workloads import make_prompt
+    rng = np.random.default_rng(7)
+    lens = [NP // 2 + (NP // 2 - 4) * b // max(1, S - 1) for b in range(S)]
+    steps = min(64, NN // 2)
+    prompts = [make_prompt(shape.vocab, n, 3000 + b) for b, n in enumerate(lens)]
+    order = rng.permutation(S)
+    nxt, _ = model.prefill([prompts[i] for i in order], slots=order)
+    ids = torch.empty(S, dtype=torch.int32, device="cuda")
+    ids[torch.as_tensor(order, device="cuda").long()] = nxt  # ids indexed by slot
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    joins, dec_tok = 0, 0
+    ev0.record()
+    for k in range(steps):
+        if k and k % 16 == 0:  # slot k % S leaves; a new prompt takes it
+            sl = k % S
+            jn, _ = model.prefill([make_prompt(shape.vocab, NP // 2, 3500 + k)], slots=[sl])
+            ids[sl] = jn[0]
+            joins += 1
+        perm = rng.permutation(S)
+        pidx = torch.as_tensor(perm, device="cuda").long()
+        out, _ = model.decode_step(ids[pidx], slots=perm)
+        ids[pidx] = out
+        dec_tok += S
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1)
+    log(f"[bench] continuous S={S}: {dec_tok} decode tokens + {joins} joins in {ms:.2f} ms")
+    return {f"continuous_s{S}_tok_s": round(dec_tok / (ms * 1e-3), 1),
+            f"continuous_s{S}_schedule": f"{S} slots, prompts {lens[0]}..{lens[-1]} tokens, "
+                                         f"{steps} steps, rows shuffled every step, "
+                                         f"{joins} joins of {NP // 2}-token prompts"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -200,6 +240,7 @@ def main():
                     help="batched decode lines measured after the main one ('' for none)")
     ap.add_argument("--no-extra", action="store_true", help="same as --extra-batches ''")
     ap.add_argument("--no-oracle", action="store_true", help="skip parity gate and CPU baseline")
+    ap.add_argument("--no-continuous", action="store_true", help="skip the continuous-batching line")
     ap.add_argument("--kernels-only", action="store_true",
                     help="no captured graphs and few dispatches: prefill prompt+new-2 tokens, "
                          "one decode step, then the per-kernel timing pass (for counter runs)")
@@ -312,6 +353,9 @@ def main():
             a, b = xr.generated[0], res.generated[0]
             extra[f"b{xb}_seq0_prefix_equal_b1"] = int(np.argmin(np.append(a == b, False)))
         log(f"[bench] B={xb}: decode {dtok:.1f} tok/s, prefill {xb * NP / (xpre * 1e-6):.0f} tok/s")
+
+    if extras and max(extras) >= 8 and not args.no_continuous:
+        extra.update(time_continuous(model, shape, max(extras), NP, NN))
 
     pf = prefill_flops(shape, NP)
     line = {

@@ -193,6 +193,32 @@ qd_status qd_prefill(qd_model* m, int32_t n_seqs, const int32_t* ids_dev,
 qd_status qd_decode_step(qd_model* m, int32_t B, const int32_t* in_ids_dev,
                          float* logits_dev, int32_t* next_ids_dev, qd_stream stream);
 
+/* Continuous batching ("LLM inference overview", section "Results": batched decode
+ * serves many independent sequences with the weights swept once per step, and sequences
+ * join and leave the running batch).  The two calls below address KV slots explicitly,
+ * so a new prompt can be prefilled into a free slot while other slots are mid-decode.
+ *
+ * qd_prefill_slots: as qd_prefill, but prompt b goes to KV slot slots_host[b] (host,
+ * n_seqs distinct values in [0, max_batch)); that slot's length is reset to lens_host[b]
+ * and its earlier contents are overwritten.  Other slots are untouched.
+ * Errors: QD_ERR_INVALID_ARGUMENTS (NULL slots_host, a slot out of range or listed
+ * twice, plus every check of qd_prefill), before any GPU work. */
+qd_status qd_prefill_slots(qd_model* m, int32_t n_seqs, const int32_t* slots_host,
+                           const int32_t* ids_dev, const int32_t* ids_host,
+                           const int32_t* lens_host, float* logits_dev, int32_t* next_ids_dev,
+                           qd_stream stream);
+
+/* qd_decode_step_slots: one decode step for the B slots slots_host[0..B-1] (host,
+ * distinct, each holding a prompt), in any order and at their own lengths: row b of
+ * in_ids_dev[B], next_ids_dev[B] and logits_dev[B, V] (nullable) belongs to slot
+ * slots_host[b].  Appends K/V at each slot's length p and increments it.  The slot
+ * list is staged through pinned host memory on `stream`; no host synchronization.
+ * Errors: QD_ERR_INVALID_ARGUMENTS (NULL slots_host, a slot out of range, listed twice,
+ * empty or full), before any GPU work. */
+qd_status qd_decode_step_slots(qd_model* m, int32_t B, const int32_t* slots_host,
+                               const int32_t* in_ids_dev, float* logits_dev,
+                               int32_t* next_ids_dev, qd_stream stream);
+
 /* One call, start to finish ("Model-agnostic LLM inference", section "Notes"):
  * prefill of B prompts (host ids, concatenated; lens_host[B]) then
  * max_new_tokens - 1 decode steps, greedy ids kept on the device between steps:

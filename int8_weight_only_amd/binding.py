@@ -88,7 +88,8 @@ class StatsC(ctypes.Structure):
 
 EXPORTS = ("qd_last_error", "qd_check_shape", "qd_query_sizes", "qd_load_weights",
            "qd_export_quantized", "qd_prefill", "qd_decode_step", "qd_generate_greedy",
-           "qd_free", "qd_profile_kernels", "qd_set_tuning")
+           "qd_free", "qd_profile_kernels", "qd_set_tuning", "qd_prefill_slots",
+           "qd_decode_step_slots")
 TUNING = {"attn_max_splits": 0, "attn_min_chunks": 1, "attn_waves": 2, "attn_merge_last": 3,
           "persistent": 4, "persist_splits": 5, "skinny_split": 6, "gemm_splits": 7, "attn_occupancy": 8, "skinny_norm": 9}
 PROF_KERNELS = ("embed", "qkv", "attn", "o", "gateup", "down", "lmhead")
@@ -122,6 +123,10 @@ def load_library(path: str = LIB_PATH):
     lib.qd_prefill.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp]
     lib.qd_decode_step.restype = i32
     lib.qd_decode_step.argtypes = [vp, i32, vp, vp, vp, vp]
+    lib.qd_prefill_slots.restype = i32
+    lib.qd_prefill_slots.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp]
+    lib.qd_decode_step_slots.restype = i32
+    lib.qd_decode_step_slots.argtypes = [vp, i32, vp, vp, vp, vp, vp]
     lib.qd_generate_greedy.restype = i32
     lib.qd_generate_greedy.argtypes = [vp, i32, vp, vp, i32, i32, vp, vp,
                                        ctypes.POINTER(StatsC), vp]
@@ -260,8 +265,9 @@ class Model:
                                         sc.ctypes.data, _stream_handle()))
         return q, sc
 
-    def prefill(self, prompts, logits: bool = False):
-        """Prefill prompts into slots 0..n-1.  Returns (next_ids [n] int32 cuda, logits [n, V] or None)."""
+    def prefill(self, prompts, logits: bool = False, slots=None):
+        """Prefill prompts into slots 0..n-1 (or into the KV slots ``slots``, one per prompt).
+        Returns (next_ids [n] int32 cuda, logits [n, V] or None)."""
         prompts = [np.asarray(p, dtype=np.int32).reshape(-1) for p in prompts]
         lens = np.array([p.size for p in prompts], dtype=np.int32)
         flat = np.concatenate(prompts) if prompts else np.zeros(0, np.int32)
@@ -269,21 +275,35 @@ class Model:
         nxt = torch.empty(len(prompts), dtype=torch.int32, device=self.device)
         lg = torch.empty((len(prompts), self.shape.vocab), dtype=torch.float32,
                          device=self.device) if logits else None
-        _check(_lib.qd_prefill(self._h, len(prompts), ids_dev.data_ptr(), flat.ctypes.data,
-                               lens.ctypes.data, lg.data_ptr() if lg is not None else None,
-                               nxt.data_ptr(), _stream_handle()))
+        lg_ptr = lg.data_ptr() if lg is not None else None
+        if slots is None:
+            _check(_lib.qd_prefill(self._h, len(prompts), ids_dev.data_ptr(), flat.ctypes.data,
+                                   lens.ctypes.data, lg_ptr, nxt.data_ptr(), _stream_handle()))
+        else:
+            sl = np.ascontiguousarray(slots, dtype=np.int32).reshape(-1)
+            _check(_lib.qd_prefill_slots(self._h, len(prompts), sl.ctypes.data, ids_dev.data_ptr(),
+                                         flat.ctypes.data, lens.ctypes.data, lg_ptr,
+                                         nxt.data_ptr(), _stream_handle()))
         return nxt, lg
 
-    def decode_step(self, in_ids, logits: bool = False):
-        """One step for slots 0..B-1 fed ``in_ids`` (int32 cuda tensor [B])."""
+    def decode_step(self, in_ids, logits: bool = False, slots=None):
+        """One step for slots 0..B-1 (or the KV slots ``slots``, row b = slots[b]) fed
+        ``in_ids`` (int32 cuda tensor [B])."""
         in_ids = torch.as_tensor(in_ids, dtype=torch.int32).to(self.device).contiguous()
         B = in_ids.numel()
         nxt = torch.empty(B, dtype=torch.int32, device=self.device)
         lg = torch.empty((B, self.shape.vocab), dtype=torch.float32,
                          device=self.device) if logits else None
-        _check(_lib.qd_decode_step(self._h, B, in_ids.data_ptr(),
-                                   lg.data_ptr() if lg is not None else None, nxt.data_ptr(),
-                                   _stream_handle()))
+        lg_ptr = lg.data_ptr() if lg is not None else None
+        if slots is None:
+            _check(_lib.qd_decode_step(self._h, B, in_ids.data_ptr(), lg_ptr, nxt.data_ptr(),
+                                       _stream_handle()))
+        else:
+            sl = np.ascontiguousarray(slots, dtype=np.int32).reshape(-1)
+            if sl.size != B:
+                raise QdError(1, f"{sl.size} slots for {B} ids")
+            _check(_lib.qd_decode_step_slots(self._h, B, sl.ctypes.data, in_ids.data_ptr(), lg_ptr,
+                                             nxt.data_ptr(), _stream_handle()))
         return nxt, lg
 
     def set_tuning(self, **knobs):

@@ -44,6 +44,7 @@ struct Plan {
   // workspace
   size_t x = 0, h = 0, qkv = 0, attn = 0, act = 0, part_o = 0, part_ml = 0;
   size_t ids = 0, row_slot = 0, row_pos = 0, last_rows = 0, lens = 0, slot_ident = 0, tiles = 0;
+  size_t slot_map = 0;  // [max_batch] KV slot of each row of a slot-addressed call
   size_t pos = 0, next_ids = 0, lm_keys = 0, att_cnt = 0, sk_cnt = 0, done = 0, step = 0, out_ids = 0;
   size_t gemm_part = 0;
   // persistent single-sequence decode: exchange buffers, barrier words, error flag
@@ -174,6 +175,7 @@ Plan make_plan(const qd_model_shape& s, const qd_limits& lim) {
   P.tiles = take((size_t)(M / FLASH_ROWS + B + 1) * 16);
   P.lens = take((size_t)B * 4);
   P.slot_ident = take((size_t)B * 4);
+  P.slot_map = take((size_t)B * 4);
   P.pos = take((size_t)B * 4);
   P.next_ids = take((size_t)B * 4);
   P.lm_keys = take((size_t)B * LM_MAX_GRID * 8);
@@ -289,7 +291,7 @@ void attn_split(int ctx, int cap, int max_splits, int min_chunks, int occupancy,
 // gathered through x_rows when given) and one MFMA sweep of the embedding serves all.
 qd_status enqueue_lm_head(qd_model* m, const bf16_t* x, const int* x_rows, int rows_total, int B,
                           float* logits, int* next_ids, bool bump_pos, bool write_out,
-                          hipStream_t st, bool normed = false) {
+                          hipStream_t st, bool normed = false, const int* row_slot = nullptr) {
   const Dims& d = m->d;
   GemvArgs a{};
   a.W = m->w<int8_t>(m->P.emb_q);
@@ -303,6 +305,7 @@ qd_status enqueue_lm_head(qd_model* m, const bf16_t* x, const int* x_rows, int r
   a.done = m->ws<unsigned int>(m->P.done);
   a.next_ids = next_ids;
   a.pos = bump_pos ? m->ws<int>(m->P.pos) : nullptr;
+  a.row_slot = row_slot;
   a.out_ids = write_out ? m->ws<int>(m->P.out_ids) : nullptr;
   a.out_ld = m->lim.max_ctx;
   a.step = m->ws<int>(m->P.step);
@@ -391,7 +394,8 @@ int attn_occupancy_for(const qd_model* m, int B) {
   return attn_waves_for(m, B) == 8 ? 1 : 3;
 }
 
-qd_status dec_attn(qd_model* m, int l, int B, int nsplit, int split_len, hipStream_t st) {
+qd_status dec_attn(qd_model* m, int l, int B, int nsplit, int split_len, hipStream_t st,
+                   const int* row_slot = nullptr) {
   const Dims& d = m->d;
   const LayerOff& o = m->P.L[l];
   AttnDecArgs aa{};
@@ -399,6 +403,7 @@ qd_status dec_attn(qd_model* m, int l, int B, int nsplit, int split_len, hipStre
   aa.q_gain = m->w<float>(o.qn_g); aa.k_gain = m->w<float>(o.kn_g); aa.eps = m->shape.rms_eps;
   aa.rope = m->w<float2>(m->P.rope);
   aa.pos = m->ws<int>(m->P.pos);
+  aa.row_slot = row_slot;
   aa.kcache = m->kcache(l); aa.vcache = m->vcache(l);
   aa.H = d.H; aa.KV = d.KV; aa.D = d.D; aa.max_ctx = m->lim.max_ctx; aa.B = B;
   aa.split_len = split_len; aa.nsplit = nsplit;
@@ -440,26 +445,29 @@ qd_status dec_down(qd_model* m, int l, int B, hipStream_t st) {
 
 // one decode step; positions read from the device
 qd_status enqueue_decode(qd_model* m, int B, const int* in_ids, float* logits, int* next_ids,
-                         bool write_out, int nsplit, int split_len, hipStream_t st) {
+                         bool write_out, int nsplit, int split_len, hipStream_t st,
+                         const int* row_slot = nullptr) {
   const Dims& d = m->d;
   HIPCHK(launch_embed(in_ids, B, m->w<int8_t>(m->P.emb_q), m->w<float>(m->P.emb_s), d.d, d.V,
                       m->ws<bf16_t>(m->P.x), st));
   for (int l = 0; l < d.L; ++l) {
     QDCHK(dec_qkv(m, l, B, st));
-    QDCHK(dec_attn(m, l, B, nsplit, split_len, st));
+    QDCHK(dec_attn(m, l, B, nsplit, split_len, st, row_slot));
     QDCHK(dec_o(m, l, B, st));
     QDCHK(dec_gateup(m, l, B, st));
     QDCHK(dec_down(m, l, B, st));
   }
   return enqueue_lm_head(m, m->ws<bf16_t>(m->P.x), nullptr, B, B, logits, next_ids, true,
-                         write_out, st);
+                         write_out, st, false, row_slot);
 }
 
 // staging layout (ints): [prompt ids: Mmax][row_slot: Mmax][row_pos: Mmax][last: B][lens: B]
-// [tiles: 4 * (Mmax / FLASH_ROWS + B + 1)]
+// [tiles: 4 * (Mmax / FLASH_ROWS + B + 1)][slots: B]
 size_t stage_ints(const Plan& P, int B) {
-  return (size_t)4 * P.mmax + 2 * (size_t)B + 4 * ((size_t)P.mmax / FLASH_ROWS + B + 1);
+  return (size_t)4 * P.mmax + 2 * (size_t)B + 4 * ((size_t)P.mmax / FLASH_ROWS + B + 1) + B;
 }
+// the last B staging ints carry a slot list (rows -> KV slots) to the device
+int* stage_slots(qd_model* m) { return m->hstage + m->hstage_ints - m->lim.max_batch; }
 
 qd_status stage_wait(qd_model* m) {
   if (m->stage_pending) {
@@ -477,7 +485,8 @@ qd_status stage_mark(qd_model* m, hipStream_t st) {
 
 // prefill of n prompts whose ids are already in the workspace (P.ids), metadata on host
 qd_status enqueue_prefill(qd_model* m, int n, const int* ids_dev, const std::vector<int>& lens,
-                          float* logits, int* next_ids, bool write_out, hipStream_t st) {
+                          float* logits, int* next_ids, bool write_out, hipStream_t st,
+                          const int* slots = nullptr) {
   const Dims& d = m->d;
   const Plan& P = m->P;
   qd_status sw = stage_wait(m);
@@ -492,13 +501,13 @@ qd_status enqueue_prefill(qd_model* m, int n, const int* ids_dev, const std::vec
   for (int b = 0; b < n; ++b) {
     for (int p0 = 0; p0 < lens[b]; p0 += FLASH_ROWS) {
       h_tiles[4 * n_tiles + 0] = M + p0;
-      h_tiles[4 * n_tiles + 1] = b;
+      h_tiles[4 * n_tiles + 1] = slots ? slots[b] : b;
       h_tiles[4 * n_tiles + 2] = p0;
       h_tiles[4 * n_tiles + 3] = std::min(FLASH_ROWS, lens[b] - p0);
       ++n_tiles;
     }
     for (int t = 0; t < lens[b]; ++t) {
-      h_rs[M + t] = b;
+      h_rs[M + t] = slots ? slots[b] : b;
       h_rp[M + t] = t;
     }
     M += lens[b];
@@ -515,6 +524,13 @@ qd_status enqueue_prefill(qd_model* m, int n, const int* ids_dev, const std::vec
   HIPCHK(hipMemcpyAsync(last_rows, h_last, n * 4, hipMemcpyHostToDevice, st));
   HIPCHK(hipMemcpyAsync(dlens, h_lens, n * 4, hipMemcpyHostToDevice, st));
   HIPCHK(hipMemcpyAsync(dtiles, h_tiles, (size_t)n_tiles * 16, hipMemcpyHostToDevice, st));
+  int* dslots = nullptr;
+  if (slots) {
+    int* hs = stage_slots(m);
+    std::memcpy(hs, slots, (size_t)n * 4);
+    dslots = m->ws<int>(P.slot_map);
+    HIPCHK(hipMemcpyAsync(dslots, hs, (size_t)n * 4, hipMemcpyHostToDevice, st));
+  }
   sw = stage_mark(m, st);
   if (sw != QD_OK) return sw;
 
@@ -574,7 +590,7 @@ qd_status enqueue_prefill(qd_model* m, int n, const int* ids_dev, const std::vec
   // h holds the final-normalized rows
   qd_status s = enqueue_lm_head(m, h, last_rows, M, n, logits, next_ids, false, write_out, st, true);
   if (s != QD_OK) return s;
-  HIPCHK(launch_set_positions(m->ws<int>(P.pos), dlens, n, st));
+  HIPCHK(launch_set_positions(m->ws<int>(P.pos), dlens, dslots, n, st));
   return QD_OK;
 }
 
@@ -879,15 +895,33 @@ qd_status qd_export_quantized(qd_model* m, int32_t tensor, int32_t layer, int8_t
   return QD_OK;
 }
 
-qd_status qd_prefill(qd_model* m, int32_t n_seqs, const int32_t* ids_dev, const int32_t* ids_host,
-                     const int32_t* lens_host, float* logits_dev, int32_t* next_ids_dev,
-                     qd_stream stream) {
+namespace {
+// a host slot list: n distinct slots in [0, max_batch); "" when valid
+std::string check_slots(const qd_model* m, int n, const int32_t* slots) {
+  std::vector<char> seen(m->lim.max_batch, 0);
+  for (int b = 0; b < n; ++b) {
+    const int sl = slots[b];
+    if (sl < 0 || sl >= m->lim.max_batch)
+      return "slot " + std::to_string(sl) + " of row " + std::to_string(b) + " is outside [0, max_batch)";
+    if (seen[sl]) return "slot " + std::to_string(sl) + " is listed twice";
+    seen[sl] = 1;
+  }
+  return "";
+}
+
+qd_status prefill_impl(qd_model* m, int32_t n_seqs, const int32_t* slots, const int32_t* ids_dev,
+                       const int32_t* ids_host, const int32_t* lens_host, float* logits_dev,
+                       int32_t* next_ids_dev, qd_stream stream) {
   g_err.clear();
   if (!m) return fail(QD_ERR_INVALID_ARGUMENTS, "model is NULL");
   if (n_seqs < 1 || n_seqs > m->lim.max_batch)
     return fail(QD_ERR_INVALID_ARGUMENTS, "n_seqs must be in [1, max_batch]");
   if (!ids_dev || !lens_host || !next_ids_dev)
     return fail(QD_ERR_INVALID_ARGUMENTS, "ids_dev, lens_host and next_ids_dev must be set");
+  if (slots) {
+    const std::string e = check_slots(m, n_seqs, slots);
+    if (!e.empty()) return fail(QD_ERR_INVALID_ARGUMENTS, e);
+  }
   std::vector<int> lens(lens_host, lens_host + n_seqs);
   long total = 0;
   for (int b = 0; b < n_seqs; ++b) {
@@ -903,38 +937,91 @@ qd_status qd_prefill(qd_model* m, int32_t n_seqs, const int32_t* ids_dev, const 
     if (!e.empty()) return fail(QD_ERR_INVALID_ARGUMENTS, e);
   }
   qd_status s = enqueue_prefill(m, n_seqs, ids_dev, lens, logits_dev, next_ids_dev, false,
-                                (hipStream_t)stream);
+                                (hipStream_t)stream, slots);
   if (s == QD_OK)
-    for (int b = 0; b < n_seqs; ++b) m->host_pos[b] = lens[b];
+    for (int b = 0; b < n_seqs; ++b) m->host_pos[slots ? slots[b] : b] = lens[b];
   return s;
 }
 
-qd_status qd_decode_step(qd_model* m, int32_t B, const int32_t* in_ids_dev, float* logits_dev,
-                         int32_t* next_ids_dev, qd_stream stream) {
+qd_status decode_impl(qd_model* m, int32_t B, const int32_t* slots, const int32_t* in_ids_dev,
+                      float* logits_dev, int32_t* next_ids_dev, qd_stream stream) {
   g_err.clear();
   if (!m) return fail(QD_ERR_INVALID_ARGUMENTS, "model is NULL");
   if (B < 1 || B > m->lim.max_batch) return fail(QD_ERR_INVALID_ARGUMENTS, "B must be in [1, max_batch]");
   if (!in_ids_dev || !next_ids_dev) return fail(QD_ERR_INVALID_ARGUMENTS, "ids pointers must be set");
+  if (slots) {
+    const std::string e = check_slots(m, B, slots);
+    if (!e.empty()) return fail(QD_ERR_INVALID_ARGUMENTS, e);
+  }
   int ctx = 0;
   for (int b = 0; b < B; ++b) {
-    if (m->host_pos[b] >= m->lim.max_ctx)
-      return fail(QD_ERR_INVALID_ARGUMENTS, "slot " + std::to_string(b) + " is full (max_ctx)");
-    ctx = std::max(ctx, m->host_pos[b] + 1);
+    const int sl = slots ? slots[b] : b;
+    if (slots && m->host_pos[sl] < 1)
+      return fail(QD_ERR_INVALID_ARGUMENTS, "slot " + std::to_string(sl) + " holds no prompt");
+    if (m->host_pos[sl] >= m->lim.max_ctx)
+      return fail(QD_ERR_INVALID_ARGUMENTS, "slot " + std::to_string(sl) + " is full (max_ctx)");
+    ctx = std::max(ctx, m->host_pos[sl] + 1);
   }
   QDCHK(persist_check_err(m));
+  hipStream_t st = (hipStream_t)stream;
   qd_status s;
-  if (B == 1 && m->persist_ok && m->persist_on) {
-    s = persist_launch(m, in_ids_dev, 1, nullptr, next_ids_dev, logits_dev, (hipStream_t)stream);
+  if (!slots && B == 1 && m->persist_ok && m->persist_on) {
+    s = persist_launch(m, in_ids_dev, 1, nullptr, next_ids_dev, logits_dev, st);
   } else {
+    const int* row_slot = nullptr;
+    if (slots) {
+      QDCHK(stage_wait(m));
+      int* hs = stage_slots(m);
+      std::memcpy(hs, slots, (size_t)B * 4);
+      int* ds = m->ws<int>(m->P.slot_map);
+      HIPCHK(hipMemcpyAsync(ds, hs, (size_t)B * 4, hipMemcpyHostToDevice, st));
+      QDCHK(stage_mark(m, st));
+      row_slot = ds;
+    }
     int nsplit, split_len;
     attn_split(ctx, m->P.nsplit_cap, m->attn_max_splits, m->attn_min_chunks, attn_occupancy_for(m, B), B * m->d.KV, &nsplit,
                &split_len);
-    s = enqueue_decode(m, B, in_ids_dev, logits_dev, next_ids_dev, false, nsplit, split_len,
-                       (hipStream_t)stream);
+    s = enqueue_decode(m, B, in_ids_dev, logits_dev, next_ids_dev, false, nsplit, split_len, st,
+                       row_slot);
   }
   if (s == QD_OK)
-    for (int b = 0; b < B; ++b) m->host_pos[b] += 1;
+    for (int b = 0; b < B; ++b) m->host_pos[slots ? slots[b] : b] += 1;
   return s;
+}
+}  // namespace
+
+qd_status qd_prefill(qd_model* m, int32_t n_seqs, const int32_t* ids_dev, const int32_t* ids_host,
+                     const int32_t* lens_host, float* logits_dev, int32_t* next_ids_dev,
+                     qd_stream stream) {
+  return prefill_impl(m, n_seqs, nullptr, ids_dev, ids_host, lens_host, logits_dev, next_ids_dev,
+                      stream);
+}
+
+qd_status qd_prefill_slots(qd_model* m, int32_t n_seqs, const int32_t* slots_host,
+                           const int32_t* ids_dev, const int32_t* ids_host,
+                           const int32_t* lens_host, float* logits_dev, int32_t* next_ids_dev,
+                           qd_stream stream) {
+  if (!slots_host) {
+    g_err.clear();
+    return fail(QD_ERR_INVALID_ARGUMENTS, "slots_host must be set");
+  }
+  return prefill_impl(m, n_seqs, slots_host, ids_dev, ids_host, lens_host, logits_dev,
+                      next_ids_dev, stream);
+}
+
+qd_status qd_decode_step(qd_model* m, int32_t B, const int32_t* in_ids_dev, float* logits_dev,
+                         int32_t* next_ids_dev, qd_stream stream) {
+  return decode_impl(m, B, nullptr, in_ids_dev, logits_dev, next_ids_dev, stream);
+}
+
+qd_status qd_decode_step_slots(qd_model* m, int32_t B, const int32_t* slots_host,
+                               const int32_t* in_ids_dev, float* logits_dev,
+                               int32_t* next_ids_dev, qd_stream stream) {
+  if (!slots_host) {
+    g_err.clear();
+    return fail(QD_ERR_INVALID_ARGUMENTS, "slots_host must be set");
+  }
+  return decode_impl(m, B, slots_host, in_ids_dev, logits_dev, next_ids_dev, stream);
 }
 
 qd_status qd_generate_greedy(qd_model* m, int32_t B, const int32_t* prompt_ids_host,

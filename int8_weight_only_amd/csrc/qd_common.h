@@ -42,7 +42,8 @@ struct GemvArgs {
   float* logits; int ldl;            // optional fp32 logits [nb][ldl]
   unsigned int* done;                // completion counter, zero on entry
   int* next_ids;                     // [nb] greedy ids out
-  int* pos;                          // optional [nb]: incremented by the last block
+  int* pos;                          // optional [slots]: the row's slot position is incremented
+  const int* row_slot;               // optional [nb]: KV slot of row b for pos (NULL: slot b)
   int* out_ids; int out_ld;          // optional: out_ids[b*out_ld + *step] = id
   unsigned long long* part_keys;     // [nb][LM_MAX_GRID] per-work-group best keys
   int* step;                         // device step counter (read when out_ids is set)
@@ -87,7 +88,8 @@ struct AttnDecArgs {
   const bf16_t* qkv; int ldqkv;   // raw q|k|v projections, row b at qkv + b*ldqkv
   const float* q_gain; const float* k_gain; float eps;
   const float2* rope;             // [max_ctx][D/2]
-  const int* pos;                 // [B] position of the token being decoded (slot b = row b)
+  const int* pos;                 // [slots] position of the token being decoded, per KV slot
+  const int* row_slot;            // [B] KV slot of row b (NULL: slot b)
   bf16_t* kcache; bf16_t* vcache; // this layer's [slots][KV][ctx][D]
   int H, KV, D, max_ctx, B;
   int split_len, nsplit;
@@ -220,7 +222,7 @@ hipError_t launch_resid_norm(bf16_t* x, int M, int d, const float* part, int spl
 hipError_t launch_qk_rope(const RopeArgs& a, hipStream_t st);
 hipError_t launch_attention_decode(const AttnDecArgs& a, hipStream_t st);
 hipError_t launch_flash_prefill(const FlashArgs& a, int n_tiles, hipStream_t st);
-hipError_t launch_set_positions(int* pos, const int* lens, int n, hipStream_t st);
+hipError_t launch_set_positions(int* pos, const int* lens, const int* slots, int n, hipStream_t st);
 hipError_t launch_iota(int* p, int n, hipStream_t st);
 
 // persistent single-sequence decode (qd_persist.hip)

@@ -58,9 +58,9 @@ __global__ void k_iota(int* p, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = i;
 }
-__global__ void k_set_positions(int* pos, const int* lens, int n) {
+__global__ void k_set_positions(int* pos, const int* lens, const int* slots, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) pos[i] = lens[i];
+  if (i < n) pos[slots ? slots[i] : i] = lens[i];
 }
 
 // ------------------------------------------------------------------------------------------
@@ -258,7 +258,7 @@ __global__ __launch_bounds__(256) void k_lm_finish(GemvArgs a, int nblocks) {
     const int id = key_index(k);
     a.next_ids[b] = id;
     if (a.out_ids) a.out_ids[(size_t)(a.batch0 + b) * a.out_ld + *a.step] = id;
-    if (a.pos) a.pos[b] += 1;
+    if (a.pos) a.pos[a.row_slot ? a.row_slot[b] : b] += 1;
     // a single row advances the step counter itself (no other work-group reads it)
     if (a.bump_step && gridDim.x == 1) *a.step += 1;
   }
@@ -1435,14 +1435,15 @@ __global__ __launch_bounds__(64 * NW) void k_attn_dec(AttnDecArgs a) {
   // wave index as a scalar: per-wave choices (which head, which gain vector) stay scalar
   const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tl = lane >> 2, part = lane & 3;
-  const int p = a.pos[b];
+  const int sl = a.row_slot ? a.row_slot[b] : b;  // KV slot of this row
+  const int p = a.pos[sl];
   const int n = p + 1;
   const int t_begin = s * a.split_len;
   const int t_end = min(n, t_begin + a.split_len);
   const bf16_t* row = a.qkv + (size_t)b * a.ldqkv;
   const float2* tab = a.rope + (size_t)p * HALF;
-  bf16_t* Kb = a.kcache + ((size_t)b * a.KV + g) * a.max_ctx * D;
-  bf16_t* Vb = a.vcache + ((size_t)b * a.KV + g) * a.max_ctx * D;
+  bf16_t* Kb = a.kcache + ((size_t)sl * a.KV + g) * a.max_ctx * D;
+  bf16_t* Vb = a.vcache + ((size_t)sl * a.KV + g) * a.max_ctx * D;
   const bool owner = (t_begin <= p) && (p < t_begin + a.split_len);
   const bool vlane = (D >= 64) || (lane < D);
 
@@ -2027,8 +2028,8 @@ hipError_t launch_fill_i32(int* p, int n, int v, hipStream_t st) {
 }
 
 
-hipError_t launch_set_positions(int* pos, const int* lens, int n, hipStream_t st) {
-  hipLaunchKernelGGL(k_set_positions, dim3((n + 255) / 256), dim3(256), 0, st, pos, lens, n);
+hipError_t launch_set_positions(int* pos, const int* lens, const int* slots, int n, hipStream_t st) {
+  hipLaunchKernelGGL(k_set_positions, dim3((n + 255) / 256), dim3(256), 0, st, pos, lens, slots, n);
   return hipGetLastError();
 }
 

@@ -361,3 +361,68 @@ def test_teacher_forced_long_context():
         _teacher_forced(m, WIDE, qm, prompt, 23, "wide-long 2 splits", "wide-long", 1, orc)
     finally:
         m.close()
+
+
+def test_continuous_batching_slots_teacher_forced():
+    """Sequences join and leave a running batch ("LLM inference overview", section
+    "Results": continuous batching): prompts are prefilled into free KV slots while other
+    slots are mid-decode, and each decode step lists its slots in any order, each at its
+    own length.  Every sequence's logits follow the oracle run of that sequence alone."""
+    import int8_weight_only_amd as qd
+    shape = TINY
+    w = make_weights(shape, seed=7, gains="uniform")
+    qm = quantize_model(w)
+    lens = {"A": 7, "B": 12, "C": 5, "D": 9}
+    prompts = {s: make_prompt(shape.vocab, n, 6000 + i) for i, (s, n) in enumerate(lens.items())}
+    need = {"A": 6, "B": 7, "C": 7, "D": 4}
+    orcs = {s: Oracle(shape, qm, mode="bf16").generate(prompts[s], need[s]) for s in prompts}
+    step = {s: 0 for s in prompts}
+    say("[gpu] continuous batching through slot-addressed prefill and decode")
+    m = _model(shape, w, max_batch=5, max_ctx=64, max_prefill_tokens=64)
+
+    def check(seq, lg_row, nxt_id):
+        k = step[seq]
+        check_step(lg_row, nxt_id, orcs[seq]["logits"][k], orcs[seq]["margin"][k], "tiny",
+                   f"{seq} step {k}")
+        step[seq] += 1
+
+    def prefill(pairs):  # [(seq, slot)]
+        nxt, lg = m.prefill([prompts[s] for s, _ in pairs], logits=True,
+                            slots=[sl for _, sl in pairs])
+        torch.cuda.synchronize()
+        for i, (s, _) in enumerate(pairs):
+            check(s, lg[i].cpu().numpy(), nxt[i].item())
+
+    def decode(pairs):  # [(seq, slot)], rows in this order
+        feed = torch.tensor([orcs[s]["ids"][step[s] - 1] for s, _ in pairs], dtype=torch.int32,
+                            device="cuda")
+        nxt, lg = m.decode_step(feed, logits=True, slots=[sl for _, sl in pairs])
+        torch.cuda.synchronize()
+        for i, (s, _) in enumerate(pairs):
+            check(s, lg[i].cpu().numpy(), nxt[i].item())
+
+    try:
+        prefill([("A", 2)])
+        decode([("A", 2)])
+        decode([("A", 2)])
+        prefill([("B", 0), ("C", 4)])           # two joins in one ragged prefill
+        for _ in range(3):
+            decode([("C", 4), ("A", 2), ("B", 0)])  # rows in slot-shuffled order
+        prefill([("D", 2)])                      # A leaves, D takes its slot
+        for _ in range(2):
+            decode([("B", 0), ("D", 2), ("C", 4)])
+        decode([("D", 2)])                       # the others idle this step
+        decode([("C", 4), ("B", 0)])
+        assert step == need, step
+        # error paths: checked on the host before any GPU work
+        feed = torch.zeros(2, dtype=torch.int32, device="cuda")
+        for bad in ([0, 0], [0, 5], [0, 1]):     # duplicate, out of range, empty slot
+            with pytest.raises(qd.QdError) as e:
+                m.decode_step(feed, slots=bad)
+            assert e.value.code == "invalid_arguments", bad
+        with pytest.raises(qd.QdError) as e:
+            m.prefill([prompts["A"], prompts["C"]], slots=[3, 3])
+        assert e.value.code == "invalid_arguments"
+        assert step == need  # the refused calls changed nothing on the host side
+    finally:
+        m.close()
