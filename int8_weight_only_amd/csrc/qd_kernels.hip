@@ -1934,31 +1934,47 @@ __global__ __launch_bounds__(256) void k_flash_prefill(FlashArgs a) {
         sacc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ks2], kf, sacc[n], 0, 0, 0);
       }
     }
-    // causal mask + online softmax; lane holds rows 4*grp+i, keys 16n + r16
+    // causal mask + online softmax; lane holds rows 4*grp+i, keys 16n + r16.  A row's
+    // reference maximum m moves only when the block's maximum exceeds it by more than
+    // 2^TAU (so probabilities stay below 2^TAU); the wave rescales its O rows only then
+    // (the result is the same softmax, any reference gives it)
+    constexpr float TAU = 8.0f;
+    float sv[4][NKT], mb[4];
+    bool need = false;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * wid + 4 * grp + i;
       const int qpos = pos0 + r;
-      float sv[NKT];
       float smax = -INFINITY;
 #pragma unroll
       for (int n = 0; n < NKT; ++n) {
         const int key = kb + 16 * n + r16;
-        sv[n] = (r < nrows && key <= qpos) ? sacc[n][i] * scale2 : -INFINITY;
-        smax = fmaxf(smax, sv[n]);
+        sv[i][n] = (r < nrows && key <= qpos) ? sacc[n][i] * scale2 : -INFINITY;
+        smax = fmaxf(smax, sv[i][n]);
       }
-      const float mnew = fmaxf(m[i], row16_max(smax));
-      const float alpha = (m[i] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m[i] - mnew);
+      mb[i] = row16_max(smax);
+      need = need || (mb[i] > m[i] + TAU);
+    }
+    if (__any(need)) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float mnew = fmaxf(m[i], mb[i]);
+        const float alpha = (m[i] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m[i] - mnew);
+        l[i] *= alpha;
+        m[i] = mnew;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) o[nt][i] *= alpha;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
       float pr[NKT], psum = 0.0f;
 #pragma unroll
       for (int n = 0; n < NKT; ++n) {
-        pr[n] = (sv[n] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sv[n] - mnew);
+        pr[n] = (sv[i][n] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sv[i][n] - m[i]);
         psum += pr[n];
       }
-      l[i] = l[i] * alpha + row16_sum(psum);
-      m[i] = mnew;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) o[nt][i] *= alpha;
+      l[i] += row16_sum(psum);
 #pragma unroll
       for (int n = 0; n < NKT; ++n) {
         const bf16_t hi = f2bf(pr[n]);
