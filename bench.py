@@ -66,7 +66,7 @@ def prefill_flops(s, M):
 
 
 KERNEL_SOURCES = [os.path.join(ROOT, "int8_weight_only_amd", "csrc", f)
-                  for f in ("qd_common.h", "qd_device.h", "qd_kernels.hip", "qd_persist.hip")]
+                  for f in ("qd_common.h", "qd_device.h", "qd_kernels.hip", "qd_persist.hip", "qd_sample.hip")]
 
 
 def kernel_source_sha() -> str:
@@ -187,6 +187,34 @@ def time_generate(model, prompts, new, steps, warmup):
     return float(np.mean(dev)), float(np.mean(pre)), float(np.mean(dec)), wall / steps, res
 
 
+SAMPLED = dict(temperature=0.8, top_k=40, top_p=0.95, min_p=0.0, repeat_penalty=1.1)
+
+
+def time_sampled(model, shape, B, NP, NN):
+    """Sampled decode ("Model-agnostic LLM inference", section "Sampling", with the
+    parameters of its example): B sequences, each step materializes the fp32 logits and
+    draws every token through the device sampler (penalties, temperature, top-k, min-p,
+    top-p, Philox draw).  Device time of the decode steps plus their draws."""
+    import torch
+    from workloads import make_prompts
+    prompts = make_prompts(shape.vocab, NP, B, seed0=1000)
+    seeds = [1234 + b for b in range(B)]
+    steps = min(64, NN - 1)
+    _, lg = model.prefill(list(prompts), logits=True)
+    ids = model.sample(lg, seeds, **SAMPLED)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(steps):
+        _, lg = model.decode_step(ids, logits=True)
+        ids = model.sample(lg, seeds, **SAMPLED)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1)
+    log(f"[bench] sampled B={B}: {steps} steps in {ms:.2f} ms")
+    return {f"sampled_b{B}_tok_s": round(B * steps / (ms * 1e-3), 1)}
+
+
 def time_continuous(model, shape, S, NP, NN):
     """Continuous batching ("LLM inference overview", section "Results"): S KV slots hold
     sequences of ragged lengths; every step lists all slots in a fresh random order
@@ -241,6 +269,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="same as --extra-batches ''")
     ap.add_argument("--no-oracle", action="store_true", help="skip parity gate and CPU baseline")
     ap.add_argument("--no-continuous", action="store_true", help="skip the continuous-batching line")
+    ap.add_argument("--no-sampled", action="store_true", help="skip the sampled-decode lines")
     ap.add_argument("--kernels-only", action="store_true",
                     help="no captured graphs and few dispatches: prefill prompt+new-2 tokens, "
                          "one decode step, then the per-kernel timing pass (for counter runs)")
@@ -356,6 +385,9 @@ def main():
 
     if extras and max(extras) >= 8 and not args.no_continuous:
         extra.update(time_continuous(model, shape, max(extras), NP, NN))
+    if not args.no_sampled:
+        for sb in sorted({B} | ({max(extras)} if extras else set())):
+            extra.update(time_sampled(model, shape, sb, NP, NN))
 
     pf = prefill_flops(shape, NP)
     line = {

@@ -219,6 +219,42 @@ qd_status qd_decode_step_slots(qd_model* m, int32_t B, const int32_t* slots_host
                                const int32_t* in_ids_dev, float* logits_dev,
                                int32_t* next_ids_dev, qd_stream stream);
 
+/* Sampled decode ("Model-agnostic LLM inference", section "Sampling"): the chain
+ * repetition / presence / frequency penalties -> temperature -> top-k -> min-p -> top-p
+ * -> seeded weighted draw.  Penalties use the occurrences of each token in the sequence
+ * so far (its prompt and every token fed since, counted on the device by the prefill and
+ * decode calls; a prefill restarts its slots' counts).  A seen token's logit is divided
+ * by repeat_penalty when positive and multiplied by it otherwise, then presence_penalty
+ * + frequency_penalty * count is subtracted; all logits are divided by temperature.
+ * top_k keeps the k largest (equal values: lower id first); min_p keeps probabilities
+ * >= min_p x the largest; top_p the shortest prefix of the rest holding top_p of its
+ * mass (at least one token).  The draw: u in [0, 1) from Philox4x64-10 with key
+ * (seed, 0) and counter (n, 0, 0, 0), n = tokens already drawn for the sequence (reset by
+ * its prefill), u = top 24 bits of the first word x 2^-24; the first candidate whose
+ * cumulative weight exceeds u x the kept weight is drawn.  Same prompt, parameters and
+ * seed give the same tokens; top_k = 1 gives the greedy id (of the penalized logits). */
+typedef struct {
+  float temperature;        /* > 0 */
+  int32_t top_k;            /* 1..1024 (this library's limit) */
+  float min_p;              /* [0, 1]; 0 keeps all */
+  float top_p;              /* (0, 1]; 1 keeps all */
+  float repeat_penalty;     /* > 0; 1 = none */
+  float presence_penalty;   /* 0 = none */
+  float frequency_penalty;  /* 0 = none */
+} qd_sampling;
+
+/* Draws one token per row from logits_dev [B, V] (device, fp32; e.g. the logits output
+ * of qd_prefill / qd_decode_step / their _slots forms) for the sequences in KV slots
+ * slots_host[b] (host, distinct; NULL: slots 0..B-1), with per-row seeds seeds_host[B]
+ * (host).  Writes next_ids_dev[B] (device) and advances each slot's draw number.  The
+ * caller feeds the drawn ids to the next decode step.  Asynchronous on `stream`.
+ * Errors: QD_ERR_INVALID_ARGUMENTS (a parameter out of range, a NULL pointer, a slot out
+ * of range, listed twice or holding no prompt), before any GPU work.  Decode steps run
+ * by the opt-in persistent kernel (QD_TUNE_PERSISTENT) do not count their tokens. */
+qd_status qd_sample(qd_model* m, int32_t B, const int32_t* slots_host, const qd_sampling* params,
+                    const uint64_t* seeds_host, const float* logits_dev, int32_t* next_ids_dev,
+                    qd_stream stream);
+
 /* One call, start to finish ("Model-agnostic LLM inference", section "Notes"):
  * prefill of B prompts (host ids, concatenated; lens_host[B]) then
  * max_new_tokens - 1 decode steps, greedy ids kept on the device between steps:

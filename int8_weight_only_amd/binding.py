@@ -89,12 +89,20 @@ class StatsC(ctypes.Structure):
 EXPORTS = ("qd_last_error", "qd_check_shape", "qd_query_sizes", "qd_load_weights",
            "qd_export_quantized", "qd_prefill", "qd_decode_step", "qd_generate_greedy",
            "qd_free", "qd_profile_kernels", "qd_set_tuning", "qd_prefill_slots",
-           "qd_decode_step_slots")
+           "qd_decode_step_slots", "qd_sample")
 TUNING = {"attn_max_splits": 0, "attn_min_chunks": 1, "attn_waves": 2, "attn_merge_last": 3,
           "persistent": 4, "persist_splits": 5, "skinny_split": 6, "gemm_splits": 7, "attn_occupancy": 8, "skinny_norm": 9}
 PROF_KERNELS = ("embed", "qkv", "attn", "o", "gateup", "down", "lmhead")
 
 _lib = None
+
+
+class SamplingC(ctypes.Structure):
+    """qd_sampling: "Model-agnostic LLM inference", section "Sampling"."""
+    _fields_ = [("temperature", ctypes.c_float), ("top_k", ctypes.c_int32),
+                ("min_p", ctypes.c_float), ("top_p", ctypes.c_float),
+                ("repeat_penalty", ctypes.c_float), ("presence_penalty", ctypes.c_float),
+                ("frequency_penalty", ctypes.c_float)]
 
 
 def load_library(path: str = LIB_PATH):
@@ -125,6 +133,8 @@ def load_library(path: str = LIB_PATH):
     lib.qd_decode_step.argtypes = [vp, i32, vp, vp, vp, vp]
     lib.qd_prefill_slots.restype = i32
     lib.qd_prefill_slots.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp]
+    lib.qd_sample.restype = i32
+    lib.qd_sample.argtypes = [vp, i32, vp, ctypes.POINTER(SamplingC), vp, vp, vp, vp]
     lib.qd_decode_step_slots.restype = i32
     lib.qd_decode_step_slots.argtypes = [vp, i32, vp, vp, vp, vp, vp]
     lib.qd_generate_greedy.restype = i32
@@ -305,6 +315,26 @@ class Model:
             _check(_lib.qd_decode_step_slots(self._h, B, sl.ctypes.data, in_ids.data_ptr(), lg_ptr,
                                              nxt.data_ptr(), _stream_handle()))
         return nxt, lg
+
+    def sample(self, logits, seeds, slots=None, temperature=1.0, top_k=40, min_p=0.0,
+               top_p=1.0, repeat_penalty=1.0, presence_penalty=0.0, frequency_penalty=0.0):
+        """Draws one id per row of ``logits`` (fp32 cuda [B, V]) for slots 0..B-1 (or
+        ``slots``) with per-row ``seeds``; returns int32 cuda [B]."""
+        logits = logits.contiguous()
+        B = logits.shape[0]
+        sd = np.ascontiguousarray(seeds, dtype=np.uint64).reshape(-1)
+        if sd.size != B:
+            raise QdError(1, f"{sd.size} seeds for {B} rows")
+        sl = None if slots is None else np.ascontiguousarray(slots, dtype=np.int32).reshape(-1)
+        if sl is not None and sl.size != B:
+            raise QdError(1, f"{sl.size} slots for {B} rows")
+        prm = SamplingC(temperature, top_k, min_p, top_p, repeat_penalty, presence_penalty,
+                        frequency_penalty)
+        nxt = torch.empty(B, dtype=torch.int32, device=self.device)
+        _check(_lib.qd_sample(self._h, B, sl.ctypes.data if sl is not None else None,
+                              ctypes.byref(prm), sd.ctypes.data, logits.data_ptr(),
+                              nxt.data_ptr(), _stream_handle()))
+        return nxt
 
     def set_tuning(self, **knobs):
         """Launch-policy knobs, e.g. attn_max_splits=8 (performance only)."""

@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libqd.so")
-SOURCES = ["qd_kernels.hip", "qd_persist.hip", "qd_api.hip"]
+SOURCES = ["qd_kernels.hip", "qd_persist.hip", "qd_sample.hip", "qd_api.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -16,6 +16,7 @@
 #include <tuple>
 #include <vector>
 #include <cstring>
+#include <cmath>
 #include <cstdio>
 
 using namespace qd;
@@ -45,6 +46,7 @@ struct Plan {
   size_t x = 0, h = 0, qkv = 0, attn = 0, act = 0, part_o = 0, part_ml = 0;
   size_t ids = 0, row_slot = 0, row_pos = 0, last_rows = 0, lens = 0, slot_ident = 0, tiles = 0;
   size_t slot_map = 0;  // [max_batch] KV slot of each row of a slot-addressed call
+  size_t tok_counts = 0, draws = 0, seeds = 0, samp_z = 0;  // sampler state and scratch
   size_t pos = 0, next_ids = 0, lm_keys = 0, att_cnt = 0, sk_cnt = 0, done = 0, step = 0, out_ids = 0;
   size_t gemm_part = 0;
   // persistent single-sequence decode: exchange buffers, barrier words, error flag
@@ -176,6 +178,10 @@ Plan make_plan(const qd_model_shape& s, const qd_limits& lim) {
   P.lens = take((size_t)B * 4);
   P.slot_ident = take((size_t)B * 4);
   P.slot_map = take((size_t)B * 4);
+  P.tok_counts = take((size_t)B * d.V * 4);
+  P.draws = take((size_t)B * 4);
+  P.seeds = take((size_t)B * 8);
+  P.samp_z = take((size_t)B * d.V * 4);
   P.pos = take((size_t)B * 4);
   P.next_ids = take((size_t)B * 4);
   P.lm_keys = take((size_t)B * LM_MAX_GRID * 8);
@@ -449,7 +455,7 @@ qd_status enqueue_decode(qd_model* m, int B, const int* in_ids, float* logits, i
                          const int* row_slot = nullptr) {
   const Dims& d = m->d;
   HIPCHK(launch_embed(in_ids, B, m->w<int8_t>(m->P.emb_q), m->w<float>(m->P.emb_s), d.d, d.V,
-                      m->ws<bf16_t>(m->P.x), st));
+                      m->ws<bf16_t>(m->P.x), st, m->ws<int>(m->P.tok_counts), row_slot));
   for (int l = 0; l < d.L; ++l) {
     QDCHK(dec_qkv(m, l, B, st));
     QDCHK(dec_attn(m, l, B, nsplit, split_len, st, row_slot));
@@ -462,11 +468,16 @@ qd_status enqueue_decode(qd_model* m, int B, const int* in_ids, float* logits, i
 }
 
 // staging layout (ints): [prompt ids: Mmax][row_slot: Mmax][row_pos: Mmax][last: B][lens: B]
-// [tiles: 4 * (Mmax / FLASH_ROWS + B + 1)][slots: B]
+// [tiles: 4 * (Mmax / FLASH_ROWS + B + 1)][pad to 8 bytes][seeds: 2B][slots: B]
 size_t stage_ints(const Plan& P, int B) {
-  return (size_t)4 * P.mmax + 2 * (size_t)B + 4 * ((size_t)P.mmax / FLASH_ROWS + B + 1) + B;
+  const size_t base = (size_t)4 * P.mmax + 2 * (size_t)B + 4 * ((size_t)P.mmax / FLASH_ROWS + B + 1);
+  return ((base + 1) & ~(size_t)1) + 3 * (size_t)B;
 }
-// the last B staging ints carry a slot list (rows -> KV slots) to the device
+// the sampler's per-row seeds and a slot list (rows -> KV slots) travel to the device
+// through the end of the staging area: [seeds: B x 8 bytes, 8-byte aligned][slots: B]
+unsigned long long* stage_seeds(qd_model* m) {
+  return reinterpret_cast<unsigned long long*>(m->hstage + m->hstage_ints - 3 * (size_t)m->lim.max_batch);
+}
 int* stage_slots(qd_model* m) { return m->hstage + m->hstage_ints - m->lim.max_batch; }
 
 qd_status stage_wait(qd_model* m) {
@@ -540,7 +551,11 @@ qd_status enqueue_prefill(qd_model* m, int n, const int* ids_dev, const std::vec
   bf16_t* attn = m->ws<bf16_t>(P.attn);
   bf16_t* act = m->ws<bf16_t>(P.act);
   float* gpart = m->ws<float>(P.gemm_part);
-  HIPCHK(launch_embed(ids_dev, M, m->w<int8_t>(P.emb_q), m->w<float>(P.emb_s), d.d, d.V, x, st));
+  // the sampler's token counts and draw numbers restart with each prompt; the embedding
+  // counts the prompt tokens
+  HIPCHK(launch_reset_seq(m->ws<int>(P.tok_counts), m->ws<int>(P.draws), dslots, n, d.V, st));
+  HIPCHK(launch_embed(ids_dev, M, m->w<int8_t>(P.emb_q), m->w<float>(P.emb_s), d.d, d.V, x, st,
+                      m->ws<int>(P.tok_counts), row_slot));
   // the input RMSNorm of layer 0; every later one (and the final norm) runs fused with
   // the split-K merge of the down projection before it
   HIPCHK(launch_rmsnorm(x, M, d.d, m->w<float>(P.L[0].in_g), m->shape.rms_eps, h, st));
@@ -1022,6 +1037,63 @@ qd_status qd_decode_step_slots(qd_model* m, int32_t B, const int32_t* slots_host
     return fail(QD_ERR_INVALID_ARGUMENTS, "slots_host must be set");
   }
   return decode_impl(m, B, slots_host, in_ids_dev, logits_dev, next_ids_dev, stream);
+}
+
+qd_status qd_sample(qd_model* m, int32_t B, const int32_t* slots_host, const qd_sampling* params,
+                    const uint64_t* seeds_host, const float* logits_dev, int32_t* next_ids_dev,
+                    qd_stream stream) {
+  g_err.clear();
+  if (!m) return fail(QD_ERR_INVALID_ARGUMENTS, "model is NULL");
+  if (B < 1 || B > m->lim.max_batch) return fail(QD_ERR_INVALID_ARGUMENTS, "B must be in [1, max_batch]");
+  if (!params || !seeds_host || !logits_dev || !next_ids_dev)
+    return fail(QD_ERR_INVALID_ARGUMENTS, "params, seeds_host, logits_dev and next_ids_dev must be set");
+  std::string p;
+  const qd_sampling& q = *params;
+  if (!(q.temperature > 0.0f) || !std::isfinite(q.temperature)) p += "temperature must be > 0; ";
+  if (q.top_k < 1 || q.top_k > SMP_MAXK) p += "top_k must be in [1, " + std::to_string(SMP_MAXK) + "]; ";
+  if (!(q.min_p >= 0.0f && q.min_p <= 1.0f)) p += "min_p must be in [0, 1]; ";
+  if (!(q.top_p > 0.0f && q.top_p <= 1.0f)) p += "top_p must be in (0, 1]; ";
+  if (!(q.repeat_penalty > 0.0f) || !std::isfinite(q.repeat_penalty)) p += "repeat_penalty must be > 0; ";
+  if (!std::isfinite(q.presence_penalty) || !std::isfinite(q.frequency_penalty)) p += "penalties must be finite; ";
+  if (slots_host) {
+    const std::string e = check_slots(m, B, slots_host);
+    if (!e.empty()) p += e + "; ";
+  }
+  for (int b = 0; b < B && p.empty(); ++b) {
+    const int sl = slots_host ? slots_host[b] : b;
+    if (m->host_pos[sl] < 1) p += "slot " + std::to_string(sl) + " holds no prompt; ";
+  }
+  if (!p.empty()) return fail(QD_ERR_INVALID_ARGUMENTS, p);
+  hipStream_t st = (hipStream_t)stream;
+  const Plan& P = m->P;
+  QDCHK(stage_wait(m));
+  unsigned long long* hs = stage_seeds(m);
+  std::memcpy(hs, seeds_host, (size_t)B * 8);
+  unsigned long long* ds = m->ws<unsigned long long>(P.seeds);
+  HIPCHK(hipMemcpyAsync(ds, hs, (size_t)B * 8, hipMemcpyHostToDevice, st));
+  const int* row_slot = nullptr;
+  if (slots_host) {
+    int* hsl = stage_slots(m);
+    std::memcpy(hsl, slots_host, (size_t)B * 4);
+    int* dsl = m->ws<int>(P.slot_map);
+    HIPCHK(hipMemcpyAsync(dsl, hsl, (size_t)B * 4, hipMemcpyHostToDevice, st));
+    row_slot = dsl;
+  }
+  QDCHK(stage_mark(m, st));
+  SampleArgs a{};
+  a.logits = logits_dev; a.ldl = m->d.V;
+  a.z = m->ws<float>(P.samp_z);
+  a.counts = m->ws<int>(P.tok_counts);
+  a.row_slot = row_slot;
+  a.draws = m->ws<int>(P.draws);
+  a.seeds = ds;
+  a.next_ids = next_ids_dev;
+  a.V = m->d.V; a.top_k = q.top_k;
+  a.temperature = q.temperature; a.min_p = q.min_p; a.top_p = q.top_p;
+  a.repeat_penalty = q.repeat_penalty; a.presence_penalty = q.presence_penalty;
+  a.frequency_penalty = q.frequency_penalty;
+  HIPCHK(launch_sample(a, B, st));
+  return QD_OK;
 }
 
 qd_status qd_generate_greedy(qd_model* m, int32_t B, const int32_t* prompt_ids_host,

@@ -204,7 +204,8 @@ hipError_t launch_quantize_rows(const float* w, int rows, int cols, int8_t* q, f
 hipError_t launch_rope_table(float2* tab, int max_ctx, int D, float theta, hipStream_t st);
 hipError_t launch_fill_i32(int* p, int n, int v, hipStream_t st);
 hipError_t launch_embed(const int* ids, int M, const int8_t* E, const float* Es, int d, int V,
-                        bf16_t* x, hipStream_t st);
+                        bf16_t* x, hipStream_t st, int* counts = nullptr,
+                        const int* row_slot = nullptr);
 hipError_t launch_rmsnorm(const bf16_t* x, int M, int d, const float* g, float eps, bf16_t* y,
                           hipStream_t st);
 hipError_t launch_gemv(const GemvArgs& a, int epi, hipStream_t st);
@@ -220,6 +221,23 @@ hipError_t launch_resid_norm(bf16_t* x, int M, int d, const float* part, int spl
                              const float* scale, const float* g, float eps, bf16_t* y,
                              hipStream_t st);
 hipError_t launch_qk_rope(const RopeArgs& a, hipStream_t st);
+
+// ---- sampled decode: one work-group per logits row ----------------------------------------
+constexpr int SMP_MAXK = 1024;  // largest top_k the device sampler takes
+struct SampleArgs {
+  const float* logits; int ldl;     // [B][ldl] fp32 logits
+  float* z;                         // scratch [B][V]: penalized, tempered logits
+  const int* counts;                // [slots][V] occurrences of each token in the sequence
+  const int* row_slot;              // [B] KV slot of row b (NULL: slot b)
+  int* draws;                       // [slots] draws so far (the Philox counter)
+  const unsigned long long* seeds;  // [B] Philox key of each row's sequence
+  int* next_ids;                    // [B] drawn ids out
+  int V, top_k;
+  float temperature, min_p, top_p, repeat_penalty, presence_penalty, frequency_penalty;
+};
+hipError_t launch_sample(const SampleArgs& a, int B, hipStream_t st);
+// zeroes counts[slot][:] and draws[slot] for slots[0..n) (NULL: slots 0..n-1)
+hipError_t launch_reset_seq(int* counts, int* draws, const int* slots, int n, int V, hipStream_t st);
 hipError_t launch_attention_decode(const AttnDecArgs& a, hipStream_t st);
 hipError_t launch_flash_prefill(const FlashArgs& a, int n_tiles, hipStream_t st);
 hipError_t launch_set_positions(int* pos, const int* lens, const int* slots, int n, hipStream_t st);

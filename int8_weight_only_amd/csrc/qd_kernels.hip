@@ -67,12 +67,16 @@ __global__ void k_set_positions(int* pos, const int* lens, const int* slots, int
 // embedding gather: x = bf16(code * row scale), product in fp32
 // (ids outside [0, V) are clamped into range so a bad id can never read out of bounds;
 // the host validates ids wherever it sees them)
+// With `counts`, the token is also counted for its sequence (the sampler's penalties):
+// counts[slot][t] += 1, slot = row_slot[r] (NULL: r).
 __global__ __launch_bounds__(256) void k_embed(const int* __restrict__ ids,
                                                const int8_t* __restrict__ E,
                                                const float* __restrict__ Es, int d, int V,
-                                               bf16_t* __restrict__ x) {
+                                               bf16_t* __restrict__ x, int* counts,
+                                               const int* row_slot) {
   const int r = blockIdx.x;
   const int t = min(max(ids[r], 0), V - 1);
+  if (counts && threadIdx.x == 0) atomicAdd(counts + (size_t)(row_slot ? row_slot[r] : r) * V + t, 1);
   const float s = Es[t];
   const int8_t* er = E + (size_t)t * d;
   for (int c = threadIdx.x; c < d; c += 256) x[(size_t)r * d + c] = f2bf((float)er[c] * s);
@@ -2055,8 +2059,8 @@ hipError_t launch_iota(int* p, int n, hipStream_t st) {
 }
 
 hipError_t launch_embed(const int* ids, int M, const int8_t* E, const float* Es, int d, int V,
-                        bf16_t* x, hipStream_t st) {
-  hipLaunchKernelGGL(k_embed, dim3(M), dim3(256), 0, st, ids, E, Es, d, V, x);
+                        bf16_t* x, hipStream_t st, int* counts, const int* row_slot) {
+  hipLaunchKernelGGL(k_embed, dim3(M), dim3(256), 0, st, ids, E, Es, d, V, x, counts, row_slot);
   return hipGetLastError();
 }
 

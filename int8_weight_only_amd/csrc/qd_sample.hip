@@ -1,0 +1,218 @@
+// Sampled decode ("Model-agnostic LLM inference", section "Sampling"): the chain
+// repetition / presence / frequency penalties -> temperature -> top-k -> min-p -> top-p
+// -> seeded weighted draw, on the device, one work-group per logits row.
+//
+// Readings (the pages name the steps, not their formulas): counts are the occurrences of
+// each token in the sequence so far (prompt and every token fed since, counted by the
+// embedding kernel); a seen token's logit is divided by the repetition penalty when
+// positive and multiplied by it otherwise, then presence + frequency * count is
+// subtracted; the result is divided by the temperature.  Top-k keeps the k largest
+// (equal values: lower token id first).  Min-p keeps probabilities >= min_p times the
+// largest; top-p the shortest prefix of what is left whose mass reaches top_p of it.  The
+// draw takes u in [0, 1) from Philox4x64-10 (Salmon et al., SC 2011) with key (seed, 0)
+// and counter (n, 0, 0, 0), n = draws so far for the sequence, u = top 24 bits of the
+// first word times 2^-24, and picks the first candidate whose cumulative weight exceeds
+// u times the kept weight.
+//
+// The k-th largest value is found exactly by a radix select over an order-preserving
+// 32-bit key (one byte per pass, histograms in LDS); the candidates (every key >= that
+// value) are sorted in LDS by (value descending, id ascending); weights, min-p, top-p
+// and the draw are block-wide counts over a fixed-order prefix sum.
+#include "qd_common.h"
+#include "qd_device.h"
+
+namespace qd {
+
+namespace {
+constexpr int SMP_T = 1024;            // threads per row
+constexpr int SMP_CAND = 2 * SMP_MAXK;  // candidate list capacity (ties at the k-th value)
+
+// order-preserving key: larger value, larger key; -0.0 and +0.0 share a key
+__device__ __forceinline__ uint32_t fkey(float v) {
+  if (v == 0.0f) v = 0.0f;
+  const uint32_t u = __float_as_uint(v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// Philox4x64-10, first output word
+__device__ __forceinline__ unsigned long long philox_word0(unsigned long long c0,
+                                                           unsigned long long key0) {
+  const unsigned long long M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  const unsigned long long W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+  unsigned long long x0 = c0, x1 = 0, x2 = 0, x3 = 0, k0 = key0, k1 = 0;
+  for (int r = 0; r < 10; ++r) {
+    const unsigned long long hi0 = __umul64hi(M0, x0), lo0 = M0 * x0;
+    const unsigned long long hi1 = __umul64hi(M1, x2), lo1 = M1 * x2;
+    x0 = hi1 ^ x1 ^ k0;
+    x1 = lo1;
+    x2 = hi0 ^ x3 ^ k1;
+    x3 = lo0;
+    k0 += W0;
+    k1 += W1;
+  }
+  return x0;
+}
+
+// inclusive prefix sum over the block in thread order (fixed order: wave scans, then the
+// wave totals)
+__device__ __forceinline__ float block_scan(float v, float* wsum) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float t = __shfl_up(v, o, 64);
+    if (lane >= o) v += t;
+  }
+  if (lane == 63) wsum[wid] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float run = 0.0f;
+    for (int w = 0; w < SMP_T / 64; ++w) {
+      const float t = wsum[w];
+      wsum[w] = run;
+      run += t;
+    }
+  }
+  __syncthreads();
+  return v + wsum[wid];
+}
+}  // namespace
+
+__global__ __launch_bounds__(SMP_T) void k_sample(SampleArgs a) {
+  __shared__ unsigned int hist[256];
+  __shared__ unsigned long long cand[SMP_CAND];
+  __shared__ float cum_s[SMP_T];
+  __shared__ float wsum[SMP_T / 64];
+  __shared__ int sh_bin, sh_want, sh_n;
+  __shared__ float sh_u;
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int sl = a.row_slot ? a.row_slot[b] : b;
+  const int V = a.V;
+  const float* lg = a.logits + (size_t)b * a.ldl;
+  float* zr = a.z + (size_t)b * V;
+  const int* cr = a.counts + (size_t)sl * V;
+  const int k = min(a.top_k, V);
+  if (tid == 0) {
+    const unsigned long long w0 = philox_word0((unsigned long long)a.draws[sl], a.seeds[b]);
+    sh_u = (float)(unsigned int)(w0 >> 40) * 0x1.0p-24f;
+    sh_n = 0;
+  }
+  for (int i = tid; i < 256; i += SMP_T) hist[i] = 0u;
+  __syncthreads();
+  // penalties and temperature; histogram of the top key byte.  Each thread keeps the same
+  // elements in every pass, so it reads back only what it wrote.
+  for (int v = tid; v < V; v += SMP_T) {
+    float l = lg[v];
+    const int c = cr[v];
+    if (c > 0) {
+      l = l > 0.0f ? l / a.repeat_penalty : l * a.repeat_penalty;
+      l -= a.presence_penalty + a.frequency_penalty * (float)c;
+    }
+    const float z = l / a.temperature;
+    zr[v] = z;
+    atomicAdd(&hist[fkey(z) >> 24], 1u);
+  }
+  __syncthreads();
+  // radix select: the key of the k-th largest value, one byte per pass from the top;
+  // `want` ends as the number of elements equal to it that top-k keeps
+  uint32_t prefix = 0u;
+  int want = k;
+  for (int byte = 3; byte >= 0; --byte) {
+    if (byte < 3) {
+      for (int i = tid; i < 256; i += SMP_T) hist[i] = 0u;
+      __syncthreads();
+      const uint32_t hmask = 0xFFFFFFFFu << (8 * (byte + 1));
+      for (int v = tid; v < V; v += SMP_T) {
+        const uint32_t kk = fkey(zr[v]);
+        if ((kk & hmask) == prefix) atomicAdd(&hist[(kk >> (8 * byte)) & 0xFFu], 1u);
+      }
+      __syncthreads();
+    }
+    if (tid == 0) {
+      int cum = 0, bin = 255;
+      for (; bin > 0; --bin) {
+        if (cum + (int)hist[bin] >= want) break;
+        cum += (int)hist[bin];
+      }
+      sh_bin = bin;
+      sh_want = want - cum;
+    }
+    __syncthreads();
+    prefix |= (uint32_t)sh_bin << (8 * byte);
+    want = sh_want;
+    __syncthreads();
+  }
+  // candidates: every key >= the k-th key (ties included), as (key, ~id) for the sort
+  for (int v = tid; v < V; v += SMP_T) {
+    const uint32_t kk = fkey(zr[v]);
+    if (kk >= prefix) {
+      const int at = atomicAdd(&sh_n, 1);
+      if (at < SMP_CAND) cand[at] = ((unsigned long long)kk << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)v);
+    }
+  }
+  __syncthreads();
+  const int nc = min(sh_n, SMP_CAND);
+  int P = 2;
+  while (P < nc) P <<= 1;
+  for (int i = nc + tid; i < P; i += SMP_T) cand[i] = 0ull;
+  __syncthreads();
+  // bitonic sort, descending
+  for (int size = 2; size <= P; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < P / 2; i += SMP_T) {
+        const int lo = 2 * i - (i & (stride - 1));
+        const int hi = lo + stride;
+        const unsigned long long x = cand[lo], y = cand[hi];
+        const bool desc = (lo & size) == 0;
+        if (desc ? (x < y) : (x > y)) {
+          cand[lo] = y;
+          cand[hi] = x;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // weights relative to the largest, min-p, top-p and the draw over the first n
+  const int n = min(k, nc);
+  const float z0 = key_value((uint32_t)(cand[0] >> 32));
+  float w = 0.0f;
+  if (tid < n) w = expf(key_value((uint32_t)(cand[tid] >> 32)) - z0);
+  const int n_minp = __syncthreads_count(tid < n && w >= a.min_p);  // a prefix: w is non-increasing
+  const float c = block_scan(tid < n_minp ? w : 0.0f, wsum);
+  cum_s[tid] = c;
+  __syncthreads();
+  const float kept = cum_s[n_minp - 1];
+  const int below = __syncthreads_count(tid < n_minp && c < a.top_p * kept);
+  const int n_topp = min(below + 1, n_minp);
+  const float t = sh_u * cum_s[n_topp - 1];
+  const int pick = min(__syncthreads_count(tid < n_topp && c <= t), n_topp - 1);
+  if (tid == 0) {
+    a.next_ids[b] = (int)(0xFFFFFFFFu - (uint32_t)(cand[pick] & 0xFFFFFFFFull));
+    a.draws[sl] += 1;
+  }
+}
+
+// clears the token counts and draw numbers of the slots a prefill is about to fill
+__global__ __launch_bounds__(256) void k_reset_seq(int* counts, int* draws, const int* slots, int V) {
+  const int sl = slots ? slots[blockIdx.y] : blockIdx.y;
+  int* cr = counts + (size_t)sl * V;
+  for (int v = blockIdx.x * 1024 + threadIdx.x; v < min(V, (blockIdx.x + 1) * 1024); v += 256) cr[v] = 0;
+  if (blockIdx.x == 0 && threadIdx.x == 0) draws[sl] = 0;
+}
+
+hipError_t launch_reset_seq(int* counts, int* draws, const int* slots, int n, int V, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_reset_seq, dim3((V + 1023) / 1024, n), dim3(256), 0, st, counts, draws, slots, V);
+  return hipGetLastError();
+}
+
+hipError_t launch_sample(const SampleArgs& a, int B, hipStream_t st) {
+  if (B <= 0) return hipSuccess;
+  if (a.top_k < 1 || a.top_k > SMP_MAXK) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_sample, dim3(B), dim3(SMP_T), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace qd

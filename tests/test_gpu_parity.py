@@ -426,3 +426,115 @@ def test_continuous_batching_slots_teacher_forced():
         assert step == need  # the refused calls changed nothing on the host side
     finally:
         m.close()
+
+
+SAMPLING = dict(temperature=0.8, top_k=40, min_p=0.05, top_p=0.9, repeat_penalty=1.3,
+                presence_penalty=0.2, frequency_penalty=0.1)
+
+
+def _safe_margins(logits, counts, p, u, tol=1e-5):
+    """True when no decision of the oracle's draw sits within ``tol`` (relative) of a
+    boundary, so fp32 and fp64 arithmetic must agree on the token."""
+    from oracle.sampling import penalize, sample_token
+    tok, d = sample_token(logits, counts, p, u, detail=True)
+    z = np.sort(penalize(logits, counts, p) / p.temperature)[::-1]
+    if z.size > p.top_k and z[p.top_k - 1] - z[p.top_k] <= tol * max(1.0, abs(z[p.top_k])):
+        return tok, False
+    w = d["w"]
+    if np.min(np.abs(w - p.min_p)) <= tol:
+        return tok, False
+    cum = d["cum"]
+    if np.min(np.abs(cum - p.top_p * cum[-1])) <= tol * cum[-1]:
+        return tok, False
+    if np.min(np.abs(cum[: d["n_topp"]] - d["t"])) <= tol * cum[-1]:
+        return tok, False
+    return tok, True
+
+
+def test_device_sampler_matches_oracle_on_its_own_logits():
+    """The sampling chain ("Model-agnostic LLM inference", section "Sampling") on the
+    device against the oracle's, both fed the GPU's fp32 logits, the token counts of
+    each sequence and the Philox draw for its seed: the drawn ids must agree wherever no
+    decision sits within 1e-5 of a boundary (fp32 against fp64)."""
+    from oracle.sampling import SamplingParams, draw_uniform
+    shape = TINY
+    w = make_weights(shape, seed=8, gains="uniform")
+    B = 3
+    prompts = [make_prompt(shape.vocab, 9 + 3 * b, 7000 + b) for b in range(B)]
+    seeds = [11, 2 ** 63 + 5, 33]
+    p = SamplingParams(**SAMPLING)
+    say("[gpu] device sampler vs oracle sampler")
+    m = _model(shape, w, max_batch=B, max_ctx=64, max_prefill_tokens=64)
+    try:
+        counts = [np.bincount(pr, minlength=shape.vocab) for pr in prompts]
+        _, lg = m.prefill(prompts, logits=True)
+        checked = total = 0
+        for step in range(10):
+            ids = m.sample(lg, seeds, **SAMPLING)
+            torch.cuda.synchronize()
+            got = ids.cpu().numpy()
+            rows = lg.cpu().numpy().astype(np.float64)
+            for b in range(B):
+                want, safe = _safe_margins(rows[b], counts[b], p, draw_uniform(seeds[b], step))
+                total += 1
+                if safe:
+                    checked += 1
+                    assert got[b] == want, f"row {b} step {step}: device {got[b]} oracle {want}"
+                counts[b][got[b]] += 1
+            _, lg = m.decode_step(ids, logits=True)
+        say(f"[gpu] sampler: {checked}/{total} draws clear of every boundary, all equal")
+        assert checked >= 0.8 * total
+    finally:
+        m.close()
+
+
+def test_top_k_one_sampling_is_the_greedy_sequence(tiny_setup):
+    """top_k = 1 at any temperature reproduces the greedy sequence exactly (the pages'
+    stated property of the sampling chain)."""
+    shape, w, qm, m = tiny_setup
+    prompt = make_prompt(shape.vocab, 11, 7100)
+    greedy = m.generate_greedy([prompt], 10).generated[0]
+    for T in (0.3, 2.0):
+        _, lg = m.prefill([prompt], logits=True)
+        got = []
+        for _ in range(10):
+            ids = m.sample(lg, [1234], temperature=T, top_k=1)
+            got.append(int(ids[0].item()))
+            _, lg = m.decode_step(ids, logits=True)
+        assert got == [int(x) for x in greedy], (T, got, greedy)
+
+
+def test_sampling_repeats_with_the_seed_in_any_slot():
+    """Same prompt, parameters and seed give the same tokens, whichever KV slot the
+    sequence occupies; another seed gives another sequence."""
+    shape = TINY
+    w = make_weights(shape, seed=9, gains="uniform")
+    prompt = make_prompt(shape.vocab, 10, 7200)
+    m = _model(shape, w, max_batch=4, max_ctx=64, max_prefill_tokens=64)
+
+    def run(slot, seed):
+        _, lg = m.prefill([prompt], logits=True, slots=[slot])
+        out = []
+        for _ in range(12):
+            ids = m.sample(lg, [seed], slots=[slot], temperature=1.5, top_k=200, top_p=0.98)
+            out.append(int(ids[0].item()))
+            _, lg = m.decode_step(ids, logits=True, slots=[slot])
+        return out
+
+    try:
+        a, b, c = run(0, 77), run(3, 77), run(1, 78)
+        assert a == b
+        assert a != c
+    finally:
+        m.close()
+
+
+def test_sampler_rejects_bad_parameters(tiny_setup):
+    import int8_weight_only_amd as qd
+    shape, w, qm, m = tiny_setup
+    _, lg = m.prefill([make_prompt(shape.vocab, 5, 7300)], logits=True)
+    for bad in (dict(temperature=0.0), dict(top_k=0), dict(top_k=1025), dict(min_p=1.5),
+                dict(top_p=0.0), dict(repeat_penalty=0.0)):
+        with pytest.raises(qd.QdError) as e:
+            m.sample(lg, [1], **bad)
+        assert e.value.code == "invalid_arguments", bad
