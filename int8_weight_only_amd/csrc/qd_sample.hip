@@ -14,8 +14,8 @@
 // first word times 2^-24, and picks the first candidate whose cumulative weight exceeds
 // u times the kept weight.
 //
-// The k-th largest value is found exactly by a radix select over an order-preserving
-// 32-bit key (one byte per pass, histograms in LDS); the candidates (every key >= that
+// The k-th largest value is found exactly by a radix select over the distance of an
+// order-preserving 32-bit key from the row's largest (histograms in LDS); the candidates (every key >= that
 // value) are sorted in LDS by (value descending, id ascending); weights, min-p, top-p
 // and the draw are block-wide counts over a fixed-order prefix sum.
 #include "qd_common.h"
@@ -56,6 +56,8 @@ __device__ __forceinline__ unsigned long long philox_word0(unsigned long long c0
   return x0;
 }
 
+constexpr int SMP_U = 16;  // elements per thread per loop trip (loads issued together)
+
 // inclusive prefix sum over the block in thread order (fixed order: wave scans, then the
 // wave totals)
 __device__ __forceinline__ float block_scan(float v, float* wsum) {
@@ -85,9 +87,11 @@ __global__ __launch_bounds__(SMP_T) void k_sample(SampleArgs a) {
   __shared__ unsigned long long cand[SMP_CAND];
   __shared__ float cum_s[SMP_T];
   __shared__ float wsum[SMP_T / 64];
-  __shared__ int sh_bin, sh_want, sh_n;
+  __shared__ uint32_t wmax[SMP_T / 64];
+  __shared__ int sh_bin, sh_want, sh_n, sh_total;
+  __shared__ uint32_t sh_maxk;
   __shared__ float sh_u;
-  const int b = blockIdx.x, tid = threadIdx.x;
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int sl = a.row_slot ? a.row_slot[b] : b;
   const int V = a.V;
   const float* lg = a.logits + (size_t)b * a.ldl;
@@ -99,57 +103,123 @@ __global__ __launch_bounds__(SMP_T) void k_sample(SampleArgs a) {
     sh_u = (float)(unsigned int)(w0 >> 40) * 0x1.0p-24f;
     sh_n = 0;
   }
-  for (int i = tid; i < 256; i += SMP_T) hist[i] = 0u;
-  __syncthreads();
-  // penalties and temperature; histogram of the top key byte.  Each thread keeps the same
-  // elements in every pass, so it reads back only what it wrote.
-  for (int v = tid; v < V; v += SMP_T) {
-    float l = lg[v];
-    const int c = cr[v];
-    if (c > 0) {
-      l = l > 0.0f ? l / a.repeat_penalty : l * a.repeat_penalty;
-      l -= a.presence_penalty + a.frequency_penalty * (float)c;
+  // penalties and temperature into the scratch row, and the row's largest key.  Each
+  // thread keeps the same elements in every pass, so it reads back only what it wrote.
+  uint32_t kmax = 0u;
+  for (int v0 = 0; v0 < V; v0 += SMP_U * SMP_T) {
+    float l[SMP_U];
+    int c[SMP_U];
+#pragma unroll
+    for (int u = 0; u < SMP_U; ++u) {  // clamped (valid) indices: every load goes out first
+      const int v = v0 + u * SMP_T + tid;
+      l[u] = lg[v < V ? v : 0];
+      c[u] = cr[v < V ? v : 0];
     }
-    const float z = l / a.temperature;
-    zr[v] = z;
-    atomicAdd(&hist[fkey(z) >> 24], 1u);
+#pragma unroll
+    for (int u = 0; u < SMP_U; ++u) {
+      const int v = v0 + u * SMP_T + tid;
+      float x = l[u];
+      if (c[u] > 0) {
+        x = x > 0.0f ? x / a.repeat_penalty : x * a.repeat_penalty;
+        x -= a.presence_penalty + a.frequency_penalty * (float)c[u];
+      }
+      const float z = x / a.temperature;
+      if (v < V) {
+        zr[v] = z;
+        kmax = max(kmax, fkey(z));
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
+  if (lane == 0) wmax[wid] = kmax;
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t mk = 0u;
+    for (int w = 0; w < SMP_T / 64; ++w) mk = max(mk, wmax[w]);
+    sh_maxk = mk;
   }
   __syncthreads();
-  // radix select: the key of the k-th largest value, one byte per pass from the top;
-  // `want` ends as the number of elements equal to it that top-k keeps
-  uint32_t prefix = 0u;
-  int want = k;
-  for (int byte = 3; byte >= 0; --byte) {
-    if (byte < 3) {
-      for (int i = tid; i < 256; i += SMP_T) hist[i] = 0u;
-      __syncthreads();
-      const uint32_t hmask = 0xFFFFFFFFu << (8 * (byte + 1));
-      for (int v = tid; v < V; v += SMP_T) {
-        const uint32_t kk = fkey(zr[v]);
-        if ((kk & hmask) == prefix) atomicAdd(&hist[(kk >> (8 * byte)) & 0xFFu], 1u);
+  const uint32_t maxk = sh_maxk;
+
+  // Radix select on the distance d = maxk - key (0 for the largest value) of the k-th
+  // largest: only elements near the top are counted, so the LDS histogram atomics rarely
+  // collide (the bulk of a logits row shares its top key bits).  First level: bins
+  // d >> s over d < 256 << s, s widened until k elements fall inside; then 8 bits a pass.
+  auto count_pass = [&](int shift, uint32_t match_shift, uint32_t match) {
+    for (int i = tid; i < 256; i += SMP_T) hist[i] = 0u;
+    __syncthreads();
+    for (int v0 = 0; v0 < V; v0 += SMP_U * SMP_T) {
+      float zz[SMP_U];
+#pragma unroll
+      for (int u = 0; u < SMP_U; ++u) {
+        const int v = v0 + u * SMP_T + tid;
+        zz[u] = zr[v < V ? v : 0];
       }
-      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < SMP_U; ++u) {
+        const int v = v0 + u * SMP_T + tid;
+        const uint32_t d = maxk - fkey(zz[u]);
+        const bool in = match_shift >= 32 ? (d >> shift) < 256u : (d >> match_shift) == match;
+        if (v < V && in) atomicAdd(&hist[(d >> shift) & 0xFFu], 1u);
+      }
     }
+    __syncthreads();
+  };
+  // the bin (from distance 0 up) holding the want-th element, and what is left of want
+  auto pick_bin = [&](int want_in) {
     if (tid == 0) {
-      int cum = 0, bin = 255;
-      for (; bin > 0; --bin) {
-        if (cum + (int)hist[bin] >= want) break;
+      int cum = 0, bin = 0;
+      for (; bin < 255; ++bin) {
+        if (cum + (int)hist[bin] >= want_in) break;
         cum += (int)hist[bin];
       }
       sh_bin = bin;
-      sh_want = want - cum;
+      sh_want = want_in - cum;
     }
     __syncthreads();
-    prefix |= (uint32_t)sh_bin << (8 * byte);
+  };
+  int s = 16;
+  for (;;) {
+    count_pass(s, 32u, 0u);
+    if (tid == 0) {
+      int t = 0;
+      for (int i = 0; i < 256; ++i) t += (int)hist[i];
+      sh_total = t;
+    }
+    __syncthreads();
+    if (sh_total >= k || s >= 24) break;  // at s = 24 every element is counted
+    s += 8;
+    __syncthreads();
+  }
+  pick_bin(k);
+  uint32_t dsel = (uint32_t)sh_bin << s;
+  int want = sh_want;
+  __syncthreads();
+  for (int shift = s - 8; shift >= 0; shift -= 8) {
+    count_pass(shift, (uint32_t)(shift + 8), dsel >> (shift + 8));
+    pick_bin(want);
+    dsel |= (uint32_t)sh_bin << shift;
     want = sh_want;
     __syncthreads();
   }
+  const uint32_t prefix = maxk - dsel;  // key of the k-th largest value
   // candidates: every key >= the k-th key (ties included), as (key, ~id) for the sort
-  for (int v = tid; v < V; v += SMP_T) {
-    const uint32_t kk = fkey(zr[v]);
-    if (kk >= prefix) {
+  for (int v0 = 0; v0 < V; v0 += SMP_U * SMP_T) {
+    float zz[SMP_U];
+#pragma unroll
+    for (int u = 0; u < SMP_U; ++u) {
+      const int v = v0 + u * SMP_T + tid;
+      zz[u] = zr[v < V ? v : 0];
+    }
+#pragma unroll
+    for (int u = 0; u < SMP_U; ++u) {
+    const int v = v0 + u * SMP_T + tid;
+    const uint32_t kk = fkey(zz[u]);
+    if (v < V && kk >= prefix) {
       const int at = atomicAdd(&sh_n, 1);
       if (at < SMP_CAND) cand[at] = ((unsigned long long)kk << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)v);
+    }
     }
   }
   __syncthreads();
