@@ -187,6 +187,42 @@ def time_generate(model, prompts, new, steps, warmup):
     return float(np.mean(dev)), float(np.mean(pre)), float(np.mean(dec)), wall / steps, res
 
 
+def time_cache_load(model, shape, max_batch, ctx, NP, load_s):
+    """The quantized load cache ("Model-agnostic LLM inference", section "The quantized
+    load cache"): wall time of a model load from fp32 host arrays (upload + quantize on
+    the GPU) against a restore from the cache file (read + gate + upload), and the file
+    size; the restored model's codes are compared with the loaded one's on two matrices."""
+    import hashlib
+    import tempfile
+    import torch
+    import int8_weight_only_amd as qd
+    digest = hashlib.sha256(b"bench weights: seed 0, N(0, 0.02^2)").digest()
+    d = tempfile.mkdtemp(prefix="qd_cache_")
+    path = os.path.join(d, "weights_i8.cache")
+    try:
+        model.save_cache(path, digest)
+        size = os.path.getsize(path)
+        t = time.time()
+        m2 = qd.Model(shape, None, max_batch=max_batch, max_ctx=ctx,
+                      max_prefill_tokens=max_batch * NP, cache_path=path, source_digest=digest)
+        torch.cuda.synchronize()
+        cache_s = time.time() - t
+        try:
+            for name, layer in (("embed", 0), ("down", shape.n_layers - 1)):
+                qa, sa = model.export_quantized(name, layer)
+                qb, sb = m2.export_quantized(name, layer)
+                assert np.array_equal(qa, qb) and np.array_equal(sa, sb), name
+        finally:
+            m2.close()
+    finally:
+        if os.path.exists(path):
+            os.remove(path)
+        os.rmdir(d)
+    log(f"[bench] load: fp32 + quantize {load_s:.2f}s, cache {cache_s:.2f}s ({size / 1e9:.3f} GB)")
+    return {"load_fp32_quantize_s": round(load_s, 3), "load_cache_s": round(cache_s, 3),
+            "cache_bytes": size}
+
+
 SAMPLED = dict(temperature=0.8, top_k=40, top_p=0.95, min_p=0.0, repeat_penalty=1.1)
 
 
@@ -270,6 +306,7 @@ def main():
     ap.add_argument("--no-oracle", action="store_true", help="skip parity gate and CPU baseline")
     ap.add_argument("--no-continuous", action="store_true", help="skip the continuous-batching line")
     ap.add_argument("--no-sampled", action="store_true", help="skip the sampled-decode lines")
+    ap.add_argument("--no-cache-timing", action="store_true", help="skip the load-cache line")
     ap.add_argument("--kernels-only", action="store_true",
                     help="no captured graphs and few dispatches: prefill prompt+new-2 tokens, "
                          "one decode step, then the per-kernel timing pass (for counter runs)")
@@ -311,7 +348,8 @@ def main():
     model = qd.Model(shape, w, max_batch=max_batch, max_ctx=ctx,
                      max_prefill_tokens=max_batch * (NP + NN if args.kernels_only else NP))
     torch.cuda.synchronize()
-    log(f"[bench] loaded + quantized on GPU in {time.time() - t:.1f}s")
+    load_s = time.time() - t
+    log(f"[bench] loaded + quantized on GPU in {load_s:.1f}s")
     prompts = make_prompts(shape.vocab, NP, B, seed0=1000)
     try:
         bar = bar_for(args.shape)[0]
@@ -343,6 +381,9 @@ def main():
         log(f"[bench] parity ok: {parity}")
     del w
 
+    load_line = {}
+    if not args.no_cache_timing:
+        load_line = time_cache_load(model, shape, max_batch, ctx, NP, load_s)
     step_us, pre_us, dec_us, wall, res = time_generate(model, prompts, NN, args.steps, args.warmup)
     value = B * NN / (step_us * 1e-6)
     decode_tok_s = B * (NN - 1) / (dec_us * 1e-6)
@@ -408,6 +449,7 @@ def main():
         "prefill_mfma_frac": round(pf * prefill_tok_s / NP / 1e12 / PEAK_BF16_TFLOPS, 4),
         "wall_ms_per_step_incl_host": round(wall * 1e3, 4),
         **extra,
+        **load_line,
         "parity": parity,
         "roofline": roofline,
         "cpu_baseline": cpu,

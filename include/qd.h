@@ -63,6 +63,9 @@ typedef enum {
   QD_ERR_BUFFER_TOO_SMALL = 5,
   /* A HIP runtime call failed, or no gfx950 device is present. */
   QD_ERR_DEVICE = 6,
+  /* The quantized weight cache is absent or fails its validity gate ("The quantized
+   * load cache"): load with qd_load_weights and write a fresh cache. */
+  QD_ERR_CACHE_MISS = 7,
 } qd_status;
 
 #define QD_MAX_CONTEXT 65536
@@ -156,6 +159,43 @@ qd_status qd_query_sizes(const qd_model_shape* shape, const qd_limits* limits, q
 qd_status qd_load_weights(const qd_model_shape* shape, const qd_limits* limits,
                           const qd_weights_f32* weights, const qd_buffers* buffers,
                           qd_stream stream, qd_model** out);
+
+/* Quantized load cache ("Model-agnostic LLM inference", section "The quantized load
+ * cache"): the exact post-quantization device bytes, restored instead of re-quantizing.
+ * File: a 128-byte little-endian header, then the payload.
+ *   header: char magic[8] = "QDI8WCV1"; uint32 version = 1; uint32 header_bytes = 128;
+ *           uint64 payload_bytes; uint32 dims[9] = hidden, n_layers, n_heads,
+ *           n_kv_heads, head_dim, intermediate, vocab, bit pattern of rms_eps, bit
+ *           pattern of rope_theta; uint8 source_digest[32]; uint8 payload_sha256[32];
+ *           uint8 pad[4].
+ *   payload: embedding codes [V, d] int8, embedding scales [V] fp32, final gain [d]
+ *           fp32, then per layer: q|k|v codes [H*D + 2*KV*D, d] and scales, O codes
+ *           [d, H*D] and scales, gate/up codes [2I, d] and scales (interleaved in blocks
+ *           of 16 rows: 16 gate rows, then the matching 16 up rows), down codes [d, I] and
+ *           scales, gains input [d], post-attention [d], q_norm [D], k_norm [D].
+ * The validity gate: magic, version, every dimension, the caller's 32-byte digest of the
+ * source checkpoint (e.g. SHA-256 of its manifest), the exact file length, and the
+ * SHA-256 of the payload.  Any mismatch returns QD_ERR_CACHE_MISS naming it, and the
+ * caller falls back to qd_load_weights + qd_save_cache. */
+
+/* Writes m's quantized weights to `path` (through `path`.tmp, then a rename).  Host
+ * memory: one payload-sized buffer.  Synchronizes `stream`. */
+qd_status qd_save_cache(qd_model* m, const char* path, const uint8_t* source_digest,
+                        qd_stream stream);
+
+/* As qd_load_weights, but the weights come from a cache file that passes the gate (the
+ * RoPE table and device state are rebuilt).  The caller's buffers as for qd_load_weights. */
+qd_status qd_load_cache(const qd_model_shape* shape, const qd_limits* limits, const char* path,
+                        const uint8_t* source_digest, const qd_buffers* buffers,
+                        qd_stream stream, qd_model** out);
+
+/* The gate alone, on the host (no GPU): QD_OK if `path` would load for this shape and
+ * digest, else QD_ERR_CACHE_MISS naming what differs. */
+qd_status qd_check_cache(const qd_model_shape* shape, const char* path,
+                         const uint8_t* source_digest);
+
+/* SHA-256 (FIPS 180-4) of n bytes of host memory into out32[32]. */
+qd_status qd_sha256(const void* data, uint64_t n, uint8_t* out32);
 
 /* Identifiers of quantized tensors for qd_export_quantized. */
 typedef enum {

@@ -4,7 +4,8 @@ The product is the C-ABI library ``libqd.so`` (include/qd.h) with hand-written H
 kernels; this package is its thin Python binding.
 """
 from .binding import (Model, GenerateResult, QdError, UnsupportedArchitectureError,
-                      check_shape, query_sizes, load_library, EXPORTS, LIB_PATH, MAX_CONTEXT)
+                      check_shape, query_sizes, load_library, EXPORTS, LIB_PATH, MAX_CONTEXT,
+                      sha256, check_cache)
 
 __all__ = ["Model", "GenerateResult", "QdError", "UnsupportedArchitectureError", "check_shape",
-           "query_sizes", "load_library", "EXPORTS", "LIB_PATH", "MAX_CONTEXT"]
+           "query_sizes", "load_library", "EXPORTS", "LIB_PATH", "MAX_CONTEXT", "sha256", "check_cache"]

@@ -25,6 +25,7 @@ STATUS_CODES = {
     4: "checkpoint_not_found",
     5: "buffer_too_small",
     6: "device_error",
+    7: "cache_miss",
 }
 TENSORS = {"embed": 0, "q": 1, "k": 2, "v": 3, "o": 4, "gate": 5, "up": 6, "down": 7}
 MAX_CONTEXT = 65536
@@ -89,7 +90,8 @@ class StatsC(ctypes.Structure):
 EXPORTS = ("qd_last_error", "qd_check_shape", "qd_query_sizes", "qd_load_weights",
            "qd_export_quantized", "qd_prefill", "qd_decode_step", "qd_generate_greedy",
            "qd_free", "qd_profile_kernels", "qd_set_tuning", "qd_prefill_slots",
-           "qd_decode_step_slots", "qd_sample")
+           "qd_decode_step_slots", "qd_sample", "qd_save_cache", "qd_load_cache",
+           "qd_check_cache", "qd_sha256")
 TUNING = {"attn_max_splits": 0, "attn_min_chunks": 1, "attn_waves": 2, "attn_merge_last": 3,
           "persistent": 4, "persist_splits": 5, "skinny_split": 6, "gemm_splits": 7, "attn_occupancy": 8, "skinny_norm": 9}
 PROF_KERNELS = ("embed", "qkv", "attn", "o", "gateup", "down", "lmhead")
@@ -133,6 +135,16 @@ def load_library(path: str = LIB_PATH):
     lib.qd_decode_step.argtypes = [vp, i32, vp, vp, vp, vp]
     lib.qd_prefill_slots.restype = i32
     lib.qd_prefill_slots.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp]
+    lib.qd_save_cache.restype = i32
+    lib.qd_save_cache.argtypes = [vp, ctypes.c_char_p, vp, vp]
+    lib.qd_load_cache.restype = i32
+    lib.qd_load_cache.argtypes = [ctypes.POINTER(ModelShapeC), ctypes.POINTER(LimitsC),
+                                  ctypes.c_char_p, vp, ctypes.POINTER(BuffersC), vp,
+                                  ctypes.POINTER(vp)]
+    lib.qd_check_cache.restype = i32
+    lib.qd_check_cache.argtypes = [ctypes.POINTER(ModelShapeC), ctypes.c_char_p, vp]
+    lib.qd_sha256.restype = i32
+    lib.qd_sha256.argtypes = [vp, ctypes.c_uint64, vp]
     lib.qd_sample.restype = i32
     lib.qd_sample.argtypes = [vp, i32, vp, ctypes.POINTER(SamplingC), vp, vp, vp, vp]
     lib.qd_decode_step_slots.restype = i32
@@ -165,6 +177,29 @@ def shape_struct(shape) -> ModelShapeC:
                        int(shape.vocab), float(shape.rms_eps), float(shape.rope_theta),
                        int(bool(getattr(shape, "tie_word_embeddings", True))),
                        int(bool(getattr(shape, "attention_bias", False))))
+
+
+def _digest(d):
+    d = bytes(d) if d is not None else b""
+    if len(d) != 32:
+        raise QdError(2, "source_digest must be 32 bytes")
+    return ctypes.create_string_buffer(d, 32)
+
+
+def sha256(data: bytes) -> bytes:
+    """SHA-256 of ``data`` computed by the library."""
+    load_library()
+    buf = ctypes.create_string_buffer(bytes(data), max(1, len(data)))
+    out = ctypes.create_string_buffer(32)
+    _check(_lib.qd_sha256(buf, len(data), out))
+    return out.raw
+
+
+def check_cache(shape, path: str, source_digest: bytes):
+    """The cache gate alone, on the host: raises QdError "cache_miss" naming the mismatch."""
+    load_library()
+    _check(_lib.qd_check_cache(ctypes.byref(shape_struct(shape)), str(path).encode(),
+                               _digest(source_digest)))
 
 
 def check_shape(shape):
@@ -206,8 +241,12 @@ class GenerateResult:
 class Model:
     """A loaded model: caller-owned device buffers plus the library handle."""
 
-    def __init__(self, shape, weights: dict, max_batch: int = 1, max_ctx: int = 512,
-                 max_prefill_tokens: int | None = None, device: str = "cuda:0"):
+    def __init__(self, shape, weights: dict | None, max_batch: int = 1, max_ctx: int = 512,
+                 max_prefill_tokens: int | None = None, device: str = "cuda:0",
+                 cache_path: str | None = None, source_digest: bytes | None = None):
+        """Quantizes ``weights`` (fp32 arrays) on the GPU, or, with ``weights=None``,
+        restores the quantized cache at ``cache_path`` written for ``source_digest``
+        (raises QdError code "cache_miss" when the cache fails its gate)."""
         lib = load_library()
         if not torch.cuda.is_available():
             raise QdError(6, "no GPU visible")
@@ -224,6 +263,18 @@ class Model:
             self.kvbuf = torch.empty(sizes["kv_bytes"], dtype=torch.uint8, device=self.device)
             self.wsbuf = torch.empty(sizes["workspace_bytes"], dtype=torch.uint8, device=self.device)
             keep = []
+            if weights is None:
+                bufs = BuffersC(self.wbuf.data_ptr(), self.wbuf.numel(), self.kvbuf.data_ptr(),
+                                self.kvbuf.numel(), self.wsbuf.data_ptr(), self.wsbuf.numel())
+                handle = ctypes.c_void_p()
+                st = torch.cuda.current_stream(self.device)
+                dg = _digest(source_digest)
+                _check(lib.qd_load_cache(ctypes.byref(self._shape_c), ctypes.byref(self._lim_c),
+                                         str(cache_path).encode(), dg, ctypes.byref(bufs),
+                                         _stream_handle(st), ctypes.byref(handle)))
+                st.synchronize()
+                self._h = handle
+                return
 
             def dev(a):
                 if a is None:
@@ -315,6 +366,11 @@ class Model:
             _check(_lib.qd_decode_step_slots(self._h, B, sl.ctypes.data, in_ids.data_ptr(), lg_ptr,
                                              nxt.data_ptr(), _stream_handle()))
         return nxt, lg
+
+    def save_cache(self, path: str, source_digest: bytes):
+        """Writes the quantized weights to ``path`` (the quantized load cache)."""
+        _check(_lib.qd_save_cache(self._h, str(path).encode(), _digest(source_digest),
+                                  _stream_handle()))
 
     def sample(self, logits, seeds, slots=None, temperature=1.0, top_k=40, min_p=0.0,
                top_p=1.0, repeat_penalty=1.0, presence_penalty=0.0, frequency_penalty=0.0):

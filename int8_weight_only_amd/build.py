@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libqd.so")
-SOURCES = ["qd_kernels.hip", "qd_persist.hip", "qd_sample.hip", "qd_api.hip"]
+SOURCES = ["qd_kernels.hip", "qd_persist.hip", "qd_sample.hip", "qd_api.hip", "qd_cache.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -25,7 +25,7 @@ FLAGS = [
 def build_library(verbose: bool = True) -> str:
     objs = []
     for src in SOURCES:
-        obj = os.path.join(CSRC, src.replace(".hip", ".o"))
+        obj = os.path.join(CSRC, os.path.splitext(src)[0] + ".o")
         cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)

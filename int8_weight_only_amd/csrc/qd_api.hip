@@ -10,6 +10,7 @@
 // characteristics").
 #include "qd.h"
 #include "qd_common.h"
+#include "qd_cache.h"
 
 #include <map>
 #include <string>
@@ -749,6 +750,111 @@ qd_status qd_query_sizes(const qd_model_shape* shape, const qd_limits* limits, q
   return QD_OK;
 }
 
+namespace {
+// checks the limits and caller buffers and creates the handle (no GPU work)
+qd_status open_model(const qd_model_shape* shape, const qd_limits* limits,
+                     const qd_buffers* bufs, qd_model** out, hipDeviceProp_t* prop) {
+  const Plan P = make_plan(*shape, *limits);
+  if (!bufs || !bufs->weights || !bufs->kv || !bufs->workspace)
+    return fail(QD_ERR_INVALID_ARGUMENTS, "a device buffer pointer is NULL");
+  std::string small;
+  if (bufs->weight_bytes < P.weight_bytes)
+    small += "weights " + std::to_string(bufs->weight_bytes) + " < " + std::to_string(P.weight_bytes) + "; ";
+  if (bufs->kv_bytes < P.kv_bytes)
+    small += "kv " + std::to_string(bufs->kv_bytes) + " < " + std::to_string(P.kv_bytes) + "; ";
+  if (bufs->workspace_bytes < P.ws_bytes)
+    small += "workspace " + std::to_string(bufs->workspace_bytes) + " < " + std::to_string(P.ws_bytes) + "; ";
+  if (!small.empty()) return fail(QD_ERR_BUFFER_TOO_SMALL, "buffers too small: " + small);
+  if ((((uintptr_t)bufs->weights) | ((uintptr_t)bufs->kv) | ((uintptr_t)bufs->workspace)) & 255)
+    return fail(QD_ERR_INVALID_ARGUMENTS, "device buffers must be 256-byte aligned");
+  int dev = 0;
+  HIPCHK(hipGetDevice(&dev));
+  HIPCHK(hipGetDeviceProperties(prop, dev));
+  if (std::strncmp(prop->gcnArchName, "gfx950", 6) != 0)
+    return fail(QD_ERR_DEVICE, std::string("device is ") + prop->gcnArchName + ", need gfx950");
+  qd_model* m = new qd_model();
+  m->shape = *shape;
+  m->lim = *limits;
+  m->d = dims_of(*shape);
+  m->P = P;
+  m->W = (char*)bufs->weights;
+  m->KVb = (char*)bufs->kv;
+  m->WS = (char*)bufs->workspace;
+  m->device = dev;
+  m->host_pos.assign(limits->max_batch, 0);
+  *out = m;
+  return QD_OK;
+}
+
+// everything after the weights are in place: RoPE table, device state, streams, staging
+qd_status finish_model(qd_model* m, const hipDeviceProp_t& prop, hipStream_t s) {
+  const Plan& P = m->P;
+  const Dims& d = m->d;
+  HIPCHK(launch_rope_table(m->w<float2>(P.rope), m->lim.max_ctx, d.D, m->shape.rope_theta, s));
+  HIPCHK(launch_fill_i32(m->ws<int>(P.pos), m->lim.max_batch, 0, s));
+  HIPCHK(launch_iota(m->ws<int>(P.slot_ident), m->lim.max_batch, s));
+  HIPCHK(launch_fill_i32(m->ws<int>(P.att_cnt), m->lim.max_batch * d.KV, 0, s));
+  HIPCHK(launch_fill_i32(m->ws<int>(P.sk_cnt), SKINNY_MAX_TILES, 0, s));
+  HIPCHK(launch_fill_i32(m->ws<int>(P.done), 16, 0, s));
+  HIPCHK(launch_fill_i32(m->ws<int>(P.step), 16, 0, s));
+  HIPCHK(hipStreamCreateWithFlags(&m->cap_stream, hipStreamNonBlocking));
+  m->hstage_ints = stage_ints(P, m->lim.max_batch);
+  HIPCHK(hipHostMalloc((void**)&m->hstage, m->hstage_ints * 4, hipHostMallocDefault));
+  HIPCHK(hipEventCreateWithFlags(&m->stage_ev, hipEventDisableTiming));
+  for (int i = 0; i < 3; ++i) HIPCHK(hipEventCreate(&m->ev[i]));
+  // persistent single-sequence decode: error flag and eligibility
+  HIPCHK(hipStreamSynchronize(s));
+  HIPCHK(hipMemset(m->ws<int>(P.perr), 0, 64));
+  HIPCHK(hipHostMalloc((void**)&m->herr, 64, hipHostMallocDefault));
+  *m->herr = 0;
+  HIPCHK(hipEventCreateWithFlags(&m->err_ev, hipEventDisableTiming));
+  m->persist_why = persist_problems(m, prop, &m->persist_nwg, &m->persist_lds);
+  m->persist_ok = m->persist_why.empty();
+  return QD_OK;
+}
+
+// the quantized regions of the weights arena, in cache order: (offset, bytes)
+std::vector<std::pair<size_t, size_t>> cache_regions(const qd_model* m) {
+  const Plan& P = m->P;
+  const Dims& d = m->d;
+  std::vector<std::pair<size_t, size_t>> r;
+  r.push_back({P.emb_q, (size_t)d.V * d.d});
+  r.push_back({P.emb_s, (size_t)d.V * 4});
+  r.push_back({P.final_g, (size_t)d.d * 4});
+  for (int l = 0; l < d.L; ++l) {
+    const LayerOff& o = P.L[l];
+    r.push_back({o.qkv_q, (size_t)d.NQKV * d.d});
+    r.push_back({o.qkv_s, (size_t)d.NQKV * 4});
+    r.push_back({o.o_q, (size_t)d.d * d.HD});
+    r.push_back({o.o_s, (size_t)d.d * 4});
+    r.push_back({o.gu_q, (size_t)2 * d.I * d.d});
+    r.push_back({o.gu_s, (size_t)2 * d.I * 4});
+    r.push_back({o.dn_q, (size_t)d.d * d.I});
+    r.push_back({o.dn_s, (size_t)d.d * 4});
+    r.push_back({o.in_g, (size_t)d.d * 4});
+    r.push_back({o.post_g, (size_t)d.d * 4});
+    r.push_back({o.qn_g, (size_t)d.D * 4});
+    r.push_back({o.kn_g, (size_t)d.D * 4});
+  }
+  return r;
+}
+
+CacheHeader cache_header_for(const qd_model_shape& s, const uint8_t digest[32], uint64_t payload) {
+  CacheHeader h;
+  std::memset(&h, 0, sizeof(h));
+  std::memcpy(h.magic, "QDI8WCV1", 8);
+  h.version = 1;
+  h.header_bytes = sizeof(CacheHeader);
+  const int32_t v[7] = {s.hidden, s.n_layers, s.n_heads, s.n_kv_heads, s.head_dim, s.intermediate, s.vocab};
+  for (int i = 0; i < 7; ++i) h.dims[i] = (uint32_t)v[i];
+  std::memcpy(&h.dims[7], &s.rms_eps, 4);
+  std::memcpy(&h.dims[8], &s.rope_theta, 4);
+  std::memcpy(h.source_digest, digest, 32);
+  h.payload_bytes = payload;
+  return h;
+}
+}  // namespace
+
 qd_status qd_load_weights(const qd_model_shape* shape, const qd_limits* limits,
                           const qd_weights_f32* wts, const qd_buffers* bufs, qd_stream stream,
                           qd_model** out) {
@@ -779,37 +885,10 @@ qd_status qd_load_weights(const qd_model_shape* shape, const qd_limits* limits,
     }
   }
   if (!missing.empty()) return fail(QD_ERR_CHECKPOINT_NOT_FOUND, "missing tensors: " + missing);
-  const Plan P = make_plan(*shape, *limits);
-  if (!bufs || !bufs->weights || !bufs->kv || !bufs->workspace)
-    return fail(QD_ERR_INVALID_ARGUMENTS, "a device buffer pointer is NULL");
-  std::string small;
-  if (bufs->weight_bytes < P.weight_bytes)
-    small += "weights " + std::to_string(bufs->weight_bytes) + " < " + std::to_string(P.weight_bytes) + "; ";
-  if (bufs->kv_bytes < P.kv_bytes)
-    small += "kv " + std::to_string(bufs->kv_bytes) + " < " + std::to_string(P.kv_bytes) + "; ";
-  if (bufs->workspace_bytes < P.ws_bytes)
-    small += "workspace " + std::to_string(bufs->workspace_bytes) + " < " + std::to_string(P.ws_bytes) + "; ";
-  if (!small.empty()) return fail(QD_ERR_BUFFER_TOO_SMALL, "buffers too small: " + small);
-  if ((((uintptr_t)bufs->weights) | ((uintptr_t)bufs->kv) | ((uintptr_t)bufs->workspace)) & 255)
-    return fail(QD_ERR_INVALID_ARGUMENTS, "device buffers must be 256-byte aligned");
-
-  int dev = 0;
-  HIPCHK(hipGetDevice(&dev));
   hipDeviceProp_t prop;
-  HIPCHK(hipGetDeviceProperties(&prop, dev));
-  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
-    return fail(QD_ERR_DEVICE, std::string("device is ") + prop.gcnArchName + ", need gfx950");
-
-  qd_model* m = new qd_model();
-  m->shape = *shape;
-  m->lim = *limits;
-  m->d = dims_of(*shape);
-  m->P = P;
-  m->W = (char*)bufs->weights;
-  m->KVb = (char*)bufs->kv;
-  m->WS = (char*)bufs->workspace;
-  m->device = dev;
-  m->host_pos.assign(limits->max_batch, 0);
+  qd_model* m = nullptr;
+  QDCHK(open_model(shape, limits, bufs, &m, &prop));
+  const Plan& P = m->P;
   hipStream_t s = (hipStream_t)stream;
   auto cleanup_fail = [&](qd_status code) {
     qd_free(m);
@@ -841,30 +920,144 @@ qd_status qd_load_weights(const qd_model_shape* shape, const qd_limits* limits,
     LCHK(hipMemcpyAsync(m->w<float>(o.qn_g), L.q_norm, d.D * 4, hipMemcpyDeviceToDevice, s));
     LCHK(hipMemcpyAsync(m->w<float>(o.kn_g), L.k_norm, d.D * 4, hipMemcpyDeviceToDevice, s));
   }
-  LCHK(launch_rope_table(m->w<float2>(P.rope), limits->max_ctx, d.D, shape->rope_theta, s));
-  LCHK(launch_fill_i32(m->ws<int>(P.pos), limits->max_batch, 0, s));
-  LCHK(launch_iota(m->ws<int>(P.slot_ident), limits->max_batch, s));
-  LCHK(launch_fill_i32(m->ws<int>(P.att_cnt), limits->max_batch * d.KV, 0, s));
-  LCHK(launch_fill_i32(m->ws<int>(P.sk_cnt), SKINNY_MAX_TILES, 0, s));
-  LCHK(launch_fill_i32(m->ws<int>(P.done), 16, 0, s));
-  LCHK(launch_fill_i32(m->ws<int>(P.step), 16, 0, s));
-  LCHK(hipStreamCreateWithFlags(&m->cap_stream, hipStreamNonBlocking));
-  m->hstage_ints = stage_ints(P, limits->max_batch);
-  LCHK(hipHostMalloc((void**)&m->hstage, m->hstage_ints * 4, hipHostMallocDefault));
-  LCHK(hipEventCreateWithFlags(&m->stage_ev, hipEventDisableTiming));
-  for (int i = 0; i < 3; ++i) LCHK(hipEventCreate(&m->ev[i]));
-  // persistent single-sequence decode: error flag and eligibility
-  {
-    LCHK(hipStreamSynchronize(s));
-    LCHK(hipMemset(m->ws<int>(P.perr), 0, 64));
-    LCHK(hipHostMalloc((void**)&m->herr, 64, hipHostMallocDefault));
-    *m->herr = 0;
-    LCHK(hipEventCreateWithFlags(&m->err_ev, hipEventDisableTiming));
-    m->persist_why = persist_problems(m, prop, &m->persist_nwg, &m->persist_lds);
-    m->persist_ok = m->persist_why.empty();
-  }
 #undef LCHK
+  st = finish_model(m, prop, s);
+  if (st != QD_OK) return cleanup_fail(st);
   *out = m;
+  return QD_OK;
+}
+
+qd_status qd_save_cache(qd_model* m, const char* path, const uint8_t* source_digest,
+                        qd_stream stream) {
+  g_err.clear();
+  if (!m || !path || !source_digest) return fail(QD_ERR_INVALID_ARGUMENTS, "NULL argument");
+  HIPCHK(hipStreamSynchronize((hipStream_t)stream));
+  const auto regions = cache_regions(m);
+  uint64_t total = 0;
+  for (const auto& r : regions) total += r.second;
+  std::vector<uint8_t> payload(total);
+  uint64_t at = 0;
+  for (const auto& r : regions) {
+    HIPCHK(hipMemcpy(payload.data() + at, m->W + r.first, r.second, hipMemcpyDeviceToHost));
+    at += r.second;
+  }
+  CacheHeader h = cache_header_for(m->shape, source_digest, total);
+  Sha256 sha;
+  sha.update(payload.data(), payload.size());
+  sha.final(h.payload_sha256);
+  const std::string tmp = std::string(path) + ".tmp";
+  FILE* f = std::fopen(tmp.c_str(), "wb");
+  if (!f) return fail(QD_ERR_INVALID_ARGUMENTS, "cannot write " + tmp);
+  const bool ok = std::fwrite(&h, sizeof(h), 1, f) == 1 &&
+                  std::fwrite(payload.data(), 1, payload.size(), f) == payload.size();
+  const bool closed = std::fclose(f) == 0;
+  if (!ok || !closed || std::rename(tmp.c_str(), path) != 0) {
+    std::remove(tmp.c_str());
+    return fail(QD_ERR_INVALID_ARGUMENTS, std::string("writing the cache ") + path + " failed");
+  }
+  return QD_OK;
+}
+
+namespace {
+// reads and gates a cache file against a shape and source digest; payload out on success
+qd_status read_cache(const qd_model_shape* shape, const char* path, const uint8_t* digest,
+                     uint64_t expect_payload, std::vector<uint8_t>* payload) {
+  FILE* f = std::fopen(path, "rb");
+  if (!f) return fail(QD_ERR_CACHE_MISS, std::string("no cache at ") + path);
+  CacheHeader h;
+  std::memset(&h, 0, sizeof(h));
+  const size_t got = std::fread(&h, 1, sizeof(h), f);
+  std::string p;
+  if (got != sizeof(h)) p = "file shorter than the header";
+  else p = cache_header_problems(h, cache_header_for(*shape, digest, expect_payload));
+  if (p.empty()) {
+    std::fseek(f, 0, SEEK_END);
+    const long len = std::ftell(f);
+    if (len < 0 || (uint64_t)len != sizeof(h) + expect_payload)
+      p = "file length " + std::to_string(len) + " != " + std::to_string(sizeof(h) + expect_payload);
+  }
+  if (p.empty()) {
+    payload->resize(expect_payload);
+    std::fseek(f, (long)sizeof(h), SEEK_SET);
+    if (std::fread(payload->data(), 1, expect_payload, f) != expect_payload) p = "short read";
+  }
+  std::fclose(f);
+  if (p.empty()) {
+    uint8_t sum[32];
+    Sha256 sha;
+    sha.update(payload->data(), payload->size());
+    sha.final(sum);
+    if (std::memcmp(sum, h.payload_sha256, 32) != 0) p = "payload SHA-256 differs";
+  }
+  if (!p.empty()) return fail(QD_ERR_CACHE_MISS, std::string(path) + ": " + p);
+  return QD_OK;
+}
+}  // namespace
+
+qd_status qd_check_cache(const qd_model_shape* shape, const char* path, const uint8_t* source_digest) {
+  g_err.clear();
+  qd_status st = qd_check_shape(shape);
+  if (st != QD_OK) return st;
+  if (!path || !source_digest) return fail(QD_ERR_INVALID_ARGUMENTS, "NULL argument");
+  const qd_limits lim{1, 64, 64};
+  qd_model tmp;
+  tmp.shape = *shape;
+  tmp.d = dims_of(*shape);
+  tmp.P = make_plan(*shape, lim);
+  uint64_t total = 0;
+  for (const auto& r : cache_regions(&tmp)) total += r.second;
+  std::vector<uint8_t> payload;
+  return read_cache(shape, path, source_digest, total, &payload);
+}
+
+qd_status qd_load_cache(const qd_model_shape* shape, const qd_limits* limits, const char* path,
+                        const uint8_t* source_digest, const qd_buffers* bufs, qd_stream stream,
+                        qd_model** out) {
+  g_err.clear();
+  qd_status st = qd_check_shape(shape);
+  if (st != QD_OK) return st;
+  if ((st = check_limits(limits)) != QD_OK) return st;
+  if (!out || !path || !source_digest) return fail(QD_ERR_INVALID_ARGUMENTS, "NULL argument");
+  *out = nullptr;
+  hipDeviceProp_t prop;
+  qd_model* m = nullptr;
+  QDCHK(open_model(shape, limits, bufs, &m, &prop));
+  const auto regions = cache_regions(m);
+  uint64_t total = 0;
+  for (const auto& r : regions) total += r.second;
+  std::vector<uint8_t> payload;
+  st = read_cache(shape, path, source_digest, total, &payload);
+  if (st != QD_OK) {
+    const std::string msg = g_err;
+    qd_free(m);
+    g_err = msg;
+    return st;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  uint64_t at = 0;
+  for (const auto& r : regions) {
+    const hipError_t e = hipMemcpy(m->W + r.first, payload.data() + at, r.second, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      qd_free(m);
+      return fail(QD_ERR_DEVICE, std::string("hipMemcpy: ") + hipGetErrorString(e));
+    }
+    at += r.second;
+  }
+  st = finish_model(m, prop, s);
+  if (st != QD_OK) {
+    qd_free(m);
+    return st;
+  }
+  *out = m;
+  return QD_OK;
+}
+
+qd_status qd_sha256(const void* data, uint64_t n, uint8_t* out32) {
+  g_err.clear();
+  if ((!data && n) || !out32) return fail(QD_ERR_INVALID_ARGUMENTS, "NULL argument");
+  Sha256 sha;
+  sha.update(data, (size_t)n);
+  sha.final(out32);
   return QD_OK;
 }
 

@@ -19,7 +19,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def test_library_exports_every_declared_symbol():
     lib = qd.load_library()
     header = open(os.path.join(ROOT, "include", "qd.h")).read()
-    declared = set(re.findall(r"\b(qd_[a-z_]+)\s*\(", header))
+    declared = set(re.findall(r"\b(qd_[a-z0-9_]+)\s*\(", header))
     assert {"qd_load_weights", "qd_prefill", "qd_decode_step", "qd_generate_greedy",
             "qd_free"} <= declared
     for name in declared:

@@ -538,3 +538,49 @@ def test_sampler_rejects_bad_parameters(tiny_setup):
         with pytest.raises(qd.QdError) as e:
             m.sample(lg, [1], **bad)
         assert e.value.code == "invalid_arguments", bad
+
+
+def test_quantized_load_cache_round_trip(tmp_path):
+    """The quantized load cache ("Model-agnostic LLM inference", section "The quantized
+    load cache"): a model restored from the cache holds bit-identical codes and scales and
+    generates the identical greedy sequence; another checkpoint's digest or a damaged
+    file is refused with cache_miss."""
+    import hashlib
+    import int8_weight_only_amd as qd
+    shape = ODD
+    w = make_weights(shape, seed=10, gains="uniform")
+    digest = hashlib.sha256(b"odd checkpoint, seed 10").digest()
+    path = str(tmp_path / "weights_i8.cache")
+    say("[gpu] quantized load cache round trip")
+    a = _model(shape, w, max_batch=2, max_ctx=64, max_prefill_tokens=64)
+    try:
+        a.save_cache(path, digest)
+        b = _model(shape, None, max_batch=2, max_ctx=64, max_prefill_tokens=64,
+                   cache_path=path, source_digest=digest)
+        try:
+            for t in ("embed",) + tuple((n, l) for l in range(shape.n_layers)
+                                        for n in ("q", "k", "v", "o", "gate", "up", "down")):
+                name, layer = (t, 0) if isinstance(t, str) else t
+                qa, sa = a.export_quantized(name, layer)
+                qb, sb = b.export_quantized(name, layer)
+                np.testing.assert_array_equal(qa, qb)
+                np.testing.assert_array_equal(sa, sb)
+            prompt = make_prompt(shape.vocab, 13, 7400)
+            ga = a.generate_greedy([prompt], 12).generated
+            gb = b.generate_greedy([prompt], 12).generated
+            np.testing.assert_array_equal(ga, gb)
+        finally:
+            b.close()
+        with pytest.raises(qd.QdError) as e:
+            _model(shape, None, max_batch=2, max_ctx=64, max_prefill_tokens=64, cache_path=path,
+                   source_digest=hashlib.sha256(b"another checkpoint").digest())
+        assert e.value.code == "cache_miss"
+        raw = bytearray(open(path, "rb").read())
+        raw[-1] ^= 0xFF
+        open(path, "wb").write(bytes(raw))
+        with pytest.raises(qd.QdError) as e:
+            _model(shape, None, max_batch=2, max_ctx=64, max_prefill_tokens=64, cache_path=path,
+                   source_digest=digest)
+        assert e.value.code == "cache_miss" and "SHA-256" in str(e.value)
+    finally:
+        a.close()
