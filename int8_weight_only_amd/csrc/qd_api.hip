@@ -48,6 +48,7 @@ struct Plan {
   size_t ids = 0, row_slot = 0, row_pos = 0, last_rows = 0, lens = 0, slot_ident = 0, tiles = 0;
   size_t slot_map = 0;  // [max_batch] KV slot of each row of a slot-addressed call
   size_t tok_counts = 0, draws = 0, seeds = 0, samp_z = 0;  // sampler state and scratch
+  size_t smp_rowmax = 0, smp_hist = 0, smp_ncand = 0, smp_cand = 0;
   size_t pos = 0, next_ids = 0, lm_keys = 0, att_cnt = 0, sk_cnt = 0, done = 0, step = 0, out_ids = 0;
   size_t gemm_part = 0;
   // persistent single-sequence decode: exchange buffers, barrier words, error flag
@@ -183,6 +184,10 @@ Plan make_plan(const qd_model_shape& s, const qd_limits& lim) {
   P.draws = take((size_t)B * 4);
   P.seeds = take((size_t)B * 8);
   P.samp_z = take((size_t)B * d.V * 4);
+  P.smp_rowmax = take((size_t)B * 4);
+  P.smp_hist = take((size_t)B * 256 * 4);
+  P.smp_ncand = take((size_t)B * 4);
+  P.smp_cand = take((size_t)B * SMP_CAND_G * 8);
   P.pos = take((size_t)B * 4);
   P.next_ids = take((size_t)B * 4);
   P.lm_keys = take((size_t)B * LM_MAX_GRID * 8);
@@ -797,6 +802,9 @@ qd_status finish_model(qd_model* m, const hipDeviceProp_t& prop, hipStream_t s) 
   HIPCHK(launch_fill_i32(m->ws<int>(P.sk_cnt), SKINNY_MAX_TILES, 0, s));
   HIPCHK(launch_fill_i32(m->ws<int>(P.done), 16, 0, s));
   HIPCHK(launch_fill_i32(m->ws<int>(P.step), 16, 0, s));
+  HIPCHK(launch_fill_i32(m->ws<int>(P.smp_rowmax), m->lim.max_batch, 0, s));
+  HIPCHK(launch_fill_i32(m->ws<int>(P.smp_hist), m->lim.max_batch * 256, 0, s));
+  HIPCHK(launch_fill_i32(m->ws<int>(P.smp_ncand), m->lim.max_batch, 0, s));
   HIPCHK(hipStreamCreateWithFlags(&m->cap_stream, hipStreamNonBlocking));
   m->hstage_ints = stage_ints(P, m->lim.max_batch);
   HIPCHK(hipHostMalloc((void**)&m->hstage, m->hstage_ints * 4, hipHostMallocDefault));
@@ -1285,6 +1293,10 @@ qd_status qd_sample(qd_model* m, int32_t B, const int32_t* slots_host, const qd_
   a.temperature = q.temperature; a.min_p = q.min_p; a.top_p = q.top_p;
   a.repeat_penalty = q.repeat_penalty; a.presence_penalty = q.presence_penalty;
   a.frequency_penalty = q.frequency_penalty;
+  a.rowmax = m->ws<unsigned int>(P.smp_rowmax);
+  a.hist = m->ws<unsigned int>(P.smp_hist);
+  a.ncand = m->ws<int>(P.smp_ncand);
+  a.cand = m->ws<unsigned long long>(P.smp_cand);
   HIPCHK(launch_sample(a, B, st));
   return QD_OK;
 }

@@ -234,7 +234,13 @@ struct SampleArgs {
   int* next_ids;                    // [B] drawn ids out
   int V, top_k;
   float temperature, min_p, top_p, repeat_penalty, presence_penalty, frequency_penalty;
+  // per-row state of one call, zero on entry and cleared again by the call's last kernel
+  unsigned int* rowmax;             // [B] largest key of the row
+  unsigned int* hist;               // [B][256] distance histogram
+  int* ncand;                       // [B] gathered candidates
+  unsigned long long* cand;         // [B][SMP_CAND_G] gathered (key, ~id)
 };
+constexpr int SMP_CAND_G = 8192;
 hipError_t launch_sample(const SampleArgs& a, int B, hipStream_t st);
 // zeroes counts[slot][:] and draws[slot] for slots[0..n) (NULL: slots 0..n-1)
 hipError_t launch_reset_seq(int* counts, int* draws, const int* slots, int n, int V, hipStream_t st);

@@ -24,8 +24,9 @@
 namespace qd {
 
 namespace {
-constexpr int SMP_T = 1024;            // threads per row
-constexpr int SMP_CAND = 2 * SMP_MAXK;  // candidate list capacity (ties at the k-th value)
+constexpr int SMP_T = 1024;            // threads of the finishing work-group of a row
+constexpr int SMP_CAND = SMP_CAND_G;    // LDS candidate capacity (the gathered list)
+constexpr int SMP_CHUNK = 4096;         // row elements per streaming work-group
 
 // order-preserving key: larger value, larger key; -0.0 and +0.0 share a key
 __device__ __forceinline__ uint32_t fkey(float v) {
@@ -82,49 +83,38 @@ __device__ __forceinline__ float block_scan(float v, float* wsum) {
 }
 }  // namespace
 
-__global__ __launch_bounds__(SMP_T) void k_sample(SampleArgs a) {
-  __shared__ unsigned int hist[256];
-  __shared__ unsigned long long cand[SMP_CAND];
-  __shared__ float cum_s[SMP_T];
-  __shared__ float wsum[SMP_T / 64];
-  __shared__ uint32_t wmax[SMP_T / 64];
-  __shared__ int sh_bin, sh_want, sh_n, sh_total;
-  __shared__ uint32_t sh_maxk;
-  __shared__ float sh_u;
-  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+// ---- streaming passes: many work-groups per row -----------------------------------------
+
+// penalized, tempered logits of one chunk into the scratch row; the row's largest key
+__global__ __launch_bounds__(256) void k_smp_prep(SampleArgs a) {
+  __shared__ uint32_t wmax[4];
+  const int b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int sl = a.row_slot ? a.row_slot[b] : b;
   const int V = a.V;
   const float* lg = a.logits + (size_t)b * a.ldl;
   float* zr = a.z + (size_t)b * V;
   const int* cr = a.counts + (size_t)sl * V;
-  const int k = min(a.top_k, V);
-  if (tid == 0) {
-    const unsigned long long w0 = philox_word0((unsigned long long)a.draws[sl], a.seeds[b]);
-    sh_u = (float)(unsigned int)(w0 >> 40) * 0x1.0p-24f;
-    sh_n = 0;
-  }
-  // penalties and temperature into the scratch row, and the row's largest key.  Each
-  // thread keeps the same elements in every pass, so it reads back only what it wrote.
+  const int v_end = min(V, (int)(blockIdx.x + 1) * SMP_CHUNK);
   uint32_t kmax = 0u;
-  for (int v0 = 0; v0 < V; v0 += SMP_U * SMP_T) {
-    float l[SMP_U];
-    int c[SMP_U];
+  for (int v0 = blockIdx.x * SMP_CHUNK; v0 < v_end; v0 += 4 * 256) {
+    float l[4];
+    int c[4];
 #pragma unroll
-    for (int u = 0; u < SMP_U; ++u) {  // clamped (valid) indices: every load goes out first
-      const int v = v0 + u * SMP_T + tid;
-      l[u] = lg[v < V ? v : 0];
-      c[u] = cr[v < V ? v : 0];
+    for (int u = 0; u < 4; ++u) {  // clamped (valid) indices: every load goes out first
+      const int v = v0 + u * 256 + tid;
+      l[u] = lg[v < v_end ? v : 0];
+      c[u] = cr[v < v_end ? v : 0];
     }
 #pragma unroll
-    for (int u = 0; u < SMP_U; ++u) {
-      const int v = v0 + u * SMP_T + tid;
+    for (int u = 0; u < 4; ++u) {
+      const int v = v0 + u * 256 + tid;
       float x = l[u];
       if (c[u] > 0) {
         x = x > 0.0f ? x / a.repeat_penalty : x * a.repeat_penalty;
         x -= a.presence_penalty + a.frequency_penalty * (float)c[u];
       }
       const float z = x / a.temperature;
-      if (v < V) {
+      if (v < v_end) {
         zr[v] = z;
         kmax = max(kmax, fkey(z));
       }
@@ -134,21 +124,186 @@ __global__ __launch_bounds__(SMP_T) void k_sample(SampleArgs a) {
   for (int o = 32; o > 0; o >>= 1) kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
   if (lane == 0) wmax[wid] = kmax;
   __syncthreads();
-  if (tid == 0) {
-    uint32_t mk = 0u;
-    for (int w = 0; w < SMP_T / 64; ++w) mk = max(mk, wmax[w]);
-    sh_maxk = mk;
+  if (tid == 0) atomicMax(a.rowmax + b, max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3])));
+}
+
+// histogram of the key distance from the row's largest, d < 2^24, bins of 2^16
+__global__ __launch_bounds__(256) void k_smp_hist(SampleArgs a) {
+  __shared__ unsigned int h[256];
+  const int b = blockIdx.y, tid = threadIdx.x;
+  const int V = a.V;
+  const float* zr = a.z + (size_t)b * V;
+  h[tid] = 0u;
+  __syncthreads();
+  const uint32_t maxk = a.rowmax[b];
+  const int v_end = min(V, (int)(blockIdx.x + 1) * SMP_CHUNK);
+  for (int v0 = blockIdx.x * SMP_CHUNK; v0 < v_end; v0 += 4 * 256) {
+    float zz[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int v = v0 + u * 256 + tid;
+      zz[u] = zr[v < v_end ? v : 0];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int v = v0 + u * 256 + tid;
+      const uint32_t d = maxk - fkey(zz[u]);
+      if (v < v_end && d < (1u << 24)) atomicAdd(&h[d >> 16], 1u);
+    }
   }
   __syncthreads();
-  const uint32_t maxk = sh_maxk;
+  if (h[tid]) atomicAdd(a.hist + (size_t)b * 256 + tid, h[tid]);
+}
 
-  // Radix select on the distance d = maxk - key (0 for the largest value) of the k-th
-  // largest: only elements near the top are counted, so the LDS histogram atomics rarely
-  // collide (the bulk of a logits row shares its top key bits).  First level: bins
-  // d >> s over d < 256 << s, s widened until k elements fall inside; then 8 bits a pass.
-  auto count_pass = [&](int shift, uint32_t match_shift, uint32_t match) {
-    for (int i = tid; i < 256; i += SMP_T) hist[i] = 0u;
+// the bin of the k-th largest (from the histogram), then every element of this chunk at
+// that distance or closer into the row's candidate list (one counter update per wave)
+__global__ __launch_bounds__(256) void k_smp_gather(SampleArgs a) {
+  __shared__ unsigned int h[256];
+  __shared__ int sh_bin;
+  const int b = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+  const int V = a.V;
+  const int k = min(a.top_k, V);
+  h[tid] = a.hist[(size_t)b * 256 + tid];
+  __syncthreads();
+  if (tid == 0) {
+    int cum = 0, bin = 0;
+    for (; bin < 256; ++bin) {
+      cum += (int)h[bin];
+      if (cum >= k) break;
+    }
+    sh_bin = bin;  // 256: fewer than k values within 2^24 of the largest (k_sample selects)
+  }
+  __syncthreads();
+  const int b1 = sh_bin;
+  if (b1 >= 256) return;
+  const float* zr = a.z + (size_t)b * V;
+  const uint32_t maxk = a.rowmax[b];
+  unsigned long long* cg = a.cand + (size_t)b * SMP_CAND;
+  const int v_end = min(V, (int)(blockIdx.x + 1) * SMP_CHUNK);
+  for (int v0 = blockIdx.x * SMP_CHUNK; v0 < v_end; v0 += 4 * 256) {
+    float zz[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int v = v0 + u * 256 + tid;
+      zz[u] = zr[v < v_end ? v : 0];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int v = v0 + u * 256 + tid;
+      const uint32_t kk = fkey(zz[u]);
+      const uint32_t d = maxk - kk;
+      const bool in = v < v_end && d < (1u << 24) && (int)(d >> 16) <= b1;
+      const unsigned long long mask = __ballot(in);
+      if (mask) {
+        const int leader = __ffsll((long long)mask) - 1;
+        int base = 0;
+        if (lane == leader) base = atomicAdd(a.ncand + b, __popcll(mask));
+        base = __shfl(base, leader, 64);
+        const int at = base + __popcll(mask & ((1ull << lane) - 1ull));
+        if (in && at < SMP_CAND)
+          cg[at] = ((unsigned long long)kk << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)v);
+      }
+    }
+  }
+}
+
+// ---- one work-group per row: the top k, min-p, top-p, the draw ---------------------------
+__global__ __launch_bounds__(SMP_T) void k_sample(SampleArgs a) {
+  __shared__ unsigned int hist[256];
+  __shared__ unsigned long long cand[SMP_CAND];
+  __shared__ float cum_s[SMP_T];
+  __shared__ float wsum[SMP_T / 64];
+  __shared__ int sh_bin, sh_want, sh_n, sh_total;
+  __shared__ float sh_u;
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int sl = a.row_slot ? a.row_slot[b] : b;
+  const int V = a.V;
+  float* zr = a.z + (size_t)b * V;
+  const int k = min(a.top_k, V);
+  if (tid == 0) {
+    const unsigned long long w0 = philox_word0((unsigned long long)a.draws[sl], a.seeds[b]);
+    sh_u = (float)(unsigned int)(w0 >> 40) * 0x1.0p-24f;
+  }
+  if (tid < 256) hist[tid] = a.hist[(size_t)b * 256 + tid];
+  __syncthreads();
+  if (tid == 0) {
+    int t = 0;
+    for (int i = 0; i < 256; ++i) t += (int)hist[i];
+    sh_total = t;
+    sh_n = a.ncand[b];
+  }
+  __syncthreads();
+  const uint32_t maxk = a.rowmax[b];
+  const bool fast = sh_total >= k && sh_n <= SMP_CAND;
+  int nc;
+  if (fast) {
+    nc = sh_n;
+    const unsigned long long* cg = a.cand + (size_t)b * SMP_CAND;
+    for (int i = tid; i < nc; i += SMP_T) cand[i] = cg[i];
+  } else {
+    // exact radix select over the whole scratch row on the distance d = maxk - key of the
+    // k-th largest: bins of d >> s over d < 256 << s (s widened until k values fall
+    // inside), then 8 bits a pass
     __syncthreads();
+    if (tid == 0) sh_n = 0;
+    auto count_pass = [&](int shift, uint32_t match_shift, uint32_t match) {
+      if (tid < 256) hist[tid] = 0u;
+      __syncthreads();
+      for (int v0 = 0; v0 < V; v0 += SMP_U * SMP_T) {
+        float zz[SMP_U];
+#pragma unroll
+        for (int u = 0; u < SMP_U; ++u) {
+          const int v = v0 + u * SMP_T + tid;
+          zz[u] = zr[v < V ? v : 0];
+        }
+#pragma unroll
+        for (int u = 0; u < SMP_U; ++u) {
+          const int v = v0 + u * SMP_T + tid;
+          const uint32_t d = maxk - fkey(zz[u]);
+          const bool in = match_shift >= 32 ? (d >> shift) < 256u : (d >> match_shift) == match;
+          if (v < V && in) atomicAdd(&hist[(d >> shift) & 0xFFu], 1u);
+        }
+      }
+      __syncthreads();
+    };
+    auto pick_bin = [&](int want_in) {
+      if (tid == 0) {
+        int cum = 0, bin = 0;
+        for (; bin < 255; ++bin) {
+          if (cum + (int)hist[bin] >= want_in) break;
+          cum += (int)hist[bin];
+        }
+        sh_bin = bin;
+        sh_want = want_in - cum;
+      }
+      __syncthreads();
+    };
+    int s = 16;
+    for (;;) {
+      count_pass(s, 32u, 0u);
+      if (tid == 0) {
+        int t = 0;
+        for (int i = 0; i < 256; ++i) t += (int)hist[i];
+        sh_total = t;
+      }
+      __syncthreads();
+      if (sh_total >= k || s >= 24) break;  // at s = 24 every element is counted
+      s += 8;
+      __syncthreads();
+    }
+    pick_bin(k);
+    uint32_t dsel = (uint32_t)sh_bin << s;
+    int want = sh_want;
+    __syncthreads();
+    for (int shift = s - 8; shift >= 0; shift -= 8) {
+      count_pass(shift, (uint32_t)(shift + 8), dsel >> (shift + 8));
+      pick_bin(want);
+      dsel |= (uint32_t)sh_bin << shift;
+      want = sh_want;
+      __syncthreads();
+    }
+    const uint32_t prefix = maxk - dsel;  // key of the k-th largest value
+    // candidates: every key >= the k-th key (ties included), as (key, ~id) for the sort
     for (int v0 = 0; v0 < V; v0 += SMP_U * SMP_T) {
       float zz[SMP_U];
 #pragma unroll
@@ -159,71 +314,23 @@ __global__ __launch_bounds__(SMP_T) void k_sample(SampleArgs a) {
 #pragma unroll
       for (int u = 0; u < SMP_U; ++u) {
         const int v = v0 + u * SMP_T + tid;
-        const uint32_t d = maxk - fkey(zz[u]);
-        const bool in = match_shift >= 32 ? (d >> shift) < 256u : (d >> match_shift) == match;
-        if (v < V && in) atomicAdd(&hist[(d >> shift) & 0xFFu], 1u);
+        const uint32_t kk = fkey(zz[u]);
+        if (v < V && kk >= prefix) {
+          const int at = atomicAdd(&sh_n, 1);
+          if (at < SMP_CAND) cand[at] = ((unsigned long long)kk << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)v);
+        }
       }
     }
     __syncthreads();
-  };
-  // the bin (from distance 0 up) holding the want-th element, and what is left of want
-  auto pick_bin = [&](int want_in) {
-    if (tid == 0) {
-      int cum = 0, bin = 0;
-      for (; bin < 255; ++bin) {
-        if (cum + (int)hist[bin] >= want_in) break;
-        cum += (int)hist[bin];
-      }
-      sh_bin = bin;
-      sh_want = want_in - cum;
-    }
-    __syncthreads();
-  };
-  int s = 16;
-  for (;;) {
-    count_pass(s, 32u, 0u);
-    if (tid == 0) {
-      int t = 0;
-      for (int i = 0; i < 256; ++i) t += (int)hist[i];
-      sh_total = t;
-    }
-    __syncthreads();
-    if (sh_total >= k || s >= 24) break;  // at s = 24 every element is counted
-    s += 8;
-    __syncthreads();
-  }
-  pick_bin(k);
-  uint32_t dsel = (uint32_t)sh_bin << s;
-  int want = sh_want;
-  __syncthreads();
-  for (int shift = s - 8; shift >= 0; shift -= 8) {
-    count_pass(shift, (uint32_t)(shift + 8), dsel >> (shift + 8));
-    pick_bin(want);
-    dsel |= (uint32_t)sh_bin << shift;
-    want = sh_want;
-    __syncthreads();
-  }
-  const uint32_t prefix = maxk - dsel;  // key of the k-th largest value
-  // candidates: every key >= the k-th key (ties included), as (key, ~id) for the sort
-  for (int v0 = 0; v0 < V; v0 += SMP_U * SMP_T) {
-    float zz[SMP_U];
-#pragma unroll
-    for (int u = 0; u < SMP_U; ++u) {
-      const int v = v0 + u * SMP_T + tid;
-      zz[u] = zr[v < V ? v : 0];
-    }
-#pragma unroll
-    for (int u = 0; u < SMP_U; ++u) {
-    const int v = v0 + u * SMP_T + tid;
-    const uint32_t kk = fkey(zz[u]);
-    if (v < V && kk >= prefix) {
-      const int at = atomicAdd(&sh_n, 1);
-      if (at < SMP_CAND) cand[at] = ((unsigned long long)kk << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)v);
-    }
-    }
+    nc = min(sh_n, SMP_CAND);
   }
   __syncthreads();
-  const int nc = min(sh_n, SMP_CAND);
+  // the per-row state is read; clear it for the next call
+  if (tid < 256) a.hist[(size_t)b * 256 + tid] = 0u;
+  if (tid == 0) {
+    a.ncand[b] = 0;
+    a.rowmax[b] = 0u;
+  }
   int P = 2;
   while (P < nc) P <<= 1;
   for (int i = nc + tid; i < P; i += SMP_T) cand[i] = 0ull;
@@ -281,6 +388,10 @@ hipError_t launch_reset_seq(int* counts, int* draws, const int* slots, int n, in
 hipError_t launch_sample(const SampleArgs& a, int B, hipStream_t st) {
   if (B <= 0) return hipSuccess;
   if (a.top_k < 1 || a.top_k > SMP_MAXK) return hipErrorInvalidValue;
+  const dim3 g((a.V + SMP_CHUNK - 1) / SMP_CHUNK, B);
+  hipLaunchKernelGGL(k_smp_prep, g, dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_smp_hist, g, dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_smp_gather, g, dim3(256), 0, st, a);
   hipLaunchKernelGGL(k_sample, dim3(B), dim3(SMP_T), 0, st, a);
   return hipGetLastError();
 }

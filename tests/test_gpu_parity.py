@@ -451,7 +451,14 @@ def _safe_margins(logits, counts, p, u, tol=1e-5):
     return tok, True
 
 
-def test_device_sampler_matches_oracle_on_its_own_logits():
+# the second set keeps nearly the whole vocabulary: too many candidates lie far from the
+# largest logit, so the device sampler takes its whole-row select path
+SAMPLING_WIDE = dict(temperature=1.5, top_k=1000, min_p=0.0, top_p=0.95, repeat_penalty=1.1,
+                     presence_penalty=0.0, frequency_penalty=0.05)
+
+
+@pytest.mark.parametrize("params", [SAMPLING, SAMPLING_WIDE], ids=["top40", "top1000"])
+def test_device_sampler_matches_oracle_on_its_own_logits(params):
     """The sampling chain ("Model-agnostic LLM inference", section "Sampling") on the
     device against the oracle's, both fed the GPU's fp32 logits, the token counts of
     each sequence and the Philox draw for its seed: the drawn ids must agree wherever no
@@ -462,15 +469,15 @@ def test_device_sampler_matches_oracle_on_its_own_logits():
     B = 3
     prompts = [make_prompt(shape.vocab, 9 + 3 * b, 7000 + b) for b in range(B)]
     seeds = [11, 2 ** 63 + 5, 33]
-    p = SamplingParams(**SAMPLING)
-    say("[gpu] device sampler vs oracle sampler")
+    p = SamplingParams(**params)
+    say(f"[gpu] device sampler vs oracle sampler, top_k {params['top_k']}")
     m = _model(shape, w, max_batch=B, max_ctx=64, max_prefill_tokens=64)
     try:
         counts = [np.bincount(pr, minlength=shape.vocab) for pr in prompts]
         _, lg = m.prefill(prompts, logits=True)
         checked = total = 0
         for step in range(10):
-            ids = m.sample(lg, seeds, **SAMPLING)
+            ids = m.sample(lg, seeds, **params)
             torch.cuda.synchronize()
             got = ids.cpu().numpy()
             rows = lg.cpu().numpy().astype(np.float64)
