@@ -1421,7 +1421,9 @@ __global__ __launch_bounds__(256) void k_qk_rope(RopeArgs a) {
 // V tiles are requested one chunk ahead, the first ones before the prologue.  The four
 // waves merge in LDS at the end.  Fused behind: with several splits, each writes its
 // partial (max, sum, unnormalized output); the split that finishes last merges them.
-template <int D, int G, int NW>
+// WIDE: more than SB = 8 splits, merged by the batched path below (its own instantiation, so
+// the short-context kernel keeps its registers and LDS)
+template <int D, int G, int NW, bool WIDE>
 __global__ __launch_bounds__(64 * NW) void k_attn_dec(AttnDecArgs a) {
   constexpr int NT = 64 * NW;              // threads
   constexpr int CHW = 16 * NW;             // positions per iteration
@@ -1435,8 +1437,6 @@ __global__ __launch_bounds__(64 * NW) void k_attn_dec(AttnDecArgs a) {
   __shared__ float wm[NW][G], wl[NW][G];
   __shared__ float wo[NW][G][D];
   __shared__ int last_flag;
-  __shared__ float mw[G][ATT_MAX_SPLITS], mlv[G][ATT_MAX_SPLITS], hl[G];  // merge of the splits
-  __shared__ f32x4_t redm[NT > G * D / 4 ? NT : G * D / 4];
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   // wave index as a scalar: per-wave choices (which head, which gain vector) stay scalar
   const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1714,71 +1714,128 @@ __global__ __launch_bounds__(64 * NW) void k_attn_dec(AttnDecArgs a) {
   __syncthreads();
   if (!last_flag) return;
   // Every split's (max, sum) of the G heads is requested at once; a wave per head turns
-  // them into weights e^(m_s - m) and the total; the outputs are then summed over the
-  // splits in 16-byte agent-coherent loads, several splits in flight per thread, the split
+  // them into weights e^(m_s - m) and the total; the outputs are summed over the splits
+  // in 16-byte agent-coherent loads, several splits in flight per thread, the split
   // subsets of one output group added through LDS.  A long context (tens of splits)
-  // costs three memory round trips instead of one per split.
-  const int ns = a.nsplit;
-  {
-    const size_t base0 = ((size_t)b * a.H + (size_t)g * G) * ns;  // this row's G heads
-    for (int i = tid; i < G * ns; i += NT) {
-      mw[i / ns][i % ns] = __hip_atomic_load(a.part_ml + (base0 + i) * 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      mlv[i / ns][i % ns] = __hip_atomic_load(a.part_ml + (base0 + i) * 2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // costs two or three memory round trips instead of one per split.
+  constexpr int SB = 8;
+  if constexpr (!WIDE) {
+    // up to SB splits: each thread merges one output from every split's (max, sum,
+    // output), all requested at once (one memory round trip, no barrier)
+    const int ns = a.nsplit;
+    auto ld = [](const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+    for (int idx = tid; idx < G * D; idx += NT) {
+      const int h = idx / D, dd = idx % D;
+      const int head = g * G + h;
+      const size_t base = ((size_t)b * a.H + head) * ns;
+      float mv[SB], lv[SB], ov[SB];
+#pragma unroll
+      for (int k = 0; k < SB; ++k) {
+        mv[k] = k < ns ? ld(a.part_ml + (base + k) * 2) : -INFINITY;
+        lv[k] = k < ns ? ld(a.part_ml + (base + k) * 2 + 1) : 0.0f;
+        ov[k] = k < ns ? ld(a.part_o + (base + k) * D + dd) : 0.0f;
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < SB; ++k) mx = fmaxf(mx, mv[k]);
+      float lsum = 0.0f, acc = 0.0f;
+#pragma unroll
+      for (int k = 0; k < SB; ++k) {
+        if (mv[k] == -INFINITY) continue;
+        const float w = expf(mv[k] - mx);
+        lsum += lv[k] * w;
+        acc += ov[k] * w;
+      }
+      a.out[(size_t)b * a.ldo + (size_t)head * D + dd] = f2bf(acc / lsum);
     }
-  }
-  __syncthreads();
-  for (int h = wid; h < G; h += NW) {
-    float mx = -INFINITY;
-    for (int q = lane; q < ns; q += 64) mx = fmaxf(mx, mw[h][q]);
-    mx = wave_max(mx);
-    float ls = 0.0f;
-    for (int q = lane; q < ns; q += 64) {
-      const float m_s = mw[h][q];
-      const float w = m_s == -INFINITY ? 0.0f : expf(m_s - mx);
-      mw[h][q] = w;
-      ls += mlv[h][q] * w;
-    }
-    ls = wave_sum(ls);
-    if (lane == 0) hl[h] = ls;
-  }
-  __syncthreads();
-  {
+  } else {
+    __shared__ float mw[G][ATT_MAX_SPLITS], mlv[G][ATT_MAX_SPLITS], hl[G];
+    __shared__ f32x4_t redm[NT > G * D / 4 ? NT : G * D / 4];
+    const int ns = a.nsplit;
     constexpr int NG4 = G * D / 4;                  // 4-float output groups
     constexpr int SQ = NT >= NG4 ? NT / NG4 : 1;    // split subsets per group
     constexpr int UB = 8;                           // splits in flight per thread
-    f32x4_t* red = redm;  // [SQ][NG4]
     const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
         a.part_o + ((size_t)b * a.H + (size_t)g * G) * ns * D, 0, G * ns * D * 4, 0x00020000);
-    for (int e = tid; e < NG4 * SQ; e += NT) {
-      const int gi = e % NG4, sq = e / NG4;
+    // the first batch of this thread's first output group goes out before the (max, sum)
+    // pairs, so a short context (up to SQ * UB splits) costs one memory round trip
+    f32x4_t vf[UB];
+    {
+      const bool ok = tid < NG4 * SQ;
+      const int gi = tid % NG4, sq = tid / NG4;
       const int h = (4 * gi) / D, dd = (4 * gi) % D;
-      f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      for (int q0 = sq; q0 < ns; q0 += SQ * UB) {
-        f32x4_t v[UB];
 #pragma unroll
-        for (int u = 0; u < UB; ++u) {
-          const int q = q0 + u * SQ;
-          v[u] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                 ors, q < ns ? ((h * ns + q) * D + dd) * 4 : OOB, 0, 16));
-        }
-#pragma unroll
-        for (int u = 0; u < UB; ++u) {
-          const int q = q0 + u * SQ;
-          if (q < ns) acc += v[u] * mw[h][q];
-        }
+      for (int u = 0; u < UB; ++u) {
+        const int q = sq + u * SQ;
+        vf[u] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                ors, (ok && q < ns) ? ((h * ns + q) * D + dd) * 4 : OOB, 0, 16));
       }
-      red[sq * NG4 + gi] = acc;
+    }
+    {
+      const size_t base0 = ((size_t)b * a.H + (size_t)g * G) * ns;  // this row's G heads
+      for (int i = tid; i < G * ns; i += NT) {
+        mw[i / ns][i % ns] = __hip_atomic_load(a.part_ml + (base0 + i) * 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        mlv[i / ns][i % ns] = __hip_atomic_load(a.part_ml + (base0 + i) * 2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
     __syncthreads();
-    for (int gi = tid; gi < NG4; gi += NT) {
-      f32x4_t acc = red[gi];
-      for (int sq = 1; sq < SQ; ++sq) acc += red[sq * NG4 + gi];
-      const int h = (4 * gi) / D, dd = (4 * gi) % D;
-      const float lh = hl[h];
-      bf16_t* o = a.out + (size_t)b * a.ldo + (size_t)(g * G + h) * D + dd;
-      const uint32_t lo = (uint32_t)f2bf(acc[0] / lh) | ((uint32_t)f2bf(acc[1] / lh) << 16);
-      const uint32_t hi = (uint32_t)f2bf(acc[2] / lh) | ((uint32_t)f2bf(acc[3] / lh) << 16);
-      *reinterpret_cast<uint2*>(o) = make_uint2(lo, hi);
+    for (int h = wid; h < G; h += NW) {
+      float mx = -INFINITY;
+      for (int q = lane; q < ns; q += 64) mx = fmaxf(mx, mw[h][q]);
+      mx = wave_max(mx);
+      float ls = 0.0f;
+      for (int q = lane; q < ns; q += 64) {
+        const float m_s = mw[h][q];
+        const float w = m_s == -INFINITY ? 0.0f : expf(m_s - mx);
+        mw[h][q] = w;
+        ls += mlv[h][q] * w;
+      }
+      ls = wave_sum(ls);
+      if (lane == 0) hl[h] = ls;
+    }
+    __syncthreads();
+    {
+      f32x4_t* red = redm;  // [SQ][NG4]
+      for (int e = tid; e < NG4 * SQ; e += NT) {
+        const int gi = e % NG4, sq = e / NG4;
+        const int h = (4 * gi) / D, dd = (4 * gi) % D;
+        f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        int q0 = sq;
+        if (e == tid) {  // the batch requested up front
+#pragma unroll
+          for (int u = 0; u < UB; ++u) {
+            const int q = sq + u * SQ;
+            if (q < ns) acc += vf[u] * mw[h][q];
+          }
+          q0 += SQ * UB;
+        }
+        for (; q0 < ns; q0 += SQ * UB) {
+          f32x4_t v[UB];
+#pragma unroll
+          for (int u = 0; u < UB; ++u) {
+            const int q = q0 + u * SQ;
+            v[u] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   ors, q < ns ? ((h * ns + q) * D + dd) * 4 : OOB, 0, 16));
+          }
+#pragma unroll
+          for (int u = 0; u < UB; ++u) {
+            const int q = q0 + u * SQ;
+            if (q < ns) acc += v[u] * mw[h][q];
+          }
+        }
+        red[sq * NG4 + gi] = acc;
+      }
+      __syncthreads();
+      for (int gi = tid; gi < NG4; gi += NT) {
+        f32x4_t acc = red[gi];
+        for (int sq = 1; sq < SQ; ++sq) acc += red[sq * NG4 + gi];
+        const int h = (4 * gi) / D, dd = (4 * gi) % D;
+        const float lh = hl[h];
+        bf16_t* o = a.out + (size_t)b * a.ldo + (size_t)(g * G + h) * D + dd;
+        const uint32_t lo = (uint32_t)f2bf(acc[0] / lh) | ((uint32_t)f2bf(acc[1] / lh) << 16);
+        const uint32_t hi = (uint32_t)f2bf(acc[2] / lh) | ((uint32_t)f2bf(acc[3] / lh) << 16);
+        *reinterpret_cast<uint2*>(o) = make_uint2(lo, hi);
+      }
     }
   }
   if (tid == 0) __hip_atomic_store(a.counters + (size_t)b * a.KV + g, 0u, __ATOMIC_RELAXED,
@@ -2306,7 +2363,10 @@ hipError_t launch_qk_rope(const RopeArgs& a, hipStream_t st) {
 template <int D, int G, int NW>
 static void attn_dec_launch(const AttnDecArgs& a, dim3 grid, hipStream_t st) {
   constexpr int W = (NW == 8 && G * D > 512) ? 4 : NW;
-  hipLaunchKernelGGL((k_attn_dec<D, G, W>), grid, dim3(64 * W), 0, st, a);
+  if (a.nsplit > 8 && a.merge_last)
+    hipLaunchKernelGGL((k_attn_dec<D, G, W, true>), grid, dim3(64 * W), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_attn_dec<D, G, W, false>), grid, dim3(64 * W), 0, st, a);
 }
 
 template <int D, int NW>
