@@ -232,7 +232,7 @@ struct qd_model {
   char* WS = nullptr;  // workspace
   int device = 0;
   hipStream_t cap_stream = nullptr;
-  std::map<std::tuple<int, int, int>, hipGraphExec_t> graphs;  // (B, nsplit, split_len)
+  std::map<std::tuple<int, int, int, int>, hipGraphExec_t> graphs;  // (B, nsplit, split_len, steps)
   std::vector<int> host_pos;                                   // mirror of device positions
   hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
   // pinned host staging for prompt ids and prefill metadata: asynchronous uploads read
@@ -341,6 +341,8 @@ qd_status enqueue_lm_head(qd_model* m, const bf16_t* x, const int* x_rows, int r
   }
   return QD_OK;
 }
+
+constexpr int GEN_GRAPH_STEPS = 8;  // decode steps per captured graph in qd_generate_greedy
 
 // ---- the kernels of one decode step, for slots 0..B-1 (rows == slots) -------------------
 // work-groups per channel tile of a skinny projection: enough to cover the CUs and to
@@ -1357,24 +1359,36 @@ qd_status qd_generate_greedy(qd_model* m, int32_t B, const int32_t* prompt_ids_h
     // round the context up so one captured graph serves many calls
     const int ctx_cap = std::min(m->lim.max_ctx, ((need + 255) / 256) * 256);
     attn_split(ctx_cap, P.nsplit_cap, m->attn_max_splits, m->attn_min_chunks, attn_occupancy_for(m, B), B * m->d.KV, &nsplit, &split_len);
-    auto key = std::make_tuple(B, nsplit, split_len);
-    auto it = m->graphs.find(key);
-    hipGraphExec_t exec = nullptr;
-    if (it == m->graphs.end()) {
+    // decode steps replayed from captured graphs of GEN_GRAPH_STEPS consecutive steps (the
+    // positions and the step counter live on the device), the remainder one step each
+    auto graph_for = [&](int n, hipGraphExec_t* out) -> qd_status {
+      auto key = std::make_tuple(B, nsplit, split_len, n);
+      auto it = m->graphs.find(key);
+      if (it != m->graphs.end()) {
+        *out = it->second;
+        return QD_OK;
+      }
       hipGraph_t graph;
       HIPCHK(hipStreamBeginCapture(m->cap_stream, hipStreamCaptureModeThreadLocal));
-      qd_status cs = enqueue_decode(m, B, next_ids, nullptr, next_ids, true, nsplit, split_len,
-                                    m->cap_stream);
+      qd_status cs = QD_OK;
+      for (int i = 0; i < n && cs == QD_OK; ++i)
+        cs = enqueue_decode(m, B, next_ids, nullptr, next_ids, true, nsplit, split_len, m->cap_stream);
       hipError_t ee = hipStreamEndCapture(m->cap_stream, &graph);
       if (cs != QD_OK) return cs;
       if (ee != hipSuccess) return fail(QD_ERR_DEVICE, std::string("hipStreamEndCapture: ") + hipGetErrorString(ee));
+      hipGraphExec_t exec = nullptr;
       HIPCHK(hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0));
       HIPCHK(hipGraphDestroy(graph));
       m->graphs[key] = exec;
-    } else {
-      exec = it->second;
-    }
-    for (int i = 0; i < steps; ++i) HIPCHK(hipGraphLaunch(exec, st));
+      *out = exec;
+      return QD_OK;
+    };
+    const int multi = steps / GEN_GRAPH_STEPS, rest = steps % GEN_GRAPH_STEPS;
+    hipGraphExec_t gm = nullptr, g1 = nullptr;
+    if (multi) QDCHK(graph_for(GEN_GRAPH_STEPS, &gm));
+    if (rest) QDCHK(graph_for(1, &g1));
+    for (int i = 0; i < multi; ++i) HIPCHK(hipGraphLaunch(gm, st));
+    for (int i = 0; i < rest; ++i) HIPCHK(hipGraphLaunch(g1, st));
   }
   HIPCHK(hipEventRecord(m->ev[2], st));
   HIPCHK(hipMemcpy2DAsync(out_ids_host, (size_t)max_new_tokens * 4, m->ws<int>(P.out_ids),
