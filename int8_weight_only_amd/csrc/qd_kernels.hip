@@ -1602,19 +1602,35 @@ __global__ __launch_bounds__(64 * NW) void k_attn_dec(AttnDecArgs a) {
     const bool more = t0 + CHW < t_end;
     if (more) load_tiles(kx, vx, t0 + CHW);
     const bool valid = t < t_end;
-    float pr[G];
+    // The reference maximum m of a head moves (a wave reduction, and the rescale of o and
+    // l) only when a score exceeds it by more than TAU, so exp(z - m) <= e^TAU; otherwise
+    // the chunk costs one ballot.  l is kept per lane (its own positions) and summed over
+    // the wave once, after the last chunk.
+    constexpr float TAU = 8.0f;
+    float pr[G], zs[G];
+    bool need = false;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       sp[h] += __shfl_xor(sp[h], 1, 64);
       sp[h] += __shfl_xor(sp[h], 2, 64);
-      const float z = valid ? sp[h] * scale : -INFINITY;
-      const float mnew = fmaxf(m[h], wave_max(z));
-      const float alpha = (m[h] == -INFINITY) ? 0.0f : expf(m[h] - mnew);
-      pr[h] = valid ? expf(z - mnew) : 0.0f;
-      l[h] = l[h] * alpha + wave_sum(part == 0 ? pr[h] : 0.0f);
-      m[h] = mnew;
+      zs[h] = valid ? sp[h] * scale : -INFINITY;
+      need = need || (zs[h] > m[h] + TAU);
+    }
+    if (__any(need)) {
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) o[h][e] *= alpha;
+      for (int h = 0; h < G; ++h) {
+        const float mnew = fmaxf(m[h], wave_max(zs[h]));
+        const float alpha = (m[h] == -INFINITY) ? 0.0f : expf(m[h] - mnew);
+        l[h] *= alpha;
+        m[h] = mnew;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) o[h][e] *= alpha;
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      pr[h] = valid ? expf(zs[h] - m[h]) : 0.0f;
+      l[h] += part == 0 ? pr[h] : 0.0f;
     }
     // P*V: lanes over head dims, the wave's 16 positions in turn
 #pragma unroll
@@ -1651,6 +1667,8 @@ __global__ __launch_bounds__(64 * NW) void k_attn_dec(AttnDecArgs a) {
     }
   }
   // ---- merge the four waves' softmax states ----
+#pragma unroll
+  for (int h = 0; h < G; ++h) l[h] = wave_sum(l[h]);
   if (lane == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
