@@ -1925,37 +1925,25 @@ __global__ __launch_bounds__(128) void k_attn_dec_merge(AttnDecArgs a) {
 // Prefill attention on MFMA (causal, flash style).  A work-group owns up to 64 query rows
 // of one sequence (4 waves x 16 rows) and one query head h of KV group g = h / (H/KV).
 // Keys and values advance in blocks of 64 positions staged once in LDS for all waves
-// (V transposed so it feeds the MFMA B operand directly).  Per wave and block:
-// S = Q K^T (16 rows x 64 keys, fp32 accumulation of bf16 products), causal mask, online
-// softmax in fp32 with each row's state in the lanes that hold that row of O, then
-// O += P V.  P is split into bf16 high and low parts (two MFMAs), so the probabilities
-// enter the product with ~16 significant bits rather than bf16's 8.
-__device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, dpp_f<0xB1>(v, v));
-  v = fmaxf(v, dpp_f<0x4E>(v, v));
-  v = fmaxf(v, dpp_f<0x141>(v, v));
-  v = fmaxf(v, dpp_f<0x140>(v, v));
-  return v;
-}
-__device__ __forceinline__ float row16_sum(float v) {
-  v += dpp_f<0xB1>(0.0f, v);
-  v += dpp_f<0x4E>(0.0f, v);
-  v += dpp_f<0x141>(0.0f, v);
-  v += dpp_f<0x140>(0.0f, v);
-  return v;
-}
-
+// (V transposed).  Each wave computes the transposed products S^T = K Q^T and
+// O^T = V^T P^T, so a lane always holds one query row (its lane index mod 16): the MFMA
+// output layout of S^T is then already the B-operand layout P^T needs, P never leaves
+// registers, and a row's softmax state is one scalar per lane.  For that, the 16 rows of
+// the S^T tile t of a 32-key step are keys 8*(r/4) + 4t + r%4; K rows are stored in LDS in
+// that order (key 8a + 4t + i of a 32-key step at row 16t + 4a + i), so the fragment reads
+// stay on consecutive rows.  P is split into bf16 high and low parts (two MFMAs), so the
+// probabilities enter the product with ~16 significant bits rather than bf16's 8.
 template <int D>
-__global__ __launch_bounds__(256) void k_flash_prefill(FlashArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 3 : 1))) void k_flash_prefill(
+    FlashArgs a) {
   constexpr int KB = 64;             // keys per block
-  constexpr int NKT = KB / 16;       // 16-key tiles of S per block
+  constexpr int NKK = KB / 32;       // 32-key steps per block (two S^T tiles each)
   constexpr int KS = D / 32;         // MFMA k-steps over the head dim
-  constexpr int NT = D / 16;         // 16-dim output tiles
+  constexpr int NT = D / 16;         // 16-dim tiles of O^T
   constexpr int VPR = D / 8;         // uint4 per key row
   constexpr int LD_PER_T = (KB * VPR + 255) / 256;  // uint4 per thread per tensor and block
   __shared__ __align__(16) bf16_t Ks[KB][D + 8];
   __shared__ __align__(16) bf16_t Vt[D][KB + 8];
-  __shared__ __align__(16) bf16_t Ps[4][2][16][KB + 8];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int grp = lane >> 4, r16 = lane & 15;
   const int4 tile = a.tiles[blockIdx.x];
@@ -1965,31 +1953,29 @@ __global__ __launch_bounds__(256) void k_flash_prefill(FlashArgs a) {
   const bf16_t* Vb = a.vcache + ((size_t)slot * a.KV + g) * a.max_ctx * D;
   const int kmax = pos0 + nrows;  // keys 0..kmax-1 are visible to some row of the tile
 
-  // Q fragments of this wave's 16 rows (A operand of S): row r16, dims 32*ks + 8*grp
+  // this lane's query row and its Q fragments (B operand of S^T): dims 32*ks + 8*grp
+  const int r = 16 * wid + r16;
+  const bool row_ok = r < nrows;
+  const int qpos = pos0 + r;
   bf16x8_t qf[KS];
   {
-    const int r = 16 * wid + r16;
-    const bool ok = r < nrows;
-    const bf16_t* qr = a.q + (size_t)(row0 + (ok ? r : 0)) * a.ldq + (size_t)h * D;
+    const bf16_t* qr = a.q + (size_t)(row0 + (row_ok ? r : 0)) * a.ldq + (size_t)h * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       qf[ks] = __builtin_bit_cast(
-          bf16x8_t, ok ? *reinterpret_cast<const uint4*>(qr + 32 * ks + 8 * grp) : make_uint4(0, 0, 0, 0));
+          bf16x8_t, row_ok ? *reinterpret_cast<const uint4*>(qr + 32 * ks + 8 * grp) : make_uint4(0, 0, 0, 0));
   }
-  // softmax state of rows 4*grp + i of this wave
-  float m[4], l[4];
-  f32x4_t o[NT];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    m[i] = -INFINITY;
-    l[i] = 0.0f;
-  }
+  // softmax state of the lane's row: m is the same in the row's four lanes (reduced), l is
+  // this lane's share of the row sum (its keys only), reduced once at the end
+  float m = -INFINITY, l = 0.0f;
+  f32x4_t o[NT];  // O^T: dims 16*nt + 4*grp + i of the lane's row
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) o[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   // scores in base 2: exp(z - m) = exp2(z*log2(e) - m*log2(e)), one hardware exp each
   const float scale2 = 1.4426950408889634f / sqrtf((float)D);
 
-  // global -> register staging of one K/V block, two blocks in flight.  K: consecutive
+  // global -> register staging of the next K/V block while this one is in use (one
+  // register set, so three work-groups fit on a CU at head dim 128).  K: consecutive
   // lanes take consecutive 16-byte pieces of a key row.  V: consecutive lanes take
   // consecutive keys (same piece), so the transposed LDS stores of a quarter-wave hit
   // consecutive addresses instead of rows 8 apart (which all map to one bank).  Buffer
@@ -2000,7 +1986,7 @@ __global__ __launch_bounds__(256) void k_flash_prefill(FlashArgs a) {
       __builtin_amdgcn_make_buffer_rsrc((void*)Kb, 0, a.max_ctx * D * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrs =
       __builtin_amdgcn_make_buffer_rsrc((void*)Vb, 0, a.max_ctx * D * 2, 0x00020000);
-  uint4 kst[2][LD_PER_T], vst[2][LD_PER_T];
+  uint4 kst[LD_PER_T], vst[LD_PER_T];
   auto fetch = [&](int kb, uint4 (&ks)[LD_PER_T], uint4 (&vs)[LD_PER_T]) {
 #pragma unroll
     for (int u = 0; u < LD_PER_T; ++u) {
@@ -2014,15 +2000,17 @@ __global__ __launch_bounds__(256) void k_flash_prefill(FlashArgs a) {
                                             vrs, (in && kb + vkey < kmax) ? ((kb + vkey) * D + 8 * vc) * 2 : OOB, 0, 0));
     }
   };
-  // one key block: stage it in LDS, refill its registers with the block two ahead, then
-  // S = Q K^T, online softmax, O += P V
+  // one key block: stage it in LDS, refill the registers with the next block, then
+  // S^T = K Q^T, online softmax, O^T += V^T P^T
   auto block = [&](int kb, uint4 (&ks)[LD_PER_T], uint4 (&vs)[LD_PER_T]) {
 #pragma unroll
     for (int u = 0; u < LD_PER_T; ++u) {
       const int idx = tid + 256 * u;
       if (idx < KB * VPR) {
         const int key = idx / VPR, c = idx % VPR;
-        *reinterpret_cast<uint4*>(&Ks[key][8 * c]) = ks[u];
+        const int kq = key & 31;  // 8a + 4t + i -> row 16t + 4a + i of its 32-key step
+        const int krow = (key & ~31) + 16 * ((kq >> 2) & 1) + 4 * (kq >> 3) + (kq & 3);
+        *reinterpret_cast<uint4*>(&Ks[krow][8 * c]) = ks[u];
         const int vkey = idx % KB, vc = idx / KB;
         const uint32_t w4[4] = {vs[u].x, vs[u].y, vs[u].z, vs[u].w};
 #pragma unroll
@@ -2033,103 +2021,88 @@ __global__ __launch_bounds__(256) void k_flash_prefill(FlashArgs a) {
       }
     }
     __syncthreads();
-    fetch(kb + 2 * KB, ks, vs);  // past kmax: reads zero, never used
+    fetch(kb + KB, ks, vs);  // past kmax: reads zero, never used
 
-    // S = Q K^T for 16 rows x KB keys (NKT 16-key tiles)
-    f32x4_t sacc[NKT];
+    // S^T tiles: st[kk][t][i] = score of the lane's row against key kb + 32kk + 8grp + 4t + i
+    f32x4_t st[NKK][2];
 #pragma unroll
-    for (int n = 0; n < NKT; ++n) {
-      sacc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
-      for (int ks2 = 0; ks2 < KS; ++ks2) {
-        const bf16x8_t kf = __builtin_bit_cast(
-            bf16x8_t, *reinterpret_cast<const uint4*>(&Ks[16 * n + r16][32 * ks2 + 8 * grp]));
-        sacc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ks2], kf, sacc[n], 0, 0, 0);
+      for (int t = 0; t < 2; ++t) {
+        st[kk][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks2 = 0; ks2 < KS; ++ks2) {
+          const bf16x8_t kf = __builtin_bit_cast(
+              bf16x8_t, *reinterpret_cast<const uint4*>(&Ks[32 * kk + 16 * t + r16][32 * ks2 + 8 * grp]));
+          st[kk][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks2], st[kk][t], 0, 0, 0);
+        }
       }
-    }
-    // causal mask + online softmax; lane holds rows 4*grp+i, keys 16n + r16.  A row's
-    // reference maximum m moves only when the block's maximum exceeds it by more than
-    // 2^TAU (so probabilities stay below 2^TAU); the wave rescales its O rows only then
-    // (the result is the same softmax, any reference gives it)
+    // causal mask + online softmax.  The row's reference maximum m moves only when the
+    // block's maximum exceeds it by more than 2^TAU (so probabilities stay below 2^TAU);
+    // the wave rescales O only then (the result is the same softmax, any reference gives it)
     constexpr float TAU = 8.0f;
-    float sv[4][NKT], mb[4];
-    bool need = false;
+    float sv[NKK][2][4];
+    float smax = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * wid + 4 * grp + i;
-      const int qpos = pos0 + r;
-      float smax = -INFINITY;
+    for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
-      for (int n = 0; n < NKT; ++n) {
-        const int key = kb + 16 * n + r16;
-        sv[i][n] = (r < nrows && key <= qpos) ? sacc[n][i] * scale2 : -INFINITY;
-        smax = fmaxf(smax, sv[i][n]);
-      }
-      mb[i] = row16_max(smax);
-      need = need || (mb[i] > m[i] + TAU);
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = kb + 32 * kk + 8 * grp + 4 * t + i;
+          sv[kk][t][i] = (row_ok && key <= qpos) ? st[kk][t][i] * scale2 : -INFINITY;
+          smax = fmaxf(smax, sv[kk][t][i]);
+        }
+    smax = fmaxf(smax, __shfl_xor(smax, 16, 64));
+    smax = fmaxf(smax, __shfl_xor(smax, 32, 64));
+    if (__any(smax > m + TAU)) {
+      const float mnew = fmaxf(m, smax);
+      const float alpha = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - mnew);
+      l *= alpha;
+      m = mnew;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[nt][i] *= alpha;
     }
-    if (__any(need)) {
+    // P^T fragments (B operand): keys 32kk + 8grp + j, j = 4t + i, in high and low bf16 parts
+    bf16x8_t phi[NKK], plo[NKK];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float mnew = fmaxf(m[i], mb[i]);
-        const float alpha = (m[i] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m[i] - mnew);
-        l[i] *= alpha;
-        m[i] = mnew;
+    for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) o[nt][i] *= alpha;
-      }
-    }
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float pr[NKT], psum = 0.0f;
+        for (int i = 0; i < 4; ++i) {
+          const float p = (sv[kk][t][i] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sv[kk][t][i] - m);
+          l += p;
+          const __bf16 hi = (__bf16)p;
+          phi[kk][4 * t + i] = hi;
+          plo[kk][4 * t + i] = (__bf16)(p - (float)hi);
+        }
+    // O^T += V^T P^T: A = V^T (dims 16nt + r16, keys 32kk + 8grp..), B = P^T
 #pragma unroll
-      for (int n = 0; n < NKT; ++n) {
-        pr[n] = (sv[i][n] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sv[i][n] - m[i]);
-        psum += pr[n];
-      }
-      l[i] += row16_sum(psum);
-#pragma unroll
-      for (int n = 0; n < NKT; ++n) {
-        const bf16_t hi = f2bf(pr[n]);
-        const bf16_t lo = f2bf(pr[n] - bf2f(hi));
-        Ps[wid][0][4 * grp + i][16 * n + r16] = hi;
-        Ps[wid][1][4 * grp + i][16 * n + r16] = lo;
-      }
-    }
-    __syncthreads();
-    // O += P V: A = P (rows r16, keys 32*kk + 8*grp..), B = V (those keys, dims 16*nt + r16)
-#pragma unroll
-    for (int kk = 0; kk < KB / 32; ++kk) {
-      const bf16x8_t phi = __builtin_bit_cast(
-          bf16x8_t, *reinterpret_cast<const uint4*>(&Ps[wid][0][r16][32 * kk + 8 * grp]));
-      const bf16x8_t plo = __builtin_bit_cast(
-          bf16x8_t, *reinterpret_cast<const uint4*>(&Ps[wid][1][r16][32 * kk + 8 * grp]));
+    for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const bf16x8_t vf = __builtin_bit_cast(
             bf16x8_t, *reinterpret_cast<const uint4*>(&Vt[16 * nt + r16][32 * kk + 8 * grp]));
-        o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi, vf, o[nt], 0, 0, 0);
-        o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo, vf, o[nt], 0, 0, 0);
+        o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, phi[kk], o[nt], 0, 0, 0);
+        o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, plo[kk], o[nt], 0, 0, 0);
       }
-    }
     __syncthreads();
   };
-  fetch(0, kst[0], vst[0]);
-  fetch(KB, kst[1], vst[1]);
-  // blocks in pairs so each register set has a fixed name; a tile's last odd block is the
-  // only branch, and the loop ends after it
-  for (int kb = 0; kb < kmax; kb += 2 * KB) {
-    block(kb, kst[0], vst[0]);
-    if (kb + KB < kmax) block(kb + KB, kst[1], vst[1]);
-  }
-  // out[r][h*D + d] for rows 4*grp + i, dims 16*nt + r16
+  fetch(0, kst, vst);
+  for (int kb = 0; kb < kmax; kb += KB) block(kb, kst, vst);
+  // the row sum over its four lanes; out[r][h*D + 16nt + 4grp + i], four dims per store
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  if (!row_ok) return;
+  bf16_t* orow = a.out + (size_t)(row0 + r) * a.ldo + (size_t)h * D + 4 * grp;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 16 * wid + 4 * grp + i;
-    if (r >= nrows) continue;
-    bf16_t* orow = a.out + (size_t)(row0 + r) * a.ldo + (size_t)h * D;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) orow[16 * nt + r16] = f2bf(o[nt][i] / l[i]);
+  for (int nt = 0; nt < NT; ++nt) {
+    const uint32_t w0 = (uint32_t)f2bf(o[nt][0] / l) | ((uint32_t)f2bf(o[nt][1] / l) << 16);
+    const uint32_t w1 = (uint32_t)f2bf(o[nt][2] / l) | ((uint32_t)f2bf(o[nt][3] / l) << 16);
+    *reinterpret_cast<uint2*>(orow + 16 * nt) = make_uint2(w0, w1);
   }
 }
 
