@@ -1564,6 +1564,18 @@ __global__ __launch_bounds__(64 * NW) void k_attn_dec(AttnDecArgs a) {
   __syncthreads();
 
   const float scale = 1.0f / sqrtf((float)D);
+  // q of this lane's key quarter in registers as bf16 pairs (q is bf16-exact), scored with
+  // two-term dot products against the raw K words; when that would take more than 32
+  // registers the scores read q from LDS
+  constexpr bool QREG = G * KQ / 2 <= 32;
+  uint32_t qp[QREG ? G : 1][QREG ? KQ / 2 : 1];
+  if constexpr (QREG) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int c = 0; c < KQ / 2; ++c)
+        qp[h][c] = (uint32_t)f2bf(qs[h][part * KQ + 2 * c]) | ((uint32_t)f2bf(qs[h][part * KQ + 2 * c + 1]) << 16);
+  }
   float m[G], l[G], o[G][DPL];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -1584,6 +1596,17 @@ __global__ __launch_bounds__(64 * NW) void k_attn_dec(AttnDecArgs a) {
         const float kv = kn[part * KQ + j];
 #pragma unroll
         for (int h = 0; h < G; ++h) sp[h] += qs[h][part * KQ + j] * kv;
+      }
+    } else if constexpr (QREG) {
+#pragma unroll
+      for (int j = 0; j < KV4; ++j) {
+        const uint32_t w4[4] = {kc[j].x, kc[j].y, kc[j].z, kc[j].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int h = 0; h < G; ++h)
+            sp[h] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qp[h][4 * j + e]),
+                                                    __builtin_bit_cast(bf16x2_t, w4[e]), sp[h], false);
       }
     } else {
 #pragma unroll
