@@ -244,6 +244,7 @@ struct qd_model {
   int attn_max_splits = 64;
   int attn_min_chunks = 1;
   int attn_occupancy = 0;  // attention work-groups per CU the split targets (0: by waves)
+  int attn_resident4 = 3;  // four-wave attention work-groups that fit on one CU (measured)
   int attn_waves = 0;  // 0: eight waves only when B x KV heads fill the GPU without splits
   int attn_merge_last = 1;
   int gemm_splits = 0;  // prefill GEMM split-K cap (0: launcher default)
@@ -403,9 +404,11 @@ int attn_waves_for(const qd_model* m, int B) {
   return m->attn_waves ? m->attn_waves : (B * m->d.KV >= 256 ? 8 : 4);
 }
 
+// eight waves: one work-group per CU (measured best at B x KV >= 256); four waves: as many
+// as fit on a CU, at most three
 int attn_occupancy_for(const qd_model* m, int B) {
   if (m->attn_occupancy) return m->attn_occupancy;
-  return attn_waves_for(m, B) == 8 ? 1 : 3;
+  return attn_waves_for(m, B) == 8 ? 1 : m->attn_resident4;
 }
 
 qd_status dec_attn(qd_model* m, int l, int B, int nsplit, int split_len, hipStream_t st,
@@ -820,6 +823,9 @@ qd_status finish_model(qd_model* m, const hipDeviceProp_t& prop, hipStream_t s) 
   HIPCHK(hipEventCreateWithFlags(&m->err_ev, hipEventDisableTiming));
   m->persist_why = persist_problems(m, prop, &m->persist_nwg, &m->persist_lds);
   m->persist_ok = m->persist_why.empty();
+  int res4 = 0;  // shapes the decode attention kernel does not take keep the default
+  if (attention_decode_residency(m->d.D, m->d.G, 4, &res4) == hipSuccess && res4 > 0)
+    m->attn_resident4 = std::min(3, res4);
   return QD_OK;
 }
 

@@ -245,6 +245,8 @@ hipError_t launch_sample(const SampleArgs& a, int B, hipStream_t st);
 // zeroes counts[slot][:] and draws[slot] for slots[0..n) (NULL: slots 0..n-1)
 hipError_t launch_reset_seq(int* counts, int* draws, const int* slots, int n, int V, hipStream_t st);
 hipError_t launch_attention_decode(const AttnDecArgs& a, hipStream_t st);
+// work-groups of the decode attention kernel for (D, G, waves) resident on one CU
+hipError_t attention_decode_residency(int D, int G, int nwaves, int* blocks_per_cu);
 hipError_t launch_flash_prefill(const FlashArgs& a, int n_tiles, hipStream_t st);
 hipError_t launch_set_positions(int* pos, const int* lens, const int* slots, int n, hipStream_t st);
 hipError_t launch_iota(int* p, int n, hipStream_t st);

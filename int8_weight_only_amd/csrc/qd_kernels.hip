@@ -2406,6 +2406,41 @@ static hipError_t attn_dec_d(const AttnDecArgs& a, int G, hipStream_t st) {
   return attn_dec_dw<D, 4>(a, G, st);
 }
 
+// the kernel instance launch_attention_decode picks at one split count of eight or fewer
+template <int D, int G, int NW>
+static const void* attn_dec_kernel() {
+  constexpr int W = (NW == 8 && G * D > 512) ? 4 : NW;
+  return reinterpret_cast<const void*>(&k_attn_dec<D, G, W, false>);
+}
+template <int D, int NW>
+static const void* attn_dec_kernel_g(int G) {
+  switch (G) {
+    case 1: return attn_dec_kernel<D, 1, NW>();
+    case 2: return attn_dec_kernel<D, 2, NW>();
+    case 3: return attn_dec_kernel<D, 3, NW>();
+    case 4: return attn_dec_kernel<D, 4, NW>();
+    case 5: return attn_dec_kernel<D, 5, NW>();
+    case 6: return attn_dec_kernel<D, 6, NW>();
+    case 7: return attn_dec_kernel<D, 7, NW>();
+    default: return attn_dec_kernel<D, 8, NW>();
+  }
+}
+
+hipError_t attention_decode_residency(int D, int G, int nwaves, int* blocks) {
+  *blocks = 0;
+  if (G < 1 || G > 8) return hipErrorInvalidValue;
+  const bool w8 = nwaves >= 8 && G * D <= 512;
+  const void* k = nullptr;
+  switch (D) {
+    case 32: k = w8 ? attn_dec_kernel_g<32, 8>(G) : attn_dec_kernel_g<32, 4>(G); break;
+    case 64: k = w8 ? attn_dec_kernel_g<64, 8>(G) : attn_dec_kernel_g<64, 4>(G); break;
+    case 128: k = w8 ? attn_dec_kernel_g<128, 8>(G) : attn_dec_kernel_g<128, 4>(G); break;
+    case 256: k = w8 ? attn_dec_kernel_g<256, 8>(G) : attn_dec_kernel_g<256, 4>(G); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, k, 64 * (w8 ? 8 : 4), 0);
+}
+
 hipError_t launch_attention_decode(const AttnDecArgs& a, hipStream_t st) {
   const int G = a.H / a.KV;
   if (G < 1 || G > 8 || a.nsplit < 1) return hipErrorInvalidValue;
