@@ -94,7 +94,7 @@ typedef struct {
 typedef struct {
   int32_t max_batch;           /* sequences decoded together, 1..64 */
   int32_t max_ctx;             /* positions per sequence, 1..QD_MAX_CONTEXT */
-  int32_t max_prefill_tokens;  /* prompt tokens summed over one qd_prefill call */
+  int32_t max_prefill_tokens;  /* prompt tokens summed over one qd_prefill call, 1..4000000 */
 } qd_limits;
 
 typedef struct {

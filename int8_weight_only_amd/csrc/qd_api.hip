@@ -123,7 +123,9 @@ qd_status check_limits(const qd_limits* lim) {
   std::string p;
   if (lim->max_batch < 1 || lim->max_batch > 64) p += "max_batch must be in [1, 64]; ";
   if (lim->max_ctx < 1) p += "max_ctx must be >= 1; ";
-  if (lim->max_prefill_tokens < 1) p += "max_prefill_tokens must be >= 1; ";
+  // one prefill attention work-group row per 64 prompt rows: at most 65535 of them
+  if (lim->max_prefill_tokens < 1 || lim->max_prefill_tokens > 4000000)
+    p += "max_prefill_tokens must be in [1, 4000000]; ";
   if (!p.empty()) return fail(QD_ERR_INVALID_ARGUMENTS, p);
   return QD_OK;
 }

@@ -1969,9 +1969,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 
   __shared__ __align__(16) bf16_t Vt[D][KB + 8];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int grp = lane >> 4, r16 = lane & 15;
-  const int4 tile = a.tiles[blockIdx.x];
+  // heads vary fastest and tiles run last to first: within a sequence later tiles see more
+  // keys, so the longest work-groups start first and the shortest fill the end of the grid
+  const int4 tile = a.tiles[gridDim.y - 1 - blockIdx.y];
   const int row0 = tile.x, slot = tile.y, pos0 = tile.z, nrows = tile.w;
-  const int h = blockIdx.y, G = a.H / a.KV, g = h / G;
+  const int h = blockIdx.x, G = a.H / a.KV, g = h / G;
   const bf16_t* Kb = a.kcache + ((size_t)slot * a.KV + g) * a.max_ctx * D;
   const bf16_t* Vb = a.vcache + ((size_t)slot * a.KV + g) * a.max_ctx * D;
   const int kmax = pos0 + nrows;  // keys 0..kmax-1 are visible to some row of the tile
@@ -2459,7 +2461,8 @@ hipError_t launch_attention_decode(const AttnDecArgs& a, hipStream_t st) {
 
 hipError_t launch_flash_prefill(const FlashArgs& a, int n_tiles, hipStream_t st) {
   if (n_tiles < 1) return hipSuccess;
-  dim3 grid(n_tiles, a.H);
+  if (n_tiles > 65535) return hipErrorInvalidValue;
+  dim3 grid(a.H, n_tiles);
   switch (a.D) {
     case 32: hipLaunchKernelGGL(k_flash_prefill<32>, grid, dim3(256), 0, st, a); break;
     case 64: hipLaunchKernelGGL(k_flash_prefill<64>, grid, dim3(256), 0, st, a); break;

@@ -98,3 +98,10 @@ def test_context_ceiling_and_limits():
     with pytest.raises(qd.QdError) as e:
         qd.query_sizes(GOOD, 65, 512, 16)
     assert e.value.code == "invalid_arguments"
+    with pytest.raises(qd.QdError) as e:
+        qd.query_sizes(GOOD, 1, 512, 0)
+    assert e.value.code == "invalid_arguments"
+    with pytest.raises(qd.QdError) as e:  # prefill attention takes at most 65535 row tiles
+        qd.query_sizes(GOOD, 1, 512, 4000001)
+    assert e.value.code == "invalid_arguments"
+    qd.query_sizes(GOOD, 1, 512, 4000000)
