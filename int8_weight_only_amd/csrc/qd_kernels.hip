@@ -2002,8 +2002,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 
   // global -> register staging of the next K/V block while this one is in use (one
   // register set, so three work-groups fit on a CU at head dim 128).  K: consecutive
   // lanes take consecutive 16-byte pieces of a key row.  V: consecutive lanes take
-  // consecutive keys (same piece), so the transposed LDS stores of a quarter-wave hit
-  // consecutive addresses instead of rows 8 apart (which all map to one bank).  Buffer
+  // consecutive key pairs (same piece), so the transposed LDS stores of half a wave hit
+  // consecutive words instead of rows 8 apart (which all map to one bank).  Buffer
   // loads: keys past the tile's last visible one read zero through an out-of-range
   // offset, so no load sits in a branch and each block waits only for its own data.
   constexpr int OOB = (int)0x80000000;
@@ -2011,23 +2011,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 
       __builtin_amdgcn_make_buffer_rsrc((void*)Kb, 0, a.max_ctx * D * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrs =
       __builtin_amdgcn_make_buffer_rsrc((void*)Vb, 0, a.max_ctx * D * 2, 0x00020000);
-  uint4 kst[LD_PER_T], vst[LD_PER_T];
-  auto fetch = [&](int kb, uint4 (&ks)[LD_PER_T], uint4 (&vs)[LD_PER_T]) {
+  // V in units of (key pair, 16-byte piece): the transposed LDS stores write both keys of
+  // a dim as one 32-bit word
+  constexpr int NVU = KB / 2 * VPR;
+  constexpr int VPT = (NVU + 255) / 256;  // V units per thread and block
+  uint4 kst[LD_PER_T], vst[VPT][2];
+  auto fetch = [&](int kb, uint4 (&ks)[LD_PER_T], uint4 (&vs)[VPT][2]) {
 #pragma unroll
     for (int u = 0; u < LD_PER_T; ++u) {
       const int idx = tid + 256 * u;
       const int key = idx / VPR, c = idx % VPR;
-      const int vkey = idx % KB, vc = idx / KB;
       const bool in = idx < KB * VPR;
       ks[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                             krs, (in && kb + key < kmax) ? ((kb + key) * D + 8 * c) * 2 : OOB, 0, 0));
-      vs[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            vrs, (in && kb + vkey < kmax) ? ((kb + vkey) * D + 8 * vc) * 2 : OOB, 0, 0));
+    }
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+      const int pidx = tid + 256 * u;
+      const int kp = pidx % (KB / 2), vc = pidx / (KB / 2);
+      const bool in = pidx < NVU;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int vkey = kb + 2 * kp + j;
+        vs[u][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 vrs, (in && vkey < kmax) ? (vkey * D + 8 * vc) * 2 : OOB, 0, 0));
+      }
     }
   };
   // one key block: stage it in LDS, refill the registers with the next block, then
   // S^T = K Q^T, online softmax, O^T += V^T P^T
-  auto block = [&](int kb, uint4 (&ks)[LD_PER_T], uint4 (&vs)[LD_PER_T]) {
+  auto block = [&](int kb, uint4 (&ks)[LD_PER_T], uint4 (&vs)[VPT][2]) {
 #pragma unroll
     for (int u = 0; u < LD_PER_T; ++u) {
       const int idx = tid + 256 * u;
@@ -2036,12 +2049,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 
         const int kq = key & 31;  // 8a + 4t + i -> row 16t + 4a + i of its 32-key step
         const int krow = (key & ~31) + 16 * ((kq >> 2) & 1) + 4 * (kq >> 3) + (kq & 3);
         *reinterpret_cast<uint4*>(&Ks[krow][8 * c]) = ks[u];
-        const int vkey = idx % KB, vc = idx / KB;
-        const uint32_t w4[4] = {vs[u].x, vs[u].y, vs[u].z, vs[u].w};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+      const int pidx = tid + 256 * u;
+      if (pidx < NVU) {
+        const int kp = pidx % (KB / 2), vc = pidx / (KB / 2);
+        const uint32_t a4[4] = {vs[u][0].x, vs[u][0].y, vs[u][0].z, vs[u][0].w};
+        const uint32_t b4[4] = {vs[u][1].x, vs[u][1].y, vs[u][1].z, vs[u][1].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          Vt[8 * vc + 2 * e][vkey] = (bf16_t)(w4[e] & 0xFFFFu);
-          Vt[8 * vc + 2 * e + 1][vkey] = (bf16_t)(w4[e] >> 16);
+          *reinterpret_cast<uint32_t*>(&Vt[8 * vc + 2 * e][2 * kp]) = (a4[e] & 0xFFFFu) | (b4[e] << 16);
+          *reinterpret_cast<uint32_t*>(&Vt[8 * vc + 2 * e + 1][2 * kp]) = (a4[e] >> 16) | (b4[e] & 0xFFFF0000u);
         }
       }
     }
