@@ -1433,6 +1433,7 @@ __global__ __launch_bounds__(64 * NW) void k_attn_dec(AttnDecArgs a) {
   constexpr int DPL = D >= 64 ? D / 64 : 1;    // output dims per lane
   constexpr int VW = DPL >= 2 ? DPL / 2 : 1;   // 32-bit words of V per lane per row
   __shared__ __align__(16) float qs[G][D];
+  __shared__ __align__(16) bf16_t qb[G][D];  // the same q as bf16 (it is bf16-exact)
   __shared__ float kn[D], vn[D];
   __shared__ float wm[NW][G], wl[NW][G];
   __shared__ float wo[NW][G][D];
@@ -1545,6 +1546,8 @@ __global__ __launch_bounds__(64 * NW) void k_attn_dec(AttnDecArgs a) {
         if (isq) {
           qs[hh][i] = bf2f(o1);
           qs[hh][i + HALF] = bf2f(o2);
+          qb[hh][i] = o1;
+          qb[hh][i + HALF] = o2;
         } else {
           kn[i] = bf2f(o1);
           kn[i + HALF] = bf2f(o2);
@@ -1564,18 +1567,6 @@ __global__ __launch_bounds__(64 * NW) void k_attn_dec(AttnDecArgs a) {
   __syncthreads();
 
   const float scale = 1.0f / sqrtf((float)D);
-  // q of this lane's key quarter in registers as bf16 pairs (q is bf16-exact), scored with
-  // two-term dot products against the raw K words; when that would take more than 32
-  // registers the scores read q from LDS
-  constexpr bool QREG = G * KQ / 2 <= 32;
-  uint32_t qp[QREG ? G : 1][QREG ? KQ / 2 : 1];
-  if constexpr (QREG) {
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int c = 0; c < KQ / 2; ++c)
-        qp[h][c] = (uint32_t)f2bf(qs[h][part * KQ + 2 * c]) | ((uint32_t)f2bf(qs[h][part * KQ + 2 * c + 1]) << 16);
-  }
   float m[G], l[G], o[G][DPL];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -1597,27 +1588,20 @@ __global__ __launch_bounds__(64 * NW) void k_attn_dec(AttnDecArgs a) {
 #pragma unroll
         for (int h = 0; h < G; ++h) sp[h] += qs[h][part * KQ + j] * kv;
       }
-    } else if constexpr (QREG) {
-#pragma unroll
-      for (int j = 0; j < KV4; ++j) {
-        const uint32_t w4[4] = {kc[j].x, kc[j].y, kc[j].z, kc[j].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-#pragma unroll
-          for (int h = 0; h < G; ++h)
-            sp[h] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qp[h][4 * j + e]),
-                                                    __builtin_bit_cast(bf16x2_t, w4[e]), sp[h], false);
-      }
     } else {
+      // q as bf16 pairs from LDS (one 16-byte read per 8 elements, broadcast to the lanes of
+      // a key quarter), two-term bf16 dot products against the raw K words
 #pragma unroll
       for (int j = 0; j < KV4; ++j) {
         const uint32_t w4[4] = {kc[j].x, kc[j].y, kc[j].z, kc[j].w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float k0 = __uint_as_float(w4[e] << 16), k1 = __uint_as_float(w4[e] & 0xFFFF0000u);
-          const int c = part * KQ + 8 * j + 2 * e;
+        for (int h = 0; h < G; ++h) {
+          const uint4 q4 = *reinterpret_cast<const uint4*>(&qb[h][part * KQ + 8 * j]);
+          const uint32_t qw[4] = {q4.x, q4.y, q4.z, q4.w};
 #pragma unroll
-          for (int h = 0; h < G; ++h) sp[h] += qs[h][c] * k0 + qs[h][c + 1] * k1;
+          for (int e = 0; e < 4; ++e)
+            sp[h] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qw[e]),
+                                                    __builtin_bit_cast(bf16x2_t, w4[e]), sp[h], false);
         }
       }
     }
