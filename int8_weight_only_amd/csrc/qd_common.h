@@ -106,7 +106,7 @@ struct AttnDecArgs {
 struct FlashArgs {
   const bf16_t* q; int ldq;                    // roped q rows; head h at q + r*ldq + h*D
   const bf16_t* kcache; const bf16_t* vcache;  // this layer's [slots][KV][ctx][D]
-  const int4* tiles;                           // [grid.x]
+  const int4* tiles;                           // [grid.y]: (row0, slot, pos0, rows)
   int H, KV, D, max_ctx;
   bf16_t* out; int ldo;                        // [M][H*D]
 };
