@@ -221,7 +221,10 @@ qd_status qd_prefill(qd_model* m, int32_t n_seqs, const int32_t* ids_dev,
                      const int32_t* ids_host, const int32_t* lens_host,
                      float* logits_dev, int32_t* next_ids_dev, qd_stream stream);
 
-/* One decode step for slots 0..B-1: feeds in_ids_dev[B] (device) at each slot's
+/* One decode step ("LLM inference overview", section "Workload characteristics": decode
+ * produces one token per sequence per step and sweeps every weight once for all B
+ * sequences; "Model-agnostic LLM inference", section "Notes": the greedy id is the fused
+ * arg-max of the step's logits) for slots 0..B-1: feeds in_ids_dev[B] (device) at each slot's
  * current length p, appends K/V at p, increments p, writes the greedy ids to
  * next_ids_dev[B] and, if logits_dev is not NULL, fp32 logits [B, V].  Teacher
  * forcing is the caller choosing in_ids.  No host synchronization; the slot
@@ -352,7 +355,40 @@ typedef enum {
  * QD_ERR_INVALID_ARGUMENTS for an unknown knob or a value out of its range. */
 qd_status qd_set_tuning(qd_model* m, int32_t knob, int32_t value);
 
-/* Frees host state and graphs.  Caller buffers remain the caller's. */
+/* Kernel classes of a decode step, for qd_run_op. */
+typedef enum {
+  QD_OP_EMBED = 0, QD_OP_QKV = 1, QD_OP_O = 2, QD_OP_GATEUP = 3, QD_OP_DOWN = 4,
+  QD_OP_LMHEAD = 5, QD_OP_COUNT = 6,
+} qd_op;
+
+/* Test aid (not part of the forward pass): runs one kernel class of a decode step for B
+ * rows, launched exactly as qd_decode_step launches it at that B (the same kernels, tile
+ * shapes and work splits), on caller-given device inputs of `layer`'s weights:
+ *   QD_OP_EMBED   in: token ids int32 [B]              out: bf16 [B, hidden] = code x row scale
+ *   QD_OP_QKV     in: residual bf16 [B, hidden]        out: bf16 [B, H*D + 2*KV*D] (q | k | v)
+ *                 of RMSNorm(in, input gain), projected (the norm runs inside the projection)
+ *   QD_OP_O       in: attention output bf16 [B, H*D], resid: bf16 [B, hidden]
+ *                 out: bf16 [B, hidden] = resid + projection
+ *   QD_OP_GATEUP  in: residual bf16 [B, hidden]        out: bf16 [B, intermediate] =
+ *                 SiLU(gate) x up of RMSNorm(in, post-attention gain)
+ *   QD_OP_DOWN    in: bf16 [B, intermediate], resid: bf16 [B, hidden]
+ *                 out: bf16 [B, hidden] = resid + projection
+ *   QD_OP_LMHEAD  in: residual bf16 [B, hidden]        out: fp32 logits [B, vocab] of
+ *                 RMSNorm(in, final gain) against the tied embedding; ids_out: int32 [B], the
+ *                 fused arg-max (lowest index among equal maxima)
+ * All pointers are device pointers, rows dense; resid is read for QD_OP_O and QD_OP_DOWN only,
+ * ids_out for QD_OP_LMHEAD only (required there).  Overwrites the workspace's activation
+ * buffers; KV cache, positions and sampler state are left unchanged.  Asynchronous on
+ * `stream`.  QD_ERR_INVALID_ARGUMENTS for an unknown op, a layer or B out of range or a NULL
+ * pointer, before any GPU work.  Its purpose is exact checks of each projection kernel:
+ * with integer-valued codes whose row maximum is 127 (scale exactly 1) and integer-valued
+ * inputs, every fp32 accumulator is an exact integer in any summation order. */
+qd_status qd_run_op(qd_model* m, int32_t op, int32_t layer, int32_t B, const void* in_dev,
+                    const void* resid_dev, void* out_dev, int32_t* ids_out_dev, qd_stream stream);
+
+/* Frees the handle's host state and captured graphs ("Model-agnostic LLM inference",
+ * section "Notes": weights stay resident across calls until the model is released).
+ * The caller's device buffers remain the caller's; NULL is a no-op. */
 void qd_free(qd_model* m);
 
 #ifdef __cplusplus

@@ -91,10 +91,11 @@ EXPORTS = ("qd_last_error", "qd_check_shape", "qd_query_sizes", "qd_load_weights
            "qd_export_quantized", "qd_prefill", "qd_decode_step", "qd_generate_greedy",
            "qd_free", "qd_profile_kernels", "qd_set_tuning", "qd_prefill_slots",
            "qd_decode_step_slots", "qd_sample", "qd_save_cache", "qd_load_cache",
-           "qd_check_cache", "qd_sha256")
+           "qd_check_cache", "qd_sha256", "qd_run_op")
 TUNING = {"attn_max_splits": 0, "attn_min_chunks": 1, "attn_waves": 2, "attn_merge_last": 3,
           "persistent": 4, "persist_splits": 5, "skinny_split": 6, "gemm_splits": 7, "attn_occupancy": 8, "skinny_norm": 9}
 PROF_KERNELS = ("embed", "qkv", "attn", "o", "gateup", "down", "lmhead")
+OPS = {"embed": 0, "qkv": 1, "o": 2, "gateup": 3, "down": 4, "lmhead": 5}
 
 _lib = None
 
@@ -156,6 +157,8 @@ def load_library(path: str = LIB_PATH):
     lib.qd_profile_kernels.argtypes = [vp, i32, i32, vp, vp]
     lib.qd_set_tuning.restype = i32
     lib.qd_set_tuning.argtypes = [vp, i32, i32]
+    lib.qd_run_op.restype = i32
+    lib.qd_run_op.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp]
     lib.qd_free.restype = None
     lib.qd_free.argtypes = [vp]
     _lib = lib
@@ -362,7 +365,7 @@ class Model:
         else:
             sl = np.ascontiguousarray(slots, dtype=np.int32).reshape(-1)
             if sl.size != B:
-                raise QdError(1, f"{sl.size} slots for {B} ids")
+                raise QdError(2, f"{sl.size} slots for {B} ids")
             _check(_lib.qd_decode_step_slots(self._h, B, sl.ctypes.data, in_ids.data_ptr(), lg_ptr,
                                              nxt.data_ptr(), _stream_handle()))
         return nxt, lg
@@ -380,10 +383,10 @@ class Model:
         B = logits.shape[0]
         sd = np.ascontiguousarray(seeds, dtype=np.uint64).reshape(-1)
         if sd.size != B:
-            raise QdError(1, f"{sd.size} seeds for {B} rows")
+            raise QdError(2, f"{sd.size} seeds for {B} rows")
         sl = None if slots is None else np.ascontiguousarray(slots, dtype=np.int32).reshape(-1)
         if sl is not None and sl.size != B:
-            raise QdError(1, f"{sl.size} slots for {B} rows")
+            raise QdError(2, f"{sl.size} slots for {B} rows")
         prm = SamplingC(temperature, top_k, min_p, top_p, repeat_penalty, presence_penalty,
                         frequency_penalty)
         nxt = torch.empty(B, dtype=torch.int32, device=self.device)
@@ -403,6 +406,24 @@ class Model:
         _check(_lib.qd_profile_kernels(self._h, int(B), int(iters), us.ctypes.data,
                                        _stream_handle()))
         return dict(zip(PROF_KERNELS, map(float, us)))
+
+    def run_op(self, op: str, x, resid=None, layer: int = 0):
+        """One decode-step kernel class on caller inputs (qd_run_op): ``x`` is int32 ids [B]
+        for "embed", else a bf16 cuda tensor [B, K]; ``resid`` bf16 [B, hidden] for "o" and
+        "down".  Returns the output tensor (and, for "lmhead", (logits, ids))."""
+        s = self.shape
+        x = x.contiguous()
+        B = x.shape[0]
+        width = {"embed": s.hidden, "qkv": (s.n_heads + 2 * s.n_kv_heads) * s.head_dim,
+                 "o": s.hidden, "gateup": s.intermediate, "down": s.hidden, "lmhead": s.vocab}[op]
+        dt = torch.float32 if op == "lmhead" else torch.bfloat16
+        out = torch.empty((B, width), dtype=dt, device=self.device)
+        ids = torch.empty(B, dtype=torch.int32, device=self.device) if op == "lmhead" else None
+        r = resid.contiguous() if resid is not None else None
+        _check(_lib.qd_run_op(self._h, OPS[op], int(layer), int(B), x.data_ptr(),
+                              r.data_ptr() if r is not None else None, out.data_ptr(),
+                              ids.data_ptr() if ids is not None else None, _stream_handle()))
+        return (out, ids) if op == "lmhead" else out
 
     def generate_greedy(self, prompts, max_new_tokens: int, eos_id: int = -1) -> GenerateResult:
         """Prefill + (max_new_tokens - 1) decode steps, greedy, in one library call."""

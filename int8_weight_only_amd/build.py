@@ -5,6 +5,7 @@ Usage: python -m int8_weight_only_amd.build
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -22,20 +23,25 @@ FLAGS = [
 ]
 
 
+def _compile(src: str, verbose: bool) -> str:
+    obj = os.path.join(CSRC, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    errs = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{errs}")
+    if errs.strip() and verbose:
+        print(errs, file=sys.stderr)
+    return obj
+
+
 def build_library(verbose: bool = True) -> str:
-    objs = []
-    for src in SOURCES:
-        obj = os.path.join(CSRC, os.path.splitext(src)[0] + ".o")
-        cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        errs = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
-        if r.returncode != 0:
-            raise RuntimeError(f"hipcc failed for {src}:\n{errs}")
-        if errs.strip() and verbose:
-            print(errs, file=sys.stderr)
-        objs.append(obj)
+    # the sources compile independently: one hipcc process each, at most MAX_JOBS at once
+    jobs = max(1, min(len(SOURCES), int(os.environ.get("MAX_JOBS", "8"))))
+    with ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:

@@ -130,6 +130,22 @@ qd_status check_limits(const qd_limits* lim) {
   return QD_OK;
 }
 
+// The prefill GEMM addresses each operand through one buffer resource with 32-bit byte
+// offsets (and reads zero at offset 2^31): every [M, width] bf16 operand it reads or writes
+// must stay below 2 GiB, so max_prefill_tokens is bounded by the widest row the shape has.
+std::string prefill_bound_problem(const qd_model_shape& s, const qd_limits& lim) {
+  const Dims d = dims_of(s);
+  const long long widest = std::max(std::max((long long)d.d, (long long)d.I),
+                                     std::max((long long)d.NQKV, (long long)d.HD));
+  const long long rows = std::max((long long)lim.max_prefill_tokens, (long long)lim.max_batch);
+  const long long cap = ((1ll << 31) - 1) / (2 * widest);
+  if (rows > cap)
+    return "max_prefill_tokens " + std::to_string(lim.max_prefill_tokens) + " exceeds " +
+           std::to_string(cap) + " for this shape (prefill operands are addressed with 32-bit " +
+           "offsets: tokens x widest row (" + std::to_string(widest) + ") x 2 bytes < 2 GiB)";
+  return "";
+}
+
 Plan make_plan(const qd_model_shape& s, const qd_limits& lim) {
   const Dims d = dims_of(s);
   Plan P;
@@ -754,6 +770,8 @@ qd_status qd_query_sizes(const qd_model_shape* shape, const qd_limits* limits, q
   if (st != QD_OK) return st;
   if ((st = check_limits(limits)) != QD_OK) return st;
   if (!out) return fail(QD_ERR_INVALID_ARGUMENTS, "out is NULL");
+  const std::string pb = prefill_bound_problem(*shape, *limits);
+  if (!pb.empty()) return fail(QD_ERR_INVALID_ARGUMENTS, pb);
   const Plan P = make_plan(*shape, *limits);
   out->weight_bytes = P.weight_bytes;
   out->kv_bytes = P.kv_bytes;
@@ -766,6 +784,8 @@ namespace {
 // checks the limits and caller buffers and creates the handle (no GPU work)
 qd_status open_model(const qd_model_shape* shape, const qd_limits* limits,
                      const qd_buffers* bufs, qd_model** out, hipDeviceProp_t* prop) {
+  const std::string pb = prefill_bound_problem(*shape, *limits);
+  if (!pb.empty()) return fail(QD_ERR_INVALID_ARGUMENTS, pb);
   const Plan P = make_plan(*shape, *limits);
   if (!bufs || !bufs->weights || !bufs->kv || !bufs->workspace)
     return fail(QD_ERR_INVALID_ARGUMENTS, "a device buffer pointer is NULL");
@@ -1473,6 +1493,65 @@ qd_status qd_profile_kernels(qd_model* m, int32_t B, int32_t iters, float* us_ou
     float ms = 0;
     HIPCHK(hipEventElapsedTime(&ms, m->ev[0], m->ev[1]));
     us_out[k] = ms * 1e3f / iters;
+  }
+  return QD_OK;
+}
+
+qd_status qd_run_op(qd_model* m, int32_t op, int32_t layer, int32_t B, const void* in_dev,
+                    const void* resid_dev, void* out_dev, int32_t* ids_out_dev, qd_stream stream) {
+  g_err.clear();
+  if (!m) return fail(QD_ERR_INVALID_ARGUMENTS, "model is NULL");
+  std::string p;
+  if (op < 0 || op >= QD_OP_COUNT) p += "unknown op " + std::to_string(op) + "; ";
+  if (layer < 0 || layer >= m->d.L) p += "layer out of range; ";
+  if (B < 1 || B > m->lim.max_batch) p += "B must be in [1, max_batch]; ";
+  if (!in_dev || !out_dev) p += "in_dev and out_dev must be set; ";
+  if ((op == QD_OP_O || op == QD_OP_DOWN) && !resid_dev) p += "resid_dev must be set for this op; ";
+  if (op == QD_OP_LMHEAD && !ids_out_dev) p += "ids_out_dev must be set for the LM head; ";
+  if (!p.empty()) return fail(QD_ERR_INVALID_ARGUMENTS, p);
+  const Dims& d = m->d;
+  const Plan& P = m->P;
+  hipStream_t st = (hipStream_t)stream;
+  auto put = [&](size_t off, const void* src, size_t bytes) -> hipError_t {
+    return hipMemcpyAsync(m->WS + off, src, bytes, hipMemcpyDeviceToDevice, st);
+  };
+  auto get = [&](size_t off, size_t bytes) -> hipError_t {
+    return hipMemcpyAsync(out_dev, m->WS + off, bytes, hipMemcpyDeviceToDevice, st);
+  };
+  const size_t xb = (size_t)B * d.d * 2;
+  switch (op) {
+    case QD_OP_EMBED:
+      // the decode step's embedding launch, without the sampler's occurrence counts
+      HIPCHK(launch_embed(static_cast<const int*>(in_dev), B, m->w<int8_t>(P.emb_q),
+                          m->w<float>(P.emb_s), d.d, d.V, static_cast<bf16_t*>(out_dev), st));
+      break;
+    case QD_OP_QKV:
+      HIPCHK(put(P.x, in_dev, xb));
+      QDCHK(dec_qkv(m, layer, B, st));
+      HIPCHK(get(P.qkv, (size_t)B * d.NQKV * 2));
+      break;
+    case QD_OP_O:
+      HIPCHK(put(P.attn, in_dev, (size_t)B * d.HD * 2));
+      HIPCHK(put(P.x, resid_dev, xb));
+      QDCHK(dec_o(m, layer, B, st));
+      HIPCHK(get(P.x, xb));
+      break;
+    case QD_OP_GATEUP:
+      HIPCHK(put(P.x, in_dev, xb));
+      QDCHK(dec_gateup(m, layer, B, st));
+      HIPCHK(get(P.act, (size_t)B * d.I * 2));
+      break;
+    case QD_OP_DOWN:
+      HIPCHK(put(P.act, in_dev, (size_t)B * d.I * 2));
+      HIPCHK(put(P.x, resid_dev, xb));
+      QDCHK(dec_down(m, layer, B, st));
+      HIPCHK(get(P.x, xb));
+      break;
+    default:
+      HIPCHK(put(P.x, in_dev, xb));
+      QDCHK(enqueue_lm_head(m, m->ws<bf16_t>(P.x), nullptr, B, B, static_cast<float*>(out_dev),
+                            ids_out_dev, false, false, st));
+      break;
   }
   return QD_OK;
 }

@@ -198,19 +198,31 @@ class Oracle:
         return self._act(out)
 
     def attention(self, q, K, V, positions):
-        """Causal GQA.  q: [rows, H, D]; K, V: [KV, T, D]; row i sees keys 0..positions[i]."""
+        """Causal GQA.  q: [rows, H, D]; K, V: [KV, T, D]; row i sees keys 0..positions[i].
+
+        Per query row and head h (KV head g = h // (H/KV)): scores z_t = (q . k_t) / sqrt(D)
+        for t = 0..p, weights w = exp(z - max z), output sum_t w_t v_t / sum_t w_t.  Rows are
+        taken in blocks as one score matrix per head; a key past a row's own position gets
+        score -inf, so its weight is exactly zero and the row sees keys 0..p only.
+        """
         H, KV, D = self.shape.n_heads, self.shape.n_kv_heads, self.shape.head_dim
         group = H // KV
         rows = q.shape[0]
+        positions = np.asarray(positions)
         out = np.zeros((rows, H, D))
         scale = 1.0 / np.sqrt(D)
-        for h in range(H):
-            g = h // group
-            for r in range(rows):
-                n = positions[r] + 1
-                z = (K[g, :n] @ q[r, h]) * scale
-                w = np.exp(z - np.max(z))
-                out[r, h] = (w @ V[g, :n]) / np.sum(w)
+        blk = 256
+        for r0 in range(0, rows, blk):
+            r1 = min(rows, r0 + blk)
+            pos = positions[r0:r1]
+            n = int(pos.max()) + 1
+            future = np.arange(n)[None, :] > pos[:, None]
+            for h in range(H):
+                g = h // group
+                z = (q[r0:r1, h] @ K[g, :n].T) * scale
+                z[future] = -np.inf
+                w = np.exp(z - np.max(z, axis=1, keepdims=True))
+                out[r0:r1, h] = (w @ V[g, :n]) / np.sum(w, axis=1, keepdims=True)
         return self._act(out)
 
     # ---- forward over new tokens of one sequence -------------------------------------

@@ -47,6 +47,15 @@ CONFIGS = {
     "wide-long": (ModelShape(hidden=128, n_layers=2, n_heads=4, n_kv_heads=2, head_dim=64,
                              intermediate=256, vocab=512), 5, "uniform", 1500, 1005, 24),
     "qwen3-0.6b": (SHAPES["qwen3-0.6b"], 0, "ones", 256, 1000, 4),
+    # every dimension of Qwen3-0.6B but 2 layers: the kernel instantiations of the full
+    # model (they depend on the widths, heads and vocabulary, not on the depth)
+    "qwen3-0.6b-l2": (ModelShape(hidden=1024, n_layers=2, n_heads=16, n_kv_heads=8,
+                                 head_dim=128, intermediate=3072, vocab=151936),
+                      0, "uniform", 256, 1000, 5),
+    # the same with an 8192-token prompt: decode attention over > 8 merged splits at D=128
+    "long-0.6b-l2": (ModelShape(hidden=1024, n_layers=2, n_heads=16, n_kv_heads=8,
+                                head_dim=128, intermediate=3072, vocab=151936),
+                     0, "uniform", 8192, 1005, 4),
     "qwen3-1.7b": (SHAPES["qwen3-1.7b"], 0, "ones", 256, 1000, 3),
 }
 PERT = 6e-8

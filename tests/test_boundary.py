@@ -104,4 +104,44 @@ def test_context_ceiling_and_limits():
     with pytest.raises(qd.QdError) as e:  # prefill attention takes at most 65535 row tiles
         qd.query_sizes(GOOD, 1, 512, 4000001)
     assert e.value.code == "invalid_arguments"
-    qd.query_sizes(GOOD, 1, 512, 4000000)
+
+
+def test_prefill_tokens_bounded_by_32_bit_gemm_offsets():
+    """The prefill GEMM reads each [tokens, width] bf16 operand through 32-bit byte offsets:
+    tokens x widest row x 2 must stay below 2 GiB (tiny: widest row 384, the intermediate)."""
+    cap = (2 ** 31 - 1) // (2 * 384)
+    qd.query_sizes(GOOD, 1, 512, cap)
+    with pytest.raises(qd.QdError) as e:
+        qd.query_sizes(GOOD, 1, 512, cap + 1)
+    assert e.value.code == "invalid_arguments" and "32-bit" in str(e.value)
+    # Qwen3-1.7B: the widest row is the 6144-wide intermediate
+    cap17 = (2 ** 31 - 1) // (2 * 6144)
+    qd.query_sizes(SHAPES["qwen3-1.7b"], 1, 512, cap17)
+    with pytest.raises(qd.QdError):
+        qd.query_sizes(SHAPES["qwen3-1.7b"], 1, 512, cap17 + 1)
+
+
+def test_run_op_rejects_a_null_model_on_the_host():
+    import ctypes
+    lib = qd.load_library()
+    st = lib.qd_run_op(None, 1, 0, 1, None, None, None, None, None)
+    assert st == 2 and b"model is NULL" in lib.qd_last_error()
+
+
+def test_binding_count_mismatches_are_argument_errors():
+    """A slot or seed list whose length differs from the batch is an argument error
+    ("Model-agnostic LLM inference", section "Errors": invalid_arguments), raised by the
+    binding before any library call."""
+    torch = pytest.importorskip("torch")
+    m = object.__new__(qd.Model)          # no device buffers: only the argument checks run
+    m.shape, m.device, m._h = GOOD, torch.device("cpu"), None
+    with pytest.raises(qd.QdError) as e:
+        m.decode_step(torch.zeros(2, dtype=torch.int32), slots=[0, 1, 2])
+    assert e.value.code == "invalid_arguments"
+    logits = torch.zeros((2, GOOD.vocab), dtype=torch.float32)
+    with pytest.raises(qd.QdError) as e:
+        m.sample(logits, seeds=[1, 2, 3])
+    assert e.value.code == "invalid_arguments"
+    with pytest.raises(qd.QdError) as e:
+        m.sample(logits, seeds=[1, 2], slots=[0])
+    assert e.value.code == "invalid_arguments"

@@ -353,10 +353,11 @@ def test_teacher_forced_long_context():
     try:
         for persist in PERSIST:
             _teacher_forced(m, WIDE, qm, prompt, 23, "wide-long", "wide-long", persist, orc)
-        # per-step kernels with the last split merging in-kernel instead of a merge launch
-        m.set_tuning(attn_merge_last=1)
-        _teacher_forced(m, WIDE, qm, prompt, 23, "wide-long merge-last", "wide-long", 0, orc)
+        # per-step kernels with the separate merge launch instead of the in-kernel merge
+        # by the last split (the default)
         m.set_tuning(attn_merge_last=0)
+        _teacher_forced(m, WIDE, qm, prompt, 23, "wide-long merge launch", "wide-long", 0, orc)
+        m.set_tuning(attn_merge_last=1)
         m.set_tuning(persist_splits=2)
         _teacher_forced(m, WIDE, qm, prompt, 23, "wide-long 2 splits", "wide-long", 1, orc)
     finally:
