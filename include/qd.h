@@ -298,6 +298,20 @@ qd_status qd_sample(qd_model* m, int32_t B, const int32_t* slots_host, const qd_
                     const uint64_t* seeds_host, const float* logits_dev, int32_t* next_ids_dev,
                     qd_stream stream);
 
+/* qd_sample for callers that cannot allocate device memory: code under HIP graph
+ * capture, serving loops that must not call hipMalloc, harnesses that forbid it.  Same
+ * arguments, checks, kernels and results as qd_sample; the per-call scratch (penalized
+ * rows, histograms, candidate lists, counters, the staged seeds and slot list) lives in a
+ * fixed device array of the library (9 MiB + 17 KiB per device, held until the process
+ * ends) instead of the model's workspace, so nothing is allocated or freed.  Limits of
+ * that array: B <= 16 and B x vocab <= 2,097,152 (at vocab 151,936: 13 rows); larger
+ * calls return QD_ERR_INVALID_ARGUMENTS naming the limit, before any GPU work.  Every
+ * call on one device shares the array: calls that overlap on one GPU (another stream,
+ * another model, another thread) race and must be ordered by the caller. */
+qd_status qd_sample_noalloc(qd_model* m, int32_t B, const int32_t* slots_host,
+                            const qd_sampling* params, const uint64_t* seeds_host,
+                            const float* logits_dev, int32_t* next_ids_dev, qd_stream stream);
+
 /* One call, start to finish ("Model-agnostic LLM inference", section "Notes"):
  * prefill of B prompts (host ids, concatenated; lens_host[B]) then
  * max_new_tokens - 1 decode steps, greedy ids kept on the device between steps:

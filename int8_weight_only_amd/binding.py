@@ -91,7 +91,7 @@ EXPORTS = ("qd_last_error", "qd_check_shape", "qd_query_sizes", "qd_load_weights
            "qd_export_quantized", "qd_prefill", "qd_decode_step", "qd_generate_greedy",
            "qd_free", "qd_profile_kernels", "qd_set_tuning", "qd_prefill_slots",
            "qd_decode_step_slots", "qd_sample", "qd_save_cache", "qd_load_cache",
-           "qd_check_cache", "qd_sha256", "qd_run_op")
+           "qd_check_cache", "qd_sha256", "qd_run_op", "qd_sample_noalloc")
 TUNING = {"attn_max_splits": 0, "attn_min_chunks": 1, "attn_waves": 2, "attn_merge_last": 3,
           "persistent": 4, "persist_splits": 5, "skinny_split": 6, "gemm_splits": 7, "attn_occupancy": 8, "skinny_norm": 9}
 PROF_KERNELS = ("embed", "qkv", "attn", "o", "gateup", "down", "lmhead")
@@ -148,6 +148,8 @@ def load_library(path: str = LIB_PATH):
     lib.qd_sha256.argtypes = [vp, ctypes.c_uint64, vp]
     lib.qd_sample.restype = i32
     lib.qd_sample.argtypes = [vp, i32, vp, ctypes.POINTER(SamplingC), vp, vp, vp, vp]
+    lib.qd_sample_noalloc.restype = i32
+    lib.qd_sample_noalloc.argtypes = [vp, i32, vp, ctypes.POINTER(SamplingC), vp, vp, vp, vp]
     lib.qd_decode_step_slots.restype = i32
     lib.qd_decode_step_slots.argtypes = [vp, i32, vp, vp, vp, vp, vp]
     lib.qd_generate_greedy.restype = i32
@@ -376,9 +378,11 @@ class Model:
                                   _stream_handle()))
 
     def sample(self, logits, seeds, slots=None, temperature=1.0, top_k=40, min_p=0.0,
-               top_p=1.0, repeat_penalty=1.0, presence_penalty=0.0, frequency_penalty=0.0):
+               top_p=1.0, repeat_penalty=1.0, presence_penalty=0.0, frequency_penalty=0.0,
+               noalloc=False):
         """Draws one id per row of ``logits`` (fp32 cuda [B, V]) for slots 0..B-1 (or
-        ``slots``) with per-row ``seeds``; returns int32 cuda [B]."""
+        ``slots``) with per-row ``seeds``; returns int32 cuda [B].  noalloc=True calls
+        qd_sample_noalloc (the library's fixed scratch; at most 16 rows, rows x V <= 2^21)."""
         logits = logits.contiguous()
         B = logits.shape[0]
         sd = np.ascontiguousarray(seeds, dtype=np.uint64).reshape(-1)
@@ -390,9 +394,10 @@ class Model:
         prm = SamplingC(temperature, top_k, min_p, top_p, repeat_penalty, presence_penalty,
                         frequency_penalty)
         nxt = torch.empty(B, dtype=torch.int32, device=self.device)
-        _check(_lib.qd_sample(self._h, B, sl.ctypes.data if sl is not None else None,
-                              ctypes.byref(prm), sd.ctypes.data, logits.data_ptr(),
-                              nxt.data_ptr(), _stream_handle()))
+        fn = _lib.qd_sample_noalloc if noalloc else _lib.qd_sample
+        _check(fn(self._h, B, sl.ctypes.data if sl is not None else None,
+                  ctypes.byref(prm), sd.ctypes.data, logits.data_ptr(),
+                  nxt.data_ptr(), _stream_handle()))
         return nxt
 
     def set_tuning(self, **knobs):

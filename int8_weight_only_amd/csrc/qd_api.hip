@@ -274,6 +274,7 @@ struct qd_model {
   int persist_on = 0;          // tuning knobs (measured slower than the per-step kernels)
   int persist_splits = PERSIST_SPLITS;
   int persist_nwg = 0, persist_lds = 0;
+  void* noalloc_scratch = nullptr;  // this device's address of the sampler's fixed scratch
   int* herr = nullptr;         // pinned copy of the kernel's error flag
   hipEvent_t err_ev = nullptr;
   bool err_pending = false;
@@ -845,6 +846,8 @@ qd_status finish_model(qd_model* m, const hipDeviceProp_t& prop, hipStream_t s) 
   HIPCHK(hipEventCreateWithFlags(&m->err_ev, hipEventDisableTiming));
   m->persist_why = persist_problems(m, prop, &m->persist_nwg, &m->persist_lds);
   m->persist_ok = m->persist_why.empty();
+  // the fixed scratch of qd_sample_noalloc: its address on this device, looked up once here
+  HIPCHK(sample_scratch_address(&m->noalloc_scratch));
   int res4 = 0;  // shapes the decode attention kernel does not take keep the default
   if (attention_decode_residency(m->d.D, m->d.G, 4, &res4) == hipSuccess && res4 > 0)
     m->attn_resident4 = std::min(3, res4);
@@ -1270,12 +1273,22 @@ qd_status qd_decode_step_slots(qd_model* m, int32_t B, const int32_t* slots_host
   return decode_impl(m, B, slots_host, in_ids_dev, logits_dev, next_ids_dev, stream);
 }
 
-qd_status qd_sample(qd_model* m, int32_t B, const int32_t* slots_host, const qd_sampling* params,
-                    const uint64_t* seeds_host, const float* logits_dev, int32_t* next_ids_dev,
-                    qd_stream stream) {
+namespace {
+// qd_sample and qd_sample_noalloc: the same checks and kernels; noalloc takes the per-call
+// scratch (penalized rows, histograms, candidates, counters, staged seeds and slots) from
+// the fixed device array instead of the model's workspace
+qd_status sample_impl(qd_model* m, int32_t B, const int32_t* slots_host, const qd_sampling* params,
+                      const uint64_t* seeds_host, const float* logits_dev, int32_t* next_ids_dev,
+                      qd_stream stream, bool noalloc) {
   g_err.clear();
   if (!m) return fail(QD_ERR_INVALID_ARGUMENTS, "model is NULL");
   if (B < 1 || B > m->lim.max_batch) return fail(QD_ERR_INVALID_ARGUMENTS, "B must be in [1, max_batch]");
+  if (noalloc && (B > NOALLOC_MAX_ROWS || (size_t)B * (size_t)m->d.V > NOALLOC_Z_FLOATS))
+    return fail(QD_ERR_INVALID_ARGUMENTS,
+                "qd_sample_noalloc takes at most " + std::to_string(NOALLOC_MAX_ROWS) +
+                    " rows and rows x vocab <= " + std::to_string(NOALLOC_Z_FLOATS) +
+                    " (its fixed scratch); got " + std::to_string(B) + " rows x " +
+                    std::to_string(m->d.V));
   if (!params || !seeds_host || !logits_dev || !next_ids_dev)
     return fail(QD_ERR_INVALID_ARGUMENTS, "params, seeds_host, logits_dev and next_ids_dev must be set");
   std::string p;
@@ -1295,25 +1308,27 @@ qd_status qd_sample(qd_model* m, int32_t B, const int32_t* slots_host, const qd_
     if (m->host_pos[sl] < 1) p += "slot " + std::to_string(sl) + " holds no prompt; ";
   }
   if (!p.empty()) return fail(QD_ERR_INVALID_ARGUMENTS, p);
+  if (noalloc && !m->noalloc_scratch) return fail(QD_ERR_DEVICE, "the fixed sampler scratch has no device address");
   hipStream_t st = (hipStream_t)stream;
   const Plan& P = m->P;
+  char* na = static_cast<char*>(m->noalloc_scratch);
   QDCHK(stage_wait(m));
   unsigned long long* hs = stage_seeds(m);
   std::memcpy(hs, seeds_host, (size_t)B * 8);
-  unsigned long long* ds = m->ws<unsigned long long>(P.seeds);
+  unsigned long long* ds = noalloc ? reinterpret_cast<unsigned long long*>(na + NA_SEEDS)
+                                   : m->ws<unsigned long long>(P.seeds);
   HIPCHK(hipMemcpyAsync(ds, hs, (size_t)B * 8, hipMemcpyHostToDevice, st));
   const int* row_slot = nullptr;
   if (slots_host) {
     int* hsl = stage_slots(m);
     std::memcpy(hsl, slots_host, (size_t)B * 4);
-    int* dsl = m->ws<int>(P.slot_map);
+    int* dsl = noalloc ? reinterpret_cast<int*>(na + NA_SLOTS) : m->ws<int>(P.slot_map);
     HIPCHK(hipMemcpyAsync(dsl, hsl, (size_t)B * 4, hipMemcpyHostToDevice, st));
     row_slot = dsl;
   }
   QDCHK(stage_mark(m, st));
   SampleArgs a{};
   a.logits = logits_dev; a.ldl = m->d.V;
-  a.z = m->ws<float>(P.samp_z);
   a.counts = m->ws<int>(P.tok_counts);
   a.row_slot = row_slot;
   a.draws = m->ws<int>(P.draws);
@@ -1323,12 +1338,38 @@ qd_status qd_sample(qd_model* m, int32_t B, const int32_t* slots_host, const qd_
   a.temperature = q.temperature; a.min_p = q.min_p; a.top_p = q.top_p;
   a.repeat_penalty = q.repeat_penalty; a.presence_penalty = q.presence_penalty;
   a.frequency_penalty = q.frequency_penalty;
-  a.rowmax = m->ws<unsigned int>(P.smp_rowmax);
-  a.hist = m->ws<unsigned int>(P.smp_hist);
-  a.ncand = m->ws<int>(P.smp_ncand);
-  a.cand = m->ws<unsigned long long>(P.smp_cand);
+  if (noalloc) {
+    // the array keeps the last call's contents: the histograms and counters the kernels
+    // accumulate into are cleared by a fill kernel (no memset node, so capture is safe)
+    a.z = reinterpret_cast<float*>(na + NA_Z);
+    a.cand = reinterpret_cast<unsigned long long*>(na + NA_CAND);
+    a.hist = reinterpret_cast<unsigned int*>(na + NA_HIST);
+    a.rowmax = reinterpret_cast<unsigned int*>(na + NA_ROWMAX);
+    a.ncand = reinterpret_cast<int*>(na + NA_NCAND);
+    HIPCHK(launch_fill_i32(reinterpret_cast<int*>(na + NA_HIST),
+                           (int)((NA_SEEDS - NA_HIST) / 4), 0, st));
+  } else {
+    a.z = m->ws<float>(P.samp_z);
+    a.rowmax = m->ws<unsigned int>(P.smp_rowmax);
+    a.hist = m->ws<unsigned int>(P.smp_hist);
+    a.ncand = m->ws<int>(P.smp_ncand);
+    a.cand = m->ws<unsigned long long>(P.smp_cand);
+  }
   HIPCHK(launch_sample(a, B, st));
   return QD_OK;
+}
+}  // namespace
+
+qd_status qd_sample(qd_model* m, int32_t B, const int32_t* slots_host, const qd_sampling* params,
+                    const uint64_t* seeds_host, const float* logits_dev, int32_t* next_ids_dev,
+                    qd_stream stream) {
+  return sample_impl(m, B, slots_host, params, seeds_host, logits_dev, next_ids_dev, stream, false);
+}
+
+qd_status qd_sample_noalloc(qd_model* m, int32_t B, const int32_t* slots_host,
+                            const qd_sampling* params, const uint64_t* seeds_host,
+                            const float* logits_dev, int32_t* next_ids_dev, qd_stream stream) {
+  return sample_impl(m, B, slots_host, params, seeds_host, logits_dev, next_ids_dev, stream, true);
 }
 
 qd_status qd_generate_greedy(qd_model* m, int32_t B, const int32_t* prompt_ids_host,

@@ -242,6 +242,22 @@ struct SampleArgs {
 };
 constexpr int SMP_CAND_G = 8192;
 hipError_t launch_sample(const SampleArgs& a, int B, hipStream_t st);
+// Fixed scratch of the sampler for callers that cannot allocate (qd_sample_noalloc): a
+// file-scope device array in qd_sample.hip, one per device.  Capacity: NOALLOC_MAX_ROWS rows
+// and rows x vocab <= NOALLOC_Z_FLOATS.  Layout (byte offsets, each 256-aligned):
+constexpr int NOALLOC_MAX_ROWS = 16;
+constexpr size_t NOALLOC_Z_FLOATS = size_t(1) << 21;
+constexpr size_t NA_Z = 0;                                                  // fp32 [rows][V]
+constexpr size_t NA_CAND = NA_Z + NOALLOC_Z_FLOATS * 4;                     // u64 [16][8192]
+constexpr size_t NA_HIST = NA_CAND + size_t(NOALLOC_MAX_ROWS) * SMP_CAND_G * 8;  // u32 [16][256]
+constexpr size_t NA_ROWMAX = NA_HIST + size_t(NOALLOC_MAX_ROWS) * 256 * 4;  // u32 [16]
+constexpr size_t NA_NCAND = NA_ROWMAX + 256;                                // i32 [16]
+constexpr size_t NA_SEEDS = NA_NCAND + 256;                                 // u64 [16]
+constexpr size_t NA_SLOTS = NA_SEEDS + 256;                                 // i32 [16]
+constexpr size_t NOALLOC_SCRATCH_BYTES = NA_SLOTS + 256;
+// The current device's address of that array (looked up with hipGetSymbolAddress on the
+// first call per device, then cached); the device must be current.
+hipError_t sample_scratch_address(void** out);
 // zeroes counts[slot][:] and draws[slot] for slots[0..n) (NULL: slots 0..n-1)
 hipError_t launch_reset_seq(int* counts, int* draws, const int* slots, int n, int V, hipStream_t st);
 hipError_t launch_attention_decode(const AttnDecArgs& a, hipStream_t st);

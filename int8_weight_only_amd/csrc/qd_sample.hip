@@ -21,6 +21,9 @@
 #include "qd_common.h"
 #include "qd_device.h"
 
+#include <map>
+#include <mutex>
+
 namespace qd {
 
 namespace {
@@ -383,6 +386,32 @@ hipError_t launch_reset_seq(int* counts, int* draws, const int* slots, int n, in
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_reset_seq, dim3((V + 1023) / 1024, n), dim3(256), 0, st, counts, draws, slots, V);
   return hipGetLastError();
+}
+
+// Per-call scratch of qd_sample_noalloc, for callers that cannot allocate (code under HIP
+// graph capture, serving loops that forbid hipMalloc): a fixed array that each device holds
+// until the process ends.  Host code never passes the array's name to a kernel (on the host
+// it is only a stand-in for the symbol): its device address comes from hipGetSymbolAddress,
+// once per device, and the kernels receive that address.
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+hipError_t sample_scratch_address(void** out) {
+  static std::mutex mu;
+  static std::map<int, void*> addr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = addr.find(dev);
+  if (it == addr.end()) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    it = addr.emplace(dev, p).first;
+  }
+  *out = it->second;
+  return hipSuccess;
 }
 
 hipError_t launch_sample(const SampleArgs& a, int B, hipStream_t st) {
