@@ -57,6 +57,8 @@ CONFIGS = {
                                 head_dim=128, intermediate=3072, vocab=151936),
                      0, "uniform", 8192, 1005, 4),
     "qwen3-1.7b": (SHAPES["qwen3-1.7b"], 0, "ones", 256, 1000, 3),
+    # Qwen3-0.6B on the first 2048 ids of the long-context prompt (8192 ids, seed 1000)
+    "qwen3-0.6b-2k": (SHAPES["qwen3-0.6b"], 0, "ones", 2048, 1000, 3),
 }
 PERT = 6e-8
 FACTOR = 1.5

@@ -58,3 +58,22 @@ def check_step(gpu_logits, gpu_id, orc_logits, orc_margin, config, where=""):
 def margin_of(logits) -> float:
     top2 = np.partition(np.asarray(logits, np.float64), -2)[-2:]
     return float(top2[1] - top2[0])
+
+
+def safe_draw(logits, counts, p, u, tol=1e-5):
+    """True when no decision of the oracle's draw sits within ``tol`` (relative) of a
+    boundary, so fp32 and fp64 arithmetic must agree on the token."""
+    from oracle.sampling import penalize, sample_token
+    tok, d = sample_token(logits, counts, p, u, detail=True)
+    z = np.sort(penalize(logits, counts, p) / p.temperature)[::-1]
+    if z.size > p.top_k and z[p.top_k - 1] - z[p.top_k] <= tol * max(1.0, abs(z[p.top_k])):
+        return tok, False
+    w = d["w"]
+    if np.min(np.abs(w - p.min_p)) <= tol:
+        return tok, False
+    cum = d["cum"]
+    if np.min(np.abs(cum - p.top_p * cum[-1])) <= tol * cum[-1]:
+        return tok, False
+    if np.min(np.abs(cum[: d["n_topp"]] - d["t"])) <= tol * cum[-1]:
+        return tok, False
+    return tok, True

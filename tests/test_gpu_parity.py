@@ -14,7 +14,7 @@ torch = pytest.importorskip("torch")
 
 from oracle import Oracle, quantize_model, quantize_rows
 from workloads import SHAPES, ModelShape, make_weights, make_prompt, make_prompts
-from parity import say, check_step, logit_err, margin_of, bar_for, STRICT_TOL
+from parity import say, check_step, logit_err, margin_of, bar_for, STRICT_TOL, safe_draw as _safe_margins
 
 pytestmark = pytest.mark.gpu
 
@@ -431,25 +431,6 @@ def test_continuous_batching_slots_teacher_forced():
 
 SAMPLING = dict(temperature=0.8, top_k=40, min_p=0.05, top_p=0.9, repeat_penalty=1.3,
                 presence_penalty=0.2, frequency_penalty=0.1)
-
-
-def _safe_margins(logits, counts, p, u, tol=1e-5):
-    """True when no decision of the oracle's draw sits within ``tol`` (relative) of a
-    boundary, so fp32 and fp64 arithmetic must agree on the token."""
-    from oracle.sampling import penalize, sample_token
-    tok, d = sample_token(logits, counts, p, u, detail=True)
-    z = np.sort(penalize(logits, counts, p) / p.temperature)[::-1]
-    if z.size > p.top_k and z[p.top_k - 1] - z[p.top_k] <= tol * max(1.0, abs(z[p.top_k])):
-        return tok, False
-    w = d["w"]
-    if np.min(np.abs(w - p.min_p)) <= tol:
-        return tok, False
-    cum = d["cum"]
-    if np.min(np.abs(cum - p.top_p * cum[-1])) <= tol * cum[-1]:
-        return tok, False
-    if np.min(np.abs(cum[: d["n_topp"]] - d["t"])) <= tol * cum[-1]:
-        return tok, False
-    return tok, True
 
 
 # the second set keeps nearly the whole vocabulary: too many candidates lie far from the
