@@ -744,6 +744,135 @@ __global__ __launch_bounds__(512) void k_gemm(GemmArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
+// Prefill GEMM for many token rows (the tile grid fills the GPU): a 128x128 output tile per
+// work-group of 4 waves, each wave a 64x64 block of 4x4 MFMA 16x16x32 tiles, so every
+// fragment read from LDS feeds four MFMAs (the 64x64-tile kernel's 32x32 wave blocks get
+// two, which caps its MFMA rate at the LDS read bandwidth).  k advances 64 per LDS stage,
+// double-buffered with one barrier per stage; the global loads of stage s+2 are in flight
+// while stage s is multiplied, and the int8 weights become bf16 (exactly) when a stage is
+// written to LDS.  Work-groups are dispatched round-robin over the 8 XCDs: XCD x takes a
+// contiguous run of tiles in row-major (token-row, channel-column) order, so the tiles that
+// share one L2 share token rows and walk neighbouring weight rows.  Residual inputs are read
+// in the epilogue.  Two work-groups fit on a CU (73.7 KB of LDS each).
+template <int EPI>
+__global__ __launch_bounds__(256, 2) void k_gemm_big(GemmArgs a) {
+  constexpr int BM = 128, BN = 128, BK = 64;
+  constexpr int LDT = BK + 8;  // 144-byte LDS rows: fragment reads of 8 lanes hit 8 bank groups
+  constexpr int OOB = (int)0x80000000;
+  __shared__ __align__(16) bf16_t As[2][BM][LDT];
+  __shared__ __align__(16) bf16_t Ws[2][BN][LDT];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid & 1, wn = wid >> 1;
+  const int grp = lane >> 4, r16 = lane & 15;
+  const int ntn = (a.N + BN - 1) / BN, ntm = (a.M + BM - 1) / BM, ntiles = ntn * ntm;
+  // XCD-contiguous tile order: XCD x = blockIdx % 8 owns tiles [start_x, start_x + count_x)
+  const int q8 = ntiles >> 3, r8 = ntiles & 7, xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
+  const int t = xcd * q8 + min(xcd, r8) + loc;
+  const int m0 = (t / ntn) * BM, n0 = (t % ntn) * BN;
+  const int nsteps = (a.K + BK - 1) / BK;
+
+  // rows past M (N) lie past the end of A (W) and read zero, as do k past K
+  const __amdgpu_buffer_rsrc_t arsc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.A, 0, a.M * a.lda * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t wrsc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.W, 0, a.N * a.K, 0x00020000);
+  // staging: thread tid brings k 32h .. 32h+31 (h = tid & 1) of tile row tid >> 1 for A
+  // (64 bytes) and W (32 bytes)
+  const int sr = tid >> 1, sh = tid & 1;
+  struct Stage { uint4 a[4]; uint4 w[2]; };
+  auto fetch = [&](int step, Stage& q) {
+    const int k = step * BK + 32 * sh;
+    const bool ok = k < a.K;  // K is a multiple of 32
+    const int ab = ((m0 + sr) * a.lda + k) * 2;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      q.a[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(arsc, ok ? ab + 16 * j : OOB, 0, 0));
+    const int wb = (n0 + sr) * a.K + k;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      q.w[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wrsc, ok ? wb + 16 * j : OOB, 0, 0));
+  };
+  auto stash = [&](const Stage& q, int buf) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(&As[buf][sr][32 * sh + 8 * j]) = q.a[j];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      *reinterpret_cast<bf16x8_t*>(&Ws[buf][sr][32 * sh + 16 * j]) = i8x8_to_bf16x8(make_uint2(q.w[j].x, q.w[j].y));
+      *reinterpret_cast<bf16x8_t*>(&Ws[buf][sr][32 * sh + 16 * j + 8]) = i8x8_to_bf16x8(make_uint2(q.w[j].z, q.w[j].w));
+    }
+  };
+
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  Stage q[2];
+  fetch(0, q[0]);
+  fetch(1, q[1]);
+  stash(q[0], 0);
+  __syncthreads();
+  for (int s0 = 0; s0 < nsteps; s0 += 2) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int st = s0 + u;  // steps past the end multiply zeros (whole pairs of steps)
+      fetch(st + 2, q[u]);    // into the slot step st vacated
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        const int kk = 32 * sub + 8 * grp;
+        bf16x8_t af[4], bw[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          af[mt] = *reinterpret_cast<const bf16x8_t*>(&As[u][wm * 64 + mt * 16 + r16][kk]);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          bw[nt] = *reinterpret_cast<const bf16x8_t*>(&Ws[u][wn * 64 + nt * 16 + r16][kk]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt)
+            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt], bw[nt], acc[mt][nt], 0, 0, 0);
+      }
+      stash(q[u ^ 1], u ^ 1);  // step st + 1
+      __syncthreads();
+    }
+  }
+
+  // scales of this lane's four output channels (gate/up: two pairs)
+  float gsc[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int n = n0 + wn * 64 + nt * 16 + r16;
+    gsc[nt] = a.scale[n < a.N ? n : 0];
+  }
+  // lane holds D[4*(lane/16)+i][lane%16] of each 16x16 tile: token rows, channel columns
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + wm * 64 + mt * 16 + 4 * grp + i;
+      if (m >= a.M) continue;
+      if (EPI == EPI_SILU) {
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+          const int ng = n0 + wn * 64 + pr * 32 + r16;
+          if (ng + GU_BLOCK < a.N)
+            gemm_epilogue<EPI_SILU>(a, m, ng, acc[mt][2 * pr][i], acc[mt][2 * pr + 1][i],
+                                    gsc[2 * pr], gsc[2 * pr + 1]);
+        }
+      } else {
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const int n = n0 + wn * 64 + nt * 16 + r16;
+          if (n < a.N) gemm_epilogue<EPI>(a, m, n, acc[mt][nt][i], 0.0f, gsc[nt], 0.0f);
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
 // batched decode GEMM on MFMA ("skinny": 2..64 token rows, weights swept once):
 // Y[t][n] = scale[n] * sum_k X[t][k] * W[n][k], X bf16 (already RMS-normalized where the
 // model normalizes), W int8 converted exactly to bf16 in registers.  The MFMA A operand is
@@ -2348,6 +2477,17 @@ hipError_t launch_gemm(const GemmArgs& a0, hipStream_t st, int* splits_used) {
   if ((a.K & 31) || (size_t)(a.M + 64) * a.lda * 2 > 0x7FFFFFFFu || (size_t)(a.N + 64) * a.K > 0x7FFFFFFFu ||
       (size_t)(a.M + 64) * a.ldo * 2 > 0x7FFFFFFFu)
     return hipErrorInvalidValue;
+  // many token rows: 128x128 tiles when they alone give every CU at least one
+  const int big_tiles = ((a.N + 127) / 128) * ((a.M + 127) / 128);
+  if (big_tiles >= 256 && a.use_big != 0) {
+    if (splits_used) *splits_used = 1;
+    switch (a.epi) {
+      case EPI_STORE: hipLaunchKernelGGL(k_gemm_big<EPI_STORE>, dim3(big_tiles), dim3(256), 0, st, a); break;
+      case EPI_RESID: hipLaunchKernelGGL(k_gemm_big<EPI_RESID>, dim3(big_tiles), dim3(256), 0, st, a); break;
+      default: hipLaunchKernelGGL(k_gemm_big<EPI_SILU>, dim3(big_tiles), dim3(256), 0, st, a); break;
+    }
+    return hipGetLastError();
+  }
   const int tiles = ((a.N + 63) / 64) * ((a.M + 63) / 64);
   // split K when the tile grid leaves most of the 256 CUs idle
   int splits = 1;
