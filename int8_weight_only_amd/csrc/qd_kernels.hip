@@ -753,14 +753,20 @@ __global__ __launch_bounds__(512) void k_gemm(GemmArgs a) {
 // written to LDS.  Work-groups are dispatched round-robin over the 8 XCDs: XCD x takes a
 // contiguous run of tiles in row-major (token-row, channel-column) order, so the tiles that
 // share one L2 share token rows and walk neighbouring weight rows.  Residual inputs are read
-// in the epilogue.  Two work-groups fit on a CU (73.7 KB of LDS each).
+// in the epilogue.  Two work-groups fit on a CU (68 KB of LDS each).
 template <int EPI>
 __global__ __launch_bounds__(256, 2) void k_gemm_big(GemmArgs a) {
   constexpr int BM = 128, BN = 128, BK = 64;
-  constexpr int LDT = BK + 8;  // 144-byte LDS rows: fragment reads of 8 lanes hit 8 bank groups
   constexpr int OOB = (int)0x80000000;
-  __shared__ __align__(16) bf16_t As[2][BM][LDT];
-  __shared__ __align__(16) bf16_t Ws[2][BN][LDT];
+  // LDS holds each 16-row x 32-k operand fragment in MFMA lane order: lane l's 8 values
+  // (row l % 16, k 8*(l/16) ..) at byte 16*l, so a fragment read is 1 KB of consecutive
+  // bytes; fragment f of a stage sits at 1088*f, so odd fragments start 16 banks (of 32)
+  // further along than even ones and the staging writes of a row's two k halves, which go
+  // to fragments 2b and 2b+1 from neighbouring lanes, use disjoint banks
+  constexpr int FRAG = 1088;                    // bytes per fragment slot
+  constexpr int NFRAG = (BM / 16) * (BK / 32);  // 16 fragments per operand per stage
+  __shared__ __align__(16) unsigned char Ab[2][NFRAG * FRAG];
+  __shared__ __align__(16) unsigned char Wb[2][NFRAG * FRAG];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid & 1, wn = wid >> 1;
   const int grp = lane >> 4, r16 = lane & 15;
@@ -776,9 +782,11 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(GemmArgs a) {
       __builtin_amdgcn_make_buffer_rsrc((void*)a.A, 0, a.M * a.lda * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t wrsc =
       __builtin_amdgcn_make_buffer_rsrc((void*)a.W, 0, a.N * a.K, 0x00020000);
-  // staging: thread tid brings k 32h .. 32h+31 (h = tid & 1) of tile row tid >> 1 for A
-  // (64 bytes) and W (32 bytes)
+  // staging: thread tid brings k 32h .. 32h+31 (h = tid & 1) of tile row r = tid >> 1 for A
+  // (64 bytes) and W (32 bytes); its 8-value chunk j lands in fragment 2*(r/16) + h at lane
+  // position r%16 + 16j
   const int sr = tid >> 1, sh = tid & 1;
+  const int sfrag = ((sr >> 4) * 2 + sh) * FRAG + (sr & 15) * 16;
   struct Stage { uint4 a[4]; uint4 w[2]; };
   auto fetch = [&](int step, Stage& q) {
     const int k = step * BK + 32 * sh;
@@ -794,11 +802,11 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(GemmArgs a) {
   };
   auto stash = [&](const Stage& q, int buf) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(&As[buf][sr][32 * sh + 8 * j]) = q.a[j];
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(&Ab[buf][sfrag + 256 * j]) = q.a[j];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      *reinterpret_cast<bf16x8_t*>(&Ws[buf][sr][32 * sh + 16 * j]) = i8x8_to_bf16x8(make_uint2(q.w[j].x, q.w[j].y));
-      *reinterpret_cast<bf16x8_t*>(&Ws[buf][sr][32 * sh + 16 * j + 8]) = i8x8_to_bf16x8(make_uint2(q.w[j].z, q.w[j].w));
+      *reinterpret_cast<bf16x8_t*>(&Wb[buf][sfrag + 512 * j]) = i8x8_to_bf16x8(make_uint2(q.w[j].x, q.w[j].y));
+      *reinterpret_cast<bf16x8_t*>(&Wb[buf][sfrag + 512 * j + 256]) = i8x8_to_bf16x8(make_uint2(q.w[j].z, q.w[j].w));
     }
   };
 
@@ -820,14 +828,13 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(GemmArgs a) {
       fetch(st + 2, q[u]);    // into the slot step st vacated
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
-        const int kk = 32 * sub + 8 * grp;
         bf16x8_t af[4], bw[4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
-          af[mt] = *reinterpret_cast<const bf16x8_t*>(&As[u][wm * 64 + mt * 16 + r16][kk]);
+          af[mt] = *reinterpret_cast<const bf16x8_t*>(&Ab[u][((wm * 4 + mt) * 2 + sub) * FRAG + 16 * lane]);
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt)
-          bw[nt] = *reinterpret_cast<const bf16x8_t*>(&Ws[u][wn * 64 + nt * 16 + r16][kk]);
+          bw[nt] = *reinterpret_cast<const bf16x8_t*>(&Wb[u][((wn * 4 + nt) * 2 + sub) * FRAG + 16 * lane]);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
