@@ -250,7 +250,7 @@ struct qd_model {
   char* WS = nullptr;  // workspace
   int device = 0;
   hipStream_t cap_stream = nullptr;
-  std::map<std::tuple<int, int, int, int>, hipGraphExec_t> graphs;  // (B, nsplit, split_len, steps)
+  std::map<std::tuple<int, int, int, int>, hipGraphExec_t> graphs;  // (B, nsplit, split_len*16 + waves, steps)
   std::vector<int> host_pos;                                   // mirror of device positions
   hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
   // pinned host staging for prompt ids and prefill metadata: asynchronous uploads read
@@ -301,11 +301,11 @@ void attn_split(int ctx, int cap, int max_splits, int min_chunks, int occupancy,
                 int* nsplit, int* split_len);
 
 // decode-attention waves per work-group: eight when the (row, KV head) pairs alone cover
-// the CUs, else four
-int attn_waves_for(const qd_model* m, int B);
+// the CUs or the context is long (more than ATT_LONG_CTX positions), else four
+int attn_waves_for(const qd_model* m, int B, int ctx);
 // work-groups per CU the split targets: as many as stay resident (the 8-wave kernel holds
 // one per CU, the 4-wave kernel three; measured best at B = 1..32)
-int attn_occupancy_for(const qd_model* m, int B);
+int attn_occupancy_for(const qd_model* m, int B, int ctx);
 
 void attn_split(int ctx, int cap, int max_splits, int min_chunks, int occupancy, int rows_x_kv,
                 int* nsplit, int* split_len) {
@@ -419,18 +419,22 @@ qd_status dec_qkv(qd_model* m, int l, int B, hipStream_t st) {
                   m->w<float>(o.qkv_s), d.NQKV, d.d, EPI_STORE, m->ws<bf16_t>(m->P.qkv), d.NQKV, st);
 }
 
-int attn_waves_for(const qd_model* m, int B) {
-  return m->attn_waves ? m->attn_waves : (B * m->d.KV >= 256 ? 8 : 4);
+// measured at B = 1, Qwen3-0.6B: 383 positions 7.1 us (4 waves) against 7.6 (8 waves);
+// ~8.2K positions 16.2 us (4 waves) against 14.5 (8 waves)
+constexpr int ATT_LONG_CTX = 2048;
+int attn_waves_for(const qd_model* m, int B, int ctx) {
+  if (m->attn_waves) return m->attn_waves;
+  return (B * m->d.KV >= 256 || ctx > ATT_LONG_CTX) ? 8 : 4;
 }
 
 // eight waves: one work-group per CU (measured best at B x KV >= 256); four waves: as many
 // as fit on a CU, at most three
-int attn_occupancy_for(const qd_model* m, int B) {
+int attn_occupancy_for(const qd_model* m, int B, int ctx) {
   if (m->attn_occupancy) return m->attn_occupancy;
-  return attn_waves_for(m, B) == 8 ? 1 : m->attn_resident4;
+  return attn_waves_for(m, B, ctx) == 8 ? 1 : m->attn_resident4;
 }
 
-qd_status dec_attn(qd_model* m, int l, int B, int nsplit, int split_len, hipStream_t st,
+qd_status dec_attn(qd_model* m, int l, int B, int nsplit, int split_len, int waves, hipStream_t st,
                    const int* row_slot = nullptr) {
   const Dims& d = m->d;
   const LayerOff& o = m->P.L[l];
@@ -443,7 +447,7 @@ qd_status dec_attn(qd_model* m, int l, int B, int nsplit, int split_len, hipStre
   aa.kcache = m->kcache(l); aa.vcache = m->vcache(l);
   aa.H = d.H; aa.KV = d.KV; aa.D = d.D; aa.max_ctx = m->lim.max_ctx; aa.B = B;
   aa.split_len = split_len; aa.nsplit = nsplit;
-  aa.nwaves = attn_waves_for(m, B);
+  aa.nwaves = waves;
   aa.merge_last = m->attn_merge_last;
   aa.part_o = m->ws<float>(m->P.part_o); aa.part_ml = m->ws<float>(m->P.part_ml);
   aa.counters = m->ws<unsigned int>(m->P.att_cnt);
@@ -481,14 +485,14 @@ qd_status dec_down(qd_model* m, int l, int B, hipStream_t st) {
 
 // one decode step; positions read from the device
 qd_status enqueue_decode(qd_model* m, int B, const int* in_ids, float* logits, int* next_ids,
-                         bool write_out, int nsplit, int split_len, hipStream_t st,
+                         bool write_out, int nsplit, int split_len, int waves, hipStream_t st,
                          const int* row_slot = nullptr) {
   const Dims& d = m->d;
   HIPCHK(launch_embed(in_ids, B, m->w<int8_t>(m->P.emb_q), m->w<float>(m->P.emb_s), d.d, d.V,
                       m->ws<bf16_t>(m->P.x), st, m->ws<int>(m->P.tok_counts), row_slot));
   for (int l = 0; l < d.L; ++l) {
     QDCHK(dec_qkv(m, l, B, st));
-    QDCHK(dec_attn(m, l, B, nsplit, split_len, st, row_slot));
+    QDCHK(dec_attn(m, l, B, nsplit, split_len, waves, st, row_slot));
     QDCHK(dec_o(m, l, B, st));
     QDCHK(dec_gateup(m, l, B, st));
     QDCHK(dec_down(m, l, B, st));
@@ -1228,10 +1232,10 @@ qd_status decode_impl(qd_model* m, int32_t B, const int32_t* slots, const int32_
       row_slot = ds;
     }
     int nsplit, split_len;
-    attn_split(ctx, m->P.nsplit_cap, m->attn_max_splits, m->attn_min_chunks, attn_occupancy_for(m, B), B * m->d.KV, &nsplit,
+    attn_split(ctx, m->P.nsplit_cap, m->attn_max_splits, m->attn_min_chunks, attn_occupancy_for(m, B, ctx), B * m->d.KV, &nsplit,
                &split_len);
-    s = enqueue_decode(m, B, in_ids_dev, logits_dev, next_ids_dev, false, nsplit, split_len, st,
-                       row_slot);
+    s = enqueue_decode(m, B, in_ids_dev, logits_dev, next_ids_dev, false, nsplit, split_len,
+                       attn_waves_for(m, B, ctx), st, row_slot);
   }
   if (s == QD_OK)
     for (int b = 0; b < B; ++b) m->host_pos[slots ? slots[b] : b] += 1;
@@ -1427,11 +1431,12 @@ qd_status qd_generate_greedy(qd_model* m, int32_t B, const int32_t* prompt_ids_h
     int nsplit, split_len;
     // round the context up so one captured graph serves many calls
     const int ctx_cap = std::min(m->lim.max_ctx, ((need + 255) / 256) * 256);
-    attn_split(ctx_cap, P.nsplit_cap, m->attn_max_splits, m->attn_min_chunks, attn_occupancy_for(m, B), B * m->d.KV, &nsplit, &split_len);
+    attn_split(ctx_cap, P.nsplit_cap, m->attn_max_splits, m->attn_min_chunks, attn_occupancy_for(m, B, ctx_cap), B * m->d.KV, &nsplit, &split_len);
+    const int waves = attn_waves_for(m, B, ctx_cap);
     // decode steps replayed from captured graphs of GEN_GRAPH_STEPS consecutive steps (the
     // positions and the step counter live on the device), the remainder one step each
     auto graph_for = [&](int n, hipGraphExec_t* out) -> qd_status {
-      auto key = std::make_tuple(B, nsplit, split_len, n);
+      auto key = std::make_tuple(B, nsplit, split_len * 16 + waves, n);
       auto it = m->graphs.find(key);
       if (it != m->graphs.end()) {
         *out = it->second;
@@ -1441,7 +1446,7 @@ qd_status qd_generate_greedy(qd_model* m, int32_t B, const int32_t* prompt_ids_h
       HIPCHK(hipStreamBeginCapture(m->cap_stream, hipStreamCaptureModeThreadLocal));
       qd_status cs = QD_OK;
       for (int i = 0; i < n && cs == QD_OK; ++i)
-        cs = enqueue_decode(m, B, next_ids, nullptr, next_ids, true, nsplit, split_len, m->cap_stream);
+        cs = enqueue_decode(m, B, next_ids, nullptr, next_ids, true, nsplit, split_len, waves, m->cap_stream);
       hipError_t ee = hipStreamEndCapture(m->cap_stream, &graph);
       if (cs != QD_OK) return cs;
       if (ee != hipSuccess) return fail(QD_ERR_DEVICE, std::string("hipStreamEndCapture: ") + hipGetErrorString(ee));
@@ -1502,7 +1507,8 @@ qd_status qd_profile_kernels(qd_model* m, int32_t B, int32_t iters, float* us_ou
     ctx = std::max(ctx, m->host_pos[b] + 1);
   }
   int nsplit, split_len;
-  attn_split(ctx, m->P.nsplit_cap, m->attn_max_splits, m->attn_min_chunks, attn_occupancy_for(m, B), B * m->d.KV, &nsplit, &split_len);
+  attn_split(ctx, m->P.nsplit_cap, m->attn_max_splits, m->attn_min_chunks, attn_occupancy_for(m, B, ctx), B * m->d.KV, &nsplit, &split_len);
+  const int waves = attn_waves_for(m, B, ctx);
   hipStream_t st = (hipStream_t)stream;
   int* scratch_ids = m->ws<int>(m->P.ids);   // prompt-id area doubles as the profiling id list
   HIPCHK(launch_fill_i32(scratch_ids, B, 0, st));
@@ -1519,7 +1525,7 @@ qd_status qd_profile_kernels(qd_model* m, int32_t B, int32_t iters, float* us_ou
                                 m->d.d, m->d.V, m->ws<bf16_t>(m->P.x), st));
             break;
           case QD_PROF_QKV: QDCHK(dec_qkv(m, i % m->d.L, B, st)); break;
-          case QD_PROF_ATTN: QDCHK(dec_attn(m, i % m->d.L, B, nsplit, split_len, st)); break;
+          case QD_PROF_ATTN: QDCHK(dec_attn(m, i % m->d.L, B, nsplit, split_len, waves, st)); break;
           case QD_PROF_O: QDCHK(dec_o(m, i % m->d.L, B, st)); break;
           case QD_PROF_GATEUP: QDCHK(dec_gateup(m, i % m->d.L, B, st)); break;
           case QD_PROF_DOWN: QDCHK(dec_down(m, i % m->d.L, B, st)); break;

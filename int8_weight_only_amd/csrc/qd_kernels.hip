@@ -1553,10 +1553,13 @@ __global__ __launch_bounds__(256) void k_qk_rope(RopeArgs a) {
 // group's G query heads and of its key head, done in LDS from the raw projections; the
 // split that holds position p writes the new K and V rows to the cache and every split
 // uses the fresh rows for p from LDS.  Each wave owns 16 positions of every 64-position
-// chunk and keeps its own online-softmax state (no block barrier inside the loop); K and
-// V tiles are requested one chunk ahead, the first ones before the prologue.  The four
-// waves merge in LDS at the end.  Fused behind: with several splits, each writes its
-// partial (max, sum, unnormalized output); the split that finishes last merges them.
+// chunk and keeps its own online-softmax state in base 2 (no block barrier inside the
+// loop); K and V tiles, all 16-byte loads, are requested one chunk ahead, the first ones
+// before the prologue.  A lane's scores become the P*V lanes' probabilities through a
+// per-wave LDS slot, and each P*V lane accumulates 8 output dims of its own positions
+// across all chunks (reduced across lanes once at the end).  The waves merge in LDS at the
+// end.  Fused behind: with several splits, each writes its partial (base-2 max, sum,
+// unnormalized output); the split that finishes last merges them.
 // WIDE: more than SB = 8 splits, merged by the batched path below (its own instantiation, so
 // the short-context kernel keeps its registers and LDS)
 template <int D, int G, int NW, bool WIDE>
@@ -1564,15 +1567,21 @@ __global__ __launch_bounds__(64 * NW) void k_attn_dec(AttnDecArgs a) {
   constexpr int NT = 64 * NW;              // threads
   constexpr int CHW = 16 * NW;             // positions per iteration
   constexpr int HALF = D / 2;
-  constexpr int KQ = D / 4;                    // key elements per lane (4 lanes per position)
-  constexpr int KV4 = KQ / 8;                  // uint4 loads per lane per key row
-  constexpr int DPL = D >= 64 ? D / 64 : 1;    // output dims per lane
-  constexpr int VW = DPL >= 2 ? DPL / 2 : 1;   // 32-bit words of V per lane per row
+  // scores: 4 lanes per position, lane part of position tl holds key dims 32j + 8*part .. +8
+  // (16-byte chunks j < KV4), so the 4 lanes of a position read 64 contiguous bytes per load
+  constexpr int KV4 = D / 32;
+  // P*V: lane (vch = lane % CL, vu = lane / CL) holds dims 8*vch .. +8 of the wave's
+  // positions vu, vu + PSL, ... (VR rows as 16-byte loads; CL lanes cover a 256-byte row)
+  // and accumulates its own partial output over every chunk; the PSL position slots are
+  // added once, after the last chunk
+  constexpr int CL = D / 8, PSL = 64 / CL, VR = 16 / PSL;
+  constexpr float LOG2E = 1.4426950408889634f;
   __shared__ __align__(16) float qs[G][D];
   __shared__ __align__(16) bf16_t qb[G][D];  // the same q as bf16 (it is bf16-exact)
   __shared__ float kn[D], vn[D];
   __shared__ float wm[NW][G], wl[NW][G];
   __shared__ float wo[NW][G][D];
+  __shared__ __align__(16) float ps[NW][G][16];  // each wave's probabilities of its 16 positions
   __shared__ int last_flag;
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   // wave index as a scalar: per-wave choices (which head, which gain vector) stay scalar
@@ -1588,7 +1597,7 @@ __global__ __launch_bounds__(64 * NW) void k_attn_dec(AttnDecArgs a) {
   bf16_t* Kb = a.kcache + ((size_t)sl * a.KV + g) * a.max_ctx * D;
   bf16_t* Vb = a.vcache + ((size_t)sl * a.KV + g) * a.max_ctx * D;
   const bool owner = (t_begin <= p) && (p < t_begin + a.split_len);
-  const bool vlane = (D >= 64) || (lane < D);
+  const int vch = lane % CL, vu = lane / CL;
 
   // ---- K/V tiles of the first chunk, requested before anything else ----
   // Buffer loads: a position outside the split (or p itself, taken from LDS) reads zero
@@ -1600,30 +1609,23 @@ __global__ __launch_bounds__(64 * NW) void k_attn_dec(AttnDecArgs a) {
       __builtin_amdgcn_make_buffer_rsrc(Vb, 0, a.max_ctx * D * 2, 0x00020000);
   constexpr int OOB = (int)0x80000000;
   uint4 kc[KV4], kx[KV4];
-  uint32_t vc[16][VW], vx[16][VW];
+  uint4 vc[VR], vx[VR];
   // (the wave index here is the per-lane one: with scalar validity conditions the
   // compiler branches around groups of loads instead of selecting offsets)
   const int wv = tid >> 6;
-  auto load_tiles = [&](uint4 (&kk)[KV4], uint32_t (&vv)[16][VW], int t0) {
+  auto load_tiles = [&](uint4 (&kk)[KV4], uint4 (&vv)[VR], int t0) {
     const int t = t0 + 16 * wv + tl;
     const bool kok = t < t_end && t != p;
 #pragma unroll
     for (int j = 0; j < KV4; ++j)
       kk[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            krs, kok ? (t * D + part * KQ + 8 * j) * 2 : OOB, 0, 0));
+                                            krs, kok ? (t * D + 32 * j + 8 * part) * 2 : OOB, 0, 0));
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int tv = t0 + 16 * wv + i;
-      const bool ok = tv < t_end && tv != p && vlane;
-#pragma unroll
-      for (int w = 0; w < VW; ++w) {
-        if (DPL >= 2) {
-          vv[i][w] = __builtin_amdgcn_raw_buffer_load_b32(
-              vrs, ok ? (tv * D + DPL * lane + 2 * w) * 2 : OOB, 0, 0);
-        } else {
-          vv[i][w] = __builtin_amdgcn_raw_buffer_load_b16(vrs, ok ? (tv * D + lane) * 2 : OOB, 0, 0);
-        }
-      }
+    for (int i = 0; i < VR; ++i) {
+      const int tv = t0 + 16 * wv + vu + PSL * i;
+      const bool ok = tv < t_end && tv != p;
+      vv[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            vrs, ok ? (tv * D + 8 * vch) * 2 : OOB, 0, 0));
     }
   };
   // ---- QK-norm + RoPE of the G query heads and the key head; copy of v ----
@@ -1702,37 +1704,41 @@ __global__ __launch_bounds__(64 * NW) void k_attn_dec(AttnDecArgs a) {
   }
   __syncthreads();
 
-  const float scale = 1.0f / sqrtf((float)D);
-  float m[G], l[G], o[G][DPL];
+  // scores in base 2: z = q.k * log2(e) / sqrt(D), weights 2^(z - m)
+  const float scale2 = LOG2E / sqrtf((float)D);
+  float m[G], l[G], o[G][8];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     m[h] = -INFINITY;
     l[h] = 0.0f;
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) o[h][e] = 0.0f;
+    for (int e = 0; e < 8; ++e) o[h][e] = 0.0f;
   }
   for (int t0 = t_begin; t0 < t_end; t0 += CHW) {
     const int t = t0 + 16 * wid + tl;
-    // scores of this lane's position (4 lanes per position, KQ key elements each)
+    // scores of this lane's position (4 lanes per position, D/4 key elements each)
     float sp[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) sp[h] = 0.0f;
     if (t == p) {
 #pragma unroll
-      for (int j = 0; j < KQ; ++j) {
-        const float kv = kn[part * KQ + j];
+      for (int j = 0; j < KV4; ++j)
 #pragma unroll
-        for (int h = 0; h < G; ++h) sp[h] += qs[h][part * KQ + j] * kv;
-      }
+        for (int e = 0; e < 8; ++e) {
+          const int dd = 32 * j + 8 * part + e;
+          const float kv = kn[dd];
+#pragma unroll
+          for (int h = 0; h < G; ++h) sp[h] += qs[h][dd] * kv;
+        }
     } else {
       // q as bf16 pairs from LDS (one 16-byte read per 8 elements, broadcast to the lanes of
-      // a key quarter), two-term bf16 dot products against the raw K words
+      // a key part), two-term bf16 dot products against the raw K words
 #pragma unroll
       for (int j = 0; j < KV4; ++j) {
         const uint32_t w4[4] = {kc[j].x, kc[j].y, kc[j].z, kc[j].w};
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-          const uint4 q4 = *reinterpret_cast<const uint4*>(&qb[h][part * KQ + 8 * j]);
+          const uint4 q4 = *reinterpret_cast<const uint4*>(&qb[h][32 * j + 8 * part]);
           const uint32_t qw[4] = {q4.x, q4.y, q4.z, q4.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e)
@@ -1746,70 +1752,87 @@ __global__ __launch_bounds__(64 * NW) void k_attn_dec(AttnDecArgs a) {
     if (more) load_tiles(kx, vx, t0 + CHW);
     const bool valid = t < t_end;
     // The reference maximum m of a head moves (a wave reduction, and the rescale of o and
-    // l) only when a score exceeds it by more than TAU, so exp(z - m) <= e^TAU; otherwise
-    // the chunk costs one ballot.  l is kept per lane (its own positions) and summed over
-    // the wave once, after the last chunk.
-    constexpr float TAU = 8.0f;
+    // l) only when a score exceeds it by more than TAU (base 2), so 2^(z - m) <= 2^TAU;
+    // otherwise the chunk costs one ballot.  l is kept per lane (its own positions) and
+    // summed over the wave once, after the last chunk.
+    constexpr float TAU = 12.0f;
     float pr[G], zs[G];
     bool need = false;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       sp[h] += __shfl_xor(sp[h], 1, 64);
       sp[h] += __shfl_xor(sp[h], 2, 64);
-      zs[h] = valid ? sp[h] * scale : -INFINITY;
+      zs[h] = valid ? sp[h] * scale2 : -INFINITY;
       need = need || (zs[h] > m[h] + TAU);
     }
     if (__any(need)) {
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         const float mnew = fmaxf(m[h], wave_max(zs[h]));
-        const float alpha = (m[h] == -INFINITY) ? 0.0f : expf(m[h] - mnew);
+        const float alpha = (m[h] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m[h] - mnew);
         l[h] *= alpha;
         m[h] = mnew;
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) o[h][e] *= alpha;
+        for (int e = 0; e < 8; ++e) o[h][e] *= alpha;
       }
     }
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      pr[h] = valid ? expf(zs[h] - m[h]) : 0.0f;
+      pr[h] = valid ? __builtin_amdgcn_exp2f(zs[h] - m[h]) : 0.0f;
       l[h] += part == 0 ? pr[h] : 0.0f;
     }
-    // P*V: lanes over head dims, the wave's 16 positions in turn
+    // the wave's 16 probabilities per head go through LDS to the P*V lanes (one wave
+    // writes and reads its own slots: the fences order the accesses within the wave)
+    if (part == 0) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int tv = t0 + 16 * wid + i;
-      float vf[DPL];
-      if (tv == p) {
+      for (int h = 0; h < G; ++h) ps[wid][h][tl] = pr[h];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // P*V: each lane its VR positions x 8 dims (position p itself reads zero here and is
+    // added from LDS below)
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) vf[e] = vlane ? vn[DPL * lane + e] : 0.0f;
-      } else if (DPL >= 2) {
+    for (int i = 0; i < VR; ++i) {
+      const uint32_t w4[4] = {vc[i].x, vc[i].y, vc[i].z, vc[i].w};
+      float vf[8];
 #pragma unroll
-        for (int w = 0; w < VW; ++w) {
-          vf[2 * w] = __uint_as_float(vc[i][w] << 16);
-          vf[2 * w + 1] = __uint_as_float(vc[i][w] & 0xFFFF0000u);
-        }
-      } else {
-        vf[0] = __uint_as_float(vc[i][0] << 16);
+      for (int e = 0; e < 4; ++e) {
+        vf[2 * e] = __uint_as_float(w4[e] << 16);
+        vf[2 * e + 1] = __uint_as_float(w4[e] & 0xFFFF0000u);
       }
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float pw = __builtin_bit_cast(
-            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pr[h]), 4 * i));
+        const float pw = ps[wid][h][vu + PSL * i];
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) o[h][e] += pw * vf[e];
+        for (int e = 0; e < 8; ++e) o[h][e] += pw * vf[e];
       }
     }
+    const int pp = p - (t0 + 16 * wid);  // p's place among this wave's positions (uniform)
+    if (pp >= 0 && pp < 16 && vu == pp % PSL) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float pw = ps[wid][h][pp];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[h][e] += pw * vn[8 * vch + e];
+      }
+    }
+    __builtin_amdgcn_wave_barrier();  // ps is rewritten by the next chunk
     if (more) {
 #pragma unroll
       for (int j = 0; j < KV4; ++j) kc[j] = kx[j];
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-#pragma unroll
-        for (int w = 0; w < VW; ++w) vc[i][w] = vx[i][w];
+      for (int i = 0; i < VR; ++i) vc[i] = vx[i];
     }
   }
-  // ---- merge the four waves' softmax states ----
+  // ---- merge the waves' softmax states ----
+  // the PSL position slots of each output dim (lanes vch + CL * u) are added first
+#pragma unroll
+  for (int msk = CL; msk < 64; msk <<= 1)
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[h][e] += __shfl_xor(o[h][e], msk, 64);
 #pragma unroll
   for (int h = 0; h < G; ++h) l[h] = wave_sum(l[h]);
   if (lane == 0) {
@@ -1819,11 +1842,11 @@ __global__ __launch_bounds__(64 * NW) void k_attn_dec(AttnDecArgs a) {
       wl[wid][h] = l[h];
     }
   }
-  if (vlane) {
+  if (vu == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) wo[wid][h][DPL * lane + e] = o[h][e];
+      for (int e = 0; e < 8; ++e) wo[wid][h][8 * vch + e] = o[h][e];
   }
   __syncthreads();
   for (int idx = tid; idx < G * D; idx += NT) {
@@ -1835,7 +1858,7 @@ __global__ __launch_bounds__(64 * NW) void k_attn_dec(AttnDecArgs a) {
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       if (wm[w][h] == -INFINITY) continue;
-      const float f = expf(wm[w][h] - M);
+      const float f = __builtin_amdgcn_exp2f(wm[w][h] - M);
       L += wl[w][h] * f;
       O += wo[w][h][dd] * f;
     }
@@ -1875,7 +1898,7 @@ __global__ __launch_bounds__(64 * NW) void k_attn_dec(AttnDecArgs a) {
   __syncthreads();
   if (!last_flag) return;
   // Every split's (max, sum) of the G heads is requested at once; a wave per head turns
-  // them into weights e^(m_s - m) and the total; the outputs are summed over the splits
+  // them into weights 2^(m_s - m) and the total; the outputs are summed over the splits
   // in 16-byte agent-coherent loads, several splits in flight per thread, the split
   // subsets of one output group added through LDS.  A long context (tens of splits)
   // costs two or three memory round trips instead of one per split.
@@ -1903,7 +1926,7 @@ __global__ __launch_bounds__(64 * NW) void k_attn_dec(AttnDecArgs a) {
 #pragma unroll
       for (int k = 0; k < SB; ++k) {
         if (mv[k] == -INFINITY) continue;
-        const float w = expf(mv[k] - mx);
+        const float w = __builtin_amdgcn_exp2f(mv[k] - mx);
         lsum += lv[k] * w;
         acc += ov[k] * w;
       }
@@ -1947,7 +1970,7 @@ __global__ __launch_bounds__(64 * NW) void k_attn_dec(AttnDecArgs a) {
       float ls = 0.0f;
       for (int q = lane; q < ns; q += 64) {
         const float m_s = mw[h][q];
-        const float w = m_s == -INFINITY ? 0.0f : expf(m_s - mx);
+        const float w = m_s == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_s - mx);
         mw[h][q] = w;
         ls += mlv[h][q] * w;
       }
@@ -2003,12 +2026,13 @@ __global__ __launch_bounds__(64 * NW) void k_attn_dec(AttnDecArgs a) {
                                    __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// split merge as its own launch: o = sum_s o_s e^(m_s - m) / sum_s l_s e^(m_s - m)
+// split merge as its own launch: o = sum_s o_s 2^(m_s - m) / sum_s l_s 2^(m_s - m) (the
+// splits' maxima are in base 2)
 // for one (row b, query head); the kernel boundary orders it after every split.  All
 // (max, sum) pairs and the first eight splits' partials are requested at once, so a short
 // context costs one memory round trip.
 __global__ __launch_bounds__(128) void k_attn_dec_merge(AttnDecArgs a) {
-  __shared__ float wsp[ATT_MAX_SPLITS];  // e^(m_s - m), zero for an empty split
+  __shared__ float wsp[ATT_MAX_SPLITS];  // 2^(m_s - m), zero for an empty split
   __shared__ float red[2];
   constexpr int SB = 8;
   const int head = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
@@ -2035,8 +2059,8 @@ __global__ __launch_bounds__(128) void k_attn_dec_merge(AttnDecArgs a) {
   if (lane == 0) red[wid] = mx;
   __syncthreads();
   mx = fmaxf(red[0], red[1]);
-  const float f0 = m0 == -INFINITY ? 0.0f : expf(m0 - mx);
-  const float f1 = m1 == -INFINITY ? 0.0f : expf(m1 - mx);
+  const float f0 = m0 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m0 - mx);
+  const float f1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - mx);
   if (tid < ns) wsp[tid] = f0;
   if (tid + 128 < ns) wsp[tid + 128] = f1;
   float ls = wave_sum(l0 * f0 + l1 * f1);
