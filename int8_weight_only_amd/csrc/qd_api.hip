@@ -300,8 +300,8 @@ namespace {
 void attn_split(int ctx, int cap, int max_splits, int min_chunks, int occupancy, int rows_x_kv,
                 int* nsplit, int* split_len);
 
-// decode-attention waves per work-group: eight when the (row, KV head) pairs alone cover
-// the CUs or the context is long (more than ATT_LONG_CTX positions), else four
+// decode-attention waves per work-group: eight from 64 (row, KV head) pairs up or when the
+// context is long (more than ATT_LONG_CTX positions), else four
 int attn_waves_for(const qd_model* m, int B, int ctx);
 // work-groups per CU the split targets: as many as stay resident (the 8-wave kernel holds
 // one per CU, the 4-wave kernel three; measured best at B = 1..32)
@@ -419,12 +419,13 @@ qd_status dec_qkv(qd_model* m, int l, int B, hipStream_t st) {
                   m->w<float>(o.qkv_s), d.NQKV, d.d, EPI_STORE, m->ws<bf16_t>(m->P.qkv), d.NQKV, st);
 }
 
-// measured at B = 1, Qwen3-0.6B: 383 positions 7.1 us (4 waves) against 7.6 (8 waves);
-// ~8.2K positions 16.2 us (4 waves) against 14.5 (8 waves)
+// measured on Qwen3-0.6B (8 KV heads): B = 1 at 383 positions 7.1 us (4 waves) against 7.6
+// (8 waves), at ~8.2K positions 16.2 against 14.5; at ~320 positions B = 8 9.4 against 8.6,
+// B = 16 10.9 against 9.2, B = 32 12.0 with 8 waves
 constexpr int ATT_LONG_CTX = 2048;
 int attn_waves_for(const qd_model* m, int B, int ctx) {
   if (m->attn_waves) return m->attn_waves;
-  return (B * m->d.KV >= 256 || ctx > ATT_LONG_CTX) ? 8 : 4;
+  return (B * m->d.KV >= 64 || ctx > ATT_LONG_CTX) ? 8 : 4;
 }
 
 // eight waves: one work-group per CU (measured best at B x KV >= 256); four waves: as many
