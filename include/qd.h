@@ -163,11 +163,14 @@ qd_status qd_load_weights(const qd_model_shape* shape, const qd_limits* limits,
 /* Quantized load cache ("Model-agnostic LLM inference", section "The quantized load
  * cache"): the exact post-quantization device bytes, restored instead of re-quantizing.
  * File: a 128-byte little-endian header, then the payload.
- *   header: char magic[8] = "QDI8WCV1"; uint32 version = 1; uint32 header_bytes = 128;
+ *   header: char magic[8] = "QDI8WCV1"; uint32 version = 2; uint32 header_bytes = 128;
  *           uint64 payload_bytes; uint32 dims[9] = hidden, n_layers, n_heads,
  *           n_kv_heads, head_dim, intermediate, vocab, bit pattern of rms_eps, bit
- *           pattern of rope_theta; uint8 source_digest[32]; uint8 payload_sha256[32];
+ *           pattern of rope_theta; uint8 source_digest[32]; uint8 payload_digest[32];
  *           uint8 pad[4].
+ *   payload_digest = SHA-256 of the concatenated SHA-256 digests of the payload's
+ *           consecutive 16 MiB chunks (the last chunk shorter), so the chunks can be hashed
+ *           on several threads.
  *   payload: embedding codes [V, d] int8, embedding scales [V] fp32, final gain [d]
  *           fp32, then per layer: q|k|v codes [H*D + 2*KV*D, d] and scales, O codes
  *           [d, H*D] and scales, gate/up codes [2I, d] and scales (interleaved in blocks
@@ -175,7 +178,7 @@ qd_status qd_load_weights(const qd_model_shape* shape, const qd_limits* limits,
  *           scales, gains input [d], post-attention [d], q_norm [D], k_norm [D].
  * The validity gate: magic, version, every dimension, the caller's 32-byte digest of the
  * source checkpoint (e.g. SHA-256 of its manifest), the exact file length, and the
- * SHA-256 of the payload.  Any mismatch returns QD_ERR_CACHE_MISS naming it, and the
+ * payload digest.  Any mismatch returns QD_ERR_CACHE_MISS naming it, and the
  * caller falls back to qd_load_weights + qd_save_cache. */
 
 /* Writes m's quantized weights to `path` (through `path`.tmp, then a rename).  Host

@@ -889,7 +889,7 @@ CacheHeader cache_header_for(const qd_model_shape& s, const uint8_t digest[32], 
   CacheHeader h;
   std::memset(&h, 0, sizeof(h));
   std::memcpy(h.magic, "QDI8WCV1", 8);
-  h.version = 1;
+  h.version = 2;
   h.header_bytes = sizeof(CacheHeader);
   const int32_t v[7] = {s.hidden, s.n_layers, s.n_heads, s.n_kv_heads, s.head_dim, s.intermediate, s.vocab};
   for (int i = 0; i < 7; ++i) h.dims[i] = (uint32_t)v[i];
@@ -988,9 +988,7 @@ qd_status qd_save_cache(qd_model* m, const char* path, const uint8_t* source_dig
     at += r.second;
   }
   CacheHeader h = cache_header_for(m->shape, source_digest, total);
-  Sha256 sha;
-  sha.update(payload.data(), payload.size());
-  sha.final(h.payload_sha256);
+  chunked_sha256(payload.data(), payload.size(), h.payload_sha256);
   const std::string tmp = std::string(path) + ".tmp";
   FILE* f = std::fopen(tmp.c_str(), "wb");
   if (!f) return fail(QD_ERR_INVALID_ARGUMENTS, "cannot write " + tmp);
@@ -1030,10 +1028,8 @@ qd_status read_cache(const qd_model_shape* shape, const char* path, const uint8_
   std::fclose(f);
   if (p.empty()) {
     uint8_t sum[32];
-    Sha256 sha;
-    sha.update(payload->data(), payload->size());
-    sha.final(sum);
-    if (std::memcmp(sum, h.payload_sha256, 32) != 0) p = "payload SHA-256 differs";
+    chunked_sha256(payload->data(), payload->size(), sum);
+    if (std::memcmp(sum, h.payload_sha256, 32) != 0) p = "payload digest (chunked SHA-256) differs";
   }
   if (!p.empty()) return fail(QD_ERR_CACHE_MISS, std::string(path) + ": " + p);
   return QD_OK;

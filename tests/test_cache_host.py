@@ -27,12 +27,20 @@ def _payload_bytes(s):
     return V * d + 4 * V + 4 * d + L * per_layer
 
 
+def _payload_digest(payload, chunk=16 << 20):
+    """The documented payload digest: SHA-256 of the concatenated SHA-256 digests of the
+    payload's consecutive 16 MiB chunks."""
+    sums = b"".join(hashlib.sha256(payload[i:i + chunk]).digest()
+                    for i in range(0, len(payload), chunk))
+    return hashlib.sha256(sums).digest()
+
+
 def _write(path, s, digest, payload, **over):
-    f = dict(magic=b"QDI8WCV1", version=1, header_bytes=128, payload_bytes=len(payload),
+    f = dict(magic=b"QDI8WCV1", version=2, header_bytes=128, payload_bytes=len(payload),
              dims=[s.hidden, s.n_layers, s.n_heads, s.n_kv_heads, s.head_dim, s.intermediate,
                    s.vocab, struct.unpack("<I", struct.pack("<f", s.rms_eps))[0],
                    struct.unpack("<I", struct.pack("<f", s.rope_theta))[0]],
-             src=digest, sha=hashlib.sha256(payload).digest())
+             src=digest, sha=_payload_digest(payload))
     f.update(over)
     hdr = (f["magic"] + struct.pack("<IIQ", f["version"], f["header_bytes"], f["payload_bytes"])
            + struct.pack("<9I", *f["dims"]) + f["src"] + f["sha"] + b"\0" * 4)
@@ -55,13 +63,34 @@ def test_gate_accepts_a_well_formed_cache(cache):
     qd.check_cache(s, path, digest)
 
 
+def test_payload_digest_over_several_chunks(tmp_path):
+    """A payload of several 16 MiB chunks (a tiny decoder with a 150,000-token vocabulary:
+    19.8 MB) passes with the two-level digest and fails if one byte of its second chunk
+    changes."""
+    import dataclasses
+    s = dataclasses.replace(SHAPES["tiny"], vocab=150000)
+    digest = hashlib.sha256(b"manifest").digest()
+    n = _payload_bytes(s)
+    assert n > 16 << 20
+    payload = np.random.default_rng(1).integers(0, 256, n, dtype=np.uint8).tobytes()
+    path = str(tmp_path / "big.cache")
+    _write(path, s, digest, payload)
+    qd.check_cache(s, path, digest)
+    bad = bytearray(payload)
+    bad[(16 << 20) + 5] ^= 1
+    _write(path, s, digest, bytes(bad), sha=_payload_digest(payload))
+    with pytest.raises(qd.QdError) as e:
+        qd.check_cache(s, path, digest)
+    assert e.value.code == "cache_miss" and "digest" in str(e.value)
+
+
 @pytest.mark.parametrize("change,needle", [
     (dict(magic=b"QDI8WCV0"), "magic"),
-    (dict(version=2), "format version"),
+    (dict(version=1), "format version"),
     (dict(dims=None), "vocab differs"),
     (dict(src=None), "source checkpoint digest"),
     (dict(payload_bytes=None), "payload length"),
-    (dict(sha=b"\0" * 32), "SHA-256"),
+    (dict(sha=b"\0" * 32), "payload digest"),
 ])
 def test_gate_names_each_mismatch(cache, change, needle):
     s, digest, payload, path = cache
