@@ -644,7 +644,7 @@ def main():
 
     if oracle:
         cpu_model, blas = cpu_info()
-        runs.get(keys[0], prompts[0], 24)   # a decode sample of ~1-2 s at this shape
+        runs.get(keys[0], prompts[0], NN)   # the workload's own 127 decode steps on the CPU
         cpu = {"value": round(runs.n_dec / runs.t_dec, 3), "unit": "tok/s",
                "cores": blas or int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0)))),
                "kind": "oracle", "cpu_model": cpu_model, "blas_threads": blas,
