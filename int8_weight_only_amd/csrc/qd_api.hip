@@ -266,6 +266,7 @@ struct qd_model {
   int attn_waves = 0;  // 0: eight waves only when B x KV heads fill the GPU without splits
   int attn_merge_last = 1;
   int gemm_splits = 0;  // prefill GEMM split-K cap (0: launcher default)
+  int gemm_ks = 1;      // prefill GEMMs of few rows may take the k-sliced kernel
   int skinny_norm = 1;   // batched projections fold the RMSNorm where the shape allows
   int skinny_split = 2;  // 1: never; 2: fewer than 128 channel tiles, over 16 rows; 3: all
   // persistent single-sequence decode (one cooperative launch per call)
@@ -607,7 +608,7 @@ qd_status enqueue_prefill(qd_model* m, int n, const int* ids_dev, const std::vec
     const LayerOff& o = P.L[l];
     GemmArgs g{};
     g.A = h; g.lda = d.d; g.W = m->w<int8_t>(o.qkv_q); g.scale = m->w<float>(o.qkv_s);
-    g.M = M; g.N = d.NQKV; g.K = d.d; g.epi = EPI_STORE; g.out = qkv; g.ldo = d.NQKV; g.part = gpart; g.cnt = m->ws<unsigned int>(P.sk_cnt); g.splits = m->gemm_splits;
+    g.M = M; g.N = d.NQKV; g.K = d.d; g.epi = EPI_STORE; g.out = qkv; g.ldo = d.NQKV; g.part = gpart; g.cnt = m->ws<unsigned int>(P.sk_cnt); g.splits = m->gemm_splits; g.use_ks = m->gemm_ks;
     HIPCHK(launch_gemm(g, st));
     RopeArgs ra{};
     ra.qkv = qkv; ra.ldqkv = d.NQKV;
@@ -626,15 +627,15 @@ qd_status enqueue_prefill(qd_model* m, int n, const int* ids_dev, const std::vec
     HIPCHK(launch_flash_prefill(fa, n_tiles, st));
     g = GemmArgs{};
     g.A = attn; g.lda = d.HD; g.W = m->w<int8_t>(o.o_q); g.scale = m->w<float>(o.o_s);
-    g.M = M; g.N = d.d; g.K = d.HD; g.epi = EPI_RESID; g.out = x; g.ldo = d.d; g.part = gpart; g.cnt = m->ws<unsigned int>(P.sk_cnt); g.splits = m->gemm_splits;
+    g.M = M; g.N = d.d; g.K = d.HD; g.epi = EPI_RESID; g.out = x; g.ldo = d.d; g.part = gpart; g.cnt = m->ws<unsigned int>(P.sk_cnt); g.splits = m->gemm_splits; g.use_ks = m->gemm_ks;
     HIPCHK(resid_proj(g, m->w<float>(o.post_g)));
     g = GemmArgs{};
     g.A = h; g.lda = d.d; g.W = m->w<int8_t>(o.gu_q); g.scale = m->w<float>(o.gu_s);
-    g.M = M; g.N = 2 * d.I; g.K = d.d; g.epi = EPI_SILU; g.out = act; g.ldo = d.I; g.part = gpart; g.cnt = m->ws<unsigned int>(P.sk_cnt); g.splits = m->gemm_splits;
+    g.M = M; g.N = 2 * d.I; g.K = d.d; g.epi = EPI_SILU; g.out = act; g.ldo = d.I; g.part = gpart; g.cnt = m->ws<unsigned int>(P.sk_cnt); g.splits = m->gemm_splits; g.use_ks = m->gemm_ks;
     HIPCHK(launch_gemm(g, st));
     g = GemmArgs{};
     g.A = act; g.lda = d.I; g.W = m->w<int8_t>(o.dn_q); g.scale = m->w<float>(o.dn_s);
-    g.M = M; g.N = d.d; g.K = d.I; g.epi = EPI_RESID; g.out = x; g.ldo = d.d; g.part = gpart; g.cnt = m->ws<unsigned int>(P.sk_cnt); g.splits = m->gemm_splits;
+    g.M = M; g.N = d.d; g.K = d.I; g.epi = EPI_RESID; g.out = x; g.ldo = d.d; g.part = gpart; g.cnt = m->ws<unsigned int>(P.sk_cnt); g.splits = m->gemm_splits; g.use_ks = m->gemm_ks;
     HIPCHK(resid_proj(g, l + 1 < d.L ? m->w<float>(P.L[l + 1].in_g) : m->w<float>(P.final_g)));
   }
   // h holds the final-normalized rows
@@ -1605,7 +1606,8 @@ qd_status qd_set_tuning(qd_model* m, int32_t knob, int32_t value) {
   if (!m) return fail(QD_ERR_INVALID_ARGUMENTS, "model is NULL");
   if (value < 0 || (value < 1 && knob != QD_TUNE_ATTN_MERGE_LAST && knob != QD_TUNE_ATTN_WAVES &&
                     knob != QD_TUNE_PERSISTENT && knob != QD_TUNE_GEMM_SPLITS &&
-                    knob != QD_TUNE_ATTN_OCCUPANCY && knob != QD_TUNE_SKINNY_NORM))
+                    knob != QD_TUNE_ATTN_OCCUPANCY && knob != QD_TUNE_SKINNY_NORM &&
+                    knob != QD_TUNE_PREFILL_GEMM))
     return fail(QD_ERR_INVALID_ARGUMENTS, "value out of range");
   switch (knob) {
     case QD_TUNE_ATTN_MAX_SPLITS: m->attn_max_splits = value; break;
@@ -1625,6 +1627,10 @@ qd_status qd_set_tuning(qd_model* m, int32_t knob, int32_t value) {
     case QD_TUNE_SKINNY_NORM:
       if (value > 1) return fail(QD_ERR_INVALID_ARGUMENTS, "skinny norm mode must be 0 or 1");
       m->skinny_norm = value;
+      break;
+    case QD_TUNE_PREFILL_GEMM:
+      if (value > 1) return fail(QD_ERR_INVALID_ARGUMENTS, "prefill GEMM mode must be 0 or 1");
+      m->gemm_ks = value;
       break;
     case QD_TUNE_ATTN_OCCUPANCY:
       if (value > 8) return fail(QD_ERR_INVALID_ARGUMENTS, "attention occupancy must be 0..8");

@@ -70,6 +70,7 @@ struct GemmArgs {
   int defer;                  // EPI_RESID with split-K: store partials (EPI_PART) instead of
                               // merging them in-kernel; the caller runs k_resid_norm next
   int use_big = 1;            // 0: never the 128x128-tile kernel (tuning)
+  int use_ks = 1;             // 0: never the k-sliced few-row kernel (tuning)
 };
 constexpr size_t GEMM_PART_FLOATS = (size_t)8 << 20;  // 32 MiB of split-K partials
 

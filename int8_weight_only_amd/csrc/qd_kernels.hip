@@ -744,6 +744,111 @@ __global__ __launch_bounds__(512) void k_gemm(GemmArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
+// Prefill GEMM for few token rows (up to 128): a 64x64 output tile per work-group of
+// 8 waves, each wave a 32*C-wide k slice of it (k-split z of the grid covers 256*C of K).
+// Every wave requests all of its operand fragments at once, straight into MFMA operand
+// registers (A: 16 bytes of 8 bf16 per lane and fragment; W: 8 int8 codes, converted
+// exactly to bf16 in registers), multiplies its slice, and the 8 partial tiles are added
+// once through LDS.  There is no per-k-step barrier or LDS staging: the tile's latency is
+// one memory round trip, its MFMAs and one reduction, where the k-stepped kernel walks a
+// serial chain of K/128 steps.  128 KB of LDS: one work-group per CU.
+template <int EPI, int C>
+__global__ __launch_bounds__(512) void k_gemm_ks(GemmArgs a) {
+  constexpr int OOB = (int)0x80000000;
+  __shared__ __align__(16) f32x4_t red[8][16][64];  // [wave][m tile * 4 + n tile][lane]
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int grp = lane >> 4, r16 = lane & 15;
+  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64, z = blockIdx.z;
+  const int k0 = z * (256 * C) + wid * (32 * C);
+  const __amdgpu_buffer_rsrc_t arsc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.A, 0, a.M * a.lda * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t wrsc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.W, 0, a.N * a.K, 0x00020000);
+  // fragment (tile t, chunk c): lane holds row 16t + lane%16, k = k0 + 32c + 8*(lane/16) .. +8;
+  // rows past M (N) and k past K read zero
+  uint4 af[4][C];
+  uint2 wf[4][C];
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const int k = k0 + 32 * c + 8 * grp;
+    const bool ok = k < a.K;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      af[t][c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               arsc, ok ? ((m0 + 16 * t + r16) * a.lda + k) * 2 : OOB, 0, 0));
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      wf[t][c] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
+                                               wrsc, ok ? (n0 + 16 * t + r16) * a.K + k : OOB, 0, 0));
+  }
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const bf16x8_t bw = i8x8_to_bf16x8(wf[nt][c]);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, af[mt][c]),
+                                                              bw, acc[mt][nt], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) red[wid][mt * 4 + nt][lane] = acc[mt][nt];
+  __syncthreads();
+  // the 8 slices of each of the 16 x 64 lane positions, added in wave order; a position
+  // (tile mt*4+nt, lane ln) holds D[m0 + 16mt + 4(ln/16) + i][n0 + 16nt + ln%16], i < 4
+  auto sum8 = [&](int t, int ln) {
+    f32x4_t v = red[0][t][ln];
+#pragma unroll
+    for (int w = 1; w < 8; ++w) v += red[w][t][ln];
+    return v;
+  };
+  if constexpr (EPI == EPI_SILU) {
+    // thread: m tile, gate/up pair, lane position -> the gate (n tile 2p) and up (2p+1) sums
+    const int mt = tid >> 7, pr = (tid >> 6) & 1, ln = tid & 63;
+    const f32x4_t g = sum8(mt * 4 + 2 * pr, ln), u = sum8(mt * 4 + 2 * pr + 1, ln);
+    const int ng = n0 + 32 * pr + (ln & 15);
+    const float sg = a.scale[ng < a.N ? ng : 0], su = a.scale[ng + GU_BLOCK < a.N ? ng + GU_BLOCK : 0];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + 16 * mt + 4 * (ln >> 4) + i;
+      if (m < a.M && ng + GU_BLOCK < a.N) gemm_epilogue<EPI_SILU>(a, m, ng, g[i], u[i], sg, su);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int idx = tid + 512 * j, t = idx >> 6, ln = idx & 63;
+      const int mt = t >> 2, nt = t & 3;
+      const f32x4_t v = sum8(t, ln);
+      const int n = n0 + 16 * nt + (ln & 15);
+      if (n >= a.N) continue;
+      if constexpr (EPI == EPI_PART) {
+        float* pz = a.part + (size_t)z * a.M * a.N;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = m0 + 16 * mt + 4 * (ln >> 4) + i;
+          if (m < a.M) pz[(size_t)m * a.N + n] = v[i];
+        }
+      } else {
+        const float sc = a.scale[n];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = m0 + 16 * mt + 4 * (ln >> 4) + i;
+          if (m < a.M) gemm_epilogue<EPI>(a, m, n, v[i], 0.0f, sc, 0.0f);
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
 // Prefill GEMM for many token rows (the tile grid fills the GPU): a 128x128 output tile per
 // work-group of 4 waves, each wave a 64x64 block of 4x4 MFMA 16x16x32 tiles, so every
 // fragment read from LDS feeds four MFMAs (the 64x64-tile kernel's 32x32 wave blocks get
@@ -2520,6 +2625,42 @@ hipError_t launch_gemm(const GemmArgs& a0, hipStream_t st, int* splits_used) {
     return hipGetLastError();
   }
   const int tiles = ((a.N + 63) / 64) * ((a.M + 63) / 64);
+  // few rows (at most two 64-row tiles): the k-sliced kernel when its k splits (256..1024 k
+  // each) cover K; more than one split only as deferred residual partials, enough splits to
+  // give every CU a tile.  Its operand fragments come straight from memory in MFMA lane
+  // order (16 rows per instruction), which streams slower than the staged kernel's row-
+  // contiguous loads once the tiles re-read enough of A: measured faster at 16 and 100 rows,
+  // slower from 256 rows up.
+  if (a.use_ks != 0 && a.M <= 128) {
+    int S = 1;
+    const bool part_ok = a.defer && a.epi == EPI_RESID && a.part;
+    if (part_ok)
+      while (S < 8 && (tiles * S < 256 || a.K > S * 1024) && a.K >= S * 2 * 256 &&
+             (size_t)(S * 2) * a.M * a.N <= GEMM_PART_FLOATS)
+        S *= 2;
+    const int C = (a.K + S * 256 - 1) / (S * 256);
+    if (C <= 4 && (S == 1 || part_ok)) {
+      a.splits = S;
+      if (splits_used) *splits_used = S;
+      dim3 grid((a.N + 63) / 64, (a.M + 63) / 64, S);
+      const int epi = S > 1 ? (int)EPI_PART : a.epi;
+#define QD_KS(E)                                                                                   \
+  switch (C) {                                                                                     \
+    case 1: hipLaunchKernelGGL((k_gemm_ks<E, 1>), grid, dim3(512), 0, st, a); break;               \
+    case 2: hipLaunchKernelGGL((k_gemm_ks<E, 2>), grid, dim3(512), 0, st, a); break;               \
+    case 3: hipLaunchKernelGGL((k_gemm_ks<E, 3>), grid, dim3(512), 0, st, a); break;               \
+    default: hipLaunchKernelGGL((k_gemm_ks<E, 4>), grid, dim3(512), 0, st, a); break;              \
+  }
+      switch (epi) {
+        case EPI_STORE: QD_KS(EPI_STORE) break;
+        case EPI_RESID: QD_KS(EPI_RESID) break;
+        case EPI_PART: QD_KS(EPI_PART) break;
+        default: QD_KS(EPI_SILU) break;
+      }
+#undef QD_KS
+      return hipGetLastError();
+    }
+  }
   // split K when the tile grid leaves most of the 256 CUs idle
   int splits = 1;
   const int max_splits = a.splits > 0 ? a.splits : 8;  // caller's cap (tuning), else 8

@@ -340,6 +340,28 @@ def test_teacher_forced_mid_split_k():
         m.close()
 
 
+@pytest.mark.parametrize("n_prompt", [64, 100])
+def test_prefill_few_rows_both_gemm_kernels(n_prompt):
+    """Prompts of one and two 64-row tiles (100: ragged): the prefill projections through the
+    k-sliced kernel (default at <= 128 rows; O and down as 4 k-split partials at this
+    shape) and through the k-stepped kernel (prefill_gemm=0), each against the oracle."""
+    w = make_weights(MID, seed=4, gains="uniform")
+    qm = quantize_model(w)
+    prompt = make_prompt(MID.vocab, n_prompt, 1004)
+    orc = Oracle(MID, qm, mode="bf16").generate(prompt, 1)
+    m = _model(MID, w, max_batch=1, max_ctx=256, max_prefill_tokens=256)
+    try:
+        for mode, name in ((1, "k-sliced"), (0, "k-stepped")):
+            say(f"[gpu] mid prefill, {n_prompt} rows, {name} GEMM")
+            m.set_tuning(prefill_gemm=mode)
+            nxt, lg = m.prefill([prompt], logits=True)
+            torch.cuda.synchronize()
+            check_step(lg[0].cpu().numpy(), nxt[0].item(), orc["logits"][0], orc["margin"][0],
+                       "mid", f"mid {n_prompt} rows {name}")
+    finally:
+        m.close()
+
+
 def test_teacher_forced_long_context():
     """1500-token prompt: 24 prefill tiles per head; decode attention over many position
     splits (per-step kernels: ~24 merged splits; persistent: 12 splits of one 128-position
