@@ -366,8 +366,10 @@ typedef enum {
   QD_TUNE_SKINNY_NORM = 9,        /* batched decode: 1 (default) folds the RMSNorm before q|k|v
                                      and gate|up into the projection where the shape allows;
                                      0: a separate normalization launch */
-  QD_TUNE_PREFILL_GEMM = 10,      /* prefill GEMMs of few token rows: 1 (default) the k-sliced
-                                     kernel where its shape limits allow; 0: the k-stepped one */
+  QD_TUNE_PREFILL_GEMM = 10,      /* prefill GEMMs: 1 (default) the k-sliced kernel for few
+                                     token rows and, for many rows, QK-norm / RoPE / K/V cache
+                                     writes in the q|k|v GEMM's epilogue where the shapes allow;
+                                     0: the k-stepped kernel and a separate QK-norm launch */
 } qd_tune_knob;
 
 /* Sets a knob; captured decode graphs are dropped so the next call re-captures.

@@ -267,6 +267,7 @@ struct qd_model {
   int attn_merge_last = 1;
   int gemm_splits = 0;  // prefill GEMM split-K cap (0: launcher default)
   int gemm_ks = 1;      // prefill GEMMs of few rows may take the k-sliced kernel
+  int gemm_rope = 1;    // the 128x128-tile q|k|v GEMM may run QK-norm / RoPE in its epilogue
   int skinny_norm = 1;   // batched projections fold the RMSNorm where the shape allows
   int skinny_split = 2;  // 1: never; 2: fewer than 128 channel tiles, over 16 rows; 3: all
   // persistent single-sequence decode (one cooperative launch per call)
@@ -609,7 +610,6 @@ qd_status enqueue_prefill(qd_model* m, int n, const int* ids_dev, const std::vec
     GemmArgs g{};
     g.A = h; g.lda = d.d; g.W = m->w<int8_t>(o.qkv_q); g.scale = m->w<float>(o.qkv_s);
     g.M = M; g.N = d.NQKV; g.K = d.d; g.epi = EPI_STORE; g.out = qkv; g.ldo = d.NQKV; g.part = gpart; g.cnt = m->ws<unsigned int>(P.sk_cnt); g.splits = m->gemm_splits; g.use_ks = m->gemm_ks;
-    HIPCHK(launch_gemm(g, st));
     RopeArgs ra{};
     ra.qkv = qkv; ra.ldqkv = d.NQKV;
     ra.q_gain = m->w<float>(o.qn_g); ra.k_gain = m->w<float>(o.kn_g); ra.eps = m->shape.rms_eps;
@@ -617,7 +617,10 @@ qd_status enqueue_prefill(qd_model* m, int n, const int* ids_dev, const std::vec
     ra.row_slot = row_slot; ra.row_pos = row_pos;
     ra.kcache = m->kcache(l); ra.vcache = m->vcache(l);
     ra.H = d.H; ra.KV = d.KV; ra.D = d.D; ra.max_ctx = m->lim.max_ctx; ra.M = M;
-    HIPCHK(launch_qk_rope(ra, st));
+    g.fuse_rope = m->gemm_rope; g.rope = ra;
+    int rope_done = 0;
+    HIPCHK(launch_gemm(g, st, nullptr, &rope_done));
+    if (!rope_done) HIPCHK(launch_qk_rope(ra, st));
     FlashArgs fa{};
     fa.q = qkv; fa.ldq = d.NQKV;
     fa.kcache = m->kcache(l); fa.vcache = m->vcache(l);
@@ -1631,6 +1634,7 @@ qd_status qd_set_tuning(qd_model* m, int32_t knob, int32_t value) {
     case QD_TUNE_PREFILL_GEMM:
       if (value > 1) return fail(QD_ERR_INVALID_ARGUMENTS, "prefill GEMM mode must be 0 or 1");
       m->gemm_ks = value;
+      m->gemm_rope = value;
       break;
     case QD_TUNE_ATTN_OCCUPANCY:
       if (value > 8) return fail(QD_ERR_INVALID_ARGUMENTS, "attention occupancy must be 0..8");

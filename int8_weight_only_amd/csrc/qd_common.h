@@ -57,6 +57,15 @@ struct GemvArgs {
 constexpr int SKINNY_MAX_SPLIT = 16;
 constexpr int SKINNY_MAX_TILES = 4096;
 
+struct RopeArgs {
+  bf16_t* qkv; int ldqkv;     // [M][(H+2KV)*D]; q heads rewritten in place
+  const float* q_gain; const float* k_gain; float eps;
+  const float2* rope;         // [max_ctx][D/2] (cos, sin)
+  const int* row_slot; const int* row_pos;  // per row
+  bf16_t* kcache; bf16_t* vcache;           // this layer's [slots][KV][ctx][D]
+  int H, KV, D, max_ctx, M;
+};
+
 struct GemmArgs {
   const bf16_t* A; int lda;   // [M][K] bf16 activations
   const int8_t* W;            // [N][K]
@@ -71,17 +80,14 @@ struct GemmArgs {
                               // merging them in-kernel; the caller runs k_resid_norm next
   int use_big = 1;            // 0: never the 128x128-tile kernel (tuning)
   int use_ks = 1;             // 0: never the k-sliced few-row kernel (tuning)
+  // EPI_STORE of the q|k|v projection: the 128x128-tile kernel may run the QK-norm, RoPE and
+  // K/V cache writes of the heads in its tile in its epilogue (rope.qkv is not read: the
+  // projection's rows are the tile; q heads go to out, K and V heads only to the caches)
+  int fuse_rope = 0;
+  RopeArgs rope{};
 };
 constexpr size_t GEMM_PART_FLOATS = (size_t)8 << 20;  // 32 MiB of split-K partials
 
-struct RopeArgs {
-  bf16_t* qkv; int ldqkv;     // [M][(H+2KV)*D]; q heads rewritten in place
-  const float* q_gain; const float* k_gain; float eps;
-  const float2* rope;         // [max_ctx][D/2] (cos, sin)
-  const int* row_slot; const int* row_pos;  // per row
-  bf16_t* kcache; bf16_t* vcache;           // this layer's [slots][KV][ctx][D]
-  int H, KV, D, max_ctx, M;
-};
 
 
 // decode attention with QK-norm, RoPE and the KV write fused in; splits of the context
@@ -216,7 +222,10 @@ hipError_t launch_skinny(const GemvArgs& a, int epi, hipStream_t st);
 bool skinny_norm_ok(int nb, int K, int epi, int ksplit);
 // *splits_used (nullable) receives the split-K ways; with a.defer and more than one
 // split, the residual is not yet updated: launch_resid_norm with that count must follow
-hipError_t launch_gemm(const GemmArgs& a, hipStream_t st, int* splits_used = nullptr);
+// rope_done (optional): set to 1 when the launch also did the QK-norm / RoPE / cache writes
+// that a.fuse_rope asked for, else 0 (the caller then runs launch_qk_rope)
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t st, int* splits_used = nullptr,
+                       int* rope_done = nullptr);
 // x[m] = bf16(x[m] + bf16(scale * sum_s part[s][m])) in split order, then
 // y[m] = RMSNorm(x[m]) * g; splits in {2, 4, 8}
 hipError_t launch_resid_norm(bf16_t* x, int M, int d, const float* part, int splits,

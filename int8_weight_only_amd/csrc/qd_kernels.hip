@@ -849,6 +849,91 @@ __global__ __launch_bounds__(512) void k_gemm_ks(GemmArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
+// Epilogue of the q|k|v projection's 128x128 tile with the QK-norm, RoPE and K/V cache
+// writes fused in (head dim D = 64 or 128, so no head straddles two tiles).  The tile's
+// projections, rounded to bf16 as the plain store would write them, go to LDS (T, pitch
+// 136 elements, over the stage buffers: every stage read has passed the loop's last
+// barrier); then D/8 lanes take one (row, head): dims 4j..4j+3 and D/2+4j..D/2+4j+3 of lane
+// j, the sum of squares over the head added across those lanes, the RMSNorm with the head's
+// shared gain and the rotate-half rotation at the row's position as k_qk_rope computes
+// them.  q heads are written back to the projection's output, K heads to the K cache at
+// (slot, position) of the row, V heads copied to the V cache.
+__device__ __forceinline__ void gemm_big_rope_epilogue(const GemmArgs& a, bf16_t* T,
+                                                       const f32x4_t (&acc)[4][4], const float (&gsc)[4],
+                                                       int m0, int n0, int wm, int wn) {
+  constexpr int TP = 136;
+  const int tid = threadIdx.x, lane = tid & 63, grp = lane >> 4, r16 = lane & 15;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        T[(wm * 64 + mt * 16 + 4 * grp + i) * TP + wn * 64 + nt * 16 + r16] = f2bf(acc[mt][nt][i] * gsc[nt]);
+  __syncthreads();
+  const RopeArgs& r = a.rope;
+  const int D = r.D, half = D >> 1, L = D >> 3, lgL = __builtin_ctz(L);
+  const int hpt = 128 / D, nheads = r.H + 2 * r.KV;
+#pragma unroll 1
+  for (int it = 0; it < 8; ++it) {
+    const int idx = it * 256 + tid;
+    const int gi = idx >> lgL, j = idx & (L - 1);
+    const int row = gi / hpt, hl = gi - row * hpt;
+    const int m = m0 + row, hh = n0 / D + hl;
+    const int c0 = row * TP + hl * D + 4 * j;
+    const uint2 u1 = *reinterpret_cast<const uint2*>(&T[c0]);
+    const uint2 u2 = *reinterpret_cast<const uint2*>(&T[c0 + half]);
+    const uint32_t w1[2] = {u1.x, u1.y}, w2[2] = {u2.x, u2.y};
+    float x1[4], x2[4], ss = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      x1[2 * e] = __uint_as_float(w1[e] << 16);
+      x1[2 * e + 1] = __uint_as_float(w1[e] & 0xFFFF0000u);
+      x2[2 * e] = __uint_as_float(w2[e] << 16);
+      x2[2 * e + 1] = __uint_as_float(w2[e] & 0xFFFF0000u);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ss += x1[e] * x1[e] + x2[e] * x2[e];
+    for (int o = 1; o < L; o <<= 1) ss += __shfl_xor(ss, o, 64);
+    if (m >= r.M || hh >= nheads) continue;
+    const int slot = r.row_slot[m], p = r.row_pos[m];
+    if (hh >= r.H + r.KV) {
+      bf16_t* dst = r.vcache + (((size_t)slot * r.KV + (hh - r.H - r.KV)) * r.max_ctx + p) * D;
+      *reinterpret_cast<uint2*>(dst + 4 * j) = u1;
+      *reinterpret_cast<uint2*>(dst + half + 4 * j) = u2;
+      continue;
+    }
+    const bool isq = hh < r.H;
+    const float* gn = isq ? r.q_gain : r.k_gain;
+    const float4 g1 = *reinterpret_cast<const float4*>(gn + 4 * j);
+    const float4 g2 = *reinterpret_cast<const float4*>(gn + half + 4 * j);
+    const float4 cs01 = *reinterpret_cast<const float4*>(r.rope + (size_t)p * half + 4 * j);
+    const float4 cs23 = *reinterpret_cast<const float4*>(r.rope + (size_t)p * half + 4 * j + 2);
+    const float gv1[4] = {g1.x, g1.y, g1.z, g1.w}, gv2[4] = {g2.x, g2.y, g2.z, g2.w};
+    const float cv[4] = {cs01.x, cs01.z, cs23.x, cs23.z}, sv[4] = {cs01.y, cs01.w, cs23.y, cs23.w};
+    const float rinv = 1.0f / sqrtf(ss / (float)D + r.eps);
+    uint32_t o1[2], o2[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      uint32_t lo1 = 0, lo2 = 0;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int q = 2 * e + h;
+        const float y1 = rbf(x1[q] * rinv * gv1[q]);
+        const float y2 = rbf(x2[q] * rinv * gv2[q]);
+        lo1 |= (uint32_t)f2bf(y1 * cv[q] - y2 * sv[q]) << (16 * h);
+        lo2 |= (uint32_t)f2bf(y2 * cv[q] + y1 * sv[q]) << (16 * h);
+      }
+      o1[e] = lo1;
+      o2[e] = lo2;
+    }
+    bf16_t* dst = isq ? a.out + (size_t)m * a.ldo + (size_t)hh * D
+                      : r.kcache + (((size_t)slot * r.KV + (hh - r.H)) * r.max_ctx + p) * D;
+    *reinterpret_cast<uint2*>(dst + 4 * j) = make_uint2(o1[0], o1[1]);
+    *reinterpret_cast<uint2*>(dst + half + 4 * j) = make_uint2(o2[0], o2[1]);
+  }
+}
+
 // Prefill GEMM for many token rows (the tile grid fills the GPU): a 128x128 output tile per
 // work-group of 4 waves, each wave a 64x64 block of 4x4 MFMA 16x16x32 tiles, so every
 // fragment read from LDS feeds four MFMAs (the 64x64-tile kernel's 32x32 wave blocks get
@@ -864,10 +949,11 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(GemmArgs a) {
   constexpr int BM = 128, BN = 128, BK = 64;
   constexpr int OOB = (int)0x80000000;
   // LDS holds each 16-row x 32-k operand fragment in MFMA lane order: lane l's 8 values
-  // (row l % 16, k 8*(l/16) ..) at byte 16*l, so a fragment read is 1 KB of consecutive
-  // bytes; fragment f of a stage sits at 1088*f, so odd fragments start 16 banks (of 32)
-  // further along than even ones and the staging writes of a row's two k halves, which go
-  // to fragments 2b and 2b+1 from neighbouring lanes, use disjoint banks
+  // (row l % 16, k 8*(l/16) ..) in 16-byte slot l ^ ((l / 16) % 4) of the fragment, so a
+  // fragment read is 1 KB of consecutive bytes in which every 8 consecutive lanes hit 8
+  // different bank groups; fragment f of a stage sits at 1088*f (odd fragments start 16
+  // banks of 32 further along).  The staging writes of 8 consecutive lanes (one A row's 8
+  // k chunks, or two W rows' 4 chunks) then also land on 8 different bank groups.
   constexpr int FRAG = 1088;                    // bytes per fragment slot
   constexpr int NFRAG = (BM / 16) * (BK / 32);  // 16 fragments per operand per stage
   __shared__ __align__(16) unsigned char Ab[2][NFRAG * FRAG];
@@ -887,33 +973,36 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(GemmArgs a) {
       __builtin_amdgcn_make_buffer_rsrc((void*)a.A, 0, a.M * a.lda * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t wrsc =
       __builtin_amdgcn_make_buffer_rsrc((void*)a.W, 0, a.N * a.K, 0x00020000);
-  // staging: thread tid brings k 32h .. 32h+31 (h = tid & 1) of tile row r = tid >> 1 for A
-  // (64 bytes) and W (32 bytes); its 8-value chunk j lands in fragment 2*(r/16) + h at lane
-  // position r%16 + 16j
-  const int sr = tid >> 1, sh = tid & 1;
-  const int sfrag = ((sr >> 4) * 2 + sh) * FRAG + (sr & 15) * 16;
+  // staging, row-contiguous across lanes: A load j of thread tid is k chunk ca = tid % 8
+  // (8 values) of tile row 32j + tid/8; W load j is k chunk cw = tid % 4 (16 codes, two
+  // 8-value chunks once converted) of tile row 64j + tid/4
+  const int ca = tid & 7, ra = tid >> 3, cw = tid & 3, rw = tid >> 2;
+  auto slot = [](int row, int c) {  // byte offset of 8-value chunk c (of 8) of stage row row
+    const int pos = (row & 15) + 16 * (c & 3);
+    return ((row >> 4) * 2 + (c >> 2)) * FRAG + 16 * (pos ^ (c & 3));
+  };
   struct Stage { uint4 a[4]; uint4 w[2]; };
   auto fetch = [&](int step, Stage& q) {
-    const int k = step * BK + 32 * sh;
-    const bool ok = k < a.K;  // K is a multiple of 32
-    const int ab = ((m0 + sr) * a.lda + k) * 2;
+    const int ka = step * BK + 8 * ca, kw = step * BK + 16 * cw;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      q.a[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(arsc, ok ? ab + 16 * j : OOB, 0, 0));
-    const int wb = (n0 + sr) * a.K + k;
+      q.a[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             arsc, ka < a.K ? ((m0 + 32 * j + ra) * a.lda + ka) * 2 : OOB, 0, 0));
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-      q.w[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wrsc, ok ? wb + 16 * j : OOB, 0, 0));
+      q.w[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             wrsc, kw < a.K ? (n0 + 64 * j + rw) * a.K + kw : OOB, 0, 0));
   };
   auto stash = [&](const Stage& q, int buf) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(&Ab[buf][sfrag + 256 * j]) = q.a[j];
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(&Ab[buf][slot(32 * j + ra, ca)]) = q.a[j];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      *reinterpret_cast<bf16x8_t*>(&Wb[buf][sfrag + 512 * j]) = i8x8_to_bf16x8(make_uint2(q.w[j].x, q.w[j].y));
-      *reinterpret_cast<bf16x8_t*>(&Wb[buf][sfrag + 512 * j + 256]) = i8x8_to_bf16x8(make_uint2(q.w[j].z, q.w[j].w));
+      *reinterpret_cast<bf16x8_t*>(&Wb[buf][slot(64 * j + rw, 2 * cw)]) = i8x8_to_bf16x8(make_uint2(q.w[j].x, q.w[j].y));
+      *reinterpret_cast<bf16x8_t*>(&Wb[buf][slot(64 * j + rw, 2 * cw + 1)]) = i8x8_to_bf16x8(make_uint2(q.w[j].z, q.w[j].w));
     }
   };
+  const int rd = 16 * (lane ^ (grp & 3));  // this lane's slot in every fragment read
 
   f32x4_t acc[4][4];
 #pragma unroll
@@ -936,10 +1025,10 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(GemmArgs a) {
         bf16x8_t af[4], bw[4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
-          af[mt] = *reinterpret_cast<const bf16x8_t*>(&Ab[u][((wm * 4 + mt) * 2 + sub) * FRAG + 16 * lane]);
+          af[mt] = *reinterpret_cast<const bf16x8_t*>(&Ab[u][((wm * 4 + mt) * 2 + sub) * FRAG + rd]);
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt)
-          bw[nt] = *reinterpret_cast<const bf16x8_t*>(&Wb[u][((wn * 4 + nt) * 2 + sub) * FRAG + 16 * lane]);
+          bw[nt] = *reinterpret_cast<const bf16x8_t*>(&Wb[u][((wn * 4 + nt) * 2 + sub) * FRAG + rd]);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -957,6 +1046,12 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(GemmArgs a) {
   for (int nt = 0; nt < 4; ++nt) {
     const int n = n0 + wn * 64 + nt * 16 + r16;
     gsc[nt] = a.scale[n < a.N ? n : 0];
+  }
+  if constexpr (EPI == EPI_STORE) {
+    if (a.fuse_rope) {
+      gemm_big_rope_epilogue(a, reinterpret_cast<bf16_t*>(&Ab[0][0]), acc, gsc, m0, n0, wm, wn);
+      return;
+    }
   }
   // lane holds D[4*(lane/16)+i][lane%16] of each 16x16 tile: token rows, channel columns
 #pragma unroll
@@ -2608,8 +2703,9 @@ hipError_t launch_skinny(const GemvArgs& a, int epi, hipStream_t st) {
   return skinny_tt<4>(a, epi, st);
 }
 
-hipError_t launch_gemm(const GemmArgs& a0, hipStream_t st, int* splits_used) {
+hipError_t launch_gemm(const GemmArgs& a0, hipStream_t st, int* splits_used, int* rope_done) {
   GemmArgs a = a0;
+  if (rope_done) *rope_done = 0;
   if ((a.K & 31) || (size_t)(a.M + 64) * a.lda * 2 > 0x7FFFFFFFu || (size_t)(a.N + 64) * a.K > 0x7FFFFFFFu ||
       (size_t)(a.M + 64) * a.ldo * 2 > 0x7FFFFFFFu)
     return hipErrorInvalidValue;
@@ -2617,6 +2713,10 @@ hipError_t launch_gemm(const GemmArgs& a0, hipStream_t st, int* splits_used) {
   const int big_tiles = ((a.N + 127) / 128) * ((a.M + 127) / 128);
   if (big_tiles >= 256 && a.use_big != 0) {
     if (splits_used) *splits_used = 1;
+    const RopeArgs& r = a.rope;
+    a.fuse_rope = a.fuse_rope && a.epi == EPI_STORE && (r.D == 64 || r.D == 128) &&
+                  a.N == (r.H + 2 * r.KV) * r.D && a.ldo % 4 == 0 && r.M == a.M;
+    if (rope_done) *rope_done = a.fuse_rope;
     switch (a.epi) {
       case EPI_STORE: hipLaunchKernelGGL(k_gemm_big<EPI_STORE>, dim3(big_tiles), dim3(256), 0, st, a); break;
       case EPI_RESID: hipLaunchKernelGGL(k_gemm_big<EPI_RESID>, dim3(big_tiles), dim3(256), 0, st, a); break;
@@ -2624,6 +2724,7 @@ hipError_t launch_gemm(const GemmArgs& a0, hipStream_t st, int* splits_used) {
     }
     return hipGetLastError();
   }
+  a.fuse_rope = 0;
   const int tiles = ((a.N + 63) / 64) * ((a.M + 63) / 64);
   // few rows (at most two 64-row tiles): the k-sliced kernel when its k splits (256..1024 k
   // each) cover K; more than one split only as deferred residual partials, enough splits to

@@ -56,6 +56,10 @@ CONFIGS = {
     "long-0.6b-l2": (ModelShape(hidden=1024, n_layers=2, n_heads=16, n_kv_heads=8,
                                 head_dim=128, intermediate=3072, vocab=151936),
                      0, "uniform", 8192, 1005, 4),
+    # head_dim 64 with 32 heads of q|k|v and a 2048-token prompt: the prefill q|k|v GEMM
+    # takes 256 tiles of 128x128 (two heads each) with QK-norm and RoPE in its epilogue
+    "rope64": (ModelShape(hidden=256, n_layers=2, n_heads=16, n_kv_heads=8, head_dim=64,
+                          intermediate=512, vocab=1000), 6, "uniform", 2048, 1006, 3),
     "qwen3-1.7b": (SHAPES["qwen3-1.7b"], 0, "ones", 256, 1000, 3),
     # Qwen3-0.6B on the first 2048 ids of the long-context prompt (8192 ids, seed 1000)
     "qwen3-0.6b-2k": (SHAPES["qwen3-0.6b"], 0, "ones", 2048, 1000, 3),

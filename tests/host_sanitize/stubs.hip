@@ -18,7 +18,7 @@ hipError_t launch_resid_norm(bf16_t*, int, int, const float*, int, const float*,
 hipError_t launch_gemv(const GemvArgs&, int, hipStream_t) { QD_STUB; }
 hipError_t launch_skinny(const GemvArgs&, int, hipStream_t) { QD_STUB; }
 bool skinny_norm_ok(int, int, int, int) { return false; }
-hipError_t launch_gemm(const GemmArgs&, hipStream_t, int*) { QD_STUB; }
+hipError_t launch_gemm(const GemmArgs&, hipStream_t, int*, int*) { QD_STUB; }
 hipError_t launch_qk_rope(const RopeArgs&, hipStream_t) { QD_STUB; }
 hipError_t launch_sample(const SampleArgs&, int, hipStream_t) { QD_STUB; }
 hipError_t sample_scratch_address(void**) { QD_STUB; }

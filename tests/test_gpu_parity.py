@@ -362,6 +362,29 @@ def test_prefill_few_rows_both_gemm_kernels(n_prompt):
         m.close()
 
 
+ROPE64 = ModelShape(hidden=256, n_layers=2, n_heads=16, n_kv_heads=8, head_dim=64,
+                    intermediate=512, vocab=1000)
+
+
+@pytest.mark.parametrize("mode", [1, 0], ids=["fused-rope", "separate-rope"])
+def test_prefill_qkv_epilogue_rope_head_dim_64(mode):
+    """2048-token prompt, head_dim 64, 32 q|k|v heads: the q|k|v projection runs as 256
+    tiles of 128x128 (two heads each); mode 1 does the QK-norm, RoPE and K/V cache writes
+    in that GEMM's epilogue, mode 0 in the separate launch.  Two teacher-forced decode steps
+    read the K/V rows the prefill wrote."""
+    w = make_weights(ROPE64, seed=6, gains="uniform")
+    qm = quantize_model(w)
+    prompt = make_prompt(ROPE64.vocab, 2048, 1006)
+    orc = Oracle(ROPE64, qm, mode="bf16").generate(prompt, 3)
+    say(f"[gpu] rope64 2048-token prefill, prefill_gemm={mode}")
+    m = _model(ROPE64, w, max_batch=1, max_ctx=2064, max_prefill_tokens=2048)
+    try:
+        m.set_tuning(prefill_gemm=mode)
+        _teacher_forced(m, ROPE64, qm, prompt, 2, "rope64", "rope64", 0, orc)
+    finally:
+        m.close()
+
+
 def test_teacher_forced_long_context():
     """1500-token prompt: 24 prefill tiles per head; decode attention over many position
     splits (per-step kernels: ~24 merged splits; persistent: 12 splits of one 128-position
