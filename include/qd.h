@@ -370,6 +370,10 @@ typedef enum {
                                      token rows and, for many rows, QK-norm / RoPE / K/V cache
                                      writes in the q|k|v GEMM's epilogue where the shapes allow;
                                      0: the k-stepped kernel and a separate QK-norm launch */
+  QD_TUNE_SKINNY_XSTAGE = 11,     /* batched decode projections of 2..16 rows (other than those
+                                     with the RMSNorm folded in): 1 (default) load activation
+                                     rows contiguously and reorder them through LDS; 0: load
+                                     them directly in the matrix-core operand layout */
 } qd_tune_knob;
 
 /* Sets a knob; captured decode graphs are dropped so the next call re-captures.

@@ -270,6 +270,7 @@ struct qd_model {
   int gemm_rope = 1;    // the 128x128-tile q|k|v GEMM may run QK-norm / RoPE in its epilogue
   int skinny_norm = 1;   // batched projections fold the RMSNorm where the shape allows
   int skinny_split = 2;  // 1: never; 2: fewer than 128 channel tiles, over 16 rows; 3: all
+  int skinny_xstage = 1; // batched projections load activations row-contiguously via LDS
   // persistent single-sequence decode (one cooperative launch per call)
   bool persist_ok = false;     // this shape and device can run it
   std::string persist_why;     // why not, when persist_ok is false
@@ -410,6 +411,7 @@ qd_status dec_proj(qd_model* m, int B, const bf16_t* x, int ldx, const float* ga
   a.x = x; a.ldx = ldx;
   a.kpart = m->ws<float>(m->P.gemm_part);
   a.kcnt = m->ws<unsigned int>(m->P.sk_cnt);
+  a.no_xstage = !m->skinny_xstage;
   HIPCHK(launch_skinny(a, epi, st));
   return QD_OK;
 }
@@ -1610,7 +1612,7 @@ qd_status qd_set_tuning(qd_model* m, int32_t knob, int32_t value) {
   if (value < 0 || (value < 1 && knob != QD_TUNE_ATTN_MERGE_LAST && knob != QD_TUNE_ATTN_WAVES &&
                     knob != QD_TUNE_PERSISTENT && knob != QD_TUNE_GEMM_SPLITS &&
                     knob != QD_TUNE_ATTN_OCCUPANCY && knob != QD_TUNE_SKINNY_NORM &&
-                    knob != QD_TUNE_PREFILL_GEMM))
+                    knob != QD_TUNE_PREFILL_GEMM && knob != QD_TUNE_SKINNY_XSTAGE))
     return fail(QD_ERR_INVALID_ARGUMENTS, "value out of range");
   switch (knob) {
     case QD_TUNE_ATTN_MAX_SPLITS: m->attn_max_splits = value; break;
@@ -1630,6 +1632,10 @@ qd_status qd_set_tuning(qd_model* m, int32_t knob, int32_t value) {
     case QD_TUNE_SKINNY_NORM:
       if (value > 1) return fail(QD_ERR_INVALID_ARGUMENTS, "skinny norm mode must be 0 or 1");
       m->skinny_norm = value;
+      break;
+    case QD_TUNE_SKINNY_XSTAGE:
+      if (value > 1) return fail(QD_ERR_INVALID_ARGUMENTS, "activation staging mode must be 0 or 1");
+      m->skinny_xstage = value;
       break;
     case QD_TUNE_PREFILL_GEMM:
       if (value > 1) return fail(QD_ERR_INVALID_ARGUMENTS, "prefill GEMM mode must be 0 or 1");

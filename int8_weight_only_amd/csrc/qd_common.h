@@ -53,6 +53,8 @@ struct GemvArgs {
   int ksplit;                        // <= 1: one work-group per tile
   float* kpart;                      // [tiles][ksplit][CTW][16*TT tokens x 16 channels] partials
   unsigned int* kcnt;                // [tiles] arrival counters, zero on entry, reset by the last
+  int no_xstage;                     // skinny, up to 16 rows: 1 = activations loaded straight in
+                                     // the MFMA operand layout instead of row-contiguous + LDS
 };
 constexpr int SKINNY_MAX_SPLIT = 16;
 constexpr int SKINNY_MAX_TILES = 4096;

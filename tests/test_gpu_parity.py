@@ -187,16 +187,20 @@ def test_batched_ragged_generate_matches_single(tiny_setup):
             assert batched[i, k] == orc["ids"][k] == single[k], (i, k)
 
 
-def test_batched_teacher_forced_logits():
-    """B=9 (two GEMV batch groups) teacher-forced against the oracle per sequence."""
+@pytest.mark.parametrize("xstage", [1, 0], ids=["row-staged", "operand-loads"])
+def test_batched_teacher_forced_logits(xstage):
+    """B=9 (one 16-row MFMA tile) teacher-forced against the oracle per sequence, with the
+    activations loaded row-contiguously and reordered in LDS (default) or loaded directly
+    in the operand layout."""
     shape = TINY
     w = make_weights(shape, seed=2, gains="uniform")
     qm = quantize_model(w)
     B = 9
     prompts = make_prompts(shape.vocab, 12, B, seed0=2000)
-    say("[gpu] batched teacher-forced B=9")
+    say(f"[gpu] batched teacher-forced B=9, skinny_xstage={xstage}")
     m = _model(shape, w, max_batch=B, max_ctx=64, max_prefill_tokens=B * 12)
     try:
+        m.set_tuning(skinny_xstage=xstage)
         orcs = [Oracle(shape, qm, mode="bf16").generate(p, 6) for p in prompts]
         nxt, lg = m.prefill(list(prompts), logits=True)
         torch.cuda.synchronize()
