@@ -374,6 +374,9 @@ typedef enum {
                                      with the RMSNorm folded in): 1 (default) load activation
                                      rows contiguously and reorder them through LDS; 0: load
                                      them directly in the matrix-core operand layout */
+  QD_TUNE_FLASH_ROWS = 12,        /* prefill attention query rows per work-group: 64, 128 (head
+                                     dim up to 128), or 0 (default: 128 when those tiles give
+                                     every CU two work-groups) */
 } qd_tune_knob;
 
 /* Sets a knob; captured decode graphs are dropped so the next call re-captures.

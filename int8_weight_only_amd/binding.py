@@ -93,7 +93,7 @@ EXPORTS = ("qd_last_error", "qd_check_shape", "qd_query_sizes", "qd_load_weights
            "qd_decode_step_slots", "qd_sample", "qd_save_cache", "qd_load_cache",
            "qd_check_cache", "qd_sha256", "qd_run_op", "qd_sample_noalloc")
 TUNING = {"attn_max_splits": 0, "attn_min_chunks": 1, "attn_waves": 2, "attn_merge_last": 3,
-          "persistent": 4, "persist_splits": 5, "skinny_split": 6, "gemm_splits": 7, "attn_occupancy": 8, "skinny_norm": 9, "prefill_gemm": 10, "skinny_xstage": 11}
+          "persistent": 4, "persist_splits": 5, "skinny_split": 6, "gemm_splits": 7, "attn_occupancy": 8, "skinny_norm": 9, "prefill_gemm": 10, "skinny_xstage": 11, "flash_rows": 12}
 PROF_KERNELS = ("embed", "qkv", "attn", "o", "gateup", "down", "lmhead")
 OPS = {"embed": 0, "qkv": 1, "o": 2, "gateup": 3, "down": 4, "lmhead": 5}
 

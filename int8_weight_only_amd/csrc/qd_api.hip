@@ -268,6 +268,7 @@ struct qd_model {
   int gemm_splits = 0;  // prefill GEMM split-K cap (0: launcher default)
   int gemm_ks = 1;      // prefill GEMMs of few rows may take the k-sliced kernel
   int gemm_rope = 1;    // the 128x128-tile q|k|v GEMM may run QK-norm / RoPE in its epilogue
+  int flash_rows = 0;   // prefill attention query tile rows: 64, 128, or 0 (by prompt size)
   int skinny_norm = 1;   // batched projections fold the RMSNorm where the shape allows
   int skinny_split = 2;  // 1: never; 2: fewer than 128 channel tiles, over 16 rows; 3: all
   int skinny_xstage = 1; // batched projections load activations row-contiguously via LDS
@@ -547,13 +548,22 @@ qd_status enqueue_prefill(qd_model* m, int n, const int* ids_dev, const std::vec
   int* h_last = h_rp + P.mmax;
   int* h_lens = h_last + Bmax;
   int* h_tiles = h_lens + Bmax;
+  // attention query tiles of 128 rows when they alone give every CU two work-groups (head
+  // dims up to 128), else 64
+  int tile_rows = m->flash_rows;
+  if (tile_rows == 0) {
+    long long t128 = 0;
+    for (int b = 0; b < n; ++b) t128 += (lens[b] + 2 * FLASH_ROWS - 1) / (2 * FLASH_ROWS);
+    tile_rows = (d.D <= 128 && t128 * d.H >= 512) ? 2 * FLASH_ROWS : FLASH_ROWS;
+  }
+  if (d.D > 128) tile_rows = FLASH_ROWS;
   int M = 0, n_tiles = 0;
   for (int b = 0; b < n; ++b) {
-    for (int p0 = 0; p0 < lens[b]; p0 += FLASH_ROWS) {
+    for (int p0 = 0; p0 < lens[b]; p0 += tile_rows) {
       h_tiles[4 * n_tiles + 0] = M + p0;
       h_tiles[4 * n_tiles + 1] = slots ? slots[b] : b;
       h_tiles[4 * n_tiles + 2] = p0;
-      h_tiles[4 * n_tiles + 3] = std::min(FLASH_ROWS, lens[b] - p0);
+      h_tiles[4 * n_tiles + 3] = std::min(tile_rows, lens[b] - p0);
       ++n_tiles;
     }
     for (int t = 0; t < lens[b]; ++t) {
@@ -629,7 +639,7 @@ qd_status enqueue_prefill(qd_model* m, int n, const int* ids_dev, const std::vec
     fa.tiles = dtiles;
     fa.H = d.H; fa.KV = d.KV; fa.D = d.D; fa.max_ctx = m->lim.max_ctx;
     fa.out = attn; fa.ldo = d.HD;
-    HIPCHK(launch_flash_prefill(fa, n_tiles, st));
+    HIPCHK(launch_flash_prefill(fa, n_tiles, tile_rows, st));
     g = GemmArgs{};
     g.A = attn; g.lda = d.HD; g.W = m->w<int8_t>(o.o_q); g.scale = m->w<float>(o.o_s);
     g.M = M; g.N = d.d; g.K = d.HD; g.epi = EPI_RESID; g.out = x; g.ldo = d.d; g.part = gpart; g.cnt = m->ws<unsigned int>(P.sk_cnt); g.splits = m->gemm_splits; g.use_ks = m->gemm_ks;
@@ -1612,7 +1622,8 @@ qd_status qd_set_tuning(qd_model* m, int32_t knob, int32_t value) {
   if (value < 0 || (value < 1 && knob != QD_TUNE_ATTN_MERGE_LAST && knob != QD_TUNE_ATTN_WAVES &&
                     knob != QD_TUNE_PERSISTENT && knob != QD_TUNE_GEMM_SPLITS &&
                     knob != QD_TUNE_ATTN_OCCUPANCY && knob != QD_TUNE_SKINNY_NORM &&
-                    knob != QD_TUNE_PREFILL_GEMM && knob != QD_TUNE_SKINNY_XSTAGE))
+                    knob != QD_TUNE_PREFILL_GEMM && knob != QD_TUNE_SKINNY_XSTAGE &&
+                    knob != QD_TUNE_FLASH_ROWS))
     return fail(QD_ERR_INVALID_ARGUMENTS, "value out of range");
   switch (knob) {
     case QD_TUNE_ATTN_MAX_SPLITS: m->attn_max_splits = value; break;
@@ -1632,6 +1643,11 @@ qd_status qd_set_tuning(qd_model* m, int32_t knob, int32_t value) {
     case QD_TUNE_SKINNY_NORM:
       if (value > 1) return fail(QD_ERR_INVALID_ARGUMENTS, "skinny norm mode must be 0 or 1");
       m->skinny_norm = value;
+      break;
+    case QD_TUNE_FLASH_ROWS:
+      if (value != 0 && value != 64 && value != 128)
+        return fail(QD_ERR_INVALID_ARGUMENTS, "prefill attention tile rows must be 0, 64 or 128");
+      m->flash_rows = value;
       break;
     case QD_TUNE_SKINNY_XSTAGE:
       if (value > 1) return fail(QD_ERR_INVALID_ARGUMENTS, "activation staging mode must be 0 or 1");

@@ -276,7 +276,8 @@ hipError_t launch_reset_seq(int* counts, int* draws, const int* slots, int n, in
 hipError_t launch_attention_decode(const AttnDecArgs& a, hipStream_t st);
 // work-groups of the decode attention kernel for (D, G, waves) resident on one CU
 hipError_t attention_decode_residency(int D, int G, int nwaves, int* blocks_per_cu);
-hipError_t launch_flash_prefill(const FlashArgs& a, int n_tiles, hipStream_t st);
+// tile_rows: FLASH_ROWS or 2 * FLASH_ROWS (head dim up to 128), as the tiles were cut
+hipError_t launch_flash_prefill(const FlashArgs& a, int n_tiles, int tile_rows, hipStream_t st);
 hipError_t launch_set_positions(int* pos, const int* lens, const int* slots, int n, hipStream_t st);
 hipError_t launch_iota(int* p, int n, hipStream_t st);
 

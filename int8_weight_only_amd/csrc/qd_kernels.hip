@@ -2373,8 +2373,11 @@ __global__ __launch_bounds__(128) void k_attn_dec_merge(AttnDecArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Prefill attention on MFMA (causal, flash style).  A work-group owns up to 64 query rows
-// of one sequence (4 waves x 16 rows) and one query head h of KV group g = h / (H/KV).
+// Prefill attention on MFMA (causal, flash style).  A work-group owns up to 64*RG query
+// rows of one sequence (4 waves x RG groups of 16 rows: wave w holds rows 64*rg + 16*w ..)
+// and one query head h of KV group g = h / (H/KV).  With RG = 2 every K and V fragment read
+// from LDS feeds two row groups' MFMAs (half the LDS reads per score), at 2 work-groups
+// per CU instead of 3; long prompts take it, short ones keep RG = 1 for more work-groups.
 // Keys and values advance in blocks of 64 positions staged once in LDS for all waves
 // (V transposed).  Each wave computes the transposed products S^T = K Q^T and
 // O^T = V^T P^T, so a lane always holds one query row (its lane index mod 16): the MFMA
@@ -2384,8 +2387,8 @@ __global__ __launch_bounds__(128) void k_attn_dec_merge(AttnDecArgs a) {
 // that order (key 8a + 4t + i of a 32-key step at row 16t + 4a + i), so the fragment reads
 // stay on consecutive rows.  P is split into bf16 high and low parts (two MFMAs), so the
 // probabilities enter the product with ~16 significant bits rather than bf16's 8.
-template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 3 : 1))) void k_flash_prefill(
+template <int D, int RG>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 4 - RG : 1))) void k_flash_prefill(
     FlashArgs a) {
   constexpr int KB = 64;             // keys per block
   constexpr int NKK = KB / 32;       // 32-key steps per block (two S^T tiles each)
@@ -2406,24 +2409,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 
   const bf16_t* Vb = a.vcache + ((size_t)slot * a.KV + g) * a.max_ctx * D;
   const int kmax = pos0 + nrows;  // keys 0..kmax-1 are visible to some row of the tile
 
-  // this lane's query row and its Q fragments (B operand of S^T): dims 32*ks + 8*grp
-  const int r = 16 * wid + r16;
-  const bool row_ok = r < nrows;
-  const int qpos = pos0 + r;
-  bf16x8_t qf[KS];
-  {
-    const bf16_t* qr = a.q + (size_t)(row0 + (row_ok ? r : 0)) * a.ldq + (size_t)h * D;
+  // this lane's query rows (one per row group) and their Q fragments (B operand of S^T):
+  // dims 32*ks + 8*grp
+  int r[RG], qpos[RG];
+  bool row_ok[RG];
+  bf16x8_t qf[RG][KS];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) {
+    r[rg] = 64 * rg + 16 * wid + r16;
+    row_ok[rg] = r[rg] < nrows;
+    qpos[rg] = pos0 + r[rg];
+    const bf16_t* qr = a.q + (size_t)(row0 + (row_ok[rg] ? r[rg] : 0)) * a.ldq + (size_t)h * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      qf[ks] = __builtin_bit_cast(
-          bf16x8_t, row_ok ? *reinterpret_cast<const uint4*>(qr + 32 * ks + 8 * grp) : make_uint4(0, 0, 0, 0));
+      qf[rg][ks] = __builtin_bit_cast(
+          bf16x8_t, row_ok[rg] ? *reinterpret_cast<const uint4*>(qr + 32 * ks + 8 * grp) : make_uint4(0, 0, 0, 0));
   }
-  // softmax state of the lane's row: m is the same in the row's four lanes (reduced), l is
+  // softmax state of the lane's rows: m is the same in a row's four lanes (reduced), l is
   // this lane's share of the row sum (its keys only), reduced once at the end
-  float m = -INFINITY, l = 0.0f;
-  f32x4_t o[NT];  // O^T: dims 16*nt + 4*grp + i of the lane's row
+  float m[RG], l[RG];
+  f32x4_t o[RG][NT];  // O^T: dims 16*nt + 4*grp + i of the lane's rows
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) o[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int rg = 0; rg < RG; ++rg) {
+    m[rg] = -INFINITY;
+    l[rg] = 0.0f;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) o[rg][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
   // scores in base 2: exp(z - m) = exp2(z*log2(e) - m*log2(e)), one hardware exp each
   const float scale2 = 1.4426950408889634f / sqrtf((float)D);
 
@@ -2496,62 +2508,69 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 
     __syncthreads();
     fetch(kb + KB, ks, vs);  // past kmax: reads zero, never used
 
-    // S^T tiles: st[kk][t][i] = score of the lane's row against key kb + 32kk + 8grp + 4t + i
-    f32x4_t st[NKK][2];
+    // S^T tiles: st[rg][kk][t][i] = score of the lane's row of group rg against key
+    // kb + 32kk + 8grp + 4t + i (each K fragment read feeds the RG row groups)
+    f32x4_t st[RG][NKK][2];
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        st[kk][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg) st[rg][kk][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks2 = 0; ks2 < KS; ++ks2) {
           const bf16x8_t kf = __builtin_bit_cast(
               bf16x8_t, *reinterpret_cast<const uint4*>(&Ks[32 * kk + 16 * t + r16][32 * ks2 + 8 * grp]));
-          st[kk][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks2], st[kk][t], 0, 0, 0);
+#pragma unroll
+          for (int rg = 0; rg < RG; ++rg)
+            st[rg][kk][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rg][ks2], st[rg][kk][t], 0, 0, 0);
         }
       }
     // causal mask + online softmax.  The row's reference maximum m moves only when the
     // block's maximum exceeds it by more than 2^TAU (so probabilities stay below 2^TAU);
     // the wave rescales O only then (the result is the same softmax, any reference gives it)
     constexpr float TAU = 8.0f;
-    float sv[NKK][2][4];
-    float smax = -INFINITY;
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk)
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = kb + 32 * kk + 8 * grp + 4 * t + i;
-          sv[kk][t][i] = (row_ok && key <= qpos) ? st[kk][t][i] * scale2 : -INFINITY;
-          smax = fmaxf(smax, sv[kk][t][i]);
-        }
-    smax = fmaxf(smax, __shfl_xor(smax, 16, 64));
-    smax = fmaxf(smax, __shfl_xor(smax, 32, 64));
-    if (__any(smax > m + TAU)) {
-      const float mnew = fmaxf(m, smax);
-      const float alpha = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - mnew);
-      l *= alpha;
-      m = mnew;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[nt][i] *= alpha;
-    }
     // P^T fragments (B operand): keys 32kk + 8grp + j, j = 4t + i, in high and low bf16 parts
-    bf16x8_t phi[NKK], plo[NKK];
+    bf16x8_t phi[RG][NKK], plo[RG][NKK];
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk)
+    for (int rg = 0; rg < RG; ++rg) {
+      float sv[NKK][2][4];
+      float smax = -INFINITY;
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = (sv[kk][t][i] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sv[kk][t][i] - m);
-          l += p;
-          const __bf16 hi = (__bf16)p;
-          phi[kk][4 * t + i] = hi;
-          plo[kk][4 * t + i] = (__bf16)(p - (float)hi);
-        }
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = kb + 32 * kk + 8 * grp + 4 * t + i;
+            sv[kk][t][i] = (row_ok[rg] && key <= qpos[rg]) ? st[rg][kk][t][i] * scale2 : -INFINITY;
+            smax = fmaxf(smax, sv[kk][t][i]);
+          }
+      smax = fmaxf(smax, __shfl_xor(smax, 16, 64));
+      smax = fmaxf(smax, __shfl_xor(smax, 32, 64));
+      if (__any(smax > m[rg] + TAU)) {
+        const float mnew = fmaxf(m[rg], smax);
+        const float alpha = (m[rg] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m[rg] - mnew);
+        l[rg] *= alpha;
+        m[rg] = mnew;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[rg][nt][i] *= alpha;
+      }
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float p = (sv[kk][t][i] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sv[kk][t][i] - m[rg]);
+            l[rg] += p;
+            const __bf16 hi = (__bf16)p;
+            phi[rg][kk][4 * t + i] = hi;
+            plo[rg][kk][4 * t + i] = (__bf16)(p - (float)hi);
+          }
+    }
     // O^T += V^T P^T: A = V^T (dims 16nt + r16, keys 32kk + 8grp..), B = P^T
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
@@ -2559,23 +2578,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 
       for (int nt = 0; nt < NT; ++nt) {
         const bf16x8_t vf = __builtin_bit_cast(
             bf16x8_t, *reinterpret_cast<const uint4*>(&Vt[16 * nt + r16][32 * kk + 8 * grp]));
-        o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, phi[kk], o[nt], 0, 0, 0);
-        o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, plo[kk], o[nt], 0, 0, 0);
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg) {
+          o[rg][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, phi[rg][kk], o[rg][nt], 0, 0, 0);
+          o[rg][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, plo[rg][kk], o[rg][nt], 0, 0, 0);
+        }
       }
     __syncthreads();
   };
   fetch(0, kst, vst);
   for (int kb = 0; kb < kmax; kb += KB) block(kb, kst, vst);
-  // the row sum over its four lanes; out[r][h*D + 16nt + 4grp + i], four dims per store
-  l += __shfl_xor(l, 16, 64);
-  l += __shfl_xor(l, 32, 64);
-  if (!row_ok) return;
-  bf16_t* orow = a.out + (size_t)(row0 + r) * a.ldo + (size_t)h * D + 4 * grp;
+  // each row sum over its four lanes; out[r][h*D + 16nt + 4grp + i], four dims per store
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const uint32_t w0 = (uint32_t)f2bf(o[nt][0] / l) | ((uint32_t)f2bf(o[nt][1] / l) << 16);
-    const uint32_t w1 = (uint32_t)f2bf(o[nt][2] / l) | ((uint32_t)f2bf(o[nt][3] / l) << 16);
-    *reinterpret_cast<uint2*>(orow + 16 * nt) = make_uint2(w0, w1);
+  for (int rg = 0; rg < RG; ++rg) {
+    float lr = l[rg];
+    lr += __shfl_xor(lr, 16, 64);
+    lr += __shfl_xor(lr, 32, 64);
+    if (!row_ok[rg]) continue;
+    bf16_t* orow = a.out + (size_t)(row0 + r[rg]) * a.ldo + (size_t)h * D + 4 * grp;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const uint32_t w0 = (uint32_t)f2bf(o[rg][nt][0] / lr) | ((uint32_t)f2bf(o[rg][nt][1] / lr) << 16);
+      const uint32_t w1 = (uint32_t)f2bf(o[rg][nt][2] / lr) | ((uint32_t)f2bf(o[rg][nt][3] / lr) << 16);
+      *reinterpret_cast<uint2*>(orow + 16 * nt) = make_uint2(w0, w1);
+    }
   }
 }
 
@@ -2985,15 +3011,27 @@ hipError_t launch_attention_decode(const AttnDecArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_flash_prefill(const FlashArgs& a, int n_tiles, hipStream_t st) {
+hipError_t launch_flash_prefill(const FlashArgs& a, int n_tiles, int tile_rows, hipStream_t st) {
   if (n_tiles < 1) return hipSuccess;
-  if (n_tiles > 65535) return hipErrorInvalidValue;
+  if (n_tiles > 65535 || (tile_rows != FLASH_ROWS && tile_rows != 2 * FLASH_ROWS) ||
+      (tile_rows == 2 * FLASH_ROWS && a.D > 128))
+    return hipErrorInvalidValue;
   dim3 grid(a.H, n_tiles);
+  const bool rg2 = tile_rows == 2 * FLASH_ROWS;
   switch (a.D) {
-    case 32: hipLaunchKernelGGL(k_flash_prefill<32>, grid, dim3(256), 0, st, a); break;
-    case 64: hipLaunchKernelGGL(k_flash_prefill<64>, grid, dim3(256), 0, st, a); break;
-    case 128: hipLaunchKernelGGL(k_flash_prefill<128>, grid, dim3(256), 0, st, a); break;
-    case 256: hipLaunchKernelGGL(k_flash_prefill<256>, grid, dim3(256), 0, st, a); break;
+    case 32:
+      if (rg2) hipLaunchKernelGGL((k_flash_prefill<32, 2>), grid, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((k_flash_prefill<32, 1>), grid, dim3(256), 0, st, a);
+      break;
+    case 64:
+      if (rg2) hipLaunchKernelGGL((k_flash_prefill<64, 2>), grid, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((k_flash_prefill<64, 1>), grid, dim3(256), 0, st, a);
+      break;
+    case 128:
+      if (rg2) hipLaunchKernelGGL((k_flash_prefill<128, 2>), grid, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((k_flash_prefill<128, 1>), grid, dim3(256), 0, st, a);
+      break;
+    case 256: hipLaunchKernelGGL((k_flash_prefill<256, 1>), grid, dim3(256), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

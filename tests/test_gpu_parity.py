@@ -344,6 +344,24 @@ def test_teacher_forced_mid_split_k():
         m.close()
 
 
+@pytest.mark.parametrize("rows", [64, 128])
+def test_prefill_attention_tile_rows(rows):
+    """200-token prompt with prefill attention query tiles of 64 rows (4 tiles) or 128 rows
+    (two row groups per wave; tiles of 128 and a ragged 72), against the oracle; later
+    layers read every row's attention output through the K/V cache."""
+    w = make_weights(MID, seed=4, gains="uniform")
+    qm = quantize_model(w)
+    prompt = make_prompt(MID.vocab, 200, 1004)
+    orc = Oracle(MID, qm, mode="bf16").generate(prompt, 3)
+    say(f"[gpu] mid prefill attention with {rows}-row tiles")
+    m = _model(MID, w, max_batch=1, max_ctx=256, max_prefill_tokens=256)
+    try:
+        m.set_tuning(flash_rows=rows)
+        _teacher_forced(m, MID, qm, prompt, 2, f"mid tiles{rows}", "mid", 0, orc)
+    finally:
+        m.close()
+
+
 @pytest.mark.parametrize("n_prompt", [64, 100])
 def test_prefill_few_rows_both_gemm_kernels(n_prompt):
     """Prompts of one and two 64-row tiles (100: ragged): the prefill projections through the
