@@ -66,7 +66,7 @@ def prefill_flops(s, M):
 
 
 KERNEL_SOURCES = [os.path.join(ROOT, "int8_weight_only_amd", "csrc", f)
-                  for f in ("qd_common.h", "qd_device.h", "qd_kernels.hip", "qd_persist.hip", "qd_sample.hip")]
+                  for f in ("qd_common.h", "qd_device.h", "qd_kernels.hip", "qd_sample.hip")]
 
 
 def kernel_source_sha() -> str:

@@ -136,7 +136,6 @@ typedef struct {
   double decode_us;    /* the max_new_tokens - 1 decode steps */
   int32_t steps;       /* decode steps run */
   int32_t n_prompt_tokens;
-  int32_t persistent;  /* 1: the decode steps ran as one persistent cooperative launch */
 } qd_stats;
 
 /* Message for the last failing call on this thread ("" if none). */
@@ -232,10 +231,7 @@ qd_status qd_prefill(qd_model* m, int32_t n_seqs, const int32_t* ids_dev,
  * next_ids_dev[B] and, if logits_dev is not NULL, fp32 logits [B, V].  Teacher
  * forcing is the caller choosing in_ids.  No host synchronization; the slot
  * lengths live on the device.  Returns QD_ERR_INVALID_ARGUMENTS if B is out of
- * range; the caller must not step a slot past max_ctx.  With QD_TUNE_PERSISTENT
- * set, B = 1 runs as one persistent cooperative launch; should one of its bounded
- * grid-barrier waits give up, the launch ends early, and the next call on the model
- * returns QD_ERR_DEVICE once that flag has reached the host. */
+ * range; the caller must not step a slot past max_ctx. */
 qd_status qd_decode_step(qd_model* m, int32_t B, const int32_t* in_ids_dev,
                          float* logits_dev, int32_t* next_ids_dev, qd_stream stream);
 
@@ -295,8 +291,7 @@ typedef struct {
  * (host).  Writes next_ids_dev[B] (device) and advances each slot's draw number.  The
  * caller feeds the drawn ids to the next decode step.  Asynchronous on `stream`.
  * Errors: QD_ERR_INVALID_ARGUMENTS (a parameter out of range, a NULL pointer, a slot out
- * of range, listed twice or holding no prompt), before any GPU work.  Decode steps run
- * by the opt-in persistent kernel (QD_TUNE_PERSISTENT) do not count their tokens. */
+ * of range, listed twice or holding no prompt), before any GPU work. */
 qd_status qd_sample(qd_model* m, int32_t B, const int32_t* slots_host, const qd_sampling* params,
                     const uint64_t* seeds_host, const float* logits_dev, int32_t* next_ids_dev,
                     qd_stream stream);
@@ -318,8 +313,7 @@ qd_status qd_sample_noalloc(qd_model* m, int32_t B, const int32_t* slots_host,
 /* One call, start to finish ("Model-agnostic LLM inference", section "Notes"):
  * prefill of B prompts (host ids, concatenated; lens_host[B]) then
  * max_new_tokens - 1 decode steps, greedy ids kept on the device between steps:
- * each step is replayed from a captured HIP graph, or, for B = 1 with
- * QD_TUNE_PERSISTENT set, one persistent cooperative launch runs every step.  out_ids_host[B * max_new_tokens] receives
+ * each step is replayed from a captured HIP graph.  out_ids_host[B * max_new_tokens] receives
  * the generated ids (row b = sequence b); n_out_host[b] the count up to and
  * including the first eos_id (eos_id < 0 disables the stop).  Synchronizes the
  * stream once at the end.  stats may be NULL. */
@@ -350,11 +344,7 @@ typedef enum {
   QD_TUNE_ATTN_MIN_CHUNKS = 1,    /* fewest 64-position chunks per split; default 1 */
   QD_TUNE_ATTN_WAVES = 2,         /* decode-attention waves per work-group: 4, 8, or 0 = by batch (default) */
   QD_TUNE_ATTN_MERGE_LAST = 3,    /* 1 (default): the last split merges in-kernel; 0: a merge launch */
-  QD_TUNE_PERSISTENT = 4,         /* 1: B = 1 decode runs as one persistent cooperative launch
-                                     where the shape allows it (head_dim 32, 64 or 128, at most
-                                     8 query heads per KV head); 0 (default): per-step kernels */
-  QD_TUNE_PERSIST_SPLITS = 5,     /* persistent decode: most position splits per KV head, 1..32
-                                     (default 32); each split is one work-group */
+  /* 4 and 5 are not used (unknown knobs) */
   QD_TUNE_SKINNY_SPLIT = 6,       /* batched decode projections split K over work-groups:
                                      1 never, 2 (default) projections with fewer than 128
                                      16-channel tiles at batches over 16, 3 all */

@@ -83,8 +83,7 @@ class BuffersC(ctypes.Structure):
 
 class StatsC(ctypes.Structure):
     _fields_ = [("prefill_us", ctypes.c_double), ("decode_us", ctypes.c_double),
-                ("steps", ctypes.c_int32), ("n_prompt_tokens", ctypes.c_int32),
-                ("persistent", ctypes.c_int32)]
+                ("steps", ctypes.c_int32), ("n_prompt_tokens", ctypes.c_int32)]
 
 
 EXPORTS = ("qd_last_error", "qd_check_shape", "qd_query_sizes", "qd_load_weights",
@@ -93,7 +92,8 @@ EXPORTS = ("qd_last_error", "qd_check_shape", "qd_query_sizes", "qd_load_weights
            "qd_decode_step_slots", "qd_sample", "qd_save_cache", "qd_load_cache",
            "qd_check_cache", "qd_sha256", "qd_run_op", "qd_sample_noalloc")
 TUNING = {"attn_max_splits": 0, "attn_min_chunks": 1, "attn_waves": 2, "attn_merge_last": 3,
-          "persistent": 4, "persist_splits": 5, "skinny_split": 6, "gemm_splits": 7, "attn_occupancy": 8, "skinny_norm": 9, "prefill_gemm": 10, "skinny_xstage": 11, "flash_rows": 12}
+          "skinny_split": 6, "gemm_splits": 7, "attn_occupancy": 8, "skinny_norm": 9,
+          "prefill_gemm": 10, "skinny_xstage": 11, "flash_rows": 12}
 PROF_KERNELS = ("embed", "qkv", "attn", "o", "gateup", "down", "lmhead")
 OPS = {"embed": 0, "qkv": 1, "o": 2, "gateup": 3, "down": 4, "lmhead": 5}
 
@@ -238,7 +238,6 @@ class GenerateResult:
     prefill_us: float
     decode_us: float
     steps: int
-    persistent: bool         # decode steps ran as one persistent cooperative launch
     prefill_tokens_per_sec: float
     decode_tokens_per_sec: float
 
@@ -447,6 +446,5 @@ class Model:
         return GenerateResult(
             token_ids=toks, n_prompt=[int(x) for x in lens], generated=out, n_generated=n_out,
             prefill_us=st.prefill_us, decode_us=st.decode_us, steps=st.steps,
-            persistent=bool(st.persistent),
             prefill_tokens_per_sec=(lens.sum() / (st.prefill_us * 1e-6)) if st.prefill_us > 0 else 0.0,
             decode_tokens_per_sec=(dec_tok / (st.decode_us * 1e-6)) if st.decode_us > 0 else 0.0)

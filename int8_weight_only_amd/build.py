@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libqd.so")
-SOURCES = ["qd_kernels.hip", "qd_persist.hip", "qd_sample.hip", "qd_api.hip", "qd_cache.cpp"]
+SOURCES = ["qd_kernels.hip", "qd_sample.hip", "qd_api.hip", "qd_cache.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

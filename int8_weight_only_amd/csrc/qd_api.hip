@@ -51,8 +51,6 @@ struct Plan {
   size_t smp_rowmax = 0, smp_hist = 0, smp_ncand = 0, smp_cand = 0;
   size_t pos = 0, next_ids = 0, lm_keys = 0, att_cnt = 0, sk_cnt = 0, done = 0, step = 0, out_ids = 0;
   size_t gemm_part = 0;
-  // persistent single-sequence decode: exchange buffers, barrier words, error flag
-  size_t pxg = 0, pqkv = 0, ppo = 0, pml = 0, pact = 0, pkeys = 0, pbar = 0, perr = 0;
   size_t ws_bytes = 0;
   size_t kv_bytes = 0;
   size_t kv_layer_elems = 0;  // bf16 elements of K (or V) per layer
@@ -215,14 +213,6 @@ Plan make_plan(const qd_model_shape& s, const qd_limits& lim) {
   P.step = take(64);
   P.out_ids = take((size_t)B * lim.max_ctx * 4);
   P.gemm_part = take(GEMM_PART_FLOATS * 4);
-  P.pxg = take((size_t)d.d * 2);
-  P.pqkv = take((size_t)d.NQKV * 2);
-  P.ppo = take((size_t)d.H * PERSIST_SPLITS * d.D * 4);
-  P.pml = take((size_t)d.H * PERSIST_SPLITS * 2 * 4);
-  P.pact = take((size_t)d.I * 2);
-  P.pkeys = take((size_t)PERSIST_MAX_WG * 8);
-  P.pbar = take((size_t)PERSIST_BAR_WORDS * 4);
-  P.perr = take(64);
   P.ws_bytes = off;
 
   P.kv_layer_elems = (size_t)B * d.KV * lim.max_ctx * d.D;
@@ -265,6 +255,7 @@ struct qd_model {
   int attn_resident4 = 3;  // four-wave attention work-groups that fit on one CU (measured)
   int attn_waves = 0;  // 0: eight waves only when B x KV heads fill the GPU without splits
   int attn_merge_last = 1;
+  void* noalloc_scratch = nullptr;  // this device's address of the sampler's fixed scratch
   int gemm_splits = 0;  // prefill GEMM split-K cap (0: launcher default)
   int gemm_ks = 1;      // prefill GEMMs of few rows may take the k-sliced kernel
   int gemm_rope = 1;    // the 128x128-tile q|k|v GEMM may run QK-norm / RoPE in its epilogue
@@ -272,16 +263,6 @@ struct qd_model {
   int skinny_norm = 1;   // batched projections fold the RMSNorm where the shape allows
   int skinny_split = 2;  // 1: never; 2: fewer than 128 channel tiles, over 16 rows; 3: all
   int skinny_xstage = 1; // batched projections load activations row-contiguously via LDS
-  // persistent single-sequence decode (one cooperative launch per call)
-  bool persist_ok = false;     // this shape and device can run it
-  std::string persist_why;     // why not, when persist_ok is false
-  int persist_on = 0;          // tuning knobs (measured slower than the per-step kernels)
-  int persist_splits = PERSIST_SPLITS;
-  int persist_nwg = 0, persist_lds = 0;
-  void* noalloc_scratch = nullptr;  // this device's address of the sampler's fixed scratch
-  int* herr = nullptr;         // pinned copy of the kernel's error flag
-  hipEvent_t err_ev = nullptr;
-  bool err_pending = false;
 
   template <class T> T* w(size_t off) { return reinterpret_cast<T*>(W + off); }
   template <class T> T* ws(size_t off) { return reinterpret_cast<T*>(WS + off); }
@@ -660,111 +641,6 @@ qd_status enqueue_prefill(qd_model* m, int n, const int* ids_dev, const std::vec
   return QD_OK;
 }
 
-// ---- persistent single-sequence decode ------------------------------------------------------
-// Shapes and devices the cooperative kernel serves; anything else keeps the multi-kernel path.
-std::string persist_problems(const qd_model* m, const hipDeviceProp_t& prop, int* nwg, int* lds) {
-  const Dims& d = m->d;
-  std::string p;
-  auto add = [&](const std::string& s) { p += (p.empty() ? "" : "; ") + s; };
-  const int PT = 64 * PERSIST_WAVES;
-  const int n = prop.multiProcessorCount;
-  if (d.D != 32 && d.D != 64 && d.D != 128) add("head_dim " + std::to_string(d.D) + " not in {32, 64, 128}");
-  if (d.G < 1 || d.G > 8) add("more than 8 query heads per KV head");
-  if (std::max(d.d, std::max(d.HD, d.I)) > PERSIST_MAX_K) add("a projection input is longer than 16384");
-  if (!prop.cooperativeLaunch) add("the device has no cooperative launch");
-  if (n < 1 || n > PERSIST_MAX_WG) add("unsupported CU count");
-  if (!p.empty()) return p;
-  // the kernel computes layer l's tensors as layer 0's plus l strides
-  const Plan& P = m->P;
-  for (int l = 1; l < d.L && p.empty(); ++l) {
-    const size_t st = P.L[1].qkv_q - P.L[0].qkv_q;
-    const size_t f0[12] = {P.L[0].qkv_q, P.L[0].qkv_s, P.L[0].o_q, P.L[0].o_s, P.L[0].gu_q, P.L[0].gu_s,
-                           P.L[0].dn_q, P.L[0].dn_s, P.L[0].in_g, P.L[0].post_g, P.L[0].qn_g, P.L[0].kn_g};
-    const size_t fl[12] = {P.L[l].qkv_q, P.L[l].qkv_s, P.L[l].o_q, P.L[l].o_s, P.L[l].gu_q, P.L[l].gu_s,
-                           P.L[l].dn_q, P.L[l].dn_s, P.L[l].in_g, P.L[l].post_g, P.L[l].qn_g, P.L[l].kn_g};
-    for (int i = 0; i < 12; ++i)
-      if (fl[i] - f0[i] != (size_t)l * st) add("layers are not laid out at a fixed stride");
-  }
-  const int PTS = 64 * PERSIST_SWAVES;
-  if ((d.NQKV + n - 1) / n > PTS || (d.d + n - 1) / n > PTS || (d.I + n - 1) / n > PTS ||
-      (d.V + n - 1) / n > 4 * PTS)
-    add("more output rows per work-group than staging threads");
-  if (d.d > PERSIST_MAX_D) add("hidden size above 8192");
-  const uint64_t lim = 1ull << 31;
-  if ((uint64_t)d.V * d.d >= lim || 2ull * d.I * d.d >= lim || (uint64_t)d.NQKV * d.d >= lim ||
-      (uint64_t)d.d * d.I >= lim || (uint64_t)m->lim.max_ctx * d.D * 2 >= lim)
-    add("a matrix or cache region of 2 GiB or more");
-  if ((uint64_t)((d.V + n - 1) / n) * persist_ks(d.d) >= 65536) add("too many LM-head units per work-group");
-  const PersistLds L = persist_lds(d.d, d.H, d.KV, d.D, d.I, d.V, n);
-  if ((size_t)L.total > prop.sharedMemPerBlock) add("LDS layout exceeds the per-block limit");
-  if (!p.empty()) return p;
-  int blocks = 0;
-  const hipError_t e = persist_occupancy(d.D, d.G, L.total, &blocks);
-  if (e != hipSuccess || blocks < 1) add("kernel cannot stay resident one work-group per CU");
-  *nwg = n;
-  *lds = L.total;
-  return p;
-}
-
-// reports a barrier time-out of an earlier persistent launch once its flag has arrived
-qd_status persist_check_err(qd_model* m) {
-  if (m->err_pending && hipEventQuery(m->err_ev) == hipSuccess) {
-    m->err_pending = false;
-    if (*m->herr != 0) {
-      *m->herr = 0;
-      (void)hipMemset(m->ws<int>(m->P.perr), 0, 4);
-      return fail(QD_ERR_DEVICE, "persistent decode: a grid barrier wait gave up (results invalid)");
-    }
-  }
-  return QD_OK;
-}
-
-// one cooperative launch of nsteps greedy steps for slot 0, starting at its device position
-qd_status persist_launch(qd_model* m, const int* in_id, int nsteps, int* out_ids, int* next_id,
-                         float* logits, hipStream_t st) {
-  const Dims& d = m->d;
-  const Plan& P = m->P;
-  PersistArgs a{};
-  const LayerOff& o0 = P.L[0];
-  const size_t base = o0.qkv_q;
-  a.lw = m->W + base;
-  a.lstride = d.L > 1 ? (long long)(P.L[1].qkv_q - base) : 0;
-  a.lo = PLayerOff{(int)(o0.qkv_q - base), (int)(o0.qkv_s - base), (int)(o0.o_q - base),
-                   (int)(o0.o_s - base), (int)(o0.gu_q - base), (int)(o0.gu_s - base),
-                   (int)(o0.dn_q - base), (int)(o0.dn_s - base), (int)(o0.in_g - base),
-                   (int)(o0.post_g - base), (int)(o0.qn_g - base), (int)(o0.kn_g - base)};
-  a.kv = reinterpret_cast<bf16_t*>(m->KVb);
-  a.kvstride = (long long)P.kv_layer_elems;
-  a.emb_q = m->w<int8_t>(P.emb_q);
-  a.emb_s = m->w<float>(P.emb_s);
-  a.final_g = m->w<float>(P.final_g);
-  a.rope = m->w<float2>(P.rope);
-  a.d = d.d; a.L = d.L; a.H = d.H; a.KV = d.KV; a.D = d.D; a.I = d.I; a.V = d.V;
-  a.max_ctx = m->lim.max_ctx;
-  a.eps = m->shape.rms_eps;
-  a.xg = m->ws<bf16_t>(P.pxg);
-  a.qkvg = m->ws<bf16_t>(P.pqkv);
-  a.po = m->ws<float>(P.ppo);
-  a.pml = m->ws<float>(P.pml);
-  a.actg = m->ws<bf16_t>(P.pact);
-  a.keys = m->ws<unsigned long long>(P.pkeys);
-  a.bar = m->ws<unsigned>(P.pbar);
-  a.err = m->ws<int>(P.perr);
-  a.in_id = in_id;
-  a.pos = m->ws<int>(P.pos);
-  a.out_ids = out_ids;
-  a.next_id = next_id;
-  a.logits = logits;
-  a.nsteps = nsteps;
-  a.max_splits = m->persist_splits;
-  a.spin_limit = 1u << 22;
-  HIPCHK(launch_decode_persistent(a, m->persist_nwg, m->persist_lds, st));
-  HIPCHK(hipMemcpyAsync(m->herr, a.err, 4, hipMemcpyDeviceToHost, st));
-  HIPCHK(hipEventRecord(m->err_ev, st));
-  m->err_pending = true;
-  return QD_OK;
-}
-
 std::string check_ids(const int32_t* ids, long n, int V) {
   for (long i = 0; i < n; ++i)
     if (ids[i] < 0 || ids[i] >= V)
@@ -859,14 +735,7 @@ qd_status finish_model(qd_model* m, const hipDeviceProp_t& prop, hipStream_t s) 
   HIPCHK(hipHostMalloc((void**)&m->hstage, m->hstage_ints * 4, hipHostMallocDefault));
   HIPCHK(hipEventCreateWithFlags(&m->stage_ev, hipEventDisableTiming));
   for (int i = 0; i < 3; ++i) HIPCHK(hipEventCreate(&m->ev[i]));
-  // persistent single-sequence decode: error flag and eligibility
   HIPCHK(hipStreamSynchronize(s));
-  HIPCHK(hipMemset(m->ws<int>(P.perr), 0, 64));
-  HIPCHK(hipHostMalloc((void**)&m->herr, 64, hipHostMallocDefault));
-  *m->herr = 0;
-  HIPCHK(hipEventCreateWithFlags(&m->err_ev, hipEventDisableTiming));
-  m->persist_why = persist_problems(m, prop, &m->persist_nwg, &m->persist_lds);
-  m->persist_ok = m->persist_why.empty();
   // the fixed scratch of qd_sample_noalloc: its address on this device, looked up once here
   HIPCHK(sample_scratch_address(&m->noalloc_scratch));
   int res4 = 0;  // shapes the decode attention kernel does not take keep the default
@@ -1228,12 +1097,9 @@ qd_status decode_impl(qd_model* m, int32_t B, const int32_t* slots, const int32_
       return fail(QD_ERR_INVALID_ARGUMENTS, "slot " + std::to_string(sl) + " is full (max_ctx)");
     ctx = std::max(ctx, m->host_pos[sl] + 1);
   }
-  QDCHK(persist_check_err(m));
   hipStream_t st = (hipStream_t)stream;
   qd_status s;
-  if (!slots && B == 1 && m->persist_ok && m->persist_on) {
-    s = persist_launch(m, in_ids_dev, 1, nullptr, next_ids_dev, logits_dev, st);
-  } else {
+  {
     const int* row_slot = nullptr;
     if (slots) {
       QDCHK(stage_wait(m));
@@ -1400,7 +1266,6 @@ qd_status qd_generate_greedy(qd_model* m, int32_t B, const int32_t* prompt_ids_h
   if (max_new_tokens < 1) p += "max_new_tokens must be >= 1; ";
   if (!prompt_ids_host || !lens_host || !out_ids_host || !n_out_host) p += "NULL pointer argument; ";
   if (!p.empty()) return fail(QD_ERR_INVALID_ARGUMENTS, p);
-  QDCHK(persist_check_err(m));
   std::vector<int> lens(lens_host, lens_host + B);
   long total = 0;
   int need = 0;
@@ -1436,11 +1301,7 @@ qd_status qd_generate_greedy(qd_model* m, int32_t B, const int32_t* prompt_ids_h
   if (s != QD_OK) return s;
   HIPCHK(hipEventRecord(m->ev[1], st));
   const int steps = max_new_tokens - 1;
-  const bool persist = B == 1 && m->persist_ok && m->persist_on;
-  if (steps > 0 && persist) {
-    // all steps in one cooperative launch; the prefill wrote generated id 0
-    QDCHK(persist_launch(m, next_ids, steps, m->ws<int>(P.out_ids) + 1, next_ids, nullptr, st));
-  } else if (steps > 0) {
+  if (steps > 0) {
     int nsplit, split_len;
     // round the context up so one captured graph serves many calls
     const int ctx_cap = std::min(m->lim.max_ctx, ((need + 255) / 256) * 256);
@@ -1482,7 +1343,6 @@ qd_status qd_generate_greedy(qd_model* m, int32_t B, const int32_t* prompt_ids_h
                           (size_t)m->lim.max_ctx * 4, (size_t)max_new_tokens * 4, B,
                           hipMemcpyDeviceToHost, st));
   HIPCHK(hipStreamSynchronize(st));
-  if (persist && steps > 0) QDCHK(persist_check_err(m));
   for (int b = 0; b < B; ++b) {
     m->host_pos[b] = lens[b] + max_new_tokens - 1;
     int n = max_new_tokens;
@@ -1502,7 +1362,6 @@ qd_status qd_generate_greedy(qd_model* m, int32_t B, const int32_t* prompt_ids_h
     stats->decode_us = t1 * 1e3;
     stats->steps = steps;
     stats->n_prompt_tokens = (int)total;
-    stats->persistent = (persist && steps > 0) ? 1 : 0;
   }
   return QD_OK;
 }
@@ -1620,7 +1479,7 @@ qd_status qd_set_tuning(qd_model* m, int32_t knob, int32_t value) {
   g_err.clear();
   if (!m) return fail(QD_ERR_INVALID_ARGUMENTS, "model is NULL");
   if (value < 0 || (value < 1 && knob != QD_TUNE_ATTN_MERGE_LAST && knob != QD_TUNE_ATTN_WAVES &&
-                    knob != QD_TUNE_PERSISTENT && knob != QD_TUNE_GEMM_SPLITS &&
+                    knob != QD_TUNE_GEMM_SPLITS &&
                     knob != QD_TUNE_ATTN_OCCUPANCY && knob != QD_TUNE_SKINNY_NORM &&
                     knob != QD_TUNE_PREFILL_GEMM && knob != QD_TUNE_SKINNY_XSTAGE &&
                     knob != QD_TUNE_FLASH_ROWS))
@@ -1631,14 +1490,6 @@ qd_status qd_set_tuning(qd_model* m, int32_t knob, int32_t value) {
     case QD_TUNE_ATTN_MERGE_LAST:
       if (value > 1) return fail(QD_ERR_INVALID_ARGUMENTS, "merge mode must be 0 or 1");
       m->attn_merge_last = value;
-      break;
-    case QD_TUNE_PERSISTENT:
-      if (value > 1) return fail(QD_ERR_INVALID_ARGUMENTS, "persistent mode must be 0 or 1");
-      m->persist_on = value;
-      break;
-    case QD_TUNE_PERSIST_SPLITS:
-      if (value > PERSIST_SPLITS) return fail(QD_ERR_INVALID_ARGUMENTS, "at most 32 splits");
-      m->persist_splits = value;
       break;
     case QD_TUNE_SKINNY_NORM:
       if (value > 1) return fail(QD_ERR_INVALID_ARGUMENTS, "skinny norm mode must be 0 or 1");
@@ -1693,11 +1544,6 @@ void qd_free(qd_model* m) {
     (void)hipEventDestroy(m->stage_ev);
   }
   if (m->hstage) (void)hipHostFree(m->hstage);
-  if (m->err_ev) {
-    (void)hipEventSynchronize(m->err_ev);
-    (void)hipEventDestroy(m->err_ev);
-  }
-  if (m->herr) (void)hipHostFree(m->herr);
   delete m;
 }
 

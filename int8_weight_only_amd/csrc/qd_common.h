@@ -124,90 +124,6 @@ constexpr int FLASH_ROWS = 64;
 
 constexpr int LM_MAX_GRID = 1024;  // work-groups of the LM-head GEMV (row blocks looped)
 
-// ---- single-sequence decode as one persistent cooperative launch ---------------------------
-// One work-group per CU runs every phase of every step; phases are separated by a grid
-// barrier, and each phase's weights are requested before the barrier that precedes it.
-constexpr int PERSIST_WAVES = 8;          // waves per work-group
-constexpr int PERSIST_SWAVES = 4;         // staging waves: activations, epilogues, barrier
-constexpr int PERSIST_WWAVES = PERSIST_WAVES - PERSIST_SWAVES;  // weight waves: codes, K/V, dots
-constexpr int PERSIST_SPLITS = 32;        // most position splits per KV head
-constexpr int PERSIST_CHUNK = 16 * PERSIST_WWAVES;  // positions per attention iteration
-constexpr int PERSIST_KSTEP = 1024;       // int8 codes of one row per unit (64 lanes x 16)
-constexpr int PERSIST_BAR_WORDS = 64 * 21;  // barrier words, zero before each launch
-constexpr int PERSIST_MAX_WG = 1024;
-constexpr int PERSIST_MAX_K = 16384;      // longest GEMV input (LDS-staged in bf16)
-constexpr int PERSIST_MAX_D = 8192;       // longest normalized input (4 chunks of 8 per staging thread)
-
-// byte offsets of one layer's tensors from the layer's first byte; layers repeat at a fixed
-// stride in the weight arena, so a layer's pointers are arithmetic, never loaded
-struct PLayerOff {
-  int qkv_q, qkv_s, o_q, o_s, gu_q, gu_s, dn_q, dn_s, in_g, post_g, qn_g, kn_g;
-};
-
-struct PersistArgs {
-  const char* lw;              // layer 0's first byte in the weight arena
-  long long lstride;           // bytes from one layer to the next
-  PLayerOff lo;
-  bf16_t* kv;                  // KV arena: layer l keys at kv + 2 l kvstride, values + kvstride
-  long long kvstride;          // elements of one layer's K (or V) region; slot 0 comes first
-  const int8_t* emb_q; const float* emb_s; const float* final_g;
-  const float2* rope;
-  int d, L, H, KV, D, I, V, max_ctx;
-  float eps;
-  // exchanged between work-groups (agent-coherent stores and loads only)
-  bf16_t* xg;                  // [d] residual stream
-  bf16_t* qkvg;                // [NQKV] raw q|k|v projections
-  float* po;                   // [H][PERSIST_SPLITS][D] unnormalized split outputs
-  float* pml;                  // [H][PERSIST_SPLITS][2] split (max, sum)
-  bf16_t* actg;                // [I] SiLU(gate) * up
-  unsigned long long* keys;    // [grid] per-work-group LM-head arg-max keys
-  unsigned* bar;               // [PERSIST_BAR_WORDS], zero on entry
-  int* err;                    // set to 1 when a barrier wait gives up
-  // inputs and outputs of the launch
-  const int* in_id;            // [1] id fed to the first step
-  int* pos;                    // [1] position of the first step; advanced by nsteps
-  int* out_ids;                // optional: out_ids[i] = id produced by step i
-  int* next_id;                // [1] id produced by the last step
-  float* logits;               // optional [V] fp32 logits of the last step
-  int nsteps;
-  int max_splits;              // most position splits per KV head (<= PERSIST_SPLITS)
-  unsigned spin_limit;         // barrier polls before giving up
-};
-
-// dynamic LDS layout of the persistent kernel (same arithmetic on host and device)
-struct PersistLds {
-  int xs, part, red, rkey, xown, att, mf, flag, total;
-};
-__host__ __device__ inline int persist_ks(int K) { return (K + PERSIST_KSTEP - 1) / PERSIST_KSTEP; }
-__host__ __device__ inline int persist_cdiv(int a, int b) { return (a + b - 1) / b; }
-__host__ __device__ inline PersistLds persist_lds(int d, int H, int KV, int D, int I, int V, int nwg) {
-  const int G = H / KV, HD = H * D, NQKV = HD + 2 * KV * D;
-  const int rq = persist_cdiv(NQKV, nwg), rd = persist_cdiv(d, nwg), rp = persist_cdiv(I, nwg),
-            rv = persist_cdiv(V, nwg);
-  int part = rq * persist_ks(d);
-  part = part > rd * persist_ks(HD) ? part : rd * persist_ks(HD);
-  part = part > 2 * rp * persist_ks(d) ? part : 2 * rp * persist_ks(d);
-  part = part > rd * persist_ks(I) ? part : rd * persist_ks(I);
-  part = part > rv * persist_ks(d) ? part : rv * persist_ks(d);
-  int xs = d > HD ? d : HD;
-  xs = xs > I ? xs : I;
-  xs = (xs + 7) / 8 * 8;
-  const int att = G * D + 2 * D + 2 * PERSIST_WWAVES * G + PERSIST_WWAVES * G * D;
-  PersistLds l;
-  int off = 0;
-  auto take = [&](int bytes) { const int o = off; off += (bytes + 15) / 16 * 16; return o; };
-  l.xs = take(2 * xs);
-  l.part = take(4 * part);
-  l.red = take(4 * PERSIST_WAVES);
-  l.rkey = take(8 * PERSIST_WAVES);
-  l.xown = take(2 * rd);
-  l.att = take(4 * att);
-  l.mf = take(4 * (2 * H * PERSIST_SPLITS + H));
-  l.flag = take(16);
-  l.total = off;
-  return l;
-}
-
 // ---- launchers (qd_kernels.hip) ------------------------------------------------------------
 hipError_t launch_quantize_rows(const float* w, int rows, int cols, int8_t* q, float* s,
                                 int dst_row0, int gu_half, hipStream_t st);
@@ -281,11 +197,5 @@ hipError_t launch_flash_prefill(const FlashArgs& a, int n_tiles, int tile_rows, 
 hipError_t launch_set_positions(int* pos, const int* lens, const int* slots, int n, hipStream_t st);
 hipError_t launch_iota(int* p, int n, hipStream_t st);
 
-// persistent single-sequence decode (qd_persist.hip)
-// blocks per CU the kernel for head_dim D (32, 64, 128) and G = H / KV (<= 8) keeps
-// resident with `lds` bytes of LDS; hipErrorInvalidValue for other shapes
-hipError_t persist_occupancy(int D, int G, int lds, int* blocks_per_cu);
-// clears the barrier words, then launches `nwg` co-resident work-groups
-hipError_t launch_decode_persistent(const PersistArgs& a, int nwg, int lds, hipStream_t st);
 
 }  // namespace qd

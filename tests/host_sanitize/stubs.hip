@@ -26,6 +26,4 @@ hipError_t launch_reset_seq(int*, int*, const int*, int, int, hipStream_t) { QD_
 hipError_t launch_attention_decode(const AttnDecArgs&, hipStream_t) { QD_STUB; }
 hipError_t attention_decode_residency(int, int, int, int*) { QD_STUB; }
 hipError_t launch_flash_prefill(const FlashArgs&, int, int, hipStream_t) { QD_STUB; }
-hipError_t launch_decode_persistent(const PersistArgs&, int, int, hipStream_t) { QD_STUB; }
-hipError_t persist_occupancy(int, int, int, int*) { QD_STUB; }
 }  // namespace qd

@@ -61,17 +61,10 @@ def test_quantization_bit_exact(shape):
         m.close()
 
 
-PERSIST = [1, 0]
-PERSIST_IDS = ["persistent", "per-step"]
-
-
-def _teacher_forced(m, shape, qm, prompt, n_steps, label, config, persist=1, orc=None):
-    """Prefill + n_steps decode steps fed the oracle's ids; check every step.  persist=1:
-    B=1 steps run as the persistent cooperative launch; 0: the per-step kernels."""
+def _teacher_forced(m, shape, qm, prompt, n_steps, label, config, orc=None):
+    """Prefill + n_steps decode steps fed the oracle's ids; check every step."""
     if orc is None:
         orc = Oracle(shape, qm, mode="bf16").generate(prompt, n_steps + 1)
-    m.set_tuning(persistent=persist)
-    label = f"{label} {PERSIST_IDS[1 - persist]}"
     nxt, lg = m.prefill([prompt], logits=True)
     torch.cuda.synchronize()
     errs = [check_step(lg[0].cpu().numpy(), nxt[0].item(), orc["logits"][0], orc["margin"][0],
@@ -88,15 +81,10 @@ def _teacher_forced(m, shape, qm, prompt, n_steps, label, config, persist=1, orc
     return errs
 
 
-@pytest.mark.parametrize("persist", PERSIST, ids=PERSIST_IDS)
-def test_teacher_forced_tiny(tiny_setup, persist):
+def test_teacher_forced_tiny(tiny_setup):
     shape, w, qm, m = tiny_setup
-    say(f"[gpu] teacher-forced tiny, 16-token prompt, 16 steps, persistent={persist}")
-    try:
-        _teacher_forced(m, shape, qm, make_prompt(shape.vocab, 16, 1000), 16, "tiny", "tiny",
-                        persist)
-    finally:
-        m.set_tuning(persistent=0)
+    say("[gpu] teacher-forced tiny, 16-token prompt, 16 steps")
+    _teacher_forced(m, shape, qm, make_prompt(shape.vocab, 16, 1000), 16, "tiny", "tiny")
 
 
 @pytest.mark.parametrize("shape,config", [(WIDE, "wide"), (ODD, "odd")], ids=["wide", "odd"])
@@ -109,23 +97,16 @@ def test_teacher_forced_other_shapes(shape, config):
     m = _model(shape, w, max_batch=2, max_ctx=200, max_prefill_tokens=200)
     try:
         # a prompt longer than one attention chunk, with a ragged tail
-        for persist in PERSIST:
-            _teacher_forced(m, shape, qm, prompt, 12, config, config, persist, orc)
+        _teacher_forced(m, shape, qm, prompt, 12, config, config, orc)
     finally:
         m.close()
 
 
-@pytest.mark.parametrize("persist", PERSIST, ids=PERSIST_IDS)
-def test_generate_greedy_matches_oracle(tiny_setup, persist):
+def test_generate_greedy_matches_oracle(tiny_setup):
     shape, w, qm, m = tiny_setup
     prompt = make_prompt(shape.vocab, 16, 1000)
-    say(f"[gpu] generate_greedy tiny 16+16, persistent={persist}")
-    m.set_tuning(persistent=persist)
-    try:
-        res = m.generate_greedy([prompt], 16)
-    finally:
-        m.set_tuning(persistent=0)
-    assert res.persistent == bool(persist)
+    say("[gpu] generate_greedy tiny 16+16")
+    res = m.generate_greedy([prompt], 16)
     orc = Oracle(shape, qm, mode="bf16").generate(prompt, 16)
     got = res.generated[0]
     # identical up to the first step whose oracle margin is not decisive
@@ -140,27 +121,24 @@ def test_generate_greedy_matches_oracle(tiny_setup, persist):
 
 @pytest.mark.parametrize("shape,config,seed", [(TINY, "tiny", 0), (WIDE, "wide", 1),
                                                (ODD, "odd", 1)], ids=["tiny", "wide", "odd"])
-def test_persistent_generate_matches_per_step(shape, config, seed):
-    """One persistent launch of all steps gives the ids of the per-step kernels wherever the
-    oracle's margin decides them (and the launch reports that it was persistent)."""
+def test_generate_greedy_other_shapes(shape, config, seed):
+    """Graph-replayed generate (24 new tokens: three 8-step graphs) gives the oracle's ids
+    wherever the oracle's margin decides them, at three shapes."""
     w = make_weights(shape, seed=seed, gains="uniform")
     qm = quantize_model(w)
     prompt = make_prompt(shape.vocab, 40, 1020)
-    say(f"[gpu] persistent vs per-step generate {config}, 40+24")
+    say(f"[gpu] generate {config}, 40+24")
     m = _model(shape, w, max_batch=1, max_ctx=128, max_prefill_tokens=64)
     try:
-        m.set_tuning(persistent=1)
         a = m.generate_greedy([prompt], 24)
-        m.set_tuning(persistent=0)
-        b = m.generate_greedy([prompt], 24)
     finally:
         m.close()
-    assert a.persistent and not b.persistent and a.steps == b.steps == 23
+    assert a.steps == 23
     orc = Oracle(shape, qm, mode="bf16").generate(prompt, 24)
     for k in range(24):
         if orc["margin"][k] <= bar_for(config)[1]:
             break
-        assert a.generated[0, k] == b.generated[0, k] == orc["ids"][k], k
+        assert a.generated[0, k] == orc["ids"][k], k
 
 
 def test_generate_repeat_is_deterministic(tiny_setup):
@@ -338,8 +316,7 @@ def test_teacher_forced_mid_split_k():
     say("[gpu] teacher-forced mid (split-K prefill), 200-token prompt")
     m = _model(MID, w, max_batch=2, max_ctx=256, max_prefill_tokens=512)
     try:
-        for persist in PERSIST:
-            _teacher_forced(m, MID, qm, prompt, 7, "mid", "mid", persist, orc)
+        _teacher_forced(m, MID, qm, prompt, 7, "mid", "mid", orc)
     finally:
         m.close()
 
@@ -357,7 +334,7 @@ def test_prefill_attention_tile_rows(rows):
     m = _model(MID, w, max_batch=1, max_ctx=256, max_prefill_tokens=256)
     try:
         m.set_tuning(flash_rows=rows)
-        _teacher_forced(m, MID, qm, prompt, 2, f"mid tiles{rows}", "mid", 0, orc)
+        _teacher_forced(m, MID, qm, prompt, 2, f"mid tiles{rows}", "mid", orc)
     finally:
         m.close()
 
@@ -402,15 +379,15 @@ def test_prefill_qkv_epilogue_rope_head_dim_64(mode):
     m = _model(ROPE64, w, max_batch=1, max_ctx=2064, max_prefill_tokens=2048)
     try:
         m.set_tuning(prefill_gemm=mode)
-        _teacher_forced(m, ROPE64, qm, prompt, 2, "rope64", "rope64", 0, orc)
+        _teacher_forced(m, ROPE64, qm, prompt, 2, "rope64", "rope64", orc)
     finally:
         m.close()
 
 
 def test_teacher_forced_long_context():
     """1500-token prompt: 24 prefill tiles per head; decode attention over many position
-    splits (per-step kernels: ~24 merged splits; persistent: 12 splits of one 128-position
-    chunk, then 2 splits of 6 chunks each to run the multi-chunk loop)."""
+    splits (~24, merged by the last split or by the merge launch), then at most 2 splits
+    (12 chunks each: the multi-chunk loop)."""
     w = make_weights(WIDE, seed=5, gains="uniform")
     qm = quantize_model(w)
     prompt = make_prompt(WIDE.vocab, 1500, 1005)
@@ -418,15 +395,14 @@ def test_teacher_forced_long_context():
     say("[gpu] teacher-forced long context: 1500-token prompt, 23 decode steps")
     m = _model(WIDE, w, max_batch=1, max_ctx=2048, max_prefill_tokens=2048)
     try:
-        for persist in PERSIST:
-            _teacher_forced(m, WIDE, qm, prompt, 23, "wide-long", "wide-long", persist, orc)
-        # per-step kernels with the separate merge launch instead of the in-kernel merge
-        # by the last split (the default)
+        _teacher_forced(m, WIDE, qm, prompt, 23, "wide-long", "wide-long", orc)
+        # the separate merge launch instead of the in-kernel merge by the last split (the
+        # default)
         m.set_tuning(attn_merge_last=0)
-        _teacher_forced(m, WIDE, qm, prompt, 23, "wide-long merge launch", "wide-long", 0, orc)
+        _teacher_forced(m, WIDE, qm, prompt, 23, "wide-long merge launch", "wide-long", orc)
         m.set_tuning(attn_merge_last=1)
-        m.set_tuning(persist_splits=2)
-        _teacher_forced(m, WIDE, qm, prompt, 23, "wide-long 2 splits", "wide-long", 1, orc)
+        m.set_tuning(attn_max_splits=2)
+        _teacher_forced(m, WIDE, qm, prompt, 23, "wide-long 2 splits", "wide-long", orc)
     finally:
         m.close()
 
