@@ -849,34 +849,25 @@ __global__ __launch_bounds__(512) void k_gemm_ks(GemmArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Epilogue of the q|k|v projection's 128x128 tile with the QK-norm, RoPE and K/V cache
-// writes fused in (head dim D = 64 or 128, so no head straddles two tiles).  The tile's
-// projections, rounded to bf16 as the plain store would write them, go to LDS (T, pitch
-// 136 elements, over the stage buffers: every stage read has passed the loop's last
-// barrier); then D/8 lanes take one (row, head): dims 4j..4j+3 and D/2+4j..D/2+4j+3 of lane
-// j, the sum of squares over the head added across those lanes, the RMSNorm with the head's
-// shared gain and the rotate-half rotation at the row's position as k_qk_rope computes
-// them.  q heads are written back to the projection's output, K heads to the K cache at
-// (slot, position) of the row, V heads copied to the V cache.
-__device__ __forceinline__ void gemm_big_rope_epilogue(const GemmArgs& a, bf16_t* T,
-                                                       const f32x4_t (&acc)[4][4], const float (&gsc)[4],
-                                                       int m0, int n0, int wm, int wn) {
-  constexpr int TP = 136;
-  const int tid = threadIdx.x, lane = tid & 63, grp = lane >> 4, r16 = lane & 15;
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        T[(wm * 64 + mt * 16 + 4 * grp + i) * TP + wn * 64 + nt * 16 + r16] = f2bf(acc[mt][nt][i] * gsc[nt]);
-  __syncthreads();
+// Epilogue of a q|k|v projection tile with the QK-norm, RoPE and K/V cache writes fused in
+// (head dim D = 64 or 128, so no head straddles two tiles).  The tile's projections,
+// rounded to bf16 as the plain store would write them, are in LDS (T: BM rows, pitch BN + 8
+// elements, over the stage buffers once every stage read has passed a barrier); then D/8
+// lanes take one (row, head): dims 4j..4j+3 and D/2+4j..D/2+4j+3 of lane j, the sum of
+// squares over the head added across those lanes, the RMSNorm with the head's shared gain
+// and the rotate-half rotation at the row's position as k_qk_rope computes them.  q heads
+// are written back to the projection's output, K heads to the K cache at (slot, position)
+// of the row, V heads copied to the V cache.  NT threads.
+template <int BM, int BN, int NT>
+__device__ __forceinline__ void gemm_rope_tile(const GemmArgs& a, const bf16_t* T, int m0, int n0) {
+  constexpr int TP = BN + 8;
+  const int tid = threadIdx.x;
   const RopeArgs& r = a.rope;
   const int D = r.D, half = D >> 1, L = D >> 3, lgL = __builtin_ctz(L);
-  const int hpt = 128 / D, nheads = r.H + 2 * r.KV;
+  const int hpt = BN / D, nheads = r.H + 2 * r.KV;
 #pragma unroll 1
-  for (int it = 0; it < 8; ++it) {
-    const int idx = it * 256 + tid;
+  for (int it = 0; it < BM * BN / 8 / NT; ++it) {
+    const int idx = it * NT + tid;
     const int gi = idx >> lgL, j = idx & (L - 1);
     const int row = gi / hpt, hl = gi - row * hpt;
     const int m = m0 + row, hh = n0 / D + hl;
@@ -931,6 +922,200 @@ __device__ __forceinline__ void gemm_big_rope_epilogue(const GemmArgs& a, bf16_t
                       : r.kcache + (((size_t)slot * r.KV + (hh - r.H)) * r.max_ctx + p) * D;
     *reinterpret_cast<uint2*>(dst + 4 * j) = make_uint2(o1[0], o1[1]);
     *reinterpret_cast<uint2*>(dst + half + 4 * j) = make_uint2(o2[0], o2[1]);
+  }
+}
+
+// the 128x128-tile kernel's accumulators (4 waves of 64x64) into T, then the epilogue
+__device__ __forceinline__ void gemm_big_rope_epilogue(const GemmArgs& a, bf16_t* T,
+                                                       const f32x4_t (&acc)[4][4], const float (&gsc)[4],
+                                                       int m0, int n0, int wm, int wn) {
+  constexpr int TP = 136;
+  const int lane = threadIdx.x & 63, grp = lane >> 4, r16 = lane & 15;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        T[(wm * 64 + mt * 16 + 4 * grp + i) * TP + wn * 64 + nt * 16 + r16] = f2bf(acc[mt][nt][i] * gsc[nt]);
+  __syncthreads();
+  gemm_rope_tile<128, 128, 256>(a, T, m0, n0);
+}
+
+// Prefill GEMM for the widest projections at many token rows, operands loaded straight
+// into LDS (global_load_lds: lane i of a load writes LDS base + 16 i), so no staging
+// registers are needed and 8 waves (two per SIMD) each hold a 128x64 block of 8x4 MFMA
+// 16x16x32 tiles of the 256x256 output tile: every A fragment read feeds four MFMAs, every
+// W fragment eight.  Three 64-k stages rotate through 144 KB of LDS; a stage's loads are
+// issued two stages ahead.  A rows (128 bytes of a stage) keep their 16-byte chunks XOR-
+// swizzled by row (chunk c at slot c ^ (row % 8)) and W rows (64 int8 bytes) theirs by
+// (row / 2) % 4, so the loads read whole row segments and 8 consecutive lanes of a
+// fragment read hit 8 bank groups.  The weights stay int8 in LDS: a lane reads 16 codes
+// (k 16g .. 16g + 15 of the stage) and converts them for both 32-k halves; the A chunks
+// follow the same k order (half h of lane group g: k 16g + 8h ..).
+constexpr int DL_STAGES = 3;
+// 16 bytes per lane from global memory to LDS at m0 + 16 * lane (m0 = lds_base, uniform
+// over the wave).  Issued from inline assembly so that the compiler does not order later
+// LDS reads behind it: it does not know these writes, and the kernel waits for them itself
+// (the load has no register result; its address registers are read at issue).
+__device__ __forceinline__ void lds_dma16(const void* src, unsigned lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_base)
+               : "memory", "m0");
+}
+template <int EPI>
+__global__ __launch_bounds__(512, 1) void k_gemm_dl(GemmArgs a) {
+  constexpr int BM = 256, BN = 256, BK = 64;
+  constexpr int A_BYTES = BM * BK * 2, W_BYTES = BN * BK;  // 32 KB + 16 KB per stage
+  // stage b: A at b * A_BYTES, W at 3 * A_BYTES + b * W_BYTES; the q|k|v epilogue reuses the
+  // first 256 x 264 bf16 (135 KB) as its tile
+  __shared__ __align__(16) unsigned char lds[DL_STAGES * (A_BYTES + W_BYTES)];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid & 1, wn = wid >> 1;  // 2 x 128 rows, 4 x 64 channels
+  const int grp = lane >> 4, r16 = lane & 15;
+  const int ntn = (a.N + BN - 1) / BN, ntm = (a.M + BM - 1) / BM, ntiles = ntn * ntm;
+  const int q8 = ntiles >> 3, r8 = ntiles & 7, xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
+  const int t = xcd * q8 + min(xcd, r8) + loc;
+  const int m0 = (t / ntn) * BM, n0 = (t % ntn) * BN;
+  const int nsteps = (a.K + BK - 1) / BK;
+  // this lane's loads: A load j (of 4) covers stage rows 8 * (4 * wid + j) .. +8 (1 KB);
+  // lane -> row r = 8 * (4 * wid + j) + lane / 8, LDS slot lane % 8, holding chunk
+  // (lane % 8) ^ (r % 8); W load j (of 2) covers rows 16 * (2 * wid + j) .. +16; lane ->
+  // row 16 * (2 * wid + j) + lane / 4, slot lane % 4, holding chunk (lane % 4) ^ ((r / 2) % 4).
+  // Rows past M (N) read row 0 of the operand (their outputs are never stored); k past K
+  // is never requested (K is a multiple of 64 here).
+  const bf16_t* ag[4];
+  const int8_t* wg[2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = 8 * (4 * wid + j) + (lane >> 3);
+    const int c = (lane & 7) ^ (r & 7);
+    const int m = m0 + r < a.M ? m0 + r : 0;
+    ag[j] = a.A + (size_t)m * a.lda + 8 * c;
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = 16 * (2 * wid + j) + (lane >> 2);
+    const int c = (lane & 3) ^ ((r >> 1) & 3);
+    const int n = n0 + r < a.N ? n0 + r : 0;
+    wg[j] = a.W + (size_t)n * a.K + 16 * c;
+  }
+  // stage buffers by compile-time index
+  auto issue = [&](auto bc, int step) {
+    constexpr int b = decltype(bc)::value;
+    unsigned char* Ad = lds + b * A_BYTES;
+    unsigned char* Wd = lds + DL_STAGES * A_BYTES + b * W_BYTES;
+    const int k0 = step * BK;
+    const unsigned ab = __builtin_amdgcn_readfirstlane((unsigned)(size_t)Ad + 4096u * wid);
+    const unsigned wb = __builtin_amdgcn_readfirstlane((unsigned)(size_t)Wd + 2048u * wid);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) lds_dma16(ag[j] + k0, ab + 1024u * j);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) lds_dma16(wg[j] + k0, wb + 1024u * j);
+  };
+  // fragment reads: A fragment f (rows 16f .. +16), half h: lane (r16, g) reads chunk
+  // 2g + h of row 16f + r16; W fragment f: lane reads chunk g of row 16f + r16
+  f32x4_t acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // one stage: its loads (issued two stages earlier) have landed in every wave once each
+  // wave waited for its own and all passed the barrier; the stage two ahead goes out into
+  // the buffer every wave finished with before this barrier
+  auto stage = [&](auto bc, int st) {
+    constexpr int b = decltype(bc)::value;
+    const unsigned char* Ab = lds + b * A_BYTES;
+    const unsigned char* Wb = lds + DL_STAGES * A_BYTES + b * W_BYTES;
+    // this wave's loads of the stage are done: at most the next stage's 6 are in flight
+    asm volatile("" ::: "memory");
+    if (st + 1 < nsteps) __builtin_amdgcn_s_waitcnt(0x0F76);  // vmcnt <= 6
+    else __builtin_amdgcn_s_waitcnt(0x0F70);                   // vmcnt 0
+    // a bare barrier: __syncthreads would also wait for the next stage's loads; no LDS
+    // access moves across it
+    __builtin_amdgcn_s_barrier();
+    uint4 w16[4];
+    bf16x8_t af[2][8];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int r = 16 * (4 * wn + nt) + r16;
+      w16[nt] = *reinterpret_cast<const uint4*>(Wb + r * 64 + 16 * (grp ^ ((r >> 1) & 3)));
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) {
+        const int r = 16 * (8 * wm + mt) + r16;
+        af[h][mt] = *reinterpret_cast<const bf16x8_t*>(Ab + r * 128 + 16 * ((2 * grp + h) ^ (r & 7)));
+      }
+    if (st + 2 < nsteps) issue(std::integral_constant<int, (b + 2) % DL_STAGES>{}, st + 2);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      bf16x8_t bw[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+        bw[nt] = i8x8_to_bf16x8(h ? make_uint2(w16[nt].z, w16[nt].w) : make_uint2(w16[nt].x, w16[nt].y));
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[h][mt], bw[nt], acc[mt][nt], 0, 0, 0);
+    }
+  };
+  issue(std::integral_constant<int, 0>{}, 0);
+  if (nsteps > 1) issue(std::integral_constant<int, 1>{}, 1);
+#pragma unroll 1
+  for (int st = 0; st < nsteps; st += DL_STAGES) {
+    stage(std::integral_constant<int, 0>{}, st);
+    if (st + 1 < nsteps) stage(std::integral_constant<int, 1>{}, st + 1);
+    if (st + 2 < nsteps) stage(std::integral_constant<int, 2>{}, st + 2);
+  }
+
+  if constexpr (EPI == EPI_STORE) {  // launched for q|k|v with the fused epilogue only
+    {
+      constexpr int TP = BN + 8;
+      bf16_t* T = reinterpret_cast<bf16_t*>(lds);
+      __syncthreads();  // every wave's last stage reads are done
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int n = n0 + wn * 64 + nt * 16 + r16;
+        const float sc = a.scale[n < a.N ? n : 0];
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            T[(wm * 128 + mt * 16 + 4 * grp + i) * TP + wn * 64 + nt * 16 + r16] = f2bf(acc[mt][nt][i] * sc);
+      }
+      __syncthreads();
+      gemm_rope_tile<BM, BN, 512>(a, T, m0, n0);
+      return;
+    }
+  }
+  // lane holds D[4*(lane/16)+i][lane%16] of each 16x16 tile: token rows, channel columns
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int n = n0 + wn * 64 + nt * 16 + r16;
+    const float sc = a.scale[n < a.N ? n : 0];
+    if (EPI == EPI_SILU) {
+      if (nt & 1) continue;
+      const int nu = n + GU_BLOCK;
+      const float su = a.scale[nu < a.N ? nu : 0];
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = m0 + wm * 128 + mt * 16 + 4 * grp + i;
+          if (m < a.M && nu < a.N) gemm_epilogue<EPI_SILU>(a, m, n, acc[mt][nt][i], acc[mt][nt + 1][i], sc, su);
+        }
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = m0 + wm * 128 + mt * 16 + 4 * grp + i;
+          if (m < a.M && n < a.N) gemm_epilogue<EPI>(a, m, n, acc[mt][nt][i], 0.0f, sc, 0.0f);
+        }
+    }
   }
 }
 
@@ -2844,6 +3029,24 @@ hipError_t launch_gemm(const GemmArgs& a0, hipStream_t st, int* splits_used, int
   if ((a.K & 31) || (size_t)(a.M + 64) * a.lda * 2 > 0x7FFFFFFFu || (size_t)(a.N + 64) * a.K > 0x7FFFFFFFu ||
       (size_t)(a.M + 64) * a.ldo * 2 > 0x7FFFFFFFu)
     return hipErrorInvalidValue;
+  // q|k|v and gate/up at many token rows: 256x256 tiles with operands loaded straight into
+  // LDS, when they alone give every CU a tile (K a multiple of 64)
+  const int dl_tiles = ((a.N + 255) / 256) * ((a.M + 255) / 256);
+  // (q|k|v only with its QK-norm / RoPE epilogue, at head dim 128: two heads per tile)
+  const bool dl_qkv = a.epi == EPI_STORE && a.fuse_rope && a.rope.D == 128 &&
+                      a.N == (a.rope.H + 2 * a.rope.KV) * a.rope.D && a.rope.M == a.M;
+  if (dl_tiles >= 256 && a.use_big != 0 && (a.epi == EPI_SILU || dl_qkv) && a.K % 64 == 0 &&
+      a.lda % 8 == 0) {
+    if (splits_used) *splits_used = 1;
+    if (a.epi == EPI_SILU) {
+      a.fuse_rope = 0;
+      hipLaunchKernelGGL(k_gemm_dl<EPI_SILU>, dim3(dl_tiles), dim3(512), 0, st, a);
+    } else {
+      if (rope_done) *rope_done = 1;
+      hipLaunchKernelGGL(k_gemm_dl<EPI_STORE>, dim3(dl_tiles), dim3(512), 0, st, a);
+    }
+    return hipGetLastError();
+  }
   // many token rows: 128x128 tiles when they alone give every CU at least one
   const int big_tiles = ((a.N + 127) / 128) * ((a.M + 127) / 128);
   if (big_tiles >= 256 && a.use_big != 0) {
