@@ -962,15 +962,19 @@ __device__ __forceinline__ void lds_dma16(const void* src, unsigned lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_base)
                : "memory", "m0");
 }
-template <int EPI>
+// WM = 2: 256x256 tiles, waves 2 (rows) x 4 (channels) of 128x64; WM = 4: 256x128 tiles for
+// the narrow projections (O and down), waves 4 x 2 of 64x64.
+template <int EPI, int WM>
 __global__ __launch_bounds__(512, 1) void k_gemm_dl(GemmArgs a) {
-  constexpr int BM = 256, BN = 256, BK = 64;
-  constexpr int A_BYTES = BM * BK * 2, W_BYTES = BN * BK;  // 32 KB + 16 KB per stage
+  constexpr int WN = 8 / WM, MT = 16 / WM;  // waves along channels, 16-row tiles per wave
+  constexpr int BM = 256, BN = 64 * WN, BK = 64;
+  constexpr int A_BYTES = BM * BK * 2, W_BYTES = BN * BK;  // 32 KB + 16 (8) KB per stage
+  constexpr int WL = BN / 128;                             // W loads per wave and stage
   // stage b: A at b * A_BYTES, W at 3 * A_BYTES + b * W_BYTES; the q|k|v epilogue reuses the
   // first 256 x 264 bf16 (135 KB) as its tile
   __shared__ __align__(16) unsigned char lds[DL_STAGES * (A_BYTES + W_BYTES)];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid & 1, wn = wid >> 1;  // 2 x 128 rows, 4 x 64 channels
+  const int wm = wid % WM, wn = wid / WM;
   const int grp = lane >> 4, r16 = lane & 15;
   const int ntn = (a.N + BN - 1) / BN, ntm = (a.M + BM - 1) / BM, ntiles = ntn * ntm;
   const int q8 = ntiles >> 3, r8 = ntiles & 7, xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
@@ -979,12 +983,12 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dl(GemmArgs a) {
   const int nsteps = (a.K + BK - 1) / BK;
   // this lane's loads: A load j (of 4) covers stage rows 8 * (4 * wid + j) .. +8 (1 KB);
   // lane -> row r = 8 * (4 * wid + j) + lane / 8, LDS slot lane % 8, holding chunk
-  // (lane % 8) ^ (r % 8); W load j (of 2) covers rows 16 * (2 * wid + j) .. +16; lane ->
-  // row 16 * (2 * wid + j) + lane / 4, slot lane % 4, holding chunk (lane % 4) ^ ((r / 2) % 4).
+  // (lane % 8) ^ (r % 8); W load j (of WL) covers rows 16 * (WL * wid + j) .. +16; lane ->
+  // row 16 * (WL * wid + j) + lane / 4, slot lane % 4, holding chunk (lane % 4) ^ ((r / 2) % 4).
   // Rows past M (N) read row 0 of the operand (their outputs are never stored); k past K
   // is never requested (K is a multiple of 64 here).
   const bf16_t* ag[4];
-  const int8_t* wg[2];
+  const int8_t* wg[WL];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int r = 8 * (4 * wid + j) + (lane >> 3);
@@ -993,8 +997,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dl(GemmArgs a) {
     ag[j] = a.A + (size_t)m * a.lda + 8 * c;
   }
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int r = 16 * (2 * wid + j) + (lane >> 2);
+  for (int j = 0; j < WL; ++j) {
+    const int r = 16 * (WL * wid + j) + (lane >> 2);
     const int c = (lane & 3) ^ ((r >> 1) & 3);
     const int n = n0 + r < a.N ? n0 + r : 0;
     wg[j] = a.W + (size_t)n * a.K + 16 * c;
@@ -1006,17 +1010,17 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dl(GemmArgs a) {
     unsigned char* Wd = lds + DL_STAGES * A_BYTES + b * W_BYTES;
     const int k0 = step * BK;
     const unsigned ab = __builtin_amdgcn_readfirstlane((unsigned)(size_t)Ad + 4096u * wid);
-    const unsigned wb = __builtin_amdgcn_readfirstlane((unsigned)(size_t)Wd + 2048u * wid);
+    const unsigned wb = __builtin_amdgcn_readfirstlane((unsigned)(size_t)Wd + 1024u * WL * wid);
 #pragma unroll
     for (int j = 0; j < 4; ++j) lds_dma16(ag[j] + k0, ab + 1024u * j);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) lds_dma16(wg[j] + k0, wb + 1024u * j);
+    for (int j = 0; j < WL; ++j) lds_dma16(wg[j] + k0, wb + 1024u * j);
   };
   // fragment reads: A fragment f (rows 16f .. +16), half h: lane (r16, g) reads chunk
   // 2g + h of row 16f + r16; W fragment f: lane reads chunk g of row 16f + r16
-  f32x4_t acc[8][4];
+  f32x4_t acc[MT][4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < MT; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
@@ -1027,15 +1031,15 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dl(GemmArgs a) {
     constexpr int b = decltype(bc)::value;
     const unsigned char* Ab = lds + b * A_BYTES;
     const unsigned char* Wb = lds + DL_STAGES * A_BYTES + b * W_BYTES;
-    // this wave's loads of the stage are done: at most the next stage's 6 are in flight
+    // this wave's loads of the stage are done: at most the next stage's 4 + WL are in flight
     asm volatile("" ::: "memory");
-    if (st + 1 < nsteps) __builtin_amdgcn_s_waitcnt(0x0F76);  // vmcnt <= 6
-    else __builtin_amdgcn_s_waitcnt(0x0F70);                   // vmcnt 0
+    if (st + 1 < nsteps) __builtin_amdgcn_s_waitcnt(0x0F70 | (4 + WL));  // vmcnt <= 4 + WL
+    else __builtin_amdgcn_s_waitcnt(0x0F70);                            // vmcnt 0
     // a bare barrier: __syncthreads would also wait for the next stage's loads; no LDS
     // access moves across it
     __builtin_amdgcn_s_barrier();
     uint4 w16[4];
-    bf16x8_t af[2][8];
+    bf16x8_t af[2][MT];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       const int r = 16 * (4 * wn + nt) + r16;
@@ -1044,8 +1048,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dl(GemmArgs a) {
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt) {
-        const int r = 16 * (8 * wm + mt) + r16;
+      for (int mt = 0; mt < MT; ++mt) {
+        const int r = 16 * (MT * wm + mt) + r16;
         af[h][mt] = *reinterpret_cast<const bf16x8_t*>(Ab + r * 128 + 16 * ((2 * grp + h) ^ (r & 7)));
       }
     if (st + 2 < nsteps) issue(std::integral_constant<int, (b + 2) % DL_STAGES>{}, st + 2);
@@ -1056,7 +1060,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dl(GemmArgs a) {
       for (int nt = 0; nt < 4; ++nt)
         bw[nt] = i8x8_to_bf16x8(h ? make_uint2(w16[nt].z, w16[nt].w) : make_uint2(w16[nt].x, w16[nt].y));
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt)
           acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[h][mt], bw[nt], acc[mt][nt], 0, 0, 0);
@@ -1081,10 +1085,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dl(GemmArgs a) {
         const int n = n0 + wn * 64 + nt * 16 + r16;
         const float sc = a.scale[n < a.N ? n : 0];
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            T[(wm * 128 + mt * 16 + 4 * grp + i) * TP + wn * 64 + nt * 16 + r16] = f2bf(acc[mt][nt][i] * sc);
+            T[(wm * 16 * MT + mt * 16 + 4 * grp + i) * TP + wn * 64 + nt * 16 + r16] = f2bf(acc[mt][nt][i] * sc);
       }
       __syncthreads();
       gemm_rope_tile<BM, BN, 512>(a, T, m0, n0);
@@ -1101,18 +1105,18 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dl(GemmArgs a) {
       const int nu = n + GU_BLOCK;
       const float su = a.scale[nu < a.N ? nu : 0];
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int m = m0 + wm * 128 + mt * 16 + 4 * grp + i;
+          const int m = m0 + wm * 16 * MT + mt * 16 + 4 * grp + i;
           if (m < a.M && nu < a.N) gemm_epilogue<EPI_SILU>(a, m, n, acc[mt][nt][i], acc[mt][nt + 1][i], sc, su);
         }
     } else {
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int m = m0 + wm * 128 + mt * 16 + 4 * grp + i;
+          const int m = m0 + wm * 16 * MT + mt * 16 + 4 * grp + i;
           if (m < a.M && n < a.N) gemm_epilogue<EPI>(a, m, n, acc[mt][nt][i], 0.0f, sc, 0.0f);
         }
     }
@@ -3040,11 +3044,18 @@ hipError_t launch_gemm(const GemmArgs& a0, hipStream_t st, int* splits_used, int
     if (splits_used) *splits_used = 1;
     if (a.epi == EPI_SILU) {
       a.fuse_rope = 0;
-      hipLaunchKernelGGL(k_gemm_dl<EPI_SILU>, dim3(dl_tiles), dim3(512), 0, st, a);
+      hipLaunchKernelGGL((k_gemm_dl<EPI_SILU, 2>), dim3(dl_tiles), dim3(512), 0, st, a);
     } else {
       if (rope_done) *rope_done = 1;
-      hipLaunchKernelGGL(k_gemm_dl<EPI_STORE>, dim3(dl_tiles), dim3(512), 0, st, a);
+      hipLaunchKernelGGL((k_gemm_dl<EPI_STORE, 2>), dim3(dl_tiles), dim3(512), 0, st, a);
     }
+    return hipGetLastError();
+  }
+  // the residual projections (O, down) at many token rows: 256x128 tiles, same loads
+  const int dl_tiles_n = ((a.N + 127) / 128) * ((a.M + 255) / 256);
+  if (dl_tiles_n >= 256 && a.use_big != 0 && a.epi == EPI_RESID && a.K % 64 == 0 && a.lda % 8 == 0) {
+    if (splits_used) *splits_used = 1;
+    hipLaunchKernelGGL((k_gemm_dl<EPI_RESID, 4>), dim3(dl_tiles_n), dim3(512), 0, st, a);
     return hipGetLastError();
   }
   // many token rows: 128x128 tiles when they alone give every CU at least one
