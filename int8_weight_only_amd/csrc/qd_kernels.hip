@@ -1046,13 +1046,16 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dl(GemmArgs a) {
       w16[nt] = *reinterpret_cast<const uint4*>(Wb + r * 64 + 16 * (grp ^ ((r >> 1) & 3)));
     }
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int r = 16 * (MT * wm + mt) + r16;
-        af[h][mt] = *reinterpret_cast<const bf16x8_t*>(Ab + r * 128 + 16 * ((2 * grp + h) ^ (r & 7)));
-      }
+    for (int mt = 0; mt < MT; ++mt) {
+      const int r = 16 * (MT * wm + mt) + r16;
+      af[0][mt] = *reinterpret_cast<const bf16x8_t*>(Ab + r * 128 + 16 * ((2 * grp) ^ (r & 7)));
+    }
     if (st + 2 < nsteps) issue(std::integral_constant<int, (b + 2) % DL_STAGES>{}, st + 2);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int r = 16 * (MT * wm + mt) + r16;
+      af[1][mt] = *reinterpret_cast<const bf16x8_t*>(Ab + r * 128 + 16 * ((2 * grp + 1) ^ (r & 7)));
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       bf16x8_t bw[4];
