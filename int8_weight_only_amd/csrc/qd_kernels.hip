@@ -948,9 +948,9 @@ __device__ __forceinline__ void gemm_big_rope_epilogue(const GemmArgs& a, bf16_t
 // 16x16x32 tiles of the 256x256 output tile: every A fragment read feeds four MFMAs, every
 // W fragment eight.  Three 64-k stages rotate through 144 KB of LDS; a stage's loads are
 // issued two stages ahead.  A rows (128 bytes of a stage) keep their 16-byte chunks XOR-
-// swizzled by row (chunk c at slot c ^ (row % 8)) and W rows (64 int8 bytes) theirs by
-// (row / 2) % 4, so the loads read whole row segments and 8 consecutive lanes of a
-// fragment read hit 8 bank groups.  The weights stay int8 in LDS: a lane reads 16 codes
+// swizzled by row (chunk c at slot c ^ ((row / 2) % 8)) and W rows (64 int8 bytes) theirs
+// by (row / 4) % 4, so the loads read whole row segments and the 16 consecutive lanes of a
+// fragment read (16 rows) hit 16 different 16-byte bank groups of the 64 banks.  The weights stay int8 in LDS: a lane reads 16 codes
 // (k 16g .. 16g + 15 of the stage) and converts them for both 32-k halves; the A chunks
 // follow the same k order (half h of lane group g: k 16g + 8h ..).
 constexpr int DL_STAGES = 3;
@@ -983,8 +983,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dl(GemmArgs a) {
   const int nsteps = (a.K + BK - 1) / BK;
   // this lane's loads: A load j (of 4) covers stage rows 8 * (4 * wid + j) .. +8 (1 KB);
   // lane -> row r = 8 * (4 * wid + j) + lane / 8, LDS slot lane % 8, holding chunk
-  // (lane % 8) ^ (r % 8); W load j (of WL) covers rows 16 * (WL * wid + j) .. +16; lane ->
-  // row 16 * (WL * wid + j) + lane / 4, slot lane % 4, holding chunk (lane % 4) ^ ((r / 2) % 4).
+  // (lane % 8) ^ ((r / 2) % 8); W load j (of WL) covers rows 16 * (WL * wid + j) .. +16;
+  // lane -> row 16 * (WL * wid + j) + lane / 4, slot lane % 4, holding chunk
+  // (lane % 4) ^ ((r / 4) % 4).
   // Rows past M (N) read row 0 of the operand (their outputs are never stored); k past K
   // is never requested (K is a multiple of 64 here).
   const bf16_t* ag[4];
@@ -992,14 +993,14 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dl(GemmArgs a) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int r = 8 * (4 * wid + j) + (lane >> 3);
-    const int c = (lane & 7) ^ (r & 7);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
     const int m = m0 + r < a.M ? m0 + r : 0;
     ag[j] = a.A + (size_t)m * a.lda + 8 * c;
   }
 #pragma unroll
   for (int j = 0; j < WL; ++j) {
     const int r = 16 * (WL * wid + j) + (lane >> 2);
-    const int c = (lane & 3) ^ ((r >> 1) & 3);
+    const int c = (lane & 3) ^ ((r >> 2) & 3);
     const int n = n0 + r < a.N ? n0 + r : 0;
     wg[j] = a.W + (size_t)n * a.K + 16 * c;
   }
@@ -1043,18 +1044,18 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dl(GemmArgs a) {
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       const int r = 16 * (4 * wn + nt) + r16;
-      w16[nt] = *reinterpret_cast<const uint4*>(Wb + r * 64 + 16 * (grp ^ ((r >> 1) & 3)));
+      w16[nt] = *reinterpret_cast<const uint4*>(Wb + r * 64 + 16 * (grp ^ ((r >> 2) & 3)));
     }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int r = 16 * (MT * wm + mt) + r16;
-      af[0][mt] = *reinterpret_cast<const bf16x8_t*>(Ab + r * 128 + 16 * ((2 * grp) ^ (r & 7)));
+      af[0][mt] = *reinterpret_cast<const bf16x8_t*>(Ab + r * 128 + 16 * ((2 * grp) ^ ((r >> 1) & 7)));
     }
     if (st + 2 < nsteps) issue(std::integral_constant<int, (b + 2) % DL_STAGES>{}, st + 2);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int r = 16 * (MT * wm + mt) + r16;
-      af[1][mt] = *reinterpret_cast<const bf16x8_t*>(Ab + r * 128 + 16 * ((2 * grp + 1) ^ (r & 7)));
+      af[1][mt] = *reinterpret_cast<const bf16x8_t*>(Ab + r * 128 + 16 * ((2 * grp + 1) ^ ((r >> 1) & 7)));
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
