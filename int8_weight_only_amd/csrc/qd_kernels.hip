@@ -2673,7 +2673,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 
   };
   // one key block: stage it in LDS, refill the registers with the next block, then
   // S^T = K Q^T, online softmax, O^T += V^T P^T
-  auto block = [&](int kb, uint4 (&ks)[LD_PER_T], uint4 (&vs)[VPT][2]) {
+  // FULL: every key of the block precedes every row of the tile (no causal mask to apply;
+  // rows past the tile's end hold zero queries whose finite results are never stored)
+  auto block = [&](auto full, int kb, uint4 (&ks)[LD_PER_T], uint4 (&vs)[VPT][2]) {
+    constexpr bool FULL = decltype(full)::value;
 #pragma unroll
     for (int u = 0; u < LD_PER_T; ++u) {
       const int idx = tid + 256 * u;
@@ -2736,7 +2739,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int key = kb + 32 * kk + 8 * grp + 4 * t + i;
-            sv[kk][t][i] = (row_ok[rg] && key <= qpos[rg]) ? st[rg][kk][t][i] * scale2 : -INFINITY;
+            sv[kk][t][i] = (FULL || (row_ok[rg] && key <= qpos[rg])) ? st[rg][kk][t][i] * scale2 : -INFINITY;
             smax = fmaxf(smax, sv[kk][t][i]);
           }
       smax = fmaxf(smax, __shfl_xor(smax, 16, 64));
@@ -2757,7 +2760,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 
         for (int t = 0; t < 2; ++t)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float p = (sv[kk][t][i] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sv[kk][t][i] - m[rg]);
+            const float p = (!FULL && sv[kk][t][i] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sv[kk][t][i] - m[rg]);
             l[rg] += p;
             const __bf16 hi = (__bf16)p;
             phi[rg][kk][4 * t + i] = hi;
@@ -2780,7 +2783,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 
     __syncthreads();
   };
   fetch(0, kst, vst);
-  for (int kb = 0; kb < kmax; kb += KB) block(kb, kst, vst);
+  const int kfull = min(kmax, (pos0 + 1) / KB * KB);
+  int kb = 0;
+  for (; kb < kfull; kb += KB) block(std::true_type{}, kb, kst, vst);
+  for (; kb < kmax; kb += KB) block(std::false_type{}, kb, kst, vst);
   // each row sum over its four lanes; out[r][h*D + 16nt + 4grp + i], four dims per store
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg) {
