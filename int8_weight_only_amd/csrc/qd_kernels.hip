@@ -2135,10 +2135,14 @@ __global__ __launch_bounds__(64 * NW) void k_attn_dec(AttnDecArgs a) {
   const bf16_t* vsrc = row + (size_t)(a.H + a.KV + g) * D;
   const int vi = tid < D ? tid : 0;
   const bf16_t vfirst = vsrc[vi];
-  head_load(wid <= G ? wid : G);  // unconditional: waves past the G + 1 heads discard it
-  load_tiles(kc, vc, t_begin);    // unconditional: an empty split reads zeros
-  for (int hh = wid; hh <= G; hh += NW) {
-    if (hh != wid) head_load(hh);
+  // waves past the G + 1 heads redo the key head and drop the result: the first head is
+  // processed by every wave in straight-line code, so its loads stay ahead of the tiles
+  // (behind a branch the compiler would sink them below the tile loads and then wait for
+  // every tile before the first head)
+  const int hh0 = wid <= G ? wid : G;
+  head_load(hh0);
+  load_tiles(kc, vc, t_begin);  // unconditional: an empty split reads zeros
+  auto head_norm_rope = [&](int hh, bool live) {
     const bool isq = hh < G;
     float ss = 0.0f, x1[HJ], x2[HJ];
 #pragma unroll
@@ -2153,11 +2157,14 @@ __global__ __launch_bounds__(64 * NW) void k_attn_dec(AttnDecArgs a) {
 #pragma unroll
     for (int j = 0; j < HJ; ++j) {
       const int i = lane + 64 * j;
+      // every wave stores its head to LDS (the waves past the G + 1 heads write the same key
+      // values as the key head's wave), so nothing here is conditional on the wave and no
+      // input load is sunk into a branch; the cache row is written once
+      const float y1 = rbf(x1[j] * inv * gg1[j]);
+      const float y2 = rbf(x2[j] * inv * gg2[j]);
+      const float2 cs = cs2[j];
+      const bf16_t o1 = f2bf(y1 * cs.x - y2 * cs.y), o2 = f2bf(y2 * cs.x + y1 * cs.y);
       if (i < HALF) {
-        const float y1 = rbf(x1[j] * inv * gg1[j]);
-        const float y2 = rbf(x2[j] * inv * gg2[j]);
-        const float2 cs = cs2[j];
-        const bf16_t o1 = f2bf(y1 * cs.x - y2 * cs.y), o2 = f2bf(y2 * cs.x + y1 * cs.y);
         if (isq) {
           qs[hh][i] = bf2f(o1);
           qs[hh][i + HALF] = bf2f(o2);
@@ -2166,13 +2173,18 @@ __global__ __launch_bounds__(64 * NW) void k_attn_dec(AttnDecArgs a) {
         } else {
           kn[i] = bf2f(o1);
           kn[i + HALF] = bf2f(o2);
-          if (owner) {
+          if (owner && live) {
             Kb[(size_t)p * D + i] = o1;
             Kb[(size_t)p * D + i + HALF] = o2;
           }
         }
       }
     }
+  };
+  head_norm_rope(hh0, wid <= G);
+  for (int hh = wid + NW; hh <= G; hh += NW) {
+    head_load(hh);
+    head_norm_rope(hh, true);
   }
   for (int i = tid; i < D; i += NT) {
     const bf16_t v = i == tid ? vfirst : vsrc[i];
