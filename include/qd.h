@@ -360,10 +360,10 @@ typedef enum {
                                      token rows and, for many rows, QK-norm / RoPE / K/V cache
                                      writes in the q|k|v GEMM's epilogue where the shapes allow;
                                      0: the k-stepped kernel and a separate QK-norm launch */
-  QD_TUNE_SKINNY_XSTAGE = 11,     /* batched decode projections of 2..16 rows (other than those
-                                     with the RMSNorm folded in): 1 (default) load activation
-                                     rows contiguously and reorder them through LDS; 0: load
-                                     them directly in the matrix-core operand layout */
+  QD_TUNE_SKINNY_XSTAGE = 11,     /* batched decode projections of 2..16 rows, and those with
+                                     the RMSNorm folded in at 9..32 rows: 1 (default) load
+                                     activation rows contiguously and reorder them through LDS;
+                                     0: load them directly in the matrix-core operand layout */
   QD_TUNE_FLASH_ROWS = 12,        /* prefill attention query rows per work-group: 64, 128 (head
                                      dim up to 128), or 0 (default: 128 when those tiles give
                                      every CU two work-groups) */

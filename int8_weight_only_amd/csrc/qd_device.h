@@ -35,6 +35,14 @@ __device__ __forceinline__ float wave_sum(float v) {
   v += dpp_f<0x143, 0xc>(0.0f, v);  // row_bcast:31 into rows 2 and 3
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
+// the total of each 16-lane row, in every lane of the row (the first four steps above)
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<0xB1>(0.0f, v);   // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(0.0f, v);   // quad_perm [2,3,0,1]
+  v += dpp_f<0x141>(0.0f, v);  // row_half_mirror
+  v += dpp_f<0x140>(0.0f, v);  // row_mirror
+  return v;
+}
 __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, dpp_f<0xB1>(v, v));
   v = fmaxf(v, dpp_f<0x4E>(v, v));

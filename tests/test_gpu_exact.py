@@ -125,22 +125,37 @@ def test_embedding_rows_bit_exact(exact_model, B):
     np.testing.assert_array_equal(_vals(out), w["embed"][ids].astype(np.float64))
 
 
+# the batched folded-norm kernels load the activation rows contiguously and reorder them
+# in LDS (default, above 8 rows) or load them in the matrix-core operand layout
+XSTAGE = pytest.mark.parametrize("xstage", [1, 0], ids=["row-staged", "operand-loads"])
+
+
+def _run_op_xstage(m, op, x, xstage):
+    m.set_tuning(skinny_xstage=xstage)
+    try:
+        return m.run_op(op, x)
+    finally:
+        m.set_tuning(skinny_xstage=1)
+
+
+@XSTAGE
 @pytest.mark.parametrize("B", BATCHES)
-def test_qkv_projection_bit_exact(exact_model, B):
+def test_qkv_projection_bit_exact(exact_model, B, xstage):
     m, w, _ = exact_model
     L = w["layers"][0]
     x, s = _norm_input(np.random.default_rng(100 + B), B)
     h = s * L["in_norm"].astype(np.float64)                  # RMSNorm(x, gain), exactly
     W = np.concatenate([L["q"], L["k"], L["v"]]).astype(np.float64)
     want = bf16(h @ W.T)
-    got = _vals(m.run_op("qkv", _bf(x)))
+    got = _vals(_run_op_xstage(m, "qkv", _bf(x), xstage))
     assert np.max(np.abs(h @ W.T)) < 2 ** 24
     np.testing.assert_array_equal(got, want, err_msg=f"B={B}")
     say(f"[gpu] exact q|k|v B={B}: {got.size} outputs bit-exact")
 
 
+@XSTAGE
 @pytest.mark.parametrize("B", BATCHES)
-def test_gate_up_silu_bit_exact(exact_model, B):
+def test_gate_up_silu_bit_exact(exact_model, B, xstage):
     m, w, aux = exact_model
     L = w["layers"][0]
     x, s = _norm_input(np.random.default_rng(200 + B), B, sign_prefix=aux["sigma"])
@@ -151,7 +166,7 @@ def test_gate_up_silu_bit_exact(exact_model, B):
     with np.errstate(over="ignore"):
         silu = (g / (np.float32(1) + np.exp(-g))).astype(np.float32)
     want = bf16((silu * u).astype(np.float32))
-    got = _vals(m.run_op("gateup", _bf(x)))
+    got = _vals(_run_op_xstage(m, "gateup", _bf(x), xstage))
     np.testing.assert_array_equal(got, want, err_msg=f"B={B}")
     say(f"[gpu] exact gate/up B={B}: {got.size} outputs bit-exact, "
         f"{int(np.sum(want != 0))} through the identity branch")
