@@ -515,9 +515,13 @@ template <int EPI>
 __global__ __launch_bounds__(512) void k_gemm(GemmArgs a) {
   constexpr int BM = 64, BN = 64, BK = 128, P = GEMM_PF;
   constexpr int OOB = (int)0x80000000;
-  constexpr int LDT = BK + 8;  // LDS row pitch (elements)
-  __shared__ __align__(16) bf16_t As[2][BM][LDT];
-  __shared__ __align__(16) bf16_t Ws[2][BN][LDT];
+  // LDS holds each 16-row x 32-k operand fragment in MFMA lane order (lane l's 8 values in
+  // 16-byte slot l ^ ((l / 16) % 4) of a 1088-byte fragment slot), so a fragment read is
+  // 1 KB of consecutive bytes
+  constexpr int FRAG = 1088;
+  constexpr int NFRAG = (BM / 16) * (BK / 32);  // 16 fragments per operand per stage
+  __shared__ __align__(16) unsigned char Ab[2][NFRAG * FRAG];
+  __shared__ __align__(16) unsigned char Wb[2][NFRAG * FRAG];
   __shared__ int is_last;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int kh = wid >> 2, wm = wid & 1, wn = (wid >> 1) & 1;
@@ -536,10 +540,13 @@ __global__ __launch_bounds__(512) void k_gemm(GemmArgs a) {
   const __amdgpu_buffer_rsrc_t wrsc =
       __builtin_amdgcn_make_buffer_rsrc((void*)a.W, 0, a.N * a.K, 0x00020000);
   // staging: thread j = tid%8 of row tid/8 brings k 16j .. 16j+15 of the step for both A
-  // and W.  Within a step, k = 16j + e sits in LDS column 8j + e (e < 8) or 64 + 8j + e - 8
-  // (e >= 8), the same permutation for both operands, so the dot products are unchanged
-  // and each 8-lane group writes 128 contiguous bytes of a row (no bank conflicts).
-  const int sr = tid >> 3, sj = tid & 7, sa = sj * 8, sw = sj * 16;
+  // and W.  Within a step, k = 16j + e sits in 8-value chunk j (e < 8) or 8 + j (e >= 8),
+  // the same permutation for both operands, so the dot products are unchanged.
+  const int sr = tid >> 3, sj = tid & 7, sw = sj * 16;
+  auto slot = [](int row, int c) {  // byte offset of 8-value chunk c (of 16) of stage row row
+    const int pos = (row & 15) + 16 * (c & 3);
+    return ((row >> 4) * 4 + (c >> 2)) * FRAG + 16 * (pos ^ (c & 3));
+  };
   struct Stage { uint4 a0, a1, w; };
   auto fetch = [&](int step, Stage& q) {
     const int k = kbeg + step * BK;
@@ -551,11 +558,12 @@ __global__ __launch_bounds__(512) void k_gemm(GemmArgs a) {
                                         wrsc, k + sw < kend ? (n0 + sr) * a.K + k + sw : OOB, 0, 0));
   };
   auto stash = [&](const Stage& q, int buf) {
-    *reinterpret_cast<uint4*>(&As[buf][sr][sa]) = q.a0;
-    *reinterpret_cast<uint4*>(&As[buf][sr][64 + sa]) = q.a1;
-    *reinterpret_cast<bf16x8_t*>(&Ws[buf][sr][sa]) = i8x8_to_bf16x8(make_uint2(q.w.x, q.w.y));
-    *reinterpret_cast<bf16x8_t*>(&Ws[buf][sr][64 + sa]) = i8x8_to_bf16x8(make_uint2(q.w.z, q.w.w));
+    *reinterpret_cast<uint4*>(&Ab[buf][slot(sr, sj)]) = q.a0;
+    *reinterpret_cast<uint4*>(&Ab[buf][slot(sr, 8 + sj)]) = q.a1;
+    *reinterpret_cast<bf16x8_t*>(&Wb[buf][slot(sr, sj)]) = i8x8_to_bf16x8(make_uint2(q.w.x, q.w.y));
+    *reinterpret_cast<bf16x8_t*>(&Wb[buf][slot(sr, 8 + sj)]) = i8x8_to_bf16x8(make_uint2(q.w.z, q.w.w));
   };
+  const int rd = 16 * (lane ^ (grp & 3));  // this lane's slot in every fragment read
 
   f32x4_t acc[2][2];
 #pragma unroll
@@ -604,14 +612,14 @@ __global__ __launch_bounds__(512) void k_gemm(GemmArgs a) {
       fetch(i + P, q[u]);  // into the slot step i vacated
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
-        const int kk = kh * 64 + 32 * sub + 8 * grp;
+        const int kf = kh * 2 + sub;  // 32-k fragment of the step
         bf16x8_t af[2], bw[2];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
-          af[mt] = *reinterpret_cast<const bf16x8_t*>(&As[buf][wm * 32 + mt * 16 + r16][kk]);
+          af[mt] = *reinterpret_cast<const bf16x8_t*>(&Ab[buf][((wm * 2 + mt) * 4 + kf) * FRAG + rd]);
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
-          bw[nt] = *reinterpret_cast<const bf16x8_t*>(&Ws[buf][wn * 32 + nt * 16 + r16][kk]);
+          bw[nt] = *reinterpret_cast<const bf16x8_t*>(&Wb[buf][((wn * 2 + nt) * 4 + kf) * FRAG + rd]);
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -624,7 +632,7 @@ __global__ __launch_bounds__(512) void k_gemm(GemmArgs a) {
   }
   // the second k half joins the first through LDS (the staging buffers are free now);
   // waves 0-3 continue with the sum
-  float* red = reinterpret_cast<float*>(&As[0][0][0]);  // [4 waves][16][64] floats
+  float* red = reinterpret_cast<float*>(&Ab[0][0]);  // [4 waves][16][64] floats
   if (kh == 1) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
