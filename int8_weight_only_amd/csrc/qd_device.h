@@ -43,6 +43,25 @@ __device__ __forceinline__ float row16_sum(float v) {
   v += dpp_f<0x140>(0.0f, v);  // row_mirror
   return v;
 }
+// v combined with the value of lane l ^ 16 (row swap) or l ^ 32 (half swap) through the
+// gfx950 lane-swap instructions instead of an LDS permute: swapping a register with itself
+// leaves each lane its own value in one result and its partner's in the other
+__device__ __forceinline__ float xor16_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor16_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, dpp_f<0xB1>(v, v));
   v = fmaxf(v, dpp_f<0x4E>(v, v));

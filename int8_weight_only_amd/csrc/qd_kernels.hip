@@ -1671,8 +1671,7 @@ __global__ __launch_bounds__(64 * SKN_WAVES) void k_skinny_norm(GemvArgs a) {
             ss[tt] += lo * lo + hi * hi;
           }
         }
-      ss[tt] += __shfl_xor(ss[tt], 16, 64);
-      ss[tt] += __shfl_xor(ss[tt], 32, 64);
+      ss[tt] = xor32_sum(xor16_sum(ss[tt]));
       if (grp == 0) sq[wid][tt * 16 + r16] = ss[tt];
     }
   }
@@ -2367,7 +2366,8 @@ __global__ __launch_bounds__(64 * NW) void k_attn_dec(AttnDecArgs a) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[h][e] += __shfl_xor(o[h][e], msk, 64);
+      for (int e = 0; e < 8; ++e)
+        o[h][e] = msk == 16 ? xor16_sum(o[h][e]) : msk == 32 ? xor32_sum(o[h][e]) : o[h][e] + __shfl_xor(o[h][e], msk, 64);
 #pragma unroll
   for (int h = 0; h < G; ++h) l[h] = wave_sum(l[h]);
   if (lane == 0) {
@@ -2800,8 +2800,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 
             sv[kk][t][i] = (FULL || (row_ok[rg] && key <= qpos[rg])) ? st[rg][kk][t][i] * scale2 : -INFINITY;
             smax = fmaxf(smax, sv[kk][t][i]);
           }
-      smax = fmaxf(smax, __shfl_xor(smax, 16, 64));
-      smax = fmaxf(smax, __shfl_xor(smax, 32, 64));
+      smax = xor32_max(xor16_max(smax));
       if (__any(smax > m[rg] + TAU)) {
         const float mnew = fmaxf(m[rg], smax);
         const float alpha = (m[rg] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m[rg] - mnew);
@@ -2849,8 +2848,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg) {
     float lr = l[rg];
-    lr += __shfl_xor(lr, 16, 64);
-    lr += __shfl_xor(lr, 32, 64);
+    lr = xor32_sum(xor16_sum(lr));
     if (!row_ok[rg]) continue;
     bf16_t* orow = a.out + (size_t)(row0 + r[rg]) * a.ldo + (size_t)h * D + 4 * grp;
 #pragma unroll
