@@ -1341,11 +1341,15 @@ constexpr int skinny_batch() { return TT * CTW >= 4 ? 2 : 3; }
 // token lane%16, k 32*(lane/16) + 8q.  Rows are XS_PITCH elements apart in the slot, so the
 // 8 lanes of a fragment read hit 8 different bank groups.
 constexpr int XS_PITCH = 136;
+// The loads are buffer loads whose out-of-range offset reads zero: none sits in a branch,
+// so the compiler's waits count exactly the loads each use needs.
 template <int TT>
 struct XRows {
   int off[TT][4];  // element offset in x of the lane's token row (clamped to a valid row)
   bool ok[TT][4];  // the token is in the batch
+  int wb[2];       // byte offset in W of the lane's weight row of each 16-channel tile, or -1
   bf16_t* slot;    // this wave's LDS slot, TT*16 rows of XS_PITCH elements
+  __amdgpu_buffer_rsrc_t xrs, wrs;  // x (unbounded: offsets are valid or out of range) and W
 };
 template <int TT>
 __device__ __forceinline__ void xrows_init(const GemvArgs& a, bf16_t* slot, XRows<TT>& xr) {
@@ -1360,28 +1364,49 @@ __device__ __forceinline__ void xrows_init(const GemvArgs& a, bf16_t* slot, XRow
       xr.off[tt][q] = (a.x_rows ? a.x_rows[tok] : tok) * a.ldx;
     }
   xr.slot = slot;
+  xr.wb[0] = xr.wb[1] = -1;
+  xr.xrs = __builtin_amdgcn_make_buffer_rsrc((void*)a.x, 0, 0x7FFFFFFF, 0x00020000);
+  xr.wrs = __builtin_amdgcn_make_buffer_rsrc((void*)a.W, 0, a.N * a.K, 0x00020000);
 }
+// the lane's weight rows of channel tile `tile` (CTW 16-channel tiles of it)
 template <int TT, int CTW>
-__device__ __forceinline__ void skinny_load_xs(const int* const (&wrow)[CTW], const bool (&wok)[CTW],
-                                               const bf16_t* x, const XRows<TT>& xr, int K, int kb,
-                                               SkinnyOps<TT, CTW>& o) {
-  const int lane = threadIdx.x & 63, grp = lane >> 4, r16 = lane & 15;
-  const int k0 = kb + 32 * grp;
-  const bool kok = k0 < K;
+__device__ __forceinline__ void xrows_tile(const GemvArgs& a, int tile, XRows<TT>& xr) {
+  const int r16 = threadIdx.x & 15;
 #pragma unroll
   for (int c = 0; c < CTW; ++c) {
-    const uint4* src = reinterpret_cast<const uint4*>(wrow[c] + k0 / 4);
-    o.w[c][0] = (kok && wok[c]) ? src[0] : make_uint4(0, 0, 0, 0);
-    o.w[c][1] = (kok && wok[c]) ? src[1] : make_uint4(0, 0, 0, 0);
+    const int ch = tile * 16 * CTW + c * 16 + r16;
+    xr.wb[c] = ch < a.N ? ch * a.K : -1;
   }
-  const int kx = kb + 8 * r16;
+}
+template <int TT, int CTW>
+__device__ __forceinline__ void skinny_load_xs_x(const XRows<TT>& xr, int K, int kb, SkinnyOps<TT, CTW>& o) {
+  constexpr int OOB = (int)0x80000000;
+  const int kx = kb + 8 * (threadIdx.x & 15);
   const bool xk = kx < K;
 #pragma unroll
   for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      o.x[tt][q] = (xk && xr.ok[tt][q]) ? *reinterpret_cast<const uint4*>(x + xr.off[tt][q] + kx)
-                                        : make_uint4(0, 0, 0, 0);
+      o.x[tt][q] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 xr.xrs, (xk && xr.ok[tt][q]) ? (xr.off[tt][q] + kx) * 2 : OOB, 0, 0));
+}
+template <int TT, int CTW>
+__device__ __forceinline__ void skinny_load_xs_w(const XRows<TT>& xr, int K, int kb, SkinnyOps<TT, CTW>& o) {
+  constexpr int OOB = (int)0x80000000;
+  const int grp = (threadIdx.x & 63) >> 4;
+  const int k0 = kb + 32 * grp;
+  const bool kok = k0 < K;
+#pragma unroll
+  for (int c = 0; c < CTW; ++c) {
+    const int wo = (kok && xr.wb[c] >= 0) ? xr.wb[c] + k0 : OOB;
+    o.w[c][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xr.wrs, wo, 0, 0));
+    o.w[c][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xr.wrs, wo < 0 ? OOB : wo + 16, 0, 0));
+  }
+}
+template <int TT, int CTW>
+__device__ __forceinline__ void skinny_load_xs(const XRows<TT>& xr, int K, int kb, SkinnyOps<TT, CTW>& o) {
+  skinny_load_xs_x<TT, CTW>(xr, K, kb, o);
+  skinny_load_xs_w<TT, CTW>(xr, K, kb, o);
 }
 template <int TT, int CTW>
 __device__ __forceinline__ void skinny_x_transpose(SkinnyOps<TT, CTW>& o, bf16_t* slot) {
@@ -1422,7 +1447,7 @@ __device__ __forceinline__ void skinny_blocks(const int* const (&wrow)[CTW], con
       int ii = ib + u + rot;
       ii = ii >= n ? ii - n : ii;
       const int kb = ib + u < n ? (first + stride * ii) * 128 : K;
-      if constexpr (XS) skinny_load_xs<TT, CTW>(wrow, wok, x, *xr, K, kb, ops[u]);
+      if constexpr (XS) skinny_load_xs<TT, CTW>(*xr, K, kb, ops[u]);
       else skinny_load<TT, CTW>(wrow, wok, xrow, xok, K, kb < K ? kb + 32 * grp : K, ops[u]);
     }
 #pragma unroll
@@ -1494,7 +1519,11 @@ __global__ __launch_bounds__(64 * NWS) void k_skinny(GemvArgs a) {
       const int ch = tile * 16 * CTW + 4 * (l >> 4) + i;
       const bool ok = e < TT * 256 && tok < a.nb;
 #pragma unroll
-      for (int c = 0; c < CTW; ++c) esc[q][c] = (ok && ch + 16 * c < a.N) ? a.scale[ch + 16 * c] : 0.0f;
+      for (int c = 0; c < CTW; ++c) {
+        const bool sok = ok && ch + 16 * c < a.N;
+        const float sv = a.scale[sok ? ch + 16 * c : 0];
+        esc[q][c] = sok ? sv : 0.0f;
+      }
       eres[q] = EPI == EPI_RESID ? a.out[(ok && ch < a.N) ? (size_t)tok * a.ldo + ch : 0] : (bf16_t)0;
     }
     f32x4_t acc[CTW][TT];
@@ -1510,6 +1539,7 @@ __global__ __launch_bounds__(64 * NWS) void k_skinny(GemvArgs a) {
       wok[c] = ch < a.N;
       wrow[c] = reinterpret_cast<const int*>(a.W + (size_t)(wok[c] ? ch : 0) * K);
     }
+    if constexpr (XS) xrows_tile<TT, CTW>(a, tile, xr);
     const int nkb = (K + 127) / 128;
     const int nmine = (nkb - wid + NWS - 1) / NWS;  // this wave's blocks: wid, wid+NWS, ...
     const int rot = nmine > 0 ? tile % nmine : 0;
@@ -1606,14 +1636,36 @@ __global__ __launch_bounds__(64 * SKN_WAVES) void k_skinny_norm(GemvArgs a) {
     wrow[c] = reinterpret_cast<const int*>(a.W + (size_t)(wok[c] ? ch : 0) * K);
   }
   XRows<TT> xr;
-  if constexpr (XS) xrows_init<TT>(a, &xsl[wid][0], xr);
-  // all of this wave's blocks (wid, wid + 8, ...) in one batch
+  if constexpr (XS) {
+    xrows_init<TT>(a, &xsl[wid][0], xr);
+    xrows_tile<TT, CTW>(a, tile, xr);
+  }
+  // all of this wave's blocks (wid, wid + 8, ...) in one batch.  XS: every load of a lane
+  // covers k = 128*kb + 8*r16 .. +8, so the lane's 8 gains of each block are requested
+  // with its activations, before the weights: the RMSNorm then waits for neither the
+  // weights nor an LDS staging of the gains (which would wait for every load in flight)
   SkinnyOps<TT, CTW> ops[NB];
+  float4 gx[XS ? NB : 1][2];
 #pragma unroll
   for (int u = 0; u < NB; ++u) {
     const int kb = wid + NWS * u;
-    if constexpr (XS) skinny_load_xs<TT, CTW>(wrow, wok, a.x, xr, K, kb * 128 < K ? kb * 128 : K, ops[u]);
-    else skinny_load<TT, CTW>(wrow, wok, xrow, xok, K, kb * 128 < K ? kb * 128 + 32 * grp : K, ops[u]);
+    if constexpr (XS) {
+      const int kx = kb * 128 + 8 * r16;
+      const float4* g4 = reinterpret_cast<const float4*>(a.gain + (kx < K ? kx : 0));
+      gx[u][0] = g4[0];
+      gx[u][1] = g4[1];
+      skinny_load_xs_x<TT, CTW>(xr, K, kb * 128 < K ? kb * 128 : K, ops[u]);
+    } else {
+      skinny_load<TT, CTW>(wrow, wok, xrow, xok, K, kb * 128 < K ? kb * 128 + 32 * grp : K, ops[u]);
+    }
+  }
+  if constexpr (XS) {  // every block's weights after every block's activations (loads retire
+                       // in order: the squares would otherwise wait for weights)
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int kb = wid + NWS * u;
+      skinny_load_xs_w<TT, CTW>(xr, K, kb * 128 < K ? kb * 128 : K, ops[u]);
+    }
   }
   // epilogue inputs (residuals as raw bits from a clamped index)
   float esc[NE][CTW];
@@ -1626,12 +1678,17 @@ __global__ __launch_bounds__(64 * SKN_WAVES) void k_skinny_norm(GemvArgs a) {
     const int ch = tile * 16 * CTW + 4 * (l >> 4) + i;
     const bool ok = e < TT * 256 && tok < a.nb;
 #pragma unroll
-    for (int c = 0; c < CTW; ++c) esc[q][c] = (ok && ch + 16 * c < a.N) ? a.scale[ch + 16 * c] : 0.0f;
+    for (int c = 0; c < CTW; ++c) {
+      const bool sok = ok && ch + 16 * c < a.N;
+      const float sv = a.scale[sok ? ch + 16 * c : 0];
+      esc[q][c] = sok ? sv : 0.0f;
+    }
     eres[q] = EPI == EPI_RESID ? a.out[(ok && ch < a.N) ? (size_t)tok * a.ldo + ch : 0] : (bf16_t)0;
   }
   // the gains, staged once per work-group (the LDS store waits for every load above)
-  for (int k = tid * 4; k < K; k += 64 * NWS * 4)
-    *reinterpret_cast<float4*>(&gs[k]) = *reinterpret_cast<const float4*>(a.gain + k);
+  if constexpr (!XS)
+    for (int k = tid * 4; k < K; k += 64 * NWS * 4)
+      *reinterpret_cast<float4*>(&gs[k]) = *reinterpret_cast<const float4*>(a.gain + k);
   if constexpr (XS) {
     // load (tt, q) of a lane holds 8 values of token 16tt + 4q + grp: squares per load,
     // then over the 16 lanes of the group
@@ -1704,11 +1761,11 @@ __global__ __launch_bounds__(64 * SKN_WAVES) void k_skinny_norm(GemvArgs a) {
     const int k0 = XS ? kb + 8 * r16 : kb + 32 * grp;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      // gains from LDS; positions past K hold zero activations
+      // gains (XS: from registers, else from LDS); positions past K hold zero activations
       const int kq = XS ? k0 : k0 + 8 * q;
       const int kg = kq < K ? kq : 0;
-      const float4 g0 = *reinterpret_cast<const float4*>(&gs[kg]);
-      const float4 g1 = *reinterpret_cast<const float4*>(&gs[kg + 4]);
+      const float4 g0 = XS ? gx[XS ? u : 0][0] : *reinterpret_cast<const float4*>(&gs[kg]);
+      const float4 g1 = XS ? gx[XS ? u : 0][1] : *reinterpret_cast<const float4*>(&gs[kg + 4]);
       const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) {
@@ -1782,7 +1839,10 @@ __global__ __launch_bounds__(64 * NWS) void k_skinny_split(GemvArgs a) {
     xrow[tt] = a.x + (size_t)xr * a.ldx;
   }
   XRows<TT> xr;
-  if constexpr (XS) xrows_init<TT>(a, &xsl[wid][0], xr);
+  if constexpr (XS) {
+    xrows_init<TT>(a, &xsl[wid][0], xr);
+    xrows_tile<TT, CTW>(a, tile, xr);
+  }
   const int* wrow[CTW];
   bool wok[CTW];
 #pragma unroll
@@ -1813,7 +1873,11 @@ __global__ __launch_bounds__(64 * NWS) void k_skinny_split(GemvArgs a) {
     const int ch = tile * 16 * CTW + 4 * (l >> 4) + i;
     const bool ok = e < TT * 256 && tok < a.nb;
 #pragma unroll
-    for (int c = 0; c < CTW; ++c) esc[q][c] = (ok && ch + 16 * c < a.N) ? a.scale[ch + 16 * c] : 0.0f;
+    for (int c = 0; c < CTW; ++c) {
+      const bool sok = ok && ch + 16 * c < a.N;
+      const float sv = a.scale[sok ? ch + 16 * c : 0];
+      esc[q][c] = sok ? sv : 0.0f;
+    }
     eres[q] = EPI == EPI_RESID ? a.out[(ok && ch < a.N) ? (size_t)tok * a.ldo + ch : 0] : (bf16_t)0;
   }
 
