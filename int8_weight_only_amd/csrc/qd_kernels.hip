@@ -274,9 +274,10 @@ __global__ void k_lm_finish_step(int* step) { *step += 1; }
 // single-row decode GEMV: y[n] = scale[n] * sum_k x[k] * W[n][k].
 // Every wave keeps the whole activation row in registers (lane l owns the 16-element
 // chunks l, l+64, ...), so the RMSNorm prologue is a wave reduction with no LDS and no
-// block barrier.  The first weight chunks are requested before the activations, so
-// the two memory latencies overlap.  A work-group owns 4*R rows (EPI_SILU: R gate rows
-// and their R up rows per wave) and loops over row blocks when the grid is capped.
+// block barrier.  The activations and gains are requested first and the first weight
+// chunks right after, so the two memory latencies overlap and the norm waits only for its
+// own inputs.  A work-group owns 4*R rows (EPI_SILU: R gate rows and their R up rows per
+// wave) and loops over row blocks when the grid is capped.
 template <int R, int KC, int EPI>
 __global__ __launch_bounds__(256) void k_gemv1(GemvArgs a) {
   constexpr int NR = (EPI == EPI_SILU) ? 2 * R : R;  // weight rows per wave
@@ -296,6 +297,13 @@ __global__ __launch_bounds__(256) void k_gemv1(GemvArgs a) {
   };
 
   int blk = blockIdx.x;
+  // Weights, scales, activations and gains are buffer loads whose out-of-range offset
+  // reads zero, so no load sits in a branch: a load under a per-lane condition becomes an
+  // exec-masked branch, and the compiler then waits for loads at the branch (one such wait
+  // held back every later request until the first weight rows had arrived from HBM).
+  constexpr int OOB = (int)0x80000000;
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc((void*)a.W, 0, a.N * K, 0x00020000);
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc((void*)a.scale, 0, a.N * 4, 0x00020000);
   // per-row scales (and residual values) of a block: requested with its weights, so the
   // epilogue after the reductions does not wait for another round trip
   // The residual values stay raw bf16 bits until the epilogue and are read from a clamped
@@ -307,7 +315,8 @@ __global__ __launch_bounds__(256) void k_gemv1(GemvArgs a) {
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
       const int r = row_of(b, i);
-      sc[i] = (r < a.N && b < nblk) ? a.scale[r] : 0.0f;
+      sc[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                            srs, (r < a.N && b < nblk) ? r * 4 : OOB, 0, 0));
     }
 #pragma unroll
     for (int i = 0; i < R; ++i) {
@@ -315,41 +324,49 @@ __global__ __launch_bounds__(256) void k_gemv1(GemvArgs a) {
       rsb[i] = EPI == EPI_RESID ? a.out[(r < a.N && b < nblk) ? r : 0] : (bf16_t)0;
     }
   };
-  // weights of the first block, requested before the activations
+  // weights of a block (rows r, 16-byte chunks ch of this lane)
   int4 wv[NR][KC];
+  auto load_weights = [&](int b) {
 #pragma unroll
-  for (int i = 0; i < NR; ++i) {
-    const int r = row_of(blk, i);
+    for (int i = 0; i < NR; ++i) {
+      const int r = row_of(b, i);
 #pragma unroll
-    for (int c = 0; c < KC; ++c) {
-      const int ch = lane + 64 * c;
-      wv[i][c] = (r < a.N && ch < nchunk && blk < nblk)
-                     ? *reinterpret_cast<const int4*>(a.W + (size_t)r * K + ch * 16)
-                     : make_int4(0, 0, 0, 0);
+      for (int c = 0; c < KC; ++c) {
+        const int ch = lane + 64 * c;
+        wv[i][c] = __builtin_bit_cast(int4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                wrs, (r < a.N && ch < nchunk && b < nblk) ? r * K + ch * 16 : OOB, 0, 0));
+      }
     }
-  }
-  load_rowdata(blk);
-  // activations (and the RMSNorm prologue) in registers
+  };
+  // the activations and RMSNorm gains go out first, then the first block's weights and row
+  // data: loads retire in order, so the norm waits only for its own inputs while the
+  // weights are still in flight (the scheduling barrier keeps every request ahead of the
+  // first use)
   const bf16_t* xrow = a.x + (size_t)(a.x_rows ? a.x_rows[0] : 0) * a.ldx;
+  const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc((void*)xrow, 0, K * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t grs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.gain, 0, a.gain ? K * 4 : 0, 0x00020000);
   float xf[KC][16];
   float4 gq[KC][4];  // RMSNorm gains of this lane's chunks, requested with the activations
-  float ss = 0.0f;
+  uint4 xu[KC][2];
 #pragma unroll
   for (int c = 0; c < KC; ++c) {
     const int ch = lane + 64 * c;
-    uint4 u0 = make_uint4(0, 0, 0, 0), u1 = u0;
+    const bool cok = ch < nchunk;
+    xu[c][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xrs, cok ? ch * 32 : OOB, 0, 0));
+    xu[c][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xrs, cok ? ch * 32 + 16 : OOB, 0, 0));
 #pragma unroll
-    for (int q = 0; q < 4; ++q) gq[c][q] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (ch < nchunk) {
-      const uint4* xv = reinterpret_cast<const uint4*>(xrow + ch * 16);
-      u0 = xv[0];
-      u1 = xv[1];
-      if (a.gain) {
-        const float4* g4 = reinterpret_cast<const float4*>(a.gain + ch * 16);
+    for (int q = 0; q < 4; ++q)
+      gq[c][q] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                grs, cok ? ch * 64 + 16 * q : OOB, 0, 0));
+  }
+  load_weights(blk);
+  load_rowdata(blk);
+  __builtin_amdgcn_sched_barrier(0);
+  float ss = 0.0f;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) gq[c][q] = g4[q];
-      }
-    }
+  for (int c = 0; c < KC; ++c) {
+    const uint4 u0 = xu[c][0], u1 = xu[c][1];
     const uint32_t w8[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -396,21 +413,10 @@ __global__ __launch_bounds__(256) void k_gemv1(GemvArgs a) {
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
       const int r = row_of(nxt, i);
-      scn[i] = (nxt < nblk && r < a.N) ? a.scale[r] : 0.0f;
+      scn[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                             srs, (nxt < nblk && r < a.N) ? r * 4 : OOB, 0, 0));
     }
-    if (nxt < nblk) {
-#pragma unroll
-      for (int i = 0; i < NR; ++i) {
-        const int r = row_of(nxt, i);
-#pragma unroll
-        for (int c = 0; c < KC; ++c) {
-          const int ch = lane + 64 * c;
-          wv[i][c] = (r < a.N && ch < nchunk)
-                         ? *reinterpret_cast<const int4*>(a.W + (size_t)r * K + ch * 16)
-                         : make_int4(0, 0, 0, 0);
-        }
-      }
-    }
+    if (nxt < nblk) load_weights(nxt);
 #pragma unroll
     for (int i = 0; i < NR; ++i) acc[i] = wave_sum(acc[i]);
     if (lane == 0) {
