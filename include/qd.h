@@ -343,7 +343,10 @@ typedef enum {
   QD_TUNE_ATTN_MAX_SPLITS = 0,    /* most position splits per (sequence, KV head); default 64 */
   QD_TUNE_ATTN_MIN_CHUNKS = 1,    /* fewest 64-position chunks per split; default 1 */
   QD_TUNE_ATTN_WAVES = 2,         /* decode-attention waves per work-group: 4, 8, or 0 = by batch (default) */
-  QD_TUNE_ATTN_MERGE_LAST = 3,    /* 1 (default): the last split merges in-kernel; 0: a merge launch */
+  QD_TUNE_ATTN_MERGE_LAST = 3,    /* 1 (default): the last split merges in-kernel, except that a
+                                     single-row step with 2..8 splits leaves the partials to the
+                                     O projection, which merges them as it loads its input;
+                                     2: the last split always merges; 0: a merge launch */
   /* 4 and 5 are not used (unknown knobs) */
   QD_TUNE_SKINNY_SPLIT = 6,       /* batched decode projections split K over work-groups:
                                      1 never, 2 (default) projections with fewer than 128

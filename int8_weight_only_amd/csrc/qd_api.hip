@@ -372,11 +372,17 @@ int skinny_splits(const qd_model* m, int B, int N, int K, int epi) {
 // gain is set); B >= 2 normalizes into h first and runs the MFMA skinny GEMM
 qd_status dec_proj(qd_model* m, int B, const bf16_t* x, int ldx, const float* gain,
                    const int8_t* W, const float* scale, int N, int K, int epi, bf16_t* out,
-                   int ldo, hipStream_t st) {
+                   int ldo, hipStream_t st, int att_ns = 0) {
   GemvArgs a{};
   a.W = W; a.scale = scale; a.N = N; a.K = K; a.nb = B; a.out = out; a.ldo = ldo;
   if (B == 1) {
     a.x = x; a.ldx = ldx; a.gain = gain; a.eps = m->shape.rms_eps;
+    if (att_ns > 0) {  // the row is merged from the decode attention's split partials
+      a.att_po = m->ws<float>(m->P.part_o);
+      a.att_ml = m->ws<float>(m->P.part_ml);
+      a.att_ns = att_ns;
+      a.att_D = m->d.D;
+    }
     HIPCHK(launch_gemv(a, epi, st));
     return QD_OK;
   }
@@ -421,6 +427,14 @@ int attn_occupancy_for(const qd_model* m, int B, int ctx) {
   return attn_waves_for(m, B, ctx) == 8 ? 1 : m->attn_resident4;
 }
 
+// single-row decode with 2..ATT_DEFER_MAX_SPLITS attention splits: the splits leave their
+// partials and the O projection merges them while it loads its input (QD_TUNE_ATTN_MERGE_LAST
+// 1, the default); the attention's own last-split merge otherwise
+bool attn_defer_merge(const qd_model* m, int B, int nsplit) {
+  return B == 1 && m->attn_merge_last == 1 && nsplit >= 2 && nsplit <= ATT_DEFER_MAX_SPLITS &&
+         m->d.HD <= 64 * 16 * 8;
+}
+
 qd_status dec_attn(qd_model* m, int l, int B, int nsplit, int split_len, int waves, hipStream_t st,
                    const int* row_slot = nullptr) {
   const Dims& d = m->d;
@@ -435,7 +449,7 @@ qd_status dec_attn(qd_model* m, int l, int B, int nsplit, int split_len, int wav
   aa.H = d.H; aa.KV = d.KV; aa.D = d.D; aa.max_ctx = m->lim.max_ctx; aa.B = B;
   aa.split_len = split_len; aa.nsplit = nsplit;
   aa.nwaves = waves;
-  aa.merge_last = m->attn_merge_last;
+  aa.merge_last = attn_defer_merge(m, B, nsplit) ? 2 : (m->attn_merge_last ? 1 : 0);
   aa.part_o = m->ws<float>(m->P.part_o); aa.part_ml = m->ws<float>(m->P.part_ml);
   aa.counters = m->ws<unsigned int>(m->P.att_cnt);
   aa.out = m->ws<bf16_t>(m->P.attn); aa.ldo = d.HD;
@@ -443,11 +457,13 @@ qd_status dec_attn(qd_model* m, int l, int B, int nsplit, int split_len, int wav
   return QD_OK;
 }
 
-qd_status dec_o(qd_model* m, int l, int B, hipStream_t st) {
+// nsplit: the attention's split count when it ran in this step (0: its output is in place)
+qd_status dec_o(qd_model* m, int l, int B, hipStream_t st, int nsplit = 0) {
   const Dims& d = m->d;
   const LayerOff& o = m->P.L[l];
   return dec_proj(m, B, m->ws<bf16_t>(m->P.attn), d.HD, nullptr, m->w<int8_t>(o.o_q),
-                  m->w<float>(o.o_s), d.d, d.HD, EPI_RESID, m->ws<bf16_t>(m->P.x), d.d, st);
+                  m->w<float>(o.o_s), d.d, d.HD, EPI_RESID, m->ws<bf16_t>(m->P.x), d.d, st,
+                  attn_defer_merge(m, B, nsplit) ? nsplit : 0);
 }
 
 qd_status dec_gateup(qd_model* m, int l, int B, hipStream_t st) {
@@ -480,7 +496,7 @@ qd_status enqueue_decode(qd_model* m, int B, const int* in_ids, float* logits, i
   for (int l = 0; l < d.L; ++l) {
     QDCHK(dec_qkv(m, l, B, st));
     QDCHK(dec_attn(m, l, B, nsplit, split_len, waves, st, row_slot));
-    QDCHK(dec_o(m, l, B, st));
+    QDCHK(dec_o(m, l, B, st, nsplit));
     QDCHK(dec_gateup(m, l, B, st));
     QDCHK(dec_down(m, l, B, st));
   }
@@ -1398,7 +1414,7 @@ qd_status qd_profile_kernels(qd_model* m, int32_t B, int32_t iters, float* us_ou
             break;
           case QD_PROF_QKV: QDCHK(dec_qkv(m, i % m->d.L, B, st)); break;
           case QD_PROF_ATTN: QDCHK(dec_attn(m, i % m->d.L, B, nsplit, split_len, waves, st)); break;
-          case QD_PROF_O: QDCHK(dec_o(m, i % m->d.L, B, st)); break;
+          case QD_PROF_O: QDCHK(dec_o(m, i % m->d.L, B, st, nsplit)); break;
           case QD_PROF_GATEUP: QDCHK(dec_gateup(m, i % m->d.L, B, st)); break;
           case QD_PROF_DOWN: QDCHK(dec_down(m, i % m->d.L, B, st)); break;
           default:
@@ -1488,7 +1504,7 @@ qd_status qd_set_tuning(qd_model* m, int32_t knob, int32_t value) {
     case QD_TUNE_ATTN_MAX_SPLITS: m->attn_max_splits = value; break;
     case QD_TUNE_ATTN_MIN_CHUNKS: m->attn_min_chunks = value; break;
     case QD_TUNE_ATTN_MERGE_LAST:
-      if (value > 1) return fail(QD_ERR_INVALID_ARGUMENTS, "merge mode must be 0 or 1");
+      if (value > 2) return fail(QD_ERR_INVALID_ARGUMENTS, "merge mode must be 0, 1 or 2");
       m->attn_merge_last = value;
       break;
     case QD_TUNE_SKINNY_NORM:

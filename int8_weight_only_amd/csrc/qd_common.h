@@ -55,7 +55,12 @@ struct GemvArgs {
   unsigned int* kcnt;                // [tiles] arrival counters, zero on entry, reset by the last
   int no_xstage;                     // skinny, up to 16 rows: 1 = activations loaded straight in
                                      // the MFMA operand layout instead of row-contiguous + LDS
+  // B=1 EPI_RESID with att_ns > 0 (the O projection after a decode attention that left its
+  // att_ns split partials): the activation row is merged from part_o [K/att_D][att_ns][att_D]
+  // and part_ml [K/att_D][att_ns][2] (base-2 maxima and sums) instead of read from x
+  const float* att_po; const float* att_ml; int att_ns; int att_D;
 };
+constexpr int ATT_DEFER_MAX_SPLITS = 8;  // most splits whose merge the O projection takes
 constexpr int SKINNY_MAX_SPLIT = 16;
 constexpr int SKINNY_MAX_TILES = 4096;
 
@@ -104,7 +109,8 @@ struct AttnDecArgs {
   int H, KV, D, max_ctx, B;
   int split_len, nsplit;
   int nwaves;                     // 4 or 8 waves per work-group (8 only when G*D <= 512)
-  int merge_last;                 // 1: the last split merges (agent-coherent partials + counter); 0: merge kernel
+  int merge_last;                 // 1: the last split merges (agent-coherent partials + counter); 0: merge
+                                  // kernel; 2: the partials are left for the next kernel to merge
   float* part_o;                  // [B][H][nsplit][D]
   float* part_ml;                 // [B][H][nsplit][2]
   unsigned int* counters;         // [B][KV], zero on entry; the merging split resets it

@@ -278,7 +278,12 @@ __global__ void k_lm_finish_step(int* step) { *step += 1; }
 // chunks right after, so the two memory latencies overlap and the norm waits only for its
 // own inputs.  A work-group owns 4*R rows (EPI_SILU: R gate rows and their R up rows per
 // wave) and loops over row blocks when the grid is capped.
-template <int R, int KC, int EPI>
+// MERGE (EPI_RESID, the O projection at B = 1): the activation row is the decode
+// attention's output, merged here from the attention's split partials (each thread 8 dims,
+// all splits requested at once) into LDS, which the waves then read instead of x.  This
+// takes the attention kernel's last-split hand-off (store completion, counter, reload)
+// off the step's critical path.
+template <int R, int KC, int EPI, bool MERGE = false>
 __global__ __launch_bounds__(256) void k_gemv1(GemvArgs a) {
   constexpr int NR = (EPI == EPI_SILU) ? 2 * R : R;  // weight rows per wave
   const int K = a.K;
@@ -349,19 +354,93 @@ __global__ __launch_bounds__(256) void k_gemv1(GemvArgs a) {
   float xf[KC][16];
   float4 gq[KC][4];  // RMSNorm gains of this lane's chunks, requested with the activations
   uint4 xu[KC][2];
+  if constexpr (MERGE) {
+    // o = sum_s o_s 2^(m_s - m) / sum_s l_s 2^(m_s - m), m = max_s m_s, per head; splits in
+    // ascending order, as the attention kernel's own merge adds them
+    __shared__ __align__(16) bf16_t xm[64 * 16 * KC];
+    constexpr int SM = ATT_DEFER_MAX_SPLITS;
+    const int ns = a.att_ns, D = a.att_D, nh = K / D;
+    const __amdgpu_buffer_rsrc_t prs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)a.att_po, 0, nh * ns * D * 4, 0x00020000);
+    const __amdgpu_buffer_rsrc_t mrs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)a.att_ml, 0, nh * ns * 2 * 4, 0x00020000);
+    struct MergeIn { float mv[SM], lv[SM]; float4 o0[SM], o1[SM]; };
+    // every split's (max, sum) and 8 output dims of one head (d0 past K: all out of range)
+    auto mload = [&](int d0, MergeIn& in) {
+      const bool ok = d0 < K;
+      const int h = ok ? d0 / D : 0, dd = ok ? d0 - h * D : 0;
 #pragma unroll
-  for (int c = 0; c < KC; ++c) {
-    const int ch = lane + 64 * c;
-    const bool cok = ch < nchunk;
-    xu[c][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xrs, cok ? ch * 32 : OOB, 0, 0));
-    xu[c][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xrs, cok ? ch * 32 + 16 : OOB, 0, 0));
+      for (int s = 0; s < SM; ++s) {
+        const bool sok = ok && s < ns;
+        const int mo = (h * ns + s) * 8, po = ((h * ns + s) * D + dd) * 4;
+        in.mv[s] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(mrs, sok ? mo : OOB, 0, 0));
+        in.lv[s] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(mrs, sok ? mo + 4 : OOB, 0, 0));
+        in.o0[s] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(prs, sok ? po : OOB, 0, 0));
+        in.o1[s] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(prs, sok ? po + 16 : OOB, 0, 0));
+      }
+    };
+    auto mstore = [&](int d0, const MergeIn& in) {
+      float mx = -INFINITY;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      gq[c][q] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                grs, cok ? ch * 64 + 16 * q : OOB, 0, 0));
+      for (int s = 0; s < SM; ++s)
+        if (s < ns) mx = fmaxf(mx, in.mv[s]);
+      float lsum = 0.0f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < SM; ++s) {
+        if (s >= ns || in.mv[s] == -INFINITY) continue;
+        const float w = __builtin_amdgcn_exp2f(in.mv[s] - mx);
+        lsum += in.lv[s] * w;
+        const float ov[8] = {in.o0[s].x, in.o0[s].y, in.o0[s].z, in.o0[s].w,
+                             in.o1[s].x, in.o1[s].y, in.o1[s].z, in.o1[s].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += ov[e] * w;
+      }
+      uint32_t pk[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        pk[e] = (uint32_t)f2bf(acc[2 * e] / lsum) | ((uint32_t)f2bf(acc[2 * e + 1] / lsum) << 16);
+      *reinterpret_cast<uint4*>(&xm[d0]) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    };
+    // the thread's first 8 dims are requested before the weights (they come from L2 and
+    // retire first), the weights and row data right behind them, then the merge
+    {
+      MergeIn in;
+      mload(tid * 8, in);
+      load_weights(blk);
+      load_rowdata(blk);
+      __builtin_amdgcn_sched_barrier(0);
+      if (tid * 8 < K) mstore(tid * 8, in);
+    }
+    for (int d0 = tid * 8 + 256 * 8; d0 < K; d0 += 256 * 8) {  // rows wider than 2048
+      MergeIn in;
+      mload(d0, in);
+      mstore(d0, in);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      const int ch = lane + 64 * c;
+      const bool cok = ch < nchunk;
+      xu[c][0] = cok ? *reinterpret_cast<const uint4*>(&xm[ch * 16]) : make_uint4(0, 0, 0, 0);
+      xu[c][1] = cok ? *reinterpret_cast<const uint4*>(&xm[ch * 16 + 8]) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) gq[c][q] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      const int ch = lane + 64 * c;
+      const bool cok = ch < nchunk;
+      xu[c][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xrs, cok ? ch * 32 : OOB, 0, 0));
+      xu[c][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xrs, cok ? ch * 32 + 16 : OOB, 0, 0));
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        gq[c][q] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  grs, cok ? ch * 64 + 16 * q : OOB, 0, 0));
+    }
+    load_weights(blk);
+    load_rowdata(blk);
   }
-  load_weights(blk);
-  load_rowdata(blk);
   __builtin_amdgcn_sched_barrier(0);
   float ss = 0.0f;
 #pragma unroll
@@ -2472,7 +2551,7 @@ __global__ __launch_bounds__(64 * NW) void k_attn_dec(AttnDecArgs a) {
       a.out[(size_t)b * a.ldo + (size_t)head * D + dd] = f2bf(O / L);
     } else {
       const size_t pi = ((size_t)b * a.H + head) * a.nsplit + s;
-      if (a.merge_last) {  // agent-coherent: the merging split reads them without a fence
+      if (a.merge_last == 1) {  // agent-coherent: the merging split reads them without a fence
         __hip_atomic_store(a.part_o + pi * D + dd, O, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (dd == 0) {
           __hip_atomic_store(a.part_ml + pi * 2, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -2487,7 +2566,7 @@ __global__ __launch_bounds__(64 * NW) void k_attn_dec(AttnDecArgs a) {
       }
     }
   }
-  if (a.nsplit == 1 || !a.merge_last) return;
+  if (a.nsplit == 1 || a.merge_last != 1) return;
   // ---- the last split to finish merges all partials of this (row, KV head) ----
   // Each wave's agent-coherent partial stores have completed (s_waitcnt 0) before thread 0
   // counts the split in; the split that counts last reads every partial with
@@ -3017,7 +3096,16 @@ static hipError_t gemv1_rk(const GemvArgs& a, int epi, hipStream_t st) {
   dim3 grid(epi == EPI_LOGITS ? (nblk < LM_MAX_GRID ? nblk : LM_MAX_GRID) : nblk);
   switch (epi) {
     case EPI_STORE: hipLaunchKernelGGL((k_gemv1<R, KC, EPI_STORE>), grid, dim3(256), 0, st, a); break;
-    case EPI_RESID: hipLaunchKernelGGL((k_gemv1<R, KC, EPI_RESID>), grid, dim3(256), 0, st, a); break;
+    case EPI_RESID:
+      if (a.att_ns > 0) {
+        if (a.att_ns > ATT_DEFER_MAX_SPLITS || a.att_D <= 0 || a.att_D % 8 || a.K % a.att_D || !a.att_po ||
+            !a.att_ml || a.K > 64 * 16 * KC)
+          return hipErrorInvalidValue;
+        hipLaunchKernelGGL((k_gemv1<R, KC, EPI_RESID, true>), grid, dim3(256), 0, st, a);
+      } else {
+        hipLaunchKernelGGL((k_gemv1<R, KC, EPI_RESID>), grid, dim3(256), 0, st, a);
+      }
+      break;
     case EPI_SILU: hipLaunchKernelGGL((k_gemv1<R, KC, EPI_SILU>), grid, dim3(256), 0, st, a); break;
     default: hipLaunchKernelGGL((k_gemv1<R, KC, EPI_LOGITS>), grid, dim3(256), 0, st, a); break;
   }
@@ -3288,7 +3376,7 @@ hipError_t launch_qk_rope(const RopeArgs& a, hipStream_t st) {
 template <int D, int G, int NW>
 static void attn_dec_launch(const AttnDecArgs& a, dim3 grid, hipStream_t st) {
   constexpr int W = (NW == 8 && G * D > 512) ? 4 : NW;
-  if (a.nsplit > 8 && a.merge_last)
+  if (a.nsplit > 8 && a.merge_last == 1)
     hipLaunchKernelGGL((k_attn_dec<D, G, W, true>), grid, dim3(64 * W), 0, st, a);
   else
     hipLaunchKernelGGL((k_attn_dec<D, G, W, false>), grid, dim3(64 * W), 0, st, a);

@@ -407,6 +407,38 @@ def test_teacher_forced_long_context():
         m.close()
 
 
+def test_decode_attention_merge_in_o_projection():
+    """Single-row decode at 250..255 positions (four position splits): by default the O
+    projection merges the attention's split partials as it loads its input; with merge
+    mode 2 the attention's last split merges them.  Both follow the oracle, and since both
+    merges add the splits in the same order with the same arithmetic, their logits are
+    bit-identical."""
+    w = make_weights(MID, seed=7, gains="uniform")
+    qm = quantize_model(w)
+    prompt = make_prompt(MID.vocab, 250, 1007)
+    orc = Oracle(MID, qm, mode="bf16").generate(prompt, 6)
+    say("[gpu] decode attention merged in the O projection vs by the last split")
+    m = _model(MID, w, max_batch=1, max_ctx=320, max_prefill_tokens=320)
+    try:
+        runs = {}
+        for mode in (1, 2):
+            m.set_tuning(attn_merge_last=mode)
+            _teacher_forced(m, MID, qm, prompt, 5, f"mid merge mode {mode}", "mid", orc)
+            nxt, lg = m.prefill([prompt], logits=True)
+            steps = [lg[0].cpu().numpy()]
+            for k in range(1, 6):
+                feed = torch.tensor([orc["ids"][k - 1]], dtype=torch.int32, device="cuda")
+                nxt, lg = m.decode_step(feed, logits=True)
+                steps.append(lg[0].cpu().numpy())
+            torch.cuda.synchronize()
+            runs[mode] = steps
+        for k in range(6):
+            np.testing.assert_array_equal(runs[1][k], runs[2][k], err_msg=f"step {k}")
+    finally:
+        m.set_tuning(attn_merge_last=1)
+        m.close()
+
+
 def test_continuous_batching_slots_teacher_forced():
     """Sequences join and leave a running batch ("LLM inference overview", section
     "Results": continuous batching): prompts are prefilled into free KV slots while other
