@@ -560,9 +560,9 @@ __device__ __forceinline__ bf16x8_t i8x8_to_bf16x8(uint2 w) {
     for (int e = 0; e < 2; ++e) {
       const int v0 = ((int)(in[h] << (24 - 16 * e))) >> 24;
       const int v1 = ((int)(in[h] << (16 - 16 * e))) >> 24;
-      const uint32_t b0 = __float_as_uint((float)v0) >> 16;
-      const uint32_t b1 = __float_as_uint((float)v1) & 0xFFFF0000u;
-      out[h * 2 + e] = b0 | b1;
+      // the upper halves of the two fp32 values (their exact bf16 forms) in one byte
+      // permute: bytes 2, 3 of the first, then bytes 2, 3 of the second
+      out[h * 2 + e] = __builtin_amdgcn_perm(__float_as_uint((float)v1), __float_as_uint((float)v0), 0x07060302u);
     }
   }
   return __builtin_bit_cast(bf16x8_t, make_uint4(out[0], out[1], out[2], out[3]));
@@ -1040,19 +1040,20 @@ __device__ __forceinline__ void gemm_big_rope_epilogue(const GemmArgs& a, bf16_t
 // registers are needed and 8 waves (two per SIMD) each hold a 128x64 block of 8x4 MFMA
 // 16x16x32 tiles of the 256x256 output tile: every A fragment read feeds four MFMAs, every
 // W fragment eight.  Three 64-k stages rotate through 144 KB of LDS; a stage's loads are
-// issued two stages ahead.  A rows (128 bytes of a stage) keep their 16-byte chunks XOR-
+// issued in the middle of the stage three before it.  A rows (128 bytes of a stage) keep their 16-byte chunks XOR-
 // swizzled by row (chunk c at slot c ^ ((row / 2) % 8)) and W rows (64 int8 bytes) theirs
 // by (row / 4) % 4, so the loads read whole row segments and the 16 consecutive lanes of a
 // fragment read (16 rows) hit 16 different 16-byte bank groups of the 64 banks.  The weights stay int8 in LDS: a lane reads 16 codes
 // (k 16g .. 16g + 15 of the stage) and converts them for both 32-k halves; the A chunks
 // follow the same k order (half h of lane group g: k 16g + 8h ..).
 constexpr int DL_STAGES = 3;
-// 16 bytes per lane from global memory to LDS at m0 + 16 * lane (m0 = lds_base, uniform
-// over the wave).  Issued from inline assembly so that the compiler does not order later
-// LDS reads behind it: it does not know these writes, and the kernel waits for them itself
-// (the load has no register result; its address registers are read at issue).
-__device__ __forceinline__ void lds_dma16(const void* src, unsigned lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_base)
+// 16 bytes per lane from global memory (a wave-uniform base address plus this lane's 32-bit
+// byte offset) to LDS at m0 + 16 * lane (m0 = lds_base, uniform over the wave).  Issued from
+// inline assembly so that the compiler does not order later LDS reads behind it: it does not
+// know these writes, and the kernel waits for them itself (the load has no register result;
+// its address registers are read at issue).
+__device__ __forceinline__ void lds_dma16_s(const void* base, unsigned off, unsigned lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds_base)
                : "memory", "m0");
 }
 // WM = 2: 256x256 tiles, waves 2 (rows) x 4 (channels) of 128x64; WM = 4: 256x128 tiles for
@@ -1081,21 +1082,21 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dl(GemmArgs a) {
   // (lane % 4) ^ ((r / 4) % 4).
   // Rows past M (N) read row 0 of the operand (their outputs are never stored); k past K
   // is never requested (K is a multiple of 64 here).
-  const bf16_t* ag[4];
-  const int8_t* wg[WL];
+  // (byte offsets from the operand bases; the launch checks that they fit 31 bits)
+  unsigned ag[4], wg[WL];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int r = 8 * (4 * wid + j) + (lane >> 3);
     const int c = (lane & 7) ^ ((r >> 1) & 7);
     const int m = m0 + r < a.M ? m0 + r : 0;
-    ag[j] = a.A + (size_t)m * a.lda + 8 * c;
+    ag[j] = (unsigned)(m * a.lda + 8 * c) * 2u;
   }
 #pragma unroll
   for (int j = 0; j < WL; ++j) {
     const int r = 16 * (WL * wid + j) + (lane >> 2);
     const int c = (lane & 3) ^ ((r >> 2) & 3);
     const int n = n0 + r < a.N ? n0 + r : 0;
-    wg[j] = a.W + (size_t)n * a.K + 16 * c;
+    wg[j] = (unsigned)(n * a.K + 16 * c);
   }
   // stage buffers by compile-time index
   auto issue = [&](auto bc, int step) {
@@ -1106,9 +1107,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dl(GemmArgs a) {
     const unsigned ab = __builtin_amdgcn_readfirstlane((unsigned)(size_t)Ad + 4096u * wid);
     const unsigned wb = __builtin_amdgcn_readfirstlane((unsigned)(size_t)Wd + 1024u * WL * wid);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) lds_dma16(ag[j] + k0, ab + 1024u * j);
+    for (int j = 0; j < 4; ++j) lds_dma16_s(a.A + k0, ag[j], ab + 1024u * j);
 #pragma unroll
-    for (int j = 0; j < WL; ++j) lds_dma16(wg[j] + k0, wb + 1024u * j);
+    for (int j = 0; j < WL; ++j) lds_dma16_s(a.W + k0, wg[j], wb + 1024u * j);
   };
   // fragment reads: A fragment f (rows 16f .. +16), half h: lane (r16, g) reads chunk
   // 2g + h of row 16f + r16; W fragment f: lane reads chunk g of row 16f + r16
@@ -1118,53 +1119,94 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dl(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // one stage: its loads (issued two stages earlier) have landed in every wave once each
-  // wave waited for its own and all passed the barrier; the stage two ahead goes out into
-  // the buffer every wave finished with before this barrier
-  auto stage = [&](auto bc, int st) {
+  // Software pipeline over the 64-k stages (buffer b = stage % 3).  A stage's W chunks and
+  // first A half are read before its MFMAs start; its second A half is read while the first
+  // half's MFMAs run.  Between the two halves, each wave waits for its own loads of the next
+  // stage, all waves meet at one barrier, the loads of the stage three ahead go out into
+  // the buffer every wave has now finished reading, and the next stage's W chunks and first A
+  // half are read while this stage's second-half MFMAs run.  The LDS reads of one stage thus
+  // overlap the MFMAs of the one before, instead of all waves reading after a barrier while
+  // the matrix cores wait.
+  uint4 w16[4];
+  bf16x8_t a0[MT], a1[MT];
+  constexpr int MH = 0;
+  // the W chunks and the first MH A fragments of the first half (read ahead, during the
+  // previous stage's MFMAs); the other MH at the stage's start
+  auto read_wa0 = [&](auto bc) {
     constexpr int b = decltype(bc)::value;
     const unsigned char* Ab = lds + b * A_BYTES;
     const unsigned char* Wb = lds + DL_STAGES * A_BYTES + b * W_BYTES;
-    // this wave's loads of the stage are done: at most the next stage's 4 + WL are in flight
-    asm volatile("" ::: "memory");
-    if (st + 1 < nsteps) __builtin_amdgcn_s_waitcnt(0x0F70 | (4 + WL));  // vmcnt <= 4 + WL
-    else __builtin_amdgcn_s_waitcnt(0x0F70);                            // vmcnt 0
-    // a bare barrier: __syncthreads would also wait for the next stage's loads; no LDS
-    // access moves across it
-    __builtin_amdgcn_s_barrier();
-    uint4 w16[4];
-    bf16x8_t af[2][MT];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       const int r = 16 * (4 * wn + nt) + r16;
       w16[nt] = *reinterpret_cast<const uint4*>(Wb + r * 64 + 16 * (grp ^ ((r >> 2) & 3)));
     }
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
+    for (int mt = 0; mt < MH; ++mt) {
       const int r = 16 * (MT * wm + mt) + r16;
-      af[0][mt] = *reinterpret_cast<const bf16x8_t*>(Ab + r * 128 + 16 * ((2 * grp) ^ ((r >> 1) & 7)));
+      a0[mt] = *reinterpret_cast<const bf16x8_t*>(Ab + r * 128 + 16 * ((2 * grp) ^ ((r >> 1) & 7)));
     }
-    if (st + 2 < nsteps) issue(std::integral_constant<int, (b + 2) % DL_STAGES>{}, st + 2);
+  };
+  auto read_a0hi = [&](auto bc) {
+    constexpr int b = decltype(bc)::value;
+    const unsigned char* Ab = lds + b * A_BYTES;
+#pragma unroll
+    for (int mt = MH; mt < MT; ++mt) {
+      const int r = 16 * (MT * wm + mt) + r16;
+      a0[mt] = *reinterpret_cast<const bf16x8_t*>(Ab + r * 128 + 16 * ((2 * grp) ^ ((r >> 1) & 7)));
+    }
+  };
+  auto read_a1 = [&](auto bc) {
+    constexpr int b = decltype(bc)::value;
+    const unsigned char* Ab = lds + b * A_BYTES;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int r = 16 * (MT * wm + mt) + r16;
-      af[1][mt] = *reinterpret_cast<const bf16x8_t*>(Ab + r * 128 + 16 * ((2 * grp + 1) ^ ((r >> 1) & 7)));
+      a1[mt] = *reinterpret_cast<const bf16x8_t*>(Ab + r * 128 + 16 * ((2 * grp + 1) ^ ((r >> 1) & 7)));
     }
+  };
+  auto mfma_half = [&](const bf16x8_t (&af)[MT], const bf16x8_t (&bw)[4]) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      bf16x8_t bw[4];
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
-        bw[nt] = i8x8_to_bf16x8(h ? make_uint2(w16[nt].z, w16[nt].w) : make_uint2(w16[nt].x, w16[nt].y));
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt], bw[nt], acc[mt][nt], 0, 0, 0);
+  };
+  constexpr int LPS = 4 + WL;  // loads per wave and stage
+  auto stage = [&](auto bc, int st) {
+    constexpr int b = decltype(bc)::value;
+    read_a0hi(bc);
+    read_a1(bc);
+    bf16x8_t bw[4];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+    for (int nt = 0; nt < 4; ++nt) bw[nt] = i8x8_to_bf16x8(make_uint2(w16[nt].x, w16[nt].y));
+    mfma_half(a0, bw);
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[h][mt], bw[nt], acc[mt][nt], 0, 0, 0);
+    for (int nt = 0; nt < 4; ++nt) bw[nt] = i8x8_to_bf16x8(make_uint2(w16[nt].z, w16[nt].w));
+    if (st + 1 < nsteps) {
+      // this wave's loads of stage st + 1 have landed (only stage st + 2's remain) and its
+      // reads of buffer b are done; after the barrier the same holds for every wave
+      asm volatile("" ::: "memory");
+      if (st + 2 < nsteps) __builtin_amdgcn_s_waitcnt(0x0070 | LPS);  // vmcnt <= LPS, lgkmcnt 0
+      else __builtin_amdgcn_s_waitcnt(0x0070);                        // vmcnt 0, lgkmcnt 0
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (st + 3 < nsteps) issue(bc, st + 3);
+      read_wa0(std::integral_constant<int, (b + 1) % DL_STAGES>{});
     }
+    mfma_half(a1, bw);
   };
   issue(std::integral_constant<int, 0>{}, 0);
   if (nsteps > 1) issue(std::integral_constant<int, 1>{}, 1);
+  if (nsteps > 2) issue(std::integral_constant<int, 2>{}, 2);
+  // stage 0 landed for this wave (stages 1 and 2 may still be in flight), then for all
+  asm volatile("" ::: "memory");
+  if (nsteps > 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * LPS));
+  else if (nsteps > 1) __builtin_amdgcn_s_waitcnt(0x0F70 | LPS);
+  else __builtin_amdgcn_s_waitcnt(0x0F70);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  read_wa0(std::integral_constant<int, 0>{});
 #pragma unroll 1
   for (int st = 0; st < nsteps; st += DL_STAGES) {
     stage(std::integral_constant<int, 0>{}, st);
