@@ -2973,9 +2973,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 
       }
     // causal mask + online softmax.  The row's reference maximum m moves only when the
     // block's maximum exceeds it by more than 2^TAU (so probabilities stay below 2^TAU);
-    // the wave rescales O only then (the result is the same softmax, any reference gives it)
+    // the wave rescales O only then (the result is the same softmax, any reference gives it).
+    // The maximum is taken over the raw scores (the scale is positive, so the scaled maximum
+    // is the maximum scaled), and each weight is 2^(s * scale2 - m) from one fused
+    // multiply-add.
     constexpr float TAU = 8.0f;
-    // P^T fragments (B operand): keys 32kk + 8grp + j, j = 4t + i, in high and low bf16 parts
+    // P^T fragments (B operand): keys 32kk + 8grp + j, j = 4t + i.  p = hi + lo exactly,
+    // hi = p with its low 16 bits cleared (a bf16 value), lo = p - hi rounded to bf16, so the
+    // probabilities enter the product with ~16 significant bits rather than bf16's 8.
     bf16x8_t phi[RG][NKK], plo[RG][NKK];
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
@@ -2988,10 +2993,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int key = kb + 32 * kk + 8 * grp + 4 * t + i;
-            sv[kk][t][i] = (FULL || (row_ok[rg] && key <= qpos[rg])) ? st[rg][kk][t][i] * scale2 : -INFINITY;
+            sv[kk][t][i] = (FULL || (row_ok[rg] && key <= qpos[rg])) ? st[rg][kk][t][i] : -INFINITY;
             smax = fmaxf(smax, sv[kk][t][i]);
           }
-      smax = xor32_max(xor16_max(smax));
+      smax = xor32_max(xor16_max(smax)) * scale2;
       if (__any(smax > m[rg] + TAU)) {
         const float mnew = fmaxf(m[rg], smax);
         const float alpha = (m[rg] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m[rg] - mnew);
@@ -3002,18 +3007,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 
 #pragma unroll
           for (int i = 0; i < 4; ++i) o[rg][nt][i] *= alpha;
       }
+      const float negm = -m[rg];
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk)
+      for (int kk = 0; kk < NKK; ++kk) {
+        uint32_t hw[4], lw[4];
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int j2 = 0; j2 < 4; ++j2) {
+          float pv[2], lo[2];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float p = (!FULL && sv[kk][t][i] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sv[kk][t][i] - m[rg]);
+          for (int e = 0; e < 2; ++e) {
+            const int j = 2 * j2 + e, t = j >> 2, i = j & 3;
+            const float p = (!FULL && sv[kk][t][i] == -INFINITY)
+                                ? 0.0f
+                                : __builtin_amdgcn_exp2f(__builtin_fmaf(sv[kk][t][i], scale2, negm));
             l[rg] += p;
-            const __bf16 hi = (__bf16)p;
-            phi[rg][kk][4 * t + i] = hi;
-            plo[rg][kk][4 * t + i] = (__bf16)(p - (float)hi);
+            pv[e] = p;
+            lo[e] = p - __uint_as_float(__float_as_uint(p) & 0xFFFF0000u);
           }
+          hw[j2] = __builtin_amdgcn_perm(__float_as_uint(pv[1]), __float_as_uint(pv[0]), 0x07060302u);
+          lw[j2] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo[0], lo[1]}, bf16x2_t));
+        }
+        phi[rg][kk] = __builtin_bit_cast(bf16x8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+        plo[rg][kk] = __builtin_bit_cast(bf16x8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+      }
     }
     // O^T += V^T P^T: A = V^T (dims 16nt + r16, keys 32kk + 8grp..), B = P^T
 #pragma unroll
