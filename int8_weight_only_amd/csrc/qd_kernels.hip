@@ -2083,11 +2083,17 @@ __global__ __launch_bounds__(64 * NWS) void k_skinny_split(GemvArgs a) {
 // Batched LM head (vocabulary-sized N): a work-group owns 4 waves x LMT 16-channel tiles
 // and walks K in chunks; each chunk of the activations is staged once in LDS for all
 // 4*LMT tiles (the activations are read from L2 once per work-group instead of once per
-// tile), and every tile's accumulators stay in registers across the chunks.
+// tile), and every tile's accumulators stay in registers across the chunks.  K advances
+// 128 per step; the weights of step s + 1 are requested (branch-free buffer loads, tiles
+// past the vocabulary read zero) before step s is multiplied, so a wave always has the
+// next step's rows in flight instead of waiting out one memory round trip per step.
+// NS > 0: K = 128 NS, the step loop fully unrolled (a loop back edge with loads in flight
+// would make the compiler wait for them to move registers)
 constexpr int LMT = 4;
-template <int TT>
+template <int TT, int NS>
 __global__ __launch_bounds__(256) void k_lm_skinny(GemvArgs a) {
   constexpr int KC = 1024 / TT;                 // k per chunk: LDS = 16*TT rows x KC
+  constexpr int OOB = (int)0x80000000;
   __shared__ __align__(16) bf16_t xs[TT * 16][KC + 8];
   __shared__ unsigned long long wkey[4][TT * 16];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -2099,68 +2105,105 @@ __global__ __launch_bounds__(256) void k_lm_skinny(GemvArgs a) {
   for (int t = 0; t < LMT; ++t)
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) acc[t][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  int tile[LMT];
-  const int8_t* wrow[LMT];
+  int tile[LMT], wofs[LMT];  // this lane's weight row offset, or -1 past the vocabulary
 #pragma unroll
   for (int t = 0; t < LMT; ++t) {
     tile[t] = (blockIdx.x * LMT + t) * 4 + wid;
     const int ch = tile[t] * 16 + r16;
-    wrow[t] = a.W + (size_t)(ch < a.N ? ch : 0) * K;
+    wofs[t] = (tile[t] < ntiles && ch < a.N) ? ch * K : -1;
   }
+  const __amdgpu_buffer_rsrc_t wrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.W, 0, a.N * K, 0x00020000);
+  const int nsteps = NS > 0 ? NS : (K + 127) / 128;
+  // step s: k = 128 s + 32 grp .. + 31 of each of the lane's rows
+  auto wload = [&](int st, uint4 (&wv)[LMT][2]) {
+    const int k = st * 128 + 32 * grp;
+#pragma unroll
+    for (int t = 0; t < LMT; ++t) {
+      const bool ok = wofs[t] >= 0 && k < K && st < nsteps;
+      wv[t][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wrs, ok ? wofs[t] + k : OOB, 0, 0));
+      wv[t][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wrs, ok ? wofs[t] + k + 16 : OOB, 0, 0));
+    }
+  };
+  // activation staging: a chunk is TT*16 rows x KC/8 16-byte pieces, NST per thread
+  // (piece idx = tid + 256 u: row idx / (KC/8), piece idx % (KC/8)); the source rows are
+  // looked up once, and a chunk's pieces are requested together (buffer loads; rows past
+  // the batch and k past K read zero)
+  constexpr int VPR = KC / 8, NST = TT * 16 * VPR / 256;
+  static_assert(TT * 16 * VPR % 256 == 0, "whole staging passes");
+  const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc((void*)a.x, 0, 0x7FFFFFFF, 0x00020000);
+  int xoff[NST];
+#pragma unroll
+  for (int u = 0; u < NST; ++u) {
+    const int r = (tid + 256 * u) / VPR, c = (tid + 256 * u) % VPR;
+    const int rc = r < a.nb ? r : 0;
+    const int xr = a.x_rows ? a.x_rows[rc] : rc;
+    xoff[u] = r < a.nb ? (xr * a.ldx + 8 * c) * 2 : -1;
+  }
+  uint4 wa[LMT][2], wb[LMT][2];
+  wload(0, wa);
   // the scales of this lane's output channels are requested before the k loop
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc((void*)a.scale, 0, a.N * 4, 0x00020000);
   float lsc[LMT][4];
 #pragma unroll
   for (int t = 0; t < LMT; ++t)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int ch = tile[t] * 16 + 4 * grp + i;
-      lsc[t][i] = (tile[t] < ntiles && ch < a.N) ? a.scale[ch] : 0.0f;
+      lsc[t][i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                srs, (tile[t] < ntiles && ch < a.N) ? ch * 4 : OOB, 0, 0));
     }
-  for (int kc = 0; kc < K; kc += KC) {
-    const int klen = min(KC, K - kc);
-    __syncthreads();
-    // stage rows (tokens) x [kc, kc+klen) of the activations, 16 bytes per thread-step
-    const int vpr = klen / 8;
-    for (int idx = tid; idx < TT * 16 * vpr; idx += 256) {
-      const int r = idx / vpr, c = idx % vpr;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (r < a.nb) {
-        const int xr = a.x_rows ? a.x_rows[r] : r;
-        v = *reinterpret_cast<const uint4*>(a.x + (size_t)xr * a.ldx + kc + 8 * c);
+  auto step = [&](int st, const uint4 (&wv)[LMT][2], uint4 (&wn)[LMT][2]) {
+    const int kc = (st * 128) / KC * KC;  // this step's chunk
+    if (st * 128 == kc) {
+      uint4 v[NST];
+#pragma unroll
+      for (int u = 0; u < NST; ++u) {
+        const int c = (tid + 256 * u) % VPR;
+        const bool ok = xoff[u] >= 0 && kc + 8 * c < K;
+        v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xrs, ok ? xoff[u] + kc * 2 : OOB, 0, 0));
       }
-      *reinterpret_cast<uint4*>(&xs[r][8 * c]) = v;
+      __syncthreads();  // every wave is done with the previous chunk
+#pragma unroll
+      for (int u = 0; u < NST; ++u) {
+        const int r = (tid + 256 * u) / VPR, c = (tid + 256 * u) % VPR;
+        *reinterpret_cast<uint4*>(&xs[r][8 * c]) = v[u];
+      }
+      __syncthreads();
     }
-    __syncthreads();
-    for (int kb = 0; kb < klen; kb += 128) {
-      const int k0 = kb + 32 * grp;     // within the chunk
-      const bool kok = k0 < klen;
-      uint4 xv[TT][4];
+    wload(st + 1, wn);  // the next step's rows go out before this step's products
+    const int k0 = st * 128 - kc + 32 * grp;  // within the chunk
+    const bool kok = st * 128 + 32 * grp < K;
+    uint4 xv[TT][4];
 #pragma unroll
-      for (int tt = 0; tt < TT; ++tt)
+    for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          xv[tt][q] = kok ? *reinterpret_cast<const uint4*>(&xs[tt * 16 + r16][k0 + 8 * q])
-                          : make_uint4(0, 0, 0, 0);
+      for (int q = 0; q < 4; ++q)
+        xv[tt][q] = kok ? *reinterpret_cast<const uint4*>(&xs[tt * 16 + r16][k0 + 8 * q]) : make_uint4(0, 0, 0, 0);
 #pragma unroll
-      for (int t = 0; t < LMT; ++t) {
-        if (tile[t] >= ntiles) continue;
-        uint4 wv0 = make_uint4(0, 0, 0, 0), wv1 = wv0;
-        if (kok && tile[t] * 16 + r16 < a.N) {
-          const uint4* src = reinterpret_cast<const uint4*>(wrow[t] + kc + k0);
-          wv0 = src[0];
-          wv1 = src[1];
-        }
+    for (int t = 0; t < LMT; ++t) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint4 w16 = (j >> 1) ? wv1 : wv0;
-          const uint2 w8 = (j & 1) ? make_uint2(w16.z, w16.w) : make_uint2(w16.x, w16.y);
-          const bf16x8_t af = i8x8_to_bf16x8(w8);
+      for (int j = 0; j < 4; ++j) {
+        const uint4 w16 = wv[t][j >> 1];
+        const uint2 w8 = (j & 1) ? make_uint2(w16.z, w16.w) : make_uint2(w16.x, w16.y);
+        const bf16x8_t af = i8x8_to_bf16x8(w8);
 #pragma unroll
-          for (int tt = 0; tt < TT; ++tt)
-            acc[t][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                af, __builtin_bit_cast(bf16x8_t, xv[tt][j]), acc[t][tt], 0, 0, 0);
-        }
+        for (int tt = 0; tt < TT; ++tt)
+          acc[t][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, __builtin_bit_cast(bf16x8_t, xv[tt][j]),
+                                                              acc[t][tt], 0, 0, 0);
       }
+    }
+  };
+  if constexpr (NS > 0) {
+#pragma unroll
+    for (int st = 0; st < NS; st += 2) {
+      step(st, wa, wb);
+      if (st + 1 < NS) step(st + 1, wb, wa);
+    }
+  } else {
+    for (int st = 0; st < nsteps; st += 2) {
+      step(st, wa, wb);
+      if (st + 1 < nsteps) step(st + 1, wb, wa);
     }
   }
   // lane holds channel tile*16 + 4*grp + i, token tt*16 + r16
@@ -3216,8 +3259,10 @@ static hipError_t skinny_tt(const GemvArgs& a, int epi, hipStream_t st) {
     // vocabulary-sized: 4 x LMT wave tiles per work-group, activations staged in LDS
     const int ntiles = (a.N + 15) / 16;
     const int g = (ntiles + 4 * LMT - 1) / (4 * LMT);
-    if (g > LM_MAX_GRID) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_lm_skinny<TT>), dim3(g), dim3(256), 0, st, a);
+    if (g > LM_MAX_GRID || (a.K & 31) || (size_t)a.N * a.K > 0x7FFFFFFFu) return hipErrorInvalidValue;
+    if (a.K == 1024) hipLaunchKernelGGL((k_lm_skinny<TT, 8>), dim3(g), dim3(256), 0, st, a);
+    else if (a.K == 2048) hipLaunchKernelGGL((k_lm_skinny<TT, 16>), dim3(g), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((k_lm_skinny<TT, 0>), dim3(g), dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();
     return e != hipSuccess ? e : lm_finish(a, g, st);
   }
