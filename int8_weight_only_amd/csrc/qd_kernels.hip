@@ -593,6 +593,47 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, int m, int n, f
   }
 }
 
+// Residual epilogue of a BM x BN tile through LDS: T (BM rows, pitch BN + 8) holds the
+// tile's projections rounded to bf16, as the per-element epilogue rounds them; each of the
+// NTH threads then updates 16-byte pieces of the residual rows, x = bf16(x + y), with all of
+// its pieces' residual values requested at once, so the update costs one memory round trip
+// where the per-element read-modify-write (each read waiting for the store before it) costs
+// one per element.  N and ldo are multiples of 8 (the launcher checks).
+template <int BM, int BN, int NTH>
+__device__ __forceinline__ void resid_tile_update(const GemmArgs& a, const bf16_t* T, int m0, int n0) {
+  constexpr int TP = BN + 8, PPR = BN / 8, NP = BM * PPR / NTH;
+  static_assert(BM * PPR % NTH == 0, "whole passes");
+  constexpr int OOB = (int)0x80000000;
+  const int tid = threadIdx.x;
+  const __amdgpu_buffer_rsrc_t ors =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.out, 0, a.M * a.ldo * 2, 0x00020000);
+  uint4 rv[NP];
+  int off[NP];
+#pragma unroll
+  for (int u = 0; u < NP; ++u) {
+    const int idx = tid + NTH * u, row = idx / PPR, pc = idx % PPR;
+    const int m = m0 + row, n = n0 + 8 * pc;
+    off[u] = (m < a.M && n < a.N) ? (m * a.ldo + n) * 2 : OOB;
+    rv[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ors, off[u], 0, 0));
+  }
+#pragma unroll
+  for (int u = 0; u < NP; ++u) {
+    const int idx = tid + NTH * u, row = idx / PPR, pc = idx % PPR;
+    const uint4 y = *reinterpret_cast<const uint4*>(&T[row * TP + 8 * pc]);
+    const uint32_t xw[4] = {rv[u].x, rv[u].y, rv[u].z, rv[u].w}, yw[4] = {y.x, y.y, y.z, y.w};
+    uint32_t ow[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float lo = __uint_as_float(xw[e] << 16) + __uint_as_float(yw[e] << 16);
+      const float hi = __uint_as_float(xw[e] & 0xFFFF0000u) + __uint_as_float(yw[e] & 0xFFFF0000u);
+      ow[e] = (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+    }
+    if (off[u] != OOB)
+      *reinterpret_cast<uint4*>(a.out + (size_t)(m0 + row) * a.ldo + n0 + 8 * pc) =
+          make_uint4(ow[0], ow[1], ow[2], ow[3]);
+  }
+}
+
 constexpr int GEMM_PF = 4;  // k-steps of loads in flight
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
@@ -1234,6 +1275,25 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dl(GemmArgs a) {
       return;
     }
   }
+  if constexpr (EPI == EPI_RESID) {
+    constexpr int TP = BN + 8;
+    static_assert(BM * TP * 2 <= sizeof(lds), "the tile fits the stage buffers");
+    bf16_t* T = reinterpret_cast<bf16_t*>(lds);
+    __syncthreads();  // every wave's last stage reads are done
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int n = n0 + wn * 64 + nt * 16 + r16;
+      const float sc = a.scale[n < a.N ? n : 0];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          T[(wm * 16 * MT + mt * 16 + 4 * grp + i) * TP + wn * 64 + nt * 16 + r16] = f2bf(acc[mt][nt][i] * sc);
+    }
+    __syncthreads();
+    resid_tile_update<BM, BN, 512>(a, T, m0, n0);
+    return;
+  }
   // lane holds D[4*(lane/16)+i][lane%16] of each 16x16 tile: token rows, channel columns
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
@@ -1380,6 +1440,22 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(GemmArgs a) {
       gemm_big_rope_epilogue(a, reinterpret_cast<bf16_t*>(&Ab[0][0]), acc, gsc, m0, n0, wm, wn);
       return;
     }
+  }
+  if constexpr (EPI == EPI_RESID) {
+    constexpr int TP = BN + 8;  // 128 x 136 bf16: exactly the A stage buffers
+    static_assert(BM * TP * 2 <= sizeof(Ab), "the tile fits the A stage buffers");
+    bf16_t* T = reinterpret_cast<bf16_t*>(&Ab[0][0]);
+    __syncthreads();
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          T[(wm * 64 + mt * 16 + 4 * grp + i) * TP + wn * 64 + nt * 16 + r16] = f2bf(acc[mt][nt][i] * gsc[nt]);
+    __syncthreads();
+    resid_tile_update<BM, BN, 256>(a, T, m0, n0);
+    return;
   }
   // lane holds D[4*(lane/16)+i][lane%16] of each 16x16 tile: token rows, channel columns
 #pragma unroll
@@ -3387,14 +3463,16 @@ hipError_t launch_gemm(const GemmArgs& a0, hipStream_t st, int* splits_used, int
   }
   // the residual projections (O, down) at many token rows: 256x128 tiles, same loads
   const int dl_tiles_n = ((a.N + 127) / 128) * ((a.M + 255) / 256);
-  if (dl_tiles_n >= 256 && a.use_big != 0 && a.epi == EPI_RESID && a.K % 64 == 0 && a.lda % 8 == 0) {
+  const bool resid_pieces = a.N % 8 == 0 && a.ldo % 8 == 0;  // 16-byte residual updates
+  if (dl_tiles_n >= 256 && a.use_big != 0 && a.epi == EPI_RESID && a.K % 64 == 0 && a.lda % 8 == 0 &&
+      resid_pieces) {
     if (splits_used) *splits_used = 1;
     hipLaunchKernelGGL((k_gemm_dl<EPI_RESID, 4>), dim3(dl_tiles_n), dim3(512), 0, st, a);
     return hipGetLastError();
   }
   // many token rows: 128x128 tiles when they alone give every CU at least one
   const int big_tiles = ((a.N + 127) / 128) * ((a.M + 127) / 128);
-  if (big_tiles >= 256 && a.use_big != 0) {
+  if (big_tiles >= 256 && a.use_big != 0 && (a.epi != EPI_RESID || resid_pieces)) {
     if (splits_used) *splits_used = 1;
     const RopeArgs& r = a.rope;
     a.fuse_rope = a.fuse_rope && a.epi == EPI_STORE && (r.D == 64 || r.D == 128) &&
