@@ -1275,6 +1275,44 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dl(GemmArgs a) {
       return;
     }
   }
+  if constexpr (EPI == EPI_SILU) {
+    // gate/up: the tile's BN/2 outputs (columns n0/2 ..) go through LDS as bf16, then out as
+    // whole 16-byte pieces of rows; the scales are requested once, before any store (a load
+    // after stores waits for them, so per-column-block scale loads serialized the stores)
+    constexpr int TP = BN / 2 + 8, PPR = BN / 16, NP = BM * PPR / 512;
+    static_assert(BM * TP * 2 <= sizeof(lds) && BM * PPR % 512 == 0, "tile and passes");
+    bf16_t* T = reinterpret_cast<bf16_t*>(lds);
+    float sg[2], su[2];
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr) {
+      const int n = n0 + wn * 64 + pr * 32 + r16;  // gate row; its up row is n + GU_BLOCK
+      sg[pr] = a.scale[n < a.N ? n : 0];
+      su[pr] = a.scale[n + GU_BLOCK < a.N ? n + GU_BLOCK : 0];
+    }
+    __syncthreads();  // every wave's last stage reads are done
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float g = rbf(acc[mt][2 * pr][i] * sg[pr]);
+          const float u = rbf(acc[mt][2 * pr + 1][i] * su[pr]);
+          T[(wm * 16 * MT + mt * 16 + 4 * grp + i) * TP + wn * 32 + pr * 16 + r16] =
+              f2bf(g / (1.0f + expf(-g)) * u);
+        }
+    __syncthreads();
+    const int j0 = n0 / 2, nout = a.N / 2;
+#pragma unroll
+    for (int u = 0; u < NP; ++u) {
+      const int idx = tid + 512 * u, row = idx / PPR, pc = idx % PPR;
+      const int m = m0 + row, j = j0 + 8 * pc;
+      if (m < a.M && j < nout)
+        *reinterpret_cast<uint4*>(a.out + (size_t)m * a.ldo + j) =
+            *reinterpret_cast<const uint4*>(&T[row * TP + 8 * pc]);
+    }
+    return;
+  }
   if constexpr (EPI == EPI_RESID) {
     constexpr int TP = BN + 8;
     static_assert(BM * TP * 2 <= sizeof(lds), "the tile fits the stage buffers");
@@ -1428,13 +1466,16 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(GemmArgs a) {
     }
   }
 
-  // scales of this lane's four output channels (gate/up: two pairs)
+  // scales of this lane's four output channels (gate/up: two pairs), waited for once
+  // here: the epilogue's stores count in the same counter as loads, so a wait for a scale
+  // placed among the (conditional) stores would also wait for the stores before it
   float gsc[4];
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
     const int n = n0 + wn * 64 + nt * 16 + r16;
     gsc[nt] = a.scale[n < a.N ? n : 0];
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0
   if constexpr (EPI == EPI_STORE) {
     if (a.fuse_rope) {
       gemm_big_rope_epilogue(a, reinterpret_cast<bf16_t*>(&Ab[0][0]), acc, gsc, m0, n0, wm, wn);
@@ -3449,8 +3490,9 @@ hipError_t launch_gemm(const GemmArgs& a0, hipStream_t st, int* splits_used, int
   // (q|k|v only with its QK-norm / RoPE epilogue, at head dim 128: two heads per tile)
   const bool dl_qkv = a.epi == EPI_STORE && a.fuse_rope && a.rope.D == 128 &&
                       a.N == (a.rope.H + 2 * a.rope.KV) * a.rope.D && a.rope.M == a.M;
-  if (dl_tiles >= 256 && a.use_big != 0 && (a.epi == EPI_SILU || dl_qkv) && a.K % 64 == 0 &&
-      a.lda % 8 == 0) {
+  // (gate/up: its outputs are stored as 16-byte pieces, 8 per row piece)
+  const bool dl_silu = a.epi == EPI_SILU && a.N % 16 == 0 && a.ldo % 8 == 0;
+  if (dl_tiles >= 256 && a.use_big != 0 && (dl_silu || dl_qkv) && a.K % 64 == 0 && a.lda % 8 == 0) {
     if (splits_used) *splits_used = 1;
     if (a.epi == EPI_SILU) {
       a.fuse_rope = 0;
