@@ -995,67 +995,101 @@ __global__ __launch_bounds__(512) void k_gemm_ks(GemmArgs a) {
 template <int BM, int BN, int NT>
 __device__ __forceinline__ void gemm_rope_tile(const GemmArgs& a, const bf16_t* T, int m0, int n0) {
   constexpr int TP = BN + 8;
+  constexpr int NIT = BM * BN / 8 / NT;  // (row, head, lane part) items per thread
   const int tid = threadIdx.x;
   const RopeArgs& r = a.rope;
   const int D = r.D, half = D >> 1, L = D >> 3, lgL = __builtin_ctz(L);
   const int hpt = BN / D, nheads = r.H + 2 * r.KV;
-#pragma unroll 1
-  for (int it = 0; it < BM * BN / 8 / NT; ++it) {
-    const int idx = it * NT + tid;
-    const int gi = idx >> lgL, j = idx & (L - 1);
-    const int row = gi / hpt, hl = gi - row * hpt;
-    const int m = m0 + row, hh = n0 / D + hl;
-    const int c0 = row * TP + hl * D + 4 * j;
-    const uint2 u1 = *reinterpret_cast<const uint2*>(&T[c0]);
-    const uint2 u2 = *reinterpret_cast<const uint2*>(&T[c0 + half]);
-    const uint32_t w1[2] = {u1.x, u1.y}, w2[2] = {u2.x, u2.y};
-    float x1[4], x2[4], ss = 0.0f;
+  // item it of this thread: idx = it * NT + tid, its dims 4j .. and D/2 + 4j .. with
+  // j = tid % L the same for every item (NT is a multiple of L), so the thread's q and k
+  // gains are loaded once.  Every item's row slot and position are requested together and
+  // waited for once, then the RoPE factors group by group, each group's before its stores:
+  // stores count with loads, so a load issued among stores would wait for them.
+  const int j = tid & (L - 1);
+  const float4 gq1 = *reinterpret_cast<const float4*>(r.q_gain + 4 * j);
+  const float4 gq2 = *reinterpret_cast<const float4*>(r.q_gain + half + 4 * j);
+  const float4 gk1 = *reinterpret_cast<const float4*>(r.k_gain + 4 * j);
+  const float4 gk2 = *reinterpret_cast<const float4*>(r.k_gain + half + 4 * j);
+  int slot[NIT], pos[NIT];
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      x1[2 * e] = __uint_as_float(w1[e] << 16);
-      x1[2 * e + 1] = __uint_as_float(w1[e] & 0xFFFF0000u);
-      x2[2 * e] = __uint_as_float(w2[e] << 16);
-      x2[2 * e + 1] = __uint_as_float(w2[e] & 0xFFFF0000u);
+  for (int it = 0; it < NIT; ++it) {
+    const int gi = (it * NT + tid) >> lgL;
+    const int m = m0 + gi / hpt;
+    const int mc = m < r.M ? m : r.M - 1;
+    slot[it] = r.row_slot[mc];
+    pos[it] = r.row_pos[mc];
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0
+  // the items in groups of NG (registers for every item's RoPE factors at once would spill):
+  // a group's factors are requested together, then its stores go out
+  constexpr int NG = NIT > 8 ? 8 : NIT;
+  static_assert(NIT % NG == 0, "whole groups");
+#pragma unroll
+  for (int g0 = 0; g0 < NIT; g0 += NG) {
+    float4 c01[NG], c23[NG];
+#pragma unroll
+    for (int k = 0; k < NG; ++k) {
+      const float2* rp = r.rope + (size_t)pos[g0 + k] * half + 4 * j;  // (cos, sin) of dims 4j ..
+      c01[k] = *reinterpret_cast<const float4*>(rp);
+      c23[k] = *reinterpret_cast<const float4*>(rp + 2);
     }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0: the group's factors (and earlier stores)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) ss += x1[e] * x1[e] + x2[e] * x2[e];
-    for (int o = 1; o < L; o <<= 1) ss += __shfl_xor(ss, o, 64);
-    if (m >= r.M || hh >= nheads) continue;
-    const int slot = r.row_slot[m], p = r.row_pos[m];
-    if (hh >= r.H + r.KV) {
-      bf16_t* dst = r.vcache + (((size_t)slot * r.KV + (hh - r.H - r.KV)) * r.max_ctx + p) * D;
-      *reinterpret_cast<uint2*>(dst + 4 * j) = u1;
-      *reinterpret_cast<uint2*>(dst + half + 4 * j) = u2;
-      continue;
-    }
-    const bool isq = hh < r.H;
-    const float* gn = isq ? r.q_gain : r.k_gain;
-    const float4 g1 = *reinterpret_cast<const float4*>(gn + 4 * j);
-    const float4 g2 = *reinterpret_cast<const float4*>(gn + half + 4 * j);
-    const float4 cs01 = *reinterpret_cast<const float4*>(r.rope + (size_t)p * half + 4 * j);
-    const float4 cs23 = *reinterpret_cast<const float4*>(r.rope + (size_t)p * half + 4 * j + 2);
-    const float gv1[4] = {g1.x, g1.y, g1.z, g1.w}, gv2[4] = {g2.x, g2.y, g2.z, g2.w};
-    const float cv[4] = {cs01.x, cs01.z, cs23.x, cs23.z}, sv[4] = {cs01.y, cs01.w, cs23.y, cs23.w};
-    const float rinv = 1.0f / sqrtf(ss / (float)D + r.eps);
-    uint32_t o1[2], o2[2];
+    for (int k = 0; k < NG; ++k) {
+      const int it = g0 + k;
+      const int idx = it * NT + tid;
+      const int gi = idx >> lgL;
+      const int row = gi / hpt, hl = gi - row * hpt;
+      const int m = m0 + row, hh = n0 / D + hl;
+      const int c0 = row * TP + hl * D + 4 * j;
+      const uint2 u1 = *reinterpret_cast<const uint2*>(&T[c0]);
+      const uint2 u2 = *reinterpret_cast<const uint2*>(&T[c0 + half]);
+      const uint32_t w1[2] = {u1.x, u1.y}, w2[2] = {u2.x, u2.y};
+      float x1[4], x2[4], ss = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      uint32_t lo1 = 0, lo2 = 0;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int q = 2 * e + h;
-        const float y1 = rbf(x1[q] * rinv * gv1[q]);
-        const float y2 = rbf(x2[q] * rinv * gv2[q]);
-        lo1 |= (uint32_t)f2bf(y1 * cv[q] - y2 * sv[q]) << (16 * h);
-        lo2 |= (uint32_t)f2bf(y2 * cv[q] + y1 * sv[q]) << (16 * h);
+      for (int e = 0; e < 2; ++e) {
+        x1[2 * e] = __uint_as_float(w1[e] << 16);
+        x1[2 * e + 1] = __uint_as_float(w1[e] & 0xFFFF0000u);
+        x2[2 * e] = __uint_as_float(w2[e] << 16);
+        x2[2 * e + 1] = __uint_as_float(w2[e] & 0xFFFF0000u);
       }
-      o1[e] = lo1;
-      o2[e] = lo2;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ss += x1[e] * x1[e] + x2[e] * x2[e];
+      for (int o = 1; o < L; o <<= 1) ss += __shfl_xor(ss, o, 64);
+      if (m >= r.M || hh >= nheads) continue;
+      const int sl = slot[it], p = pos[it];
+      if (hh >= r.H + r.KV) {
+        bf16_t* dst = r.vcache + (((size_t)sl * r.KV + (hh - r.H - r.KV)) * r.max_ctx + p) * D;
+        *reinterpret_cast<uint2*>(dst + 4 * j) = u1;
+        *reinterpret_cast<uint2*>(dst + half + 4 * j) = u2;
+        continue;
+      }
+      const bool isq = hh < r.H;
+      const float4 g1 = isq ? gq1 : gk1, g2 = isq ? gq2 : gk2;
+      const float4 cs01 = c01[k], cs23 = c23[k];
+      const float gv1[4] = {g1.x, g1.y, g1.z, g1.w}, gv2[4] = {g2.x, g2.y, g2.z, g2.w};
+      const float cv[4] = {cs01.x, cs01.z, cs23.x, cs23.z}, sv[4] = {cs01.y, cs01.w, cs23.y, cs23.w};
+      const float rinv = 1.0f / sqrtf(ss / (float)D + r.eps);
+      uint32_t o1[2], o2[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        uint32_t lo1 = 0, lo2 = 0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int q = 2 * e + h;
+          const float y1 = rbf(x1[q] * rinv * gv1[q]);
+          const float y2 = rbf(x2[q] * rinv * gv2[q]);
+          lo1 |= (uint32_t)f2bf(y1 * cv[q] - y2 * sv[q]) << (16 * h);
+          lo2 |= (uint32_t)f2bf(y2 * cv[q] + y1 * sv[q]) << (16 * h);
+        }
+        o1[e] = lo1;
+        o2[e] = lo2;
+      }
+      bf16_t* dst = isq ? a.out + (size_t)m * a.ldo + (size_t)hh * D
+                        : r.kcache + (((size_t)sl * r.KV + (hh - r.H)) * r.max_ctx + p) * D;
+      *reinterpret_cast<uint2*>(dst + 4 * j) = make_uint2(o1[0], o1[1]);
+      *reinterpret_cast<uint2*>(dst + half + 4 * j) = make_uint2(o2[0], o2[1]);
     }
-    bf16_t* dst = isq ? a.out + (size_t)m * a.ldo + (size_t)hh * D
-                      : r.kcache + (((size_t)slot * r.KV + (hh - r.H)) * r.max_ctx + p) * D;
-    *reinterpret_cast<uint2*>(dst + 4 * j) = make_uint2(o1[0], o1[1]);
-    *reinterpret_cast<uint2*>(dst + half + 4 * j) = make_uint2(o2[0], o2[1]);
   }
 }
 
