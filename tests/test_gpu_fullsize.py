@@ -7,9 +7,10 @@ take the same code paths as the 28-layer model ("Run local LLM decode", section
 "Limitations": the Qwen3-0.6B-Base dimensions):
   * B = 1: the register GEMV for q|k|v, O, gate/up and down, the LM head's grid-capped
     row-block loop over 151,936 rows with its fused arg-max, decode attention in 5 splits;
-  * B = 8 and 32: the MFMA skinny projections (RMSNorm folded into q|k|v and gate/up; at
-    32 rows the O and down projections split over K across work-groups), the batched LM
-    head, and at B = 32 (32 x 8 KV heads = 256 pairs) the eight-wave attention kernel;
+  * B = 8, 16 and 32: the MFMA skinny projections (RMSNorm folded into q|k|v and gate/up;
+    at 32 rows the O and down projections split over K across work-groups), the batched LM
+    head, and at B = 32 (32 x 8 KV heads = 256 pairs) the eight-wave attention kernel; their
+    prompts prefilled together (M = 2048, 4096, 8192) take the three many-row GEMMs;
   * an 8192-token prompt: flash prefill over 128 query tiles per head, then decode
     attention over about 43 position splits (split count from the measured residency) merged by the last split (and, in a second run, by
     the separate merge launch).
@@ -79,11 +80,14 @@ def test_fullsize_b1_teacher_forced(full_setup):
     _report("fullsize B=1 (prefill row + 4 steps)", errs, "qwen3-0.6b-l2")
 
 
-@pytest.mark.parametrize("B", [8, 32])
+@pytest.mark.parametrize("B", [8, 16, 32])
 def test_fullsize_batched_teacher_forced(full_setup, B):
     """B prompts of 256 tokens prefilled together (M = 256 B), then 3 decode steps; rows 0,
     B/2 and B-1 are teacher-forced against their own oracle runs, every row's fused arg-max
-    is checked against the arg-max of its own logits."""
+    is checked against the arg-max of its own logits.  The prefill GEMMs: M = 2048 runs the
+    128x128-tile kernel for q|k|v (QK-norm/RoPE epilogue) and gate/up; M = 4096 the direct-
+    load kernel for those and the 128x128 kernel's residual epilogue for O and down; M = 8192
+    the direct-load kernel for every projection."""
     w, qm, m = full_setup
     prompts = [make_prompt(SH.vocab, 256, 1000 + b) for b in range(B)]
     rows = [0, B // 2, B - 1]
