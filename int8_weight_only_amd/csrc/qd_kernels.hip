@@ -3381,6 +3381,9 @@ static hipError_t gemv1_r(const GemvArgs& a, int epi, hipStream_t st) {
 static hipError_t gemv1(const GemvArgs& a, int epi, hipStream_t st) {
   if (a.K > 8192) return hipErrorInvalidValue;
   const int nout = epi == EPI_SILU ? a.N / 2 : a.N;
+  // rows per wave: 2 for the q|k|v projection of a 1024-wide model (512 work-groups; 1 and 4
+  // rows measured slower), 4 for the LM head and other wide projections, else 1
+  if (epi == EPI_STORE && nout >= 4096 && a.K <= 1024) return gemv1_rk<2, 1>(a, epi, st);
   if ((epi == EPI_LOGITS || nout >= 4096) && a.K <= 2048)
     return a.K <= 1024 ? gemv1_rk<4, 1>(a, epi, st) : gemv1_rk<4, 2>(a, epi, st);
   return gemv1_r<1>(a, epi, st);
