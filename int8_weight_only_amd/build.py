@@ -19,6 +19,9 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 instructions stay off (hipcc's host pass warns it does not know the feature)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # leading scalar kernel arguments preloaded into SGPRs at wave launch (no memory round
+    # trip before the first loads that need them)
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wno-unused-result",
 ]
 

@@ -283,8 +283,31 @@ __global__ void k_lm_finish_step(int* step) { *step += 1; }
 // all splits requested at once) into LDS, which the waves then read instead of x.  This
 // takes the attention kernel's last-split hand-off (store completion, counter, reload)
 // off the step's critical path.
+// The fields the first loads need come as leading scalar arguments, which the hardware
+// preloads into SGPRs at wave launch (the library is built with kernel-argument preloading);
+// the rest are read from the argument segment in memory, off the first loads' path.  After the
+// weights and scales, p0, p1, p2, i0, i1: the activation row, RMSNorm gains, row indices and
+// row stride, or with MERGE the attention's split partials, their (max, sum) pairs, (unused),
+// split count and head dim.
 template <int R, int KC, int EPI, bool MERGE = false>
-__global__ __launch_bounds__(256) void k_gemv1(GemvArgs a) {
+__global__ __launch_bounds__(256) void k_gemv1(const int8_t* W_, const float* scale_, const void* p0,
+                                               const void* p1, const void* p2, int N_, int K_, int i0,
+                                               int i1, GemvArgs a) {
+  a.W = W_;
+  a.scale = scale_;
+  a.N = N_;
+  a.K = K_;
+  if constexpr (MERGE) {
+    a.att_po = static_cast<const float*>(p0);
+    a.att_ml = static_cast<const float*>(p1);
+    a.att_ns = i0;
+    a.att_D = i1;
+  } else {
+    a.x = static_cast<const bf16_t*>(p0);
+    a.gain = static_cast<const float*>(p1);
+    a.x_rows = static_cast<const int*>(p2);
+    a.ldx = i0;
+  }
   constexpr int NR = (EPI == EPI_SILU) ? 2 * R : R;  // weight rows per wave
   const int K = a.K;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -3346,21 +3369,30 @@ static hipError_t gemv1_rk(const GemvArgs& a, int epi, hipStream_t st) {
   const int nout = epi == EPI_SILU ? a.N / 2 : a.N;
   const int nblk = (nout + 4 * R - 1) / (4 * R);
   dim3 grid(epi == EPI_LOGITS ? (nblk < LM_MAX_GRID ? nblk : LM_MAX_GRID) : nblk);
+  // the leading (preloaded) arguments: see k_gemv1
+  const void* xp = a.x;
+  const void* gp = a.gain;
+  const void* rp = a.x_rows;
+#define QD_GEMV1(E, M, P0, P1, I0, I1)                                                            \
+  hipLaunchKernelGGL((k_gemv1<R, KC, E, M>), grid, dim3(256), 0, st, a.W, a.scale, P0, P1, rp, a.N, \
+                     a.K, I0, I1, a)
   switch (epi) {
-    case EPI_STORE: hipLaunchKernelGGL((k_gemv1<R, KC, EPI_STORE>), grid, dim3(256), 0, st, a); break;
+    case EPI_STORE: QD_GEMV1(EPI_STORE, false, xp, gp, a.ldx, 0); break;
     case EPI_RESID:
       if (a.att_ns > 0) {
         if (a.att_ns > ATT_DEFER_MAX_SPLITS || a.att_D <= 0 || a.att_D % 8 || a.K % a.att_D || !a.att_po ||
             !a.att_ml || a.K > 64 * 16 * KC)
           return hipErrorInvalidValue;
-        hipLaunchKernelGGL((k_gemv1<R, KC, EPI_RESID, true>), grid, dim3(256), 0, st, a);
+        QD_GEMV1(EPI_RESID, true, static_cast<const void*>(a.att_po), static_cast<const void*>(a.att_ml),
+                 a.att_ns, a.att_D);
       } else {
-        hipLaunchKernelGGL((k_gemv1<R, KC, EPI_RESID>), grid, dim3(256), 0, st, a);
+        QD_GEMV1(EPI_RESID, false, xp, gp, a.ldx, 0);
       }
       break;
-    case EPI_SILU: hipLaunchKernelGGL((k_gemv1<R, KC, EPI_SILU>), grid, dim3(256), 0, st, a); break;
-    default: hipLaunchKernelGGL((k_gemv1<R, KC, EPI_LOGITS>), grid, dim3(256), 0, st, a); break;
+    case EPI_SILU: QD_GEMV1(EPI_SILU, false, xp, gp, a.ldx, 0); break;
+    default: QD_GEMV1(EPI_LOGITS, false, xp, gp, a.ldx, 0); break;
   }
+#undef QD_GEMV1
   return hipGetLastError();
 }
 
