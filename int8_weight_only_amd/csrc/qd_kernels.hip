@@ -2492,8 +2492,22 @@ __global__ __launch_bounds__(256) void k_qk_rope(RopeArgs a) {
 // unnormalized output); the split that finishes last merges them.
 // WIDE: more than SB = 8 splits, merged by the batched path below (its own instantiation, so
 // the short-context kernel keeps its registers and LDS)
+// The fields of the first dependent loads (the row's slot, its position, the K/V tile and
+// projection addresses) come as leading scalar arguments, preloaded into SGPRs at wave launch.
 template <int D, int G, int NW, bool WIDE>
-__global__ __launch_bounds__(64 * NW) void k_attn_dec(AttnDecArgs a) {
+__global__ __launch_bounds__(64 * NW) void k_attn_dec(const int* row_slot_, const int* pos_,
+                                                      const bf16_t* qkv_, bf16_t* kcache_, bf16_t* vcache_,
+                                                      int ldqkv_, int KV_, int max_ctx_, int split_len_,
+                                                      AttnDecArgs a) {
+  a.row_slot = row_slot_;
+  a.pos = pos_;
+  a.qkv = qkv_;
+  a.kcache = kcache_;
+  a.vcache = vcache_;
+  a.ldqkv = ldqkv_;
+  a.KV = KV_;
+  a.max_ctx = max_ctx_;
+  a.split_len = split_len_;
   constexpr int NT = 64 * NW;              // threads
   constexpr int CHW = 16 * NW;             // positions per iteration
   constexpr int HALF = D / 2;
@@ -3668,10 +3682,13 @@ hipError_t launch_qk_rope(const RopeArgs& a, hipStream_t st) {
 template <int D, int G, int NW>
 static void attn_dec_launch(const AttnDecArgs& a, dim3 grid, hipStream_t st) {
   constexpr int W = (NW == 8 && G * D > 512) ? 4 : NW;
+  // the leading (preloaded) arguments: see k_attn_dec
   if (a.nsplit > 8 && a.merge_last == 1)
-    hipLaunchKernelGGL((k_attn_dec<D, G, W, true>), grid, dim3(64 * W), 0, st, a);
+    hipLaunchKernelGGL((k_attn_dec<D, G, W, true>), grid, dim3(64 * W), 0, st, a.row_slot, a.pos, a.qkv,
+                       a.kcache, a.vcache, a.ldqkv, a.KV, a.max_ctx, a.split_len, a);
   else
-    hipLaunchKernelGGL((k_attn_dec<D, G, W, false>), grid, dim3(64 * W), 0, st, a);
+    hipLaunchKernelGGL((k_attn_dec<D, G, W, false>), grid, dim3(64 * W), 0, st, a.row_slot, a.pos, a.qkv,
+                       a.kcache, a.vcache, a.ldqkv, a.KV, a.max_ctx, a.split_len, a);
 }
 
 template <int D, int NW>
