@@ -283,6 +283,26 @@ __global__ void k_lm_finish_step(int* step) { *step += 1; }
 // all splits requested at once) into LDS, which the waves then read instead of x.  This
 // takes the attention kernel's last-split hand-off (store completion, counter, reload)
 // off the step's critical path.
+// Leading scalar arguments of the batched projection kernels (k_skinny, k_skinny_norm,
+// k_skinny_split, k_lm_skinny): the fields their first loads need, preloaded into SGPRs at
+// wave launch, copied over the argument struct's (which is read from memory).
+#define QD_SKINNY_PRELOAD_PARAMS                                                                \
+  const int8_t *W_, const float *scale_, const bf16_t *x_, const int *x_rows_, const float *gain_, \
+      int N_, int K_, int ldx_, int nb_
+#define QD_SKINNY_PRELOAD_SET(a)                                                                  \
+  do {                                                                                            \
+    (a).W = W_;                                                                                   \
+    (a).scale = scale_;                                                                           \
+    (a).x = x_;                                                                                   \
+    (a).x_rows = x_rows_;                                                                         \
+    (a).gain = gain_;                                                                             \
+    (a).N = N_;                                                                                   \
+    (a).K = K_;                                                                                   \
+    (a).ldx = ldx_;                                                                               \
+    (a).nb = nb_;                                                                                 \
+  } while (0)
+#define QD_SKINNY_PRELOAD_ARGS(a) (a).W, (a).scale, (a).x, (a).x_rows, (a).gain, (a).N, (a).K, (a).ldx, (a).nb
+
 // The fields the first loads need come as leading scalar arguments, which the hardware
 // preloads into SGPRs at wave launch (the library is built with kernel-argument preloading);
 // the rest are read from the argument segment in memory, off the first loads' path.  After the
@@ -1778,7 +1798,8 @@ __device__ __forceinline__ void skinny_out(const GemvArgs& a, int tile, int tok,
 }
 
 template <int TT, int EPI, int NWS, bool XS = false>
-__global__ __launch_bounds__(64 * NWS) void k_skinny(GemvArgs a) {
+__global__ __launch_bounds__(64 * NWS) void k_skinny(QD_SKINNY_PRELOAD_PARAMS, GemvArgs a) {
+  QD_SKINNY_PRELOAD_SET(a);
   constexpr int CTW = (EPI == EPI_SILU) ? 2 : 1;
   constexpr int NACC = CTW * TT;
   __shared__ float red[NWS][NACC][4][64];
@@ -1903,7 +1924,8 @@ constexpr int SKN_MAX_K = 4096;  // 8 waves x 4 blocks x 128
 // that streams from L2 at full rate), squared and normalized in that layout, then turned
 // into the matrix-core operand layout through the wave's own LDS slot before the MFMAs.
 template <int TT, int EPI, int NB, bool XS = false>
-__global__ __launch_bounds__(64 * SKN_WAVES) void k_skinny_norm(GemvArgs a) {
+__global__ __launch_bounds__(64 * SKN_WAVES) void k_skinny_norm(QD_SKINNY_PRELOAD_PARAMS, GemvArgs a) {
+  QD_SKINNY_PRELOAD_SET(a);
   constexpr int NWS = SKN_WAVES;
   constexpr int CTW = (EPI == EPI_SILU) ? 2 : 1;
   constexpr int NACC = CTW * TT;
@@ -2117,7 +2139,8 @@ __global__ __launch_bounds__(64 * SKN_WAVES) void k_skinny_norm(GemvArgs a) {
 // counts in last adds the S partials in split order (fixed order: the result does not
 // depend on arrival order) and runs the epilogue.  No work-group waits for another.
 template <int TT, int EPI, int NWS, bool XS = false>
-__global__ __launch_bounds__(64 * NWS) void k_skinny_split(GemvArgs a) {
+__global__ __launch_bounds__(64 * NWS) void k_skinny_split(QD_SKINNY_PRELOAD_PARAMS, GemvArgs a) {
+  QD_SKINNY_PRELOAD_SET(a);
   constexpr int CTW = (EPI == EPI_SILU) ? 2 : 1;
   constexpr int NACC = CTW * TT;
   constexpr int NE = (TT * 256 + 64 * NWS - 1) / (64 * NWS);
@@ -2265,7 +2288,8 @@ __global__ __launch_bounds__(64 * NWS) void k_skinny_split(GemvArgs a) {
 // would make the compiler wait for them to move registers)
 constexpr int LMT = 4;
 template <int TT, int NS>
-__global__ __launch_bounds__(256) void k_lm_skinny(GemvArgs a) {
+__global__ __launch_bounds__(256) void k_lm_skinny(QD_SKINNY_PRELOAD_PARAMS, GemvArgs a) {
+  QD_SKINNY_PRELOAD_SET(a);
   constexpr int KC = 1024 / TT;                 // k per chunk: LDS = 16*TT rows x KC
   constexpr int OOB = (int)0x80000000;
   __shared__ __align__(16) bf16_t xs[TT * 16][KC + 8];
@@ -3460,9 +3484,9 @@ static hipError_t skinny_tt(const GemvArgs& a, int epi, hipStream_t st) {
     const int ntiles = (a.N + 15) / 16;
     const int g = (ntiles + 4 * LMT - 1) / (4 * LMT);
     if (g > LM_MAX_GRID || (a.K & 31) || (size_t)a.N * a.K > 0x7FFFFFFFu) return hipErrorInvalidValue;
-    if (a.K == 1024) hipLaunchKernelGGL((k_lm_skinny<TT, 8>), dim3(g), dim3(256), 0, st, a);
-    else if (a.K == 2048) hipLaunchKernelGGL((k_lm_skinny<TT, 16>), dim3(g), dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((k_lm_skinny<TT, 0>), dim3(g), dim3(256), 0, st, a);
+    if (a.K == 1024) hipLaunchKernelGGL((k_lm_skinny<TT, 8>), dim3(g), dim3(256), 0, st, QD_SKINNY_PRELOAD_ARGS(a), a);
+    else if (a.K == 2048) hipLaunchKernelGGL((k_lm_skinny<TT, 16>), dim3(g), dim3(256), 0, st, QD_SKINNY_PRELOAD_ARGS(a), a);
+    else hipLaunchKernelGGL((k_lm_skinny<TT, 0>), dim3(g), dim3(256), 0, st, QD_SKINNY_PRELOAD_ARGS(a), a);
     hipError_t e = hipGetLastError();
     return e != hipSuccess ? e : lm_finish(a, g, st);
   }
@@ -3475,15 +3499,15 @@ static hipError_t skinny_tt(const GemvArgs& a, int epi, hipStream_t st) {
     dim3 g(ntiles * a.ksplit);
     if (XS) {
       switch (epi) {
-        case EPI_STORE: hipLaunchKernelGGL((k_skinny_split<TT, EPI_STORE, 4, XS>), g, dim3(256), 0, st, a); break;
-        case EPI_RESID: hipLaunchKernelGGL((k_skinny_split<TT, EPI_RESID, 4, XS>), g, dim3(256), 0, st, a); break;
-        default: hipLaunchKernelGGL((k_skinny_split<TT, EPI_SILU, 4, XS>), g, dim3(256), 0, st, a); break;
+        case EPI_STORE: hipLaunchKernelGGL((k_skinny_split<TT, EPI_STORE, 4, XS>), g, dim3(256), 0, st, QD_SKINNY_PRELOAD_ARGS(a), a); break;
+        case EPI_RESID: hipLaunchKernelGGL((k_skinny_split<TT, EPI_RESID, 4, XS>), g, dim3(256), 0, st, QD_SKINNY_PRELOAD_ARGS(a), a); break;
+        default: hipLaunchKernelGGL((k_skinny_split<TT, EPI_SILU, 4, XS>), g, dim3(256), 0, st, QD_SKINNY_PRELOAD_ARGS(a), a); break;
       }
     } else {
       switch (epi) {
-        case EPI_STORE: hipLaunchKernelGGL((k_skinny_split<TT, EPI_STORE, 4>), g, dim3(256), 0, st, a); break;
-        case EPI_RESID: hipLaunchKernelGGL((k_skinny_split<TT, EPI_RESID, 4>), g, dim3(256), 0, st, a); break;
-        default: hipLaunchKernelGGL((k_skinny_split<TT, EPI_SILU, 4>), g, dim3(256), 0, st, a); break;
+        case EPI_STORE: hipLaunchKernelGGL((k_skinny_split<TT, EPI_STORE, 4>), g, dim3(256), 0, st, QD_SKINNY_PRELOAD_ARGS(a), a); break;
+        case EPI_RESID: hipLaunchKernelGGL((k_skinny_split<TT, EPI_RESID, 4>), g, dim3(256), 0, st, QD_SKINNY_PRELOAD_ARGS(a), a); break;
+        default: hipLaunchKernelGGL((k_skinny_split<TT, EPI_SILU, 4>), g, dim3(256), 0, st, QD_SKINNY_PRELOAD_ARGS(a), a); break;
       }
     }
     return hipGetLastError();
@@ -3492,28 +3516,28 @@ static hipError_t skinny_tt(const GemvArgs& a, int epi, hipStream_t st) {
   if (ntiles < 128) {  // few tiles: eight waves split K eight ways
     if (XS) {
       switch (epi) {
-        case EPI_STORE: hipLaunchKernelGGL((k_skinny<TT, EPI_STORE, 8, XS>), grid, dim3(512), 0, st, a); break;
-        case EPI_RESID: hipLaunchKernelGGL((k_skinny<TT, EPI_RESID, 8, XS>), grid, dim3(512), 0, st, a); break;
-        default: hipLaunchKernelGGL((k_skinny<TT, EPI_SILU, 8, XS>), grid, dim3(512), 0, st, a); break;
+        case EPI_STORE: hipLaunchKernelGGL((k_skinny<TT, EPI_STORE, 8, XS>), grid, dim3(512), 0, st, QD_SKINNY_PRELOAD_ARGS(a), a); break;
+        case EPI_RESID: hipLaunchKernelGGL((k_skinny<TT, EPI_RESID, 8, XS>), grid, dim3(512), 0, st, QD_SKINNY_PRELOAD_ARGS(a), a); break;
+        default: hipLaunchKernelGGL((k_skinny<TT, EPI_SILU, 8, XS>), grid, dim3(512), 0, st, QD_SKINNY_PRELOAD_ARGS(a), a); break;
       }
     } else {
       switch (epi) {
-        case EPI_STORE: hipLaunchKernelGGL((k_skinny<TT, EPI_STORE, 8>), grid, dim3(512), 0, st, a); break;
-        case EPI_RESID: hipLaunchKernelGGL((k_skinny<TT, EPI_RESID, 8>), grid, dim3(512), 0, st, a); break;
-        default: hipLaunchKernelGGL((k_skinny<TT, EPI_SILU, 8>), grid, dim3(512), 0, st, a); break;
+        case EPI_STORE: hipLaunchKernelGGL((k_skinny<TT, EPI_STORE, 8>), grid, dim3(512), 0, st, QD_SKINNY_PRELOAD_ARGS(a), a); break;
+        case EPI_RESID: hipLaunchKernelGGL((k_skinny<TT, EPI_RESID, 8>), grid, dim3(512), 0, st, QD_SKINNY_PRELOAD_ARGS(a), a); break;
+        default: hipLaunchKernelGGL((k_skinny<TT, EPI_SILU, 8>), grid, dim3(512), 0, st, QD_SKINNY_PRELOAD_ARGS(a), a); break;
       }
     }
   } else if (XS) {
     switch (epi) {
-      case EPI_STORE: hipLaunchKernelGGL((k_skinny<TT, EPI_STORE, 4, XS>), grid, dim3(256), 0, st, a); break;
-      case EPI_RESID: hipLaunchKernelGGL((k_skinny<TT, EPI_RESID, 4, XS>), grid, dim3(256), 0, st, a); break;
-      default: hipLaunchKernelGGL((k_skinny<TT, EPI_SILU, 4, XS>), grid, dim3(256), 0, st, a); break;
+      case EPI_STORE: hipLaunchKernelGGL((k_skinny<TT, EPI_STORE, 4, XS>), grid, dim3(256), 0, st, QD_SKINNY_PRELOAD_ARGS(a), a); break;
+      case EPI_RESID: hipLaunchKernelGGL((k_skinny<TT, EPI_RESID, 4, XS>), grid, dim3(256), 0, st, QD_SKINNY_PRELOAD_ARGS(a), a); break;
+      default: hipLaunchKernelGGL((k_skinny<TT, EPI_SILU, 4, XS>), grid, dim3(256), 0, st, QD_SKINNY_PRELOAD_ARGS(a), a); break;
     }
   } else {
     switch (epi) {
-      case EPI_STORE: hipLaunchKernelGGL((k_skinny<TT, EPI_STORE, 4>), grid, dim3(256), 0, st, a); break;
-      case EPI_RESID: hipLaunchKernelGGL((k_skinny<TT, EPI_RESID, 4>), grid, dim3(256), 0, st, a); break;
-      default: hipLaunchKernelGGL((k_skinny<TT, EPI_SILU, 4>), grid, dim3(256), 0, st, a); break;
+      case EPI_STORE: hipLaunchKernelGGL((k_skinny<TT, EPI_STORE, 4>), grid, dim3(256), 0, st, QD_SKINNY_PRELOAD_ARGS(a), a); break;
+      case EPI_RESID: hipLaunchKernelGGL((k_skinny<TT, EPI_RESID, 4>), grid, dim3(256), 0, st, QD_SKINNY_PRELOAD_ARGS(a), a); break;
+      default: hipLaunchKernelGGL((k_skinny<TT, EPI_SILU, 4>), grid, dim3(256), 0, st, QD_SKINNY_PRELOAD_ARGS(a), a); break;
     }
   }
   return hipGetLastError();
@@ -3526,11 +3550,11 @@ static hipError_t skinny_norm_launch(const GemvArgs& a, int epi, hipStream_t st)
   // row-contiguous staging above 8 rows (measured per step: B = 32 +2.0%, B = 16 +0.9%,
   // B = 8 -0.7%)
   if (!a.no_xstage && a.nb > 8) {
-    if (epi == EPI_STORE) hipLaunchKernelGGL((k_skinny_norm<TT, EPI_STORE, NB, true>), grid, blk, 0, st, a);
-    else hipLaunchKernelGGL((k_skinny_norm<TT, EPI_SILU, NB, true>), grid, blk, 0, st, a);
+    if (epi == EPI_STORE) hipLaunchKernelGGL((k_skinny_norm<TT, EPI_STORE, NB, true>), grid, blk, 0, st, QD_SKINNY_PRELOAD_ARGS(a), a);
+    else hipLaunchKernelGGL((k_skinny_norm<TT, EPI_SILU, NB, true>), grid, blk, 0, st, QD_SKINNY_PRELOAD_ARGS(a), a);
   } else {
-    if (epi == EPI_STORE) hipLaunchKernelGGL((k_skinny_norm<TT, EPI_STORE, NB>), grid, blk, 0, st, a);
-    else hipLaunchKernelGGL((k_skinny_norm<TT, EPI_SILU, NB>), grid, blk, 0, st, a);
+    if (epi == EPI_STORE) hipLaunchKernelGGL((k_skinny_norm<TT, EPI_STORE, NB>), grid, blk, 0, st, QD_SKINNY_PRELOAD_ARGS(a), a);
+    else hipLaunchKernelGGL((k_skinny_norm<TT, EPI_SILU, NB>), grid, blk, 0, st, QD_SKINNY_PRELOAD_ARGS(a), a);
   }
   return hipGetLastError();
 }
