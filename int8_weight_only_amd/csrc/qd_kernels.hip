@@ -244,7 +244,16 @@ __device__ __forceinline__ void lm_head_store(const GemvArgs& a, unsigned long l
 // one work-group per batch row: reduces that row's keys over the LM-head work-groups and
 // writes the greedy id (advancing its position).  The step counter advances once every
 // row has read it: in k_lm_finish_step, launched after, or here when there is one row
-__global__ __launch_bounds__(256) void k_lm_finish(GemvArgs a, int nblocks) {
+__global__ __launch_bounds__(256) void k_lm_finish(unsigned long long* keys_, int* next_ids_, int* pos_,
+                                                   const int* row_slot_, int* out_ids_, int* step_,
+                                                   int nblocks, GemvArgs a) {
+  // the pointers come as leading scalar arguments, preloaded into SGPRs at wave launch
+  a.part_keys = keys_;
+  a.next_ids = next_ids_;
+  a.pos = pos_;
+  a.row_slot = row_slot_;
+  a.out_ids = out_ids_;
+  a.step = step_;
   __shared__ unsigned long long red[4];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int b = blockIdx.x;
@@ -283,6 +292,56 @@ __global__ void k_lm_finish_step(int* step) { *step += 1; }
 // all splits requested at once) into LDS, which the waves then read instead of x.  This
 // takes the attention kernel's last-split hand-off (store completion, counter, reload)
 // off the step's critical path.
+// Leading scalar arguments of the prefill GEMMs (k_gemm, k_gemm_ks, k_gemm_dl, k_gemm_big),
+// prefill attention (k_flash_prefill) and the prefill QK-norm/RoPE (k_qk_rope): the fields
+// their first loads need, preloaded into SGPRs at wave launch.
+#define QD_GEMM_PRELOAD_PARAMS                                                                  \
+  const bf16_t *A_, const int8_t *W_, const float *scale_, bf16_t *out_, int M_, int N_, int K_, \
+      int lda_, int ldo_, int splits_
+#define QD_GEMM_PRELOAD_SET(a)                                                                    \
+  do {                                                                                            \
+    (a).A = A_;                                                                                   \
+    (a).W = W_;                                                                                   \
+    (a).scale = scale_;                                                                           \
+    (a).out = out_;                                                                               \
+    (a).M = M_;                                                                                   \
+    (a).N = N_;                                                                                   \
+    (a).K = K_;                                                                                   \
+    (a).lda = lda_;                                                                               \
+    (a).ldo = ldo_;                                                                               \
+    (a).splits = splits_;                                                                         \
+  } while (0)
+#define QD_GEMM_PRELOAD_ARGS(a) (a).A, (a).W, (a).scale, (a).out, (a).M, (a).N, (a).K, (a).lda, (a).ldo, (a).splits
+#define QD_FLASH_PRELOAD_PARAMS \
+  const int4 *tiles_, const bf16_t *q_, const bf16_t *kc_, const bf16_t *vc_, int ldq_, int H_, int KV_, int max_ctx_
+#define QD_FLASH_PRELOAD_SET(a) \
+  do {                          \
+    (a).tiles = tiles_;         \
+    (a).q = q_;                 \
+    (a).kcache = kc_;           \
+    (a).vcache = vc_;           \
+    (a).ldq = ldq_;             \
+    (a).H = H_;                 \
+    (a).KV = KV_;               \
+    (a).max_ctx = max_ctx_;     \
+  } while (0)
+#define QD_FLASH_PRELOAD_ARGS(a) (a).tiles, (a).q, (a).kcache, (a).vcache, (a).ldq, (a).H, (a).KV, (a).max_ctx
+#define QD_ROPE_PRELOAD_PARAMS                                                                     \
+  bf16_t *qkv_, const int *row_pos_, const int *row_slot_, const float *q_gain_, const float *k_gain_, \
+      const float2 *rope_, int ldqkv_, int H_
+#define QD_ROPE_PRELOAD_SET(a) \
+  do {                         \
+    (a).qkv = qkv_;            \
+    (a).row_pos = row_pos_;    \
+    (a).row_slot = row_slot_;  \
+    (a).q_gain = q_gain_;      \
+    (a).k_gain = k_gain_;      \
+    (a).rope = rope_;          \
+    (a).ldqkv = ldqkv_;        \
+    (a).H = H_;                \
+  } while (0)
+#define QD_ROPE_PRELOAD_ARGS(a) (a).qkv, (a).row_pos, (a).row_slot, (a).q_gain, (a).k_gain, (a).rope, (a).ldqkv, (a).H
+
 // Leading scalar arguments of the batched projection kernels (k_skinny, k_skinny_norm,
 // k_skinny_split, k_lm_skinny): the fields their first loads need, preloaded into SGPRs at
 // wave launch, copied over the argument struct's (which is read from memory).
@@ -681,7 +740,8 @@ constexpr int GEMM_PF = 4;  // k-steps of loads in flight
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 template <int EPI>
-__global__ __launch_bounds__(512) void k_gemm(GemmArgs a) {
+__global__ __launch_bounds__(512) void k_gemm(QD_GEMM_PRELOAD_PARAMS, GemmArgs a) {
+  QD_GEMM_PRELOAD_SET(a);
   constexpr int BM = 64, BN = 64, BK = 128, P = GEMM_PF;
   constexpr int OOB = (int)0x80000000;
   // LDS holds each 16-row x 32-k operand fragment in MFMA lane order (lane l's 8 values in
@@ -930,7 +990,8 @@ __global__ __launch_bounds__(512) void k_gemm(GemmArgs a) {
 // one memory round trip, its MFMAs and one reduction, where the k-stepped kernel walks a
 // serial chain of K/128 steps.  128 KB of LDS: one work-group per CU.
 template <int EPI, int C>
-__global__ __launch_bounds__(512) void k_gemm_ks(GemmArgs a) {
+__global__ __launch_bounds__(512) void k_gemm_ks(QD_GEMM_PRELOAD_PARAMS, GemmArgs a) {
+  QD_GEMM_PRELOAD_SET(a);
   constexpr int OOB = (int)0x80000000;
   __shared__ __align__(16) f32x4_t red[8][16][64];  // [wave][m tile * 4 + n tile][lane]
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -1177,7 +1238,8 @@ __device__ __forceinline__ void lds_dma16_s(const void* base, unsigned off, unsi
 // WM = 2: 256x256 tiles, waves 2 (rows) x 4 (channels) of 128x64; WM = 4: 256x128 tiles for
 // the narrow projections (O and down), waves 4 x 2 of 64x64.
 template <int EPI, int WM>
-__global__ __launch_bounds__(512, 1) void k_gemm_dl(GemmArgs a) {
+__global__ __launch_bounds__(512, 1) void k_gemm_dl(QD_GEMM_PRELOAD_PARAMS, GemmArgs a) {
+  QD_GEMM_PRELOAD_SET(a);
   constexpr int WN = 8 / WM, MT = 16 / WM;  // waves along channels, 16-row tiles per wave
   constexpr int BM = 256, BN = 64 * WN, BK = 64;
   constexpr int A_BYTES = BM * BK * 2, W_BYTES = BN * BK;  // 32 KB + 16 (8) KB per stage
@@ -1448,7 +1510,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dl(GemmArgs a) {
 // share one L2 share token rows and walk neighbouring weight rows.  Residual inputs are read
 // in the epilogue.  Two work-groups fit on a CU (68 KB of LDS each).
 template <int EPI>
-__global__ __launch_bounds__(256, 2) void k_gemm_big(GemmArgs a) {
+__global__ __launch_bounds__(256, 2) void k_gemm_big(QD_GEMM_PRELOAD_PARAMS, GemmArgs a) {
+  QD_GEMM_PRELOAD_SET(a);
   constexpr int BM = 128, BN = 128, BK = 64;
   constexpr int OOB = (int)0x80000000;
   // LDS holds each 16-row x 32-k operand fragment in MFMA lane order: lane l's 8 values
@@ -2443,7 +2506,8 @@ __global__ __launch_bounds__(256) void k_lm_skinny(QD_SKINNY_PRELOAD_PARAMS, Gem
 // slot of the row (q heads, then k heads, then v heads), so a wave makes one round trip.
 // q and k heads: RMSNorm over head_dim with a shared gain, then rotate-half RoPE at
 // the row's position; q is written back in place, k and v go to the cache.
-__global__ __launch_bounds__(256) void k_qk_rope(RopeArgs a) {
+__global__ __launch_bounds__(256) void k_qk_rope(QD_ROPE_PRELOAD_PARAMS, RopeArgs a) {
+  QD_ROPE_PRELOAD_SET(a);
   const int r = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
   const int hh = blockIdx.y * 4 + __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -3086,7 +3150,8 @@ __global__ __launch_bounds__(128) void k_attn_dec_merge(AttnDecArgs a) {
 // probabilities enter the product with ~16 significant bits rather than bf16's 8.
 template <int D, int RG>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 4 - RG : 1))) void k_flash_prefill(
-    FlashArgs a) {
+    QD_FLASH_PRELOAD_PARAMS, FlashArgs a) {
+  QD_FLASH_PRELOAD_SET(a);
   constexpr int KB = 64;             // keys per block
   constexpr int NKK = KB / 32;       // 32-key steps per block (two S^T tiles each)
   constexpr int KS = D / 32;         // MFMA k-steps over the head dim
@@ -3460,7 +3525,8 @@ static hipError_t gemv1(const GemvArgs& a, int epi, hipStream_t st) {
 }
 
 static hipError_t lm_finish(const GemvArgs& a, int nblocks, hipStream_t st) {
-  hipLaunchKernelGGL(k_lm_finish, dim3(a.nb), dim3(256), 0, st, a, nblocks);
+  hipLaunchKernelGGL(k_lm_finish, dim3(a.nb), dim3(256), 0, st, a.part_keys, a.next_ids, a.pos, a.row_slot,
+                     a.out_ids, a.step, nblocks, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !a.bump_step || a.nb == 1) return e;
   hipLaunchKernelGGL(k_lm_finish_step, dim3(1), dim3(1), 0, st, a.step);
@@ -3603,10 +3669,10 @@ hipError_t launch_gemm(const GemmArgs& a0, hipStream_t st, int* splits_used, int
     if (splits_used) *splits_used = 1;
     if (a.epi == EPI_SILU) {
       a.fuse_rope = 0;
-      hipLaunchKernelGGL((k_gemm_dl<EPI_SILU, 2>), dim3(dl_tiles), dim3(512), 0, st, a);
+      hipLaunchKernelGGL((k_gemm_dl<EPI_SILU, 2>), dim3(dl_tiles), dim3(512), 0, st, QD_GEMM_PRELOAD_ARGS(a), a);
     } else {
       if (rope_done) *rope_done = 1;
-      hipLaunchKernelGGL((k_gemm_dl<EPI_STORE, 2>), dim3(dl_tiles), dim3(512), 0, st, a);
+      hipLaunchKernelGGL((k_gemm_dl<EPI_STORE, 2>), dim3(dl_tiles), dim3(512), 0, st, QD_GEMM_PRELOAD_ARGS(a), a);
     }
     return hipGetLastError();
   }
@@ -3616,7 +3682,7 @@ hipError_t launch_gemm(const GemmArgs& a0, hipStream_t st, int* splits_used, int
   if (dl_tiles_n >= 256 && a.use_big != 0 && a.epi == EPI_RESID && a.K % 64 == 0 && a.lda % 8 == 0 &&
       resid_pieces) {
     if (splits_used) *splits_used = 1;
-    hipLaunchKernelGGL((k_gemm_dl<EPI_RESID, 4>), dim3(dl_tiles_n), dim3(512), 0, st, a);
+    hipLaunchKernelGGL((k_gemm_dl<EPI_RESID, 4>), dim3(dl_tiles_n), dim3(512), 0, st, QD_GEMM_PRELOAD_ARGS(a), a);
     return hipGetLastError();
   }
   // many token rows: 128x128 tiles when they alone give every CU at least one
@@ -3628,9 +3694,9 @@ hipError_t launch_gemm(const GemmArgs& a0, hipStream_t st, int* splits_used, int
                   a.N == (r.H + 2 * r.KV) * r.D && a.ldo % 4 == 0 && r.M == a.M;
     if (rope_done) *rope_done = a.fuse_rope;
     switch (a.epi) {
-      case EPI_STORE: hipLaunchKernelGGL(k_gemm_big<EPI_STORE>, dim3(big_tiles), dim3(256), 0, st, a); break;
-      case EPI_RESID: hipLaunchKernelGGL(k_gemm_big<EPI_RESID>, dim3(big_tiles), dim3(256), 0, st, a); break;
-      default: hipLaunchKernelGGL(k_gemm_big<EPI_SILU>, dim3(big_tiles), dim3(256), 0, st, a); break;
+      case EPI_STORE: hipLaunchKernelGGL(k_gemm_big<EPI_STORE>, dim3(big_tiles), dim3(256), 0, st, QD_GEMM_PRELOAD_ARGS(a), a); break;
+      case EPI_RESID: hipLaunchKernelGGL(k_gemm_big<EPI_RESID>, dim3(big_tiles), dim3(256), 0, st, QD_GEMM_PRELOAD_ARGS(a), a); break;
+      default: hipLaunchKernelGGL(k_gemm_big<EPI_SILU>, dim3(big_tiles), dim3(256), 0, st, QD_GEMM_PRELOAD_ARGS(a), a); break;
     }
     return hipGetLastError();
   }
@@ -3657,10 +3723,10 @@ hipError_t launch_gemm(const GemmArgs& a0, hipStream_t st, int* splits_used, int
       const int epi = S > 1 ? (int)EPI_PART : a.epi;
 #define QD_KS(E)                                                                                   \
   switch (C) {                                                                                     \
-    case 1: hipLaunchKernelGGL((k_gemm_ks<E, 1>), grid, dim3(512), 0, st, a); break;               \
-    case 2: hipLaunchKernelGGL((k_gemm_ks<E, 2>), grid, dim3(512), 0, st, a); break;               \
-    case 3: hipLaunchKernelGGL((k_gemm_ks<E, 3>), grid, dim3(512), 0, st, a); break;               \
-    default: hipLaunchKernelGGL((k_gemm_ks<E, 4>), grid, dim3(512), 0, st, a); break;              \
+    case 1: hipLaunchKernelGGL((k_gemm_ks<E, 1>), grid, dim3(512), 0, st, QD_GEMM_PRELOAD_ARGS(a), a); break;               \
+    case 2: hipLaunchKernelGGL((k_gemm_ks<E, 2>), grid, dim3(512), 0, st, QD_GEMM_PRELOAD_ARGS(a), a); break;               \
+    case 3: hipLaunchKernelGGL((k_gemm_ks<E, 3>), grid, dim3(512), 0, st, QD_GEMM_PRELOAD_ARGS(a), a); break;               \
+    default: hipLaunchKernelGGL((k_gemm_ks<E, 4>), grid, dim3(512), 0, st, QD_GEMM_PRELOAD_ARGS(a), a); break;              \
   }
       switch (epi) {
         case EPI_STORE: QD_KS(EPI_STORE) break;
@@ -3684,20 +3750,20 @@ hipError_t launch_gemm(const GemmArgs& a0, hipStream_t st, int* splits_used, int
   dim3 grid((a.N + 63) / 64, (a.M + 63) / 64, splits);
   if (a.defer && a.epi == EPI_RESID && splits > 1) {
     if ((size_t)splits * a.M * a.N > GEMM_PART_FLOATS) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_gemm<EPI_PART>, grid, dim3(512), 0, st, a);
+    hipLaunchKernelGGL(k_gemm<EPI_PART>, grid, dim3(512), 0, st, QD_GEMM_PRELOAD_ARGS(a), a);
     return hipGetLastError();
   }
   switch (a.epi) {
-    case EPI_STORE: hipLaunchKernelGGL(k_gemm<EPI_STORE>, grid, dim3(512), 0, st, a); break;
-    case EPI_RESID: hipLaunchKernelGGL(k_gemm<EPI_RESID>, grid, dim3(512), 0, st, a); break;
-    default: hipLaunchKernelGGL(k_gemm<EPI_SILU>, grid, dim3(512), 0, st, a); break;
+    case EPI_STORE: hipLaunchKernelGGL(k_gemm<EPI_STORE>, grid, dim3(512), 0, st, QD_GEMM_PRELOAD_ARGS(a), a); break;
+    case EPI_RESID: hipLaunchKernelGGL(k_gemm<EPI_RESID>, grid, dim3(512), 0, st, QD_GEMM_PRELOAD_ARGS(a), a); break;
+    default: hipLaunchKernelGGL(k_gemm<EPI_SILU>, grid, dim3(512), 0, st, QD_GEMM_PRELOAD_ARGS(a), a); break;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_qk_rope(const RopeArgs& a, hipStream_t st) {
   if (a.M <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_qk_rope, dim3(a.M, (a.H + 2 * a.KV + 3) / 4), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_qk_rope, dim3(a.M, (a.H + 2 * a.KV + 3) / 4), dim3(256), 0, st, QD_ROPE_PRELOAD_ARGS(a), a);
   return hipGetLastError();
 }
 
@@ -3798,18 +3864,18 @@ hipError_t launch_flash_prefill(const FlashArgs& a, int n_tiles, int tile_rows, 
   const bool rg2 = tile_rows == 2 * FLASH_ROWS;
   switch (a.D) {
     case 32:
-      if (rg2) hipLaunchKernelGGL((k_flash_prefill<32, 2>), grid, dim3(256), 0, st, a);
-      else hipLaunchKernelGGL((k_flash_prefill<32, 1>), grid, dim3(256), 0, st, a);
+      if (rg2) hipLaunchKernelGGL((k_flash_prefill<32, 2>), grid, dim3(256), 0, st, QD_FLASH_PRELOAD_ARGS(a), a);
+      else hipLaunchKernelGGL((k_flash_prefill<32, 1>), grid, dim3(256), 0, st, QD_FLASH_PRELOAD_ARGS(a), a);
       break;
     case 64:
-      if (rg2) hipLaunchKernelGGL((k_flash_prefill<64, 2>), grid, dim3(256), 0, st, a);
-      else hipLaunchKernelGGL((k_flash_prefill<64, 1>), grid, dim3(256), 0, st, a);
+      if (rg2) hipLaunchKernelGGL((k_flash_prefill<64, 2>), grid, dim3(256), 0, st, QD_FLASH_PRELOAD_ARGS(a), a);
+      else hipLaunchKernelGGL((k_flash_prefill<64, 1>), grid, dim3(256), 0, st, QD_FLASH_PRELOAD_ARGS(a), a);
       break;
     case 128:
-      if (rg2) hipLaunchKernelGGL((k_flash_prefill<128, 2>), grid, dim3(256), 0, st, a);
-      else hipLaunchKernelGGL((k_flash_prefill<128, 1>), grid, dim3(256), 0, st, a);
+      if (rg2) hipLaunchKernelGGL((k_flash_prefill<128, 2>), grid, dim3(256), 0, st, QD_FLASH_PRELOAD_ARGS(a), a);
+      else hipLaunchKernelGGL((k_flash_prefill<128, 1>), grid, dim3(256), 0, st, QD_FLASH_PRELOAD_ARGS(a), a);
       break;
-    case 256: hipLaunchKernelGGL((k_flash_prefill<256, 1>), grid, dim3(256), 0, st, a); break;
+    case 256: hipLaunchKernelGGL((k_flash_prefill<256, 1>), grid, dim3(256), 0, st, QD_FLASH_PRELOAD_ARGS(a), a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
