@@ -77,9 +77,30 @@ __global__ __launch_bounds__(256) void k_embed(const int* __restrict__ ids,
   const int r = blockIdx.x;
   const int t = min(max(ids[r], 0), V - 1);
   if (counts && threadIdx.x == 0) atomicAdd(counts + (size_t)(row_slot ? row_slot[r] : r) * V + t, 1);
+  // the row's scale and every code of it are requested at once (4 codes per thread and pass,
+  // passes unrolled, clamped offsets), then converted and stored: one round trip after the
+  // id (d is a multiple of 32 and at most 8192)
+  constexpr int NP = 8;
   const float s = Es[t];
   const int8_t* er = E + (size_t)t * d;
-  for (int c = threadIdx.x; c < d; c += 256) x[(size_t)r * d + c] = f2bf((float)er[c] * s);
+  uint32_t w[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int c = 4 * threadIdx.x + 1024 * p;
+    w[p] = *reinterpret_cast<const uint32_t*>(er + (c < d ? c : 0));
+  }
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int c = 4 * threadIdx.x + 1024 * p;
+    if (c >= d) break;
+    uint32_t o[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int v0 = ((int)(w[p] << (24 - 16 * h))) >> 24, v1 = ((int)(w[p] << (16 - 16 * h))) >> 24;
+      o[h] = (uint32_t)f2bf((float)v0 * s) | ((uint32_t)f2bf((float)v1 * s) << 16);
+    }
+    *reinterpret_cast<uint2*>(x + (size_t)r * d + c) = make_uint2(o[0], o[1]);
+  }
 }
 
 // RMSNorm of M rows, y = bf16(x / sqrt(mean(x^2) + eps) * g) (d % 8 == 0, d <= 8192): one
@@ -3423,6 +3444,7 @@ hipError_t launch_iota(int* p, int n, hipStream_t st) {
 
 hipError_t launch_embed(const int* ids, int M, const int8_t* E, const float* Es, int d, int V,
                         bf16_t* x, hipStream_t st, int* counts, const int* row_slot) {
+  if (d % 4 || d > 8192) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_embed, dim3(M), dim3(256), 0, st, ids, E, Es, d, V, x, counts, row_slot);
   return hipGetLastError();
 }
