@@ -360,7 +360,7 @@ typedef enum {
                                      and gate|up into the projection where the shape allows;
                                      0: a separate normalization launch */
   QD_TUNE_PREFILL_GEMM = 10,      /* prefill GEMMs: 1 (default) the k-sliced kernel for few
-                                     token rows and, for many rows, QK-norm / RoPE / K/V cache
+                                     token rows and, for more rows, QK-norm / RoPE / K/V cache
                                      writes in the q|k|v GEMM's epilogue where the shapes allow;
                                      0: the k-stepped kernel and a separate QK-norm launch */
   QD_TUNE_SKINNY_XSTAGE = 11,     /* batched decode projections of 2..16 rows, and those with

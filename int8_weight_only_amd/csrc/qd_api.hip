@@ -258,7 +258,7 @@ struct qd_model {
   void* noalloc_scratch = nullptr;  // this device's address of the sampler's fixed scratch
   int gemm_splits = 0;  // prefill GEMM split-K cap (0: launcher default)
   int gemm_ks = 1;      // prefill GEMMs of few rows may take the k-sliced kernel
-  int gemm_rope = 1;    // the 128x128-tile q|k|v GEMM may run QK-norm / RoPE in its epilogue
+  int gemm_rope = 1;    // the q|k|v GEMM may run QK-norm / RoPE in its epilogue (above the k-sliced kernel's rows)
   int flash_rows = 0;   // prefill attention query tile rows: 64, 128, or 0 (by prompt size)
   int skinny_norm = 1;   // batched projections fold the RMSNorm where the shape allows
   int skinny_split = 2;  // 1: never; 2: fewer than 128 channel tiles, over 16 rows; 3: all

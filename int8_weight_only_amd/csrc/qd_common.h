@@ -87,8 +87,8 @@ struct GemmArgs {
                               // merging them in-kernel; the caller runs k_resid_norm next
   int use_big = 1;            // 0: never the 128x128-tile kernel (tuning)
   int use_ks = 1;             // 0: never the k-sliced few-row kernel (tuning)
-  // EPI_STORE of the q|k|v projection: the 128x128-tile kernel may run the QK-norm, RoPE and
-  // K/V cache writes of the heads in its tile in its epilogue (rope.qkv is not read: the
+  // EPI_STORE of the q|k|v projection: the 32x128-, 128x128- and 256x256-tile kernels may run
+  // the QK-norm, RoPE and K/V cache writes of the heads in a tile in their epilogues (rope.qkv is not read: the
   // projection's rows are the tile; q heads go to out, K and V heads only to the caches)
   int fuse_rope = 0;
   RopeArgs rope{};

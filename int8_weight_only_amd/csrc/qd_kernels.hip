@@ -1107,6 +1107,65 @@ __global__ __launch_bounds__(512) void k_gemm_ks(QD_GEMM_PRELOAD_PARAMS, GemmArg
   }
 }
 
+// One (row, head) item of the q|k|v epilogue below, dims 4j .. 4j+3 and D/2+4j .. of lane j
+// (the head's L = D/8 lanes are consecutive): the head's sum of squares across those lanes,
+// then the q / K RMSNorm and RoPE at the row's position (slot sl, position p, factors
+// c01 = (cos, sin) of dims 4j, 4j+1 and c23 of 4j+2, 4j+3), or the V copy.  Every lane
+// takes part in the sum, also for rows past M.
+__device__ __forceinline__ void rope_item(const GemmArgs& a, const bf16_t* T, int TP, int row, int hl, int m0,
+                                          int n0, int j, int sl, int p, float4 c01, float4 c23, float4 gq1,
+                                          float4 gq2, float4 gk1, float4 gk2) {
+  const RopeArgs& r = a.rope;
+  const int D = r.D, half = D >> 1, L = D >> 3, nheads = r.H + 2 * r.KV;
+  const int m = m0 + row, hh = n0 / D + hl;
+  const int c0 = row * TP + hl * D + 4 * j;
+  const uint2 u1 = *reinterpret_cast<const uint2*>(&T[c0]);
+  const uint2 u2 = *reinterpret_cast<const uint2*>(&T[c0 + half]);
+  const uint32_t w1[2] = {u1.x, u1.y}, w2[2] = {u2.x, u2.y};
+  float x1[4], x2[4], ss = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    x1[2 * e] = __uint_as_float(w1[e] << 16);
+    x1[2 * e + 1] = __uint_as_float(w1[e] & 0xFFFF0000u);
+    x2[2 * e] = __uint_as_float(w2[e] << 16);
+    x2[2 * e + 1] = __uint_as_float(w2[e] & 0xFFFF0000u);
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) ss += x1[e] * x1[e] + x2[e] * x2[e];
+  for (int o = 1; o < L; o <<= 1) ss += __shfl_xor(ss, o, 64);
+  if (m >= r.M || hh >= nheads) return;
+  if (hh >= r.H + r.KV) {
+    bf16_t* dst = r.vcache + (((size_t)sl * r.KV + (hh - r.H - r.KV)) * r.max_ctx + p) * D;
+    *reinterpret_cast<uint2*>(dst + 4 * j) = u1;
+    *reinterpret_cast<uint2*>(dst + half + 4 * j) = u2;
+    return;
+  }
+  const bool isq = hh < r.H;
+  const float4 g1 = isq ? gq1 : gk1, g2 = isq ? gq2 : gk2;
+  const float gv1[4] = {g1.x, g1.y, g1.z, g1.w}, gv2[4] = {g2.x, g2.y, g2.z, g2.w};
+  const float cv[4] = {c01.x, c01.z, c23.x, c23.z}, sv[4] = {c01.y, c01.w, c23.y, c23.w};
+  const float rinv = 1.0f / sqrtf(ss / (float)D + r.eps);
+  uint32_t o1[2], o2[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    uint32_t lo1 = 0, lo2 = 0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int q = 2 * e + h;
+      const float y1 = rbf(x1[q] * rinv * gv1[q]);
+      const float y2 = rbf(x2[q] * rinv * gv2[q]);
+      lo1 |= (uint32_t)f2bf(y1 * cv[q] - y2 * sv[q]) << (16 * h);
+      lo2 |= (uint32_t)f2bf(y2 * cv[q] + y1 * sv[q]) << (16 * h);
+    }
+    o1[e] = lo1;
+    o2[e] = lo2;
+  }
+  bf16_t* dst = isq ? a.out + (size_t)m * a.ldo + (size_t)hh * D
+                    : r.kcache + (((size_t)sl * r.KV + (hh - r.H)) * r.max_ctx + p) * D;
+  *reinterpret_cast<uint2*>(dst + 4 * j) = make_uint2(o1[0], o1[1]);
+  *reinterpret_cast<uint2*>(dst + half + 4 * j) = make_uint2(o2[0], o2[1]);
+}
+
 // ------------------------------------------------------------------------------------------
 // Epilogue of a q|k|v projection tile with the QK-norm, RoPE and K/V cache writes fused in
 // (head dim D = 64 or 128, so no head straddles two tiles).  The tile's projections,
@@ -1124,7 +1183,7 @@ __device__ __forceinline__ void gemm_rope_tile(const GemmArgs& a, const bf16_t* 
   const int tid = threadIdx.x;
   const RopeArgs& r = a.rope;
   const int D = r.D, half = D >> 1, L = D >> 3, lgL = __builtin_ctz(L);
-  const int hpt = BN / D, nheads = r.H + 2 * r.KV;
+  const int hpt = BN / D;
   // item it of this thread: idx = it * NT + tid, its dims 4j .. and D/2 + 4j .. with
   // j = tid % L the same for every item (NT is a multiple of L), so the thread's q and k
   // gains are loaded once.  Every item's row slot and position are requested together and
@@ -1161,59 +1220,10 @@ __device__ __forceinline__ void gemm_rope_tile(const GemmArgs& a, const bf16_t* 
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0: the group's factors (and earlier stores)
 #pragma unroll
     for (int k = 0; k < NG; ++k) {
-      const int it = g0 + k;
-      const int idx = it * NT + tid;
-      const int gi = idx >> lgL;
-      const int row = gi / hpt, hl = gi - row * hpt;
-      const int m = m0 + row, hh = n0 / D + hl;
-      const int c0 = row * TP + hl * D + 4 * j;
-      const uint2 u1 = *reinterpret_cast<const uint2*>(&T[c0]);
-      const uint2 u2 = *reinterpret_cast<const uint2*>(&T[c0 + half]);
-      const uint32_t w1[2] = {u1.x, u1.y}, w2[2] = {u2.x, u2.y};
-      float x1[4], x2[4], ss = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        x1[2 * e] = __uint_as_float(w1[e] << 16);
-        x1[2 * e + 1] = __uint_as_float(w1[e] & 0xFFFF0000u);
-        x2[2 * e] = __uint_as_float(w2[e] << 16);
-        x2[2 * e + 1] = __uint_as_float(w2[e] & 0xFFFF0000u);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) ss += x1[e] * x1[e] + x2[e] * x2[e];
-      for (int o = 1; o < L; o <<= 1) ss += __shfl_xor(ss, o, 64);
-      if (m >= r.M || hh >= nheads) continue;
-      const int sl = slot[it], p = pos[it];
-      if (hh >= r.H + r.KV) {
-        bf16_t* dst = r.vcache + (((size_t)sl * r.KV + (hh - r.H - r.KV)) * r.max_ctx + p) * D;
-        *reinterpret_cast<uint2*>(dst + 4 * j) = u1;
-        *reinterpret_cast<uint2*>(dst + half + 4 * j) = u2;
-        continue;
-      }
-      const bool isq = hh < r.H;
-      const float4 g1 = isq ? gq1 : gk1, g2 = isq ? gq2 : gk2;
-      const float4 cs01 = c01[k], cs23 = c23[k];
-      const float gv1[4] = {g1.x, g1.y, g1.z, g1.w}, gv2[4] = {g2.x, g2.y, g2.z, g2.w};
-      const float cv[4] = {cs01.x, cs01.z, cs23.x, cs23.z}, sv[4] = {cs01.y, cs01.w, cs23.y, cs23.w};
-      const float rinv = 1.0f / sqrtf(ss / (float)D + r.eps);
-      uint32_t o1[2], o2[2];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        uint32_t lo1 = 0, lo2 = 0;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int q = 2 * e + h;
-          const float y1 = rbf(x1[q] * rinv * gv1[q]);
-          const float y2 = rbf(x2[q] * rinv * gv2[q]);
-          lo1 |= (uint32_t)f2bf(y1 * cv[q] - y2 * sv[q]) << (16 * h);
-          lo2 |= (uint32_t)f2bf(y2 * cv[q] + y1 * sv[q]) << (16 * h);
-        }
-        o1[e] = lo1;
-        o2[e] = lo2;
-      }
-      bf16_t* dst = isq ? a.out + (size_t)m * a.ldo + (size_t)hh * D
-                        : r.kcache + (((size_t)sl * r.KV + (hh - r.H)) * r.max_ctx + p) * D;
-      *reinterpret_cast<uint2*>(dst + 4 * j) = make_uint2(o1[0], o1[1]);
-      *reinterpret_cast<uint2*>(dst + half + 4 * j) = make_uint2(o2[0], o2[1]);
+      const int gi = ((g0 + k) * NT + tid) >> lgL;
+      const int row = gi / hpt;
+      rope_item(a, T, TP, row, gi - row * hpt, m0, n0, j, slot[g0 + k], pos[g0 + k], c01[k], c23[k], gq1, gq2,
+                gk1, gk2);
     }
   }
 }
@@ -1233,6 +1243,157 @@ __device__ __forceinline__ void gemm_big_rope_epilogue(const GemmArgs& a, bf16_t
         T[(wm * 64 + mt * 16 + 4 * grp + i) * TP + wn * 64 + nt * 16 + r16] = f2bf(acc[mt][nt][i] * gsc[nt]);
   __syncthreads();
   gemm_rope_tile<128, 128, 256>(a, T, m0, n0);
+}
+
+// q|k|v projection at a few hundred token rows with the QK-norm, RoPE and K/V cache writes
+// in its epilogue: 32x128 output tiles (a 128-wide tile holds whole heads, so the epilogue
+// needs no other tile's outputs), the same 4096 outputs and 8 waves per work-group as the
+// 64x64 kernel above, so a 256-row prompt still gives every CU a tile.  k advances 128 per
+// step; waves 0-3 take the first 64 k of each step and waves 4-7 the second, each wave a
+// 32x32 block of 2x2 MFMA 16x16x32 tiles, the halves added in LDS at the end.  GEMM_PF
+// steps of loads in flight, double-buffered LDS, one barrier per step, the weights turned
+// into bf16 when a step is written to LDS.  Staging: A row t / 16 takes k 8 (t % 16) ..
+// of the step from thread t, W row t / 4 takes k 32 (t % 4) .. (two 16-byte loads), both
+// in natural k order.  No split-K: one work-group per tile.
+__global__ __launch_bounds__(512) void k_gemm_qr(QD_GEMM_PRELOAD_PARAMS, GemmArgs a) {
+  QD_GEMM_PRELOAD_SET(a);
+  constexpr int BM = 32, BN = 128, BK = 128, P = GEMM_PF;
+  constexpr int OOB = (int)0x80000000;
+  constexpr int FRAG = 1088;  // one 16-row x 32-k fragment in MFMA lane order (+ padding)
+  constexpr int AFR = (BM / 16) * (BK / 32), WFR = (BN / 16) * (BK / 32);
+  __shared__ __align__(16) unsigned char Ab[2][AFR * FRAG];
+  __shared__ __align__(16) unsigned char Wb[2][WFR * FRAG];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int kh = wid >> 2, wn = wid & 3;
+  const int grp = lane >> 4, r16 = lane & 15;
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const int K = a.K;
+  const int nsteps = (K + BK - 1) / BK;
+
+  // rows past M (N) lie past the end of A (W) and read zero; k past K is sent out of range
+  const __amdgpu_buffer_rsrc_t arsc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.A, 0, a.M * a.lda * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t wrsc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.W, 0, a.N * K, 0x00020000);
+  const int ar = tid >> 4, ac = tid & 15;  // A: row, 8-value chunk
+  const int wr = tid >> 2, wq = tid & 3;   // W: row, 32-value quarter
+  auto slot = [](int row, int c) {  // byte offset of 8-value chunk c (of 16) of stage row row
+    const int pos = (row & 15) + 16 * (c & 3);
+    return ((row >> 4) * 4 + (c >> 2)) * FRAG + 16 * (pos ^ (c & 3));
+  };
+  struct Stage { uint4 a, w0, w1; };
+  auto fetch = [&](int step, Stage& q) {
+    const int k = step * BK;
+    q.a = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                        arsc, k + 8 * ac < K ? ((m0 + ar) * a.lda + k + 8 * ac) * 2 : OOB, 0, 0));
+    const int wo = (n0 + wr) * K + k + 32 * wq;
+    q.w0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wrsc, k + 32 * wq < K ? wo : OOB, 0, 0));
+    q.w1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                         wrsc, k + 32 * wq + 16 < K ? wo + 16 : OOB, 0, 0));
+  };
+  auto stash = [&](const Stage& q, int buf) {
+    *reinterpret_cast<uint4*>(&Ab[buf][slot(ar, ac)]) = q.a;
+    *reinterpret_cast<bf16x8_t*>(&Wb[buf][slot(wr, 4 * wq)]) = i8x8_to_bf16x8(make_uint2(q.w0.x, q.w0.y));
+    *reinterpret_cast<bf16x8_t*>(&Wb[buf][slot(wr, 4 * wq + 1)]) = i8x8_to_bf16x8(make_uint2(q.w0.z, q.w0.w));
+    *reinterpret_cast<bf16x8_t*>(&Wb[buf][slot(wr, 4 * wq + 2)]) = i8x8_to_bf16x8(make_uint2(q.w1.x, q.w1.y));
+    *reinterpret_cast<bf16x8_t*>(&Wb[buf][slot(wr, 4 * wq + 3)]) = i8x8_to_bf16x8(make_uint2(q.w1.z, q.w1.w));
+  };
+  const int rd = 16 * (lane ^ (grp & 3));  // this lane's slot in every fragment read
+
+  f32x4_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float gsc[2];  // scales of this lane's two output channels, requested first
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int n = n0 + wn * 32 + nt * 16 + r16;
+    gsc[nt] = a.scale[n < a.N ? n : 0];
+  }
+
+  // the epilogue's inputs, requested ahead of the k loop.  One (row, head) item per thread
+  // (32 rows x 128 columns in parts of 8 dims): row and head from tid / (D/8), dims 4j ..
+  // and D/2 + 4j .. with j = tid % (D/8).  Its row's slot and position, the q and k gains of
+  // its dims (the RoPE factors at its position follow the k loop)
+  const RopeArgs& r = a.rope;
+  const int L = r.D >> 3, half = r.D >> 1, hpt = BN / r.D;
+  const int rj = tid & (L - 1), rgi = tid >> __builtin_ctz(L), rrow = rgi / hpt;
+  const int rmc = min(m0 + rrow, a.M - 1);
+  const int rsl = r.row_slot[rmc], rpos = r.row_pos[rmc];
+  const float4 gq1 = *reinterpret_cast<const float4*>(r.q_gain + 4 * rj);
+  const float4 gq2 = *reinterpret_cast<const float4*>(r.q_gain + half + 4 * rj);
+  const float4 gk1 = *reinterpret_cast<const float4*>(r.k_gain + 4 * rj);
+  const float4 gk2 = *reinterpret_cast<const float4*>(r.k_gain + half + 4 * rj);
+
+  Stage q[P];
+#pragma unroll
+  for (int u = 0; u < P; ++u) fetch(u, q[u]);
+  stash(q[0], 0);
+  __syncthreads();
+  // whole groups of P steps (steps past the end multiply zeros), as in the 64x64 kernel
+  for (int i0 = 0; i0 < nsteps; i0 += P) {
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+      const int i = i0 + u;
+      const int buf = i & 1;
+      fetch(i + P, q[u]);  // into the slot step i vacated
+      // (the next step's conversion stays behind this step's MFMAs, so its wait counts the
+      // loads issued since)
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        const int kf = kh * 2 + sub;  // 32-k fragment of the step
+        bf16x8_t af[2], bw[2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+          af[mt] = *reinterpret_cast<const bf16x8_t*>(&Ab[buf][(mt * 4 + kf) * FRAG + rd]);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+          bw[nt] = *reinterpret_cast<const bf16x8_t*>(&Wb[buf][((wn * 2 + nt) * 4 + kf) * FRAG + rd]);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt)
+            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt], bw[nt], acc[mt][nt], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      stash(q[u + 1 < P ? u + 1 : 0], buf ^ 1);  // step i + 1 (zeros past the end)
+      __syncthreads();
+    }
+  }
+  // the RoPE factors of the epilogue's item ((cos, sin) of dims 4j ..), in flight while the
+  // k halves are added
+  const float2* rp = r.rope + (size_t)rpos * half + 4 * rj;
+  const float4 c01 = *reinterpret_cast<const float4*>(rp);
+  const float4 c23 = *reinterpret_cast<const float4*>(rp + 2);
+  // the second k half joins the first through LDS (the staging buffers are free now)
+  float* red = reinterpret_cast<float*>(&Wb[0][0]);  // [4 waves][16][64] floats
+  if (kh == 1) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[((wid - 4) * 16 + (mt * 2 + nt) * 4 + i) * 64 + lane] = acc[mt][nt][i];
+  }
+  __syncthreads();
+  // the tile's projections, rounded to bf16 as the plain store would write them, into T
+  // (32 rows, pitch 136) for the QK-norm / RoPE epilogue
+  bf16_t* T = reinterpret_cast<bf16_t*>(&Ab[0][0]);
+  constexpr int TP = BN + 8;
+  if (kh == 0) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          T[(mt * 16 + 4 * grp + i) * TP + wn * 32 + nt * 16 + r16] =
+              f2bf((acc[mt][nt][i] + red[(wid * 16 + (mt * 2 + nt) * 4 + i) * 64 + lane]) * gsc[nt]);
+  }
+  __syncthreads();
+  rope_item(a, T, TP, rrow, rgi - rrow * hpt, m0, n0, rj, rsl, rpos, c01, c23, gq1, gq2, gk1, gk2);
 }
 
 // Prefill GEMM for the widest projections at many token rows, operands loaded straight
@@ -3722,6 +3883,7 @@ hipError_t launch_gemm(const GemmArgs& a0, hipStream_t st, int* splits_used, int
     }
     return hipGetLastError();
   }
+  const bool want_rope = a.fuse_rope != 0;
   a.fuse_rope = 0;
   const int tiles = ((a.N + 63) / 64) * ((a.M + 63) / 64);
   // few rows (at most two 64-row tiles): the k-sliced kernel when its k splits (256..1024 k
@@ -3757,6 +3919,19 @@ hipError_t launch_gemm(const GemmArgs& a0, hipStream_t st, int* splits_used, int
         default: QD_KS(EPI_SILU) break;
       }
 #undef QD_KS
+      return hipGetLastError();
+    }
+  }
+  // q|k|v with its QK-norm / RoPE epilogue at more rows than the k-sliced kernel took:
+  // 32x128 tiles, each holding whole heads
+  {
+    const RopeArgs& r = a.rope;
+    if (want_rope && a.epi == EPI_STORE && (r.D == 64 || r.D == 128) && a.N % 128 == 0 &&
+        a.N == (r.H + 2 * r.KV) * r.D && a.ldo % 4 == 0 && r.M == a.M) {
+      a.fuse_rope = 1;
+      if (splits_used) *splits_used = 1;
+      if (rope_done) *rope_done = 1;
+      hipLaunchKernelGGL(k_gemm_qr, dim3(a.N / 128, (a.M + 31) / 32), dim3(512), 0, st, QD_GEMM_PRELOAD_ARGS(a), a);
       return hipGetLastError();
     }
   }
