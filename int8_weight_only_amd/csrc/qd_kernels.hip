@@ -674,6 +674,14 @@ __global__ __launch_bounds__(256) void k_gemv1(const int8_t* W_, const float* sc
 // prefill GEMM on MFMA: C[m][n] = scale[n] * sum_k A[m][k] * W[n][k]
 // A bf16 [M][K], W int8 [N][K] converted to bf16 in registers (exact for |q| <= 127).
 // 64x64 output tile per work-group, 4 waves in 2x2, each 32x32 = 2x2 MFMA 16x16x32 tiles.
+// A buffer-load offset the compiler must hold in a register as computed (an empty asm
+// statement that claims to change it): keeps a select between an in-range offset and the
+// out-of-range one a select, instead of a branch around each load.
+__device__ __forceinline__ int opaque_off(int off) {
+  asm("" : "+v"(off));
+  return off;
+}
+
 __device__ __forceinline__ bf16x8_t i8x8_to_bf16x8(uint2 w) {
   const uint32_t in[2] = {w.x, w.y};
   uint32_t out[4];
@@ -1730,16 +1738,19 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(QD_GEMM_PRELOAD_PARAMS, Gem
     return ((row >> 4) * 2 + (c >> 2)) * FRAG + 16 * (pos ^ (c & 3));
   };
   struct Stage { uint4 a[4]; uint4 w[2]; };
+  // (each offset passes through opaque_off: loads sharing one in-range condition were
+  // otherwise turned into a branch per load, and the branch's wait drained every load in
+  // flight)
   auto fetch = [&](int step, Stage& q) {
     const int ka = step * BK + 8 * ca, kw = step * BK + 16 * cw;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       q.a[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                             arsc, ka < a.K ? ((m0 + 32 * j + ra) * a.lda + ka) * 2 : OOB, 0, 0));
+                                             arsc, opaque_off(ka < a.K ? ((m0 + 32 * j + ra) * a.lda + ka) * 2 : OOB), 0, 0));
 #pragma unroll
     for (int j = 0; j < 2; ++j)
       q.w[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                             wrsc, kw < a.K ? (n0 + 64 * j + rw) * a.K + kw : OOB, 0, 0));
+                                             wrsc, opaque_off(kw < a.K ? (n0 + 64 * j + rw) * a.K + kw : OOB), 0, 0));
   };
   auto stash = [&](const Stage& q, int buf) {
 #pragma unroll
@@ -1768,6 +1779,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(QD_GEMM_PRELOAD_PARAMS, Gem
     for (int u = 0; u < 2; ++u) {
       const int st = s0 + u;  // steps past the end multiply zeros (whole pairs of steps)
       fetch(st + 2, q[u]);    // into the slot step st vacated
+      // (the next step's conversion stays behind this step's MFMAs, so its wait counts the
+      // loads just issued)
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
         bf16x8_t af[4], bw[4];
@@ -1783,6 +1797,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(QD_GEMM_PRELOAD_PARAMS, Gem
           for (int nt = 0; nt < 4; ++nt)
             acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt], bw[nt], acc[mt][nt], 0, 0, 0);
       }
+      __builtin_amdgcn_sched_barrier(0);
       stash(q[u ^ 1], u ^ 1);  // step st + 1
       __syncthreads();
     }
