@@ -1119,12 +1119,14 @@ __global__ __launch_bounds__(512) void k_gemm_ks(QD_GEMM_PRELOAD_PARAMS, GemmArg
 // (the head's L = D/8 lanes are consecutive): the head's sum of squares across those lanes,
 // then the q / K RMSNorm and RoPE at the row's position (slot sl, position p, factors
 // c01 = (cos, sin) of dims 4j, 4j+1 and c23 of 4j+2, 4j+3), or the V copy.  Every lane
-// takes part in the sum, also for rows past M.
+// takes part in the sum, also for rows past M.  D is 64 or 128.
+template <int D>
 __device__ __forceinline__ void rope_item(const GemmArgs& a, const bf16_t* T, int TP, int row, int hl, int m0,
                                           int n0, int j, int sl, int p, float4 c01, float4 c23, float4 gq1,
                                           float4 gq2, float4 gk1, float4 gk2) {
   const RopeArgs& r = a.rope;
-  const int D = r.D, half = D >> 1, L = D >> 3, nheads = r.H + 2 * r.KV;
+  constexpr int half = D >> 1, L = D >> 3;
+  const int nheads = r.H + 2 * r.KV;
   const int m = m0 + row, hh = n0 / D + hl;
   const int c0 = row * TP + hl * D + 4 * j;
   const uint2 u1 = *reinterpret_cast<const uint2*>(&T[c0]);
@@ -1183,15 +1185,15 @@ __device__ __forceinline__ void rope_item(const GemmArgs& a, const bf16_t* T, in
 // squares over the head added across those lanes, the RMSNorm with the head's shared gain
 // and the rotate-half rotation at the row's position as k_qk_rope computes them.  q heads
 // are written back to the projection's output, K heads to the K cache at (slot, position)
-// of the row, V heads copied to the V cache.  NT threads.
-template <int BM, int BN, int NT>
+// of the row, V heads copied to the V cache.  NT threads; D (64 or 128) equals rope.D.
+template <int BM, int BN, int NT, int D>
 __device__ __forceinline__ void gemm_rope_tile(const GemmArgs& a, const bf16_t* T, int m0, int n0) {
   constexpr int TP = BN + 8;
   constexpr int NIT = BM * BN / 8 / NT;  // (row, head, lane part) items per thread
   const int tid = threadIdx.x;
   const RopeArgs& r = a.rope;
-  const int D = r.D, half = D >> 1, L = D >> 3, lgL = __builtin_ctz(L);
-  const int hpt = BN / D;
+  constexpr int half = D >> 1, L = D >> 3, lgL = __builtin_ctz(L);
+  constexpr int hpt = BN / D;
   // item it of this thread: idx = it * NT + tid, its dims 4j .. and D/2 + 4j .. with
   // j = tid % L the same for every item (NT is a multiple of L), so the thread's q and k
   // gains are loaded once.  Every item's row slot and position are requested together and
@@ -1230,7 +1232,7 @@ __device__ __forceinline__ void gemm_rope_tile(const GemmArgs& a, const bf16_t* 
     for (int k = 0; k < NG; ++k) {
       const int gi = ((g0 + k) * NT + tid) >> lgL;
       const int row = gi / hpt;
-      rope_item(a, T, TP, row, gi - row * hpt, m0, n0, j, slot[g0 + k], pos[g0 + k], c01[k], c23[k], gq1, gq2,
+      rope_item<D>(a, T, TP, row, gi - row * hpt, m0, n0, j, slot[g0 + k], pos[g0 + k], c01[k], c23[k], gq1, gq2,
                 gk1, gk2);
     }
   }
@@ -1250,7 +1252,8 @@ __device__ __forceinline__ void gemm_big_rope_epilogue(const GemmArgs& a, bf16_t
       for (int i = 0; i < 4; ++i)
         T[(wm * 64 + mt * 16 + 4 * grp + i) * TP + wn * 64 + nt * 16 + r16] = f2bf(acc[mt][nt][i] * gsc[nt]);
   __syncthreads();
-  gemm_rope_tile<128, 128, 256>(a, T, m0, n0);
+  if (a.rope.D == 128) gemm_rope_tile<128, 128, 256, 128>(a, T, m0, n0);
+  else gemm_rope_tile<128, 128, 256, 64>(a, T, m0, n0);
 }
 
 // q|k|v projection at a few hundred token rows with the QK-norm, RoPE and K/V cache writes
@@ -1401,7 +1404,8 @@ __global__ __launch_bounds__(512) void k_gemm_qr(QD_GEMM_PRELOAD_PARAMS, GemmArg
               f2bf((acc[mt][nt][i] + red[(wid * 16 + (mt * 2 + nt) * 4 + i) * 64 + lane]) * gsc[nt]);
   }
   __syncthreads();
-  rope_item(a, T, TP, rrow, rgi - rrow * hpt, m0, n0, rj, rsl, rpos, c01, c23, gq1, gq2, gk1, gk2);
+  if (r.D == 128) rope_item<128>(a, T, TP, rrow, rgi - rrow * hpt, m0, n0, rj, rsl, rpos, c01, c23, gq1, gq2, gk1, gk2);
+  else rope_item<64>(a, T, TP, rrow, rgi - rrow * hpt, m0, n0, rj, rsl, rpos, c01, c23, gq1, gq2, gk1, gk2);
 }
 
 // Prefill GEMM for the widest projections at many token rows, operands loaded straight
@@ -1600,7 +1604,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dl(QD_GEMM_PRELOAD_PARAMS, Gemm
             T[(wm * 16 * MT + mt * 16 + 4 * grp + i) * TP + wn * 64 + nt * 16 + r16] = f2bf(acc[mt][nt][i] * sc);
       }
       __syncthreads();
-      gemm_rope_tile<BM, BN, 512>(a, T, m0, n0);
+      gemm_rope_tile<BM, BN, 512, 128>(a, T, m0, n0);  // (launched at head dim 128 only)
       return;
     }
   }
