@@ -1115,6 +1115,22 @@ __global__ __launch_bounds__(512) void k_gemm_ks(QD_GEMM_PRELOAD_PARAMS, GemmArg
   }
 }
 
+// Sum of v over an aligned group of L = 8 or 16 lanes in the order of a butterfly over the
+// lane index (lane ^ 1, then lane ^ 2, ..: every lane adds its partner's partial to its
+// own), with DPP lane moves in place of LDS permutes: after the first two levels the four
+// lanes of a quad hold equal values, so the half-row mirror (lane 7 - i) brings lane i the
+// other quad's sum exactly as lane ^ 4 would, and the row mirror (lane 15 - i) the other
+// eight lanes' sum as lane ^ 8 would.
+template <int L>
+__device__ __forceinline__ float lane_group_sum(float v) {
+  static_assert(L == 8 || L == 16, "8 or 16 lanes");
+  if constexpr (L == 16) return row16_sum(v);
+  v += dpp_f<0xB1>(0.0f, v);   // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(0.0f, v);   // quad_perm [2,3,0,1]
+  v += dpp_f<0x141>(0.0f, v);  // row_half_mirror
+  return v;
+}
+
 // One (row, head) item of the q|k|v epilogue below, dims 4j .. 4j+3 and D/2+4j .. of lane j
 // (the head's L = D/8 lanes are consecutive): the head's sum of squares across those lanes,
 // then the q / K RMSNorm and RoPE at the row's position (slot sl, position p, factors
@@ -1142,7 +1158,7 @@ __device__ __forceinline__ void rope_item(const GemmArgs& a, const bf16_t* T, in
   }
 #pragma unroll
   for (int e = 0; e < 4; ++e) ss += x1[e] * x1[e] + x2[e] * x2[e];
-  for (int o = 1; o < L; o <<= 1) ss += __shfl_xor(ss, o, 64);
+  ss = lane_group_sum<L>(ss);
   if (m >= r.M || hh >= nheads) return;
   if (hh >= r.H + r.KV) {
     bf16_t* dst = r.vcache + (((size_t)sl * r.KV + (hh - r.H - r.KV)) * r.max_ctx + p) * D;
