@@ -1171,20 +1171,20 @@ __device__ __forceinline__ void rope_item(const GemmArgs& a, const bf16_t* T, in
   const float gv1[4] = {g1.x, g1.y, g1.z, g1.w}, gv2[4] = {g2.x, g2.y, g2.z, g2.w};
   const float cv[4] = {c01.x, c01.z, c23.x, c23.z}, sv[4] = {c01.y, c01.w, c23.y, c23.w};
   const float rinv = 1.0f / sqrtf(ss / (float)D + r.eps);
+  // (bf16 roundings two at a time: one conversion instruction per pair of values)
+  auto bf2 = [](float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+  };
   uint32_t o1[2], o2[2];
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
-    uint32_t lo1 = 0, lo2 = 0;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int q = 2 * e + h;
-      const float y1 = rbf(x1[q] * rinv * gv1[q]);
-      const float y2 = rbf(x2[q] * rinv * gv2[q]);
-      lo1 |= (uint32_t)f2bf(y1 * cv[q] - y2 * sv[q]) << (16 * h);
-      lo2 |= (uint32_t)f2bf(y2 * cv[q] + y1 * sv[q]) << (16 * h);
-    }
-    o1[e] = lo1;
-    o2[e] = lo2;
+    const int q0 = 2 * e, q1 = 2 * e + 1;
+    const uint32_t yb1 = bf2(x1[q0] * rinv * gv1[q0], x1[q1] * rinv * gv1[q1]);
+    const uint32_t yb2 = bf2(x2[q0] * rinv * gv2[q0], x2[q1] * rinv * gv2[q1]);
+    const float y1a = __uint_as_float(yb1 << 16), y1b = __uint_as_float(yb1 & 0xFFFF0000u);
+    const float y2a = __uint_as_float(yb2 << 16), y2b = __uint_as_float(yb2 & 0xFFFF0000u);
+    o1[e] = bf2(y1a * cv[q0] - y2a * sv[q0], y1b * cv[q1] - y2b * sv[q1]);
+    o2[e] = bf2(y2a * cv[q0] + y1a * sv[q0], y2b * cv[q1] + y1b * sv[q1]);
   }
   bf16_t* dst = isq ? a.out + (size_t)m * a.ldo + (size_t)hh * D
                     : r.kcache + (((size_t)sl * r.KV + (hh - r.H)) * r.max_ctx + p) * D;
